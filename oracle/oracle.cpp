@@ -1,0 +1,401 @@
+// CPU oracle for the sparse embedding layer: multi-table EmbeddingBag forward,
+// id sort/unique, segmented gradient reduction with element-wise Adagrad, and
+// the raw-key to row map of dynamically inserted feature keys.
+//
+// TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+// benchmark's CPU-baseline leg may load this library.  It is a plain, slow,
+// sequential definition of what the GPU path computes, written from the
+// definitions directly: std::map for the key map, nested loops for gather and
+// update, fp64 accumulation with one rounding to fp32 per stored value.  It
+// shares no code, header, table or constant with the GPU library.
+//
+// Sources for what is computed (the pages are web articles; no code is given):
+//  * Embedding lookup maps categorical ids to dense vectors and dominates the
+//    parameters:  "NVIDIA Merlin Distributed Embeddings" page, introduction and
+//    section "Background" (lookup is memory bound, HBM bandwidth is the lever).
+//  * Pooling of several looked-up vectors per feature:  "Merlin HugeCTR
+//    interview" page, section three, technique (5) (pooling fused with the
+//    next layer) and section two (thousands of feature fields per sample).
+//  * Sparse optimizer touching only the rows that were used:  HugeCTR
+//    interview, section three, technique (1) ("memory-saving sparse
+//    optimizer"); the optimizer is Adagrad in every synthetic benchmark of the
+//    Merlin Distributed Embeddings page, section "Performance", synthetic
+//    model benchmarks.
+//  * Deduplicating repeated ids / one access per id per pass:  DeepRec page,
+//    section "model quality", EmbeddingVariable item 2; EcoRec page, section
+//    "research method" (merging redundant work on identical indices).
+//  * Dynamic insertion of unseen feature keys, no capacity planning:
+//    OneFlow OneEmbedding page, section "ease of use"; HugeCTR interview,
+//    section two (a hash table identifies every input feature before the
+//    embedding layer) and section three technique (1) (GPU hash table).
+//
+// Readings where the pages are silent (each is listed in the design notes):
+//  * Adagrad is the textbook form (Duchi, Hazan and Singer, JMLR 2011):
+//    G <- G + g*g (per element), w <- w - lr * g / (sqrt(G) + eps).
+//  * Sum or mean pooling; mean divides by the bag length L (duplicates count,
+//    out-of-range ids count in L but contribute nothing); an empty bag is 0.
+//  * Bags are table-major (bag b = t*B + s); the output is [B, T, D].
+//  * Duplicate ids in one batch: their gradients are summed and the row gets
+//    one Adagrad step.  Accumulation is in ascending occurrence order.
+//  * Sort is stable: equal rows keep ascending occurrence position.
+//  * A key not yet in table t's map gets row n_live[t] + (rank of its first
+//    occurrence among this call's new keys); the call is all-or-nothing when
+//    the new keys would exceed the table's row capacity.
+//  * Initial values come from a counter-based generator built on SplitMix64
+//    (Steele, Lea and Flood, OOPSLA 2014): uniform rows for dense tables and
+//    Box-Muller (1958) normal rows for inserted keys.
+//
+// Return values of the orc_* calls that check data: a bit mask,
+//   1 = an id outside [0, rows of its table)       (occurrence contributes 0)
+//   2 = offsets not starting at 0, decreasing, or not ending at nnz
+//   4 = a key equal to the reserved all-ones value (id -1, nothing inserted)
+//   8 = table full (nothing inserted, new keys get id -1)
+//  -1 = bad arguments.
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <map>
+#include <set>
+#include <vector>
+#include <algorithm>
+#include <utility>
+
+namespace {
+
+const uint64_t kReservedKey = ~0ull;
+const uint32_t kInvalidRow32 = 0xFFFFFFFFu;
+
+// SplitMix64, one output step: the state advances by the golden-ratio
+// increment and the new state is passed through the variant-13 finalizer.
+// Written from the published description of the generator.
+uint64_t splitmix64(uint64_t state) {
+  uint64_t z = state + 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+// Counter-based draw for element i of row-or-key r of table t:
+//   h = SM(SM(SM(SM(seed) ^ t) ^ r) ^ i)
+uint64_t draw_bits(uint64_t seed, int64_t t, uint64_t r, uint64_t i) {
+  uint64_t h = splitmix64(seed);
+  h = splitmix64(h ^ (uint64_t)t);
+  h = splitmix64(h ^ r);
+  return splitmix64(h ^ i);
+}
+
+// Top 24 bits as a fraction in [0, 1).
+double unit_from_bits(uint64_t h) { return (double)(h >> 40) * (1.0 / 16777216.0); }
+
+float uniform_value(uint64_t seed, int64_t t, int64_t row, int64_t d, float lo, float hi) {
+  float u = (float)unit_from_bits(draw_bits(seed, t, (uint64_t)row, (uint64_t)d));  // exact
+  float span = hi - lo;
+  return std::fmaf(u, span, lo);
+}
+
+float normal_value(uint64_t seed, int64_t t, uint64_t key, int64_t d, float stdv) {
+  uint64_t h1 = draw_bits(seed, t, key, 2ull * (uint64_t)d);
+  uint64_t h2 = draw_bits(seed, t, key, 2ull * (uint64_t)d + 1ull);
+  double u1 = ((double)(h1 >> 40) + 0.5) * (1.0 / 16777216.0);  // (0, 1)
+  double u2 = unit_from_bits(h2);                                // [0, 1)
+  const double two_pi = 6.283185307179586476925286766559;
+  double z = std::sqrt(-2.0 * std::log(u1)) * std::cos(two_pi * u2);
+  return (float)((double)stdv * z);
+}
+
+struct RowState {
+  std::vector<float> w, g;
+};
+
+struct Model {
+  int64_t T = 0, D = 0;
+  std::vector<int64_t> rows;     // capacity of each table
+  std::vector<int64_t> row_off;  // T + 1 prefix sums
+  bool hashed = false;
+  uint64_t seed = 0;
+  float lo = 0, hi = 0, stdv = 0, accum0 = 0;
+  bool has_dense = false;
+  std::vector<float> W0, G0;               // explicit initial table (small cases)
+  std::map<int64_t, RowState> touched;     // rows written since creation
+  std::vector<std::map<uint64_t, int64_t>> keymap;
+  std::vector<int64_t> n_live;
+
+  int64_t table_of(int64_t grow) const {
+    int64_t t = 0;
+    while (t + 1 < T && row_off[t + 1] <= grow) ++t;
+    return t;
+  }
+
+  // Current fp32 value of W and G for global row grow.
+  void read(int64_t grow, float* w, float* g) const {
+    auto it = touched.find(grow);
+    if (it != touched.end()) {
+      for (int64_t d = 0; d < D; ++d) { w[d] = it->second.w[d]; g[d] = it->second.g[d]; }
+      return;
+    }
+    if (has_dense) {
+      for (int64_t d = 0; d < D; ++d) { w[d] = W0[grow * D + d]; g[d] = G0[grow * D + d]; }
+      return;
+    }
+    int64_t t = table_of(grow);
+    int64_t local = grow - row_off[t];
+    if (hashed) {  // a row that was never handed out holds no defined value
+      for (int64_t d = 0; d < D; ++d) { w[d] = 0.0f; g[d] = 0.0f; }
+      return;
+    }
+    for (int64_t d = 0; d < D; ++d) {
+      w[d] = uniform_value(seed, t, local, d, lo, hi);
+      g[d] = accum0;
+    }
+  }
+};
+
+bool offsets_ok(const int64_t* offsets, int64_t bags, int64_t nnz) {
+  if (offsets[0] != 0 || offsets[bags] != nnz) return false;
+  for (int64_t b = 0; b < bags; ++b)
+    if (offsets[b + 1] < offsets[b]) return false;
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+uint64_t orc_splitmix64(uint64_t state) { return splitmix64(state); }
+uint64_t orc_draw_bits(uint64_t seed, int64_t t, uint64_t r, uint64_t i) {
+  return draw_bits(seed, t, r, i);
+}
+float orc_init_uniform(uint64_t seed, int64_t t, int64_t row, int64_t d, float lo, float hi) {
+  return uniform_value(seed, t, row, d, lo, hi);
+}
+float orc_init_normal(uint64_t seed, int64_t t, uint64_t key, int64_t d, float stdv) {
+  return normal_value(seed, t, key, d, stdv);
+}
+
+void* orc_create(int64_t T, int64_t D, const int64_t* rows, int32_t hashed, uint64_t seed,
+                 float lo, float hi, float stdv, float accum0) {
+  if (T < 1 || D < 1 || !rows) return nullptr;
+  Model* m = new Model();
+  m->T = T;
+  m->D = D;
+  m->rows.assign(rows, rows + T);
+  m->row_off.assign(T + 1, 0);
+  for (int64_t t = 0; t < T; ++t) m->row_off[t + 1] = m->row_off[t] + rows[t];
+  m->hashed = hashed != 0;
+  m->seed = seed;
+  m->lo = lo;
+  m->hi = hi;
+  m->stdv = stdv;
+  m->accum0 = accum0;
+  m->keymap.resize(T);
+  m->n_live.assign(T, 0);
+  return m;
+}
+
+void orc_destroy(void* h) { delete static_cast<Model*>(h); }
+
+// Replace the initial table with explicit values (all rows, row-major).
+int32_t orc_set_dense(void* h, const float* W, const float* G) {
+  Model* m = static_cast<Model*>(h);
+  int64_t n = m->row_off[m->T] * m->D;
+  m->W0.assign(W, W + n);
+  m->G0.assign(G, G + n);
+  m->has_dense = true;
+  m->touched.clear();
+  return 0;
+}
+
+// out[s, t, :] = c_b * sum_{j in bag b} W[row_off[t] + ids[j], :],  b = t*B + s.
+int32_t orc_forward(void* h, const int64_t* offsets, const int64_t* ids, int64_t B,
+                    int64_t nnz, int32_t pool_mean, float* out) {
+  Model* m = static_cast<Model*>(h);
+  const int64_t T = m->T, D = m->D, bags = T * B;
+  if (!offsets_ok(offsets, bags, nnz)) return 2;
+  int32_t flags = 0;
+  std::vector<double> acc(D);
+  std::vector<float> w(D), g(D);
+  for (int64_t b = 0; b < bags; ++b) {
+    const int64_t t = b / B, s = b % B;
+    const int64_t L = offsets[b + 1] - offsets[b];
+    std::fill(acc.begin(), acc.end(), 0.0);
+    for (int64_t j = offsets[b]; j < offsets[b + 1]; ++j) {
+      const int64_t id = ids[j];
+      if (id < 0 || id >= m->rows[t]) { flags |= 1; continue; }
+      m->read(m->row_off[t] + id, w.data(), g.data());
+      for (int64_t d = 0; d < D; ++d) acc[d] += (double)w[d];
+    }
+    const double c = (pool_mean && L > 0) ? 1.0 / (double)L : 1.0;
+    float* o = out + (s * T + t) * D;
+    for (int64_t d = 0; d < D; ++d) o[d] = (float)(c * acc[d]);
+  }
+  return flags;
+}
+
+// Row of every occurrence, a stable sort of (row, position) by row, and the
+// run-length decomposition of the sorted rows.  An occurrence whose id is out
+// of range gets the row 0xFFFFFFFF: it sorts last and belongs to no unique row
+// (inverse = 0xFFFFFFFF).
+int32_t orc_sort_unique(void* h, const int64_t* offsets, const int64_t* ids, int64_t B,
+                        int64_t nnz, uint32_t* sorted_rows, uint32_t* perm, uint32_t* unique,
+                        uint32_t* counts, uint32_t* seg_off, uint32_t* inverse,
+                        int64_t* num_unique) {
+  Model* m = static_cast<Model*>(h);
+  const int64_t T = m->T, bags = T * B;
+  if (!offsets_ok(offsets, bags, nnz)) return 2;
+  int32_t flags = 0;
+  std::vector<std::pair<uint32_t, uint32_t>> occ(nnz);
+  for (int64_t b = 0; b < bags; ++b) {
+    const int64_t t = b / B;
+    for (int64_t j = offsets[b]; j < offsets[b + 1]; ++j) {
+      const int64_t id = ids[j];
+      uint32_t row = kInvalidRow32;
+      if (id < 0 || id >= m->rows[t]) flags |= 1;
+      else row = (uint32_t)(m->row_off[t] + id);
+      occ[j] = {row, (uint32_t)j};
+    }
+  }
+  std::stable_sort(occ.begin(), occ.end(),
+                   [](const std::pair<uint32_t, uint32_t>& a,
+                      const std::pair<uint32_t, uint32_t>& b) { return a.first < b.first; });
+  int64_t U = 0;
+  for (int64_t k = 0; k < nnz; ++k) {
+    sorted_rows[k] = occ[k].first;
+    perm[k] = occ[k].second;
+    if (occ[k].first == kInvalidRow32) {
+      inverse[occ[k].second] = kInvalidRow32;
+      continue;
+    }
+    if (k == 0 || occ[k].first != occ[k - 1].first) {
+      unique[U] = occ[k].first;
+      seg_off[U] = (uint32_t)k;
+      counts[U] = 0;
+      ++U;
+    }
+    counts[U - 1] += 1;
+    inverse[occ[k].second] = (uint32_t)(U - 1);
+  }
+  int64_t valid = 0;
+  for (int64_t u = 0; u < U; ++u) valid += counts[u];
+  seg_off[U] = (uint32_t)valid;
+  *num_unique = U;
+  return flags;
+}
+
+// Gradient of the pooled lookup summed per row, then one Adagrad step on every
+// row that occurs in the batch (and on no other row).
+int32_t orc_backward_adagrad(void* h, const int64_t* offsets, const int64_t* ids, int64_t B,
+                             int64_t nnz, int32_t pool_mean, const float* grad_out, float lr,
+                             float eps) {
+  Model* m = static_cast<Model*>(h);
+  const int64_t T = m->T, D = m->D, bags = T * B;
+  if (!offsets_ok(offsets, bags, nnz)) return 2;
+  int32_t flags = 0;
+  std::map<int64_t, std::vector<double>> gsum;
+  for (int64_t b = 0; b < bags; ++b) {
+    const int64_t t = b / B, s = b % B;
+    const int64_t L = offsets[b + 1] - offsets[b];
+    const double c = (pool_mean && L > 0) ? 1.0 / (double)L : 1.0;
+    const float* go = grad_out + (s * T + t) * D;
+    for (int64_t j = offsets[b]; j < offsets[b + 1]; ++j) {
+      const int64_t id = ids[j];
+      if (id < 0 || id >= m->rows[t]) { flags |= 1; continue; }
+      std::vector<double>& acc = gsum[m->row_off[t] + id];
+      if (acc.empty()) acc.assign(D, 0.0);
+      for (int64_t d = 0; d < D; ++d) acc[d] += c * (double)go[d];
+    }
+  }
+  const double dlr = (double)lr, deps = (double)eps;
+  std::vector<float> w(D), g(D);
+  for (auto& kv : gsum) {
+    m->read(kv.first, w.data(), g.data());
+    RowState next;
+    next.w.resize(D);
+    next.g.resize(D);
+    for (int64_t d = 0; d < D; ++d) {
+      const double gr = kv.second[d];
+      const double G1 = (double)g[d] + gr * gr;
+      const double w1 = (double)w[d] - dlr * gr / (std::sqrt(G1) + deps);
+      next.g[d] = (float)G1;
+      next.w[d] = (float)w1;
+    }
+    m->touched[kv.first] = std::move(next);
+  }
+  return flags;
+}
+
+// Current values of global rows grows[0..n).
+int32_t orc_read_rows(void* h, const int64_t* grows, int64_t n, float* W, float* G) {
+  Model* m = static_cast<Model*>(h);
+  const int64_t total = m->row_off[m->T];
+  for (int64_t i = 0; i < n; ++i) {
+    if (grows[i] < 0 || grows[i] >= total) return -1;
+    m->read(grows[i], W + i * m->D, G + i * m->D);
+  }
+  return 0;
+}
+
+int64_t orc_touched_count(void* h) { return (int64_t) static_cast<Model*>(h)->touched.size(); }
+
+int64_t orc_touched_rows(void* h, int64_t* out) {
+  Model* m = static_cast<Model*>(h);
+  int64_t i = 0;
+  for (auto& kv : m->touched) out[i++] = kv.first;
+  return i;
+}
+
+// keys (CSR, table-major like ids) -> table-local rows, inserting unseen keys.
+int32_t orc_hash_find_or_insert(void* h, const int64_t* offsets, const uint64_t* keys,
+                                int64_t B, int64_t nnz, int64_t* ids_out) {
+  Model* m = static_cast<Model*>(h);
+  const int64_t T = m->T, D = m->D, bags = T * B;
+  if (!m->hashed) return -1;
+  if (!offsets_ok(offsets, bags, nnz)) return 2;
+  int32_t flags = 0;
+  // Pass 1: would this call's distinct new keys fit in every table?
+  bool full = false;
+  for (int64_t t = 0; t < T; ++t) {
+    std::set<uint64_t> fresh;
+    for (int64_t j = offsets[t * B]; j < offsets[(t + 1) * B]; ++j) {
+      if (keys[j] == kReservedKey) continue;
+      if (m->keymap[t].find(keys[j]) == m->keymap[t].end()) fresh.insert(keys[j]);
+    }
+    if (m->n_live[t] + (int64_t)fresh.size() > m->rows[t]) full = true;
+  }
+  if (full) flags |= 8;
+  // Pass 2: look up, inserting in order of first occurrence unless full.
+  std::vector<float> w(D);
+  for (int64_t t = 0; t < T; ++t) {
+    for (int64_t j = offsets[t * B]; j < offsets[(t + 1) * B]; ++j) {
+      const uint64_t key = keys[j];
+      if (key == kReservedKey) { flags |= 4; ids_out[j] = -1; continue; }
+      auto it = m->keymap[t].find(key);
+      if (it != m->keymap[t].end()) { ids_out[j] = it->second; continue; }
+      if (full) { ids_out[j] = -1; continue; }
+      const int64_t row = m->n_live[t]++;
+      m->keymap[t][key] = row;
+      RowState rs;
+      rs.w.resize(D);
+      rs.g.assign(D, m->accum0);
+      for (int64_t d = 0; d < D; ++d) rs.w[d] = normal_value(m->seed, t, key, d, m->stdv);
+      m->touched[m->row_off[t] + row] = std::move(rs);
+      ids_out[j] = row;
+    }
+  }
+  return flags;
+}
+
+int64_t orc_n_live(void* h, int64_t t) { return static_cast<Model*>(h)->n_live[t]; }
+
+// The key -> row map of table t in ascending key order; returns its size.
+int64_t orc_hash_export(void* h, int64_t t, uint64_t* keys, int64_t* rows, int64_t cap) {
+  Model* m = static_cast<Model*>(h);
+  int64_t i = 0;
+  for (auto& kv : m->keymap[t]) {
+    if (i < cap) { keys[i] = kv.first; rows[i] = kv.second; }
+    ++i;
+  }
+  return i;
+}
+
+}  // extern "C"
