@@ -1,0 +1,200 @@
+/*
+ * embtab.h -- C ABI of the MI355X (gfx950) sparse embedding layer.
+ *
+ * What is computed (all pages are web articles; none gives code):
+ *  - Embedding lookup: an id selects one row of a table; tables hold most of a
+ *    recommender's parameters and lookups are memory bound ("NVIDIA Merlin
+ *    Distributed Embeddings" page, introduction and section "Background").
+ *  - Pooled lookup: the rows of one multi-hot feature are pooled (summed or
+ *    averaged) into one vector ("Merlin HugeCTR interview" page, section three,
+ *    technique (5), and section two: thousands of feature fields per sample).
+ *  - Sparse Adagrad: only rows touched by the batch are updated, with the
+ *    Adagrad optimizer of the synthetic DLRM benchmarks ("NVIDIA Merlin
+ *    Distributed Embeddings", section "Performance", synthetic models; HugeCTR
+ *    interview, section three, technique (1): memory-saving sparse optimizer).
+ *  - Deduplication: repeated ids are merged so each touched row is read and
+ *    written once per pass (DeepRec page, section "model quality",
+ *    EmbeddingVariable item 2; EcoRec page, section "research method").
+ *  - Dynamic keys: a GPU hash table maps raw feature keys to rows and inserts
+ *    unseen keys on first sight (OneFlow OneEmbedding page, section "ease of
+ *    use"; HugeCTR interview, section two and section three technique (1)).
+ *
+ * Conventions shared by every call
+ *  - Pointers are DEVICE pointers unless marked HOST.  The library allocates
+ *    no device memory: weights, accumulators, state, hash slots, workspaces and
+ *    outputs all belong to the caller and must outlive the handle (or the call).
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Calls enqueue
+ *    work and return without waiting; results are ready when the stream is.
+ *    A handle must not be used on two streams at the same time.
+ *  - Batches are CSR and table-major: bag b = t*B + s (table t, sample s),
+ *    bag b holds occurrences offsets[b] .. offsets[b+1]-1, offsets[0] = 0 and
+ *    offsets[T*B] = nnz.  `ids` are table-local rows (int64).  Pooled outputs
+ *    and upstream gradients are fp32 [B, T, D], row-major.
+ *  - Argument errors found on the host (null pointers, sizes, workspace too
+ *    small) return at once and enqueue nothing.  Data errors found on the
+ *    device set bits of a sticky error word in the state buffer, read and
+ *    cleared by emb_status_sync:
+ *      EMB_FLAG_OUT_OF_RANGE  an id outside [0, rows of its table): that
+ *                             occurrence contributes 0 and updates nothing;
+ *      EMB_FLAG_BAD_OFFSETS   offsets not starting at 0, decreasing, or not
+ *                             ending at nnz: outputs of that call are
+ *                             unspecified, but no memory outside the given
+ *                             arrays is touched;
+ *      EMB_FLAG_RESERVED_KEY  a raw key equal to EMB_EMPTY_KEY (id -1);
+ *      EMB_FLAG_TABLE_FULL    see emb_hash_find_or_insert.
+ */
+#ifndef EMBTAB_H
+#define EMBTAB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct emb_table_s* emb_table_t;
+
+typedef enum {
+  EMB_OK = 0,
+  EMB_ERR_INVALID_ARG = 1,
+  EMB_ERR_UNSUPPORTED = 2,
+  EMB_ERR_WORKSPACE = 3,
+  EMB_ERR_OUT_OF_RANGE = 4,
+  EMB_ERR_BAD_OFFSETS = 5,
+  EMB_ERR_RESERVED_KEY = 6,
+  EMB_ERR_TABLE_FULL = 7,
+  EMB_ERR_HIP = 8
+} emb_status_t;
+
+#define EMB_FLAG_OUT_OF_RANGE 1u
+#define EMB_FLAG_BAD_OFFSETS 2u
+#define EMB_FLAG_RESERVED_KEY 4u
+#define EMB_FLAG_TABLE_FULL 8u
+
+/* The all-ones key marks an empty hash slot and may not be used as a key. */
+#define EMB_EMPTY_KEY 0xFFFFFFFFFFFFFFFFull
+
+typedef enum { EMB_POOL_SUM = 0, EMB_POOL_MEAN = 1 } emb_pool_t;
+
+typedef struct {
+  int32_t num_tables;             /* T >= 1 */
+  int32_t dim;                    /* D: 4 <= D <= 1024, D % 4 == 0, same for all tables */
+  const int64_t* rows_per_table;  /* HOST [T], each >= 1; sum < 2^32 - 1.  For hashed
+                                     tables: the row capacity, <= max_load * hash_capacity */
+  float* weights;                 /* [sum rows, D] fp32, row-major; table t starts at row
+                                     off_t = sum_{t' < t} rows_per_table[t'] */
+  float* accum;                   /* Adagrad accumulator, same shape as weights */
+  void* state;                    /* emb_state_bytes(T) bytes, 256-byte aligned */
+  int32_t hashed;                 /* 0: ids are rows; 1: every table is keyed by raw u64 keys */
+  int64_t hash_capacity;          /* slots per table, a power of two >= 16 (hashed only) */
+  float max_load;                 /* rows_per_table[t] <= max_load * capacity; max_load <= 0.9 */
+  void* hash_slots;               /* emb_hash_bytes(T, capacity) bytes (hashed only) */
+  uint64_t seed;                  /* seed of the counter-based initialiser */
+  float init_lo, init_hi;         /* dense tables: W ~ U[init_lo, init_hi) */
+  float init_std;                 /* hashed tables: a new key's row ~ N(0, init_std^2) */
+  float accum_init;               /* initial Adagrad accumulator of every row */
+  int32_t init_storage;           /* 1: initialise weights, accum, slots and state;
+                                     0: attach to storage written by an earlier handle */
+} emb_table_desc_t;
+
+/* Bytes of the caller-owned state buffer for T tables (row offsets, row
+ * capacities, live-row counters, error word). */
+size_t emb_state_bytes(int32_t num_tables);
+
+/* Bytes of the hash slot array: T * capacity slots of 16 bytes,
+ * slot = { uint64 key; uint64 row } with key EMB_EMPTY_KEY when empty; the home
+ * slot of a key is SplitMix64's finalizer of the key masked to capacity - 1
+ * and collisions probe linearly.  Returns 0 on invalid arguments. */
+size_t emb_hash_bytes(int32_t num_tables, int64_t capacity);
+
+/* Workspace bytes that any call on handle h with `batch` samples and `nnz`
+ * occurrences needs (the maximum over all calls).  0 on invalid arguments. */
+size_t emb_workspace_bytes(emb_table_t h, int64_t batch, int64_t nnz);
+
+/* Create a handle over caller-owned storage.  With init_storage = 1 it enqueues
+ * the initialisation on `stream`: dense rows W[off_t + r, d] = init_lo +
+ * u * (init_hi - init_lo) with u the top 24 bits of
+ * SM(SM(SM(SM(seed) ^ t) ^ r) ^ d) (SM = one SplitMix64 step, Steele, Lea and
+ * Flood 2014), accum = accum_init, slots empty, live-row counters 0.  The
+ * handle itself is host memory; emb_table_destroy frees it. */
+emb_status_t emb_table_create(const emb_table_desc_t* desc, void* stream, emb_table_t* out);
+emb_status_t emb_table_destroy(emb_table_t h);
+
+/* Raw keys -> table-local rows, inserting unseen keys (OneFlow OneEmbedding
+ * page, section "ease of use"; HugeCTR interview, section three, technique (1)).
+ *   offsets [T*B+1] int64, keys [nnz] uint64 (CSR, table-major like ids),
+ *   ids_out [nnz] int64.
+ * A key already in table t's map gets its row.  A key not yet there gets row
+ * n_live[t] + r, where r ranks its first occurrence among this call's new keys
+ * of table t (in occurrence order); its weights are initialised to
+ * init_std * z, z the Box-Muller normal of the draws SM-chain(seed, t, key,
+ * 2d) and (.., 2d+1), and its accumulator to accum_init.  All-or-nothing: if
+ * the new keys of any table would exceed rows_per_table, nothing is inserted,
+ * new keys get id -1 and EMB_FLAG_TABLE_FULL is set.  Reserved keys get -1.
+ * Row assignment is deterministic; slot positions are not (several layouts
+ * are correct).  Needs a hashed handle. */
+emb_status_t emb_hash_find_or_insert(emb_table_t h, const int64_t* offsets,
+                                     const uint64_t* keys, int64_t batch, int64_t nnz,
+                                     int64_t* ids_out, void* ws, size_t ws_bytes,
+                                     void* stream);
+
+/* Pooled lookup ("Merlin Distributed Embeddings", introduction and
+ * "Background"; HugeCTR interview, section three, technique (5)):
+ *   out[s, t, :] = c_b * sum_{j in bag b} W[off_t + ids[j], :],  b = t*B + s,
+ *   c_b = 1 (EMB_POOL_SUM) or 1 / (offsets[b+1] - offsets[b]) (EMB_POOL_MEAN);
+ *   an empty bag gives 0.  fp32 accumulation.  `ws` may be NULL. */
+emb_status_t emb_bag_forward(emb_table_t h, const int64_t* offsets, const int64_t* ids,
+                             int64_t batch, int64_t nnz, emb_pool_t pool, float* out,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/* Backward of emb_bag_forward fused with one element-wise Adagrad step on the
+ * touched rows (Adagrad per the synthetic benchmarks of "Merlin Distributed
+ * Embeddings", section "Performance"; textbook form of Duchi, Hazan and
+ * Singer 2011):
+ *   rows_j = off_t + ids[j]; stable sort by row; unique / inverse / counts;
+ *   g_u = sum over occurrences j of row u of c_b(j) * grad_out[s(j), t(j), :]
+ *   G_u += g_u * g_u;   W_u -= lr * g_u / (sqrt(G_u) + eps)       (per element)
+ * Each touched row gets exactly one step however often it occurs; rows not in
+ * the batch are neither read nor written.  Deterministic: no float atomics.
+ *   grad_out [B, T, D] fp32.  ws: emb_workspace_bytes(h, batch, nnz) bytes. */
+emb_status_t emb_bag_backward_adagrad(emb_table_t h, const int64_t* offsets,
+                                      const int64_t* ids, int64_t batch, int64_t nnz,
+                                      emb_pool_t pool, const float* grad_out, float lr,
+                                      float eps, void* ws, size_t ws_bytes, void* stream);
+
+/* Waits for `stream`, returns the highest-priority device error (TABLE_FULL,
+ * RESERVED_KEY, BAD_OFFSETS, OUT_OF_RANGE, in that order) or EMB_OK, stores
+ * the raw EMB_FLAG_* bits in *flags_out (HOST, may be NULL) and clears them. */
+emb_status_t emb_status_sync(emb_table_t h, void* stream, uint32_t* flags_out);
+
+/* HOST n_live_out[T]: rows handed out so far in each hashed table (waits for
+ * the stream). */
+emb_status_t emb_hash_n_live(emb_table_t h, void* stream, int64_t* n_live_out);
+
+/* For table t: key_of_row[r] = the key mapped to row r, for r < n_live[t]
+ * (the map is a bijection onto [0, n_live)); key_of_row [rows_per_table[t]]. */
+emb_status_t emb_hash_export(emb_table_t h, int32_t table, uint64_t* key_of_row,
+                             void* stream);
+
+/* The sort / unique stage of emb_bag_backward_adagrad with its results copied
+ * out (same kernels).  sorted_rows[nnz] (global rows; an out-of-range
+ * occurrence has 0xFFFFFFFF and sorts last), perm[nnz] (occurrence index of
+ * each sorted entry; stable), unique[nnz] (first num_unique used, ascending),
+ * counts[nnz], seg_off[nnz+1] (first num_unique+1 used), inverse[nnz]
+ * (unique index of each occurrence, 0xFFFFFFFF when out of range), num_unique
+ * (device uint32).  Outputs other than num_unique may be NULL. */
+emb_status_t emb_debug_sort_unique(emb_table_t h, const int64_t* offsets, const int64_t* ids,
+                                   int64_t batch, int64_t nnz, uint32_t* sorted_rows,
+                                   uint32_t* perm, uint32_t* unique, uint32_t* counts,
+                                   uint32_t* seg_off, uint32_t* inverse, uint32_t* num_unique,
+                                   void* ws, size_t ws_bytes, void* stream);
+
+/* Human-readable name of a status code (static string). */
+const char* emb_status_string(emb_status_t s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EMBTAB_H */

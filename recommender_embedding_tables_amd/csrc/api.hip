@@ -1,0 +1,338 @@
+// C ABI of the sparse embedding library (declared in include/embtab.h):
+// host-side validation, workspace planning and the launch sequence of each
+// call on the caller's stream.  No device memory is allocated here.
+#include <cmath>
+#include <cstring>
+#include <new>
+
+#include "embtab_internal.hpp"
+
+namespace embtab {
+
+namespace {
+
+size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int bit_width(uint64_t v) {
+  int b = 0;
+  while (v) {
+    ++b;
+    v >>= 1;
+  }
+  return b;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+emb_status_t hip_status(hipError_t e) { return e == hipSuccess ? EMB_OK : EMB_ERR_HIP; }
+
+}  // namespace
+
+bool make_plan(const Handle& h, int64_t B, int64_t nnz, Plan* p) {
+  if (B < 0 || nnz < 0 || nnz >= 0xFFFFFFF0ll) return false;
+  if (B * (int64_t)h.T >= 0xFFFFFFF0ll) return false;
+  p->nnz = nnz;
+  p->B = B;
+  p->T = h.T;
+  p->D = h.D;
+  int bits = bit_width((uint64_t)h.total_rows);  // the sentinel total_rows must fit
+  if (bits < 1) bits = 1;
+  p->passes = (bits + kMaxDigitBits - 1) / kMaxDigitBits;
+  int base = bits / p->passes, extra = bits % p->passes, sh = 0;
+  for (int i = 0; i < p->passes; ++i) {
+    p->dbits[i] = base + (i < extra ? 1 : 0);
+    p->shift[i] = sh;
+    sh += p->dbits[i];
+  }
+  p->ntiles = (nnz + kSortTile - 1) / kSortTile;
+  p->chunk = chunk_len(h.D);
+  p->nchunks = (nnz + p->chunk - 1) / p->chunk;
+  const size_t n4 = sizeof(uint32_t) * (size_t)(nnz > 0 ? nnz : 1);
+  const size_t nt = (size_t)(p->ntiles > 0 ? p->ntiles : 1);
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o += align_up(bytes);
+    return at;
+  };
+  p->misc = take(sizeof(uint32_t) * (64 + 2 * (size_t)h.T));
+  p->keysA = take(n4);
+  p->valsA = take(n4);
+  p->keysB = take(n4);
+  p->valsB = take(n4);
+  p->gr = take(n4);
+  p->scale = take(n4);
+  p->tile_hist = take(sizeof(uint32_t) * kMaxRadix * nt);
+  p->digit_tot = take(sizeof(uint32_t) * kMaxRadix);
+  p->unique = take(n4);
+  p->seg_off = take(n4 + sizeof(uint32_t));
+  p->counts = take(n4);
+  p->inverse = take(n4);
+  p->ucnt = take(sizeof(uint32_t) * nt);
+  p->vcnt = take(sizeof(uint32_t) * nt);
+  const size_t nc = (size_t)(p->nchunks > 0 ? p->nchunks : 1);
+  p->part_head = take(sizeof(float) * nc * (size_t)h.D);
+  p->part_tail = take(sizeof(float) * nc * (size_t)h.D);
+  p->span_list = take(sizeof(uint32_t) * nc);
+  if (h.hashed) {
+    p->h_slot = take(n4);
+    p->h_first = take(n4);
+    p->h_tcnt = take(sizeof(uint32_t) * (size_t)((nnz + 255) / 256 + 1));
+  } else {
+    p->h_slot = p->h_first = p->h_tcnt = 0;
+  }
+  p->total = o;
+  return true;
+}
+
+}  // namespace embtab
+
+using namespace embtab;
+
+struct emb_table_s {
+  Handle h;
+};
+
+extern "C" {
+
+size_t emb_state_bytes(int32_t num_tables) {
+  if (num_tables < 1 || num_tables > (1 << 20)) return 0;
+  return state_bytes(num_tables);
+}
+
+size_t emb_hash_bytes(int32_t num_tables, int64_t capacity) {
+  if (num_tables < 1 || capacity < 16 || (capacity & (capacity - 1)) != 0 ||
+      capacity > (1ll << 31))
+    return 0;
+  return (size_t)num_tables * (size_t)capacity * 16u;
+}
+
+size_t emb_workspace_bytes(emb_table_t t, int64_t batch, int64_t nnz) {
+  if (!t) return 0;
+  Plan p;
+  if (!make_plan(t->h, batch, nnz, &p)) return 0;
+  return p.total;
+}
+
+const char* emb_status_string(emb_status_t s) {
+  switch (s) {
+    case EMB_OK: return "ok";
+    case EMB_ERR_INVALID_ARG: return "invalid argument";
+    case EMB_ERR_UNSUPPORTED: return "unsupported";
+    case EMB_ERR_WORKSPACE: return "workspace too small";
+    case EMB_ERR_OUT_OF_RANGE: return "id out of range";
+    case EMB_ERR_BAD_OFFSETS: return "bad offsets";
+    case EMB_ERR_RESERVED_KEY: return "reserved key";
+    case EMB_ERR_TABLE_FULL: return "table full";
+    case EMB_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+emb_status_t emb_table_create(const emb_table_desc_t* d, void* stream, emb_table_t* out) {
+  if (!d || !out) return EMB_ERR_INVALID_ARG;
+  *out = nullptr;
+  if (d->num_tables < 1 || d->num_tables > 1024) return EMB_ERR_INVALID_ARG;
+  if (d->dim < 4 || d->dim > 1024 || d->dim % 4 != 0) return EMB_ERR_INVALID_ARG;
+  if (!d->rows_per_table || !d->weights || !d->accum || !d->state) return EMB_ERR_INVALID_ARG;
+  if (!aligned16(d->weights) || !aligned16(d->accum) ||
+      (reinterpret_cast<uintptr_t>(d->state) & 255u) != 0)
+    return EMB_ERR_INVALID_ARG;
+  int64_t total = 0;
+  for (int t = 0; t < d->num_tables; ++t) {
+    if (d->rows_per_table[t] < 1) return EMB_ERR_INVALID_ARG;
+    total += d->rows_per_table[t];
+    if (total >= 0xFFFFFFFFll) return EMB_ERR_UNSUPPORTED;  // rows are 32-bit inside
+  }
+  if (d->hashed) {
+    if (emb_hash_bytes(d->num_tables, d->hash_capacity) == 0 || !d->hash_slots ||
+        !aligned16(d->hash_slots))
+      return EMB_ERR_INVALID_ARG;
+    if (!(d->max_load > 0.0f && d->max_load <= 0.9f)) return EMB_ERR_INVALID_ARG;
+    for (int t = 0; t < d->num_tables; ++t)
+      if ((double)d->rows_per_table[t] > (double)d->max_load * (double)d->hash_capacity)
+        return EMB_ERR_INVALID_ARG;
+  }
+  emb_table_s* tb = new (std::nothrow) emb_table_s();
+  if (!tb) return EMB_ERR_INVALID_ARG;
+  Handle& h = tb->h;
+  h.T = d->num_tables;
+  h.D = d->dim;
+  h.rows.assign(d->rows_per_table, d->rows_per_table + h.T);
+  h.row_off.assign(h.T + 1, 0);
+  for (int t = 0; t < h.T; ++t) h.row_off[t + 1] = h.row_off[t] + h.rows[t];
+  h.total_rows = h.row_off[h.T];
+  h.W = d->weights;
+  h.G = d->accum;
+  h.state = d->state;
+  h.sv = state_view(d->state, h.T);
+  h.hashed = d->hashed != 0;
+  h.capacity = h.hashed ? d->hash_capacity : 0;
+  h.slots = h.hashed ? d->hash_slots : nullptr;
+  h.seed = d->seed;
+  h.lo = d->init_lo;
+  h.hi = d->init_hi;
+  h.stdv = d->init_std;
+  h.accum0 = d->accum_init;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  if (d->init_storage) {
+    // state: flags 0, row offsets, capacities, live rows 0
+    std::vector<int64_t> host(3 * (size_t)h.T + 1, 0);
+    for (int t = 0; t <= h.T; ++t) host[t] = h.row_off[t];
+    for (int t = 0; t < h.T; ++t) host[h.T + 1 + t] = h.rows[t];
+    e = hipMemsetAsync(h.sv.flags, 0, 256, s);
+    if (e == hipSuccess)
+      e = hipMemcpyAsync(h.sv.row_off, host.data(), sizeof(int64_t) * host.size(),
+                         hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);  // `host` goes out of scope
+    if (e == hipSuccess) e = launch_init_dense(h, s);
+    if (e == hipSuccess && h.hashed)
+      e = launch_fill_u64(static_cast<uint64_t*>(h.slots), kEmptyKey,
+                          2 * (size_t)h.T * (size_t)h.capacity, s);
+  }
+  if (e != hipSuccess) {
+    delete tb;
+    return EMB_ERR_HIP;
+  }
+  *out = tb;
+  return EMB_OK;
+}
+
+emb_status_t emb_table_destroy(emb_table_t t) {
+  delete t;
+  return EMB_OK;
+}
+
+static emb_status_t check_batch(const Handle& h, const int64_t* offsets, int64_t batch,
+                                int64_t nnz) {
+  if (!offsets || batch < 0 || nnz < 0) return EMB_ERR_INVALID_ARG;
+  if (nnz >= 0xFFFFFFF0ll || batch * (int64_t)h.T >= 0xFFFFFFF0ll) return EMB_ERR_UNSUPPORTED;
+  return EMB_OK;
+}
+
+emb_status_t emb_bag_forward(emb_table_t t, const int64_t* offsets, const int64_t* ids,
+                             int64_t batch, int64_t nnz, emb_pool_t pool, float* out, void* ws,
+                             size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  if (!t || !out || (nnz > 0 && !ids)) return EMB_ERR_INVALID_ARG;
+  if (pool != EMB_POOL_SUM && pool != EMB_POOL_MEAN) return EMB_ERR_INVALID_ARG;
+  emb_status_t st = check_batch(t->h, offsets, batch, nnz);
+  if (st != EMB_OK) return st;
+  if (!aligned16(out)) return EMB_ERR_INVALID_ARG;
+  if (batch == 0) return EMB_OK;
+  return hip_status(launch_forward(t->h, offsets, ids, batch, nnz, pool == EMB_POOL_MEAN, out,
+                                   static_cast<hipStream_t>(stream)));
+}
+
+emb_status_t emb_bag_backward_adagrad(emb_table_t t, const int64_t* offsets, const int64_t* ids,
+                                      int64_t batch, int64_t nnz, emb_pool_t pool,
+                                      const float* grad_out, float lr, float eps, void* ws,
+                                      size_t ws_bytes, void* stream) {
+  if (!t || !grad_out || (nnz > 0 && !ids)) return EMB_ERR_INVALID_ARG;
+  if (pool != EMB_POOL_SUM && pool != EMB_POOL_MEAN) return EMB_ERR_INVALID_ARG;
+  if (!std::isfinite(lr) || !std::isfinite(eps) || eps < 0.0f) return EMB_ERR_INVALID_ARG;
+  emb_status_t st = check_batch(t->h, offsets, batch, nnz);
+  if (st != EMB_OK) return st;
+  if (!aligned16(grad_out)) return EMB_ERR_INVALID_ARG;
+  Plan p;
+  if (!make_plan(t->h, batch, nnz, &p)) return EMB_ERR_UNSUPPORTED;
+  if (!ws || ws_bytes < p.total || (reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
+    return EMB_ERR_WORKSPACE;
+  if (batch == 0) return EMB_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+  uint32_t *keys = nullptr, *perm = nullptr;
+  const bool mean = pool == EMB_POOL_MEAN;
+  hipError_t e = launch_sort_unique(t->h, p, offsets, ids, mean, w, &keys, &perm, s);
+  if (e == hipSuccess)
+    e = launch_segment_adagrad(t->h, p, keys, perm, mean, grad_out, lr, eps, w, s);
+  return hip_status(e);
+}
+
+emb_status_t emb_debug_sort_unique(emb_table_t t, const int64_t* offsets, const int64_t* ids,
+                                   int64_t batch, int64_t nnz, uint32_t* sorted_rows,
+                                   uint32_t* perm, uint32_t* unique, uint32_t* counts,
+                                   uint32_t* seg_off, uint32_t* inverse, uint32_t* num_unique,
+                                   void* ws, size_t ws_bytes, void* stream) {
+  if (!t || !num_unique || (nnz > 0 && !ids)) return EMB_ERR_INVALID_ARG;
+  emb_status_t st = check_batch(t->h, offsets, batch, nnz);
+  if (st != EMB_OK) return st;
+  Plan p;
+  if (!make_plan(t->h, batch, nnz, &p)) return EMB_ERR_UNSUPPORTED;
+  if (!ws || ws_bytes < p.total || (reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
+    return EMB_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+  uint32_t *keys = nullptr, *vals = nullptr;
+  hipError_t e = launch_sort_unique(t->h, p, offsets, ids, false, w, &keys, &vals, s);
+  const size_t nb = sizeof(uint32_t) * (size_t)nnz;
+  if (e == hipSuccess && sorted_rows)
+    e = launch_debug_copy_sorted(keys, (uint32_t)t->h.total_rows, sorted_rows, nnz, s);
+  if (e == hipSuccess && perm && nb)
+    e = hipMemcpyAsync(perm, vals, nb, hipMemcpyDeviceToDevice, s);
+  if (e == hipSuccess && unique && nb)
+    e = hipMemcpyAsync(unique, w + p.unique, nb, hipMemcpyDeviceToDevice, s);
+  if (e == hipSuccess && counts && nb)
+    e = hipMemcpyAsync(counts, w + p.counts, nb, hipMemcpyDeviceToDevice, s);
+  if (e == hipSuccess && seg_off)
+    e = hipMemcpyAsync(seg_off, w + p.seg_off, nb + sizeof(uint32_t), hipMemcpyDeviceToDevice, s);
+  if (e == hipSuccess && inverse && nb)
+    e = hipMemcpyAsync(inverse, w + p.inverse, nb, hipMemcpyDeviceToDevice, s);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(num_unique, w + p.misc + sizeof(uint32_t) * kMiscNumUnique,
+                       sizeof(uint32_t), hipMemcpyDeviceToDevice, s);
+  return hip_status(e);
+}
+
+emb_status_t emb_hash_find_or_insert(emb_table_t t, const int64_t* offsets, const uint64_t* keys,
+                                     int64_t batch, int64_t nnz, int64_t* ids_out, void* ws,
+                                     size_t ws_bytes, void* stream) {
+  if (!t || (nnz > 0 && (!keys || !ids_out))) return EMB_ERR_INVALID_ARG;
+  if (!t->h.hashed) return EMB_ERR_UNSUPPORTED;
+  emb_status_t st = check_batch(t->h, offsets, batch, nnz);
+  if (st != EMB_OK) return st;
+  Plan p;
+  if (!make_plan(t->h, batch, nnz, &p)) return EMB_ERR_UNSUPPORTED;
+  if (!ws || ws_bytes < p.total || (reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
+    return EMB_ERR_WORKSPACE;
+  if (nnz == 0) return EMB_OK;
+  return hip_status(launch_hash_find_or_insert(t->h, p, offsets, keys, ids_out,
+                                               static_cast<char*>(ws),
+                                               static_cast<hipStream_t>(stream)));
+}
+
+emb_status_t emb_status_sync(emb_table_t t, void* stream, uint32_t* flags_out) {
+  if (!t) return EMB_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint32_t f = 0;
+  hipError_t e = hipStreamSynchronize(s);
+  if (e == hipSuccess) e = hipMemcpy(&f, t->h.sv.flags, sizeof(f), hipMemcpyDeviceToHost);
+  if (e == hipSuccess) e = hipMemset(t->h.sv.flags, 0, sizeof(f));
+  if (e != hipSuccess) return EMB_ERR_HIP;
+  if (flags_out) *flags_out = f;
+  if (f & EMB_FLAG_TABLE_FULL) return EMB_ERR_TABLE_FULL;
+  if (f & EMB_FLAG_RESERVED_KEY) return EMB_ERR_RESERVED_KEY;
+  if (f & EMB_FLAG_BAD_OFFSETS) return EMB_ERR_BAD_OFFSETS;
+  if (f & EMB_FLAG_OUT_OF_RANGE) return EMB_ERR_OUT_OF_RANGE;
+  return EMB_OK;
+}
+
+emb_status_t emb_hash_n_live(emb_table_t t, void* stream, int64_t* n_live_out) {
+  if (!t || !n_live_out) return EMB_ERR_INVALID_ARG;
+  if (!t->h.hashed) return EMB_ERR_UNSUPPORTED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipStreamSynchronize(s);
+  if (e == hipSuccess)
+    e = hipMemcpy(n_live_out, t->h.sv.n_live, sizeof(int64_t) * t->h.T, hipMemcpyDeviceToHost);
+  return hip_status(e);
+}
+
+emb_status_t emb_hash_export(emb_table_t t, int32_t table, uint64_t* key_of_row, void* stream) {
+  if (!t || !key_of_row || table < 0 || table >= t->h.T) return EMB_ERR_INVALID_ARG;
+  if (!t->h.hashed) return EMB_ERR_UNSUPPORTED;
+  return hip_status(launch_hash_export(t->h, table, key_of_row, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

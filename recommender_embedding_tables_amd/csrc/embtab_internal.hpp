@@ -1,0 +1,166 @@
+// Internal declarations of the gfx950 sparse embedding library: handle,
+// state-buffer layout, workspace plan, device helpers and kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+#include <vector>
+
+#include "embtab.h"
+
+namespace embtab {
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+constexpr uint64_t kEmptyKey = 0xFFFFFFFFFFFFFFFFull;
+constexpr uint64_t kUnsetRow = 0xFFFFFFFFFFFFFFFFull;  // row word of an empty slot
+constexpr uint64_t kPendingBit = 1ull << 62;           // row word = kPendingBit | first j
+constexpr uint32_t kNoRow = 0xFFFFFFFFu;
+
+// Sort and unique tiles: 256 threads x 16 keys.
+constexpr int kSortThreads = 256;
+constexpr int kSortItems = 16;
+constexpr int kSortTile = kSortThreads * kSortItems;
+constexpr int kMaxDigitBits = 9;
+constexpr int kMaxRadix = 1 << kMaxDigitBits;
+
+// ---------------------------------------------------------------- state buffer
+// [0, 256): uint32 error word (+ padding); then int64 row_off[T+1], rows[T],
+// n_live[T].
+struct StateView {
+  uint32_t* flags;
+  int64_t* row_off;
+  int64_t* rows;
+  int64_t* n_live;
+};
+
+inline size_t state_bytes(int T) {
+  size_t b = 256 + sizeof(int64_t) * (size_t)(3 * T + 1);
+  return (b + 255) & ~(size_t)255;
+}
+
+inline StateView state_view(void* state, int T) {
+  char* p = static_cast<char*>(state);
+  StateView v;
+  v.flags = reinterpret_cast<uint32_t*>(p);
+  v.row_off = reinterpret_cast<int64_t*>(p + 256);
+  v.rows = v.row_off + (T + 1);
+  v.n_live = v.rows + T;
+  return v;
+}
+
+// ---------------------------------------------------------------- handle
+struct Handle {
+  int T = 0, D = 0;
+  std::vector<int64_t> rows, row_off;  // host copies
+  int64_t total_rows = 0;
+  float* W = nullptr;
+  float* G = nullptr;
+  void* state = nullptr;
+  StateView sv{};
+  bool hashed = false;
+  int64_t capacity = 0;
+  void* slots = nullptr;
+  uint64_t seed = 0;
+  float lo = 0, hi = 0, stdv = 0, accum0 = 0;
+};
+
+// Lanes that share one embedding row (a power of two <= 64) and float4s per lane.
+inline int subgroup_lanes(int D) {
+  int v = D / 4;
+  int sg = 1;
+  while (sg < v && sg < 64) sg <<= 1;
+  return sg;
+}
+inline int vec_per_lane(int D) {
+  int sg = subgroup_lanes(D);
+  return (D / 4 + sg - 1) / sg;
+}
+// Sorted occurrences per reduction chunk.
+inline int chunk_len(int D) {
+  int sg = subgroup_lanes(D);
+  return sg >= 32 ? sg : 32;
+}
+
+// ---------------------------------------------------------------- workspace plan
+struct Plan {
+  int64_t nnz = 0, B = 0;
+  int T = 0, D = 0;
+  int passes = 0;
+  int shift[4] = {0, 0, 0, 0};
+  int dbits[4] = {0, 0, 0, 0};
+  int64_t ntiles = 0;   // sort / unique tiles
+  int64_t nchunks = 0;  // reduction chunks
+  int chunk = 0;
+  size_t keysA, valsA, keysB, valsB, gr, scale;
+  size_t tile_hist, digit_tot;
+  size_t unique, seg_off, counts, inverse;
+  size_t ucnt, vcnt;
+  size_t misc;  // uint32[64]
+  size_t part_head, part_tail, span_list;
+  size_t h_slot, h_first, h_tcnt;  // hash find-or-insert
+  size_t total = 0;
+};
+
+// misc[] words
+enum : int {
+  kMiscNumUnique = 0,
+  kMiscNumValid = 1,
+  kMiscSpanCount = 2,
+  kMiscHashOverflow = 3,
+  kMiscHashNew = 8,  // uint32 per table from here (up to T)
+};
+
+bool make_plan(const Handle& h, int64_t B, int64_t nnz, Plan* p);
+
+// ---------------------------------------------------------------- device helpers
+__device__ inline uint32_t lanes_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// One SplitMix64 step from `state` (Steele, Lea and Flood 2014).
+__device__ inline uint64_t sm64(uint64_t state) {
+  uint64_t z = state + 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+// Home slot mixer of the hash table: SplitMix64's finalizer alone.
+__device__ inline uint64_t slot_mix(uint64_t k) {
+  k = (k ^ (k >> 30)) * 0xBF58476D1CE4E5B9ull;
+  k = (k ^ (k >> 27)) * 0x94D049BB133111EBull;
+  return k ^ (k >> 31);
+}
+
+// ---------------------------------------------------------------- launchers
+hipError_t launch_init_dense(const Handle& h, hipStream_t s);
+hipError_t launch_fill_u64(uint64_t* p, uint64_t v, size_t n, hipStream_t s);
+hipError_t launch_fill_f32(float* p, float v, size_t n, hipStream_t s);
+
+hipError_t launch_forward(const Handle& h, const int64_t* offsets, const int64_t* ids,
+                          int64_t B, int64_t nnz, bool mean, float* out, hipStream_t s);
+
+// Keys, radix sort and unique; results stay in the workspace.  *sorted_keys
+// and *sorted_vals receive the workspace addresses of the sorted arrays.
+hipError_t launch_sort_unique(const Handle& h, const Plan& p, const int64_t* offsets,
+                              const int64_t* ids, bool mean, char* ws, uint32_t** sorted_keys,
+                              uint32_t** sorted_vals, hipStream_t s);
+
+hipError_t launch_segment_adagrad(const Handle& h, const Plan& p, const uint32_t* keys,
+                                  const uint32_t* perm, bool mean, const float* grad_out,
+                                  float lr, float eps, char* ws, hipStream_t s);
+
+hipError_t launch_hash_find_or_insert(const Handle& h, const Plan& p, const int64_t* offsets,
+                                      const uint64_t* keys, int64_t* ids_out, char* ws,
+                                      hipStream_t s);
+
+hipError_t launch_hash_export(const Handle& h, int t, uint64_t* key_of_row, hipStream_t s);
+
+hipError_t launch_debug_copy_sorted(const uint32_t* keys, uint32_t sentinel, uint32_t* out,
+                                    int64_t n, hipStream_t s);
+
+}  // namespace embtab

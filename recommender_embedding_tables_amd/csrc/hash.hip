@@ -1,0 +1,353 @@
+// Raw-key -> row hash table with dynamic insertion, for gfx950.
+//
+// Feature keys are mapped to rows by a GPU hash table that inserts keys it has
+// not seen, so no capacity planning is needed (OneFlow OneEmbedding page,
+// section "ease of use"; "Merlin HugeCTR interview", section two: a hash table
+// identifies every input feature before the embedding layer, and section
+// three, technique (1): GPU-accelerated hash table; DeepRec page, section
+// "model quality": lock-free hash with one access per pass).
+//
+// Table t owns `cap` slots of 16 bytes {key, row}; an empty slot holds
+// key = row = all ones.  The home slot of a key is SplitMix64's finalizer of
+// the key masked to cap - 1; collisions probe linearly.  One call runs:
+//   k_hash_probe   one thread per occurrence: look the key up; a live key
+//                  gives its row.  A missing key claims a slot with a 64-bit
+//                  CAS on the key word (lock-free), and every occurrence of it
+//                  lowers the slot's row word to (PENDING | j) with atomicMin,
+//                  which leaves the first occurrence j in the slot.  A probe
+//                  sequence is bounded by `cap`: running out marks the call
+//                  full instead of looping.
+//   k_hash_first   flags first occurrences; per-block counts; per-table new-key
+//                  counts.
+//   k_hash_plan    one block: block bases (exclusive scan), per-table bases,
+//                  and the call's capacity decision (all-or-nothing).
+//   k_hash_assign  a first occurrence of table t with rank r (its order among
+//                  table t's first occurrences) writes row n_live[t] + r into
+//                  its slot and lists itself for initialisation; when the call
+//                  is full it empties the claimed slot again instead, which
+//                  restores the table exactly (the slot was empty before).
+//   k_hash_init    new rows: W = init_std * Box-Muller normal of the counter
+//                  draws (seed, t, key, 2d) and (.., 2d+1); G = accum_init.
+//   k_hash_finish  ids of new keys from their slots, live-row counters.
+// Row assignment follows first occurrence and is deterministic; which slot a
+// key lands in depends on CAS order and is not part of the contract.
+#include "embtab_internal.hpp"
+
+namespace embtab {
+
+namespace {
+
+constexpr uint32_t kNoSlot = 0xFFFFFFFFu;
+
+__device__ inline int32_t table_of(const int64_t* tb, int32_t T, int64_t j) {
+  // tb[t] = first occurrence of table t (T + 1 entries, non-decreasing).
+  int32_t lo = 0, hi = T;  // answer in [0, T)
+  while (hi - lo > 1) {
+    const int32_t mid = (lo + hi) >> 1;
+    if (tb[mid] <= j) lo = mid;
+    else hi = mid;
+  }
+  return lo;
+}
+
+__device__ inline void load_table_bounds(int64_t* tb, const int64_t* offsets, int64_t B, int32_t T,
+                                         int64_t nnz) {
+  for (int t = threadIdx.x; t <= T; t += blockDim.x) {
+    int64_t v = offsets[(int64_t)t * B];
+    tb[t] = v < 0 ? 0 : (v > nnz ? nnz : v);
+  }
+  __syncthreads();
+}
+
+__global__ void k_zero_words(uint32_t* __restrict__ p, int32_t n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0u;
+}
+
+struct Slot {
+  uint64_t key;
+  uint64_t row;
+};
+
+__global__ __launch_bounds__(256) void k_hash_probe(
+    const int64_t* __restrict__ offsets, const uint64_t* __restrict__ keys, int64_t B, int32_t T,
+    int64_t nnz, Slot* __restrict__ slots, int64_t cap, int64_t* __restrict__ ids_out,
+    uint32_t* __restrict__ slot_of, uint32_t* __restrict__ flags, uint32_t* __restrict__ misc) {
+  extern __shared__ int64_t tb[];
+  load_table_bounds(tb, offsets, B, T, nnz);
+  const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= nnz) return;
+  const uint64_t key = keys[j];
+  if (key == kEmptyKey) {
+    ids_out[j] = -1;
+    slot_of[j] = kNoSlot;
+    atomicOr(flags, EMB_FLAG_RESERVED_KEY);
+    return;
+  }
+  const int32_t t = table_of(tb, T, j);
+  Slot* st = slots + (size_t)t * (size_t)cap;
+  const uint64_t mask = (uint64_t)cap - 1u;
+  const uint64_t pend = kPendingBit | (uint64_t)j;
+  uint64_t s = slot_mix(key) & mask;
+  for (int64_t probe = 0; probe < cap; ++probe, s = (s + 1) & mask) {
+    uint64_t k = __hip_atomic_load(&st[s].key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (k == kEmptyKey) {
+      const uint64_t old = atomicCAS((unsigned long long*)&st[s].key, (unsigned long long)kEmptyKey,
+                                     (unsigned long long)key);
+      k = (old == kEmptyKey) ? key : old;
+    }
+    if (k != key) continue;
+    const uint64_t r = __hip_atomic_load(&st[s].row, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (r < kPendingBit) {  // live key from an earlier call
+      ids_out[j] = (int64_t)r;
+      slot_of[j] = kNoSlot;
+    } else {
+      if (pend < r) atomicMin((unsigned long long*)&st[s].row, (unsigned long long)pend);
+      slot_of[j] = (uint32_t)s;
+    }
+    return;
+  }
+  // every slot of the table is taken: the call cannot insert
+  slot_of[j] = kNoSlot;
+  ids_out[j] = -1;
+  misc[kMiscHashOverflow] = 1u;
+}
+
+__device__ inline bool is_first(const Slot* slots, int64_t cap, const uint32_t* slot_of,
+                                int32_t t, int64_t j) {
+  const uint32_t s = slot_of[j];
+  if (s == kNoSlot) return false;
+  return slots[(size_t)t * (size_t)cap + s].row == (kPendingBit | (uint64_t)j);
+}
+
+__global__ __launch_bounds__(256) void k_hash_first(const int64_t* __restrict__ offsets, int64_t B,
+                                                    int32_t T, int64_t nnz,
+                                                    const Slot* __restrict__ slots, int64_t cap,
+                                                    const uint32_t* __restrict__ slot_of,
+                                                    uint32_t* __restrict__ bcnt,
+                                                    uint32_t* __restrict__ misc) {
+  extern __shared__ int64_t tb[];
+  __shared__ uint32_t lds_cnt;
+  load_table_bounds(tb, offsets, B, T, nnz);
+  if (threadIdx.x == 0) lds_cnt = 0u;
+  __syncthreads();
+  const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  bool f = false;
+  int32_t t = 0;
+  if (j < nnz) {
+    t = table_of(tb, T, j);
+    f = is_first(slots, cap, slot_of, t, j);
+  }
+  const uint64_t m = __ballot(f);
+  if ((threadIdx.x & 63) == 0 && m) atomicAdd(&lds_cnt, (uint32_t)__popcll(m));
+  // per-table totals: aggregate lanes of the same table within the wave
+  if (f) {
+    const int32_t t0 = __shfl(t, __ffsll((unsigned long long)m) - 1, 64);
+    const uint64_t same = __ballot(f && t == t0);
+    if (t == t0) {
+      if (lanes_below(same) == 0u) atomicAdd(&misc[kMiscHashNew + t], (uint32_t)__popcll(same));
+    } else {
+      atomicAdd(&misc[kMiscHashNew + t], 1u);
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) bcnt[blockIdx.x] = lds_cnt;
+}
+
+__global__ __launch_bounds__(256) void k_hash_plan(uint32_t* __restrict__ bcnt, uint32_t nblocks,
+                                                   int32_t T, const int64_t* __restrict__ n_live,
+                                                   const int64_t* __restrict__ rows,
+                                                   uint32_t* __restrict__ misc,
+                                                   uint32_t* __restrict__ flags) {
+  __shared__ uint32_t lds4[4];
+  uint32_t carry = 0;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  for (uint32_t base = 0; base < nblocks; base += 256) {
+    const uint32_t idx = base + threadIdx.x;
+    const uint32_t v = idx < nblocks ? bcnt[idx] : 0u;
+    uint32_t x = v;
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t y = (uint32_t)__shfl_up((int)x, o, 64);
+      if (lane >= o) x += y;
+    }
+    if (lane == 63) lds4[w] = x;
+    __syncthreads();
+    uint32_t before = 0, all = 0;
+    for (int i = 0; i < 4; ++i) {
+      before += i < w ? lds4[i] : 0u;
+      all += lds4[i];
+    }
+    __syncthreads();
+    if (idx < nblocks) bcnt[idx] = carry + before + x - v;
+    carry += all;
+  }
+  if (threadIdx.x == 0) {
+    uint32_t full = misc[kMiscHashOverflow];
+    uint32_t acc = 0;
+    for (int t = 0; t < T; ++t) {
+      const uint32_t nw = misc[kMiscHashNew + t];
+      misc[kMiscHashNew + T + t] = acc;
+      acc += nw;
+      if (n_live[t] + (int64_t)nw > rows[t]) full = 1u;
+    }
+    misc[kMiscHashOverflow] = full;
+    misc[kMiscNumUnique] = acc;  // new keys of this call (all tables)
+    if (full) atomicOr(flags, EMB_FLAG_TABLE_FULL);
+  }
+}
+
+__global__ __launch_bounds__(256) void k_hash_assign(
+    const int64_t* __restrict__ offsets, int64_t B, int32_t T, int64_t nnz,
+    Slot* __restrict__ slots, int64_t cap, const uint32_t* __restrict__ slot_of,
+    const uint32_t* __restrict__ bbase, const int64_t* __restrict__ n_live,
+    const uint32_t* __restrict__ misc, uint32_t* __restrict__ newlist) {
+  extern __shared__ int64_t tb[];
+  __shared__ uint32_t lds4[4];
+  load_table_bounds(tb, offsets, B, T, nnz);
+  const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  bool f = false;
+  int32_t t = 0;
+  if (j < nnz) {
+    t = table_of(tb, T, j);
+    f = is_first(slots, cap, slot_of, t, j);
+  }
+  // block-wide exclusive count of first occurrences before this thread
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const uint64_t m = __ballot(f);
+  if (lane == 0) lds4[w] = (uint32_t)__popcll(m);
+  __syncthreads();
+  uint32_t before = 0;
+  for (int i = 0; i < w; ++i) before += lds4[i];
+  if (!f) return;
+  const uint32_t g = bbase[blockIdx.x] + before + lanes_below(m);
+  const uint32_t full = misc[kMiscHashOverflow];
+  Slot* sl = slots + (size_t)t * (size_t)cap + slot_of[j];
+  if (full) {
+    sl->key = kEmptyKey;
+    sl->row = kUnsetRow;
+    return;
+  }
+  const uint32_t rank = g - misc[kMiscHashNew + T + t];
+  sl->row = (uint64_t)(n_live[t] + (int64_t)rank);
+  newlist[g] = (uint32_t)j;
+}
+
+__global__ __launch_bounds__(256) void k_hash_init(
+    const int64_t* __restrict__ offsets, const uint64_t* __restrict__ keys, int64_t B, int32_t T,
+    int64_t nnz, const Slot* __restrict__ slots, int64_t cap, const uint32_t* __restrict__ slot_of,
+    const uint32_t* __restrict__ newlist, const uint32_t* __restrict__ misc,
+    const int64_t* __restrict__ row_off, float* __restrict__ W, float* __restrict__ G, int32_t D,
+    uint64_t seed, float stdv, float g0) {
+  extern __shared__ int64_t tb[];
+  load_table_bounds(tb, offsets, B, T, nnz);
+  if (misc[kMiscHashOverflow]) return;
+  const uint32_t nnew = misc[kMiscNumUnique];
+  const int32_t D4 = D >> 2;
+  const uint64_t total = (uint64_t)nnew * (uint64_t)D4;
+  const uint64_t s0 = sm64(seed);
+  for (uint64_t e = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
+       e += (uint64_t)gridDim.x * blockDim.x) {
+    const uint32_t g = (uint32_t)(e / D4);
+    const int32_t d4 = (int32_t)(e - (uint64_t)g * D4);
+    const uint32_t j = newlist[g];
+    const int32_t t = table_of(tb, T, j);
+    const uint64_t key = keys[j];
+    const uint64_t row = slots[(size_t)t * (size_t)cap + slot_of[j]].row;
+    const uint64_t pre = sm64(sm64(s0 ^ (uint64_t)t) ^ key);
+    f4 w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint64_t d = (uint64_t)(4 * d4 + i);
+      const uint64_t h1 = sm64(pre ^ (2u * d)), h2 = sm64(pre ^ (2u * d + 1u));
+      const double u1 = ((double)(h1 >> 40) + 0.5) * (1.0 / 16777216.0);
+      const double u2 = (double)(h2 >> 40) * (1.0 / 16777216.0);
+      const double z = sqrt(-2.0 * log(u1)) * cos(6.283185307179586476925286766559 * u2);
+      w[i] = (float)((double)stdv * z);
+    }
+    const size_t gi = (size_t)(row_off[t] + (int64_t)row) * D + 4 * d4;
+    *reinterpret_cast<f4*>(W + gi) = w;
+    *reinterpret_cast<f4*>(G + gi) = f4{g0, g0, g0, g0};
+  }
+}
+
+__global__ __launch_bounds__(256) void k_hash_finish(
+    const int64_t* __restrict__ offsets, int64_t B, int32_t T, int64_t nnz,
+    const Slot* __restrict__ slots, int64_t cap, const uint32_t* __restrict__ slot_of,
+    int64_t* __restrict__ ids_out, const uint32_t* __restrict__ misc) {
+  extern __shared__ int64_t tb[];
+  load_table_bounds(tb, offsets, B, T, nnz);
+  const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= nnz) return;
+  const uint32_t s = slot_of[j];
+  if (s == kNoSlot) return;
+  if (misc[kMiscHashOverflow]) {
+    ids_out[j] = -1;
+    return;
+  }
+  const int32_t t = table_of(tb, T, j);
+  ids_out[j] = (int64_t)slots[(size_t)t * (size_t)cap + s].row;
+}
+
+__global__ void k_hash_live(int32_t T, int64_t* __restrict__ n_live,
+                            const uint32_t* __restrict__ misc) {
+  const int t = threadIdx.x;
+  if (t < T && !misc[kMiscHashOverflow]) n_live[t] += (int64_t)misc[kMiscHashNew + t];
+}
+
+__global__ __launch_bounds__(256) void k_hash_export(const Slot* __restrict__ st, int64_t cap,
+                                                     uint64_t* __restrict__ key_of_row,
+                                                     int64_t nrows) {
+  for (int64_t s = (int64_t)blockIdx.x * 256 + threadIdx.x; s < cap;
+       s += (int64_t)gridDim.x * 256) {
+    const uint64_t k = st[s].key;
+    const uint64_t r = st[s].row;
+    if (k != kEmptyKey && r < kPendingBit && (int64_t)r < nrows) key_of_row[r] = k;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_hash_find_or_insert(const Handle& h, const Plan& p, const int64_t* offsets,
+                                      const uint64_t* keys, int64_t* ids_out, char* ws,
+                                      hipStream_t s) {
+  const int64_t nnz = p.nnz;
+  uint32_t* misc = reinterpret_cast<uint32_t*>(ws + p.misc);
+  uint32_t* slot_of = reinterpret_cast<uint32_t*>(ws + p.h_slot);
+  uint32_t* bcnt = reinterpret_cast<uint32_t*>(ws + p.h_tcnt);
+  uint32_t* newlist = reinterpret_cast<uint32_t*>(ws + p.h_first);
+  Slot* slots = static_cast<Slot*>(h.slots);
+  const size_t shm = sizeof(int64_t) * (size_t)(h.T + 1);
+  const unsigned nb = (unsigned)((nnz + 255) / 256);
+  const unsigned grid = nb > 0 ? nb : 1;
+  hipLaunchKernelGGL(k_zero_words, dim3(1), dim3(256), 0, s, misc, kMiscHashNew + 2 * h.T);
+  hipLaunchKernelGGL(k_hash_probe, dim3(grid), dim3(256), shm, s, offsets, keys, p.B, h.T, nnz,
+                     slots, h.capacity, ids_out, slot_of, h.sv.flags, misc);
+  hipLaunchKernelGGL(k_hash_first, dim3(grid), dim3(256), shm, s, offsets, p.B, h.T, nnz, slots,
+                     h.capacity, slot_of, bcnt, misc);
+  hipLaunchKernelGGL(k_hash_plan, dim3(1), dim3(256), 0, s, bcnt, nb, h.T, h.sv.n_live,
+                     h.sv.rows, misc, h.sv.flags);
+  hipLaunchKernelGGL(k_hash_assign, dim3(grid), dim3(256), shm, s, offsets, p.B, h.T, nnz, slots,
+                     h.capacity, slot_of, bcnt, h.sv.n_live, misc, newlist);
+  const int64_t igrid_max = (nnz * (h.D / 4) + 255) / 256;
+  const unsigned igrid = (unsigned)(igrid_max < 1 ? 1 : (igrid_max > 4096 ? 4096 : igrid_max));
+  hipLaunchKernelGGL(k_hash_init, dim3(igrid), dim3(256), shm, s, offsets, keys, p.B, h.T, nnz,
+                     slots, h.capacity, slot_of, newlist, misc, h.sv.row_off, h.W, h.G, h.D,
+                     h.seed, h.stdv, h.accum0);
+  hipLaunchKernelGGL(k_hash_finish, dim3(grid), dim3(256), shm, s, offsets, p.B, h.T, nnz, slots,
+                     h.capacity, slot_of, ids_out, misc);
+  hipLaunchKernelGGL(k_hash_live, dim3(1), dim3(h.T < 64 ? 64 : ((h.T + 63) / 64) * 64), 0, s,
+                     h.T, h.sv.n_live, misc);
+  return hipGetLastError();
+}
+
+hipError_t launch_hash_export(const Handle& h, int t, uint64_t* key_of_row, hipStream_t s) {
+  const Slot* st = static_cast<const Slot*>(h.slots) + (size_t)t * (size_t)h.capacity;
+  int64_t g = (h.capacity + 255) / 256;
+  if (g > 8192) g = 8192;
+  hipError_t e = launch_fill_u64(key_of_row, kEmptyKey, (size_t)h.rows[t], s);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_hash_export, dim3((unsigned)g), dim3(256), 0, s, st, h.capacity, key_of_row,
+                     h.rows[t]);
+  return hipGetLastError();
+}
+
+}  // namespace embtab

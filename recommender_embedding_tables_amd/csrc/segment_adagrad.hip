@@ -1,0 +1,331 @@
+// Segmented gradient reduction fused with element-wise Adagrad, for gfx950.
+//
+// After the stable sort, the occurrences of one row are contiguous.  For each
+// touched row u:  g_u = sum_k c_b(k) * grad_out[s(k), t(k), :]  and
+//   G_u += g_u * g_u;  W_u -= lr * g_u / (sqrt(G_u) + eps)   (per element),
+// the sparse, memory-saving Adagrad of the "Merlin HugeCTR interview" page
+// (section three, technique (1)) with the Adagrad optimizer of the synthetic
+// benchmarks of "NVIDIA Merlin Distributed Embeddings" (section
+// "Performance").  The form of the step is the textbook one (Duchi, Hazan and
+// Singer 2011).
+//
+// Schedule.  The sorted occurrences are cut into fixed chunks of CH positions,
+// one chunk per sub-group of SG lanes (a row is D/4 float4 columns spread over
+// the lanes), so a Zipf-hot row with tens of thousands of occurrences is
+// spread over many sub-groups instead of serialising one.  A sub-group loads
+// the chunk's metadata once (sorted key, occurrence, grad row, mean scale: one
+// element per lane), then walks the positions UF at a time: it issues the UF
+// gradient-row loads and, for every segment that ends inside the group and
+// lies wholly in the chunk, the W and G rows, before accumulating in position
+// order; a finished segment is updated in registers and written back once.
+// A segment that crosses a chunk boundary leaves fp32 partial sums (the
+// chunk's "tail" part where it starts, "head" parts in the chunks it covers);
+// its start chunk is appended to a span list and k_seg_fixup adds the parts
+// in chunk order and applies the step.  Every sum has a fixed order, so the
+// result is deterministic and no float atomics are used.
+#include "embtab_internal.hpp"
+
+namespace embtab {
+
+namespace {
+
+__device__ inline void adagrad_step(f4& w, f4& g2, const f4 g, float lr, float eps) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float G1 = __builtin_fmaf(g[i], g[i], g2[i]);
+    w[i] = w[i] - lr * g[i] / (__builtin_sqrtf(G1) + eps);
+    g2[i] = G1;
+  }
+}
+
+template <int SG, int VEC, bool MEAN, int MPL, int UF>
+__global__ __launch_bounds__(256) void k_seg_adagrad(
+    const uint32_t* __restrict__ keys, const uint32_t* __restrict__ perm,
+    const uint32_t* __restrict__ gr, const float* __restrict__ scale,
+    const float* __restrict__ grad, float* __restrict__ W, float* __restrict__ G, uint32_t n,
+    uint32_t sentinel, int32_t D, float lr, float eps, float* __restrict__ part_head,
+    float* __restrict__ part_tail, uint32_t* __restrict__ span_list,
+    uint32_t* __restrict__ misc, uint32_t nbags) {
+  constexpr int CH = SG * MPL;
+  constexpr int SGPB = 256 / SG;
+  const int lane = threadIdx.x % SG;
+  const int sgb = threadIdx.x / SG;
+  const uint32_t c = blockIdx.x * SGPB + sgb;
+  const uint32_t k0 = c * CH;
+  if (k0 >= n) return;
+  const uint32_t k1 = (k0 + CH < n) ? k0 + CH : n;
+  const int D4 = D >> 2;
+  const uint32_t key_prev = k0 > 0 ? keys[k0 - 1] : kNoRow;
+  const uint32_t key_next = k1 < n ? keys[k1] : kNoRow;
+
+  uint32_t mkey[MPL], mgr[MPL];
+  float msc[MPL];
+#pragma unroll
+  for (int i = 0; i < MPL; ++i) {
+    const uint32_t k = k0 + i * SG + lane;
+    mkey[i] = kNoRow;
+    mgr[i] = 0u;
+    msc[i] = 1.0f;
+    if (k < k1) mkey[i] = keys[k];
+  }
+#pragma unroll
+  for (int i = 0; i < MPL; ++i) {
+    const uint32_t k = k0 + i * SG + lane;
+    if (k < k1 && mkey[i] < sentinel) {
+      // Positions not written by any bag (offsets that do not tile [0, nnz))
+      // may hold stale values: such an occurrence is dropped, never followed.
+      const uint32_t j = perm[k];
+      const uint32_t g = j < n ? gr[j] : nbags;
+      if (g < nbags) {
+        mgr[i] = g;
+        if (MEAN) msc[i] = scale[j];
+      } else {
+        mkey[i] = sentinel;
+      }
+    }
+  }
+
+  f4 acc[VEC];
+#pragma unroll
+  for (int v = 0; v < VEC; ++v) acc[v] = f4{0.f, 0.f, 0.f, 0.f};
+  bool first_seg = true;
+  const uint32_t last = k1 - k0 - 1;  // last position of the chunk
+
+#pragma unroll
+  for (int i = 0; i < MPL; ++i) {
+    for (int l0 = 0; l0 < SG; l0 += UF) {
+      uint32_t kk[UF + 1], gg[UF];
+      float cc[UF];
+#pragma unroll
+      for (int u = 0; u < UF; ++u) {
+        kk[u] = (uint32_t)__shfl((int)mkey[i], l0 + u, SG);
+        gg[u] = (uint32_t)__shfl((int)mgr[i], l0 + u, SG);
+        cc[u] = MEAN ? __shfl(msc[i], l0 + u, SG) : 1.0f;
+      }
+      {
+        // key of the position after the group
+        uint32_t nx;
+        if (l0 + UF < SG) nx = (uint32_t)__shfl((int)mkey[i], l0 + UF, SG);
+        else if (i + 1 < MPL) nx = (uint32_t)__shfl((int)mkey[(i + 1) < MPL ? i + 1 : i], 0, SG);
+        else nx = key_next;
+        kk[UF] = nx;
+      }
+      bool vld[UF], endf[UF], startb[UF], cont[UF];
+      bool fs = first_seg;
+#pragma unroll
+      for (int u = 0; u < UF; ++u) {
+        const uint32_t p = (uint32_t)(i * SG + l0 + u);
+        vld[u] = (p <= last) && kk[u] < sentinel;
+        const uint32_t nxt = (p == last) ? key_next : kk[u + 1];
+        endf[u] = vld[u] && nxt != kk[u];
+        cont[u] = vld[u] && (p == last) && nxt == kk[u];
+        startb[u] = fs && kk[u] == key_prev;
+        if (endf[u]) fs = false;
+      }
+      if (!vld[0]) break;  // the rest of the chunk holds no valid keys
+      f4 g[UF][VEC], wv[UF][VEC], gv[UF][VEC];
+#pragma unroll
+      for (int u = 0; u < UF; ++u) {
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) {
+          const int d4 = lane + v * SG;
+          g[u][v] = f4{0.f, 0.f, 0.f, 0.f};
+          wv[u][v] = f4{0.f, 0.f, 0.f, 0.f};
+          gv[u][v] = f4{0.f, 0.f, 0.f, 0.f};
+          if (vld[u] && d4 < D4)
+            g[u][v] = *reinterpret_cast<const f4*>(grad + (size_t)gg[u] * D + 4 * d4);
+          if (endf[u] && !startb[u] && d4 < D4) {
+            wv[u][v] = *reinterpret_cast<const f4*>(W + (size_t)kk[u] * D + 4 * d4);
+            gv[u][v] = *reinterpret_cast<const f4*>(G + (size_t)kk[u] * D + 4 * d4);
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < UF; ++u) {
+        if (!vld[u]) continue;
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) acc[v] += MEAN ? g[u][v] * cc[u] : g[u][v];
+        if (endf[u]) {
+          if (!startb[u]) {
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) {
+              const int d4 = lane + v * SG;
+              if (d4 < D4) {
+                adagrad_step(wv[u][v], gv[u][v], acc[v], lr, eps);
+                *reinterpret_cast<f4*>(W + (size_t)kk[u] * D + 4 * d4) = wv[u][v];
+                *reinterpret_cast<f4*>(G + (size_t)kk[u] * D + 4 * d4) = gv[u][v];
+              }
+            }
+          } else {
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) {
+              const int d4 = lane + v * SG;
+              if (d4 < D4) *reinterpret_cast<f4*>(part_head + (size_t)c * D + 4 * d4) = acc[v];
+            }
+          }
+#pragma unroll
+          for (int v = 0; v < VEC; ++v) acc[v] = f4{0.f, 0.f, 0.f, 0.f};
+        } else if (cont[u]) {
+          float* dst = startb[u] ? part_head : part_tail;
+#pragma unroll
+          for (int v = 0; v < VEC; ++v) {
+            const int d4 = lane + v * SG;
+            if (d4 < D4) *reinterpret_cast<f4*>(dst + (size_t)c * D + 4 * d4) = acc[v];
+          }
+          if (!startb[u] && lane == 0) {
+            const uint32_t slot = atomicAdd(&misc[kMiscSpanCount], 1u);
+            span_list[slot] = c;
+          }
+        }
+      }
+      first_seg = fs;
+    }
+  }
+}
+
+// Adds the parts of every segment that crosses chunk boundaries and applies
+// the Adagrad step.  One block per listed span; SGPB sub-groups each add every
+// SGPB-th head part in chunk order, then sub-group 0 adds
+// tail + part_sum[0] + ... + part_sum[SGPB-1] in that order.
+template <int SG, int VEC>
+__global__ __launch_bounds__(256) void k_seg_fixup(
+    const uint32_t* __restrict__ keys, uint32_t n, int32_t CH, float* __restrict__ W,
+    float* __restrict__ G, int32_t D, float lr, float eps, const float* __restrict__ part_head,
+    const float* __restrict__ part_tail, const uint32_t* __restrict__ span_list,
+    const uint32_t* __restrict__ misc) {
+  constexpr int SGPB = 256 / SG;
+  __shared__ f4 red[SGPB][SG * VEC];
+  __shared__ uint32_t s_end;
+  const int lane = threadIdx.x % SG;
+  const int sgb = threadIdx.x / SG;
+  const int D4 = D >> 2;
+  const uint32_t nspan = misc[kMiscSpanCount];
+  for (uint32_t sp = blockIdx.x; sp < nspan; sp += gridDim.x) {
+    const uint32_t c0 = span_list[sp];
+    const uint32_t pos_last = (c0 + 1) * (uint32_t)CH - 1u;  // chunk c0 is full
+    const uint32_t row = keys[pos_last];
+    // Find the chunk where the run ends: first chunk c > c0 whose successor
+    // position no longer holds `row`.  256 chunks are tested per round.
+    if (threadIdx.x == 0) s_end = 0xFFFFFFFFu;
+    __syncthreads();
+    for (uint32_t cb = c0 + 1;; cb += 256) {
+      const uint32_t cc = cb + threadIdx.x;
+      const uint64_t nxt = (uint64_t)(cc + 1) * (uint32_t)CH;  // first position after chunk cc
+      bool ends = false;
+      if ((uint64_t)cc * (uint32_t)CH < n) ends = (nxt >= n) || keys[nxt] != row;
+      if (ends) atomicMin(&s_end, cc);
+      __syncthreads();
+      const uint32_t e = s_end;
+      __syncthreads();
+      if (e != 0xFFFFFFFFu) break;
+      if ((uint64_t)(cb + 256) * (uint32_t)CH >= n) break;  // cannot happen for a listed span
+    }
+    const uint32_t c1 = s_end;
+    f4 acc[VEC];
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) acc[v] = f4{0.f, 0.f, 0.f, 0.f};
+    if (c1 != 0xFFFFFFFFu) {
+      uint32_t cc = c0 + 1 + sgb;
+      for (; cc + 3 * SGPB <= c1; cc += 4 * SGPB) {
+        f4 x[4][VEC];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int v = 0; v < VEC; ++v) {
+            const int d4 = lane + v * SG;
+            x[q][v] = d4 < D4 ? *reinterpret_cast<const f4*>(part_head + (size_t)(cc + q * SGPB) * D + 4 * d4)
+                              : f4{0.f, 0.f, 0.f, 0.f};
+          }
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int v = 0; v < VEC; ++v) acc[v] += x[q][v];
+      }
+      for (; cc <= c1; cc += SGPB) {
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) {
+          const int d4 = lane + v * SG;
+          if (d4 < D4) acc[v] += *reinterpret_cast<const f4*>(part_head + (size_t)cc * D + 4 * d4);
+        }
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) red[sgb][lane + v * SG] = acc[v];
+    __syncthreads();
+    if (sgb == 0 && c1 != 0xFFFFFFFFu) {
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) {
+        const int d4 = lane + v * SG;
+        if (d4 >= D4) continue;
+        f4 tot = *reinterpret_cast<const f4*>(part_tail + (size_t)c0 * D + 4 * d4);
+        for (int q = 0; q < SGPB; ++q) tot += red[q][lane + v * SG];
+        f4 w = *reinterpret_cast<const f4*>(W + (size_t)row * D + 4 * d4);
+        f4 g2 = *reinterpret_cast<const f4*>(G + (size_t)row * D + 4 * d4);
+        adagrad_step(w, g2, tot, lr, eps);
+        *reinterpret_cast<f4*>(W + (size_t)row * D + 4 * d4) = w;
+        *reinterpret_cast<f4*>(G + (size_t)row * D + 4 * d4) = g2;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+template <int SG, int VEC, bool MEAN>
+hipError_t launch_t(const Handle& h, const Plan& p, const uint32_t* keys, const uint32_t* perm,
+                    const float* grad_out, float lr, float eps, char* ws, hipStream_t s) {
+  constexpr int MPL = SG >= 32 ? 1 : 32 / SG;
+  constexpr int UF = VEC > 1 ? 2 : (SG < 4 ? SG : 4);
+  constexpr int SGPB = 256 / SG;
+  static_assert(SG * MPL >= 32, "chunk");
+  const uint32_t n = (uint32_t)p.nnz;
+  if (n == 0) return hipSuccess;
+  const int64_t chunks = (p.nnz + SG * MPL - 1) / (SG * MPL);
+  const int64_t grid = (chunks + SGPB - 1) / SGPB;
+  uint32_t* gr = reinterpret_cast<uint32_t*>(ws + p.gr);
+  float* scale = reinterpret_cast<float*>(ws + p.scale);
+  float* ph = reinterpret_cast<float*>(ws + p.part_head);
+  float* pt = reinterpret_cast<float*>(ws + p.part_tail);
+  uint32_t* spans = reinterpret_cast<uint32_t*>(ws + p.span_list);
+  uint32_t* misc = reinterpret_cast<uint32_t*>(ws + p.misc);
+  hipLaunchKernelGGL((k_seg_adagrad<SG, VEC, MEAN, MPL, UF>), dim3((unsigned)grid), dim3(256), 0,
+                     s, keys, perm, gr, scale, grad_out, h.W, h.G, n, (uint32_t)h.total_rows, h.D,
+                     lr, eps, ph, pt, spans, misc, (uint32_t)(p.B * h.T));
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  int64_t fgrid = chunks < 2048 ? chunks : 2048;
+  hipLaunchKernelGGL((k_seg_fixup<SG, VEC>), dim3((unsigned)fgrid), dim3(256), 0, s, keys, n,
+                     SG * MPL, h.W, h.G, h.D, lr, eps, ph, pt, spans, misc);
+  return hipGetLastError();
+}
+
+template <bool MEAN>
+hipError_t dispatch(const Handle& h, const Plan& p, const uint32_t* keys, const uint32_t* perm,
+                    const float* grad_out, float lr, float eps, char* ws, hipStream_t s) {
+  const int sg = subgroup_lanes(h.D), vec = vec_per_lane(h.D);
+  switch (sg) {
+    case 1: return launch_t<1, 1, MEAN>(h, p, keys, perm, grad_out, lr, eps, ws, s);
+    case 2: return launch_t<2, 1, MEAN>(h, p, keys, perm, grad_out, lr, eps, ws, s);
+    case 4: return launch_t<4, 1, MEAN>(h, p, keys, perm, grad_out, lr, eps, ws, s);
+    case 8: return launch_t<8, 1, MEAN>(h, p, keys, perm, grad_out, lr, eps, ws, s);
+    case 16: return launch_t<16, 1, MEAN>(h, p, keys, perm, grad_out, lr, eps, ws, s);
+    case 32: return launch_t<32, 1, MEAN>(h, p, keys, perm, grad_out, lr, eps, ws, s);
+    default:
+      switch (vec) {
+        case 1: return launch_t<64, 1, MEAN>(h, p, keys, perm, grad_out, lr, eps, ws, s);
+        case 2: return launch_t<64, 2, MEAN>(h, p, keys, perm, grad_out, lr, eps, ws, s);
+        case 3: return launch_t<64, 3, MEAN>(h, p, keys, perm, grad_out, lr, eps, ws, s);
+        default: return launch_t<64, 4, MEAN>(h, p, keys, perm, grad_out, lr, eps, ws, s);
+      }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_segment_adagrad(const Handle& h, const Plan& p, const uint32_t* keys,
+                                  const uint32_t* perm, bool mean, const float* grad_out,
+                                  float lr, float eps, char* ws, hipStream_t s) {
+  return mean ? dispatch<true>(h, p, keys, perm, grad_out, lr, eps, ws, s)
+              : dispatch<false>(h, p, keys, perm, grad_out, lr, eps, ws, s);
+}
+
+}  // namespace embtab

@@ -1,0 +1,445 @@
+// Occurrence keys, LSD radix sort and run-length unique for gfx950.
+//
+// Deduplicating the ids of a batch so that every touched row is read and
+// updated once follows the DeepRec page (section "model quality",
+// EmbeddingVariable item 2: one table access per row per pass) and the EcoRec
+// page (section "research method": merging work on identical indices, and
+// reordering by index).  The sort is stable, so equal rows keep ascending
+// occurrence order and the permutation is unique.
+//
+// Kernels, in launch order:
+//   k_keys          one thread per bag: key = off_t + id (out-of-range ids get
+//                   the sentinel key total_rows, which sorts last), value = j,
+//                   grad row s*T + t and, for mean pooling, 1/L of the bag.
+//   k_sort_hist     per 4096-key tile, digit counts -> tile_hist[digit][tile].
+//   k_sort_scan     one block per digit: exclusive scan over tiles, digit totals.
+//   k_sort_scatter  per tile: stable rank of every key (per-wave ballot match
+//                   of the digit, waves own contiguous quarters of the tile),
+//                   staging of the tile in LDS in digit order, then writes in
+//                   which consecutive lanes store consecutive addresses.
+//   (hist / scan / scatter once per digit; digits of at most 9 bits cover
+//    ceil(log2(total_rows + 1)) key bits, so three passes sort 2^27 rows.)
+//   k_unique_count  per tile: run heads and valid keys.
+//   k_unique_scan   one block: tile bases, num_unique, num_valid, seg_off[U].
+//   k_unique_write  unique[u], seg_off[u], inverse[perm[k]].
+//   k_unique_counts counts[u] = seg_off[u+1] - seg_off[u].
+#include "embtab_internal.hpp"
+
+namespace embtab {
+
+namespace {
+
+// Exclusive scan of one value per thread over a 256-thread block.
+__device__ inline uint32_t block_excl_scan(uint32_t v, uint32_t* total, uint32_t* lds4) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  uint32_t x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    uint32_t y = (uint32_t)__shfl_up((int)x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) lds4[w] = x;
+  __syncthreads();
+  uint32_t before = 0, all = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t s = lds4[i];
+    before += (i < w) ? s : 0u;
+    all += s;
+  }
+  __syncthreads();
+  if (total) *total = all;
+  return x - v + before;
+}
+
+__global__ __launch_bounds__(256) void k_keys(const int64_t* __restrict__ offsets,
+                                              const int64_t* __restrict__ ids,
+                                              const int64_t* __restrict__ row_off,
+                                              const int64_t* __restrict__ rows,
+                                              uint32_t* __restrict__ keys,
+                                              uint32_t* __restrict__ vals,
+                                              uint32_t* __restrict__ gr, float* __restrict__ scale,
+                                              uint32_t* __restrict__ flags,
+                                              uint32_t* __restrict__ misc, int64_t B, int32_t T,
+                                              int64_t nnz, uint32_t sentinel, int32_t mean) {
+  if (blockIdx.x == 0 && threadIdx.x < 64) misc[threadIdx.x] = 0u;
+  const int64_t nbags = B * (int64_t)T;
+  const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= nbags) return;
+  const int64_t t = b / B, s = b - t * B;
+  int64_t o0 = offsets[b], o1 = offsets[b + 1];
+  uint32_t bad = 0;
+  if ((b == 0 && o0 != 0) || (b == nbags - 1 && o1 != nnz) || o1 < o0 || o0 < 0 || o1 > nnz)
+    bad |= EMB_FLAG_BAD_OFFSETS;
+  o0 = o0 < 0 ? 0 : (o0 > nnz ? nnz : o0);
+  o1 = o1 < o0 ? o0 : (o1 > nnz ? nnz : o1);
+  const uint32_t roff = (uint32_t)row_off[t];
+  const int64_t nr = rows[t];
+  const uint32_t g = (uint32_t)(s * T + t);
+  const float c = (o1 > o0) ? 1.0f / (float)(o1 - o0) : 1.0f;
+  for (int64_t j = o0; j < o1; ++j) {
+    const int64_t id = ids[j];
+    uint32_t key = sentinel;
+    if (id >= 0 && id < nr) key = roff + (uint32_t)id;
+    else bad |= EMB_FLAG_OUT_OF_RANGE;
+    keys[j] = key;
+    vals[j] = (uint32_t)j;
+    gr[j] = g;
+    if (mean) scale[j] = c;
+  }
+  if (bad) atomicOr(flags, bad);
+}
+
+// Per-wave stable digit ranking of 64 keys: returns the lanes of this wave that
+// share the digit (mask) for valid lanes.
+__device__ inline uint64_t match_digit(uint32_t d, bool valid, int nbits) {
+  uint64_t m = __ballot(valid);
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = (d >> b) & 1u;
+    const uint64_t bb = __ballot(bit);
+    m &= bit ? bb : ~bb;
+  }
+  return m;
+}
+
+__global__ __launch_bounds__(256) void k_sort_hist(const uint32_t* __restrict__ keys, uint32_t n,
+                                                   int shift, int nbits,
+                                                   uint32_t* __restrict__ tile_hist,
+                                                   uint32_t ntiles) {
+  __shared__ uint32_t whist[4][kMaxRadix];
+  const int radix = 1 << nbits;
+  const uint32_t mask = (uint32_t)radix - 1u;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  for (int i = threadIdx.x; i < 4 * kMaxRadix; i += 256) (&whist[0][0])[i] = 0u;
+  const uint32_t tile = blockIdx.x;
+  const uint32_t base = tile * (uint32_t)kSortTile + (uint32_t)w * (kSortItems * 64);
+  uint32_t kv[kSortItems];
+#pragma unroll
+  for (int r = 0; r < kSortItems; ++r) {
+    const uint32_t idx = base + r * 64 + lane;
+    kv[r] = idx < n ? keys[idx] : 0u;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < kSortItems; ++r) {
+    const uint32_t idx = base + r * 64 + lane;
+    const bool valid = idx < n;
+    const uint32_t d = (kv[r] >> shift) & mask;
+    const uint64_t m = match_digit(d, valid, nbits);
+    if (valid && lanes_below(m) == 0u) whist[w][d] += (uint32_t)__popcll(m);
+  }
+  __syncthreads();
+  for (int d = threadIdx.x; d < radix; d += 256)
+    tile_hist[(size_t)d * ntiles + tile] = whist[0][d] + whist[1][d] + whist[2][d] + whist[3][d];
+}
+
+__global__ __launch_bounds__(256) void k_sort_scan(uint32_t* __restrict__ tile_hist,
+                                                   uint32_t ntiles,
+                                                   uint32_t* __restrict__ digit_tot) {
+  __shared__ uint32_t lds4[4];
+  uint32_t* row = tile_hist + (size_t)blockIdx.x * ntiles;
+  uint32_t carry = 0;
+  for (uint32_t base = 0; base < ntiles; base += 256 * 4) {
+    uint32_t v[4];
+    uint32_t sum = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t idx = base + threadIdx.x * 4 + i;
+      v[i] = idx < ntiles ? row[idx] : 0u;
+      sum += v[i];
+    }
+    uint32_t total;
+    uint32_t ex = block_excl_scan(sum, &total, lds4) + carry;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t idx = base + threadIdx.x * 4 + i;
+      if (idx < ntiles) row[idx] = ex;
+      ex += v[i];
+    }
+    carry += total;
+  }
+  if (threadIdx.x == 0) digit_tot[blockIdx.x] = carry;
+}
+
+__global__ __launch_bounds__(256) void k_sort_scatter(
+    const uint32_t* __restrict__ keys_in, const uint32_t* __restrict__ vals_in,
+    uint32_t* __restrict__ keys_out, uint32_t* __restrict__ vals_out, uint32_t n, int shift,
+    int nbits, const uint32_t* __restrict__ tile_off, const uint32_t* __restrict__ digit_tot,
+    uint32_t ntiles) {
+  __shared__ uint32_t whist[4][kMaxRadix];
+  __shared__ uint32_t dstart[kMaxRadix];
+  __shared__ uint32_t gbase[kMaxRadix];
+  __shared__ uint32_t skeys[kSortTile];
+  __shared__ uint32_t svals[kSortTile];
+  __shared__ uint32_t lds4[4];
+  const int radix = 1 << nbits;
+  const uint32_t mask = (uint32_t)radix - 1u;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const uint32_t tile = blockIdx.x;
+  for (int i = threadIdx.x; i < 4 * kMaxRadix; i += 256) (&whist[0][0])[i] = 0u;
+  const uint32_t base = tile * (uint32_t)kSortTile + (uint32_t)w * (kSortItems * 64);
+  uint32_t kv[kSortItems], vv[kSortItems], lr[kSortItems];
+#pragma unroll
+  for (int r = 0; r < kSortItems; ++r) {
+    const uint32_t idx = base + r * 64 + lane;
+    kv[r] = 0u;
+    vv[r] = 0u;
+    if (idx < n) {
+      kv[r] = keys_in[idx];
+      vv[r] = vals_in[idx];
+    }
+  }
+  __syncthreads();
+  // Stable rank inside the wave's quarter: rounds go in position order.
+#pragma unroll
+  for (int r = 0; r < kSortItems; ++r) {
+    const uint32_t idx = base + r * 64 + lane;
+    const bool valid = idx < n;
+    const uint32_t d = (kv[r] >> shift) & mask;
+    const uint64_t m = match_digit(d, valid, nbits);
+    const uint32_t below = lanes_below(m);
+    uint32_t old = 0u;
+    if (valid) old = whist[w][d];
+    if (valid && below == 0u) whist[w][d] = old + (uint32_t)__popcll(m);
+    lr[r] = old + below;
+  }
+  __syncthreads();
+  // Per digit: exclusive prefix over waves; tile count into dstart.
+  for (int d = threadIdx.x; d < radix; d += 256) {
+    const uint32_t c0 = whist[0][d], c1 = whist[1][d], c2 = whist[2][d], c3 = whist[3][d];
+    whist[0][d] = 0u;
+    whist[1][d] = c0;
+    whist[2][d] = c0 + c1;
+    whist[3][d] = c0 + c1 + c2;
+    dstart[d] = c0 + c1 + c2 + c3;
+  }
+  __syncthreads();
+  {
+    // Tile-local digit starts and global digit bases (radix <= 512: two per thread).
+    const int d0 = 2 * threadIdx.x, d1 = d0 + 1;
+    const uint32_t a0 = d0 < radix ? dstart[d0] : 0u, a1 = d1 < radix ? dstart[d1] : 0u;
+    const uint32_t t0 = d0 < radix ? digit_tot[d0] : 0u, t1 = d1 < radix ? digit_tot[d1] : 0u;
+    const uint32_t ea = block_excl_scan(a0 + a1, nullptr, lds4);
+    const uint32_t et = block_excl_scan(t0 + t1, nullptr, lds4);
+    if (d0 < radix) {
+      dstart[d0] = ea;
+      gbase[d0] = et + tile_off[(size_t)d0 * ntiles + tile];
+    }
+    if (d1 < radix) {
+      dstart[d1] = ea + a0;
+      gbase[d1] = et + t0 + tile_off[(size_t)d1 * ntiles + tile];
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < kSortItems; ++r) {
+    const uint32_t idx = base + r * 64 + lane;
+    if (idx < n) {
+      const uint32_t d = (kv[r] >> shift) & mask;
+      const uint32_t pos = dstart[d] + whist[w][d] + lr[r];
+      skeys[pos] = kv[r];
+      svals[pos] = vv[r];
+    }
+  }
+  __syncthreads();
+  const uint32_t tbase = tile * (uint32_t)kSortTile;
+  const uint32_t tn = (n - tbase) < (uint32_t)kSortTile ? (n - tbase) : (uint32_t)kSortTile;
+  for (uint32_t i = threadIdx.x; i < tn; i += 256) {
+    const uint32_t k = skeys[i];
+    const uint32_t d = (k >> shift) & mask;
+    const uint32_t g = gbase[d] + (i - dstart[d]);
+    keys_out[g] = k;
+    vals_out[g] = svals[i];
+  }
+}
+
+__global__ __launch_bounds__(256) void k_unique_count(const uint32_t* __restrict__ keys, uint32_t n,
+                                                      uint32_t sentinel,
+                                                      uint32_t* __restrict__ ucnt,
+                                                      uint32_t* __restrict__ vcnt) {
+  __shared__ uint32_t lds4[4];
+  const uint32_t tbase = blockIdx.x * (uint32_t)kSortTile;
+  uint32_t heads = 0, valid = 0;
+  for (int r = 0; r < kSortItems; ++r) {
+    const uint32_t k = tbase + r * 256 + threadIdx.x;
+    if (k < n) {
+      const uint32_t key = keys[k];
+      if (key < sentinel) {
+        ++valid;
+        if (k == 0 || keys[k - 1] != key) ++heads;
+      }
+    }
+  }
+  uint32_t th, tv;
+  block_excl_scan(heads, &th, lds4);
+  block_excl_scan(valid, &tv, lds4);
+  if (threadIdx.x == 0) {
+    ucnt[blockIdx.x] = th;
+    vcnt[blockIdx.x] = tv;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_unique_scan(uint32_t* __restrict__ ucnt,
+                                                     const uint32_t* __restrict__ vcnt,
+                                                     uint32_t ntiles, uint32_t* __restrict__ misc,
+                                                     uint32_t* __restrict__ seg_off) {
+  __shared__ uint32_t lds4[4];
+  uint32_t carry = 0, vsum = 0;
+  for (uint32_t base = 0; base < ntiles; base += 256) {
+    const uint32_t idx = base + threadIdx.x;
+    const uint32_t v = idx < ntiles ? ucnt[idx] : 0u;
+    const uint32_t vv = idx < ntiles ? vcnt[idx] : 0u;
+    uint32_t total, tv;
+    const uint32_t ex = block_excl_scan(v, &total, lds4);
+    block_excl_scan(vv, &tv, lds4);
+    if (idx < ntiles) ucnt[idx] = ex + carry;
+    carry += total;
+    vsum += tv;
+  }
+  if (threadIdx.x == 0) {
+    misc[kMiscNumUnique] = carry;
+    misc[kMiscNumValid] = vsum;
+    seg_off[carry] = vsum;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_unique_write(const uint32_t* __restrict__ keys,
+                                                      const uint32_t* __restrict__ vals,
+                                                      uint32_t n, uint32_t sentinel,
+                                                      const uint32_t* __restrict__ ubase,
+                                                      uint32_t* __restrict__ unique,
+                                                      uint32_t* __restrict__ seg_off,
+                                                      uint32_t* __restrict__ inverse) {
+  __shared__ uint32_t sk[kSortTile + 1];
+  __shared__ uint32_t lds4[4];
+  const uint32_t tbase = blockIdx.x * (uint32_t)kSortTile;
+  const uint32_t tn = (n - tbase) < (uint32_t)kSortTile ? (n - tbase) : (uint32_t)kSortTile;
+  for (uint32_t i = threadIdx.x; i < tn; i += 256) sk[i + 1] = keys[tbase + i];
+  if (threadIdx.x == 0) sk[0] = tbase > 0 ? keys[tbase - 1] : kNoRow;
+  __syncthreads();
+  // Thread i owns positions i*16 .. i*16+15 of the tile.
+  const uint32_t p0 = threadIdx.x * kSortItems;
+  uint32_t heads = 0;
+#pragma unroll
+  for (int r = 0; r < kSortItems; ++r) {
+    const uint32_t p = p0 + r;
+    if (p < tn) {
+      const uint32_t key = sk[p + 1];
+      heads += (key < sentinel && (tbase + p == 0 || sk[p] != key)) ? 1u : 0u;
+    }
+  }
+  uint32_t u = ubase[blockIdx.x] + block_excl_scan(heads, nullptr, lds4);
+  // u is now the unique index of the first head among this thread's positions.
+#pragma unroll
+  for (int r = 0; r < kSortItems; ++r) {
+    const uint32_t p = p0 + r;
+    if (p < tn) {
+      const uint32_t key = sk[p + 1];
+      const uint32_t j = vals[tbase + p];
+      if (key < sentinel) {
+        if (tbase + p == 0 || sk[p] != key) {
+          unique[u] = key;
+          seg_off[u] = tbase + p;
+          ++u;
+        }
+        if (j < n) inverse[j] = u - 1u;
+      } else if (j < n) {
+        inverse[j] = kNoRow;
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void k_unique_counts(const uint32_t* __restrict__ seg_off,
+                                                       const uint32_t* __restrict__ misc,
+                                                       uint32_t* __restrict__ counts, uint32_t n) {
+  const uint32_t U = misc[kMiscNumUnique];
+  for (uint32_t u = blockIdx.x * 256 + threadIdx.x; u < U && u < n; u += gridDim.x * 256)
+    counts[u] = seg_off[u + 1] - seg_off[u];
+}
+
+__global__ __launch_bounds__(256) void k_copy_sorted(const uint32_t* __restrict__ keys,
+                                                     uint32_t sentinel, uint32_t* __restrict__ out,
+                                                     int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const uint32_t k = keys[i];
+    out[i] = k >= sentinel ? kNoRow : k;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_sort_unique(const Handle& h, const Plan& p, const int64_t* offsets,
+                              const int64_t* ids, bool mean, char* ws, uint32_t** sorted_keys,
+                              uint32_t** sorted_vals, hipStream_t s) {
+  const uint32_t n = (uint32_t)p.nnz;
+  const uint32_t sentinel = (uint32_t)h.total_rows;
+  uint32_t* misc = reinterpret_cast<uint32_t*>(ws + p.misc);
+  uint32_t* kA = reinterpret_cast<uint32_t*>(ws + p.keysA);
+  uint32_t* vA = reinterpret_cast<uint32_t*>(ws + p.valsA);
+  uint32_t* kB = reinterpret_cast<uint32_t*>(ws + p.keysB);
+  uint32_t* vB = reinterpret_cast<uint32_t*>(ws + p.valsB);
+  uint32_t* gr = reinterpret_cast<uint32_t*>(ws + p.gr);
+  float* scale = reinterpret_cast<float*>(ws + p.scale);
+  uint32_t* tile_hist = reinterpret_cast<uint32_t*>(ws + p.tile_hist);
+  uint32_t* digit_tot = reinterpret_cast<uint32_t*>(ws + p.digit_tot);
+  uint32_t* unique = reinterpret_cast<uint32_t*>(ws + p.unique);
+  uint32_t* seg_off = reinterpret_cast<uint32_t*>(ws + p.seg_off);
+  uint32_t* counts = reinterpret_cast<uint32_t*>(ws + p.counts);
+  uint32_t* inverse = reinterpret_cast<uint32_t*>(ws + p.inverse);
+  uint32_t* ucnt = reinterpret_cast<uint32_t*>(ws + p.ucnt);
+  uint32_t* vcnt = reinterpret_cast<uint32_t*>(ws + p.vcnt);
+
+  const int64_t nbags = p.B * (int64_t)h.T;
+  const unsigned kgrid = (unsigned)((nbags + 255) / 256);
+  hipLaunchKernelGGL(k_keys, dim3(kgrid > 0 ? kgrid : 1), dim3(256), 0, s, offsets, ids,
+                     h.sv.row_off, h.sv.rows, kA, vA, gr, scale, h.sv.flags, misc, p.B, h.T,
+                     p.nnz, sentinel, mean ? 1 : 0);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const uint32_t ntiles = (uint32_t)p.ntiles;
+  uint32_t* kin = kA;
+  uint32_t* vin = vA;
+  uint32_t* kout = kB;
+  uint32_t* vout = vB;
+  if (n > 0) {
+    for (int pass = 0; pass < p.passes; ++pass) {
+      const int radix = 1 << p.dbits[pass];
+      hipLaunchKernelGGL(k_sort_hist, dim3(ntiles), dim3(256), 0, s, kin, n, p.shift[pass],
+                         p.dbits[pass], tile_hist, ntiles);
+      hipLaunchKernelGGL(k_sort_scan, dim3(radix), dim3(256), 0, s, tile_hist, ntiles, digit_tot);
+      hipLaunchKernelGGL(k_sort_scatter, dim3(ntiles), dim3(256), 0, s, kin, vin, kout, vout, n,
+                         p.shift[pass], p.dbits[pass], tile_hist, digit_tot, ntiles);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      uint32_t* tk = kin;
+      kin = kout;
+      kout = tk;
+      uint32_t* tv = vin;
+      vin = vout;
+      vout = tv;
+    }
+    hipLaunchKernelGGL(k_unique_count, dim3(ntiles), dim3(256), 0, s, kin, n, sentinel, ucnt, vcnt);
+  }
+  hipLaunchKernelGGL(k_unique_scan, dim3(1), dim3(256), 0, s, ucnt, vcnt, ntiles, misc, seg_off);
+  if (n > 0) {
+    hipLaunchKernelGGL(k_unique_write, dim3(ntiles), dim3(256), 0, s, kin, vin, n, sentinel, ucnt,
+                       unique, seg_off, inverse);
+    const unsigned cgrid = (unsigned)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096);
+    hipLaunchKernelGGL(k_unique_counts, dim3(cgrid), dim3(256), 0, s, seg_off, misc, counts, n);
+  }
+  *sorted_keys = kin;
+  *sorted_vals = vin;
+  return hipGetLastError();
+}
+
+hipError_t launch_debug_copy_sorted(const uint32_t* keys, uint32_t sentinel, uint32_t* out,
+                                    int64_t n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  const int64_t g = (n + 255) / 256;
+  hipLaunchKernelGGL(k_copy_sorted, dim3((unsigned)(g < 4096 ? g : 4096)), dim3(256), 0, s, keys,
+                     sentinel, out, n);
+  return hipGetLastError();
+}
+
+}  // namespace embtab

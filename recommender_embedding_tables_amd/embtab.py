@@ -1,0 +1,271 @@
+"""ctypes binding of libembtab.so, the gfx950 sparse embedding library.
+
+Argument marshalling only: every function here has the name of a C entry point
+of include/embtab.h and forwards device pointers (torch tensors) and sizes to
+it.  All computation runs in the library's HIP kernels; importing this module
+fails when the library has not been built.
+
+Status codes are returned as ints (EMB_OK = 0); `check(status)` raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libembtab.so")
+
+EMB_OK = 0
+EMB_ERR_INVALID_ARG = 1
+EMB_ERR_UNSUPPORTED = 2
+EMB_ERR_WORKSPACE = 3
+EMB_ERR_OUT_OF_RANGE = 4
+EMB_ERR_BAD_OFFSETS = 5
+EMB_ERR_RESERVED_KEY = 6
+EMB_ERR_TABLE_FULL = 7
+EMB_ERR_HIP = 8
+
+EMB_FLAG_OUT_OF_RANGE = 1
+EMB_FLAG_BAD_OFFSETS = 2
+EMB_FLAG_RESERVED_KEY = 4
+EMB_FLAG_TABLE_FULL = 8
+
+EMB_POOL_SUM = 0
+EMB_POOL_MEAN = 1
+
+EMB_EMPTY_KEY = 0xFFFFFFFFFFFFFFFF
+
+EXPORTED = [
+    "emb_state_bytes", "emb_hash_bytes", "emb_workspace_bytes", "emb_table_create",
+    "emb_table_destroy", "emb_hash_find_or_insert", "emb_bag_forward",
+    "emb_bag_backward_adagrad", "emb_status_sync", "emb_hash_n_live", "emb_hash_export",
+    "emb_debug_sort_unique", "emb_status_string",
+]
+
+
+class emb_table_desc_t(C.Structure):
+    _fields_ = [
+        ("num_tables", C.c_int32),
+        ("dim", C.c_int32),
+        ("rows_per_table", C.c_void_p),
+        ("weights", C.c_void_p),
+        ("accum", C.c_void_p),
+        ("state", C.c_void_p),
+        ("hashed", C.c_int32),
+        ("hash_capacity", C.c_int64),
+        ("max_load", C.c_float),
+        ("hash_slots", C.c_void_p),
+        ("seed", C.c_uint64),
+        ("init_lo", C.c_float),
+        ("init_hi", C.c_float),
+        ("init_std", C.c_float),
+        ("accum_init", C.c_float),
+        ("init_storage", C.c_int32),
+    ]
+
+
+class EmbError(RuntimeError):
+    def __init__(self, status: int, what: str = ""):
+        self.status = status
+        super().__init__(f"{what}: {emb_status_string(status)} (status {status})")
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python recommender_embedding_tables_amd/build.py`")
+    lib = C.CDLL(LIB_PATH)
+    P, i32, i64, u32, f32, sz = C.c_void_p, C.c_int32, C.c_int64, C.c_uint32, C.c_float, C.c_size_t
+    sig = {
+        "emb_state_bytes": (sz, [i32]),
+        "emb_hash_bytes": (sz, [i32, i64]),
+        "emb_workspace_bytes": (sz, [P, i64, i64]),
+        "emb_table_create": (i32, [C.POINTER(emb_table_desc_t), P, C.POINTER(P)]),
+        "emb_table_destroy": (i32, [P]),
+        "emb_hash_find_or_insert": (i32, [P, P, P, i64, i64, P, P, sz, P]),
+        "emb_bag_forward": (i32, [P, P, P, i64, i64, i32, P, P, sz, P]),
+        "emb_bag_backward_adagrad": (i32, [P, P, P, i64, i64, i32, P, f32, f32, P, sz, P]),
+        "emb_status_sync": (i32, [P, P, C.POINTER(u32)]),
+        "emb_hash_n_live": (i32, [P, P, P]),
+        "emb_hash_export": (i32, [P, i32, P, P]),
+        "emb_debug_sort_unique": (i32, [P, P, P, i64, i64, P, P, P, P, P, P, P, P, sz, P]),
+        "emb_status_string": (C.c_char_p, [i32]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    return lib
+
+
+_lib = _load()
+
+
+def lib():
+    return _lib
+
+
+def _ptr(x):
+    """Device (or host) address of a torch tensor, an int address, or None."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def check(status: int, what: str = "embtab") -> None:
+    if status != EMB_OK:
+        raise EmbError(status, what)
+
+
+def emb_status_string(status: int) -> str:
+    return _lib.emb_status_string(status).decode()
+
+
+def emb_state_bytes(num_tables: int) -> int:
+    return int(_lib.emb_state_bytes(num_tables))
+
+
+def emb_hash_bytes(num_tables: int, capacity: int) -> int:
+    return int(_lib.emb_hash_bytes(num_tables, capacity))
+
+
+def emb_workspace_bytes(handle, batch: int, nnz: int) -> int:
+    return int(_lib.emb_workspace_bytes(handle, batch, nnz))
+
+
+def emb_table_create(desc: emb_table_desc_t, stream=None):
+    """Returns (status, handle)."""
+    h = C.c_void_p()
+    st = _lib.emb_table_create(C.byref(desc), _stream(stream), C.byref(h))
+    return st, h.value
+
+
+def emb_table_destroy(handle) -> int:
+    return _lib.emb_table_destroy(handle)
+
+
+def emb_hash_find_or_insert(handle, offsets, keys, batch, nnz, ids_out, ws, ws_bytes,
+                            stream=None) -> int:
+    return _lib.emb_hash_find_or_insert(handle, _ptr(offsets), _ptr(keys), batch, nnz,
+                                        _ptr(ids_out), _ptr(ws), ws_bytes, _stream(stream))
+
+
+def emb_bag_forward(handle, offsets, ids, batch, nnz, pool, out, ws=None, ws_bytes=0,
+                    stream=None) -> int:
+    return _lib.emb_bag_forward(handle, _ptr(offsets), _ptr(ids), batch, nnz, pool, _ptr(out),
+                                _ptr(ws), ws_bytes, _stream(stream))
+
+
+def emb_bag_backward_adagrad(handle, offsets, ids, batch, nnz, pool, grad_out, lr, eps, ws,
+                             ws_bytes, stream=None) -> int:
+    return _lib.emb_bag_backward_adagrad(handle, _ptr(offsets), _ptr(ids), batch, nnz, pool,
+                                         _ptr(grad_out), lr, eps, _ptr(ws), ws_bytes,
+                                         _stream(stream))
+
+
+def emb_status_sync(handle, stream=None):
+    """Returns (status, flag bits)."""
+    f = C.c_uint32(0)
+    st = _lib.emb_status_sync(handle, _stream(stream), C.byref(f))
+    return st, int(f.value)
+
+
+def emb_hash_n_live(handle, num_tables, stream=None):
+    arr = (C.c_int64 * num_tables)()
+    st = _lib.emb_hash_n_live(handle, _stream(stream), C.cast(arr, C.c_void_p))
+    return st, [int(v) for v in arr]
+
+
+def emb_hash_export(handle, table, key_of_row, stream=None) -> int:
+    return _lib.emb_hash_export(handle, table, _ptr(key_of_row), _stream(stream))
+
+
+def emb_debug_sort_unique(handle, offsets, ids, batch, nnz, sorted_rows, perm, unique, counts,
+                          seg_off, inverse, num_unique, ws, ws_bytes, stream=None) -> int:
+    return _lib.emb_debug_sort_unique(handle, _ptr(offsets), _ptr(ids), batch, nnz,
+                                      _ptr(sorted_rows), _ptr(perm), _ptr(unique), _ptr(counts),
+                                      _ptr(seg_off), _ptr(inverse), _ptr(num_unique), _ptr(ws),
+                                      ws_bytes, _stream(stream))
+
+
+class EmbTables:
+    """Owns the device storage of one table set (weights, accumulators, state,
+    hash slots) as torch tensors and the library handle over it.
+
+    Storage allocation is torch's; every computation is a library call.
+    """
+
+    def __init__(self, rows_per_table, dim, *, hashed=False, hash_capacity=0, max_load=0.625,
+                 seed=0, init_lo=-0.05, init_hi=0.05, init_std=0.01, accum_init=0.1,
+                 device="cuda", stream=None, storage=None):
+        import torch
+        self.rows = [int(r) for r in rows_per_table]
+        self.T = len(self.rows)
+        self.D = int(dim)
+        self.total_rows = sum(self.rows)
+        self.hashed = bool(hashed)
+        self.hash_capacity = int(hash_capacity)
+        dev = torch.device(device)
+        if storage is None:
+            self.weights = torch.empty((self.total_rows, self.D), dtype=torch.float32, device=dev)
+            self.accum = torch.empty_like(self.weights)
+            self.state = torch.zeros(emb_state_bytes(self.T), dtype=torch.uint8, device=dev)
+            hb = emb_hash_bytes(self.T, self.hash_capacity) if hashed else 0
+            self.slots = torch.empty(max(hb, 16), dtype=torch.uint8, device=dev) if hashed else None
+            init = 1
+        else:
+            self.weights, self.accum, self.state, self.slots = storage
+            init = 0
+        self._rows_c = (C.c_int64 * self.T)(*self.rows)
+        d = emb_table_desc_t()
+        d.num_tables = self.T
+        d.dim = self.D
+        d.rows_per_table = C.cast(self._rows_c, C.c_void_p)
+        d.weights = self.weights.data_ptr()
+        d.accum = self.accum.data_ptr()
+        d.state = self.state.data_ptr()
+        d.hashed = 1 if hashed else 0
+        d.hash_capacity = self.hash_capacity
+        d.max_load = max_load
+        d.hash_slots = self.slots.data_ptr() if hashed else None
+        d.seed = seed
+        d.init_lo = init_lo
+        d.init_hi = init_hi
+        d.init_std = init_std
+        d.accum_init = accum_init
+        d.init_storage = init
+        st, self.handle = emb_table_create(d, stream)
+        check(st, "emb_table_create")
+        self._ws = None
+
+    def close(self):
+        if getattr(self, "handle", None):
+            emb_table_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def workspace(self, batch, nnz):
+        """A torch uint8 workspace large enough for (batch, nnz), reused when possible."""
+        import torch
+        need = emb_workspace_bytes(self.handle, batch, nnz)
+        if need == 0:
+            raise EmbError(EMB_ERR_INVALID_ARG, "emb_workspace_bytes")
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = torch.empty(need + 256, dtype=torch.uint8, device=self.weights.device)
+        return self._ws, need

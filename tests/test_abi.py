@@ -1,0 +1,126 @@
+"""The C ABI without a GPU: the library loads, exports every declared entry
+point, and rejects bad arguments on the host before any launch."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "embtab.h")
+
+eb = pytest.importorskip("recommender_embedding_tables_amd.embtab",
+                         reason="libembtab.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(emb_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) >= 12
+    lib = C.CDLL(eb.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(eb.EXPORTED) == names
+
+
+def test_size_queries():
+    assert eb.emb_state_bytes(0) == 0
+    assert eb.emb_state_bytes(1) >= 256 + 8 * 4
+    assert eb.emb_state_bytes(26) % 256 == 0
+    assert eb.emb_hash_bytes(4, 1 << 25) == 4 * (1 << 25) * 16
+    assert eb.emb_hash_bytes(4, 1000) == 0  # not a power of two
+    assert eb.emb_hash_bytes(0, 1024) == 0
+    assert eb.emb_workspace_bytes(None, 10, 10) == 0
+
+
+def _desc(**kw):
+    rows = kw.pop("rows", [100, 200])
+    arr = (C.c_int64 * len(rows))(*rows)
+    d = eb.emb_table_desc_t()
+    d.num_tables = len(rows)
+    d.dim = kw.pop("dim", 16)
+    d.rows_per_table = C.cast(arr, C.c_void_p)
+    # fake, aligned device addresses: with init_storage = 0 nothing is touched
+    d.weights = kw.pop("weights", 0x10000000)
+    d.accum = kw.pop("accum", 0x20000000)
+    d.state = kw.pop("state", 0x30000000)
+    d.hashed = kw.pop("hashed", 0)
+    d.hash_capacity = kw.pop("hash_capacity", 0)
+    d.max_load = kw.pop("max_load", 0.625)
+    d.hash_slots = kw.pop("hash_slots", None)
+    d.init_storage = 0
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d, arr
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dim=3), eb.EMB_ERR_INVALID_ARG),
+    (dict(dim=0), eb.EMB_ERR_INVALID_ARG),
+    (dict(dim=2048), eb.EMB_ERR_INVALID_ARG),
+    (dict(rows=[0]), eb.EMB_ERR_INVALID_ARG),
+    (dict(weights=None), eb.EMB_ERR_INVALID_ARG),
+    (dict(weights=0x10000004), eb.EMB_ERR_INVALID_ARG),  # misaligned
+    (dict(state=0x30000010), eb.EMB_ERR_INVALID_ARG),    # state needs 256-byte alignment
+    (dict(rows=[2**31, 2**31]), eb.EMB_ERR_UNSUPPORTED),  # rows are 32-bit inside
+    (dict(hashed=1, hash_capacity=1000, hash_slots=0x40000000), eb.EMB_ERR_INVALID_ARG),
+    (dict(hashed=1, hash_capacity=1024, hash_slots=None), eb.EMB_ERR_INVALID_ARG),
+    (dict(hashed=1, rows=[700], hash_capacity=1024, hash_slots=0x40000000),
+     eb.EMB_ERR_INVALID_ARG),  # 700 rows > 0.625 * 1024
+])
+def test_create_rejects(kw, code):
+    d, _keep = _desc(**kw)
+    st, h = eb.emb_table_create(d, 0)
+    assert st == code and h is None
+
+
+def test_host_checks_on_attached_handle():
+    d, _keep = _desc(rows=[1000, 24], dim=64)
+    st, h = eb.emb_table_create(d, 0)
+    assert st == eb.EMB_OK and h
+    try:
+        ws = eb.emb_workspace_bytes(h, 4096, 10000)
+        assert ws > 0 and ws % 256 == 0
+        assert eb.emb_workspace_bytes(h, 4096, 20000) > ws
+        assert eb.emb_workspace_bytes(h, -1, 10) == 0
+        fake = 0x50000000
+        # workspace too small / missing / misaligned
+        assert eb.emb_bag_backward_adagrad(h, fake, fake, 4096, 10000, 0, fake, 0.01, 1e-8,
+                                           fake, ws - 1, 0) == eb.EMB_ERR_WORKSPACE
+        assert eb.emb_bag_backward_adagrad(h, fake, fake, 4096, 10000, 0, fake, 0.01, 1e-8,
+                                           None, ws, 0) == eb.EMB_ERR_WORKSPACE
+        assert eb.emb_bag_backward_adagrad(h, fake, fake, 4096, 10000, 0, fake, 0.01, 1e-8,
+                                           fake + 16, ws, 0) == eb.EMB_ERR_WORKSPACE
+        # bad pool, null pointers, bad lr / eps
+        assert eb.emb_bag_forward(h, fake, fake, 4096, 10000, 7, fake, stream=0) == eb.EMB_ERR_INVALID_ARG
+        assert eb.emb_bag_forward(h, fake, fake, 4096, 10000, 0, None, stream=0) == eb.EMB_ERR_INVALID_ARG
+        assert eb.emb_bag_forward(h, None, fake, 4096, 10000, 0, fake, stream=0) == eb.EMB_ERR_INVALID_ARG
+        assert eb.emb_bag_forward(h, fake, None, 4096, 10000, 0, fake, stream=0) == eb.EMB_ERR_INVALID_ARG
+        assert eb.emb_bag_forward(h, fake, fake, -1, 10000, 0, fake, stream=0) == eb.EMB_ERR_INVALID_ARG
+        assert eb.emb_bag_forward(h, fake, fake, 4096, 10000, 0, fake + 4, stream=0) == eb.EMB_ERR_INVALID_ARG
+        assert eb.emb_bag_backward_adagrad(h, fake, fake, 4096, 10000, 0, fake, float("nan"),
+                                           1e-8, fake, ws, 0) == eb.EMB_ERR_INVALID_ARG
+        assert eb.emb_bag_backward_adagrad(h, fake, fake, 4096, 10000, 0, fake, 0.01, -1.0,
+                                           fake, ws, 0) == eb.EMB_ERR_INVALID_ARG
+        # hash calls on a dense handle
+        assert eb.emb_hash_find_or_insert(h, fake, fake, 4096, 10000, fake, fake, ws,
+                                          0) == eb.EMB_ERR_UNSUPPORTED
+        assert eb.emb_hash_export(h, 0, fake, 0) == eb.EMB_ERR_UNSUPPORTED
+        assert eb.emb_hash_export(h, 5, fake, 0) == eb.EMB_ERR_INVALID_ARG
+        # sizes beyond the 32-bit internal indices
+        assert eb.emb_bag_forward(h, fake, fake, 4096, 2**33, 0, fake, stream=0) == eb.EMB_ERR_UNSUPPORTED
+        # an empty batch is a no-op
+        assert eb.emb_bag_forward(h, fake, fake, 0, 0, 0, fake, stream=0) == eb.EMB_OK
+    finally:
+        eb.emb_table_destroy(h)
+
+
+def test_status_strings():
+    assert eb.emb_status_string(eb.EMB_ERR_TABLE_FULL) == "table full"
+    assert eb.emb_status_string(eb.EMB_OK) == "ok"
+    assert eb.emb_status_string(99) == "unknown status"
