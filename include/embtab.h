@@ -190,6 +190,31 @@ emb_status_t emb_debug_sort_unique(emb_table_t h, const int64_t* offsets, const 
                                    uint32_t* seg_off, uint32_t* inverse, uint32_t* num_unique,
                                    void* ws, size_t ws_bytes, void* stream);
 
+/* Measurement hook.  Phases of the calls, in launch order:
+ *   EMB_PHASE_FORWARD  the pooled-gather kernel of emb_bag_forward;
+ *   EMB_PHASE_KEYS     occurrence keys of emb_bag_backward_adagrad;
+ *   EMB_PHASE_SORT     all radix passes;
+ *   EMB_PHASE_UNIQUE   unique / inverse / counts;
+ *   EMB_PHASE_REDUCE   the fused segmented-reduction + Adagrad kernel;
+ *   EMB_PHASE_FIXUP    the kernel finishing rows that span reduction chunks;
+ *   EMB_PHASE_HASH     all of emb_hash_find_or_insert.
+ * When `events` is not NULL, later calls on h record events[2p] (if not NULL)
+ * just before phase p and events[2p+1] (if not NULL) just after it, with
+ * hipEventRecord on the call's stream.  The array (2 * EMB_NUM_PHASES
+ * hipEvent_t handles) is copied; the events stay the caller's.  NULL turns
+ * recording off. */
+typedef enum {
+  EMB_PHASE_FORWARD = 0,
+  EMB_PHASE_KEYS = 1,
+  EMB_PHASE_SORT = 2,
+  EMB_PHASE_UNIQUE = 3,
+  EMB_PHASE_REDUCE = 4,
+  EMB_PHASE_FIXUP = 5,
+  EMB_PHASE_HASH = 6,
+  EMB_NUM_PHASES = 7
+} emb_phase_t;
+emb_status_t emb_set_phase_events(emb_table_t h, void* const* events);
+
 /* Human-readable name of a status code (static string). */
 const char* emb_status_string(emb_status_t s);
 

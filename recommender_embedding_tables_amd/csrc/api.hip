@@ -329,6 +329,14 @@ emb_status_t emb_hash_n_live(emb_table_t t, void* stream, int64_t* n_live_out) {
   return hip_status(e);
 }
 
+emb_status_t emb_set_phase_events(emb_table_t t, void* const* events) {
+  if (!t) return EMB_ERR_INVALID_ARG;
+  t->h.timing = events != nullptr;
+  for (int i = 0; i < 2 * EMB_NUM_PHASES; ++i)
+    t->h.events[i] = events ? static_cast<hipEvent_t>(events[i]) : nullptr;
+  return EMB_OK;
+}
+
 emb_status_t emb_hash_export(emb_table_t t, int32_t table, uint64_t* key_of_row, void* stream) {
   if (!t || !key_of_row || table < 0 || table >= t->h.T) return EMB_ERR_INVALID_ARG;
   if (!t->h.hashed) return EMB_ERR_UNSUPPORTED;

@@ -65,7 +65,16 @@ struct Handle {
   void* slots = nullptr;
   uint64_t seed = 0;
   float lo = 0, hi = 0, stdv = 0, accum0 = 0;
+  bool timing = false;
+  hipEvent_t events[2 * EMB_NUM_PHASES] = {};
 };
+
+// Measurement hook: events recorded around a phase when the caller set them.
+inline void phase_mark(const Handle& h, int phase, bool end, hipStream_t s) {
+  if (!h.timing) return;
+  hipEvent_t e = h.events[2 * phase + (end ? 1 : 0)];
+  if (e) (void)hipEventRecord(e, s);
+}
 
 // Lanes that share one embedding row (a power of two <= 64) and float4s per lane.
 inline int subgroup_lanes(int D) {

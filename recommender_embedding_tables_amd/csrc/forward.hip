@@ -164,8 +164,11 @@ hipError_t dispatch(const Handle& h, const int64_t* offsets, const int64_t* ids,
 
 hipError_t launch_forward(const Handle& h, const int64_t* offsets, const int64_t* ids,
                           int64_t B, int64_t nnz, bool mean, float* out, hipStream_t s) {
-  return mean ? dispatch<true>(h, offsets, ids, B, nnz, out, s)
-              : dispatch<false>(h, offsets, ids, B, nnz, out, s);
+  phase_mark(h, EMB_PHASE_FORWARD, false, s);
+  hipError_t e = mean ? dispatch<true>(h, offsets, ids, B, nnz, out, s)
+                      : dispatch<false>(h, offsets, ids, B, nnz, out, s);
+  phase_mark(h, EMB_PHASE_FORWARD, true, s);
+  return e;
 }
 
 }  // namespace embtab

@@ -318,6 +318,7 @@ hipError_t launch_hash_find_or_insert(const Handle& h, const Plan& p, const int6
   const size_t shm = sizeof(int64_t) * (size_t)(h.T + 1);
   const unsigned nb = (unsigned)((nnz + 255) / 256);
   const unsigned grid = nb > 0 ? nb : 1;
+  phase_mark(h, EMB_PHASE_HASH, false, s);
   hipLaunchKernelGGL(k_zero_words, dim3(1), dim3(256), 0, s, misc, kMiscHashNew + 2 * h.T);
   hipLaunchKernelGGL(k_hash_probe, dim3(grid), dim3(256), shm, s, offsets, keys, p.B, h.T, nnz,
                      slots, h.capacity, ids_out, slot_of, h.sv.flags, misc);
@@ -336,6 +337,7 @@ hipError_t launch_hash_find_or_insert(const Handle& h, const Plan& p, const int6
                      h.capacity, slot_of, ids_out, misc);
   hipLaunchKernelGGL(k_hash_live, dim3(1), dim3(h.T < 64 ? 64 : ((h.T + 63) / 64) * 64), 0, s,
                      h.T, h.sv.n_live, misc);
+  phase_mark(h, EMB_PHASE_HASH, true, s);
   return hipGetLastError();
 }
 

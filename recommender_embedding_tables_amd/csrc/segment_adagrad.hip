@@ -287,14 +287,18 @@ hipError_t launch_t(const Handle& h, const Plan& p, const uint32_t* keys, const 
   float* pt = reinterpret_cast<float*>(ws + p.part_tail);
   uint32_t* spans = reinterpret_cast<uint32_t*>(ws + p.span_list);
   uint32_t* misc = reinterpret_cast<uint32_t*>(ws + p.misc);
+  phase_mark(h, EMB_PHASE_REDUCE, false, s);
   hipLaunchKernelGGL((k_seg_adagrad<SG, VEC, MEAN, MPL, UF>), dim3((unsigned)grid), dim3(256), 0,
                      s, keys, perm, gr, scale, grad_out, h.W, h.G, n, (uint32_t)h.total_rows, h.D,
                      lr, eps, ph, pt, spans, misc, (uint32_t)(p.B * h.T));
+  phase_mark(h, EMB_PHASE_REDUCE, true, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   int64_t fgrid = chunks < 2048 ? chunks : 2048;
+  phase_mark(h, EMB_PHASE_FIXUP, false, s);
   hipLaunchKernelGGL((k_seg_fixup<SG, VEC>), dim3((unsigned)fgrid), dim3(256), 0, s, keys, n,
                      SG * MPL, h.W, h.G, h.D, lr, eps, ph, pt, spans, misc);
+  phase_mark(h, EMB_PHASE_FIXUP, true, s);
   return hipGetLastError();
 }
 

@@ -392,9 +392,11 @@ hipError_t launch_sort_unique(const Handle& h, const Plan& p, const int64_t* off
 
   const int64_t nbags = p.B * (int64_t)h.T;
   const unsigned kgrid = (unsigned)((nbags + 255) / 256);
+  phase_mark(h, EMB_PHASE_KEYS, false, s);
   hipLaunchKernelGGL(k_keys, dim3(kgrid > 0 ? kgrid : 1), dim3(256), 0, s, offsets, ids,
                      h.sv.row_off, h.sv.rows, kA, vA, gr, scale, h.sv.flags, misc, p.B, h.T,
                      p.nnz, sentinel, mean ? 1 : 0);
+  phase_mark(h, EMB_PHASE_KEYS, true, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const uint32_t ntiles = (uint32_t)p.ntiles;
@@ -402,6 +404,7 @@ hipError_t launch_sort_unique(const Handle& h, const Plan& p, const int64_t* off
   uint32_t* vin = vA;
   uint32_t* kout = kB;
   uint32_t* vout = vB;
+  phase_mark(h, EMB_PHASE_SORT, false, s);
   if (n > 0) {
     for (int pass = 0; pass < p.passes; ++pass) {
       const int radix = 1 << p.dbits[pass];
@@ -419,6 +422,10 @@ hipError_t launch_sort_unique(const Handle& h, const Plan& p, const int64_t* off
       vin = vout;
       vout = tv;
     }
+  }
+  phase_mark(h, EMB_PHASE_SORT, true, s);
+  phase_mark(h, EMB_PHASE_UNIQUE, false, s);
+  if (n > 0) {
     hipLaunchKernelGGL(k_unique_count, dim3(ntiles), dim3(256), 0, s, kin, n, sentinel, ucnt, vcnt);
   }
   hipLaunchKernelGGL(k_unique_scan, dim3(1), dim3(256), 0, s, ucnt, vcnt, ntiles, misc, seg_off);
@@ -428,6 +435,7 @@ hipError_t launch_sort_unique(const Handle& h, const Plan& p, const int64_t* off
     const unsigned cgrid = (unsigned)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096);
     hipLaunchKernelGGL(k_unique_counts, dim3(cgrid), dim3(256), 0, s, seg_off, misc, counts, n);
   }
+  phase_mark(h, EMB_PHASE_UNIQUE, true, s);
   *sorted_keys = kin;
   *sorted_vals = vin;
   return hipGetLastError();

@@ -39,8 +39,12 @@ EXPORTED = [
     "emb_state_bytes", "emb_hash_bytes", "emb_workspace_bytes", "emb_table_create",
     "emb_table_destroy", "emb_hash_find_or_insert", "emb_bag_forward",
     "emb_bag_backward_adagrad", "emb_status_sync", "emb_hash_n_live", "emb_hash_export",
-    "emb_debug_sort_unique", "emb_status_string",
+    "emb_debug_sort_unique", "emb_status_string", "emb_set_phase_events",
 ]
+
+EMB_PHASE_FORWARD, EMB_PHASE_KEYS, EMB_PHASE_SORT, EMB_PHASE_UNIQUE = 0, 1, 2, 3
+EMB_PHASE_REDUCE, EMB_PHASE_FIXUP, EMB_PHASE_HASH, EMB_NUM_PHASES = 4, 5, 6, 7
+PHASE_NAMES = ["forward", "keys", "sort", "unique", "reduce_adagrad", "fixup", "hash"]
 
 
 class emb_table_desc_t(C.Structure):
@@ -71,6 +75,10 @@ class EmbError(RuntimeError):
 
 
 def _load():
+    # torch first: its bundled HIP runtime then satisfies libembtab.so's
+    # libamdhip64 dependency, so streams and events from torch and the
+    # library's launches live in one runtime instance.
+    import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
                           "`python recommender_embedding_tables_amd/build.py`")
@@ -90,6 +98,7 @@ def _load():
         "emb_hash_export": (i32, [P, i32, P, P]),
         "emb_debug_sort_unique": (i32, [P, P, P, i64, i64, P, P, P, P, P, P, P, P, sz, P]),
         "emb_status_string": (C.c_char_p, [i32]),
+        "emb_set_phase_events": (i32, [P, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -189,6 +198,14 @@ def emb_hash_n_live(handle, num_tables, stream=None):
 
 def emb_hash_export(handle, table, key_of_row, stream=None) -> int:
     return _lib.emb_hash_export(handle, table, _ptr(key_of_row), _stream(stream))
+
+
+def emb_set_phase_events(handle, events) -> int:
+    """events: None, or 2 * EMB_NUM_PHASES raw hipEvent_t addresses (0 = skip)."""
+    if events is None:
+        return _lib.emb_set_phase_events(handle, None)
+    arr = (C.c_void_p * (2 * EMB_NUM_PHASES))(*[e or None for e in events])
+    return _lib.emb_set_phase_events(handle, C.cast(arr, C.c_void_p))
 
 
 def emb_debug_sort_unique(handle, offsets, ids, batch, nnz, sorted_rows, perm, unique, counts,
