@@ -163,6 +163,27 @@ emb_status_t emb_bag_backward_adagrad(emb_table_t h, const int64_t* offsets,
                                       emb_pool_t pool, const float* grad_out, float lr,
                                       float eps, void* ws, size_t ws_bytes, void* stream);
 
+/* The same backward split in two, so that the id-only stages can overlap the
+ * forward gather (they need offsets and ids but not grad_out):
+ *   emb_bag_prepare                    occurrence keys, stable sort, unique /
+ *                                      inverse / counts, left in `ws`;
+ *   emb_bag_backward_adagrad_prepared  segmented reduction + Adagrad from a
+ *                                      workspace prepared for the same batch,
+ *                                      nnz and pool (same semantics as
+ *                                      emb_bag_backward_adagrad).
+ * Typical use: prepare on a second stream right after the ids are known, run
+ * emb_bag_forward on the main stream, make the main stream wait for the second
+ * one, then call the prepared backward.  Calling the prepared backward on a
+ * workspace that was not prepared for this batch updates unspecified rows (no
+ * memory outside W, G and ws is touched). */
+emb_status_t emb_bag_prepare(emb_table_t h, const int64_t* offsets, const int64_t* ids,
+                             int64_t batch, int64_t nnz, emb_pool_t pool, void* ws,
+                             size_t ws_bytes, void* stream);
+emb_status_t emb_bag_backward_adagrad_prepared(emb_table_t h, int64_t batch, int64_t nnz,
+                                               emb_pool_t pool, const float* grad_out, float lr,
+                                               float eps, void* ws, size_t ws_bytes,
+                                               void* stream);
+
 /* Waits for `stream`, returns the highest-priority device error (TABLE_FULL,
  * RESERVED_KEY, BAD_OFFSETS, OUT_OF_RANGE, in that order) or EMB_OK, stores
  * the raw EMB_FLAG_* bits in *flags_out (HOST, may be NULL) and clears them. */

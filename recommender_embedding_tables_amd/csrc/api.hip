@@ -74,6 +74,7 @@ bool make_plan(const Handle& h, int64_t B, int64_t nnz, Plan* p) {
   p->part_head = take(sizeof(float) * nc * (size_t)h.D);
   p->part_tail = take(sizeof(float) * nc * (size_t)h.D);
   p->span_list = take(sizeof(uint32_t) * nc);
+  p->long_list = take(sizeof(uint32_t) * nc);
   if (h.hashed) {
     p->h_slot = take(n4);
     p->h_first = take(n4);
@@ -249,6 +250,52 @@ emb_status_t emb_bag_backward_adagrad(emb_table_t t, const int64_t* offsets, con
   if (e == hipSuccess)
     e = launch_segment_adagrad(t->h, p, keys, perm, mean, grad_out, lr, eps, w, s);
   return hip_status(e);
+}
+
+static void sorted_arrays(const Plan& p, char* w, uint32_t** keys, uint32_t** vals) {
+  // launch_sort_unique ping-pongs A -> B -> A ... once per radix pass
+  const bool in_b = p.nnz > 0 && (p.passes % 2) == 1;
+  *keys = reinterpret_cast<uint32_t*>(w + (in_b ? p.keysB : p.keysA));
+  *vals = reinterpret_cast<uint32_t*>(w + (in_b ? p.valsB : p.valsA));
+}
+
+emb_status_t emb_bag_prepare(emb_table_t t, const int64_t* offsets, const int64_t* ids,
+                             int64_t batch, int64_t nnz, emb_pool_t pool, void* ws,
+                             size_t ws_bytes, void* stream) {
+  if (!t || (nnz > 0 && !ids)) return EMB_ERR_INVALID_ARG;
+  if (pool != EMB_POOL_SUM && pool != EMB_POOL_MEAN) return EMB_ERR_INVALID_ARG;
+  emb_status_t st = check_batch(t->h, offsets, batch, nnz);
+  if (st != EMB_OK) return st;
+  Plan p;
+  if (!make_plan(t->h, batch, nnz, &p)) return EMB_ERR_UNSUPPORTED;
+  if (!ws || ws_bytes < p.total || (reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
+    return EMB_ERR_WORKSPACE;
+  if (batch == 0) return EMB_OK;
+  uint32_t *keys = nullptr, *vals = nullptr;
+  return hip_status(launch_sort_unique(t->h, p, offsets, ids, pool == EMB_POOL_MEAN,
+                                       static_cast<char*>(ws), &keys, &vals,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+emb_status_t emb_bag_backward_adagrad_prepared(emb_table_t t, int64_t batch, int64_t nnz,
+                                               emb_pool_t pool, const float* grad_out, float lr,
+                                               float eps, void* ws, size_t ws_bytes,
+                                               void* stream) {
+  if (!t || !grad_out) return EMB_ERR_INVALID_ARG;
+  if (pool != EMB_POOL_SUM && pool != EMB_POOL_MEAN) return EMB_ERR_INVALID_ARG;
+  if (!std::isfinite(lr) || !std::isfinite(eps) || eps < 0.0f) return EMB_ERR_INVALID_ARG;
+  if (batch < 0 || nnz < 0) return EMB_ERR_INVALID_ARG;
+  if (!aligned16(grad_out)) return EMB_ERR_INVALID_ARG;
+  Plan p;
+  if (!make_plan(t->h, batch, nnz, &p)) return EMB_ERR_UNSUPPORTED;
+  if (!ws || ws_bytes < p.total || (reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
+    return EMB_ERR_WORKSPACE;
+  if (batch == 0) return EMB_OK;
+  uint32_t *keys = nullptr, *vals = nullptr;
+  char* w = static_cast<char*>(ws);
+  sorted_arrays(p, w, &keys, &vals);
+  return hip_status(launch_segment_adagrad(t->h, p, keys, vals, pool == EMB_POOL_MEAN, grad_out,
+                                           lr, eps, w, static_cast<hipStream_t>(stream)));
 }
 
 emb_status_t emb_debug_sort_unique(emb_table_t t, const int64_t* offsets, const int64_t* ids,

@@ -18,6 +18,7 @@ constexpr uint64_t kEmptyKey = 0xFFFFFFFFFFFFFFFFull;
 constexpr uint64_t kUnsetRow = 0xFFFFFFFFFFFFFFFFull;  // row word of an empty slot
 constexpr uint64_t kPendingBit = 1ull << 62;           // row word = kPendingBit | first j
 constexpr uint32_t kNoRow = 0xFFFFFFFFu;
+constexpr int kMaxTables = 1024;
 
 // Sort and unique tiles: 256 threads x 16 keys.
 constexpr int kSortThreads = 256;
@@ -108,7 +109,7 @@ struct Plan {
   size_t unique, seg_off, counts, inverse;
   size_t ucnt, vcnt;
   size_t misc;  // uint32[64]
-  size_t part_head, part_tail, span_list;
+  size_t part_head, part_tail, span_list, long_list;
   size_t h_slot, h_first, h_tcnt;  // hash find-or-insert
   size_t total = 0;
 };
@@ -119,6 +120,7 @@ enum : int {
   kMiscNumValid = 1,
   kMiscSpanCount = 2,
   kMiscHashOverflow = 3,
+  kMiscLongCount = 4,
   kMiscHashNew = 8,  // uint32 per table from here (up to T)
 };
 
@@ -128,6 +130,15 @@ bool make_plan(const Handle& h, int64_t B, int64_t nnz, Plan* p);
 __device__ inline uint32_t lanes_below(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
                                    __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// Block index remapped so that each of the 8 XCDs (which take hardware blocks
+// round-robin) works on one contiguous range of logical blocks, keeping the
+// cache lines a range shares inside one XCD's L2.
+__device__ inline uint32_t xcd_block() {
+  const uint32_t nb = gridDim.x, b = blockIdx.x;
+  const uint32_t q = nb >> 3, r = nb & 7u, x = b & 7u;
+  return x * q + (x < r ? x : r) + (b >> 3);
 }
 
 // One SplitMix64 step from `state` (Steele, Lea and Flood 2014).

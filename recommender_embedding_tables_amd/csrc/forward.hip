@@ -6,15 +6,18 @@
 // interview", section three, technique (5)).
 //
 // Layout and schedule: a sub-group of SG lanes (SG = D/4 rounded up to a power
-// of two, at most 64) owns one bag; each lane holds VEC float4 columns, so a
-// row is read with dwordx4 loads that cover it contiguously.  A sub-group keeps
-// UNR bags in flight at once.  Bags are visited in output order (sample-major,
-// q = s*T + t), so consecutive sub-groups write consecutive 16-byte columns of
-// `out` and each store instruction of a wave covers one contiguous span.  The
-// ids of a bag are fetched SG at a time with one coalesced load and broadcast
-// by lane shuffles, so a multi-hot bag costs one id round trip per SG ids.
-// Rows are gathered through the cache hierarchy (hot Zipf rows stay in L2 /
-// MALL); `out` is written with non-temporal stores since it is streamed once.
+// of two, at most 64) reads a row with one dwordx4 load per lane (VEC float4
+// columns per lane when D > 256).  It owns SG consecutive bags in CSR
+// (table-major) order, one per lane for metadata: their offsets come in with
+// one coalesced load, and when every bag of the wave holds at most one id
+// (one-hot features) their ids with a second one, so a bag costs no dependent
+// metadata round trip of its own.  The sub-group then walks its bags UNR at a
+// time, broadcasting each bag's row by lane shuffle, with UNR row loads in
+// flight per lane.  Multi-hot bags fetch their ids SG at a time with one
+// coalesced load and broadcast them the same way.  Rows go through the cache
+// hierarchy (hot Zipf rows stay in L2 / MALL); `out` is written once with
+// non-temporal stores.  Blocks are remapped so that each XCD covers one
+// contiguous range of bags.
 #include "embtab_internal.hpp"
 
 namespace embtab {
@@ -26,98 +29,145 @@ __global__ __launch_bounds__(256) void k_bag_forward(
     const int64_t* __restrict__ offsets, const int64_t* __restrict__ ids,
     const float* __restrict__ W, const int64_t* __restrict__ row_off,
     const int64_t* __restrict__ rows, float* __restrict__ out, uint32_t* __restrict__ flags,
-    int64_t B, int32_t T, int32_t D, int64_t nnz) {
+    uint32_t B, uint32_t T, uint32_t D, uint32_t nnz) {
   constexpr int SGPB = 256 / SG;
-  const int lane = threadIdx.x % SG;
-  const int sgb = threadIdx.x / SG;
-  const int64_t nbags = B * (int64_t)T;
-  const int64_t qbase = (int64_t)blockIdx.x * SGPB * UNR + sgb;
-  const int D4 = D >> 2;
+  const uint32_t lane = threadIdx.x % SG;
+  const uint32_t sgb = threadIdx.x / SG;
+  const uint32_t nbags = B * T;
+  const uint32_t b0 = (xcd_block() * SGPB + sgb) * (uint32_t)SG;  // first bag of the sub-group
+  const uint32_t D4 = D >> 2;
 
-  int64_t start[UNR];
-  int32_t len[UNR];
-  uint32_t roff[UNR];
-  int64_t nrows[UNR];
-  uint32_t bad = 0;
-  int32_t maxlen = 0;
-#pragma unroll
-  for (int u = 0; u < UNR; ++u) {
-    const int64_t q = qbase + (int64_t)u * SGPB;
-    start[u] = 0;
-    len[u] = 0;
-    roff[u] = 0;
-    nrows[u] = 0;
-    if (q < nbags) {
-      const int64_t t = q % T;
-      const int64_t s = q / T;
-      const int64_t b = t * B + s;
-      int64_t o0 = offsets[b], o1 = offsets[b + 1];
-      if ((b == 0 && o0 != 0) || (b == nbags - 1 && o1 != nnz) || o1 < o0 || o0 < 0 || o1 > nnz)
-        bad |= EMB_FLAG_BAD_OFFSETS;
-      o0 = o0 < 0 ? 0 : (o0 > nnz ? nnz : o0);
-      o1 = o1 < o0 ? o0 : (o1 > nnz ? nnz : o1);
-      start[u] = o0;
-      len[u] = (int32_t)(o1 - o0);
-      roff[u] = (uint32_t)row_off[t];
-      nrows[u] = rows[t];
-      maxlen = len[u] > maxlen ? len[u] : maxlen;
-    }
+  // Lane metadata: bag b0 + lane.
+  const uint32_t b = b0 + lane;
+  uint32_t start = 0u, len = 0u, t = 0u, s = 0u, bad = 0u;
+  uint32_t roff = 0u, nrow = 0u;
+  if (b < nbags) {
+    t = b / B;
+    s = b - t * B;
+    int64_t o0 = offsets[b], o1 = offsets[b + 1];
+    roff = (uint32_t)row_off[t];
+    nrow = (uint32_t)rows[t];
+    if ((b == 0 && o0 != 0) || (b == nbags - 1 && o1 != (int64_t)nnz) || o1 < o0 || o0 < 0 ||
+        o1 > (int64_t)nnz)
+      bad |= EMB_FLAG_BAD_OFFSETS;
+    o0 = o0 < 0 ? 0 : (o0 > (int64_t)nnz ? (int64_t)nnz : o0);
+    o1 = o1 < o0 ? o0 : (o1 > (int64_t)nnz ? (int64_t)nnz : o1);
+    start = (uint32_t)o0;
+    len = (uint32_t)(o1 - o0);
+  }
+  const bool onehot = __all(len <= 1u);
+  uint32_t myrow = kNoRow;
+  if (onehot && len == 1u) {
+    const int64_t id = ids[start];
+    if (id >= 0 && id < (int64_t)nrow) myrow = roff + (uint32_t)id;
+    else bad |= EMB_FLAG_OUT_OF_RANGE;
   }
 
-  f4 acc[UNR][VEC];
-#pragma unroll
-  for (int u = 0; u < UNR; ++u)
-#pragma unroll
-    for (int v = 0; v < VEC; ++v) acc[u][v] = f4{0.f, 0.f, 0.f, 0.f};
-
-  for (int32_t kb = 0; kb < maxlen; kb += SG) {
-    // One coalesced id load per bag per SG occurrences; invalid -> kNoRow.
-    uint32_t myrow[UNR];
-#pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-      myrow[u] = kNoRow;
-      if (kb + lane < len[u]) {
-        const int64_t id = ids[start[u] + kb + lane];
-        if (id >= 0 && id < nrows[u]) myrow[u] = roff[u] + (uint32_t)id;
-        else bad |= EMB_FLAG_OUT_OF_RANGE;
-      }
-    }
-    int32_t kend = maxlen - kb;
-    kend = kend > SG ? SG : kend;
-    for (int32_t kk = 0; kk < kend; ++kk) {
-      uint32_t grow[UNR];
-#pragma unroll
-      for (int u = 0; u < UNR; ++u) grow[u] = (uint32_t)__shfl((int)myrow[u], kk, SG);
-      f4 x[UNR][VEC];
+  if (onehot) {
+#pragma unroll 1
+    for (uint32_t i0 = 0; i0 < (uint32_t)SG; i0 += UNR) {
+      if (b0 + i0 >= nbags) break;
+      f4 acc[UNR][VEC];
 #pragma unroll
       for (int u = 0; u < UNR; ++u) {
+        const uint32_t grow = (uint32_t)__shfl((int)myrow, (int)(i0 + u), SG);
 #pragma unroll
         for (int v = 0; v < VEC; ++v) {
-          const int d4 = lane + v * SG;
-          x[u][v] = f4{0.f, 0.f, 0.f, 0.f};
-          if (grow[u] != kNoRow && d4 < D4)
-            x[u][v] = *reinterpret_cast<const f4*>(W + (size_t)grow[u] * D + 4 * d4);
+          const uint32_t d4 = lane + v * SG;
+          acc[u][v] = f4{0.f, 0.f, 0.f, 0.f};
+          if (grow != kNoRow && d4 < D4)
+            acc[u][v] = *reinterpret_cast<const f4*>(W + (size_t)grow * D + 4 * d4);
         }
       }
 #pragma unroll
-      for (int u = 0; u < UNR; ++u)
+      for (int u = 0; u < UNR; ++u) {
+        const uint32_t bt = (uint32_t)__shfl((int)t, (int)(i0 + u), SG);
+        const uint32_t bs = (uint32_t)__shfl((int)s, (int)(i0 + u), SG);
+        if (b0 + i0 + u >= nbags) continue;
+        const size_t o = ((size_t)bs * T + bt) * D;
 #pragma unroll
-        for (int v = 0; v < VEC; ++v) acc[u][v] += x[u][v];
+        for (int v = 0; v < VEC; ++v) {
+          const uint32_t d4 = lane + v * SG;
+          if (d4 < D4)
+            __builtin_nontemporal_store(acc[u][v], reinterpret_cast<f4*>(out + o + 4 * d4));
+        }
+      }
     }
-  }
-
+  } else {
+    // Multi-hot: MU bags at a time, their ids SG at a time, KU rows in flight per bag.
+    constexpr int MU = 2, KU = 4;
+#pragma unroll 1
+    for (uint32_t i0 = 0; i0 < (uint32_t)SG; i0 += MU) {
+      if (b0 + i0 >= nbags) break;
+      uint32_t bl[MU], bst[MU], broff[MU], bnr[MU];
+      uint32_t maxlen = 0u;
+      f4 acc[MU][VEC];
 #pragma unroll
-  for (int u = 0; u < UNR; ++u) {
-    const int64_t q = qbase + (int64_t)u * SGPB;
-    if (q >= nbags) continue;
-    float c = 1.0f;
-    if (MEAN && len[u] > 0) c = 1.0f / (float)len[u];
+      for (int u = 0; u < MU; ++u) {
+        bl[u] = (uint32_t)__shfl((int)len, (int)(i0 + u), SG);
+        bst[u] = (uint32_t)__shfl((int)start, (int)(i0 + u), SG);
+        broff[u] = (uint32_t)__shfl((int)roff, (int)(i0 + u), SG);
+        bnr[u] = (uint32_t)__shfl((int)nrow, (int)(i0 + u), SG);
+        maxlen = bl[u] > maxlen ? bl[u] : maxlen;
 #pragma unroll
-    for (int v = 0; v < VEC; ++v) {
-      const int d4 = lane + v * SG;
-      if (d4 < D4) {
-        f4 r = MEAN ? acc[u][v] * c : acc[u][v];
-        __builtin_nontemporal_store(r, reinterpret_cast<f4*>(out + (size_t)q * D + 4 * d4));
+        for (int v = 0; v < VEC; ++v) acc[u][v] = f4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll 1
+      for (uint32_t kb = 0; kb < maxlen; kb += SG) {
+        uint32_t r[MU];
+#pragma unroll
+        for (int u = 0; u < MU; ++u) {
+          r[u] = kNoRow;
+          if (kb + lane < bl[u]) {
+            const int64_t id = ids[bst[u] + kb + lane];
+            if (id >= 0 && id < (int64_t)bnr[u]) r[u] = broff[u] + (uint32_t)id;
+            else bad |= EMB_FLAG_OUT_OF_RANGE;
+          }
+        }
+        const uint32_t kend = (maxlen - kb) < (uint32_t)SG ? (maxlen - kb) : (uint32_t)SG;
+#pragma unroll 1
+        for (uint32_t kk = 0; kk < kend; kk += KU) {
+          f4 x[MU][KU][VEC];
+#pragma unroll
+          for (int u = 0; u < MU; ++u)
+#pragma unroll
+            for (int k = 0; k < KU; ++k) {
+              // lanes past kend hold kNoRow, so the tail of the last group loads nothing
+              const uint32_t src = kk + k < (uint32_t)SG ? kk + k : (uint32_t)SG - 1u;
+              uint32_t grow = (uint32_t)__shfl((int)r[u], (int)src, SG);
+              if (kk + k >= kend) grow = kNoRow;
+#pragma unroll
+              for (int v = 0; v < VEC; ++v) {
+                const uint32_t d4 = lane + v * SG;
+                x[u][k][v] = f4{0.f, 0.f, 0.f, 0.f};
+                if (grow != kNoRow && d4 < D4)
+                  x[u][k][v] = *reinterpret_cast<const f4*>(W + (size_t)grow * D + 4 * d4);
+              }
+            }
+#pragma unroll
+          for (int u = 0; u < MU; ++u)
+#pragma unroll
+            for (int k = 0; k < KU; ++k)
+#pragma unroll
+              for (int v = 0; v < VEC; ++v) acc[u][v] += x[u][k][v];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < MU; ++u) {
+        const uint32_t bt = (uint32_t)__shfl((int)t, (int)(i0 + u), SG);
+        const uint32_t bs = (uint32_t)__shfl((int)s, (int)(i0 + u), SG);
+        if (b0 + i0 + u >= nbags) continue;
+        float c = 1.0f;
+        if (MEAN && bl[u] > 0) c = 1.0f / (float)bl[u];
+        const size_t o = ((size_t)bs * T + bt) * D;
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) {
+          const uint32_t d4 = lane + v * SG;
+          if (d4 < D4) {
+            const f4 rr = MEAN ? acc[u][v] * c : acc[u][v];
+            __builtin_nontemporal_store(rr, reinterpret_cast<f4*>(out + o + 4 * d4));
+          }
+        }
       }
     }
   }
@@ -127,15 +177,15 @@ __global__ __launch_bounds__(256) void k_bag_forward(
 template <int SG, int VEC, bool MEAN>
 hipError_t launch_t(const Handle& h, const int64_t* offsets, const int64_t* ids, int64_t B,
                     int64_t nnz, float* out, hipStream_t s) {
-  constexpr int UNR = 4;
+  constexpr int UNR = VEC == 1 ? (SG >= 8 ? 8 : SG) : (VEC == 2 ? 4 : 2);  // one-hot rows in flight
   constexpr int SGPB = 256 / SG;
   const int64_t nbags = B * (int64_t)h.T;
-  const int64_t per_block = (int64_t)SGPB * UNR;
+  const int64_t per_block = (int64_t)SGPB * SG;
   const int64_t grid = (nbags + per_block - 1) / per_block;
   if (grid == 0) return hipSuccess;
   hipLaunchKernelGGL((k_bag_forward<SG, VEC, MEAN, UNR>), dim3((unsigned)grid), dim3(256), 0, s,
-                     offsets, ids, h.W, h.sv.row_off, h.sv.rows, out, h.sv.flags, B, h.T, h.D,
-                     nnz);
+                     offsets, ids, h.W, h.sv.row_off, h.sv.rows, out, h.sv.flags, (uint32_t)B,
+                     (uint32_t)h.T, (uint32_t)h.D, (uint32_t)nnz);
   return hipGetLastError();
 }
 

@@ -183,34 +183,90 @@ __global__ __launch_bounds__(256) void k_seg_adagrad(
   }
 }
 
-// Adds the parts of every segment that crosses chunk boundaries and applies
-// the Adagrad step.  One block per listed span; SGPB sub-groups each add every
-// SGPB-th head part in chunk order, then sub-group 0 adds
-// tail + part_sum[0] + ... + part_sum[SGPB-1] in that order.
+// Rows whose occurrences cross chunk boundaries ("spans") are finished in two
+// tiers.  k_fix_short: one sub-group per span; lane i tests whether the run
+// ends in chunk c0+1+i, so a span of up to SG chunks is found with one load
+// per lane, then its parts are added in chunk order (tail of c0, heads of
+// c0+1 .. c1) and the Adagrad step applied.  Longer spans (Zipf-hot rows) are
+// appended to a second list for k_fix_long.
 template <int SG, int VEC>
-__global__ __launch_bounds__(256) void k_seg_fixup(
+__global__ __launch_bounds__(256) void k_fix_short(
     const uint32_t* __restrict__ keys, uint32_t n, int32_t CH, float* __restrict__ W,
     float* __restrict__ G, int32_t D, float lr, float eps, const float* __restrict__ part_head,
     const float* __restrict__ part_tail, const uint32_t* __restrict__ span_list,
-    const uint32_t* __restrict__ misc) {
+    uint32_t* __restrict__ long_list, uint32_t* __restrict__ misc) {
   constexpr int SGPB = 256 / SG;
+  const int lane = threadIdx.x % SG;
+  const uint32_t gsg = blockIdx.x * SGPB + threadIdx.x / SG;
+  const uint32_t nsg = gridDim.x * SGPB;
+  const int D4 = D >> 2;
+  const uint32_t nspan = misc[kMiscSpanCount];
+  const int lane_base = (int)(threadIdx.x & 63u) - lane;  // first lane of this sub-group in the wave
+  for (uint32_t sp = gsg; sp < nspan; sp += nsg) {
+    const uint32_t c0 = span_list[sp];
+    const uint32_t row = keys[(c0 + 1) * (uint32_t)CH - 1u];  // chunk c0 is full
+    const uint32_t cc = c0 + 1 + lane;
+    const uint64_t nxt = (uint64_t)(cc + 1) * (uint32_t)CH;
+    bool ends = false;
+    if ((uint64_t)cc * (uint32_t)CH < n) ends = (nxt >= n) || keys[nxt] != row;
+    const uint64_t m = (__ballot(ends) >> lane_base) & (SG == 64 ? ~0ull : ((1ull << SG) - 1ull));
+    if (m == 0) {
+      if (lane == 0) long_list[atomicAdd(&misc[kMiscLongCount], 1u)] = c0;
+      continue;
+    }
+    const uint32_t c1 = c0 + 1 + (uint32_t)(__ffsll((unsigned long long)m) - 1);
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) {
+      const int d4 = lane + v * SG;
+      if (d4 >= D4) continue;
+      f4 tot = *reinterpret_cast<const f4*>(part_tail + (size_t)c0 * D + 4 * d4);
+      uint32_t c = c0 + 1;
+      for (; c + 3 <= c1; c += 4) {
+        const f4 x0 = *reinterpret_cast<const f4*>(part_head + (size_t)c * D + 4 * d4);
+        const f4 x1 = *reinterpret_cast<const f4*>(part_head + (size_t)(c + 1) * D + 4 * d4);
+        const f4 x2 = *reinterpret_cast<const f4*>(part_head + (size_t)(c + 2) * D + 4 * d4);
+        const f4 x3 = *reinterpret_cast<const f4*>(part_head + (size_t)(c + 3) * D + 4 * d4);
+        tot += x0;
+        tot += x1;
+        tot += x2;
+        tot += x3;
+      }
+      for (; c <= c1; ++c) tot += *reinterpret_cast<const f4*>(part_head + (size_t)c * D + 4 * d4);
+      f4 w = *reinterpret_cast<const f4*>(W + (size_t)row * D + 4 * d4);
+      f4 g2 = *reinterpret_cast<const f4*>(G + (size_t)row * D + 4 * d4);
+      adagrad_step(w, g2, tot, lr, eps);
+      *reinterpret_cast<f4*>(W + (size_t)row * D + 4 * d4) = w;
+      *reinterpret_cast<f4*>(G + (size_t)row * D + 4 * d4) = g2;
+    }
+  }
+}
+
+// Long spans: one block of NT threads per span.  NT/SG sub-groups each add
+// every (NT/SG)-th head part in chunk order, then sub-group 0 adds
+// tail + part_sum[0] + ... + part_sum[NT/SG - 1] in that order.
+template <int SG, int VEC, int NT>
+__global__ __launch_bounds__(NT) void k_fix_long(
+    const uint32_t* __restrict__ keys, uint32_t n, int32_t CH, float* __restrict__ W,
+    float* __restrict__ G, int32_t D, float lr, float eps, const float* __restrict__ part_head,
+    const float* __restrict__ part_tail, const uint32_t* __restrict__ long_list,
+    const uint32_t* __restrict__ misc) {
+  constexpr int SGPB = NT / SG;
   __shared__ f4 red[SGPB][SG * VEC];
   __shared__ uint32_t s_end;
   const int lane = threadIdx.x % SG;
   const int sgb = threadIdx.x / SG;
   const int D4 = D >> 2;
-  const uint32_t nspan = misc[kMiscSpanCount];
+  const uint32_t nspan = misc[kMiscLongCount];
   for (uint32_t sp = blockIdx.x; sp < nspan; sp += gridDim.x) {
-    const uint32_t c0 = span_list[sp];
-    const uint32_t pos_last = (c0 + 1) * (uint32_t)CH - 1u;  // chunk c0 is full
-    const uint32_t row = keys[pos_last];
-    // Find the chunk where the run ends: first chunk c > c0 whose successor
-    // position no longer holds `row`.  256 chunks are tested per round.
+    const uint32_t c0 = long_list[sp];
+    const uint32_t row = keys[(c0 + 1) * (uint32_t)CH - 1u];
+    // The chunk where the run ends: the first chunk c > c0 whose successor
+    // position no longer holds `row`.  NT chunks are tested per round.
     if (threadIdx.x == 0) s_end = 0xFFFFFFFFu;
     __syncthreads();
-    for (uint32_t cb = c0 + 1;; cb += 256) {
+    for (uint32_t cb = c0 + 1;; cb += NT) {
       const uint32_t cc = cb + threadIdx.x;
-      const uint64_t nxt = (uint64_t)(cc + 1) * (uint32_t)CH;  // first position after chunk cc
+      const uint64_t nxt = (uint64_t)(cc + 1) * (uint32_t)CH;
       bool ends = false;
       if ((uint64_t)cc * (uint32_t)CH < n) ends = (nxt >= n) || keys[nxt] != row;
       if (ends) atomicMin(&s_end, cc);
@@ -218,7 +274,7 @@ __global__ __launch_bounds__(256) void k_seg_fixup(
       const uint32_t e = s_end;
       __syncthreads();
       if (e != 0xFFFFFFFFu) break;
-      if ((uint64_t)(cb + 256) * (uint32_t)CH >= n) break;  // cannot happen for a listed span
+      if ((uint64_t)(cb + NT) * (uint32_t)CH >= n) break;  // cannot happen for a listed span
     }
     const uint32_t c1 = s_end;
     f4 acc[VEC];
@@ -294,10 +350,16 @@ hipError_t launch_t(const Handle& h, const Plan& p, const uint32_t* keys, const 
   phase_mark(h, EMB_PHASE_REDUCE, true, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  int64_t fgrid = chunks < 2048 ? chunks : 2048;
+  constexpr int FNT = VEC == 1 ? 1024 : (VEC == 2 ? 512 : 256);
+  uint32_t* longs = reinterpret_cast<uint32_t*>(ws + p.long_list);
+  int64_t sgrid = (chunks + SGPB - 1) / SGPB;
+  sgrid = sgrid < 2048 ? sgrid : 2048;
+  const int64_t lgrid = chunks < 512 ? chunks : 512;
   phase_mark(h, EMB_PHASE_FIXUP, false, s);
-  hipLaunchKernelGGL((k_seg_fixup<SG, VEC>), dim3((unsigned)fgrid), dim3(256), 0, s, keys, n,
-                     SG * MPL, h.W, h.G, h.D, lr, eps, ph, pt, spans, misc);
+  hipLaunchKernelGGL((k_fix_short<SG, VEC>), dim3((unsigned)sgrid), dim3(256), 0, s, keys, n,
+                     SG * MPL, h.W, h.G, h.D, lr, eps, ph, pt, spans, longs, misc);
+  hipLaunchKernelGGL((k_fix_long<SG, VEC, FNT>), dim3((unsigned)lgrid), dim3(FNT), 0, s, keys, n,
+                     SG * MPL, h.W, h.G, h.D, lr, eps, ph, pt, longs, misc);
   phase_mark(h, EMB_PHASE_FIXUP, true, s);
   return hipGetLastError();
 }

@@ -409,3 +409,37 @@ def test_hash_then_train_step():
         o.backward_adagrad(offsets, ids, w.B, False, grad, w.lr, w.eps)
         check_rows(tabs, o, offsets, ids, w.B, False, grad, w.lr, w.eps)
     check_hash_state(tabs, o, trained_lr=2 * w.lr)
+
+
+def test_prepared_backward_on_side_stream_matches_oracle():
+    # keys/sort/unique on a second stream beside the forward, then the prepared backward
+    w = synth.workload(3, T=3, B=5000)
+    w.rows = np.array([300, 40_000, 7])
+    tabs, o = make_pair(w.rows, w.D, seed=12)
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    ev_a, ev_b = torch.cuda.Event(), torch.cuda.Event()
+    for step in range(2):
+        offsets, ids = synth.gen_batch(w, step)
+        grad = synth.gen_grad(w, step)
+        d_off, d_ids, d_grad = _t(offsets), _t(ids), _t(grad)
+        out = torch.empty((w.B, w.T, w.D), dtype=torch.float32, device=DEV)
+        ws, need = tabs.workspace(w.B, ids.size)
+        ev_a.record(main)
+        side.wait_event(ev_a)
+        eb.check(eb.emb_bag_prepare(tabs.handle, d_off, d_ids, w.B, ids.size, eb.EMB_POOL_MEAN, ws,
+                                    need, side), "prepare")
+        ev_b.record(side)
+        eb.check(eb.emb_bag_forward(tabs.handle, d_off, d_ids, w.B, ids.size, eb.EMB_POOL_MEAN,
+                                    out, stream=main), "forward")
+        main.wait_event(ev_b)
+        eb.check(eb.emb_bag_backward_adagrad_prepared(tabs.handle, w.B, ids.size, eb.EMB_POOL_MEAN,
+                                                      d_grad, w.lr, w.eps, ws, need, main),
+                 "prepared backward")
+        torch.cuda.synchronize()
+        ref, _ = o.forward(offsets, ids, w.B, True)
+        S = forward_S(offsets, ids, w.B, o.rows, lambda r: o.read_rows(r)[0], True, w.D)
+        assert_within(out.cpu().numpy(), ref, S, "forward (side-stream step)")
+        o.backward_adagrad(offsets, ids, w.B, True, grad, w.lr, w.eps)
+        check_rows(tabs, o, offsets, ids, w.B, True, grad, w.lr, w.eps)
+    assert status(tabs) == (eb.EMB_OK, 0)
