@@ -179,6 +179,13 @@ emb_status_t emb_bag_backward_adagrad(emb_table_t h, const int64_t* offsets,
 emb_status_t emb_bag_prepare(emb_table_t h, const int64_t* offsets, const int64_t* ids,
                              int64_t batch, int64_t nnz, emb_pool_t pool, void* ws,
                              size_t ws_bytes, void* stream);
+/* emb_bag_forward from a workspace prepared for this batch (same result).
+ * When every bag holds exactly one id it gathers the rows in sorted order, so
+ * a row shared by many bags is read once per reduction chunk and W is walked
+ * in ascending order; otherwise it runs the same kernel as emb_bag_forward. */
+emb_status_t emb_bag_forward_prepared(emb_table_t h, const int64_t* offsets, const int64_t* ids,
+                                      int64_t batch, int64_t nnz, emb_pool_t pool, float* out,
+                                      void* ws, size_t ws_bytes, void* stream);
 emb_status_t emb_bag_backward_adagrad_prepared(emb_table_t h, int64_t batch, int64_t nnz,
                                                emb_pool_t pool, const float* grad_out, float lr,
                                                float eps, void* ws, size_t ws_bytes,

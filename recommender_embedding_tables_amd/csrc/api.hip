@@ -75,6 +75,7 @@ bool make_plan(const Handle& h, int64_t B, int64_t nnz, Plan* p) {
   p->part_tail = take(sizeof(float) * nc * (size_t)h.D);
   p->span_list = take(sizeof(uint32_t) * nc);
   p->long_list = take(sizeof(uint32_t) * nc);
+  p->chunk_base = take(sizeof(uint32_t) * (nc + 1));
   if (h.hashed) {
     p->h_slot = take(n4);
     p->h_first = take(n4);
@@ -277,6 +278,32 @@ emb_status_t emb_bag_prepare(emb_table_t t, const int64_t* offsets, const int64_
                                        static_cast<hipStream_t>(stream)));
 }
 
+emb_status_t emb_bag_forward_prepared(emb_table_t t, const int64_t* offsets, const int64_t* ids,
+                                      int64_t batch, int64_t nnz, emb_pool_t pool, float* out,
+                                      void* ws, size_t ws_bytes, void* stream) {
+  if (!t || !out || (nnz > 0 && !ids)) return EMB_ERR_INVALID_ARG;
+  if (pool != EMB_POOL_SUM && pool != EMB_POOL_MEAN) return EMB_ERR_INVALID_ARG;
+  emb_status_t st = check_batch(t->h, offsets, batch, nnz);
+  if (st != EMB_OK) return st;
+  if (!aligned16(out)) return EMB_ERR_INVALID_ARG;
+  Plan p;
+  if (!make_plan(t->h, batch, nnz, &p)) return EMB_ERR_UNSUPPORTED;
+  if (!ws || ws_bytes < p.total || (reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
+    return EMB_ERR_WORKSPACE;
+  if (batch == 0) return EMB_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+  uint32_t *keys = nullptr, *vals = nullptr;
+  sorted_arrays(p, w, &keys, &vals);
+  phase_mark(t->h, EMB_PHASE_FORWARD, false, s);
+  hipError_t e = launch_forward_sorted(t->h, p, keys, vals, out, w, s);
+  if (e == hipSuccess)
+    e = launch_forward_bags(t->h, offsets, ids, batch, nnz, pool == EMB_POOL_MEAN, out,
+                            reinterpret_cast<const uint32_t*>(w + p.misc), s);
+  phase_mark(t->h, EMB_PHASE_FORWARD, true, s);
+  return hip_status(e);
+}
+
 emb_status_t emb_bag_backward_adagrad_prepared(emb_table_t t, int64_t batch, int64_t nnz,
                                                emb_pool_t pool, const float* grad_out, float lr,
                                                float eps, void* ws, size_t ws_bytes,
@@ -314,6 +341,8 @@ emb_status_t emb_debug_sort_unique(emb_table_t t, const int64_t* offsets, const 
   char* w = static_cast<char*>(ws);
   uint32_t *keys = nullptr, *vals = nullptr;
   hipError_t e = launch_sort_unique(t->h, p, offsets, ids, false, w, &keys, &vals, s);
+  if (e == hipSuccess)  // unique / seg_off / inverse / counts; W and G untouched
+    e = launch_segment_adagrad(t->h, p, keys, vals, false, nullptr, 0.0f, 0.0f, w, s);
   const size_t nb = sizeof(uint32_t) * (size_t)nnz;
   if (e == hipSuccess && sorted_rows)
     e = launch_debug_copy_sorted(keys, (uint32_t)t->h.total_rows, sorted_rows, nnz, s);

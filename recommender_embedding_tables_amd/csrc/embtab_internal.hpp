@@ -110,6 +110,7 @@ struct Plan {
   size_t ucnt, vcnt;
   size_t misc;  // uint32[64]
   size_t part_head, part_tail, span_list, long_list;
+  size_t chunk_base;  // heads before each reduction chunk (nchunks + 1)
   size_t h_slot, h_first, h_tcnt;  // hash find-or-insert
   size_t total = 0;
 };
@@ -121,6 +122,7 @@ enum : int {
   kMiscSpanCount = 2,
   kMiscHashOverflow = 3,
   kMiscLongCount = 4,
+  kMiscNotOneHot = 5,  // some bag of the prepared batch does not hold exactly one id
   kMiscHashNew = 8,  // uint32 per table from here (up to T)
 };
 
@@ -139,6 +141,16 @@ __device__ inline uint32_t xcd_block() {
   const uint32_t nb = gridDim.x, b = blockIdx.x;
   const uint32_t q = nb >> 3, r = nb & 7u, x = b & 7u;
   return x * q + (x < r ? x : r) + (b >> 3);
+}
+
+// Row columns 4*d4 .. 4*d4+3 of `base`, or zeros when !ok.  The load is
+// unconditional (from column 0 of row 0 when !ok), which keeps the code free
+// of divergent branches around loads; `base` must hold at least 4 floats.
+__device__ inline f4 load4_or_zero(const float* __restrict__ base, size_t row, uint32_t D,
+                                   uint32_t d4, bool ok) {
+  const size_t off = ok ? row * D + 4u * d4 : 0u;
+  const f4 x = *reinterpret_cast<const f4*>(base + off);
+  return ok ? x : f4{0.f, 0.f, 0.f, 0.f};
 }
 
 // One SplitMix64 step from `state` (Steele, Lea and Flood 2014).
@@ -160,6 +172,7 @@ __device__ inline uint64_t slot_mix(uint64_t k) {
 hipError_t launch_init_dense(const Handle& h, hipStream_t s);
 hipError_t launch_fill_u64(uint64_t* p, uint64_t v, size_t n, hipStream_t s);
 hipError_t launch_fill_f32(float* p, float v, size_t n, hipStream_t s);
+hipError_t launch_zero_words(uint32_t* p, int n, hipStream_t s);
 
 hipError_t launch_forward(const Handle& h, const int64_t* offsets, const int64_t* ids,
                           int64_t B, int64_t nnz, bool mean, float* out, hipStream_t s);
@@ -170,9 +183,24 @@ hipError_t launch_sort_unique(const Handle& h, const Plan& p, const int64_t* off
                               const int64_t* ids, bool mean, char* ws, uint32_t** sorted_keys,
                               uint32_t** sorted_vals, hipStream_t s);
 
+// Segmented reduction + Adagrad over the sorted occurrences; on the way it
+// writes unique / seg_off / inverse / counts.  With grad_out == nullptr it only
+// writes those (W and G untouched).
 hipError_t launch_segment_adagrad(const Handle& h, const Plan& p, const uint32_t* keys,
                                   const uint32_t* perm, bool mean, const float* grad_out,
                                   float lr, float eps, char* ws, hipStream_t s);
+
+// One-hot forward from a prepared workspace (rows gathered in sorted order);
+// the kernel leaves the batch to the bag kernel when it is not one-hot.
+hipError_t launch_forward_sorted(const Handle& h, const Plan& p, const uint32_t* keys,
+                                 const uint32_t* perm, float* out, char* ws, hipStream_t s);
+// Bag forward that returns at once when `skip_if_onehot` (a prepared
+// workspace's misc words) says the sorted kernel owns the batch.
+hipError_t launch_forward_bags(const Handle& h, const int64_t* offsets, const int64_t* ids,
+                               int64_t B, int64_t nnz, bool mean, float* out,
+                               const uint32_t* skip_if_onehot, hipStream_t s);
+
+hipError_t launch_unique_counts(const Plan& p, char* ws, hipStream_t s);
 
 hipError_t launch_hash_find_or_insert(const Handle& h, const Plan& p, const int64_t* offsets,
                                       const uint64_t* keys, int64_t* ids_out, char* ws,

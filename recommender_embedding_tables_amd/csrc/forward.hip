@@ -24,188 +24,303 @@ namespace embtab {
 
 namespace {
 
+// Sample tile staged through LDS: a block owns samples [s0, s0 + S) of every
+// table, i.e. the contiguous output rows q = s0*T .. (s0+S)*T - 1.  Offsets of
+// table t for those samples are contiguous (bag b = t*B + s), so they are
+// staged with coalesced loads, and so are the ids of one-id bags.  Sub-groups
+// then walk the tile in output order.
+constexpr int kFwdTileBags = 1024;
+
 template <int SG, int VEC, bool MEAN, int UNR>
 __global__ __launch_bounds__(256) void k_bag_forward(
     const int64_t* __restrict__ offsets, const int64_t* __restrict__ ids,
     const float* __restrict__ W, const int64_t* __restrict__ row_off,
     const int64_t* __restrict__ rows, float* __restrict__ out, uint32_t* __restrict__ flags,
-    uint32_t B, uint32_t T, uint32_t D, uint32_t nnz) {
+    uint32_t B, uint32_t T, uint32_t D, uint32_t nnz, uint32_t S,
+    const uint32_t* __restrict__ skip) {
+  if (skip && skip[kMiscNotOneHot] == 0u) return;  // the sorted kernel owns this batch
   constexpr int SGPB = 256 / SG;
+  __shared__ uint32_t s_start[kFwdTileBags], s_len[kFwdTileBags], s_row[kFwdTileBags];
   const uint32_t lane = threadIdx.x % SG;
   const uint32_t sgb = threadIdx.x / SG;
   const uint32_t nbags = B * T;
-  const uint32_t b0 = (xcd_block() * SGPB + sgb) * (uint32_t)SG;  // first bag of the sub-group
+  const uint32_t s0 = xcd_block() * S;
+  if (s0 >= B) return;
+  const uint32_t Sl = (B - s0) < S ? (B - s0) : S;
+  const uint32_t ntile = Sl * T;  // bags of the tile; tile bag i = t * Sl + sl
   const uint32_t D4 = D >> 2;
+  uint32_t bad = 0u;
 
-  // Lane metadata: bag b0 + lane.
-  const uint32_t b = b0 + lane;
-  uint32_t start = 0u, len = 0u, t = 0u, s = 0u, bad = 0u;
-  uint32_t roff = 0u, nrow = 0u;
-  if (b < nbags) {
-    t = b / B;
-    s = b - t * B;
-    int64_t o0 = offsets[b], o1 = offsets[b + 1];
-    roff = (uint32_t)row_off[t];
-    nrow = (uint32_t)rows[t];
-    if ((b == 0 && o0 != 0) || (b == nbags - 1 && o1 != (int64_t)nnz) || o1 < o0 || o0 < 0 ||
-        o1 > (int64_t)nnz)
-      bad |= EMB_FLAG_BAD_OFFSETS;
-    o0 = o0 < 0 ? 0 : (o0 > (int64_t)nnz ? (int64_t)nnz : o0);
-    o1 = o1 < o0 ? o0 : (o1 > (int64_t)nnz ? (int64_t)nnz : o1);
-    start = (uint32_t)o0;
-    len = (uint32_t)(o1 - o0);
-  }
-  const bool onehot = __all(len <= 1u);
-  uint32_t myrow = kNoRow;
-  if (onehot && len == 1u) {
-    const int64_t id = ids[start];
-    if (id >= 0 && id < (int64_t)nrow) myrow = roff + (uint32_t)id;
-    else bad |= EMB_FLAG_OUT_OF_RANGE;
-  }
-
-  if (onehot) {
-#pragma unroll 1
-    for (uint32_t i0 = 0; i0 < (uint32_t)SG; i0 += UNR) {
-      if (b0 + i0 >= nbags) break;
-      f4 acc[UNR][VEC];
+  // Stage offsets (coalesced per table), then the ids of one-id bags; each
+  // thread owns tile bags tid + 256k, k < 4, with all their loads in flight.
+  constexpr int NST = kFwdTileBags / 256;
+  int64_t o0[NST], o1[NST];
 #pragma unroll
-      for (int u = 0; u < UNR; ++u) {
-        const uint32_t grow = (uint32_t)__shfl((int)myrow, (int)(i0 + u), SG);
+  for (int k = 0; k < NST; ++k) {
+    const uint32_t i = threadIdx.x + 256u * k;
+    o0[k] = 0;
+    o1[k] = 0;
+    if (i < ntile) {
+      const uint32_t t = i / Sl, sl = i - t * Sl;
+      const uint32_t b = t * B + s0 + sl;
+      o0[k] = offsets[b];
+      o1[k] = offsets[b + 1];
+      if ((b == 0 && o0[k] != 0) || (b == nbags - 1 && o1[k] != (int64_t)nnz))
+        bad |= EMB_FLAG_BAD_OFFSETS;
+    }
+  }
+  uint32_t tb[NST];
+  int64_t idv[NST];
 #pragma unroll
-        for (int v = 0; v < VEC; ++v) {
-          const uint32_t d4 = lane + v * SG;
-          acc[u][v] = f4{0.f, 0.f, 0.f, 0.f};
-          if (grow != kNoRow && d4 < D4)
-            acc[u][v] = *reinterpret_cast<const f4*>(W + (size_t)grow * D + 4 * d4);
-        }
+  for (int k = 0; k < NST; ++k) {
+    const uint32_t i = threadIdx.x + 256u * k;
+    tb[k] = i / Sl;
+    idv[k] = -1;
+    if (i < ntile) {
+      if (o1[k] < o0[k] || o0[k] < 0 || o1[k] > (int64_t)nnz) bad |= EMB_FLAG_BAD_OFFSETS;
+      const int64_t a = o0[k] < 0 ? 0 : (o0[k] > (int64_t)nnz ? (int64_t)nnz : o0[k]);
+      const int64_t e = o1[k] < a ? a : (o1[k] > (int64_t)nnz ? (int64_t)nnz : o1[k]);
+      s_start[i] = (uint32_t)a;
+      s_len[i] = (uint32_t)(e - a);
+      if (e - a == 1) idv[k] = ids[a];
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < NST; ++k) {
+    const uint32_t i = threadIdx.x + 256u * k;
+    if (i < ntile) {
+      uint32_t r = kNoRow;
+      if (s_len[i] == 1u) {
+        const int64_t id = idv[k];
+        if (id >= 0 && id < rows[tb[k]]) r = (uint32_t)row_off[tb[k]] + (uint32_t)id;
+        else bad |= EMB_FLAG_OUT_OF_RANGE;
       }
+      s_row[i] = r;
+    }
+  }
+  __syncthreads();
+
+  // Output order: tile-local q = sl * T + t  ->  out row s0 * T + q.
+  const size_t qbase = (size_t)s0 * T;
+#pragma unroll 1
+  for (uint32_t q0 = sgb * UNR; q0 < ntile; q0 += SGPB * UNR) {
+    uint32_t bi[UNR];
+    bool simple = true;
+    uint32_t sl = q0 / T, t = q0 - (q0 / T) * T;  // walk (sample, table) in output order
 #pragma unroll
-      for (int u = 0; u < UNR; ++u) {
-        const uint32_t bt = (uint32_t)__shfl((int)t, (int)(i0 + u), SG);
-        const uint32_t bs = (uint32_t)__shfl((int)s, (int)(i0 + u), SG);
-        if (b0 + i0 + u >= nbags) continue;
-        const size_t o = ((size_t)bs * T + bt) * D;
-#pragma unroll
-        for (int v = 0; v < VEC; ++v) {
-          const uint32_t d4 = lane + v * SG;
-          if (d4 < D4)
-            __builtin_nontemporal_store(acc[u][v], reinterpret_cast<f4*>(out + o + 4 * d4));
-        }
+    for (int u = 0; u < UNR; ++u) {
+      bi[u] = 0u;
+      if (q0 + u < ntile) {
+        bi[u] = t * Sl + sl;
+        simple = simple && s_len[bi[u]] <= 1u;
+      }
+      if (++t == T) {
+        t = 0;
+        ++sl;
       }
     }
-  } else {
-    // Multi-hot: MU bags at a time, their ids SG at a time, KU rows in flight per bag.
-    constexpr int MU = 2, KU = 4;
-#pragma unroll 1
-    for (uint32_t i0 = 0; i0 < (uint32_t)SG; i0 += MU) {
-      if (b0 + i0 >= nbags) break;
-      uint32_t bl[MU], bst[MU], broff[MU], bnr[MU];
-      uint32_t maxlen = 0u;
-      f4 acc[MU][VEC];
+    f4 acc[UNR][VEC];
 #pragma unroll
-      for (int u = 0; u < MU; ++u) {
-        bl[u] = (uint32_t)__shfl((int)len, (int)(i0 + u), SG);
-        bst[u] = (uint32_t)__shfl((int)start, (int)(i0 + u), SG);
-        broff[u] = (uint32_t)__shfl((int)roff, (int)(i0 + u), SG);
-        bnr[u] = (uint32_t)__shfl((int)nrow, (int)(i0 + u), SG);
-        maxlen = bl[u] > maxlen ? bl[u] : maxlen;
+    for (int u = 0; u < UNR; ++u)
 #pragma unroll
-        for (int v = 0; v < VEC; ++v) acc[u][v] = f4{0.f, 0.f, 0.f, 0.f};
+      for (int v = 0; v < VEC; ++v) acc[u][v] = f4{0.f, 0.f, 0.f, 0.f};
+    if (simple) {
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        const uint32_t r = q0 + u < ntile ? s_row[bi[u]] : kNoRow;
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) {
+          const uint32_t d4 = lane + v * SG;
+          acc[u][v] = load4_or_zero(W, r, D, d4, r != kNoRow && d4 < D4);
+        }
       }
+    } else {
+      // Multi-hot bags: ids SG at a time (one coalesced load), KU rows in flight.
+      constexpr int KU = 4;
+      uint32_t msl = q0 / T, mt = q0 - (q0 / T) * T;
 #pragma unroll 1
-      for (uint32_t kb = 0; kb < maxlen; kb += SG) {
-        uint32_t r[MU];
+      for (int u = 0; u < UNR; ++u) {
+        if (q0 + u >= ntile) break;
+        const uint32_t i = mt * Sl + msl;
+        if (++mt == T) {
+          mt = 0;
+          ++msl;
+        }
+        const uint32_t len = s_len[i], st = s_start[i];
+        const uint32_t tt = i / Sl;
+        const uint32_t roff = (uint32_t)row_off[tt];
+        const int64_t nr = rows[tt];
+        f4 a[VEC];
 #pragma unroll
-        for (int u = 0; u < MU; ++u) {
-          r[u] = kNoRow;
-          if (kb + lane < bl[u]) {
-            const int64_t id = ids[bst[u] + kb + lane];
-            if (id >= 0 && id < (int64_t)bnr[u]) r[u] = broff[u] + (uint32_t)id;
+        for (int v = 0; v < VEC; ++v) a[v] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+        for (uint32_t kb = 0; kb < len; kb += SG) {
+          uint32_t r = kNoRow;
+          if (kb + lane < len) {
+            const int64_t id = ids[st + kb + lane];
+            if (id >= 0 && id < nr) r = roff + (uint32_t)id;
             else bad |= EMB_FLAG_OUT_OF_RANGE;
           }
-        }
-        const uint32_t kend = (maxlen - kb) < (uint32_t)SG ? (maxlen - kb) : (uint32_t)SG;
+          const uint32_t kend = (len - kb) < (uint32_t)SG ? (len - kb) : (uint32_t)SG;
 #pragma unroll 1
-        for (uint32_t kk = 0; kk < kend; kk += KU) {
-          f4 x[MU][KU][VEC];
-#pragma unroll
-          for (int u = 0; u < MU; ++u)
+          for (uint32_t kk = 0; kk < kend; kk += KU) {
+            f4 x[KU][VEC];
 #pragma unroll
             for (int k = 0; k < KU; ++k) {
-              // lanes past kend hold kNoRow, so the tail of the last group loads nothing
               const uint32_t src = kk + k < (uint32_t)SG ? kk + k : (uint32_t)SG - 1u;
-              uint32_t grow = (uint32_t)__shfl((int)r[u], (int)src, SG);
+              uint32_t grow = (uint32_t)__shfl((int)r, (int)src, SG);
               if (kk + k >= kend) grow = kNoRow;
 #pragma unroll
               for (int v = 0; v < VEC; ++v) {
                 const uint32_t d4 = lane + v * SG;
-                x[u][k][v] = f4{0.f, 0.f, 0.f, 0.f};
-                if (grow != kNoRow && d4 < D4)
-                  x[u][k][v] = *reinterpret_cast<const f4*>(W + (size_t)grow * D + 4 * d4);
+                x[k][v] = load4_or_zero(W, grow, D, d4, grow != kNoRow && d4 < D4);
               }
             }
 #pragma unroll
-          for (int u = 0; u < MU; ++u)
-#pragma unroll
             for (int k = 0; k < KU; ++k)
 #pragma unroll
-              for (int v = 0; v < VEC; ++v) acc[u][v] += x[u][k][v];
+              for (int v = 0; v < VEC; ++v) a[v] += x[k][v];
+          }
         }
-      }
-#pragma unroll
-      for (int u = 0; u < MU; ++u) {
-        const uint32_t bt = (uint32_t)__shfl((int)t, (int)(i0 + u), SG);
-        const uint32_t bs = (uint32_t)__shfl((int)s, (int)(i0 + u), SG);
-        if (b0 + i0 + u >= nbags) continue;
-        float c = 1.0f;
-        if (MEAN && bl[u] > 0) c = 1.0f / (float)bl[u];
-        const size_t o = ((size_t)bs * T + bt) * D;
+        const float c = (MEAN && len > 0u) ? 1.0f / (float)len : 1.0f;
+        const size_t o = (qbase + q0 + u) * D;
 #pragma unroll
         for (int v = 0; v < VEC; ++v) {
           const uint32_t d4 = lane + v * SG;
           if (d4 < D4) {
-            const f4 rr = MEAN ? acc[u][v] * c : acc[u][v];
+            const f4 rr = MEAN ? a[v] * c : a[v];
             __builtin_nontemporal_store(rr, reinterpret_cast<f4*>(out + o + 4 * d4));
           }
         }
+      }
+      continue;
+    }
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      if (q0 + u >= ntile) continue;
+      const size_t o = (qbase + q0 + u) * D;
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) {
+        const uint32_t d4 = lane + v * SG;
+        if (d4 < D4)
+          __builtin_nontemporal_store(acc[u][v], reinterpret_cast<f4*>(out + o + 4 * d4));
       }
     }
   }
   if (bad) atomicOr(flags, bad);
 }
 
+// One-hot batches after the sort: every bag holds one id, so the output row of
+// occurrence j is W[row_j] stored at out[grad_row(j)].  Walking the sorted
+// occurrences, a Zipf-hot row is read once per chunk and then stored to each
+// of its bags, and W is visited in ascending address order.  Chunks and
+// sub-groups are those of the reduction kernel; MPL metadata entries per lane.
+template <int SG, int VEC, int MPL>
+__global__ __launch_bounds__(256) void k_fwd_sorted(
+    const uint32_t* __restrict__ keys, const uint32_t* __restrict__ perm,
+    const uint32_t* __restrict__ gr, const float* __restrict__ W, float* __restrict__ out,
+    uint32_t n, uint32_t sentinel, uint32_t D, uint32_t nbags,
+    const uint32_t* __restrict__ misc) {
+  if (misc[kMiscNotOneHot] != 0u) return;  // the bag kernel owns this batch
+  constexpr int CH = SG * MPL;
+  constexpr int SGPB = 256 / SG;
+  constexpr int UF = VEC > 1 ? 2 : (SG < 4 ? SG : 4);
+  const uint32_t lane = threadIdx.x % SG;
+  const uint32_t c = xcd_block() * SGPB + threadIdx.x / SG;
+  const uint32_t k0 = c * CH;
+  if (k0 >= n) return;
+  const uint32_t D4 = D >> 2;
+  uint32_t mkey[MPL], mgr[MPL];
+#pragma unroll
+  for (int i = 0; i < MPL; ++i) {
+    const uint32_t k = k0 + i * SG + lane;
+    mkey[i] = kNoRow;
+    mgr[i] = nbags;
+    if (k < n) {
+      mkey[i] = keys[k];
+      const uint32_t j = perm[k];
+      mgr[i] = j < n ? gr[j] : nbags;
+    }
+  }
+  uint32_t prevkey = kNoRow;
+  f4 prevrow[VEC];
+#pragma unroll
+  for (int v = 0; v < VEC; ++v) prevrow[v] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < MPL; ++i) {
+#pragma unroll 1
+    for (int l0 = 0; l0 < SG; l0 += UF) {
+      uint32_t kk[UF], gg[UF];
+#pragma unroll
+      for (int u = 0; u < UF; ++u) {
+        kk[u] = (uint32_t)__shfl((int)mkey[i], l0 + u, SG);
+        gg[u] = (uint32_t)__shfl((int)mgr[i], l0 + u, SG);
+      }
+      f4 x[UF][VEC];
+#pragma unroll
+      for (int u = 0; u < UF; ++u) {
+        const uint32_t pk = u == 0 ? prevkey : kk[u > 0 ? u - 1 : 0];
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) {
+          const uint32_t d4 = lane + v * SG;
+          x[u][v] = load4_or_zero(W, kk[u], D, d4, kk[u] < sentinel && kk[u] != pk && d4 < D4);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < UF; ++u) {
+        const uint32_t pk = u == 0 ? prevkey : kk[u > 0 ? u - 1 : 0];
+        if (kk[u] < sentinel && kk[u] == pk) {
+#pragma unroll
+          for (int v = 0; v < VEC; ++v) x[u][v] = u == 0 ? prevrow[v] : x[u > 0 ? u - 1 : 0][v];
+        }
+        if (gg[u] < nbags) {
+#pragma unroll
+          for (int v = 0; v < VEC; ++v) {
+            const uint32_t d4 = lane + v * SG;
+            if (d4 < D4)
+              __builtin_nontemporal_store(x[u][v],
+                                          reinterpret_cast<f4*>(out + (size_t)gg[u] * D + 4 * d4));
+          }
+        }
+      }
+      prevkey = kk[UF - 1];
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) prevrow[v] = x[UF - 1][v];
+    }
+  }
+}
+
 template <int SG, int VEC, bool MEAN>
 hipError_t launch_t(const Handle& h, const int64_t* offsets, const int64_t* ids, int64_t B,
-                    int64_t nnz, float* out, hipStream_t s) {
-  constexpr int UNR = VEC == 1 ? (SG >= 8 ? 8 : SG) : (VEC == 2 ? 4 : 2);  // one-hot rows in flight
-  constexpr int SGPB = 256 / SG;
-  const int64_t nbags = B * (int64_t)h.T;
-  const int64_t per_block = (int64_t)SGPB * SG;
-  const int64_t grid = (nbags + per_block - 1) / per_block;
+                    int64_t nnz, float* out, const uint32_t* skip, hipStream_t s) {
+  constexpr int UNR = VEC == 1 ? 8 : (VEC == 2 ? 4 : 2);  // one-hot rows in flight
+  int64_t S = kFwdTileBags / h.T;
+  S = S > 64 ? 64 : (S < 1 ? 1 : S);
+  const int64_t grid = (B + S - 1) / S;
   if (grid == 0) return hipSuccess;
   hipLaunchKernelGGL((k_bag_forward<SG, VEC, MEAN, UNR>), dim3((unsigned)grid), dim3(256), 0, s,
                      offsets, ids, h.W, h.sv.row_off, h.sv.rows, out, h.sv.flags, (uint32_t)B,
-                     (uint32_t)h.T, (uint32_t)h.D, (uint32_t)nnz);
+                     (uint32_t)h.T, (uint32_t)h.D, (uint32_t)nnz, (uint32_t)S, skip);
   return hipGetLastError();
 }
 
 template <bool MEAN>
 hipError_t dispatch(const Handle& h, const int64_t* offsets, const int64_t* ids, int64_t B,
-                    int64_t nnz, float* out, hipStream_t s) {
+                    int64_t nnz, float* out, const uint32_t* skip, hipStream_t s) {
   const int sg = subgroup_lanes(h.D), vec = vec_per_lane(h.D);
   switch (sg) {
-    case 1: return launch_t<1, 1, MEAN>(h, offsets, ids, B, nnz, out, s);
-    case 2: return launch_t<2, 1, MEAN>(h, offsets, ids, B, nnz, out, s);
-    case 4: return launch_t<4, 1, MEAN>(h, offsets, ids, B, nnz, out, s);
-    case 8: return launch_t<8, 1, MEAN>(h, offsets, ids, B, nnz, out, s);
-    case 16: return launch_t<16, 1, MEAN>(h, offsets, ids, B, nnz, out, s);
-    case 32: return launch_t<32, 1, MEAN>(h, offsets, ids, B, nnz, out, s);
+    case 1: return launch_t<1, 1, MEAN>(h, offsets, ids, B, nnz, out, skip, s);
+    case 2: return launch_t<2, 1, MEAN>(h, offsets, ids, B, nnz, out, skip, s);
+    case 4: return launch_t<4, 1, MEAN>(h, offsets, ids, B, nnz, out, skip, s);
+    case 8: return launch_t<8, 1, MEAN>(h, offsets, ids, B, nnz, out, skip, s);
+    case 16: return launch_t<16, 1, MEAN>(h, offsets, ids, B, nnz, out, skip, s);
+    case 32: return launch_t<32, 1, MEAN>(h, offsets, ids, B, nnz, out, skip, s);
     default:
       switch (vec) {
-        case 1: return launch_t<64, 1, MEAN>(h, offsets, ids, B, nnz, out, s);
-        case 2: return launch_t<64, 2, MEAN>(h, offsets, ids, B, nnz, out, s);
-        case 3: return launch_t<64, 3, MEAN>(h, offsets, ids, B, nnz, out, s);
-        default: return launch_t<64, 4, MEAN>(h, offsets, ids, B, nnz, out, s);
+        case 1: return launch_t<64, 1, MEAN>(h, offsets, ids, B, nnz, out, skip, s);
+        case 2: return launch_t<64, 2, MEAN>(h, offsets, ids, B, nnz, out, skip, s);
+        case 3: return launch_t<64, 3, MEAN>(h, offsets, ids, B, nnz, out, skip, s);
+        default: return launch_t<64, 4, MEAN>(h, offsets, ids, B, nnz, out, skip, s);
       }
   }
 }
@@ -215,10 +330,54 @@ hipError_t dispatch(const Handle& h, const int64_t* offsets, const int64_t* ids,
 hipError_t launch_forward(const Handle& h, const int64_t* offsets, const int64_t* ids,
                           int64_t B, int64_t nnz, bool mean, float* out, hipStream_t s) {
   phase_mark(h, EMB_PHASE_FORWARD, false, s);
-  hipError_t e = mean ? dispatch<true>(h, offsets, ids, B, nnz, out, s)
-                      : dispatch<false>(h, offsets, ids, B, nnz, out, s);
+  hipError_t e = mean ? dispatch<true>(h, offsets, ids, B, nnz, out, nullptr, s)
+                      : dispatch<false>(h, offsets, ids, B, nnz, out, nullptr, s);
   phase_mark(h, EMB_PHASE_FORWARD, true, s);
   return e;
+}
+
+hipError_t launch_forward_bags(const Handle& h, const int64_t* offsets, const int64_t* ids,
+                               int64_t B, int64_t nnz, bool mean, float* out,
+                               const uint32_t* skip_if_onehot, hipStream_t s) {
+  return mean ? dispatch<true>(h, offsets, ids, B, nnz, out, skip_if_onehot, s)
+              : dispatch<false>(h, offsets, ids, B, nnz, out, skip_if_onehot, s);
+}
+
+namespace {
+template <int SG, int VEC>
+hipError_t launch_sorted_t(const Handle& h, const Plan& p, const uint32_t* keys,
+                           const uint32_t* perm, float* out, char* ws, hipStream_t s) {
+  constexpr int MPL = SG >= 32 ? 1 : 32 / SG;
+  constexpr int SGPB = 256 / SG;
+  const int64_t chunks = (p.nnz + SG * MPL - 1) / (SG * MPL);
+  const int64_t grid = (chunks + SGPB - 1) / SGPB;
+  if (grid == 0) return hipSuccess;
+  hipLaunchKernelGGL((k_fwd_sorted<SG, VEC, MPL>), dim3((unsigned)grid), dim3(256), 0, s, keys,
+                     perm, reinterpret_cast<const uint32_t*>(ws + p.gr), h.W, out,
+                     (uint32_t)p.nnz, (uint32_t)h.total_rows, (uint32_t)h.D,
+                     (uint32_t)(p.B * h.T), reinterpret_cast<const uint32_t*>(ws + p.misc));
+  return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_forward_sorted(const Handle& h, const Plan& p, const uint32_t* keys,
+                                 const uint32_t* perm, float* out, char* ws, hipStream_t s) {
+  const int sg = subgroup_lanes(h.D), vec = vec_per_lane(h.D);
+  switch (sg) {
+    case 1: return launch_sorted_t<1, 1>(h, p, keys, perm, out, ws, s);
+    case 2: return launch_sorted_t<2, 1>(h, p, keys, perm, out, ws, s);
+    case 4: return launch_sorted_t<4, 1>(h, p, keys, perm, out, ws, s);
+    case 8: return launch_sorted_t<8, 1>(h, p, keys, perm, out, ws, s);
+    case 16: return launch_sorted_t<16, 1>(h, p, keys, perm, out, ws, s);
+    case 32: return launch_sorted_t<32, 1>(h, p, keys, perm, out, ws, s);
+    default:
+      switch (vec) {
+        case 1: return launch_sorted_t<64, 1>(h, p, keys, perm, out, ws, s);
+        case 2: return launch_sorted_t<64, 2>(h, p, keys, perm, out, ws, s);
+        case 3: return launch_sorted_t<64, 3>(h, p, keys, perm, out, ws, s);
+        default: return launch_sorted_t<64, 4>(h, p, keys, perm, out, ws, s);
+      }
+  }
 }
 
 }  // namespace embtab

@@ -59,10 +59,6 @@ __device__ inline void load_table_bounds(int64_t* tb, const int64_t* offsets, in
   __syncthreads();
 }
 
-__global__ void k_zero_words(uint32_t* __restrict__ p, int32_t n) {
-  for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0u;
-}
-
 struct Slot {
   uint64_t key;
   uint64_t row;
@@ -319,7 +315,7 @@ hipError_t launch_hash_find_or_insert(const Handle& h, const Plan& p, const int6
   const unsigned nb = (unsigned)((nnz + 255) / 256);
   const unsigned grid = nb > 0 ? nb : 1;
   phase_mark(h, EMB_PHASE_HASH, false, s);
-  hipLaunchKernelGGL(k_zero_words, dim3(1), dim3(256), 0, s, misc, kMiscHashNew + 2 * h.T);
+  launch_zero_words(misc, kMiscHashNew + 2 * h.T, s);
   hipLaunchKernelGGL(k_hash_probe, dim3(grid), dim3(256), shm, s, offsets, keys, p.B, h.T, nnz,
                      slots, h.capacity, ids_out, slot_of, h.sv.flags, misc);
   hipLaunchKernelGGL(k_hash_first, dim3(grid), dim3(256), shm, s, offsets, p.B, h.T, nnz, slots,

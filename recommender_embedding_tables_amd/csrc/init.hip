@@ -56,6 +56,10 @@ __global__ __launch_bounds__(256) void k_fill_f32(float* __restrict__ p, float v
     p[i] = v;
 }
 
+__global__ void k_zero_words(uint32_t* __restrict__ p, int32_t n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0u;
+}
+
 unsigned grid_for(size_t n) {
   size_t g = (n + 255) / 256;
   const size_t cap = 256 * 64;  // 64 blocks per CU, then grid-stride
@@ -76,6 +80,11 @@ hipError_t launch_init_dense(const Handle& h, hipStream_t s) {
 hipError_t launch_fill_u64(uint64_t* p, uint64_t v, size_t n, hipStream_t s) {
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL(k_fill_u64, dim3(grid_for(n)), dim3(256), 0, s, p, v, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_words(uint32_t* p, int n, hipStream_t s) {
+  hipLaunchKernelGGL(k_zero_words, dim3(1), dim3(256), 0, s, p, n);
   return hipGetLastError();
 }
 

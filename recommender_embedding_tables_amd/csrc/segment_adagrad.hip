@@ -25,9 +25,16 @@
 // result is deterministic and no float atomics are used.
 #include "embtab_internal.hpp"
 
+#ifndef EMBTAB_SEG_UF
+#define EMBTAB_SEG_UF 4
+#endif
+
 namespace embtab {
 
 namespace {
+
+// Sorted positions walked per group by one sub-group (rows in flight).
+constexpr int kSegUF = EMBTAB_SEG_UF;
 
 __device__ inline void adagrad_step(f4& w, f4& g2, const f4 g, float lr, float eps) {
 #pragma unroll
@@ -38,14 +45,16 @@ __device__ inline void adagrad_step(f4& w, f4& g2, const f4 g, float lr, float e
   }
 }
 
-template <int SG, int VEC, bool MEAN, int MPL, int UF>
+template <int SG, int VEC, bool MEAN, int MPL, int UF, bool UPDATE>
 __global__ __launch_bounds__(256) void k_seg_adagrad(
     const uint32_t* __restrict__ keys, const uint32_t* __restrict__ perm,
     const uint32_t* __restrict__ gr, const float* __restrict__ scale,
     const float* __restrict__ grad, float* __restrict__ W, float* __restrict__ G, uint32_t n,
     uint32_t sentinel, int32_t D, float lr, float eps, float* __restrict__ part_head,
     float* __restrict__ part_tail, uint32_t* __restrict__ span_list,
-    uint32_t* __restrict__ misc, uint32_t nbags) {
+    uint32_t* __restrict__ misc, uint32_t nbags, const uint32_t* __restrict__ chunk_base,
+    uint32_t* __restrict__ unique, uint32_t* __restrict__ seg_off,
+    uint32_t* __restrict__ inverse) {
   constexpr int CH = SG * MPL;
   constexpr int SGPB = 256 / SG;
   const int lane = threadIdx.x % SG;
@@ -57,13 +66,15 @@ __global__ __launch_bounds__(256) void k_seg_adagrad(
   const int D4 = D >> 2;
   const uint32_t key_prev = k0 > 0 ? keys[k0 - 1] : kNoRow;
   const uint32_t key_next = k1 < n ? keys[k1] : kNoRow;
+  uint32_t ucur = chunk_base[c] - 1u;  // unique index of a run entering the chunk
 
-  uint32_t mkey[MPL], mgr[MPL];
+  uint32_t mkey[MPL], mj[MPL], mgr[MPL];
   float msc[MPL];
 #pragma unroll
   for (int i = 0; i < MPL; ++i) {
     const uint32_t k = k0 + i * SG + lane;
     mkey[i] = kNoRow;
+    mj[i] = 0u;
     mgr[i] = 0u;
     msc[i] = 1.0f;
     if (k < k1) mkey[i] = keys[k];
@@ -77,11 +88,16 @@ __global__ __launch_bounds__(256) void k_seg_adagrad(
       const uint32_t j = perm[k];
       const uint32_t g = j < n ? gr[j] : nbags;
       if (g < nbags) {
+        mj[i] = j;
         mgr[i] = g;
-        if (MEAN) msc[i] = scale[j];
+        if (MEAN && UPDATE) msc[i] = scale[j];
       } else {
         mkey[i] = sentinel;
       }
+    } else if (k < k1) {
+      // an out-of-range occurrence (sentinel key) belongs to no unique row
+      const uint32_t j = perm[k];
+      if (j < n) inverse[j] = kNoRow;
     }
   }
 
@@ -89,18 +105,20 @@ __global__ __launch_bounds__(256) void k_seg_adagrad(
 #pragma unroll
   for (int v = 0; v < VEC; ++v) acc[v] = f4{0.f, 0.f, 0.f, 0.f};
   bool first_seg = true;
+  uint32_t lastkey = key_prev;
   const uint32_t last = k1 - k0 - 1;  // last position of the chunk
 
 #pragma unroll
   for (int i = 0; i < MPL; ++i) {
     for (int l0 = 0; l0 < SG; l0 += UF) {
-      uint32_t kk[UF + 1], gg[UF];
+      uint32_t kk[UF + 1], gg[UF], jj[UF];
       float cc[UF];
 #pragma unroll
       for (int u = 0; u < UF; ++u) {
         kk[u] = (uint32_t)__shfl((int)mkey[i], l0 + u, SG);
-        gg[u] = (uint32_t)__shfl((int)mgr[i], l0 + u, SG);
-        cc[u] = MEAN ? __shfl(msc[i], l0 + u, SG) : 1.0f;
+        jj[u] = (uint32_t)__shfl((int)mj[i], l0 + u, SG);
+        gg[u] = UPDATE ? (uint32_t)__shfl((int)mgr[i], l0 + u, SG) : 0u;
+        cc[u] = (MEAN && UPDATE) ? __shfl(msc[i], l0 + u, SG) : 1.0f;
       }
       {
         // key of the position after the group
@@ -124,25 +142,33 @@ __global__ __launch_bounds__(256) void k_seg_adagrad(
       }
       if (!vld[0]) break;  // the rest of the chunk holds no valid keys
       f4 g[UF][VEC], wv[UF][VEC], gv[UF][VEC];
+      if (UPDATE) {
 #pragma unroll
-      for (int u = 0; u < UF; ++u) {
+        for (int u = 0; u < UF; ++u) {
 #pragma unroll
-        for (int v = 0; v < VEC; ++v) {
-          const int d4 = lane + v * SG;
-          g[u][v] = f4{0.f, 0.f, 0.f, 0.f};
-          wv[u][v] = f4{0.f, 0.f, 0.f, 0.f};
-          gv[u][v] = f4{0.f, 0.f, 0.f, 0.f};
-          if (vld[u] && d4 < D4)
-            g[u][v] = *reinterpret_cast<const f4*>(grad + (size_t)gg[u] * D + 4 * d4);
-          if (endf[u] && !startb[u] && d4 < D4) {
-            wv[u][v] = *reinterpret_cast<const f4*>(W + (size_t)kk[u] * D + 4 * d4);
-            gv[u][v] = *reinterpret_cast<const f4*>(G + (size_t)kk[u] * D + 4 * d4);
+          for (int v = 0; v < VEC; ++v) {
+            const uint32_t d4 = (uint32_t)(lane + v * SG);
+            const bool own = endf[u] && !startb[u] && d4 < (uint32_t)D4;
+            g[u][v] = load4_or_zero(grad, gg[u], (uint32_t)D, d4, vld[u] && d4 < (uint32_t)D4);
+            wv[u][v] = load4_or_zero(W, kk[u], (uint32_t)D, d4, own);
+            gv[u][v] = load4_or_zero(G, kk[u], (uint32_t)D, d4, own);
           }
         }
       }
 #pragma unroll
       for (int u = 0; u < UF; ++u) {
         if (!vld[u]) continue;
+        const uint32_t p = (uint32_t)(i * SG + l0 + u);
+        const uint32_t prevk = u > 0 ? kk[u > 0 ? u - 1 : 0] : lastkey;
+        if (kk[u] != prevk) {
+          ++ucur;
+          if (lane == 0) {
+            unique[ucur] = kk[u];
+            seg_off[ucur] = k0 + p;
+          }
+        }
+        if (lane == 0) inverse[jj[u]] = ucur;
+        if (!UPDATE) continue;
 #pragma unroll
         for (int v = 0; v < VEC; ++v) acc[v] += MEAN ? g[u][v] * cc[u] : g[u][v];
         if (endf[u]) {
@@ -178,6 +204,7 @@ __global__ __launch_bounds__(256) void k_seg_adagrad(
           }
         }
       }
+      lastkey = kk[UF - 1];
       first_seg = fs;
     }
   }
@@ -330,7 +357,7 @@ template <int SG, int VEC, bool MEAN>
 hipError_t launch_t(const Handle& h, const Plan& p, const uint32_t* keys, const uint32_t* perm,
                     const float* grad_out, float lr, float eps, char* ws, hipStream_t s) {
   constexpr int MPL = SG >= 32 ? 1 : 32 / SG;
-  constexpr int UF = VEC > 1 ? 2 : (SG < 4 ? SG : 4);
+  constexpr int UF = VEC > 1 ? 2 : (SG < kSegUF ? SG : kSegUF);
   constexpr int SGPB = 256 / SG;
   static_assert(SG * MPL >= 32, "chunk");
   const uint32_t n = (uint32_t)p.nnz;
@@ -343,12 +370,27 @@ hipError_t launch_t(const Handle& h, const Plan& p, const uint32_t* keys, const 
   float* pt = reinterpret_cast<float*>(ws + p.part_tail);
   uint32_t* spans = reinterpret_cast<uint32_t*>(ws + p.span_list);
   uint32_t* misc = reinterpret_cast<uint32_t*>(ws + p.misc);
+  const uint32_t* cbase = reinterpret_cast<const uint32_t*>(ws + p.chunk_base);
+  uint32_t* uniq = reinterpret_cast<uint32_t*>(ws + p.unique);
+  uint32_t* segs = reinterpret_cast<uint32_t*>(ws + p.seg_off);
+  uint32_t* inv = reinterpret_cast<uint32_t*>(ws + p.inverse);
+  const uint32_t nbags = (uint32_t)(p.B * h.T);
+  hipError_t e;
+  if (!grad_out) {  // unique / seg_off / inverse only
+    hipLaunchKernelGGL((k_seg_adagrad<SG, VEC, false, MPL, UF, false>), dim3((unsigned)grid),
+                       dim3(256), 0, s, keys, perm, gr, scale, grad_out, h.W, h.G, n,
+                       (uint32_t)h.total_rows, h.D, lr, eps, ph, pt, spans, misc, nbags, cbase,
+                       uniq, segs, inv);
+    e = hipGetLastError();
+    return e == hipSuccess ? launch_unique_counts(p, ws, s) : e;
+  }
   phase_mark(h, EMB_PHASE_REDUCE, false, s);
-  hipLaunchKernelGGL((k_seg_adagrad<SG, VEC, MEAN, MPL, UF>), dim3((unsigned)grid), dim3(256), 0,
-                     s, keys, perm, gr, scale, grad_out, h.W, h.G, n, (uint32_t)h.total_rows, h.D,
-                     lr, eps, ph, pt, spans, misc, (uint32_t)(p.B * h.T));
+  hipLaunchKernelGGL((k_seg_adagrad<SG, VEC, MEAN, MPL, UF, true>), dim3((unsigned)grid),
+                     dim3(256), 0, s, keys, perm, gr, scale, grad_out, h.W, h.G, n,
+                     (uint32_t)h.total_rows, h.D, lr, eps, ph, pt, spans, misc, nbags, cbase,
+                     uniq, segs, inv);
   phase_mark(h, EMB_PHASE_REDUCE, true, s);
-  hipError_t e = hipGetLastError();
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   constexpr int FNT = VEC == 1 ? 1024 : (VEC == 2 ? 512 : 256);
   uint32_t* longs = reinterpret_cast<uint32_t*>(ws + p.long_list);
@@ -360,7 +402,9 @@ hipError_t launch_t(const Handle& h, const Plan& p, const uint32_t* keys, const 
                      SG * MPL, h.W, h.G, h.D, lr, eps, ph, pt, spans, longs, misc);
   hipLaunchKernelGGL((k_fix_long<SG, VEC, FNT>), dim3((unsigned)lgrid), dim3(FNT), 0, s, keys, n,
                      SG * MPL, h.W, h.G, h.D, lr, eps, ph, pt, longs, misc);
+  e = launch_unique_counts(p, ws, s);
   phase_mark(h, EMB_PHASE_FIXUP, true, s);
+  if (e != hipSuccess) return e;
   return hipGetLastError();
 }
 

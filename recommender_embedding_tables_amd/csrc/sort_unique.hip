@@ -10,7 +10,8 @@
 // Kernels, in launch order:
 //   k_keys          one thread per bag: key = off_t + id (out-of-range ids get
 //                   the sentinel key total_rows, which sorts last), value = j,
-//                   grad row s*T + t and, for mean pooling, 1/L of the bag.
+//                   grad row s*T + t and, for mean pooling, 1/L of the bag;
+//                   flags the batch as not one-hot when a bag's length is not 1.
 //   k_sort_hist     per 4096-key tile, digit counts -> tile_hist[digit][tile].
 //   k_sort_scan     one block per digit: exclusive scan over tiles, digit totals.
 //   k_sort_scatter  per tile: stable rank of every key (per-wave ballot match
@@ -19,10 +20,14 @@
 //                   which consecutive lanes store consecutive addresses.
 //   (hist / scan / scatter once per digit; digits of at most 9 bits cover
 //    ceil(log2(total_rows + 1)) key bits, so three passes sort 2^27 rows.)
-//   k_unique_count  per tile: run heads and valid keys.
-//   k_unique_scan   one block: tile bases, num_unique, num_valid, seg_off[U].
-//   k_unique_write  unique[u], seg_off[u], inverse[perm[k]].
-//   k_unique_counts counts[u] = seg_off[u+1] - seg_off[u].
+//   k_chunk_heads   run heads per reduction chunk (ballot), and the number of
+//                   valid (in-range) occurrences.
+//   k_chunk_scan    one block: exclusive scan of the chunk head counts, giving
+//                   the unique index of each chunk's first run; num_unique and
+//                   seg_off[num_unique].
+// The reduction kernel that follows walks the sorted occurrences anyway and
+// writes unique[u], seg_off[u] and inverse[perm[k]] on the way; counts[u] =
+// seg_off[u+1] - seg_off[u] (k_unique_counts) closes the stage.
 #include "embtab_internal.hpp"
 
 namespace embtab {
@@ -62,12 +67,19 @@ __global__ __launch_bounds__(256) void k_keys(const int64_t* __restrict__ offset
                                               uint32_t* __restrict__ flags,
                                               uint32_t* __restrict__ misc, int64_t B, int32_t T,
                                               int64_t nnz, uint32_t sentinel, int32_t mean) {
-  if (blockIdx.x == 0 && threadIdx.x < 64) misc[threadIdx.x] = 0u;
   const int64_t nbags = B * (int64_t)T;
   const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  int64_t o0 = 0, o1 = 1;
+  if (b < nbags) {
+    o0 = offsets[b];
+    o1 = offsets[b + 1];
+  }
+  {
+    const uint64_t mm = __ballot(o1 - o0 != 1);
+    if ((threadIdx.x & 63u) == 0u && mm != 0ull) atomicOr(&misc[kMiscNotOneHot], 1u);
+  }
   if (b >= nbags) return;
   const int64_t t = b / B, s = b - t * B;
-  int64_t o0 = offsets[b], o1 = offsets[b + 1];
   uint32_t bad = 0;
   if ((b == 0 && o0 != 0) || (b == nbags - 1 && o1 != nnz) || o1 < o0 || o0 < 0 || o1 > nnz)
     bad |= EMB_FLAG_BAD_OFFSETS;
@@ -253,100 +265,94 @@ __global__ __launch_bounds__(256) void k_sort_scatter(
   }
 }
 
-__global__ __launch_bounds__(256) void k_unique_count(const uint32_t* __restrict__ keys, uint32_t n,
-                                                      uint32_t sentinel,
-                                                      uint32_t* __restrict__ ucnt,
-                                                      uint32_t* __restrict__ vcnt) {
-  __shared__ uint32_t lds4[4];
-  const uint32_t tbase = blockIdx.x * (uint32_t)kSortTile;
-  uint32_t heads = 0, valid = 0;
-  for (int r = 0; r < kSortItems; ++r) {
-    const uint32_t k = tbase + r * 256 + threadIdx.x;
-    if (k < n) {
-      const uint32_t key = keys[k];
-      if (key < sentinel) {
-        ++valid;
-        if (k == 0 || keys[k - 1] != key) ++heads;
-      }
+template <int CH>
+__global__ __launch_bounds__(256) void k_chunk_heads(const uint32_t* __restrict__ keys, uint32_t n,
+                                                     uint32_t sentinel,
+                                                     uint32_t* __restrict__ hc,
+                                                     uint32_t* __restrict__ misc) {
+  const uint32_t k = blockIdx.x * 256u + threadIdx.x;
+  bool head = false;
+  if (k < n) {
+    const uint32_t key = keys[k];
+    if (key < sentinel) {
+      head = (k == 0) || keys[k - 1] != key;
+      if (k + 1 == n || keys[k + 1] >= sentinel) misc[kMiscNumValid] = k + 1;
     }
   }
-  uint32_t th, tv;
-  block_excl_scan(heads, &th, lds4);
-  block_excl_scan(valid, &tv, lds4);
-  if (threadIdx.x == 0) {
-    ucnt[blockIdx.x] = th;
-    vcnt[blockIdx.x] = tv;
+  const uint64_t m = __ballot(head);
+  const uint32_t lane = threadIdx.x & 63u;
+  if ((lane % CH) == 0u && k < n) {
+    const uint64_t bits = CH == 64 ? m : (m >> lane) & ((1ull << CH) - 1ull);
+    hc[k / CH] = (uint32_t)__popcll(bits);
   }
 }
 
-__global__ __launch_bounds__(256) void k_unique_scan(uint32_t* __restrict__ ucnt,
-                                                     const uint32_t* __restrict__ vcnt,
-                                                     uint32_t ntiles, uint32_t* __restrict__ misc,
+// Exclusive scan of the chunk head counts in one block: each pass covers
+// 1024 threads x 32 consecutive counts, read and written with dwordx4 accesses.
+__global__ __launch_bounds__(1024) void k_chunk_scan(uint32_t* __restrict__ hc, uint32_t nchunks,
+                                                     uint32_t* __restrict__ misc,
                                                      uint32_t* __restrict__ seg_off) {
-  __shared__ uint32_t lds4[4];
-  uint32_t carry = 0, vsum = 0;
-  for (uint32_t base = 0; base < ntiles; base += 256) {
-    const uint32_t idx = base + threadIdx.x;
-    const uint32_t v = idx < ntiles ? ucnt[idx] : 0u;
-    const uint32_t vv = idx < ntiles ? vcnt[idx] : 0u;
-    uint32_t total, tv;
-    const uint32_t ex = block_excl_scan(v, &total, lds4);
-    block_excl_scan(vv, &tv, lds4);
-    if (idx < ntiles) ucnt[idx] = ex + carry;
+  constexpr uint32_t PER = 32;
+  __shared__ uint32_t wsum[16];
+  const uint32_t lane = threadIdx.x & 63u, w = threadIdx.x >> 6;
+  uint32_t carry = 0;
+  for (uint32_t base = 0; base < nchunks; base += 1024u * PER) {
+    const uint32_t lo = base + threadIdx.x * PER;
+    uint32_t v[PER];
+    if (lo + PER <= nchunks) {
+#pragma unroll
+      for (int q = 0; q < (int)PER / 4; ++q) {
+        const uint4 x = reinterpret_cast<const uint4*>(hc + lo)[q];
+        v[4 * q] = x.x;
+        v[4 * q + 1] = x.y;
+        v[4 * q + 2] = x.z;
+        v[4 * q + 3] = x.w;
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < (int)PER; ++q) v[q] = lo + q < nchunks ? hc[lo + q] : 0u;
+    }
+    uint32_t sum = 0;
+#pragma unroll
+    for (int q = 0; q < (int)PER; ++q) sum += v[q];
+    uint32_t x = sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t y = (uint32_t)__shfl_up((int)x, o, 64);
+      if (lane >= (uint32_t)o) x += y;
+    }
+    if (lane == 63u) wsum[w] = x;
+    __syncthreads();
+    uint32_t before = 0, total = 0;
+#pragma unroll
+    for (uint32_t i = 0; i < 16u; ++i) {
+      before += i < w ? wsum[i] : 0u;
+      total += wsum[i];
+    }
+    __syncthreads();
+    uint32_t run = carry + before + x - sum;
+#pragma unroll
+    for (int q = 0; q < (int)PER; ++q) {
+      const uint32_t c = v[q];
+      v[q] = run;
+      run += c;
+    }
+    if (lo + PER <= nchunks) {
+#pragma unroll
+      for (int q = 0; q < (int)PER / 4; ++q)
+        reinterpret_cast<uint4*>(hc + lo)[q] = make_uint4(v[4 * q], v[4 * q + 1], v[4 * q + 2],
+                                                          v[4 * q + 3]);
+    } else {
+#pragma unroll
+      for (int q = 0; q < (int)PER; ++q)
+        if (lo + q < nchunks) hc[lo + q] = v[q];
+    }
     carry += total;
-    vsum += tv;
   }
   if (threadIdx.x == 0) {
+    hc[nchunks] = carry;
     misc[kMiscNumUnique] = carry;
-    misc[kMiscNumValid] = vsum;
-    seg_off[carry] = vsum;
-  }
-}
-
-__global__ __launch_bounds__(256) void k_unique_write(const uint32_t* __restrict__ keys,
-                                                      const uint32_t* __restrict__ vals,
-                                                      uint32_t n, uint32_t sentinel,
-                                                      const uint32_t* __restrict__ ubase,
-                                                      uint32_t* __restrict__ unique,
-                                                      uint32_t* __restrict__ seg_off,
-                                                      uint32_t* __restrict__ inverse) {
-  __shared__ uint32_t sk[kSortTile + 1];
-  __shared__ uint32_t lds4[4];
-  const uint32_t tbase = blockIdx.x * (uint32_t)kSortTile;
-  const uint32_t tn = (n - tbase) < (uint32_t)kSortTile ? (n - tbase) : (uint32_t)kSortTile;
-  for (uint32_t i = threadIdx.x; i < tn; i += 256) sk[i + 1] = keys[tbase + i];
-  if (threadIdx.x == 0) sk[0] = tbase > 0 ? keys[tbase - 1] : kNoRow;
-  __syncthreads();
-  // Thread i owns positions i*16 .. i*16+15 of the tile.
-  const uint32_t p0 = threadIdx.x * kSortItems;
-  uint32_t heads = 0;
-#pragma unroll
-  for (int r = 0; r < kSortItems; ++r) {
-    const uint32_t p = p0 + r;
-    if (p < tn) {
-      const uint32_t key = sk[p + 1];
-      heads += (key < sentinel && (tbase + p == 0 || sk[p] != key)) ? 1u : 0u;
-    }
-  }
-  uint32_t u = ubase[blockIdx.x] + block_excl_scan(heads, nullptr, lds4);
-  // u is now the unique index of the first head among this thread's positions.
-#pragma unroll
-  for (int r = 0; r < kSortItems; ++r) {
-    const uint32_t p = p0 + r;
-    if (p < tn) {
-      const uint32_t key = sk[p + 1];
-      const uint32_t j = vals[tbase + p];
-      if (key < sentinel) {
-        if (tbase + p == 0 || sk[p] != key) {
-          unique[u] = key;
-          seg_off[u] = tbase + p;
-          ++u;
-        }
-        if (j < n) inverse[j] = u - 1u;
-      } else if (j < n) {
-        inverse[j] = kNoRow;
-      }
-    }
+    seg_off[carry] = misc[kMiscNumValid];
   }
 }
 
@@ -383,21 +389,19 @@ hipError_t launch_sort_unique(const Handle& h, const Plan& p, const int64_t* off
   float* scale = reinterpret_cast<float*>(ws + p.scale);
   uint32_t* tile_hist = reinterpret_cast<uint32_t*>(ws + p.tile_hist);
   uint32_t* digit_tot = reinterpret_cast<uint32_t*>(ws + p.digit_tot);
-  uint32_t* unique = reinterpret_cast<uint32_t*>(ws + p.unique);
   uint32_t* seg_off = reinterpret_cast<uint32_t*>(ws + p.seg_off);
-  uint32_t* counts = reinterpret_cast<uint32_t*>(ws + p.counts);
-  uint32_t* inverse = reinterpret_cast<uint32_t*>(ws + p.inverse);
-  uint32_t* ucnt = reinterpret_cast<uint32_t*>(ws + p.ucnt);
-  uint32_t* vcnt = reinterpret_cast<uint32_t*>(ws + p.vcnt);
+  uint32_t* cbase = reinterpret_cast<uint32_t*>(ws + p.chunk_base);
 
   const int64_t nbags = p.B * (int64_t)h.T;
   const unsigned kgrid = (unsigned)((nbags + 255) / 256);
   phase_mark(h, EMB_PHASE_KEYS, false, s);
+  hipError_t e = launch_zero_words(misc, 64 + 2 * h.T, s);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_keys, dim3(kgrid > 0 ? kgrid : 1), dim3(256), 0, s, offsets, ids,
                      h.sv.row_off, h.sv.rows, kA, vA, gr, scale, h.sv.flags, misc, p.B, h.T,
                      p.nnz, sentinel, mean ? 1 : 0);
   phase_mark(h, EMB_PHASE_KEYS, true, s);
-  hipError_t e = hipGetLastError();
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   const uint32_t ntiles = (uint32_t)p.ntiles;
   uint32_t* kin = kA;
@@ -425,19 +429,31 @@ hipError_t launch_sort_unique(const Handle& h, const Plan& p, const int64_t* off
   }
   phase_mark(h, EMB_PHASE_SORT, true, s);
   phase_mark(h, EMB_PHASE_UNIQUE, false, s);
+  const uint32_t nchunks = (uint32_t)p.nchunks;
   if (n > 0) {
-    hipLaunchKernelGGL(k_unique_count, dim3(ntiles), dim3(256), 0, s, kin, n, sentinel, ucnt, vcnt);
+    const unsigned hgrid = (unsigned)((n + 255) / 256);
+    if (p.chunk == 64)
+      hipLaunchKernelGGL((k_chunk_heads<64>), dim3(hgrid), dim3(256), 0, s, kin, n, sentinel,
+                         cbase, misc);
+    else
+      hipLaunchKernelGGL((k_chunk_heads<32>), dim3(hgrid), dim3(256), 0, s, kin, n, sentinel,
+                         cbase, misc);
   }
-  hipLaunchKernelGGL(k_unique_scan, dim3(1), dim3(256), 0, s, ucnt, vcnt, ntiles, misc, seg_off);
-  if (n > 0) {
-    hipLaunchKernelGGL(k_unique_write, dim3(ntiles), dim3(256), 0, s, kin, vin, n, sentinel, ucnt,
-                       unique, seg_off, inverse);
-    const unsigned cgrid = (unsigned)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096);
-    hipLaunchKernelGGL(k_unique_counts, dim3(cgrid), dim3(256), 0, s, seg_off, misc, counts, n);
-  }
+  hipLaunchKernelGGL(k_chunk_scan, dim3(1), dim3(1024), 0, s, cbase, nchunks, misc, seg_off);
   phase_mark(h, EMB_PHASE_UNIQUE, true, s);
   *sorted_keys = kin;
   *sorted_vals = vin;
+  return hipGetLastError();
+}
+
+hipError_t launch_unique_counts(const Plan& p, char* ws, hipStream_t s) {
+  const uint32_t n = (uint32_t)p.nnz;
+  if (n == 0) return hipSuccess;
+  const uint32_t* misc = reinterpret_cast<const uint32_t*>(ws + p.misc);
+  const uint32_t* seg_off = reinterpret_cast<const uint32_t*>(ws + p.seg_off);
+  uint32_t* counts = reinterpret_cast<uint32_t*>(ws + p.counts);
+  const unsigned cgrid = (unsigned)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096);
+  hipLaunchKernelGGL(k_unique_counts, dim3(cgrid), dim3(256), 0, s, seg_off, misc, counts, n);
   return hipGetLastError();
 }
 

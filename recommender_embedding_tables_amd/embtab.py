@@ -40,7 +40,7 @@ EXPORTED = [
     "emb_table_destroy", "emb_hash_find_or_insert", "emb_bag_forward",
     "emb_bag_backward_adagrad", "emb_status_sync", "emb_hash_n_live", "emb_hash_export",
     "emb_debug_sort_unique", "emb_status_string", "emb_set_phase_events", "emb_bag_prepare",
-    "emb_bag_backward_adagrad_prepared",
+    "emb_bag_backward_adagrad_prepared", "emb_bag_forward_prepared",
 ]
 
 EMB_PHASE_FORWARD, EMB_PHASE_KEYS, EMB_PHASE_SORT, EMB_PHASE_UNIQUE = 0, 1, 2, 3
@@ -101,6 +101,7 @@ def _load():
         "emb_status_string": (C.c_char_p, [i32]),
         "emb_set_phase_events": (i32, [P, P]),
         "emb_bag_prepare": (i32, [P, P, P, i64, i64, i32, P, sz, P]),
+        "emb_bag_forward_prepared": (i32, [P, P, P, i64, i64, i32, P, P, sz, P]),
         "emb_bag_backward_adagrad_prepared": (i32, [P, i64, i64, i32, P, f32, f32, P, sz, P]),
     }
     for name, (res, args) in sig.items():
@@ -189,6 +190,12 @@ def emb_bag_backward_adagrad(handle, offsets, ids, batch, nnz, pool, grad_out, l
 def emb_bag_prepare(handle, offsets, ids, batch, nnz, pool, ws, ws_bytes, stream=None) -> int:
     return _lib.emb_bag_prepare(handle, _ptr(offsets), _ptr(ids), batch, nnz, pool, _ptr(ws),
                                 ws_bytes, _stream(stream))
+
+
+def emb_bag_forward_prepared(handle, offsets, ids, batch, nnz, pool, out, ws, ws_bytes,
+                             stream=None) -> int:
+    return _lib.emb_bag_forward_prepared(handle, _ptr(offsets), _ptr(ids), batch, nnz, pool,
+                                         _ptr(out), _ptr(ws), ws_bytes, _stream(stream))
 
 
 def emb_bag_backward_adagrad_prepared(handle, batch, nnz, pool, grad_out, lr, eps, ws, ws_bytes,

@@ -120,6 +120,10 @@ def test_host_checks_on_attached_handle():
                                                     ws, 0) == eb.EMB_ERR_INVALID_ARG
         assert eb.emb_bag_backward_adagrad_prepared(h, 4096, 10000, 0, fake, 0.01, float("inf"),
                                                     fake, ws, 0) == eb.EMB_ERR_INVALID_ARG
+        assert eb.emb_bag_forward_prepared(h, fake, fake, 4096, 10000, 0, fake, fake, ws - 1,
+                                           0) == eb.EMB_ERR_WORKSPACE
+        assert eb.emb_bag_forward_prepared(h, fake, fake, 4096, 10000, 0, None, fake, ws,
+                                           0) == eb.EMB_ERR_INVALID_ARG
         # hash calls on a dense handle
         assert eb.emb_hash_find_or_insert(h, fake, fake, 4096, 10000, fake, fake, ws,
                                           0) == eb.EMB_ERR_UNSUPPORTED

@@ -443,3 +443,56 @@ def test_prepared_backward_on_side_stream_matches_oracle():
         o.backward_adagrad(offsets, ids, w.B, True, grad, w.lr, w.eps)
         check_rows(tabs, o, offsets, ids, w.B, True, grad, w.lr, w.eps)
     assert status(tabs) == (eb.EMB_OK, 0)
+
+
+@pytest.mark.parametrize("case", ["one_hot", "one_hot_oor", "multi_hot", "with_empty"])
+def test_forward_prepared_matches_oracle(case):
+    if case.startswith("one_hot"):
+        w = synth.workload(2, T=4, B=7000, rows=[50, 9000, 1_000_000, 3])
+        mean = False
+    else:
+        w = synth.workload(3, T=2, B=3000)
+        mean = True
+    offsets, ids = synth.gen_batch(w)
+    if case == "one_hot_oor":
+        ids = ids.copy()
+        ids[::97] = -5
+    if case == "with_empty":
+        lens = np.diff(offsets)
+        lens[::5] = 0
+        offsets = np.concatenate([[0], np.cumsum(lens)])
+        ids = ids[:offsets[-1]]
+    tabs, o = make_pair(w.rows, w.D, seed=31)
+    d_off, d_ids = _t(offsets), _t(ids)
+    ws, need = tabs.workspace(w.B, ids.size)
+    pool = eb.EMB_POOL_MEAN if mean else eb.EMB_POOL_SUM
+    eb.check(eb.emb_bag_prepare(tabs.handle, d_off, d_ids, w.B, ids.size, pool, ws, need),
+             "prepare")
+    out = torch.full((w.B, w.T, w.D), float("nan"), dtype=torch.float32, device=DEV)
+    eb.check(eb.emb_bag_forward_prepared(tabs.handle, d_off, d_ids, w.B, ids.size, pool, out, ws,
+                                         need), "forward_prepared")
+    torch.cuda.synchronize()
+    ref, fl = o.forward(offsets, ids, w.B, mean)
+    if case.startswith("one_hot"):
+        np.testing.assert_array_equal(out.cpu().numpy(), ref)  # a copy of one row, or 0
+    else:
+        S = forward_S(offsets, ids, w.B, o.rows, lambda r: o.read_rows(r)[0], mean, w.D)
+        assert_within(out.cpu().numpy(), ref, S, "forward_prepared")
+    # the prepared workspace then drives the backward
+    grad = synth.gen_grad(w)
+    eb.check(eb.emb_bag_backward_adagrad_prepared(tabs.handle, w.B, ids.size, pool, _t(grad), w.lr,
+                                                  w.eps, ws, need), "backward_prepared")
+    o.backward_adagrad(offsets, ids, w.B, mean, grad, w.lr, w.eps)
+    torch.cuda.synchronize()
+    check_rows(tabs, o, offsets, ids, w.B, mean, grad, w.lr, w.eps)
+
+
+def test_debug_export_leaves_tables_untouched():
+    w = synth.workload(3, T=2, B=2000)
+    offsets, ids = synth.gen_batch(w)
+    tabs, o = make_pair(w.rows, w.D, seed=2)
+    W0 = tabs.weights.clone()
+    G0 = tabs.accum.clone()
+    check_sort_unique(tabs, o, offsets, ids, w.B)
+    torch.cuda.synchronize()
+    assert torch.equal(W0, tabs.weights) and torch.equal(G0, tabs.accum)
