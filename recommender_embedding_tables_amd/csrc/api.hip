@@ -62,6 +62,8 @@ bool make_plan(const Handle& h, int64_t B, int64_t nnz, Plan* p) {
   p->valsB = take(n4);
   p->gr = take(n4);
   p->scale = take(n4);
+  p->sgr = take(n4);
+  p->sscale = take(n4);
   p->tile_hist = take(sizeof(uint32_t) * kMaxRadix * nt);
   p->digit_tot = take(sizeof(uint32_t) * kMaxRadix);
   p->unique = take(n4);

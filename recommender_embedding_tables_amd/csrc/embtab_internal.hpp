@@ -105,6 +105,7 @@ struct Plan {
   int64_t nchunks = 0;  // reduction chunks
   int chunk = 0;
   size_t keysA, valsA, keysB, valsB, gr, scale;
+  size_t sgr, sscale;  // grad row and mean scale of each sorted occurrence
   size_t tile_hist, digit_tot;
   size_t unique, seg_off, counts, inverse;
   size_t ucnt, vcnt;
@@ -150,6 +151,15 @@ __device__ inline f4 load4_or_zero(const float* __restrict__ base, size_t row, u
                                    uint32_t d4, bool ok) {
   const size_t off = ok ? row * D + 4u * d4 : 0u;
   const f4 x = *reinterpret_cast<const f4*>(base + off);
+  return ok ? x : f4{0.f, 0.f, 0.f, 0.f};
+}
+
+// Same, with a non-temporal load (data read once: keep it out of the way of
+// rows that are reused).
+__device__ inline f4 load4_nt_or_zero(const float* __restrict__ base, size_t row, uint32_t D,
+                                      uint32_t d4, bool ok) {
+  const size_t off = ok ? row * D + 4u * d4 : 0u;
+  const f4 x = __builtin_nontemporal_load(reinterpret_cast<const f4*>(base + off));
   return ok ? x : f4{0.f, 0.f, 0.f, 0.f};
 }
 

@@ -238,8 +238,8 @@ __global__ __launch_bounds__(256) void k_fwd_sorted(
     mgr[i] = nbags;
     if (k < n) {
       mkey[i] = keys[k];
-      const uint32_t j = perm[k];
-      mgr[i] = j < n ? gr[j] : nbags;
+      const uint32_t g = gr[k];  // grad row (= output row) of sorted position k
+      mgr[i] = g < nbags ? g : nbags;
     }
   }
   uint32_t prevkey = kNoRow;
@@ -353,7 +353,7 @@ hipError_t launch_sorted_t(const Handle& h, const Plan& p, const uint32_t* keys,
   const int64_t grid = (chunks + SGPB - 1) / SGPB;
   if (grid == 0) return hipSuccess;
   hipLaunchKernelGGL((k_fwd_sorted<SG, VEC, MPL>), dim3((unsigned)grid), dim3(256), 0, s, keys,
-                     perm, reinterpret_cast<const uint32_t*>(ws + p.gr), h.W, out,
+                     perm, reinterpret_cast<const uint32_t*>(ws + p.sgr), h.W, out,
                      (uint32_t)p.nnz, (uint32_t)h.total_rows, (uint32_t)h.D,
                      (uint32_t)(p.B * h.T), reinterpret_cast<const uint32_t*>(ws + p.misc));
   return hipGetLastError();

@@ -48,7 +48,7 @@ __device__ inline void adagrad_step(f4& w, f4& g2, const f4 g, float lr, float e
 template <int SG, int VEC, bool MEAN, int MPL, int UF, bool UPDATE>
 __global__ __launch_bounds__(256) void k_seg_adagrad(
     const uint32_t* __restrict__ keys, const uint32_t* __restrict__ perm,
-    const uint32_t* __restrict__ gr, const float* __restrict__ scale,
+    const uint32_t* __restrict__ sgr, const float* __restrict__ sscale,
     const float* __restrict__ grad, float* __restrict__ W, float* __restrict__ G, uint32_t n,
     uint32_t sentinel, int32_t D, float lr, float eps, float* __restrict__ part_head,
     float* __restrict__ part_tail, uint32_t* __restrict__ span_list,
@@ -82,22 +82,23 @@ __global__ __launch_bounds__(256) void k_seg_adagrad(
 #pragma unroll
   for (int i = 0; i < MPL; ++i) {
     const uint32_t k = k0 + i * SG + lane;
-    if (k < k1 && mkey[i] < sentinel) {
-      // Positions not written by any bag (offsets that do not tile [0, nnz))
-      // may hold stale values: such an occurrence is dropped, never followed.
+    if (k < k1) {
+      // grad row and scale were gathered into sorted order by the last sort
+      // pass.  Positions not written by any bag (offsets that do not tile
+      // [0, nnz)) may hold stale values: such an occurrence is dropped.
       const uint32_t j = perm[k];
-      const uint32_t g = j < n ? gr[j] : nbags;
-      if (g < nbags) {
-        mj[i] = j;
-        mgr[i] = g;
-        if (MEAN && UPDATE) msc[i] = scale[j];
-      } else {
-        mkey[i] = sentinel;
+      const uint32_t g = sgr[k];
+      if (mkey[i] < sentinel) {
+        if (j < n && g < nbags) {
+          mj[i] = j;
+          mgr[i] = g;
+          if (MEAN && UPDATE) msc[i] = sscale[k];
+        } else {
+          mkey[i] = sentinel;
+        }
+      } else if (j < n) {
+        inverse[j] = kNoRow;  // an out-of-range occurrence belongs to no unique row
       }
-    } else if (k < k1) {
-      // an out-of-range occurrence (sentinel key) belongs to no unique row
-      const uint32_t j = perm[k];
-      if (j < n) inverse[j] = kNoRow;
     }
   }
 
@@ -149,7 +150,7 @@ __global__ __launch_bounds__(256) void k_seg_adagrad(
           for (int v = 0; v < VEC; ++v) {
             const uint32_t d4 = (uint32_t)(lane + v * SG);
             const bool own = endf[u] && !startb[u] && d4 < (uint32_t)D4;
-            g[u][v] = load4_or_zero(grad, gg[u], (uint32_t)D, d4, vld[u] && d4 < (uint32_t)D4);
+            g[u][v] = load4_nt_or_zero(grad, gg[u], (uint32_t)D, d4, vld[u] && d4 < (uint32_t)D4);
             wv[u][v] = load4_or_zero(W, kk[u], (uint32_t)D, d4, own);
             gv[u][v] = load4_or_zero(G, kk[u], (uint32_t)D, d4, own);
           }
@@ -364,8 +365,8 @@ hipError_t launch_t(const Handle& h, const Plan& p, const uint32_t* keys, const 
   if (n == 0) return hipSuccess;
   const int64_t chunks = (p.nnz + SG * MPL - 1) / (SG * MPL);
   const int64_t grid = (chunks + SGPB - 1) / SGPB;
-  uint32_t* gr = reinterpret_cast<uint32_t*>(ws + p.gr);
-  float* scale = reinterpret_cast<float*>(ws + p.scale);
+  uint32_t* gr = reinterpret_cast<uint32_t*>(ws + p.sgr);
+  float* scale = reinterpret_cast<float*>(ws + p.sscale);
   float* ph = reinterpret_cast<float*>(ws + p.part_head);
   float* pt = reinterpret_cast<float*>(ws + p.part_tail);
   uint32_t* spans = reinterpret_cast<uint32_t*>(ws + p.span_list);

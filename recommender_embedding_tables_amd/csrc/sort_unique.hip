@@ -173,11 +173,16 @@ __global__ __launch_bounds__(256) void k_sort_scan(uint32_t* __restrict__ tile_h
   if (threadIdx.x == 0) digit_tot[blockIdx.x] = carry;
 }
 
+// In the last pass (gr_in != nullptr) the scatter also gathers each
+// occurrence's grad row (and mean scale) into sorted order, so the consumers
+// of the sort read them with coalesced loads; a stale occurrence index gets the
+// invalid grad row 0xFFFFFFFF.
 __global__ __launch_bounds__(256) void k_sort_scatter(
     const uint32_t* __restrict__ keys_in, const uint32_t* __restrict__ vals_in,
     uint32_t* __restrict__ keys_out, uint32_t* __restrict__ vals_out, uint32_t n, int shift,
     int nbits, const uint32_t* __restrict__ tile_off, const uint32_t* __restrict__ digit_tot,
-    uint32_t ntiles) {
+    uint32_t ntiles, const uint32_t* __restrict__ gr_in, const float* __restrict__ sc_in,
+    uint32_t* __restrict__ gr_out, float* __restrict__ sc_out) {
   __shared__ uint32_t whist[4][kMaxRadix];
   __shared__ uint32_t dstart[kMaxRadix];
   __shared__ uint32_t gbase[kMaxRadix];
@@ -260,8 +265,13 @@ __global__ __launch_bounds__(256) void k_sort_scatter(
     const uint32_t k = skeys[i];
     const uint32_t d = (k >> shift) & mask;
     const uint32_t g = gbase[d] + (i - dstart[d]);
+    const uint32_t v = svals[i];
     keys_out[g] = k;
-    vals_out[g] = svals[i];
+    vals_out[g] = v;
+    if (gr_in) {
+      gr_out[g] = v < n ? gr_in[v] : 0xFFFFFFFFu;
+      if (sc_in) sc_out[g] = v < n ? sc_in[v] : 0.0f;
+    }
   }
 }
 
@@ -415,8 +425,12 @@ hipError_t launch_sort_unique(const Handle& h, const Plan& p, const int64_t* off
       hipLaunchKernelGGL(k_sort_hist, dim3(ntiles), dim3(256), 0, s, kin, n, p.shift[pass],
                          p.dbits[pass], tile_hist, ntiles);
       hipLaunchKernelGGL(k_sort_scan, dim3(radix), dim3(256), 0, s, tile_hist, ntiles, digit_tot);
+      const bool last = pass + 1 == p.passes;
       hipLaunchKernelGGL(k_sort_scatter, dim3(ntiles), dim3(256), 0, s, kin, vin, kout, vout, n,
-                         p.shift[pass], p.dbits[pass], tile_hist, digit_tot, ntiles);
+                         p.shift[pass], p.dbits[pass], tile_hist, digit_tot, ntiles,
+                         last ? gr : nullptr, (last && mean) ? scale : nullptr,
+                         reinterpret_cast<uint32_t*>(ws + p.sgr),
+                         reinterpret_cast<float*>(ws + p.sscale));
       e = hipGetLastError();
       if (e != hipSuccess) return e;
       uint32_t* tk = kin;
