@@ -47,25 +47,35 @@ def occurrence_rows(offsets, ids, B, rows):
 def abs_grad_sums(offsets, ids, B, rows, grad, pool_mean, D):
     """For every touched global row: sum_k c_k |grad_k| (float64 [U, D]) and the rows."""
     _, grow, gr, sc, valid = occurrence_rows(offsets, ids, B, rows)
-    c = sc if pool_mean else np.ones_like(sc)
-    g = np.abs(grad.reshape(-1, D)[gr[valid]].astype(np.float64)) * c[valid, None]
     r = grow[valid]
     order = np.argsort(r, kind="stable")
     r = r[order]
-    g = g[order]
+    g = np.abs(grad.reshape(-1, D)[gr[valid][order]])
+    if pool_mean:
+        g = g * sc[valid][order, None].astype(np.float32)
     uniq, start = np.unique(r, return_index=True)
-    sums = np.add.reduceat(g, start, axis=0) if r.size else np.zeros((0, D))
+    sums = np.add.reduceat(g.astype(np.float64), start, axis=0) if r.size else np.zeros((0, D))
     return uniq, sums
 
 
 def forward_S(offsets, ids, B, rows, W_rows_of, pool_mean, D):
-    """S for every pooled output: c_b * sum |W[row_j]| ([B, T, D]); W_rows_of(grows)->values."""
+    """S for every pooled output: c_b * sum |W[row_j]| ([B, T, D]); W_rows_of(grows)->values.
+
+    Occurrences are in CSR order, so each bag's terms are one contiguous run.
+    """
     rows = np.asarray(rows, np.int64)
     T = rows.size
     t, grow, gr, sc, valid = occurrence_rows(offsets, ids, B, rows)
-    S = np.zeros((B * T, D), np.float64)
-    vals = np.abs(W_rows_of(grow[valid]).astype(np.float64))
+    vals = np.zeros((ids.size, D), np.float32)
+    if valid.any():
+        vals[valid] = np.abs(W_rows_of(grow[valid]))
+    lens = np.diff(offsets)
+    nonempty = lens > 0
+    S_bag = np.zeros((T * B, D), np.float64)
+    if ids.size:
+        sums = np.add.reduceat(vals.astype(np.float64), offsets[:-1][nonempty], axis=0)
+        S_bag[nonempty] = sums
     if pool_mean:
-        vals = vals * sc[valid, None]
-    np.add.at(S, gr[valid], vals)
-    return S.reshape(B, T, D)
+        S_bag[nonempty] /= lens[nonempty, None]
+    # table-major bags -> [B, T, D]
+    return S_bag.reshape(T, B, D).transpose(1, 0, 2)
