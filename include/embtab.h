@@ -152,7 +152,7 @@ emb_status_t emb_bag_forward(emb_table_t h, const int64_t* offsets, const int64_
  * touched rows (Adagrad per the synthetic benchmarks of "Merlin Distributed
  * Embeddings", section "Performance"; textbook form of Duchi, Hazan and
  * Singer 2011):
- *   rows_j = off_t + ids[j]; stable sort by row; unique / inverse / counts;
+ *   rows_j = off_t + ids[j]; stable sort by row; unique rows and inverse;
  *   g_u = sum over occurrences j of row u of c_b(j) * grad_out[s(j), t(j), :]
  *   G_u += g_u * g_u;   W_u -= lr * g_u / (sqrt(G_u) + eps)       (per element)
  * Each touched row gets exactly one step however often it occurs; rows not in
@@ -165,8 +165,8 @@ emb_status_t emb_bag_backward_adagrad(emb_table_t h, const int64_t* offsets,
 
 /* The same backward split in two, so that the id-only stages can overlap the
  * forward gather (they need offsets and ids but not grad_out):
- *   emb_bag_prepare                    occurrence keys, stable sort, unique /
- *                                      inverse / counts, left in `ws`;
+ *   emb_bag_prepare                    occurrence keys, stable sort and run
+ *                                      heads (unique indexing), left in `ws`;
  *   emb_bag_backward_adagrad_prepared  segmented reduction + Adagrad from a
  *                                      workspace prepared for the same batch,
  *                                      nnz and pool (same semantics as
@@ -222,7 +222,7 @@ emb_status_t emb_debug_sort_unique(emb_table_t h, const int64_t* offsets, const 
  *   EMB_PHASE_FORWARD  the pooled-gather kernel of emb_bag_forward;
  *   EMB_PHASE_KEYS     occurrence keys of emb_bag_backward_adagrad;
  *   EMB_PHASE_SORT     all radix passes;
- *   EMB_PHASE_UNIQUE   unique / inverse / counts;
+ *   EMB_PHASE_UNIQUE   run heads and the unique index of each reduction chunk;
  *   EMB_PHASE_REDUCE   the fused segmented-reduction + Adagrad kernel;
  *   EMB_PHASE_FIXUP    the kernel finishing rows that span reduction chunks;
  *   EMB_PHASE_HASH     all of emb_hash_find_or_insert.

@@ -178,6 +178,15 @@ emb_status_t emb_table_create(const emb_table_desc_t* d, void* stream, emb_table
   h.hi = d->init_hi;
   h.stdv = d->init_std;
   h.accum0 = d->accum_init;
+  {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        cus > 0)
+      h.cus = cus;
+    else
+      (void)hipGetLastError();  // no device visible: keep the default
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
   if (d->init_storage) {
@@ -298,10 +307,12 @@ emb_status_t emb_bag_forward_prepared(emb_table_t t, const int64_t* offsets, con
   uint32_t *keys = nullptr, *vals = nullptr;
   sorted_arrays(p, w, &keys, &vals);
   phase_mark(t->h, EMB_PHASE_FORWARD, false, s);
-  hipError_t e = launch_forward_sorted(t->h, p, keys, vals, out, w, s);
-  if (e == hipSuccess)
-    e = launch_forward_bags(t->h, offsets, ids, batch, nnz, pool == EMB_POOL_MEAN, out,
-                            reinterpret_cast<const uint32_t*>(w + p.misc), s);
+  const bool mean = pool == EMB_POOL_MEAN;
+  // As many ids as bags may be one-hot (a device flag decides inside the
+  // launch); any other count is certainly not.
+  hipError_t e = nnz == batch * (int64_t)t->h.T
+                     ? launch_forward_sorted(t->h, p, offsets, ids, mean, keys, vals, out, w, s)
+                     : launch_forward_bags(t->h, offsets, ids, batch, nnz, mean, out, s);
   phase_mark(t->h, EMB_PHASE_FORWARD, true, s);
   return hip_status(e);
 }

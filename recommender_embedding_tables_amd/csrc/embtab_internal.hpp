@@ -68,6 +68,7 @@ struct Handle {
   float lo = 0, hi = 0, stdv = 0, accum0 = 0;
   bool timing = false;
   hipEvent_t events[2 * EMB_NUM_PHASES] = {};
+  int cus = 256;  // compute units of the device current at creation
 };
 
 // Measurement hook: events recorded around a phase when the caller set them.
@@ -124,6 +125,7 @@ enum : int {
   kMiscHashOverflow = 3,
   kMiscLongCount = 4,
   kMiscNotOneHot = 5,  // some bag of the prepared batch does not hold exactly one id
+  kMiscFixDone = 6,    // blocks of the span fixup that have finished
   kMiscHashNew = 8,  // uint32 per table from here (up to T)
 };
 
@@ -194,21 +196,21 @@ hipError_t launch_sort_unique(const Handle& h, const Plan& p, const int64_t* off
                               uint32_t** sorted_vals, hipStream_t s);
 
 // Segmented reduction + Adagrad over the sorted occurrences; on the way it
-// writes unique / seg_off / inverse / counts.  With grad_out == nullptr it only
-// writes those (W and G untouched).
+// writes unique / seg_off / inverse.  With grad_out == nullptr it only writes
+// those and counts (W and G untouched).
 hipError_t launch_segment_adagrad(const Handle& h, const Plan& p, const uint32_t* keys,
                                   const uint32_t* perm, bool mean, const float* grad_out,
                                   float lr, float eps, char* ws, hipStream_t s);
 
-// One-hot forward from a prepared workspace (rows gathered in sorted order);
-// the kernel leaves the batch to the bag kernel when it is not one-hot.
-hipError_t launch_forward_sorted(const Handle& h, const Plan& p, const uint32_t* keys,
+// Forward from a prepared workspace.  One-hot batches gather the rows in
+// sorted order; otherwise (a device flag of the prepare) the same launch runs
+// the pooled kernel.
+hipError_t launch_forward_sorted(const Handle& h, const Plan& p, const int64_t* offsets,
+                                 const int64_t* ids, bool mean, const uint32_t* keys,
                                  const uint32_t* perm, float* out, char* ws, hipStream_t s);
-// Bag forward that returns at once when `skip_if_onehot` (a prepared
-// workspace's misc words) says the sorted kernel owns the batch.
+// The pooled kernel alone (the ids and offsets are read directly).
 hipError_t launch_forward_bags(const Handle& h, const int64_t* offsets, const int64_t* ids,
-                               int64_t B, int64_t nnz, bool mean, float* out,
-                               const uint32_t* skip_if_onehot, hipStream_t s);
+                               int64_t B, int64_t nnz, bool mean, float* out, hipStream_t s);
 
 hipError_t launch_unique_counts(const Plan& p, char* ws, hipStream_t s);
 

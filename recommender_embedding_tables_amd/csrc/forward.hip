@@ -31,21 +31,28 @@ namespace {
 // then walk the tile in output order.
 constexpr int kFwdTileBags = 1024;
 
+// The staging arrays of one sample tile (LDS).
+struct BagTileLds {
+  uint32_t start[kFwdTileBags], len[kFwdTileBags], row[kFwdTileBags];
+};
+
+// Pools sample tile `tile` (samples tile*S .. tile*S + S - 1 of every table);
+// returns the EMB_FLAG_* bits it found.  Called by all 256 threads of a block.
 template <int SG, int VEC, bool MEAN, int UNR>
-__global__ __launch_bounds__(256) void k_bag_forward(
-    const int64_t* __restrict__ offsets, const int64_t* __restrict__ ids,
+__device__ __forceinline__ uint32_t bag_tile(
+    uint32_t tile, const int64_t* __restrict__ offsets, const int64_t* __restrict__ ids,
     const float* __restrict__ W, const int64_t* __restrict__ row_off,
-    const int64_t* __restrict__ rows, float* __restrict__ out, uint32_t* __restrict__ flags,
-    uint32_t B, uint32_t T, uint32_t D, uint32_t nnz, uint32_t S,
-    const uint32_t* __restrict__ skip) {
-  if (skip && skip[kMiscNotOneHot] == 0u) return;  // the sorted kernel owns this batch
+    const int64_t* __restrict__ rows, float* __restrict__ out, uint32_t B, uint32_t T,
+    uint32_t D, uint32_t nnz, uint32_t S, BagTileLds& lds) {
   constexpr int SGPB = 256 / SG;
-  __shared__ uint32_t s_start[kFwdTileBags], s_len[kFwdTileBags], s_row[kFwdTileBags];
+  uint32_t* s_start = lds.start;
+  uint32_t* s_len = lds.len;
+  uint32_t* s_row = lds.row;
   const uint32_t lane = threadIdx.x % SG;
   const uint32_t sgb = threadIdx.x / SG;
   const uint32_t nbags = B * T;
-  const uint32_t s0 = xcd_block() * S;
-  if (s0 >= B) return;
+  const uint32_t s0 = tile * S;
+  if (s0 >= B) return 0u;
   const uint32_t Sl = (B - s0) < S ? (B - s0) : S;
   const uint32_t ntile = Sl * T;  // bags of the tile; tile bag i = t * Sl + sl
   const uint32_t D4 = D >> 2;
@@ -207,6 +214,18 @@ __global__ __launch_bounds__(256) void k_bag_forward(
       }
     }
   }
+  return bad;
+}
+
+template <int SG, int VEC, bool MEAN, int UNR>
+__global__ __launch_bounds__(256) void k_bag_forward(
+    const int64_t* __restrict__ offsets, const int64_t* __restrict__ ids,
+    const float* __restrict__ W, const int64_t* __restrict__ row_off,
+    const int64_t* __restrict__ rows, float* __restrict__ out, uint32_t* __restrict__ flags,
+    uint32_t B, uint32_t T, uint32_t D, uint32_t nnz, uint32_t S) {
+  __shared__ BagTileLds lds;
+  const uint32_t bad = bag_tile<SG, VEC, MEAN, UNR>(xcd_block(), offsets, ids, W, row_off, rows,
+                                                    out, B, T, D, nnz, S, lds);
   if (bad) atomicOr(flags, bad);
 }
 
@@ -215,13 +234,26 @@ __global__ __launch_bounds__(256) void k_bag_forward(
 // occurrences, a Zipf-hot row is read once per chunk and then stored to each
 // of its bags, and W is visited in ascending address order.  Chunks and
 // sub-groups are those of the reduction kernel; MPL metadata entries per lane.
-template <int SG, int VEC, int MPL>
+//
+// Whether the batch is one-hot is known only on the device (a flag set while
+// the keys were built), so the same launch also holds the general pooled
+// kernel: when the flag is set, block i pools sample tile i instead.
+template <int SG, int VEC, int MPL, bool MEAN, int UNR>
 __global__ __launch_bounds__(256) void k_fwd_sorted(
     const uint32_t* __restrict__ keys, const uint32_t* __restrict__ perm,
     const uint32_t* __restrict__ gr, const float* __restrict__ W, float* __restrict__ out,
     uint32_t n, uint32_t sentinel, uint32_t D, uint32_t nbags,
-    const uint32_t* __restrict__ misc) {
-  if (misc[kMiscNotOneHot] != 0u) return;  // the bag kernel owns this batch
+    const uint32_t* __restrict__ misc, const int64_t* __restrict__ offsets,
+    const int64_t* __restrict__ ids, const int64_t* __restrict__ row_off,
+    const int64_t* __restrict__ rows, uint32_t* __restrict__ flags, uint32_t B, uint32_t T,
+    uint32_t S) {
+  if (misc[kMiscNotOneHot] != 0u) {
+    __shared__ BagTileLds lds;
+    const uint32_t bad = bag_tile<SG, VEC, MEAN, UNR>(xcd_block(), offsets, ids, W, row_off,
+                                                      rows, out, B, T, D, n, S, lds);
+    if (bad) atomicOr(flags, bad);
+    return;
+  }
   constexpr int CH = SG * MPL;
   constexpr int SGPB = 256 / SG;
   constexpr int UF = VEC > 1 ? 2 : (SG < 4 ? SG : 4);
@@ -290,37 +322,47 @@ __global__ __launch_bounds__(256) void k_fwd_sorted(
   }
 }
 
+// Samples per tile of the pooled kernel: about kFwdTileBags bags of all tables.
+int64_t tile_samples(int T) {
+  int64_t S = kFwdTileBags / T;
+  return S > 64 ? 64 : (S < 1 ? 1 : S);
+}
+
+template <int VEC>
+constexpr int fwd_unroll() {
+  return VEC == 1 ? 8 : (VEC == 2 ? 4 : 2);  // one-hot rows in flight per lane
+}
+
 template <int SG, int VEC, bool MEAN>
 hipError_t launch_t(const Handle& h, const int64_t* offsets, const int64_t* ids, int64_t B,
-                    int64_t nnz, float* out, const uint32_t* skip, hipStream_t s) {
-  constexpr int UNR = VEC == 1 ? 8 : (VEC == 2 ? 4 : 2);  // one-hot rows in flight
-  int64_t S = kFwdTileBags / h.T;
-  S = S > 64 ? 64 : (S < 1 ? 1 : S);
+                    int64_t nnz, float* out, hipStream_t s) {
+  const int64_t S = tile_samples(h.T);
   const int64_t grid = (B + S - 1) / S;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((k_bag_forward<SG, VEC, MEAN, UNR>), dim3((unsigned)grid), dim3(256), 0, s,
-                     offsets, ids, h.W, h.sv.row_off, h.sv.rows, out, h.sv.flags, (uint32_t)B,
-                     (uint32_t)h.T, (uint32_t)h.D, (uint32_t)nnz, (uint32_t)S, skip);
+  hipLaunchKernelGGL((k_bag_forward<SG, VEC, MEAN, fwd_unroll<VEC>()>), dim3((unsigned)grid),
+                     dim3(256), 0, s, offsets, ids, h.W, h.sv.row_off, h.sv.rows, out,
+                     h.sv.flags, (uint32_t)B, (uint32_t)h.T, (uint32_t)h.D, (uint32_t)nnz,
+                     (uint32_t)S);
   return hipGetLastError();
 }
 
 template <bool MEAN>
 hipError_t dispatch(const Handle& h, const int64_t* offsets, const int64_t* ids, int64_t B,
-                    int64_t nnz, float* out, const uint32_t* skip, hipStream_t s) {
+                    int64_t nnz, float* out, hipStream_t s) {
   const int sg = subgroup_lanes(h.D), vec = vec_per_lane(h.D);
   switch (sg) {
-    case 1: return launch_t<1, 1, MEAN>(h, offsets, ids, B, nnz, out, skip, s);
-    case 2: return launch_t<2, 1, MEAN>(h, offsets, ids, B, nnz, out, skip, s);
-    case 4: return launch_t<4, 1, MEAN>(h, offsets, ids, B, nnz, out, skip, s);
-    case 8: return launch_t<8, 1, MEAN>(h, offsets, ids, B, nnz, out, skip, s);
-    case 16: return launch_t<16, 1, MEAN>(h, offsets, ids, B, nnz, out, skip, s);
-    case 32: return launch_t<32, 1, MEAN>(h, offsets, ids, B, nnz, out, skip, s);
+    case 1: return launch_t<1, 1, MEAN>(h, offsets, ids, B, nnz, out, s);
+    case 2: return launch_t<2, 1, MEAN>(h, offsets, ids, B, nnz, out, s);
+    case 4: return launch_t<4, 1, MEAN>(h, offsets, ids, B, nnz, out, s);
+    case 8: return launch_t<8, 1, MEAN>(h, offsets, ids, B, nnz, out, s);
+    case 16: return launch_t<16, 1, MEAN>(h, offsets, ids, B, nnz, out, s);
+    case 32: return launch_t<32, 1, MEAN>(h, offsets, ids, B, nnz, out, s);
     default:
       switch (vec) {
-        case 1: return launch_t<64, 1, MEAN>(h, offsets, ids, B, nnz, out, skip, s);
-        case 2: return launch_t<64, 2, MEAN>(h, offsets, ids, B, nnz, out, skip, s);
-        case 3: return launch_t<64, 3, MEAN>(h, offsets, ids, B, nnz, out, skip, s);
-        default: return launch_t<64, 4, MEAN>(h, offsets, ids, B, nnz, out, skip, s);
+        case 1: return launch_t<64, 1, MEAN>(h, offsets, ids, B, nnz, out, s);
+        case 2: return launch_t<64, 2, MEAN>(h, offsets, ids, B, nnz, out, s);
+        case 3: return launch_t<64, 3, MEAN>(h, offsets, ids, B, nnz, out, s);
+        default: return launch_t<64, 4, MEAN>(h, offsets, ids, B, nnz, out, s);
       }
   }
 }
@@ -330,54 +372,71 @@ hipError_t dispatch(const Handle& h, const int64_t* offsets, const int64_t* ids,
 hipError_t launch_forward(const Handle& h, const int64_t* offsets, const int64_t* ids,
                           int64_t B, int64_t nnz, bool mean, float* out, hipStream_t s) {
   phase_mark(h, EMB_PHASE_FORWARD, false, s);
-  hipError_t e = mean ? dispatch<true>(h, offsets, ids, B, nnz, out, nullptr, s)
-                      : dispatch<false>(h, offsets, ids, B, nnz, out, nullptr, s);
+  hipError_t e = mean ? dispatch<true>(h, offsets, ids, B, nnz, out, s)
+                      : dispatch<false>(h, offsets, ids, B, nnz, out, s);
   phase_mark(h, EMB_PHASE_FORWARD, true, s);
   return e;
 }
 
 hipError_t launch_forward_bags(const Handle& h, const int64_t* offsets, const int64_t* ids,
-                               int64_t B, int64_t nnz, bool mean, float* out,
-                               const uint32_t* skip_if_onehot, hipStream_t s) {
-  return mean ? dispatch<true>(h, offsets, ids, B, nnz, out, skip_if_onehot, s)
-              : dispatch<false>(h, offsets, ids, B, nnz, out, skip_if_onehot, s);
+                               int64_t B, int64_t nnz, bool mean, float* out, hipStream_t s) {
+  return mean ? dispatch<true>(h, offsets, ids, B, nnz, out, s)
+              : dispatch<false>(h, offsets, ids, B, nnz, out, s);
 }
 
 namespace {
-template <int SG, int VEC>
-hipError_t launch_sorted_t(const Handle& h, const Plan& p, const uint32_t* keys,
-                           const uint32_t* perm, float* out, char* ws, hipStream_t s) {
+template <int SG, int VEC, bool MEAN>
+hipError_t launch_sorted_t(const Handle& h, const Plan& p, const int64_t* offsets,
+                           const int64_t* ids, const uint32_t* keys, const uint32_t* perm,
+                           float* out, char* ws, hipStream_t s) {
   constexpr int MPL = SG >= 32 ? 1 : 32 / SG;
   constexpr int SGPB = 256 / SG;
   const int64_t chunks = (p.nnz + SG * MPL - 1) / (SG * MPL);
-  const int64_t grid = (chunks + SGPB - 1) / SGPB;
+  const int64_t S = tile_samples(h.T);
+  const int64_t tiles = (p.B + S - 1) / S;
+  int64_t grid = (chunks + SGPB - 1) / SGPB;
+  grid = grid > tiles ? grid : tiles;  // enough blocks for either path
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((k_fwd_sorted<SG, VEC, MPL>), dim3((unsigned)grid), dim3(256), 0, s, keys,
-                     perm, reinterpret_cast<const uint32_t*>(ws + p.sgr), h.W, out,
-                     (uint32_t)p.nnz, (uint32_t)h.total_rows, (uint32_t)h.D,
-                     (uint32_t)(p.B * h.T), reinterpret_cast<const uint32_t*>(ws + p.misc));
+  hipLaunchKernelGGL((k_fwd_sorted<SG, VEC, MPL, MEAN, fwd_unroll<VEC>()>), dim3((unsigned)grid),
+                     dim3(256), 0, s, keys, perm,
+                     reinterpret_cast<const uint32_t*>(ws + p.sgr), h.W, out, (uint32_t)p.nnz,
+                     (uint32_t)h.total_rows, (uint32_t)h.D, (uint32_t)(p.B * h.T),
+                     reinterpret_cast<const uint32_t*>(ws + p.misc), offsets, ids, h.sv.row_off,
+                     h.sv.rows, h.sv.flags, (uint32_t)p.B, (uint32_t)h.T, (uint32_t)S);
   return hipGetLastError();
+}
+
+template <bool MEAN>
+hipError_t dispatch_sorted(const Handle& h, const Plan& p, const int64_t* offsets,
+                           const int64_t* ids, const uint32_t* keys, const uint32_t* perm,
+                           float* out, char* ws, hipStream_t s) {
+  const int sg = subgroup_lanes(h.D), vec = vec_per_lane(h.D);
+#define EMB_SORTED(SG_, VEC_) \
+  launch_sorted_t<SG_, VEC_, MEAN>(h, p, offsets, ids, keys, perm, out, ws, s)
+  switch (sg) {
+    case 1: return EMB_SORTED(1, 1);
+    case 2: return EMB_SORTED(2, 1);
+    case 4: return EMB_SORTED(4, 1);
+    case 8: return EMB_SORTED(8, 1);
+    case 16: return EMB_SORTED(16, 1);
+    case 32: return EMB_SORTED(32, 1);
+    default:
+      switch (vec) {
+        case 1: return EMB_SORTED(64, 1);
+        case 2: return EMB_SORTED(64, 2);
+        case 3: return EMB_SORTED(64, 3);
+        default: return EMB_SORTED(64, 4);
+      }
+  }
+#undef EMB_SORTED
 }
 }  // namespace
 
-hipError_t launch_forward_sorted(const Handle& h, const Plan& p, const uint32_t* keys,
+hipError_t launch_forward_sorted(const Handle& h, const Plan& p, const int64_t* offsets,
+                                 const int64_t* ids, bool mean, const uint32_t* keys,
                                  const uint32_t* perm, float* out, char* ws, hipStream_t s) {
-  const int sg = subgroup_lanes(h.D), vec = vec_per_lane(h.D);
-  switch (sg) {
-    case 1: return launch_sorted_t<1, 1>(h, p, keys, perm, out, ws, s);
-    case 2: return launch_sorted_t<2, 1>(h, p, keys, perm, out, ws, s);
-    case 4: return launch_sorted_t<4, 1>(h, p, keys, perm, out, ws, s);
-    case 8: return launch_sorted_t<8, 1>(h, p, keys, perm, out, ws, s);
-    case 16: return launch_sorted_t<16, 1>(h, p, keys, perm, out, ws, s);
-    case 32: return launch_sorted_t<32, 1>(h, p, keys, perm, out, ws, s);
-    default:
-      switch (vec) {
-        case 1: return launch_sorted_t<64, 1>(h, p, keys, perm, out, ws, s);
-        case 2: return launch_sorted_t<64, 2>(h, p, keys, perm, out, ws, s);
-        case 3: return launch_sorted_t<64, 3>(h, p, keys, perm, out, ws, s);
-        default: return launch_sorted_t<64, 4>(h, p, keys, perm, out, ws, s);
-      }
-  }
+  return mean ? dispatch_sorted<true>(h, p, offsets, ids, keys, perm, out, ws, s)
+              : dispatch_sorted<false>(h, p, offsets, ids, keys, perm, out, ws, s);
 }
 
 }  // namespace embtab

@@ -20,9 +20,15 @@
 // order; a finished segment is updated in registers and written back once.
 // A segment that crosses a chunk boundary leaves fp32 partial sums (the
 // chunk's "tail" part where it starts, "head" parts in the chunks it covers);
-// its start chunk is appended to a span list and k_seg_fixup adds the parts
-// in chunk order and applies the step.  Every sum has a fixed order, so the
+// its start chunk is appended to one of two span lists, by whether the
+// segment ends within SG chunks of its start, and k_fixup adds the parts in
+// chunk order and applies the step.  Every sum has a fixed order, so the
 // result is deterministic and no float atomics are used.
+//
+// Finishing such a segment inside this kernel, by the sub-group of the chunk
+// where it starts reading on into the next one, was measured slower: the two
+// sub-groups of a wave run in lockstep, so a wave whose one sub-group does
+// extra rows holds the other idle for that time.
 #include "embtab_internal.hpp"
 
 #ifndef EMBTAB_SEG_UF
@@ -52,7 +58,8 @@ __global__ __launch_bounds__(256) void k_seg_adagrad(
     const float* __restrict__ grad, float* __restrict__ W, float* __restrict__ G, uint32_t n,
     uint32_t sentinel, int32_t D, float lr, float eps, float* __restrict__ part_head,
     float* __restrict__ part_tail, uint32_t* __restrict__ span_list,
-    uint32_t* __restrict__ misc, uint32_t nbags, const uint32_t* __restrict__ chunk_base,
+    uint32_t* __restrict__ long_list, uint32_t* __restrict__ misc, uint32_t nbags,
+    const uint32_t* __restrict__ chunk_base,
     uint32_t* __restrict__ unique, uint32_t* __restrict__ seg_off,
     uint32_t* __restrict__ inverse) {
   constexpr int CH = SG * MPL;
@@ -66,6 +73,11 @@ __global__ __launch_bounds__(256) void k_seg_adagrad(
   const int D4 = D >> 2;
   const uint32_t key_prev = k0 > 0 ? keys[k0 - 1] : kNoRow;
   const uint32_t key_next = k1 < n ? keys[k1] : kNoRow;
+  // First position of chunk c + 1 + SG: a segment that starts here and still
+  // holds it spans more than SG chunks and goes to the long-span list.
+  const uint64_t kfar = (uint64_t)k1 + (uint64_t)SG * CH;
+  const uint32_t key_far = kfar < n ? keys[kfar] : kNoRow;
+  const uint32_t nchunks = (n + CH - 1) / CH;
   uint32_t ucur = chunk_base[c] - 1u;  // unique index of a run entering the chunk
 
   uint32_t mkey[MPL], mj[MPL], mgr[MPL];
@@ -163,7 +175,7 @@ __global__ __launch_bounds__(256) void k_seg_adagrad(
         const uint32_t prevk = u > 0 ? kk[u > 0 ? u - 1 : 0] : lastkey;
         if (kk[u] != prevk) {
           ++ucur;
-          if (lane == 0) {
+          if (lane == 0 && ucur < n) {  // always true for a prepared workspace
             unique[ucur] = kk[u];
             seg_off[ucur] = k0 + p;
           }
@@ -200,8 +212,9 @@ __global__ __launch_bounds__(256) void k_seg_adagrad(
             if (d4 < D4) *reinterpret_cast<f4*>(dst + (size_t)c * D + 4 * d4) = acc[v];
           }
           if (!startb[u] && lane == 0) {
-            const uint32_t slot = atomicAdd(&misc[kMiscSpanCount], 1u);
-            span_list[slot] = c;
+            const bool lng = key_far == kk[u];
+            const uint32_t slot = atomicAdd(&misc[lng ? kMiscLongCount : kMiscSpanCount], 1u);
+            if (slot < nchunks) (lng ? long_list : span_list)[slot] = c;
           }
         }
       }
@@ -211,81 +224,36 @@ __global__ __launch_bounds__(256) void k_seg_adagrad(
   }
 }
 
-// Rows whose occurrences cross chunk boundaries ("spans") are finished in two
-// tiers.  k_fix_short: one sub-group per span; lane i tests whether the run
-// ends in chunk c0+1+i, so a span of up to SG chunks is found with one load
-// per lane, then its parts are added in chunk order (tail of c0, heads of
-// c0+1 .. c1) and the Adagrad step applied.  Longer spans (Zipf-hot rows) are
-// appended to a second list for k_fix_long.
-template <int SG, int VEC>
-__global__ __launch_bounds__(256) void k_fix_short(
+// Rows whose occurrences cross chunk boundaries ("spans") are finished by one
+// kernel in two tiers.  A long span (more than SG chunks; Zipf-hot rows) gets
+// a whole block: NT/SG sub-groups each add every (NT/SG)-th head part in chunk
+// order, then sub-group 0 adds tail + their sums in sub-group order.  A short
+// span gets one sub-group: lane i tests whether the run ends in chunk
+// c0+1+i, so the end is found with one load per lane, then the tail of c0 and
+// the heads of c0+1 .. c1 are added in chunk order.  Blocks take long spans
+// from the front of the grid and sub-groups of the other blocks take the
+// short spans first; the grid is sized to be resident at once, so the two
+// tiers run side by side.  The last block to finish clears the two span
+// counters, so every call starts from empty lists.
+template <int SG, int VEC, int NT>
+__global__ __launch_bounds__(NT) void k_fixup(
     const uint32_t* __restrict__ keys, uint32_t n, int32_t CH, float* __restrict__ W,
     float* __restrict__ G, int32_t D, float lr, float eps, const float* __restrict__ part_head,
     const float* __restrict__ part_tail, const uint32_t* __restrict__ span_list,
-    uint32_t* __restrict__ long_list, uint32_t* __restrict__ misc) {
-  constexpr int SGPB = 256 / SG;
-  const int lane = threadIdx.x % SG;
-  const uint32_t gsg = blockIdx.x * SGPB + threadIdx.x / SG;
-  const uint32_t nsg = gridDim.x * SGPB;
-  const int D4 = D >> 2;
-  const uint32_t nspan = misc[kMiscSpanCount];
-  const int lane_base = (int)(threadIdx.x & 63u) - lane;  // first lane of this sub-group in the wave
-  for (uint32_t sp = gsg; sp < nspan; sp += nsg) {
-    const uint32_t c0 = span_list[sp];
-    const uint32_t row = keys[(c0 + 1) * (uint32_t)CH - 1u];  // chunk c0 is full
-    const uint32_t cc = c0 + 1 + lane;
-    const uint64_t nxt = (uint64_t)(cc + 1) * (uint32_t)CH;
-    bool ends = false;
-    if ((uint64_t)cc * (uint32_t)CH < n) ends = (nxt >= n) || keys[nxt] != row;
-    const uint64_t m = (__ballot(ends) >> lane_base) & (SG == 64 ? ~0ull : ((1ull << SG) - 1ull));
-    if (m == 0) {
-      if (lane == 0) long_list[atomicAdd(&misc[kMiscLongCount], 1u)] = c0;
-      continue;
-    }
-    const uint32_t c1 = c0 + 1 + (uint32_t)(__ffsll((unsigned long long)m) - 1);
-#pragma unroll
-    for (int v = 0; v < VEC; ++v) {
-      const int d4 = lane + v * SG;
-      if (d4 >= D4) continue;
-      f4 tot = *reinterpret_cast<const f4*>(part_tail + (size_t)c0 * D + 4 * d4);
-      uint32_t c = c0 + 1;
-      for (; c + 3 <= c1; c += 4) {
-        const f4 x0 = *reinterpret_cast<const f4*>(part_head + (size_t)c * D + 4 * d4);
-        const f4 x1 = *reinterpret_cast<const f4*>(part_head + (size_t)(c + 1) * D + 4 * d4);
-        const f4 x2 = *reinterpret_cast<const f4*>(part_head + (size_t)(c + 2) * D + 4 * d4);
-        const f4 x3 = *reinterpret_cast<const f4*>(part_head + (size_t)(c + 3) * D + 4 * d4);
-        tot += x0;
-        tot += x1;
-        tot += x2;
-        tot += x3;
-      }
-      for (; c <= c1; ++c) tot += *reinterpret_cast<const f4*>(part_head + (size_t)c * D + 4 * d4);
-      f4 w = *reinterpret_cast<const f4*>(W + (size_t)row * D + 4 * d4);
-      f4 g2 = *reinterpret_cast<const f4*>(G + (size_t)row * D + 4 * d4);
-      adagrad_step(w, g2, tot, lr, eps);
-      *reinterpret_cast<f4*>(W + (size_t)row * D + 4 * d4) = w;
-      *reinterpret_cast<f4*>(G + (size_t)row * D + 4 * d4) = g2;
-    }
-  }
-}
-
-// Long spans: one block of NT threads per span.  NT/SG sub-groups each add
-// every (NT/SG)-th head part in chunk order, then sub-group 0 adds
-// tail + part_sum[0] + ... + part_sum[NT/SG - 1] in that order.
-template <int SG, int VEC, int NT>
-__global__ __launch_bounds__(NT) void k_fix_long(
-    const uint32_t* __restrict__ keys, uint32_t n, int32_t CH, float* __restrict__ W,
-    float* __restrict__ G, int32_t D, float lr, float eps, const float* __restrict__ part_head,
-    const float* __restrict__ part_tail, const uint32_t* __restrict__ long_list,
-    const uint32_t* __restrict__ misc) {
+    const uint32_t* __restrict__ long_list, uint32_t* __restrict__ misc) {
   constexpr int SGPB = NT / SG;
   __shared__ f4 red[SGPB][SG * VEC];
   __shared__ uint32_t s_end;
   const int lane = threadIdx.x % SG;
   const int sgb = threadIdx.x / SG;
   const int D4 = D >> 2;
-  const uint32_t nspan = misc[kMiscLongCount];
-  for (uint32_t sp = blockIdx.x; sp < nspan; sp += gridDim.x) {
+  const uint32_t nchunks = (n + (uint32_t)CH - 1) / (uint32_t)CH;
+  uint32_t nlong = misc[kMiscLongCount];
+  uint32_t nshort = misc[kMiscSpanCount];
+  nlong = nlong < nchunks ? nlong : nchunks;
+  nshort = nshort < nchunks ? nshort : nchunks;
+
+  for (uint32_t sp = blockIdx.x; sp < nlong; sp += gridDim.x) {
     const uint32_t c0 = long_list[sp];
     const uint32_t row = keys[(c0 + 1) * (uint32_t)CH - 1u];
     // The chunk where the run ends: the first chunk c > c0 whose successor
@@ -352,6 +320,57 @@ __global__ __launch_bounds__(NT) void k_fix_long(
     }
     __syncthreads();
   }
+
+  const int lane_base = (int)(threadIdx.x & 63u) - lane;  // first lane of this sub-group in the wave
+  const uint32_t nsg = gridDim.x * SGPB;
+  // Short spans go first to the blocks without a long span.
+  const uint32_t rb = (blockIdx.x + gridDim.x - nlong % gridDim.x) % gridDim.x;
+  for (uint32_t sp = rb * SGPB + sgb; sp < nshort; sp += nsg) {
+    const uint32_t c0 = span_list[sp];
+    const uint32_t row = keys[(c0 + 1) * (uint32_t)CH - 1u];  // chunk c0 is full
+    const uint32_t cc = c0 + 1 + lane;
+    const uint64_t nxt = (uint64_t)(cc + 1) * (uint32_t)CH;
+    bool ends = false;
+    if ((uint64_t)cc * (uint32_t)CH < n) ends = (nxt >= n) || keys[nxt] != row;
+    const uint64_t m = (__ballot(ends) >> lane_base) & (SG == 64 ? ~0ull : ((1ull << SG) - 1ull));
+    if (m == 0) continue;  // cannot happen for a listed span
+    const uint32_t c1 = c0 + 1 + (uint32_t)(__ffsll((unsigned long long)m) - 1);
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) {
+      const int d4 = lane + v * SG;
+      if (d4 >= D4) continue;
+      f4 w = *reinterpret_cast<const f4*>(W + (size_t)row * D + 4 * d4);
+      f4 g2 = *reinterpret_cast<const f4*>(G + (size_t)row * D + 4 * d4);
+      f4 tot = *reinterpret_cast<const f4*>(part_tail + (size_t)c0 * D + 4 * d4);
+      uint32_t c = c0 + 1;
+      for (; c + 3 <= c1; c += 4) {
+        const f4 x0 = *reinterpret_cast<const f4*>(part_head + (size_t)c * D + 4 * d4);
+        const f4 x1 = *reinterpret_cast<const f4*>(part_head + (size_t)(c + 1) * D + 4 * d4);
+        const f4 x2 = *reinterpret_cast<const f4*>(part_head + (size_t)(c + 2) * D + 4 * d4);
+        const f4 x3 = *reinterpret_cast<const f4*>(part_head + (size_t)(c + 3) * D + 4 * d4);
+        tot += x0;
+        tot += x1;
+        tot += x2;
+        tot += x3;
+      }
+      for (; c <= c1; ++c) tot += *reinterpret_cast<const f4*>(part_head + (size_t)c * D + 4 * d4);
+      adagrad_step(w, g2, tot, lr, eps);
+      *reinterpret_cast<f4*>(W + (size_t)row * D + 4 * d4) = w;
+      *reinterpret_cast<f4*>(G + (size_t)row * D + 4 * d4) = g2;
+    }
+  }
+
+  // Every block has read the counters (they bound its loops); the last block
+  // to get here clears them for the next call on this workspace.
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t done = atomicAdd(&misc[kMiscFixDone], 1u);
+    if (done == gridDim.x - 1u) {
+      atomicExch(&misc[kMiscSpanCount], 0u);
+      atomicExch(&misc[kMiscLongCount], 0u);
+      atomicExch(&misc[kMiscFixDone], 0u);
+    }
+  }
 }
 
 template <int SG, int VEC, bool MEAN>
@@ -370,6 +389,7 @@ hipError_t launch_t(const Handle& h, const Plan& p, const uint32_t* keys, const 
   float* ph = reinterpret_cast<float*>(ws + p.part_head);
   float* pt = reinterpret_cast<float*>(ws + p.part_tail);
   uint32_t* spans = reinterpret_cast<uint32_t*>(ws + p.span_list);
+  uint32_t* longs = reinterpret_cast<uint32_t*>(ws + p.long_list);
   uint32_t* misc = reinterpret_cast<uint32_t*>(ws + p.misc);
   const uint32_t* cbase = reinterpret_cast<const uint32_t*>(ws + p.chunk_base);
   uint32_t* uniq = reinterpret_cast<uint32_t*>(ws + p.unique);
@@ -380,7 +400,7 @@ hipError_t launch_t(const Handle& h, const Plan& p, const uint32_t* keys, const 
   if (!grad_out) {  // unique / seg_off / inverse only
     hipLaunchKernelGGL((k_seg_adagrad<SG, VEC, false, MPL, UF, false>), dim3((unsigned)grid),
                        dim3(256), 0, s, keys, perm, gr, scale, grad_out, h.W, h.G, n,
-                       (uint32_t)h.total_rows, h.D, lr, eps, ph, pt, spans, misc, nbags, cbase,
+                       (uint32_t)h.total_rows, h.D, lr, eps, ph, pt, spans, longs, misc, nbags, cbase,
                        uniq, segs, inv);
     e = hipGetLastError();
     return e == hipSuccess ? launch_unique_counts(p, ws, s) : e;
@@ -388,24 +408,20 @@ hipError_t launch_t(const Handle& h, const Plan& p, const uint32_t* keys, const 
   phase_mark(h, EMB_PHASE_REDUCE, false, s);
   hipLaunchKernelGGL((k_seg_adagrad<SG, VEC, MEAN, MPL, UF, true>), dim3((unsigned)grid),
                      dim3(256), 0, s, keys, perm, gr, scale, grad_out, h.W, h.G, n,
-                     (uint32_t)h.total_rows, h.D, lr, eps, ph, pt, spans, misc, nbags, cbase,
+                     (uint32_t)h.total_rows, h.D, lr, eps, ph, pt, spans, longs, misc, nbags, cbase,
                      uniq, segs, inv);
   phase_mark(h, EMB_PHASE_REDUCE, true, s);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   constexpr int FNT = VEC == 1 ? 1024 : (VEC == 2 ? 512 : 256);
-  uint32_t* longs = reinterpret_cast<uint32_t*>(ws + p.long_list);
-  int64_t sgrid = (chunks + SGPB - 1) / SGPB;
-  sgrid = sgrid < 2048 ? sgrid : 2048;
-  const int64_t lgrid = chunks < 512 ? chunks : 512;
+  constexpr int FSG = FNT / SG;
+  int64_t fgrid = (chunks + FSG - 1) / FSG;
+  const int64_t resident = (int64_t)h.cus * (2048 / FNT);  // 32 waves per CU
+  fgrid = fgrid < resident ? fgrid : resident;
   phase_mark(h, EMB_PHASE_FIXUP, false, s);
-  hipLaunchKernelGGL((k_fix_short<SG, VEC>), dim3((unsigned)sgrid), dim3(256), 0, s, keys, n,
+  hipLaunchKernelGGL((k_fixup<SG, VEC, FNT>), dim3((unsigned)fgrid), dim3(FNT), 0, s, keys, n,
                      SG * MPL, h.W, h.G, h.D, lr, eps, ph, pt, spans, longs, misc);
-  hipLaunchKernelGGL((k_fix_long<SG, VEC, FNT>), dim3((unsigned)lgrid), dim3(FNT), 0, s, keys, n,
-                     SG * MPL, h.W, h.G, h.D, lr, eps, ph, pt, longs, misc);
-  e = launch_unique_counts(p, ws, s);
   phase_mark(h, EMB_PHASE_FIXUP, true, s);
-  if (e != hipSuccess) return e;
   return hipGetLastError();
 }
 

@@ -27,7 +27,8 @@
 //                   seg_off[num_unique].
 // The reduction kernel that follows walks the sorted occurrences anyway and
 // writes unique[u], seg_off[u] and inverse[perm[k]] on the way; counts[u] =
-// seg_off[u+1] - seg_off[u] (k_unique_counts) closes the stage.
+// seg_off[u+1] - seg_off[u] (k_unique_counts) is formed only for the sort /
+// unique export, since no training step reads it.
 #include "embtab_internal.hpp"
 
 namespace embtab {

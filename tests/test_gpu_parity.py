@@ -258,6 +258,33 @@ def test_backward_hot_rows_span_many_chunks():
     check_rows(tabs, o, offsets, ids, w.B, True, grad, w.lr, w.eps, extra_rows=np.arange(3050))
 
 
+@pytest.mark.parametrize("D,mean", [(4, False), (16, True), (128, False), (256, True)])
+def test_backward_run_lengths_cross_chunk_boundaries(D, mean):
+    # Row r occurs 1 + (r % 97) times, so the runs of the sorted occurrences
+    # start and end at every offset of the 32- and 64-position reduction
+    # chunks: runs inside one chunk, across one boundary (finished by the chunk
+    # where they start) and across several (partial sums + fixup).
+    nrows = 600
+    lens = 1 + np.arange(nrows) % 97
+    ids = np.repeat(np.arange(nrows, dtype=np.int64), lens)
+    rng = np.random.default_rng(D)
+    ids = ids[rng.permutation(ids.size)]
+    bag_lens = rng.integers(1, 4, ids.size)  # multi-hot bags of 1..3 ids
+    ends = np.cumsum(bag_lens)
+    B = int(np.searchsorted(ends, ids.size))
+    offsets = np.concatenate([[0], ends[:B]]).astype(np.int64)
+    offsets[-1] = ids.size
+    grad = rng.standard_normal((B, 1, D)).astype(np.float32)
+    tabs, o = make_pair(np.array([nrows + 5]), D, seed=3)
+    r = check_sort_unique(tabs, o, offsets, ids, B)
+    assert r["num_unique"] == nrows
+    gpu_backward(tabs, offsets, ids, B, mean, grad, 0.01, 1e-8)
+    o.backward_adagrad(offsets, ids, B, mean, grad, 0.01, 1e-8)
+    check_rows(tabs, o, offsets, ids, B, mean, grad, 0.01, 1e-8,
+               extra_rows=np.arange(nrows, nrows + 5))
+    assert status(tabs) == (eb.EMB_OK, 0)
+
+
 def test_backward_one_hot_zipf_two_steps():
     w = synth.workload(2, T=4, B=20000, rows=[100, 3000, 1_000_000, 20])
     tabs, o = make_pair(w.rows, w.D, seed=4)
@@ -445,9 +472,10 @@ def test_prepared_backward_on_side_stream_matches_oracle():
     assert status(tabs) == (eb.EMB_OK, 0)
 
 
-@pytest.mark.parametrize("case", ["one_hot", "one_hot_oor", "multi_hot", "with_empty"])
+@pytest.mark.parametrize("case", ["one_hot", "one_hot_oor", "multi_hot", "with_empty",
+                                  "nnz_equals_bags"])
 def test_forward_prepared_matches_oracle(case):
-    if case.startswith("one_hot"):
+    if case.startswith("one_hot") or case == "nnz_equals_bags":
         w = synth.workload(2, T=4, B=7000, rows=[50, 9000, 1_000_000, 3])
         mean = False
     else:
@@ -462,6 +490,15 @@ def test_forward_prepared_matches_oracle(case):
         lens[::5] = 0
         offsets = np.concatenate([[0], np.cumsum(lens)])
         ids = ids[:offsets[-1]]
+    if case == "nnz_equals_bags":
+        # as many ids as bags, but not one per bag: bag pairs (2k, 2k+1) of a
+        # table get lengths (2, 0) every third pair
+        lens = np.diff(offsets)
+        pairs = np.arange(0, lens.size, 6)
+        lens[pairs] = 2
+        lens[pairs + 1] = 0
+        offsets = np.concatenate([[0], np.cumsum(lens)])
+        assert offsets[-1] == ids.size == w.B * w.T
     tabs, o = make_pair(w.rows, w.D, seed=31)
     d_off, d_ids = _t(offsets), _t(ids)
     ws, need = tabs.workspace(w.B, ids.size)
@@ -475,6 +512,9 @@ def test_forward_prepared_matches_oracle(case):
     ref, fl = o.forward(offsets, ids, w.B, mean)
     if case.startswith("one_hot"):
         np.testing.assert_array_equal(out.cpu().numpy(), ref)  # a copy of one row, or 0
+    elif case == "nnz_equals_bags":  # sums of at most two rows: exact up to one rounding
+        S = forward_S(offsets, ids, w.B, o.rows, lambda r: o.read_rows(r)[0], mean, w.D)
+        assert_within(out.cpu().numpy(), ref, S, "forward_prepared")
     else:
         S = forward_S(offsets, ids, w.B, o.rows, lambda r: o.read_rows(r)[0], mean, w.D)
         assert_within(out.cpu().numpy(), ref, S, "forward_prepared")
@@ -485,6 +525,38 @@ def test_forward_prepared_matches_oracle(case):
     o.backward_adagrad(offsets, ids, w.B, mean, grad, w.lr, w.eps)
     torch.cuda.synchronize()
     check_rows(tabs, o, offsets, ids, w.B, mean, grad, w.lr, w.eps)
+
+
+def test_prepared_backward_twice_on_one_prepare():
+    # Two Adagrad steps from one prepared workspace (same ids, two gradients):
+    # the span lists of the first call must not leak into the second.
+    w = synth.workload(3, T=2, B=6000)
+    w.rows = np.array([40, 5000])  # hot rows: short and long spans
+    offsets, ids = synth.gen_batch(w)
+    tabs, o = make_pair(w.rows, w.D, seed=12)
+    ws, need = tabs.workspace(w.B, ids.size)
+    pool = eb.EMB_POOL_MEAN
+    eb.check(eb.emb_bag_prepare(tabs.handle, _t(offsets), _t(ids), w.B, ids.size, pool, ws, need),
+             "prepare")
+    grads = [synth.gen_grad(w, step) for step in range(2)]
+    for grad in grads:
+        eb.check(eb.emb_bag_backward_adagrad_prepared(tabs.handle, w.B, ids.size, pool, _t(grad),
+                                                      w.lr, w.eps, ws, need), "backward_prepared")
+        o.backward_adagrad(offsets, ids, w.B, True, grad, w.lr, w.eps)
+    torch.cuda.synchronize()
+    # bound of two steps: the per-step terms of both steps added
+    uniq, g0 = abs_grad_sums(offsets, ids, w.B, o.rows, grads[0], True, w.D)
+    _, g1 = abs_grad_sums(offsets, ids, w.B, o.rows, grads[1], True, w.D)
+    Wr, Gr = o.read_rows(uniq)
+    Gr64 = Gr.astype(np.float64)
+    assert_within(tabs.accum[_t(uniq)].cpu().numpy(), Gr, Gr64 + g0 ** 2 + g1 ** 2, "accumulator")
+    assert_within(tabs.weights[_t(uniq)].cpu().numpy(), Wr,
+                  np.abs(Wr) + 2 * w.lr + w.lr * (g0 + g1) / np.sqrt(Gr64), "weights")
+    untouched = np.setdiff1d(np.arange(int(w.rows.sum())), uniq)
+    Wu, Gu = o.read_rows(untouched)
+    np.testing.assert_array_equal(tabs.weights[_t(untouched)].cpu().numpy(), Wu)
+    np.testing.assert_array_equal(tabs.accum[_t(untouched)].cpu().numpy(), Gu)
+    assert status(tabs) == (eb.EMB_OK, 0)
 
 
 def test_debug_export_leaves_tables_untouched():
