@@ -60,8 +60,7 @@ bool make_plan(const Handle& h, int64_t B, int64_t nnz, Plan* p) {
   p->valsA = take(n4);
   p->keysB = take(n4);
   p->valsB = take(n4);
-  p->gr = take(n4);
-  p->scale = take(n4);
+  p->gr = take(2 * n4);  // grad row, or (grad row, mean scale) pairs
   p->sgr = take(n4);
   p->sscale = take(n4);
   p->tile_hist = take(sizeof(uint32_t) * kMaxRadix * nt);
@@ -70,8 +69,6 @@ bool make_plan(const Handle& h, int64_t B, int64_t nnz, Plan* p) {
   p->seg_off = take(n4 + sizeof(uint32_t));
   p->counts = take(n4);
   p->inverse = take(n4);
-  p->ucnt = take(sizeof(uint32_t) * nt);
-  p->vcnt = take(sizeof(uint32_t) * nt);
   const size_t nc = (size_t)(p->nchunks > 0 ? p->nchunks : 1);
   p->part_head = take(sizeof(float) * nc * (size_t)h.D);
   p->part_tail = take(sizeof(float) * nc * (size_t)h.D);

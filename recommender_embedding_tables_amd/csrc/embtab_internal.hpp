@@ -105,12 +105,11 @@ struct Plan {
   int64_t ntiles = 0;   // sort / unique tiles
   int64_t nchunks = 0;  // reduction chunks
   int chunk = 0;
-  size_t keysA, valsA, keysB, valsB, gr, scale;
+  size_t keysA, valsA, keysB, valsB, gr;
   size_t sgr, sscale;  // grad row and mean scale of each sorted occurrence
   size_t tile_hist, digit_tot;
   size_t unique, seg_off, counts, inverse;
-  size_t ucnt, vcnt;
-  size_t misc;  // uint32[64]
+  size_t misc;  // uint32[64 + 2T]
   size_t part_head, part_tail, span_list, long_list;
   size_t chunk_base;  // heads before each reduction chunk (nchunks + 1)
   size_t h_slot, h_first, h_tcnt;  // hash find-or-insert

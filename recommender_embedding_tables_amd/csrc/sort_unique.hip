@@ -8,10 +8,11 @@
 // occurrence order and the permutation is unique.
 //
 // Kernels, in launch order:
-//   k_keys          one thread per bag: key = off_t + id (out-of-range ids get
-//                   the sentinel key total_rows, which sorts last), value = j,
-//                   grad row s*T + t and, for mean pooling, 1/L of the bag;
-//                   flags the batch as not one-hot when a bag's length is not 1.
+//   k_keys          per occurrence j: key = off_t + id (out-of-range ids get
+//                   the sentinel key total_rows, which sorts last), grad row
+//                   s*T + t and, for mean pooling, 1/L of its bag; flags the
+//                   batch as not one-hot when a bag's length is not 1.  The
+//                   sort's value of occurrence j is j itself (not stored).
 //   k_sort_hist     per 4096-key tile, digit counts -> tile_hist[digit][tile].
 //   k_sort_scan     one block per digit: exclusive scan over tiles, digit totals.
 //   k_sort_scatter  per tile: stable rank of every key (per-wave ballot match
@@ -58,49 +59,79 @@ __device__ inline uint32_t block_excl_scan(uint32_t v, uint32_t* total, uint32_t
   return x - v + before;
 }
 
+// One block per `bpb` consecutive bags in CSR order (bpb <= 256, chosen so
+// a block covers about 256 occurrences).  Thread i < bpb checks bag b0 + i;
+// the bag offsets go to LDS, and the block then walks the occurrences
+// [offsets[b0], offsets[b0 + bpb]) with consecutive threads on consecutive
+// occurrences (coalesced id loads and key stores, whatever the bag lengths),
+// finding each occurrence's bag by binary search in LDS.  The value of
+// occurrence j is j itself, so it is not stored.
 __global__ __launch_bounds__(256) void k_keys(const int64_t* __restrict__ offsets,
                                               const int64_t* __restrict__ ids,
                                               const int64_t* __restrict__ row_off,
                                               const int64_t* __restrict__ rows,
                                               uint32_t* __restrict__ keys,
-                                              uint32_t* __restrict__ vals,
-                                              uint32_t* __restrict__ gr, float* __restrict__ scale,
+                                              uint32_t* __restrict__ gr,
                                               uint32_t* __restrict__ flags,
                                               uint32_t* __restrict__ misc, int64_t B, int32_t T,
-                                              int64_t nnz, uint32_t sentinel, int32_t mean) {
+                                              int64_t nnz, uint32_t sentinel, int32_t mean,
+                                              int32_t bpb) {
+  __shared__ int64_t s_off[257];
+  __shared__ uint32_t s_bad;
   const int64_t nbags = B * (int64_t)T;
-  const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t b0 = (int64_t)blockIdx.x * bpb;
+  const int64_t b = b0 + threadIdx.x;
+  const int64_t nb = (nbags - b0) < bpb ? (nbags - b0) : bpb;  // bags of this block
+  if (nb <= 0) return;  // empty batch (the grid has one block)
+  if (threadIdx.x == 0) s_bad = 0u;
+  const bool mine = threadIdx.x < nb;
   int64_t o0 = 0, o1 = 1;
-  if (b < nbags) {
+  if (mine) {
     o0 = offsets[b];
     o1 = offsets[b + 1];
   }
   {
     const uint64_t mm = __ballot(o1 - o0 != 1);
-    if ((threadIdx.x & 63u) == 0u && mm != 0ull) atomicOr(&misc[kMiscNotOneHot], 1u);
+    // a plain store of a constant: device atomics on one word from every
+    // block would serialise
+    if ((threadIdx.x & 63u) == 0u && mm != 0ull) misc[kMiscNotOneHot] = 1u;
   }
-  if (b >= nbags) return;
-  const int64_t t = b / B, s = b - t * B;
   uint32_t bad = 0;
-  if ((b == 0 && o0 != 0) || (b == nbags - 1 && o1 != nnz) || o1 < o0 || o0 < 0 || o1 > nnz)
-    bad |= EMB_FLAG_BAD_OFFSETS;
-  o0 = o0 < 0 ? 0 : (o0 > nnz ? nnz : o0);
-  o1 = o1 < o0 ? o0 : (o1 > nnz ? nnz : o1);
-  const uint32_t roff = (uint32_t)row_off[t];
-  const int64_t nr = rows[t];
-  const uint32_t g = (uint32_t)(s * T + t);
-  const float c = (o1 > o0) ? 1.0f / (float)(o1 - o0) : 1.0f;
-  for (int64_t j = o0; j < o1; ++j) {
+  if (mine) {
+    if ((b == 0 && o0 != 0) || (b == nbags - 1 && o1 != nnz) || o1 < o0 || o0 < 0 || o1 > nnz)
+      bad |= EMB_FLAG_BAD_OFFSETS;
+    // clamped to [0, nnz]: with offsets that are not monotone the search
+    // below still lands on a bag of this block, and the batch is flagged
+    s_off[threadIdx.x] = o0 < 0 ? 0 : (o0 > nnz ? nnz : o0);
+    if (threadIdx.x == nb - 1) s_off[nb] = o1 < 0 ? 0 : (o1 > nnz ? nnz : o1);
+  }
+  __syncthreads();
+  const int64_t j0 = s_off[0], j1 = s_off[nb];
+  for (int64_t j = j0 + threadIdx.x; j < j1; j += 256) {
+    // last bag i of the block with s_off[i] <= j (bags of length 0 are skipped)
+    int lo = 0, hi = (int)nb - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_off[mid] <= j) lo = mid;
+      else hi = mid - 1;
+    }
+    const int64_t bag = b0 + lo;
+    const int64_t t = bag / B, s = bag - t * B;
     const int64_t id = ids[j];
     uint32_t key = sentinel;
-    if (id >= 0 && id < nr) key = roff + (uint32_t)id;
+    if (id >= 0 && id < rows[t]) key = (uint32_t)row_off[t] + (uint32_t)id;
     else bad |= EMB_FLAG_OUT_OF_RANGE;
     keys[j] = key;
-    vals[j] = (uint32_t)j;
-    gr[j] = g;
-    if (mean) scale[j] = c;
+    const uint32_t g = (uint32_t)(s * T + t);
+    if (mean)  // grad row and scale side by side: one gather in the last pass
+      reinterpret_cast<uint2*>(gr)[j] =
+          make_uint2(g, __float_as_uint(1.0f / (float)(s_off[lo + 1] - s_off[lo])));
+    else
+      gr[j] = g;
   }
-  if (bad) atomicOr(flags, bad);
+  if (bad) atomicOr(&s_bad, bad);
+  __syncthreads();
+  if (threadIdx.x == 0 && s_bad) atomicOr(flags, s_bad);
 }
 
 // Per-wave stable digit ranking of 64 keys: returns the lanes of this wave that
@@ -174,16 +205,19 @@ __global__ __launch_bounds__(256) void k_sort_scan(uint32_t* __restrict__ tile_h
   if (threadIdx.x == 0) digit_tot[blockIdx.x] = carry;
 }
 
-// In the last pass (gr_in != nullptr) the scatter also gathers each
-// occurrence's grad row (and mean scale) into sorted order, so the consumers
-// of the sort read them with coalesced loads; a stale occurrence index gets the
-// invalid grad row 0xFFFFFFFF.
+// FIRST: the values are the positions themselves (not read).  The last pass
+// (gr_out != nullptr) also writes each sorted occurrence's grad row (and mean
+// scale), so the consumers of the sort read them with coalesced loads: computed
+// from the occurrence index when every bag holds one id (a flag of k_keys),
+// else gathered; a stale occurrence index gets the invalid grad row
+// 0xFFFFFFFF.
+template <bool FIRST>
 __global__ __launch_bounds__(256) void k_sort_scatter(
     const uint32_t* __restrict__ keys_in, const uint32_t* __restrict__ vals_in,
     uint32_t* __restrict__ keys_out, uint32_t* __restrict__ vals_out, uint32_t n, int shift,
     int nbits, const uint32_t* __restrict__ tile_off, const uint32_t* __restrict__ digit_tot,
-    uint32_t ntiles, const uint32_t* __restrict__ gr_in, const float* __restrict__ sc_in,
-    uint32_t* __restrict__ gr_out, float* __restrict__ sc_out) {
+    uint32_t ntiles, const uint32_t* __restrict__ gr_in, uint32_t* __restrict__ gr_out,
+    float* __restrict__ sc_out, const uint32_t* __restrict__ misc, uint32_t B, uint32_t T) {
   __shared__ uint32_t whist[4][kMaxRadix];
   __shared__ uint32_t dstart[kMaxRadix];
   __shared__ uint32_t gbase[kMaxRadix];
@@ -201,10 +235,10 @@ __global__ __launch_bounds__(256) void k_sort_scatter(
   for (int r = 0; r < kSortItems; ++r) {
     const uint32_t idx = base + r * 64 + lane;
     kv[r] = 0u;
-    vv[r] = 0u;
+    vv[r] = idx;
     if (idx < n) {
       kv[r] = keys_in[idx];
-      vv[r] = vals_in[idx];
+      if (!FIRST) vv[r] = vals_in[idx];
     }
   }
   __syncthreads();
@@ -262,6 +296,7 @@ __global__ __launch_bounds__(256) void k_sort_scatter(
   __syncthreads();
   const uint32_t tbase = tile * (uint32_t)kSortTile;
   const uint32_t tn = (n - tbase) < (uint32_t)kSortTile ? (n - tbase) : (uint32_t)kSortTile;
+  const bool one_hot = gr_out && misc[kMiscNotOneHot] == 0u;
   for (uint32_t i = threadIdx.x; i < tn; i += 256) {
     const uint32_t k = skeys[i];
     const uint32_t d = (k >> shift) & mask;
@@ -269,9 +304,18 @@ __global__ __launch_bounds__(256) void k_sort_scatter(
     const uint32_t v = svals[i];
     keys_out[g] = k;
     vals_out[g] = v;
-    if (gr_in) {
-      gr_out[g] = v < n ? gr_in[v] : 0xFFFFFFFFu;
-      if (sc_in) sc_out[g] = v < n ? sc_in[v] : 0.0f;
+    if (gr_out) {
+      if (one_hot) {  // occurrence v is bag v: table v / B, sample v % B
+        gr_out[g] = v < n ? (v % B) * T + v / B : 0xFFFFFFFFu;
+        if (sc_out) sc_out[g] = 1.0f;
+      } else if (sc_out) {  // (grad row, scale) pairs
+        const uint2 x = v < n ? reinterpret_cast<const uint2*>(gr_in)[v]
+                              : make_uint2(0xFFFFFFFFu, 0u);
+        gr_out[g] = x.x;
+        sc_out[g] = __uint_as_float(x.y);
+      } else {
+        gr_out[g] = v < n ? gr_in[v] : 0xFFFFFFFFu;
+      }
     }
   }
 }
@@ -397,20 +441,22 @@ hipError_t launch_sort_unique(const Handle& h, const Plan& p, const int64_t* off
   uint32_t* kB = reinterpret_cast<uint32_t*>(ws + p.keysB);
   uint32_t* vB = reinterpret_cast<uint32_t*>(ws + p.valsB);
   uint32_t* gr = reinterpret_cast<uint32_t*>(ws + p.gr);
-  float* scale = reinterpret_cast<float*>(ws + p.scale);
   uint32_t* tile_hist = reinterpret_cast<uint32_t*>(ws + p.tile_hist);
   uint32_t* digit_tot = reinterpret_cast<uint32_t*>(ws + p.digit_tot);
   uint32_t* seg_off = reinterpret_cast<uint32_t*>(ws + p.seg_off);
   uint32_t* cbase = reinterpret_cast<uint32_t*>(ws + p.chunk_base);
 
   const int64_t nbags = p.B * (int64_t)h.T;
-  const unsigned kgrid = (unsigned)((nbags + 255) / 256);
+  // bags per key block: a power of two near 256 / (mean bag length)
+  int bpb = 256;
+  while (bpb > 1 && (int64_t)bpb * p.nnz > 256 * nbags * 2) bpb >>= 1;
+  const unsigned kgrid = (unsigned)((nbags + bpb - 1) / bpb);
   phase_mark(h, EMB_PHASE_KEYS, false, s);
   hipError_t e = launch_zero_words(misc, 64 + 2 * h.T, s);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_keys, dim3(kgrid > 0 ? kgrid : 1), dim3(256), 0, s, offsets, ids,
-                     h.sv.row_off, h.sv.rows, kA, vA, gr, scale, h.sv.flags, misc, p.B, h.T,
-                     p.nnz, sentinel, mean ? 1 : 0);
+                     h.sv.row_off, h.sv.rows, kA, gr, h.sv.flags, misc, p.B, h.T,
+                     p.nnz, sentinel, mean ? 1 : 0, bpb);
   phase_mark(h, EMB_PHASE_KEYS, true, s);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -427,11 +473,16 @@ hipError_t launch_sort_unique(const Handle& h, const Plan& p, const int64_t* off
                          p.dbits[pass], tile_hist, ntiles);
       hipLaunchKernelGGL(k_sort_scan, dim3(radix), dim3(256), 0, s, tile_hist, ntiles, digit_tot);
       const bool last = pass + 1 == p.passes;
-      hipLaunchKernelGGL(k_sort_scatter, dim3(ntiles), dim3(256), 0, s, kin, vin, kout, vout, n,
-                         p.shift[pass], p.dbits[pass], tile_hist, digit_tot, ntiles,
-                         last ? gr : nullptr, (last && mean) ? scale : nullptr,
-                         reinterpret_cast<uint32_t*>(ws + p.sgr),
-                         reinterpret_cast<float*>(ws + p.sscale));
+      uint32_t* gro = last ? reinterpret_cast<uint32_t*>(ws + p.sgr) : nullptr;
+      float* sco = (last && mean) ? reinterpret_cast<float*>(ws + p.sscale) : nullptr;
+      if (pass == 0)
+        hipLaunchKernelGGL(k_sort_scatter<true>, dim3(ntiles), dim3(256), 0, s, kin, vin, kout,
+                           vout, n, p.shift[pass], p.dbits[pass], tile_hist, digit_tot, ntiles, gr,
+                           gro, sco, misc, (uint32_t)p.B, (uint32_t)h.T);
+      else
+        hipLaunchKernelGGL(k_sort_scatter<false>, dim3(ntiles), dim3(256), 0, s, kin, vin, kout,
+                           vout, n, p.shift[pass], p.dbits[pass], tile_hist, digit_tot, ntiles, gr,
+                           gro, sco, misc, (uint32_t)p.B, (uint32_t)h.T);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
       uint32_t* tk = kin;

@@ -25,7 +25,7 @@ from typing import Optional
 
 import numpy as np
 
-S_ROWS, S_IDS, S_LENS, S_GRAD, S_UNIVERSE = 0, 1, 2, 3, 4
+S_ROWS, S_IDS, S_LENS, S_GRAD, S_UNIVERSE, S_PREFILL = 0, 1, 2, 3, 4, 5
 
 
 @dataclasses.dataclass
@@ -226,6 +226,13 @@ def gen_keys(w: Workload, offsets: np.ndarray, ranks: np.ndarray) -> np.ndarray:
         a, b = int(offsets[t * w.B]), int(offsets[(t + 1) * w.B])
         keys[a:b] = key_universe(w, t)[ranks[a:b]]
     return keys
+
+
+def prefill_keys(w: Workload, t: int, n: int) -> np.ndarray:
+    """Keys of ranks 0 .. n-1 of table t in a seeded random order: the keys a
+    long training run has already inserted (warm start of a hashed workload)."""
+    r = _rng(w.seed, w.cfg, S_PREFILL, t)
+    return key_universe(w, t)[r.permutation(n)]
 
 
 def gen_grad(w: Workload, batch: int = 0, out: Optional[np.ndarray] = None) -> np.ndarray:
