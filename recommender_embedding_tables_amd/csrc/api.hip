@@ -75,6 +75,7 @@ bool make_plan(const Handle& h, int64_t B, int64_t nnz, Plan* p) {
   p->span_list = take(sizeof(uint32_t) * nc);
   p->long_list = take(sizeof(uint32_t) * nc);
   p->chunk_base = take(sizeof(uint32_t) * (nc + 1));
+  p->head_base = take(sizeof(uint32_t) * ((size_t)(nnz + 255) / 256 + 1));
   if (h.hashed) {
     p->h_slot = take(n4);
     p->h_first = take(n4);

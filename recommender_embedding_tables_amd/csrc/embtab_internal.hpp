@@ -111,7 +111,8 @@ struct Plan {
   size_t unique, seg_off, counts, inverse;
   size_t misc;  // uint32[64 + 2T]
   size_t part_head, part_tail, span_list, long_list;
-  size_t chunk_base;  // heads before each reduction chunk (nchunks + 1)
+  size_t chunk_base;  // heads in the earlier chunks of the chunk's 256-position block
+  size_t head_base;   // heads before each 256-position block (nnz / 256 + 1)
   size_t h_slot, h_first, h_tcnt;  // hash find-or-insert
   size_t total = 0;
 };

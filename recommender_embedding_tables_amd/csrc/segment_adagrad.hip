@@ -59,7 +59,7 @@ __global__ __launch_bounds__(256) void k_seg_adagrad(
     uint32_t sentinel, int32_t D, float lr, float eps, float* __restrict__ part_head,
     float* __restrict__ part_tail, uint32_t* __restrict__ span_list,
     uint32_t* __restrict__ long_list, uint32_t* __restrict__ misc, uint32_t nbags,
-    const uint32_t* __restrict__ chunk_base,
+    const uint32_t* __restrict__ chunk_base, const uint32_t* __restrict__ head_base,
     uint32_t* __restrict__ unique, uint32_t* __restrict__ seg_off,
     uint32_t* __restrict__ inverse) {
   constexpr int CH = SG * MPL;
@@ -78,7 +78,8 @@ __global__ __launch_bounds__(256) void k_seg_adagrad(
   const uint64_t kfar = (uint64_t)k1 + (uint64_t)SG * CH;
   const uint32_t key_far = kfar < n ? keys[kfar] : kNoRow;
   const uint32_t nchunks = (n + CH - 1) / CH;
-  uint32_t ucur = chunk_base[c] - 1u;  // unique index of a run entering the chunk
+  // unique index of a run entering the chunk
+  uint32_t ucur = head_base[c / (256 / CH)] + chunk_base[c] - 1u;
 
   uint32_t mkey[MPL], mj[MPL], mgr[MPL];
   float msc[MPL];
@@ -392,6 +393,7 @@ hipError_t launch_t(const Handle& h, const Plan& p, const uint32_t* keys, const 
   uint32_t* longs = reinterpret_cast<uint32_t*>(ws + p.long_list);
   uint32_t* misc = reinterpret_cast<uint32_t*>(ws + p.misc);
   const uint32_t* cbase = reinterpret_cast<const uint32_t*>(ws + p.chunk_base);
+  const uint32_t* hbase = reinterpret_cast<const uint32_t*>(ws + p.head_base);
   uint32_t* uniq = reinterpret_cast<uint32_t*>(ws + p.unique);
   uint32_t* segs = reinterpret_cast<uint32_t*>(ws + p.seg_off);
   uint32_t* inv = reinterpret_cast<uint32_t*>(ws + p.inverse);
@@ -400,16 +402,16 @@ hipError_t launch_t(const Handle& h, const Plan& p, const uint32_t* keys, const 
   if (!grad_out) {  // unique / seg_off / inverse only
     hipLaunchKernelGGL((k_seg_adagrad<SG, VEC, false, MPL, UF, false>), dim3((unsigned)grid),
                        dim3(256), 0, s, keys, perm, gr, scale, grad_out, h.W, h.G, n,
-                       (uint32_t)h.total_rows, h.D, lr, eps, ph, pt, spans, longs, misc, nbags, cbase,
-                       uniq, segs, inv);
+                       (uint32_t)h.total_rows, h.D, lr, eps, ph, pt, spans, longs, misc, nbags,
+                       cbase, hbase, uniq, segs, inv);
     e = hipGetLastError();
     return e == hipSuccess ? launch_unique_counts(p, ws, s) : e;
   }
   phase_mark(h, EMB_PHASE_REDUCE, false, s);
   hipLaunchKernelGGL((k_seg_adagrad<SG, VEC, MEAN, MPL, UF, true>), dim3((unsigned)grid),
                      dim3(256), 0, s, keys, perm, gr, scale, grad_out, h.W, h.G, n,
-                     (uint32_t)h.total_rows, h.D, lr, eps, ph, pt, spans, longs, misc, nbags, cbase,
-                     uniq, segs, inv);
+                     (uint32_t)h.total_rows, h.D, lr, eps, ph, pt, spans, longs, misc, nbags,
+                     cbase, hbase, uniq, segs, inv);
   phase_mark(h, EMB_PHASE_REDUCE, true, s);
   e = hipGetLastError();
   if (e != hipSuccess) return e;

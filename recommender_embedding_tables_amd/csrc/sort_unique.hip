@@ -320,11 +320,18 @@ __global__ __launch_bounds__(256) void k_sort_scatter(
   }
 }
 
+// Run heads (first position of each distinct valid key) per reduction chunk
+// of CH positions.  A block covers 256 positions = 256 / CH chunks: each
+// chunk gets the number of heads in the block's earlier chunks (cloc) and
+// the block its total (btot), which k_chunk_scan turns into block bases.
 template <int CH>
 __global__ __launch_bounds__(256) void k_chunk_heads(const uint32_t* __restrict__ keys, uint32_t n,
                                                      uint32_t sentinel,
-                                                     uint32_t* __restrict__ hc,
+                                                     uint32_t* __restrict__ cloc,
+                                                     uint32_t* __restrict__ btot,
                                                      uint32_t* __restrict__ misc) {
+  constexpr int CPB = 256 / CH;
+  __shared__ uint32_t s_cnt[CPB];
   const uint32_t k = blockIdx.x * 256u + threadIdx.x;
   bool head = false;
   if (k < n) {
@@ -336,14 +343,28 @@ __global__ __launch_bounds__(256) void k_chunk_heads(const uint32_t* __restrict_
   }
   const uint64_t m = __ballot(head);
   const uint32_t lane = threadIdx.x & 63u;
-  if ((lane % CH) == 0u && k < n) {
+  if ((lane % CH) == 0u) {
     const uint64_t bits = CH == 64 ? m : (m >> lane) & ((1ull << CH) - 1ull);
-    hc[k / CH] = (uint32_t)__popcll(bits);
+    s_cnt[threadIdx.x / CH] = (uint32_t)__popcll(bits);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t nch = (n + CH - 1) / CH;
+    uint32_t run = 0;
+#pragma unroll
+    for (int i = 0; i < CPB; ++i) {
+      const uint32_t c = blockIdx.x * CPB + i;
+      if (c < nch) cloc[c] = run;
+      run += s_cnt[i];
+    }
+    btot[blockIdx.x] = run;
   }
 }
 
-// Exclusive scan of the chunk head counts in one block: each pass covers
-// 1024 threads x 32 consecutive counts, read and written with dwordx4 accesses.
+// Exclusive scan of the per-block head totals in one block (in place): each
+// pass covers 1024 threads x 32 consecutive counts, read and written with
+// dwordx4 accesses.  The unique index of the first run head of reduction
+// chunk c is then btot[c / (256 / CH)] + cloc[c].
 __global__ __launch_bounds__(1024) void k_chunk_scan(uint32_t* __restrict__ hc, uint32_t nchunks,
                                                      uint32_t* __restrict__ misc,
                                                      uint32_t* __restrict__ seg_off) {
@@ -495,17 +516,17 @@ hipError_t launch_sort_unique(const Handle& h, const Plan& p, const int64_t* off
   }
   phase_mark(h, EMB_PHASE_SORT, true, s);
   phase_mark(h, EMB_PHASE_UNIQUE, false, s);
-  const uint32_t nchunks = (uint32_t)p.nchunks;
+  const unsigned hgrid = (unsigned)((n + 255) / 256);
+  uint32_t* btot = reinterpret_cast<uint32_t*>(ws + p.head_base);
   if (n > 0) {
-    const unsigned hgrid = (unsigned)((n + 255) / 256);
     if (p.chunk == 64)
       hipLaunchKernelGGL((k_chunk_heads<64>), dim3(hgrid), dim3(256), 0, s, kin, n, sentinel,
-                         cbase, misc);
+                         cbase, btot, misc);
     else
       hipLaunchKernelGGL((k_chunk_heads<32>), dim3(hgrid), dim3(256), 0, s, kin, n, sentinel,
-                         cbase, misc);
+                         cbase, btot, misc);
   }
-  hipLaunchKernelGGL(k_chunk_scan, dim3(1), dim3(1024), 0, s, cbase, nchunks, misc, seg_off);
+  hipLaunchKernelGGL(k_chunk_scan, dim3(1), dim3(1024), 0, s, btot, hgrid, misc, seg_off);
   phase_mark(h, EMB_PHASE_UNIQUE, true, s);
   *sorted_keys = kin;
   *sorted_vals = vin;
