@@ -55,7 +55,7 @@ bool make_plan(const Handle& h, int64_t B, int64_t nnz, Plan* p) {
     o += align_up(bytes);
     return at;
   };
-  p->misc = take(sizeof(uint32_t) * (64 + 2 * (size_t)h.T));
+  p->misc = take(sizeof(uint32_t) * (64 + 3 * (size_t)h.T));
   p->keysA = take(n4);
   p->valsA = take(n4);
   p->keysB = take(n4);
@@ -80,8 +80,9 @@ bool make_plan(const Handle& h, int64_t B, int64_t nnz, Plan* p) {
     p->h_slot = take(n4);
     p->h_first = take(n4);
     p->h_tcnt = take(sizeof(uint32_t) * (size_t)((nnz + 255) / 256 + 1));
+    p->h_tb = take(sizeof(int64_t) * (size_t)(h.T + 1));
   } else {
-    p->h_slot = p->h_first = p->h_tcnt = 0;
+    p->h_slot = p->h_first = p->h_tcnt = p->h_tb = 0;
   }
   p->total = o;
   return true;

@@ -109,11 +109,11 @@ struct Plan {
   size_t sgr, sscale;  // grad row and mean scale of each sorted occurrence
   size_t tile_hist, digit_tot;
   size_t unique, seg_off, counts, inverse;
-  size_t misc;  // uint32[64 + 2T]
+  size_t misc;  // uint32[64 + 3T]
   size_t part_head, part_tail, span_list, long_list;
   size_t chunk_base;  // heads in the earlier chunks of the chunk's 256-position block
   size_t head_base;   // heads before each 256-position block (nnz / 256 + 1)
-  size_t h_slot, h_first, h_tcnt;  // hash find-or-insert
+  size_t h_slot, h_first, h_tcnt, h_tb;  // hash find-or-insert
   size_t total = 0;
 };
 
@@ -126,7 +126,7 @@ enum : int {
   kMiscLongCount = 4,
   kMiscNotOneHot = 5,  // some bag of the prepared batch does not hold exactly one id
   kMiscFixDone = 6,    // blocks of the span fixup that have finished
-  kMiscHashNew = 8,  // uint32 per table from here (up to T)
+  kMiscHashNew = 8,  // per table: new keys [T], their base rank [T], block part [T]
 };
 
 bool make_plan(const Handle& h, int64_t B, int64_t nnz, Plan* p);

@@ -10,25 +10,27 @@
 // Table t owns `cap` slots of 16 bytes {key, row}; an empty slot holds
 // key = row = all ones.  The home slot of a key is SplitMix64's finalizer of
 // the key masked to cap - 1; collisions probe linearly.  One call runs:
-//   k_hash_probe   one thread per occurrence: look the key up; a live key
-//                  gives its row.  A missing key claims a slot with a 64-bit
+//   k_hash_probe   one thread per occurrence: look the key up (plain 16-byte
+//                  slot loads first); a live key gives its row.  A missing key claims a slot with a 64-bit
 //                  CAS on the key word (lock-free), and every occurrence of it
 //                  lowers the slot's row word to (PENDING | j) with atomicMin,
 //                  which leaves the first occurrence j in the slot.  A probe
 //                  sequence is bounded by `cap`: running out marks the call
 //                  full instead of looping.
-//   k_hash_first   flags first occurrences; per-block counts; per-table new-key
-//                  counts.
-//   k_hash_plan    one block: block bases (exclusive scan), per-table bases,
-//                  and the call's capacity decision (all-or-nothing).
+//   k_hash_first   flags first occurrences; per-block counts, and per table
+//                  the count before its first position inside its block.
+//   k_hash_plan    one block: block bases (exclusive scan), per-table bases
+//                  and new-key counts, and the call's capacity decision
+//                  (all-or-nothing).
 //   k_hash_assign  a first occurrence of table t with rank r (its order among
 //                  table t's first occurrences) writes row n_live[t] + r into
 //                  its slot and lists itself for initialisation; when the call
 //                  is full it empties the claimed slot again instead, which
 //                  restores the table exactly (the slot was empty before).
-//   k_hash_init    new rows: W = init_std * Box-Muller normal of the counter
-//                  draws (seed, t, key, 2d) and (.., 2d+1); G = accum_init.
-//   k_hash_finish  ids of new keys from their slots, live-row counters.
+//   k_hash_finish  ids of new keys from their slots, live-row counters and,
+//                  in the same launch, the new rows: W = init_std *
+//                  Box-Muller normal of the counter draws (seed, t, key, 2d)
+//                  and (.., 2d+1); G = accum_init.
 // Row assignment follows first occurrence and is deterministic; which slot a
 // key lands in depends on CAS order and is not part of the contract.
 #include "embtab_internal.hpp"
@@ -38,6 +40,7 @@ namespace embtab {
 namespace {
 
 constexpr uint32_t kNoSlot = 0xFFFFFFFFu;
+constexpr int64_t kFastProbes = 8;  // plain-load probes before the atomic path
 
 __device__ inline int32_t table_of(const int64_t* tb, int32_t T, int64_t j) {
   // tb[t] = first occurrence of table t (T + 1 entries, non-decreasing).
@@ -50,13 +53,37 @@ __device__ inline int32_t table_of(const int64_t* tb, int32_t T, int64_t j) {
   return lo;
 }
 
-__device__ inline void load_table_bounds(int64_t* tb, const int64_t* offsets, int64_t B, int32_t T,
-                                         int64_t nnz) {
+// First occurrence of every table (T + 1 entries), clamped to [0, nnz] and
+// made non-decreasing (a running maximum), so that tables are contiguous
+// ranges of occurrences even when the offsets are not valid.  Computed once
+// per call by k_hash_start; the other kernels copy it to LDS.
+__device__ inline void load_table_bounds(int64_t* tb, const int64_t* __restrict__ tbw, int32_t T) {
+  for (int t = threadIdx.x; t <= T; t += blockDim.x) tb[t] = tbw[t];
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(256) void k_hash_start(const int64_t* __restrict__ offsets, int64_t B,
+                                                    int32_t T, int64_t nnz,
+                                                    int64_t* __restrict__ tbw,
+                                                    uint32_t* __restrict__ misc, int32_t nzero) {
+  extern __shared__ int64_t tb[];
+  for (int i = threadIdx.x; i < nzero; i += blockDim.x) misc[i] = 0u;
   for (int t = threadIdx.x; t <= T; t += blockDim.x) {
-    int64_t v = offsets[(int64_t)t * B];
+    const int64_t v = offsets[(int64_t)t * B];
     tb[t] = v < 0 ? 0 : (v > nnz ? nnz : v);
   }
   __syncthreads();
+  for (int o = 1; o <= T; o <<= 1) {  // running maximum, log-step (T + 1 <= 1025)
+    int64_t mine[5];
+    int k = 0;
+    for (int t = threadIdx.x; t <= T; t += blockDim.x, ++k)
+      mine[k] = (t >= o && tb[t - o] > tb[t]) ? tb[t - o] : tb[t];
+    __syncthreads();
+    k = 0;
+    for (int t = threadIdx.x; t <= T; t += blockDim.x, ++k) tb[t] = mine[k];
+    __syncthreads();
+  }
+  for (int t = threadIdx.x; t <= T; t += blockDim.x) tbw[t] = tb[t];
 }
 
 struct Slot {
@@ -65,11 +92,11 @@ struct Slot {
 };
 
 __global__ __launch_bounds__(256) void k_hash_probe(
-    const int64_t* __restrict__ offsets, const uint64_t* __restrict__ keys, int64_t B, int32_t T,
+    const int64_t* __restrict__ tbw, const uint64_t* __restrict__ keys, int64_t B, int32_t T,
     int64_t nnz, Slot* __restrict__ slots, int64_t cap, int64_t* __restrict__ ids_out,
     uint32_t* __restrict__ slot_of, uint32_t* __restrict__ flags, uint32_t* __restrict__ misc) {
   extern __shared__ int64_t tb[];
-  load_table_bounds(tb, offsets, B, T, nnz);
+  load_table_bounds(tb, tbw, T);
   const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (j >= nnz) return;
   const uint64_t key = keys[j];
@@ -84,7 +111,20 @@ __global__ __launch_bounds__(256) void k_hash_probe(
   const uint64_t mask = (uint64_t)cap - 1u;
   const uint64_t pend = kPendingBit | (uint64_t)j;
   uint64_t s = slot_mix(key) & mask;
-  for (int64_t probe = 0; probe < cap; ++probe, s = (s + 1) & mask) {
+  int64_t probe = 0;
+  // Keys inserted by earlier calls are found with plain 16-byte slot loads
+  // (key and row together); an empty slot or a key still pending in this call
+  // goes on with the atomic protocol below, from the same slot.
+  for (; probe < kFastProbes && probe < cap; ++probe, s = (s + 1) & mask) {
+    const Slot sl = st[s];
+    if (sl.key == key && sl.row < kPendingBit) {
+      ids_out[j] = (int64_t)sl.row;
+      slot_of[j] = kNoSlot;
+      return;
+    }
+    if (sl.key == kEmptyKey || sl.key == key) break;
+  }
+  for (; probe < cap; ++probe, s = (s + 1) & mask) {
     uint64_t k = __hip_atomic_load(&st[s].key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (k == kEmptyKey) {
       const uint64_t old = atomicCAS((unsigned long long*)&st[s].key, (unsigned long long)kEmptyKey,
@@ -115,17 +155,19 @@ __device__ inline bool is_first(const Slot* slots, int64_t cap, const uint32_t* 
   return slots[(size_t)t * (size_t)cap + s].row == (kPendingBit | (uint64_t)j);
 }
 
-__global__ __launch_bounds__(256) void k_hash_first(const int64_t* __restrict__ offsets, int64_t B,
+// Per block: the number of first occurrences (bcnt) and, for every table
+// whose first occurrence position tb[t] falls in this block, the number of
+// first occurrences of the block before tb[t] (tpart[t]).  With the block
+// bases these give each table's base rank without device atomics.
+__global__ __launch_bounds__(256) void k_hash_first(const int64_t* __restrict__ tbw, int64_t B,
                                                     int32_t T, int64_t nnz,
                                                     const Slot* __restrict__ slots, int64_t cap,
                                                     const uint32_t* __restrict__ slot_of,
                                                     uint32_t* __restrict__ bcnt,
-                                                    uint32_t* __restrict__ misc) {
+                                                    uint32_t* __restrict__ tpart) {
   extern __shared__ int64_t tb[];
-  __shared__ uint32_t lds_cnt;
-  load_table_bounds(tb, offsets, B, T, nnz);
-  if (threadIdx.x == 0) lds_cnt = 0u;
-  __syncthreads();
+  __shared__ uint32_t lds4[4];
+  load_table_bounds(tb, tbw, T);
   const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   bool f = false;
   int32_t t = 0;
@@ -133,28 +175,30 @@ __global__ __launch_bounds__(256) void k_hash_first(const int64_t* __restrict__ 
     t = table_of(tb, T, j);
     f = is_first(slots, cap, slot_of, t, j);
   }
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const uint64_t m = __ballot(f);
-  if ((threadIdx.x & 63) == 0 && m) atomicAdd(&lds_cnt, (uint32_t)__popcll(m));
-  // per-table totals: aggregate lanes of the same table within the wave
-  if (f) {
-    const int32_t t0 = __shfl(t, __ffsll((unsigned long long)m) - 1, 64);
-    const uint64_t same = __ballot(f && t == t0);
-    if (t == t0) {
-      if (lanes_below(same) == 0u) atomicAdd(&misc[kMiscHashNew + t], (uint32_t)__popcll(same));
-    } else {
-      atomicAdd(&misc[kMiscHashNew + t], 1u);
-    }
-  }
+  if (lane == 0) lds4[w] = (uint32_t)__popcll(m);
   __syncthreads();
-  if (threadIdx.x == 0) bcnt[blockIdx.x] = lds_cnt;
+  uint32_t before = 0;
+  for (int i = 0; i < w; ++i) before += lds4[i];
+  before += lanes_below(m);  // first occurrences of this block before j
+  if (j < nnz) {
+    // tables starting at j: t and the empty tables just before it
+    for (int32_t u = t; u >= 0 && tb[u] == j; --u) tpart[u] = before;
+  }
+  if (threadIdx.x == 0) bcnt[blockIdx.x] = lds4[0] + lds4[1] + lds4[2] + lds4[3];
 }
 
 __global__ __launch_bounds__(256) void k_hash_plan(uint32_t* __restrict__ bcnt, uint32_t nblocks,
-                                                   int32_t T, const int64_t* __restrict__ n_live,
+                                                   const int64_t* __restrict__ tbw, int32_t T,
+                                                   int64_t nnz,
+                                                   const uint32_t* __restrict__ tpart,
+                                                   const int64_t* __restrict__ n_live,
                                                    const int64_t* __restrict__ rows,
                                                    uint32_t* __restrict__ misc,
                                                    uint32_t* __restrict__ flags) {
   __shared__ uint32_t lds4[4];
+  __shared__ uint32_t s_full;
   uint32_t carry = 0;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   for (uint32_t base = 0; base < nblocks; base += 256) {
@@ -176,29 +220,38 @@ __global__ __launch_bounds__(256) void k_hash_plan(uint32_t* __restrict__ bcnt, 
     if (idx < nblocks) bcnt[idx] = carry + before + x - v;
     carry += all;
   }
+  if (threadIdx.x == 0) s_full = misc[kMiscHashOverflow];
+  __syncthreads();
+  // table t's first occurrences have ranks [base_t, base_{t+1}) among this
+  // call's first occurrences, in occurrence (and so table) order
+  auto table_base = [&](int32_t t) -> uint32_t {
+    const int64_t q = tbw[t];  // tbw[T] = nnz
+    if (q >= nnz) return carry;
+    return bcnt[q >> 8] + tpart[t];
+  };
+  for (int32_t t = threadIdx.x; t < T; t += blockDim.x) {
+    const uint32_t b0 = table_base(t), b1 = table_base(t + 1);
+    const uint32_t nw = b1 >= b0 ? b1 - b0 : 0u;
+    misc[kMiscHashNew + t] = nw;
+    misc[kMiscHashNew + T + t] = b0;
+    if (n_live[t] + (int64_t)nw > rows[t]) s_full = 1u;  // every writer stores 1
+  }
+  __syncthreads();
   if (threadIdx.x == 0) {
-    uint32_t full = misc[kMiscHashOverflow];
-    uint32_t acc = 0;
-    for (int t = 0; t < T; ++t) {
-      const uint32_t nw = misc[kMiscHashNew + t];
-      misc[kMiscHashNew + T + t] = acc;
-      acc += nw;
-      if (n_live[t] + (int64_t)nw > rows[t]) full = 1u;
-    }
-    misc[kMiscHashOverflow] = full;
-    misc[kMiscNumUnique] = acc;  // new keys of this call (all tables)
-    if (full) atomicOr(flags, EMB_FLAG_TABLE_FULL);
+    misc[kMiscHashOverflow] = s_full;
+    misc[kMiscNumUnique] = carry;  // new keys of this call (all tables)
+    if (s_full) atomicOr(flags, EMB_FLAG_TABLE_FULL);
   }
 }
 
 __global__ __launch_bounds__(256) void k_hash_assign(
-    const int64_t* __restrict__ offsets, int64_t B, int32_t T, int64_t nnz,
+    const int64_t* __restrict__ tbw, int64_t B, int32_t T, int64_t nnz,
     Slot* __restrict__ slots, int64_t cap, const uint32_t* __restrict__ slot_of,
     const uint32_t* __restrict__ bbase, const int64_t* __restrict__ n_live,
     const uint32_t* __restrict__ misc, uint32_t* __restrict__ newlist) {
   extern __shared__ int64_t tb[];
   __shared__ uint32_t lds4[4];
-  load_table_bounds(tb, offsets, B, T, nnz);
+  load_table_bounds(tb, tbw, T);
   const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   bool f = false;
   int32_t t = 0;
@@ -227,27 +280,52 @@ __global__ __launch_bounds__(256) void k_hash_assign(
   newlist[g] = (uint32_t)j;
 }
 
-__global__ __launch_bounds__(256) void k_hash_init(
-    const int64_t* __restrict__ offsets, const uint64_t* __restrict__ keys, int64_t B, int32_t T,
+// Blocks [0, nfin) write the ids of this call's new keys (and block 0 the
+// live-row counters); the blocks after them initialise the new rows:
+// W = init_std * Box-Muller normal of the counter draws (seed, t, key, 2d) and
+// (.., 2d+1), G = accum_init.  Nothing else reads n_live in this step.
+__global__ __launch_bounds__(256) void k_hash_finish(
+    const int64_t* __restrict__ tbw, const uint64_t* __restrict__ keys, int64_t B, int32_t T,
     int64_t nnz, const Slot* __restrict__ slots, int64_t cap, const uint32_t* __restrict__ slot_of,
-    const uint32_t* __restrict__ newlist, const uint32_t* __restrict__ misc,
-    const int64_t* __restrict__ row_off, float* __restrict__ W, float* __restrict__ G, int32_t D,
-    uint64_t seed, float stdv, float g0) {
+    int64_t* __restrict__ ids_out, const uint32_t* __restrict__ newlist,
+    const uint32_t* __restrict__ misc, int64_t* __restrict__ n_live,
+    const int64_t* __restrict__ row_off, const int64_t* __restrict__ rows, float* __restrict__ W,
+    float* __restrict__ G, int32_t D,
+    uint64_t seed, float stdv, float g0, uint32_t nfin) {
   extern __shared__ int64_t tb[];
-  load_table_bounds(tb, offsets, B, T, nnz);
-  if (misc[kMiscHashOverflow]) return;
+  load_table_bounds(tb, tbw, T);
+  const bool full = misc[kMiscHashOverflow] != 0u;
+  if (blockIdx.x < nfin) {
+    if (blockIdx.x == 0 && !full)
+      for (int t = threadIdx.x; t < T; t += blockDim.x)
+        n_live[t] += (int64_t)misc[kMiscHashNew + t];
+    const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (j >= nnz) return;
+    const uint32_t s = slot_of[j];
+    if (s == kNoSlot) return;
+    if (full) {
+      ids_out[j] = -1;
+      return;
+    }
+    const int32_t t = table_of(tb, T, j);
+    ids_out[j] = (int64_t)slots[(size_t)t * (size_t)cap + s].row;
+    return;
+  }
+  if (full) return;
   const uint32_t nnew = misc[kMiscNumUnique];
   const int32_t D4 = D >> 2;
   const uint64_t total = (uint64_t)nnew * (uint64_t)D4;
   const uint64_t s0 = sm64(seed);
-  for (uint64_t e = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
-       e += (uint64_t)gridDim.x * blockDim.x) {
+  const uint32_t ib = blockIdx.x - nfin, nib = gridDim.x - nfin;
+  for (uint64_t e = (uint64_t)ib * blockDim.x + threadIdx.x; e < total;
+       e += (uint64_t)nib * blockDim.x) {
     const uint32_t g = (uint32_t)(e / D4);
     const int32_t d4 = (int32_t)(e - (uint64_t)g * D4);
     const uint32_t j = newlist[g];
     const int32_t t = table_of(tb, T, j);
     const uint64_t key = keys[j];
     const uint64_t row = slots[(size_t)t * (size_t)cap + slot_of[j]].row;
+    if (row >= (uint64_t)rows[t]) continue;  // only with invalid offsets
     const uint64_t pre = sm64(sm64(s0 ^ (uint64_t)t) ^ key);
     f4 w;
 #pragma unroll
@@ -263,30 +341,6 @@ __global__ __launch_bounds__(256) void k_hash_init(
     *reinterpret_cast<f4*>(W + gi) = w;
     *reinterpret_cast<f4*>(G + gi) = f4{g0, g0, g0, g0};
   }
-}
-
-__global__ __launch_bounds__(256) void k_hash_finish(
-    const int64_t* __restrict__ offsets, int64_t B, int32_t T, int64_t nnz,
-    const Slot* __restrict__ slots, int64_t cap, const uint32_t* __restrict__ slot_of,
-    int64_t* __restrict__ ids_out, const uint32_t* __restrict__ misc) {
-  extern __shared__ int64_t tb[];
-  load_table_bounds(tb, offsets, B, T, nnz);
-  const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (j >= nnz) return;
-  const uint32_t s = slot_of[j];
-  if (s == kNoSlot) return;
-  if (misc[kMiscHashOverflow]) {
-    ids_out[j] = -1;
-    return;
-  }
-  const int32_t t = table_of(tb, T, j);
-  ids_out[j] = (int64_t)slots[(size_t)t * (size_t)cap + s].row;
-}
-
-__global__ void k_hash_live(int32_t T, int64_t* __restrict__ n_live,
-                            const uint32_t* __restrict__ misc) {
-  const int t = threadIdx.x;
-  if (t < T && !misc[kMiscHashOverflow]) n_live[t] += (int64_t)misc[kMiscHashNew + t];
 }
 
 __global__ __launch_bounds__(256) void k_hash_export(const Slot* __restrict__ st, int64_t cap,
@@ -315,24 +369,25 @@ hipError_t launch_hash_find_or_insert(const Handle& h, const Plan& p, const int6
   const unsigned nb = (unsigned)((nnz + 255) / 256);
   const unsigned grid = nb > 0 ? nb : 1;
   phase_mark(h, EMB_PHASE_HASH, false, s);
-  launch_zero_words(misc, kMiscHashNew + 2 * h.T, s);
-  hipLaunchKernelGGL(k_hash_probe, dim3(grid), dim3(256), shm, s, offsets, keys, p.B, h.T, nnz,
+  int64_t* tbw = reinterpret_cast<int64_t*>(ws + p.h_tb);
+  hipLaunchKernelGGL(k_hash_start, dim3(1), dim3(256), shm, s, offsets, p.B, h.T, nnz, tbw, misc,
+                     kMiscHashNew + 2 * h.T);
+  hipLaunchKernelGGL(k_hash_probe, dim3(grid), dim3(256), shm, s, tbw, keys, p.B, h.T, nnz,
                      slots, h.capacity, ids_out, slot_of, h.sv.flags, misc);
-  hipLaunchKernelGGL(k_hash_first, dim3(grid), dim3(256), shm, s, offsets, p.B, h.T, nnz, slots,
-                     h.capacity, slot_of, bcnt, misc);
-  hipLaunchKernelGGL(k_hash_plan, dim3(1), dim3(256), 0, s, bcnt, nb, h.T, h.sv.n_live,
-                     h.sv.rows, misc, h.sv.flags);
-  hipLaunchKernelGGL(k_hash_assign, dim3(grid), dim3(256), shm, s, offsets, p.B, h.T, nnz, slots,
+  uint32_t* tpart = misc + kMiscHashNew + 2 * h.T;
+  hipLaunchKernelGGL(k_hash_first, dim3(grid), dim3(256), shm, s, tbw, p.B, h.T, nnz, slots,
+                     h.capacity, slot_of, bcnt, tpart);
+  hipLaunchKernelGGL(k_hash_plan, dim3(1), dim3(256), 0, s, bcnt, nb, tbw, h.T, nnz, tpart,
+                     h.sv.n_live, h.sv.rows, misc, h.sv.flags);
+  hipLaunchKernelGGL(k_hash_assign, dim3(grid), dim3(256), shm, s, tbw, p.B, h.T, nnz, slots,
                      h.capacity, slot_of, bcnt, h.sv.n_live, misc, newlist);
-  const int64_t igrid_max = (nnz * (h.D / 4) + 255) / 256;
-  const unsigned igrid = (unsigned)(igrid_max < 1 ? 1 : (igrid_max > 4096 ? 4096 : igrid_max));
-  hipLaunchKernelGGL(k_hash_init, dim3(igrid), dim3(256), shm, s, offsets, keys, p.B, h.T, nnz,
-                     slots, h.capacity, slot_of, newlist, misc, h.sv.row_off, h.W, h.G, h.D,
-                     h.seed, h.stdv, h.accum0);
-  hipLaunchKernelGGL(k_hash_finish, dim3(grid), dim3(256), shm, s, offsets, p.B, h.T, nnz, slots,
-                     h.capacity, slot_of, ids_out, misc);
-  hipLaunchKernelGGL(k_hash_live, dim3(1), dim3(h.T < 64 ? 64 : ((h.T + 63) / 64) * 64), 0, s,
-                     h.T, h.sv.n_live, misc);
+  // new rows: at most one per occurrence; enough blocks for a cold start
+  int64_t igrid = (nnz * (h.D / 4) + 255) / 256;
+  igrid = igrid < 1 ? 1 : (igrid > 2048 ? 2048 : igrid);
+  hipLaunchKernelGGL(k_hash_finish, dim3(grid + (unsigned)igrid), dim3(256), shm, s, tbw,
+                     keys, p.B, h.T, nnz, slots, h.capacity, slot_of, ids_out, newlist, misc,
+                     h.sv.n_live, h.sv.row_off, h.sv.rows, h.W, h.G, h.D, h.seed, h.stdv,
+                     h.accum0, grid);
   phase_mark(h, EMB_PHASE_HASH, true, s);
   return hipGetLastError();
 }

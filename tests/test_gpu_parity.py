@@ -420,6 +420,29 @@ def test_hash_full_is_all_or_nothing_and_reserved_key():
     check_hash_state(tabs, o)
 
 
+def test_hash_ragged_tables_and_empty_table():
+    # Tables start at arbitrary positions inside the 256-occurrence blocks,
+    # table 2 has no occurrences at all and table 4 repeats one key: the
+    # per-table new-key counts and bases come from block partial counts.
+    T, B = 5, 97
+    rows = np.full(T, 900, np.int64)
+    tabs, o = make_pair(rows, 16, seed=13, hashed=True, cap=2048)
+    rng = np.random.default_rng(5)
+    for call in range(3):
+        lens = rng.integers(0, 6, T * B)
+        lens[2 * B:3 * B] = 0
+        offsets = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+        keys = rng.integers(1, 400 + 200 * call, offsets[-1]).astype(np.uint64)
+        a, b = offsets[4 * B], offsets[5 * B]
+        keys[a:b] = 77
+        ids = _hash_call(tabs, offsets, keys, B)
+        ref, fl = o.find_or_insert(offsets, keys, B)
+        assert fl == 0
+        np.testing.assert_array_equal(ids, ref)
+        assert status(tabs) == (eb.EMB_OK, 0)
+    check_hash_state(tabs, o)
+
+
 def test_hash_then_train_step():
     w = synth.workload(5, T=2, B=2000, universe=20_000, hash_capacity=1 << 15)
     w.rows = np.full(2, int(0.625 * (1 << 15)), np.int64)
