@@ -90,9 +90,19 @@ inline int vec_per_lane(int D) {
   return (D / 4 + sg - 1) / sg;
 }
 // Sorted occurrences per reduction chunk.
+// Sorted positions per reduction chunk: at least kChunkMin, and a whole number
+// of sub-group rounds (MPL metadata entries per lane).
+#ifndef EMBTAB_CHUNK_MIN
+#define EMBTAB_CHUNK_MIN 32
+#endif
+constexpr int kChunkMin = EMBTAB_CHUNK_MIN;
+template <int SG>
+constexpr int chunk_rounds() {
+  return SG >= kChunkMin ? 1 : kChunkMin / SG;
+}
 inline int chunk_len(int D) {
   int sg = subgroup_lanes(D);
-  return sg >= 32 ? sg : 32;
+  return sg >= kChunkMin ? sg : kChunkMin;
 }
 
 // ---------------------------------------------------------------- workspace plan

@@ -389,7 +389,7 @@ template <int SG, int VEC, bool MEAN>
 hipError_t launch_sorted_t(const Handle& h, const Plan& p, const int64_t* offsets,
                            const int64_t* ids, const uint32_t* keys, const uint32_t* perm,
                            float* out, char* ws, hipStream_t s) {
-  constexpr int MPL = SG >= 32 ? 1 : 32 / SG;
+  constexpr int MPL = chunk_rounds<SG>();
   constexpr int SGPB = 256 / SG;
   const int64_t chunks = (p.nnz + SG * MPL - 1) / (SG * MPL);
   const int64_t S = tile_samples(h.T);

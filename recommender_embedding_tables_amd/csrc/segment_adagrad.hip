@@ -377,10 +377,10 @@ __global__ __launch_bounds__(NT) void k_fixup(
 template <int SG, int VEC, bool MEAN>
 hipError_t launch_t(const Handle& h, const Plan& p, const uint32_t* keys, const uint32_t* perm,
                     const float* grad_out, float lr, float eps, char* ws, hipStream_t s) {
-  constexpr int MPL = SG >= 32 ? 1 : 32 / SG;
+  constexpr int MPL = chunk_rounds<SG>();
   constexpr int UF = VEC > 1 ? 2 : (SG < kSegUF ? SG : kSegUF);
   constexpr int SGPB = 256 / SG;
-  static_assert(SG * MPL >= 32, "chunk");
+  static_assert(SG * MPL >= kChunkMin, "chunk");
   const uint32_t n = (uint32_t)p.nnz;
   if (n == 0) return hipSuccess;
   const int64_t chunks = (p.nnz + SG * MPL - 1) / (SG * MPL);
