@@ -189,37 +189,75 @@ __global__ __launch_bounds__(256) void k_hash_first(const int64_t* __restrict__ 
   if (threadIdx.x == 0) bcnt[blockIdx.x] = lds4[0] + lds4[1] + lds4[2] + lds4[3];
 }
 
-__global__ __launch_bounds__(256) void k_hash_plan(uint32_t* __restrict__ bcnt, uint32_t nblocks,
-                                                   const int64_t* __restrict__ tbw, int32_t T,
-                                                   int64_t nnz,
-                                                   const uint32_t* __restrict__ tpart,
-                                                   const int64_t* __restrict__ n_live,
-                                                   const int64_t* __restrict__ rows,
-                                                   uint32_t* __restrict__ misc,
-                                                   uint32_t* __restrict__ flags) {
-  __shared__ uint32_t lds4[4];
+// One block of 1024 threads.  Exclusive scan of the block counts in place
+// (each pass: 16 consecutive counts per thread, read and written as uint4).
+__global__ __launch_bounds__(1024) void k_hash_plan(uint32_t* __restrict__ bcnt, uint32_t nblocks,
+                                                    const int64_t* __restrict__ tbw, int32_t T,
+                                                    int64_t nnz,
+                                                    const uint32_t* __restrict__ tpart,
+                                                    const int64_t* __restrict__ n_live,
+                                                    const int64_t* __restrict__ rows,
+                                                    uint32_t* __restrict__ misc,
+                                                    uint32_t* __restrict__ flags) {
+  constexpr uint32_t PER = 16;
+  __shared__ uint32_t wsum[16];
   __shared__ uint32_t s_full;
   uint32_t carry = 0;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  for (uint32_t base = 0; base < nblocks; base += 256) {
-    const uint32_t idx = base + threadIdx.x;
-    const uint32_t v = idx < nblocks ? bcnt[idx] : 0u;
-    uint32_t x = v;
+  const uint32_t lane = threadIdx.x & 63u, w = threadIdx.x >> 6;
+  for (uint32_t base = 0; base < nblocks; base += 1024u * PER) {
+    const uint32_t lo = base + threadIdx.x * PER;
+    uint32_t v[PER];
+    if (lo + PER <= nblocks) {
+#pragma unroll
+      for (int q = 0; q < (int)PER / 4; ++q) {
+        const uint4 x = reinterpret_cast<const uint4*>(bcnt + lo)[q];
+        v[4 * q] = x.x;
+        v[4 * q + 1] = x.y;
+        v[4 * q + 2] = x.z;
+        v[4 * q + 3] = x.w;
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < (int)PER; ++q) v[q] = lo + q < nblocks ? bcnt[lo + q] : 0u;
+    }
+    uint32_t sum = 0;
+#pragma unroll
+    for (int q = 0; q < (int)PER; ++q) sum += v[q];
+    uint32_t x = sum;
+#pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
       const uint32_t y = (uint32_t)__shfl_up((int)x, o, 64);
-      if (lane >= o) x += y;
+      if (lane >= (uint32_t)o) x += y;
     }
-    if (lane == 63) lds4[w] = x;
+    if (lane == 63u) wsum[w] = x;
     __syncthreads();
-    uint32_t before = 0, all = 0;
-    for (int i = 0; i < 4; ++i) {
-      before += i < w ? lds4[i] : 0u;
-      all += lds4[i];
+    uint32_t before = 0, total = 0;
+#pragma unroll
+    for (uint32_t i = 0; i < 16u; ++i) {
+      before += i < w ? wsum[i] : 0u;
+      total += wsum[i];
     }
     __syncthreads();
-    if (idx < nblocks) bcnt[idx] = carry + before + x - v;
-    carry += all;
+    uint32_t run = carry + before + x - sum;
+#pragma unroll
+    for (int q = 0; q < (int)PER; ++q) {
+      const uint32_t c = v[q];
+      v[q] = run;
+      run += c;
+    }
+    if (lo + PER <= nblocks) {
+#pragma unroll
+      for (int q = 0; q < (int)PER / 4; ++q)
+        reinterpret_cast<uint4*>(bcnt + lo)[q] = make_uint4(v[4 * q], v[4 * q + 1], v[4 * q + 2],
+                                                            v[4 * q + 3]);
+    } else {
+#pragma unroll
+      for (int q = 0; q < (int)PER; ++q)
+        if (lo + q < nblocks) bcnt[lo + q] = v[q];
+    }
+    carry += total;
   }
+  __syncthreads();  // the bases written above are read back below
   if (threadIdx.x == 0) s_full = misc[kMiscHashOverflow];
   __syncthreads();
   // table t's first occurrences have ranks [base_t, base_{t+1}) among this
@@ -377,7 +415,7 @@ hipError_t launch_hash_find_or_insert(const Handle& h, const Plan& p, const int6
   uint32_t* tpart = misc + kMiscHashNew + 2 * h.T;
   hipLaunchKernelGGL(k_hash_first, dim3(grid), dim3(256), shm, s, tbw, p.B, h.T, nnz, slots,
                      h.capacity, slot_of, bcnt, tpart);
-  hipLaunchKernelGGL(k_hash_plan, dim3(1), dim3(256), 0, s, bcnt, nb, tbw, h.T, nnz, tpart,
+  hipLaunchKernelGGL(k_hash_plan, dim3(1), dim3(1024), 0, s, bcnt, nb, tbw, h.T, nnz, tpart,
                      h.sv.n_live, h.sv.rows, misc, h.sv.flags);
   hipLaunchKernelGGL(k_hash_assign, dim3(grid), dim3(256), shm, s, tbw, p.B, h.T, nnz, slots,
                      h.capacity, slot_of, bcnt, h.sv.n_live, misc, newlist);
