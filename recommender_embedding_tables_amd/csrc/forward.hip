@@ -322,9 +322,12 @@ __global__ __launch_bounds__(256) void k_fwd_sorted(
   }
 }
 
-// Samples per tile of the pooled kernel: about kFwdTileBags bags of all tables.
-int64_t tile_samples(int T) {
-  int64_t S = kFwdTileBags / T;
+// Samples per tile of the pooled kernel: about kFwdTileBags bags of all
+// tables, and about as many ids, so that long bags still give enough blocks.
+int64_t tile_samples(int T, int64_t B, int64_t nnz) {
+  const int64_t bags = B * (int64_t)T;
+  const int64_t mean_len = bags > 0 ? (nnz + bags - 1) / bags : 1;
+  int64_t S = kFwdTileBags / ((int64_t)T * (mean_len > 1 ? mean_len : 1));
   return S > 64 ? 64 : (S < 1 ? 1 : S);
 }
 
@@ -336,7 +339,7 @@ constexpr int fwd_unroll() {
 template <int SG, int VEC, bool MEAN>
 hipError_t launch_t(const Handle& h, const int64_t* offsets, const int64_t* ids, int64_t B,
                     int64_t nnz, float* out, hipStream_t s) {
-  const int64_t S = tile_samples(h.T);
+  const int64_t S = tile_samples(h.T, B, nnz);
   const int64_t grid = (B + S - 1) / S;
   if (grid == 0) return hipSuccess;
   hipLaunchKernelGGL((k_bag_forward<SG, VEC, MEAN, fwd_unroll<VEC>()>), dim3((unsigned)grid),
@@ -392,7 +395,7 @@ hipError_t launch_sorted_t(const Handle& h, const Plan& p, const int64_t* offset
   constexpr int MPL = chunk_rounds<SG>();
   constexpr int SGPB = 256 / SG;
   const int64_t chunks = (p.nnz + SG * MPL - 1) / (SG * MPL);
-  const int64_t S = tile_samples(h.T);
+  const int64_t S = tile_samples(h.T, p.B, p.nnz);
   const int64_t tiles = (p.B + S - 1) / S;
   int64_t grid = (chunks + SGPB - 1) / SGPB;
   grid = grid > tiles ? grid : tiles;  // enough blocks for either path
