@@ -150,6 +150,56 @@ def test_full_cfg2_26_one_hot_tables():
     run_dense_workload(2, steps=2, exact_forward=True)
 
 
+def test_full_cfg2_pipelined_schedule():
+    # The launch pattern bench.py times by default: batch i+1's
+    # emb_bag_prepare on a second stream into the other of two workspaces,
+    # beside batch i's forward_prepared and backward_prepared on the main
+    # stream.  Rows are checked against the oracle after each step.
+    need_bytes(44 << 30)
+    w = synth.workload(2)
+    tabs, o = tables_for(w)
+    steps = 3
+    batches = [synth.gen_batch(w, b) for b in range(steps)]
+    d_batches = [(_t(off), _t(ids)) for off, ids in batches]
+    grads = [synth.gen_grad(w, b) for b in range(steps)]
+    pool = eb.EMB_POOL_SUM
+    nnz = batches[0][1].size
+    ws0, need = tabs.workspace(w.B, nnz)
+    wss = [ws0, torch.empty_like(ws0)]
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    done = [torch.cuda.Event(), torch.cuda.Event()]
+    prep = [torch.cuda.Event(), torch.cuda.Event()]
+    out = torch.empty((w.B, w.T, w.D), dtype=torch.float32, device=DEV)
+
+    def prepare(i):
+        side.wait_event(done[i % 2])
+        d_off, d_ids = d_batches[i]
+        eb.check(eb.emb_bag_prepare(tabs.handle, d_off, d_ids, w.B, nnz, pool, wss[i % 2], need,
+                                    side), "prepare")
+        prep[i % 2].record(side)
+
+    prepare(0)
+    for i in range(steps):
+        if i + 1 < steps:
+            prepare(i + 1)
+        main.wait_event(prep[i % 2])
+        d_off, d_ids = d_batches[i]
+        eb.check(eb.emb_bag_forward_prepared(tabs.handle, d_off, d_ids, w.B, nnz, pool, out,
+                                             wss[i % 2], need, main), "forward")
+        g = _t(grads[i])
+        eb.check(eb.emb_bag_backward_adagrad_prepared(tabs.handle, w.B, nnz, pool, g, w.lr, w.eps,
+                                                      wss[i % 2], need, main), "backward")
+        done[i % 2].record(main)
+        torch.cuda.synchronize()
+        offsets, ids = batches[i]
+        check_forward(out, o, w, offsets, ids, exact=(i == 0))
+        o.backward_adagrad(offsets, ids, w.B, False, grads[i], w.lr, w.eps)
+        check_rows_after(tabs, o, w, offsets, ids, grads[i], None, seed=i)
+    assert eb.emb_status_sync(tabs.handle) == (eb.EMB_OK, 0)
+    tabs.close()
+
+
 def test_full_cfg3_multi_hot_mean():
     need_bytes(30 << 30)
     run_dense_workload(3, steps=1)
