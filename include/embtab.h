@@ -41,7 +41,13 @@
  *                             unspecified, but no memory outside the given
  *                             arrays is touched;
  *      EMB_FLAG_RESERVED_KEY  a raw key equal to EMB_EMPTY_KEY (id -1);
- *      EMB_FLAG_TABLE_FULL    see emb_hash_find_or_insert.
+ *      EMB_FLAG_TABLE_FULL    see emb_hash_find_or_insert;
+ *      EMB_FLAG_CACHE_FULL    tiered tables: a cache set had no slot for a
+ *                             missing row (see emb_table_create_tiered); the
+ *                             outputs of that batch and the values of its
+ *                             rows are unspecified, every other row keeps its
+ *                             value and no memory outside the given arrays
+ *                             is touched.
  */
 #ifndef EMBTAB_H
 #define EMBTAB_H
@@ -64,13 +70,15 @@ typedef enum {
   EMB_ERR_BAD_OFFSETS = 5,
   EMB_ERR_RESERVED_KEY = 6,
   EMB_ERR_TABLE_FULL = 7,
-  EMB_ERR_HIP = 8
+  EMB_ERR_HIP = 8,
+  EMB_ERR_CACHE_FULL = 9
 } emb_status_t;
 
 #define EMB_FLAG_OUT_OF_RANGE 1u
 #define EMB_FLAG_BAD_OFFSETS 2u
 #define EMB_FLAG_RESERVED_KEY 4u
 #define EMB_FLAG_TABLE_FULL 8u
+#define EMB_FLAG_CACHE_FULL 32u
 
 /* The all-ones key marks an empty hash slot and may not be used as a key. */
 #define EMB_EMPTY_KEY 0xFFFFFFFFFFFFFFFFull
@@ -192,8 +200,9 @@ emb_status_t emb_bag_backward_adagrad_prepared(emb_table_t h, int64_t batch, int
                                                void* stream);
 
 /* Waits for `stream`, returns the highest-priority device error (TABLE_FULL,
- * RESERVED_KEY, BAD_OFFSETS, OUT_OF_RANGE, in that order) or EMB_OK, stores
- * the raw EMB_FLAG_* bits in *flags_out (HOST, may be NULL) and clears them. */
+ * CACHE_FULL, RESERVED_KEY, BAD_OFFSETS, OUT_OF_RANGE, in that order) or
+ * EMB_OK, stores the raw EMB_FLAG_* bits in *flags_out (HOST, may be NULL)
+ * and clears them. */
 emb_status_t emb_status_sync(emb_table_t h, void* stream, uint32_t* flags_out);
 
 /* HOST n_live_out[T]: rows handed out so far in each hashed table (waits for
@@ -245,6 +254,62 @@ emb_status_t emb_set_phase_events(emb_table_t h, void* const* events);
 
 /* Human-readable name of a status code (static string). */
 const char* emb_status_string(emb_status_t s);
+
+/* ------------------------------------------------------------------------
+ * Tiered tables: weights and accumulators in host memory, an HBM cache of hot
+ * rows (DeepRec page, section "deployment and serving", multi-level hybrid
+ * embedding storage: frequently used features on fast memory, rarely used ones
+ * on cheaper memory; OneFlow OneEmbedding page, closing section: layered
+ * storage for tables beyond device memory).  Every result equals that of the
+ * same table held wholly in device memory.
+ *
+ * The cache holds cache_rows rows in sets of EMB_CACHE_WAYS; a row's set is
+ * SplitMix64's finalizer of the row modulo the number of sets (a power of
+ * two).  emb_bag_prepare on a tiered table also looks every distinct row of
+ * the batch up: a hit marks its slot used by this batch; a miss claims the
+ * least recently used slot of its set that neither this batch nor the one
+ * prepared just before it uses, writes that slot's row (weights and
+ * accumulator) back to host memory and fetches the missing row into it.  So
+ * the prepare of batch i+1 may run beside the forward and backward of batch
+ * i on another stream, and must wait for the backward of batch i-1.  A set
+ * has to hold the distinct rows that two consecutive batches place in it;
+ * when it cannot, EMB_FLAG_CACHE_FULL is raised.  The forward and backward of
+ * a batch run on the cache (emb_bag_forward_prepared,
+ * emb_bag_backward_adagrad_prepared, or the one-call
+ * emb_bag_backward_adagrad); emb_bag_forward without a prepared workspace,
+ * hashed tiered tables and emb_hash_* are not supported.  Rows updated in the
+ * cache reach host memory when evicted or at emb_cache_flush. */
+#define EMB_CACHE_WAYS 16
+
+typedef struct {
+  float* host_weights;  /* [sum rows, D] fp32, host memory the device can read and write
+                           (pinned: hipHostMalloc or torch pin_memory), 16-byte aligned */
+  float* host_accum;    /* same shape */
+  int64_t cache_rows;   /* C: EMB_CACHE_WAYS * 2^k, C <= sum rows */
+  void* cache_state;    /* device, emb_cache_state_bytes(C) bytes, 256-byte aligned */
+} emb_tier_desc_t;
+
+/* Bytes of the cache state: per slot the row it holds and the step it was
+ * last used at, plus counters.  0 if cache_rows is not EMB_CACHE_WAYS * 2^k. */
+size_t emb_cache_state_bytes(int64_t cache_rows);
+
+/* Like emb_table_create, with desc->weights / desc->accum the HBM cache
+ * ([C, D] each) and the table itself in tier->host_weights / host_accum.
+ * init_storage must be 1: it initialises the host rows exactly as a dense
+ * table's (same counter-based values) and empties the cache.  desc->hashed
+ * must be 0 (else EMB_ERR_UNSUPPORTED).  EMB_ERR_INVALID_ARG for a null tier,
+ * null or misaligned pointers, init_storage 0, cache_rows that
+ * emb_cache_state_bytes rejects or above the table's total rows. */
+emb_status_t emb_table_create_tiered(const emb_table_desc_t* desc, const emb_tier_desc_t* tier,
+                                     void* stream, emb_table_t* out);
+
+/* Writes every row held in the cache back to host memory (the cache keeps
+ * them).  Afterwards the host arrays hold the table's current values. */
+emb_status_t emb_cache_flush(emb_table_t h, void* stream);
+
+/* HOST out: cumulative distinct rows looked up and misses over all prepares
+ * of h (waits for the stream). */
+emb_status_t emb_cache_stats(emb_table_t h, void* stream, int64_t* lookups, int64_t* misses);
 
 #ifdef __cplusplus
 }

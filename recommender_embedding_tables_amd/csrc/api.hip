@@ -84,6 +84,15 @@ bool make_plan(const Handle& h, int64_t B, int64_t nnz, Plan* p) {
   } else {
     p->h_slot = p->h_first = p->h_tcnt = p->h_tb = 0;
   }
+  if (h.tiered) {
+    p->c_slot = take(n4);       // cache slot of each distinct row
+    p->c_miss = take(2 * n4);   // misses: unique index, then row
+    p->c_vict = take(n4);       // evicted row of each miss
+    p->c_mslot = take(n4);      // slot of each miss
+    p->c_rowmap = take(n4);     // slot of each occurrence (batches that are not one-hot)
+  } else {
+    p->c_slot = p->c_miss = p->c_vict = p->c_mslot = p->c_rowmap = 0;
+  }
   p->total = o;
   return true;
 }
@@ -128,11 +137,13 @@ const char* emb_status_string(emb_status_t s) {
     case EMB_ERR_RESERVED_KEY: return "reserved key";
     case EMB_ERR_TABLE_FULL: return "table full";
     case EMB_ERR_HIP: return "HIP runtime error";
+    case EMB_ERR_CACHE_FULL: return "cache set full";
   }
   return "unknown status";
 }
 
-emb_status_t emb_table_create(const emb_table_desc_t* d, void* stream, emb_table_t* out) {
+static emb_status_t create_impl(const emb_table_desc_t* d, const emb_tier_desc_t* tier,
+                                void* stream, emb_table_t* out) {
   if (!d || !out) return EMB_ERR_INVALID_ARG;
   *out = nullptr;
   if (d->num_tables < 1 || d->num_tables > 1024) return EMB_ERR_INVALID_ARG;
@@ -156,9 +167,28 @@ emb_status_t emb_table_create(const emb_table_desc_t* d, void* stream, emb_table
       if ((double)d->rows_per_table[t] > (double)d->max_load * (double)d->hash_capacity)
         return EMB_ERR_INVALID_ARG;
   }
+  if (tier) {
+    if (d->hashed) return EMB_ERR_UNSUPPORTED;
+    // the step stamps of a cache state belong to the handle that filled it
+    if (!d->init_storage) return EMB_ERR_INVALID_ARG;
+    if (!tier->host_weights || !tier->host_accum || !tier->cache_state ||
+        !aligned16(tier->host_weights) || !aligned16(tier->host_accum) ||
+        (reinterpret_cast<uintptr_t>(tier->cache_state) & 255u) != 0)
+      return EMB_ERR_INVALID_ARG;
+    if (emb_cache_state_bytes(tier->cache_rows) == 0 || tier->cache_rows > total)
+      return EMB_ERR_INVALID_ARG;
+  }
   emb_table_s* tb = new (std::nothrow) emb_table_s();
   if (!tb) return EMB_ERR_INVALID_ARG;
   Handle& h = tb->h;
+  if (tier) {
+    h.tiered = true;
+    h.hostW = tier->host_weights;
+    h.hostG = tier->host_accum;
+    h.cache_rows = tier->cache_rows;
+    h.cache_sets = (uint32_t)(tier->cache_rows / kCacheWays);
+    h.cache_state = static_cast<char*>(tier->cache_state);
+  }
   h.T = d->num_tables;
   h.D = d->dim;
   h.rows.assign(d->rows_per_table, d->rows_per_table + h.T);
@@ -198,7 +228,16 @@ emb_status_t emb_table_create(const emb_table_desc_t* d, void* stream, emb_table
       e = hipMemcpyAsync(h.sv.row_off, host.data(), sizeof(int64_t) * host.size(),
                          hipMemcpyHostToDevice, s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);  // `host` goes out of scope
-    if (e == hipSuccess) e = launch_init_dense(h, s);
+    if (e == hipSuccess && h.tiered) {
+      // the table's rows live in host memory; the cache starts empty
+      Handle hh = h;
+      hh.W = h.hostW;
+      hh.G = h.hostG;
+      e = launch_init_dense(hh, s);
+      if (e == hipSuccess) e = launch_cache_init(h, s);
+    } else if (e == hipSuccess) {
+      e = launch_init_dense(h, s);
+    }
     if (e == hipSuccess && h.hashed)
       e = launch_fill_u64(static_cast<uint64_t*>(h.slots), kEmptyKey,
                           2 * (size_t)h.T * (size_t)h.capacity, s);
@@ -211,9 +250,50 @@ emb_status_t emb_table_create(const emb_table_desc_t* d, void* stream, emb_table
   return EMB_OK;
 }
 
+emb_status_t emb_table_create(const emb_table_desc_t* d, void* stream, emb_table_t* out) {
+  return create_impl(d, nullptr, stream, out);
+}
+
+size_t emb_cache_state_bytes(int64_t cache_rows) {
+  if (cache_rows < kCacheWays || cache_rows % kCacheWays != 0) return 0;
+  const int64_t sets = cache_rows / kCacheWays;
+  if ((sets & (sets - 1)) != 0 || cache_rows >= 0xFFFFFFFFll) return 0;
+  return cache_state_bytes(cache_rows);
+}
+
+emb_status_t emb_table_create_tiered(const emb_table_desc_t* d, const emb_tier_desc_t* tier,
+                                     void* stream, emb_table_t* out) {
+  if (!tier) return EMB_ERR_INVALID_ARG;
+  return create_impl(d, tier, stream, out);
+}
+
+emb_status_t emb_cache_flush(emb_table_t t, void* stream) {
+  if (!t) return EMB_ERR_INVALID_ARG;
+  if (!t->h.tiered) return EMB_ERR_UNSUPPORTED;
+  return hip_status(launch_cache_flush(t->h, static_cast<hipStream_t>(stream)));
+}
+
+emb_status_t emb_cache_stats(emb_table_t t, void* stream, int64_t* lookups, int64_t* misses) {
+  if (!t || !lookups || !misses) return EMB_ERR_INVALID_ARG;
+  if (!t->h.tiered) return EMB_ERR_UNSUPPORTED;
+  uint64_t c[2] = {0, 0};
+  hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+  if (e == hipSuccess) e = hipMemcpy(c, t->h.cache_state, sizeof(c), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return EMB_ERR_HIP;
+  *lookups = (int64_t)c[0];
+  *misses = (int64_t)c[1];
+  return EMB_OK;
+}
+
 emb_status_t emb_table_destroy(emb_table_t t) {
   delete t;
   return EMB_OK;
+}
+
+// The sort's key buffer that does not hold the final sorted keys.
+static uint32_t* spare_keys(const Plan& p, char* w) {
+  const bool in_b = p.nnz > 0 && (p.passes % 2) == 1;
+  return reinterpret_cast<uint32_t*>(w + (in_b ? p.keysA : p.keysB));
 }
 
 static emb_status_t check_batch(const Handle& h, const int64_t* offsets, int64_t batch,
@@ -233,6 +313,7 @@ emb_status_t emb_bag_forward(emb_table_t t, const int64_t* offsets, const int64_
   emb_status_t st = check_batch(t->h, offsets, batch, nnz);
   if (st != EMB_OK) return st;
   if (!aligned16(out)) return EMB_ERR_INVALID_ARG;
+  if (t->h.tiered) return EMB_ERR_UNSUPPORTED;  // rows are resolved by emb_bag_prepare
   if (batch == 0) return EMB_OK;
   return hip_status(launch_forward(t->h, offsets, ids, batch, nnz, pool == EMB_POOL_MEAN, out,
                                    static_cast<hipStream_t>(stream)));
@@ -258,15 +339,24 @@ emb_status_t emb_bag_backward_adagrad(emb_table_t t, const int64_t* offsets, con
   uint32_t *keys = nullptr, *perm = nullptr;
   const bool mean = pool == EMB_POOL_MEAN;
   hipError_t e = launch_sort_unique(t->h, p, offsets, ids, mean, w, &keys, &perm, s);
+  if (e == hipSuccess && t->h.tiered) {
+    uint32_t* slot_keys = spare_keys(p, w);
+    e = launch_cache_prepare(t->h, p, keys, perm, slot_keys, w, s);
+    keys = slot_keys;
+  }
   if (e == hipSuccess)
     e = launch_segment_adagrad(t->h, p, keys, perm, mean, grad_out, lr, eps, w, s);
   return hip_status(e);
 }
 
-static void sorted_arrays(const Plan& p, char* w, uint32_t** keys, uint32_t** vals) {
-  // launch_sort_unique ping-pongs A -> B -> A ... once per radix pass
+// launch_sort_unique ping-pongs A -> B -> A ... once per radix pass.  For a
+// tiered table the prepare writes the cache slot keys to the other key buffer,
+// and the prepared forward and backward use those.
+static void sorted_arrays(const Handle& h, const Plan& p, char* w, uint32_t** keys,
+                          uint32_t** vals) {
   const bool in_b = p.nnz > 0 && (p.passes % 2) == 1;
-  *keys = reinterpret_cast<uint32_t*>(w + (in_b ? p.keysB : p.keysA));
+  const bool keys_b = h.tiered ? !in_b : in_b;
+  *keys = reinterpret_cast<uint32_t*>(w + (keys_b ? p.keysB : p.keysA));
   *vals = reinterpret_cast<uint32_t*>(w + (in_b ? p.valsB : p.valsA));
 }
 
@@ -283,9 +373,13 @@ emb_status_t emb_bag_prepare(emb_table_t t, const int64_t* offsets, const int64_
     return EMB_ERR_WORKSPACE;
   if (batch == 0) return EMB_OK;
   uint32_t *keys = nullptr, *vals = nullptr;
-  return hip_status(launch_sort_unique(t->h, p, offsets, ids, pool == EMB_POOL_MEAN,
-                                       static_cast<char*>(ws), &keys, &vals,
-                                       static_cast<hipStream_t>(stream)));
+  char* w = static_cast<char*>(ws);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e =
+      launch_sort_unique(t->h, p, offsets, ids, pool == EMB_POOL_MEAN, w, &keys, &vals, s);
+  if (e == hipSuccess && t->h.tiered)
+    e = launch_cache_prepare(t->h, p, keys, vals, spare_keys(p, w), w, s);
+  return hip_status(e);
 }
 
 emb_status_t emb_bag_forward_prepared(emb_table_t t, const int64_t* offsets, const int64_t* ids,
@@ -304,14 +398,17 @@ emb_status_t emb_bag_forward_prepared(emb_table_t t, const int64_t* offsets, con
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* w = static_cast<char*>(ws);
   uint32_t *keys = nullptr, *vals = nullptr;
-  sorted_arrays(p, w, &keys, &vals);
+  sorted_arrays(t->h, p, w, &keys, &vals);
   phase_mark(t->h, EMB_PHASE_FORWARD, false, s);
   const bool mean = pool == EMB_POOL_MEAN;
   // As many ids as bags may be one-hot (a device flag decides inside the
   // launch); any other count is certainly not.
-  hipError_t e = nnz == batch * (int64_t)t->h.T
-                     ? launch_forward_sorted(t->h, p, offsets, ids, mean, keys, vals, out, w, s)
-                     : launch_forward_bags(t->h, offsets, ids, batch, nnz, mean, out, s);
+  const uint32_t* rowmap =
+      t->h.tiered ? reinterpret_cast<const uint32_t*>(w + p.c_rowmap) : nullptr;
+  hipError_t e =
+      nnz == batch * (int64_t)t->h.T
+          ? launch_forward_sorted(t->h, p, offsets, ids, mean, keys, vals, out, w, rowmap, s)
+          : launch_forward_bags(t->h, offsets, ids, batch, nnz, mean, out, rowmap, s);
   phase_mark(t->h, EMB_PHASE_FORWARD, true, s);
   return hip_status(e);
 }
@@ -332,7 +429,7 @@ emb_status_t emb_bag_backward_adagrad_prepared(emb_table_t t, int64_t batch, int
   if (batch == 0) return EMB_OK;
   uint32_t *keys = nullptr, *vals = nullptr;
   char* w = static_cast<char*>(ws);
-  sorted_arrays(p, w, &keys, &vals);
+  sorted_arrays(t->h, p, w, &keys, &vals);
   return hip_status(launch_segment_adagrad(t->h, p, keys, vals, pool == EMB_POOL_MEAN, grad_out,
                                            lr, eps, w, static_cast<hipStream_t>(stream)));
 }
@@ -401,6 +498,7 @@ emb_status_t emb_status_sync(emb_table_t t, void* stream, uint32_t* flags_out) {
   if (e != hipSuccess) return EMB_ERR_HIP;
   if (flags_out) *flags_out = f;
   if (f & EMB_FLAG_TABLE_FULL) return EMB_ERR_TABLE_FULL;
+  if (f & EMB_FLAG_CACHE_FULL) return EMB_ERR_CACHE_FULL;
   if (f & EMB_FLAG_RESERVED_KEY) return EMB_ERR_RESERVED_KEY;
   if (f & EMB_FLAG_BAD_OFFSETS) return EMB_ERR_BAD_OFFSETS;
   if (f & EMB_FLAG_OUT_OF_RANGE) return EMB_ERR_OUT_OF_RANGE;

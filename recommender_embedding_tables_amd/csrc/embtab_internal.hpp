@@ -69,7 +69,36 @@ struct Handle {
   bool timing = false;
   hipEvent_t events[2 * EMB_NUM_PHASES] = {};
   int cus = 256;  // compute units of the device current at creation
+  // tiered tables: W / G above are the HBM cache, the table is in host memory
+  bool tiered = false;
+  float* hostW = nullptr;
+  float* hostG = nullptr;
+  int64_t cache_rows = 0;
+  uint32_t cache_sets = 0;  // a power of two
+  char* cache_state = nullptr;
+  uint32_t step = 0;  // prepares so far (cache recency stamps)
 };
+
+// Cache state of a tiered table: counters, then per slot the row it holds
+// (kNoRow when empty) and the step it was last used at (0: never).
+struct CacheView {
+  uint64_t* counters;  // [0] distinct rows looked up, [1] misses
+  uint32_t* tag;
+  uint32_t* stamp;
+};
+constexpr int kCacheWays = 16;
+inline size_t cache_state_bytes(int64_t C) {
+  auto up = [](size_t b) { return (b + 255) & ~(size_t)255; };
+  return 256 + 2 * up(sizeof(uint32_t) * (size_t)C);
+}
+inline CacheView cache_view(char* st, int64_t C) {
+  auto up = [](size_t b) { return (b + 255) & ~(size_t)255; };
+  CacheView v;
+  v.counters = reinterpret_cast<uint64_t*>(st);
+  v.tag = reinterpret_cast<uint32_t*>(st + 256);
+  v.stamp = reinterpret_cast<uint32_t*>(st + 256 + up(sizeof(uint32_t) * (size_t)C));
+  return v;
+}
 
 // Measurement hook: events recorded around a phase when the caller set them.
 inline void phase_mark(const Handle& h, int phase, bool end, hipStream_t s) {
@@ -124,6 +153,7 @@ struct Plan {
   size_t chunk_base;  // heads in the earlier chunks of the chunk's 256-position block
   size_t head_base;   // heads before each 256-position block (nnz / 256 + 1)
   size_t h_slot, h_first, h_tcnt, h_tb;  // hash find-or-insert
+  size_t c_slot, c_miss, c_vict, c_mslot, c_rowmap;  // tiered: cache lookup
   size_t total = 0;
 };
 
@@ -136,6 +166,7 @@ enum : int {
   kMiscLongCount = 4,
   kMiscNotOneHot = 5,  // some bag of the prepared batch does not hold exactly one id
   kMiscFixDone = 6,    // blocks of the span fixup that have finished
+  kMiscCacheMiss = 7,  // tiered: misses of this prepare
   kMiscHashNew = 8,  // per table: new keys [T], their base rank [T], block part [T]
 };
 
@@ -215,14 +246,29 @@ hipError_t launch_segment_adagrad(const Handle& h, const Plan& p, const uint32_t
 // Forward from a prepared workspace.  One-hot batches gather the rows in
 // sorted order; otherwise (a device flag of the prepare) the same launch runs
 // the pooled kernel.
+// rowmap (tiered tables; NULL otherwise): the row of every occurrence, which
+// the pooled kernel reads instead of computing it from the ids.
 hipError_t launch_forward_sorted(const Handle& h, const Plan& p, const int64_t* offsets,
                                  const int64_t* ids, bool mean, const uint32_t* keys,
-                                 const uint32_t* perm, float* out, char* ws, hipStream_t s);
+                                 const uint32_t* perm, float* out, char* ws,
+                                 const uint32_t* rowmap, hipStream_t s);
 // The pooled kernel alone (the ids and offsets are read directly).
 hipError_t launch_forward_bags(const Handle& h, const int64_t* offsets, const int64_t* ids,
-                               int64_t B, int64_t nnz, bool mean, float* out, hipStream_t s);
+                               int64_t B, int64_t nnz, bool mean, float* out,
+                               const uint32_t* rowmap, hipStream_t s);
 
 hipError_t launch_unique_counts(const Plan& p, char* ws, hipStream_t s);
+
+// Tiered tables, after launch_sort_unique: look the batch's distinct rows up
+// in the HBM cache, bring the missing ones in (writing evicted rows back to
+// host memory), then write the cache slot of every sorted occurrence to
+// *slot_keys (the sort's spare key buffer) and, when the batch is not
+// one-hot, of every occurrence in input order to the workspace row map.
+hipError_t launch_cache_prepare(Handle& h, const Plan& p, const uint32_t* sorted_keys,
+                                const uint32_t* perm, uint32_t* slot_keys, char* ws,
+                                hipStream_t s);
+hipError_t launch_cache_flush(const Handle& h, hipStream_t s);
+hipError_t launch_cache_init(const Handle& h, hipStream_t s);
 
 hipError_t launch_hash_find_or_insert(const Handle& h, const Plan& p, const int64_t* offsets,
                                       const uint64_t* keys, int64_t* ids_out, char* ws,

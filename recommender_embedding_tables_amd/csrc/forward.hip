@@ -43,7 +43,7 @@ __device__ __forceinline__ uint32_t bag_tile(
     uint32_t tile, const int64_t* __restrict__ offsets, const int64_t* __restrict__ ids,
     const float* __restrict__ W, const int64_t* __restrict__ row_off,
     const int64_t* __restrict__ rows, float* __restrict__ out, uint32_t B, uint32_t T,
-    uint32_t D, uint32_t nnz, uint32_t S, BagTileLds& lds) {
+    uint32_t D, uint32_t nnz, uint32_t S, BagTileLds& lds, const uint32_t* __restrict__ rowmap) {
   constexpr int SGPB = 256 / SG;
   uint32_t* s_start = lds.start;
   uint32_t* s_len = lds.len;
@@ -99,7 +99,8 @@ __device__ __forceinline__ uint32_t bag_tile(
       uint32_t r = kNoRow;
       if (s_len[i] == 1u) {
         const int64_t id = idv[k];
-        if (id >= 0 && id < rows[tb[k]]) r = (uint32_t)row_off[tb[k]] + (uint32_t)id;
+        if (rowmap) r = rowmap[s_start[i]];  // resolved by the prepare (tiered tables)
+        else if (id >= 0 && id < rows[tb[k]]) r = (uint32_t)row_off[tb[k]] + (uint32_t)id;
         else bad |= EMB_FLAG_OUT_OF_RANGE;
       }
       s_row[i] = r;
@@ -164,9 +165,13 @@ __device__ __forceinline__ uint32_t bag_tile(
         for (uint32_t kb = 0; kb < len; kb += SG) {
           uint32_t r = kNoRow;
           if (kb + lane < len) {
-            const int64_t id = ids[st + kb + lane];
-            if (id >= 0 && id < nr) r = roff + (uint32_t)id;
-            else bad |= EMB_FLAG_OUT_OF_RANGE;
+            if (rowmap) {
+              r = rowmap[st + kb + lane];
+            } else {
+              const int64_t id = ids[st + kb + lane];
+              if (id >= 0 && id < nr) r = roff + (uint32_t)id;
+              else bad |= EMB_FLAG_OUT_OF_RANGE;
+            }
           }
           const uint32_t kend = (len - kb) < (uint32_t)SG ? (len - kb) : (uint32_t)SG;
 #pragma unroll 1
@@ -222,10 +227,11 @@ __global__ __launch_bounds__(256) void k_bag_forward(
     const int64_t* __restrict__ offsets, const int64_t* __restrict__ ids,
     const float* __restrict__ W, const int64_t* __restrict__ row_off,
     const int64_t* __restrict__ rows, float* __restrict__ out, uint32_t* __restrict__ flags,
-    uint32_t B, uint32_t T, uint32_t D, uint32_t nnz, uint32_t S) {
+    uint32_t B, uint32_t T, uint32_t D, uint32_t nnz, uint32_t S,
+    const uint32_t* __restrict__ rowmap) {
   __shared__ BagTileLds lds;
   const uint32_t bad = bag_tile<SG, VEC, MEAN, UNR>(xcd_block(), offsets, ids, W, row_off, rows,
-                                                    out, B, T, D, nnz, S, lds);
+                                                    out, B, T, D, nnz, S, lds, rowmap);
   if (bad) atomicOr(flags, bad);
 }
 
@@ -246,11 +252,11 @@ __global__ __launch_bounds__(256) void k_fwd_sorted(
     const uint32_t* __restrict__ misc, const int64_t* __restrict__ offsets,
     const int64_t* __restrict__ ids, const int64_t* __restrict__ row_off,
     const int64_t* __restrict__ rows, uint32_t* __restrict__ flags, uint32_t B, uint32_t T,
-    uint32_t S) {
+    uint32_t S, const uint32_t* __restrict__ rowmap) {
   if (misc[kMiscNotOneHot] != 0u) {
     __shared__ BagTileLds lds;
     const uint32_t bad = bag_tile<SG, VEC, MEAN, UNR>(xcd_block(), offsets, ids, W, row_off,
-                                                      rows, out, B, T, D, n, S, lds);
+                                                      rows, out, B, T, D, n, S, lds, rowmap);
     if (bad) atomicOr(flags, bad);
     return;
   }
@@ -338,34 +344,34 @@ constexpr int fwd_unroll() {
 
 template <int SG, int VEC, bool MEAN>
 hipError_t launch_t(const Handle& h, const int64_t* offsets, const int64_t* ids, int64_t B,
-                    int64_t nnz, float* out, hipStream_t s) {
+                    int64_t nnz, float* out, const uint32_t* rowmap, hipStream_t s) {
   const int64_t S = tile_samples(h.T, B, nnz);
   const int64_t grid = (B + S - 1) / S;
   if (grid == 0) return hipSuccess;
   hipLaunchKernelGGL((k_bag_forward<SG, VEC, MEAN, fwd_unroll<VEC>()>), dim3((unsigned)grid),
                      dim3(256), 0, s, offsets, ids, h.W, h.sv.row_off, h.sv.rows, out,
                      h.sv.flags, (uint32_t)B, (uint32_t)h.T, (uint32_t)h.D, (uint32_t)nnz,
-                     (uint32_t)S);
+                     (uint32_t)S, rowmap);
   return hipGetLastError();
 }
 
 template <bool MEAN>
 hipError_t dispatch(const Handle& h, const int64_t* offsets, const int64_t* ids, int64_t B,
-                    int64_t nnz, float* out, hipStream_t s) {
+                    int64_t nnz, float* out, const uint32_t* rowmap, hipStream_t s) {
   const int sg = subgroup_lanes(h.D), vec = vec_per_lane(h.D);
   switch (sg) {
-    case 1: return launch_t<1, 1, MEAN>(h, offsets, ids, B, nnz, out, s);
-    case 2: return launch_t<2, 1, MEAN>(h, offsets, ids, B, nnz, out, s);
-    case 4: return launch_t<4, 1, MEAN>(h, offsets, ids, B, nnz, out, s);
-    case 8: return launch_t<8, 1, MEAN>(h, offsets, ids, B, nnz, out, s);
-    case 16: return launch_t<16, 1, MEAN>(h, offsets, ids, B, nnz, out, s);
-    case 32: return launch_t<32, 1, MEAN>(h, offsets, ids, B, nnz, out, s);
+    case 1: return launch_t<1, 1, MEAN>(h, offsets, ids, B, nnz, out, rowmap, s);
+    case 2: return launch_t<2, 1, MEAN>(h, offsets, ids, B, nnz, out, rowmap, s);
+    case 4: return launch_t<4, 1, MEAN>(h, offsets, ids, B, nnz, out, rowmap, s);
+    case 8: return launch_t<8, 1, MEAN>(h, offsets, ids, B, nnz, out, rowmap, s);
+    case 16: return launch_t<16, 1, MEAN>(h, offsets, ids, B, nnz, out, rowmap, s);
+    case 32: return launch_t<32, 1, MEAN>(h, offsets, ids, B, nnz, out, rowmap, s);
     default:
       switch (vec) {
-        case 1: return launch_t<64, 1, MEAN>(h, offsets, ids, B, nnz, out, s);
-        case 2: return launch_t<64, 2, MEAN>(h, offsets, ids, B, nnz, out, s);
-        case 3: return launch_t<64, 3, MEAN>(h, offsets, ids, B, nnz, out, s);
-        default: return launch_t<64, 4, MEAN>(h, offsets, ids, B, nnz, out, s);
+        case 1: return launch_t<64, 1, MEAN>(h, offsets, ids, B, nnz, out, rowmap, s);
+        case 2: return launch_t<64, 2, MEAN>(h, offsets, ids, B, nnz, out, rowmap, s);
+        case 3: return launch_t<64, 3, MEAN>(h, offsets, ids, B, nnz, out, rowmap, s);
+        default: return launch_t<64, 4, MEAN>(h, offsets, ids, B, nnz, out, rowmap, s);
       }
   }
 }
@@ -375,23 +381,24 @@ hipError_t dispatch(const Handle& h, const int64_t* offsets, const int64_t* ids,
 hipError_t launch_forward(const Handle& h, const int64_t* offsets, const int64_t* ids,
                           int64_t B, int64_t nnz, bool mean, float* out, hipStream_t s) {
   phase_mark(h, EMB_PHASE_FORWARD, false, s);
-  hipError_t e = mean ? dispatch<true>(h, offsets, ids, B, nnz, out, s)
-                      : dispatch<false>(h, offsets, ids, B, nnz, out, s);
+  hipError_t e = mean ? dispatch<true>(h, offsets, ids, B, nnz, out, nullptr, s)
+                      : dispatch<false>(h, offsets, ids, B, nnz, out, nullptr, s);
   phase_mark(h, EMB_PHASE_FORWARD, true, s);
   return e;
 }
 
 hipError_t launch_forward_bags(const Handle& h, const int64_t* offsets, const int64_t* ids,
-                               int64_t B, int64_t nnz, bool mean, float* out, hipStream_t s) {
-  return mean ? dispatch<true>(h, offsets, ids, B, nnz, out, s)
-              : dispatch<false>(h, offsets, ids, B, nnz, out, s);
+                               int64_t B, int64_t nnz, bool mean, float* out,
+                               const uint32_t* rowmap, hipStream_t s) {
+  return mean ? dispatch<true>(h, offsets, ids, B, nnz, out, rowmap, s)
+              : dispatch<false>(h, offsets, ids, B, nnz, out, rowmap, s);
 }
 
 namespace {
 template <int SG, int VEC, bool MEAN>
 hipError_t launch_sorted_t(const Handle& h, const Plan& p, const int64_t* offsets,
                            const int64_t* ids, const uint32_t* keys, const uint32_t* perm,
-                           float* out, char* ws, hipStream_t s) {
+                           float* out, char* ws, const uint32_t* rowmap, hipStream_t s) {
   constexpr int MPL = chunk_rounds<SG>();
   constexpr int SGPB = 256 / SG;
   const int64_t chunks = (p.nnz + SG * MPL - 1) / (SG * MPL);
@@ -405,17 +412,17 @@ hipError_t launch_sorted_t(const Handle& h, const Plan& p, const int64_t* offset
                      reinterpret_cast<const uint32_t*>(ws + p.sgr), h.W, out, (uint32_t)p.nnz,
                      (uint32_t)h.total_rows, (uint32_t)h.D, (uint32_t)(p.B * h.T),
                      reinterpret_cast<const uint32_t*>(ws + p.misc), offsets, ids, h.sv.row_off,
-                     h.sv.rows, h.sv.flags, (uint32_t)p.B, (uint32_t)h.T, (uint32_t)S);
+                     h.sv.rows, h.sv.flags, (uint32_t)p.B, (uint32_t)h.T, (uint32_t)S, rowmap);
   return hipGetLastError();
 }
 
 template <bool MEAN>
 hipError_t dispatch_sorted(const Handle& h, const Plan& p, const int64_t* offsets,
                            const int64_t* ids, const uint32_t* keys, const uint32_t* perm,
-                           float* out, char* ws, hipStream_t s) {
+                           float* out, char* ws, const uint32_t* rowmap, hipStream_t s) {
   const int sg = subgroup_lanes(h.D), vec = vec_per_lane(h.D);
 #define EMB_SORTED(SG_, VEC_) \
-  launch_sorted_t<SG_, VEC_, MEAN>(h, p, offsets, ids, keys, perm, out, ws, s)
+  launch_sorted_t<SG_, VEC_, MEAN>(h, p, offsets, ids, keys, perm, out, ws, rowmap, s)
   switch (sg) {
     case 1: return EMB_SORTED(1, 1);
     case 2: return EMB_SORTED(2, 1);
@@ -437,9 +444,10 @@ hipError_t dispatch_sorted(const Handle& h, const Plan& p, const int64_t* offset
 
 hipError_t launch_forward_sorted(const Handle& h, const Plan& p, const int64_t* offsets,
                                  const int64_t* ids, bool mean, const uint32_t* keys,
-                                 const uint32_t* perm, float* out, char* ws, hipStream_t s) {
-  return mean ? dispatch_sorted<true>(h, p, offsets, ids, keys, perm, out, ws, s)
-              : dispatch_sorted<false>(h, p, offsets, ids, keys, perm, out, ws, s);
+                                 const uint32_t* perm, float* out, char* ws,
+                                 const uint32_t* rowmap, hipStream_t s) {
+  return mean ? dispatch_sorted<true>(h, p, offsets, ids, keys, perm, out, ws, rowmap, s)
+              : dispatch_sorted<false>(h, p, offsets, ids, keys, perm, out, ws, rowmap, s);
 }
 
 }  // namespace embtab

@@ -24,11 +24,15 @@ EMB_ERR_BAD_OFFSETS = 5
 EMB_ERR_RESERVED_KEY = 6
 EMB_ERR_TABLE_FULL = 7
 EMB_ERR_HIP = 8
+EMB_ERR_CACHE_FULL = 9
 
 EMB_FLAG_OUT_OF_RANGE = 1
 EMB_FLAG_BAD_OFFSETS = 2
 EMB_FLAG_RESERVED_KEY = 4
 EMB_FLAG_TABLE_FULL = 8
+EMB_FLAG_CACHE_FULL = 32
+
+EMB_CACHE_WAYS = 16
 
 EMB_POOL_SUM = 0
 EMB_POOL_MEAN = 1
@@ -40,7 +44,8 @@ EXPORTED = [
     "emb_table_destroy", "emb_hash_find_or_insert", "emb_bag_forward",
     "emb_bag_backward_adagrad", "emb_status_sync", "emb_hash_n_live", "emb_hash_export",
     "emb_debug_sort_unique", "emb_status_string", "emb_set_phase_events", "emb_bag_prepare",
-    "emb_bag_backward_adagrad_prepared", "emb_bag_forward_prepared",
+    "emb_bag_backward_adagrad_prepared", "emb_bag_forward_prepared", "emb_cache_state_bytes",
+    "emb_table_create_tiered", "emb_cache_flush", "emb_cache_stats",
 ]
 
 EMB_PHASE_FORWARD, EMB_PHASE_KEYS, EMB_PHASE_SORT, EMB_PHASE_UNIQUE = 0, 1, 2, 3
@@ -66,6 +71,15 @@ class emb_table_desc_t(C.Structure):
         ("init_std", C.c_float),
         ("accum_init", C.c_float),
         ("init_storage", C.c_int32),
+    ]
+
+
+class emb_tier_desc_t(C.Structure):
+    _fields_ = [
+        ("host_weights", C.c_void_p),
+        ("host_accum", C.c_void_p),
+        ("cache_rows", C.c_int64),
+        ("cache_state", C.c_void_p),
     ]
 
 
@@ -103,6 +117,11 @@ def _load():
         "emb_bag_prepare": (i32, [P, P, P, i64, i64, i32, P, sz, P]),
         "emb_bag_forward_prepared": (i32, [P, P, P, i64, i64, i32, P, P, sz, P]),
         "emb_bag_backward_adagrad_prepared": (i32, [P, i64, i64, i32, P, f32, f32, P, sz, P]),
+        "emb_cache_state_bytes": (sz, [i64]),
+        "emb_table_create_tiered": (i32, [C.POINTER(emb_table_desc_t),
+                                          C.POINTER(emb_tier_desc_t), P, C.POINTER(P)]),
+        "emb_cache_flush": (i32, [P, P]),
+        "emb_cache_stats": (i32, [P, P, C.POINTER(i64), C.POINTER(i64)]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -162,6 +181,28 @@ def emb_table_create(desc: emb_table_desc_t, stream=None):
     h = C.c_void_p()
     st = _lib.emb_table_create(C.byref(desc), _stream(stream), C.byref(h))
     return st, h.value
+
+
+def emb_cache_state_bytes(cache_rows: int) -> int:
+    return int(_lib.emb_cache_state_bytes(cache_rows))
+
+
+def emb_table_create_tiered(desc: emb_table_desc_t, tier: emb_tier_desc_t, stream=None):
+    """Returns (status, handle)."""
+    h = C.c_void_p()
+    st = _lib.emb_table_create_tiered(C.byref(desc), C.byref(tier), _stream(stream), C.byref(h))
+    return st, h.value
+
+
+def emb_cache_flush(handle, stream=None) -> int:
+    return _lib.emb_cache_flush(handle, _stream(stream))
+
+
+def emb_cache_stats(handle, stream=None):
+    """Returns (status, lookups, misses)."""
+    a, b = C.c_int64(0), C.c_int64(0)
+    st = _lib.emb_cache_stats(handle, _stream(stream), C.byref(a), C.byref(b))
+    return st, int(a.value), int(b.value)
 
 
 def emb_table_destroy(handle) -> int:
@@ -246,7 +287,7 @@ class EmbTables:
 
     def __init__(self, rows_per_table, dim, *, hashed=False, hash_capacity=0, max_load=0.625,
                  seed=0, init_lo=-0.05, init_hi=0.05, init_std=0.01, accum_init=0.1,
-                 device="cuda", stream=None, storage=None):
+                 device="cuda", stream=None, storage=None, cache_rows=0):
         import torch
         self.rows = [int(r) for r in rows_per_table]
         self.T = len(self.rows)
@@ -255,8 +296,17 @@ class EmbTables:
         self.hashed = bool(hashed)
         self.hash_capacity = int(hash_capacity)
         dev = torch.device(device)
+        self.tiered = cache_rows > 0
+        if self.tiered:
+            # the table in pinned host memory; weights / accum below are the HBM cache
+            self.host_weights = torch.empty((self.total_rows, self.D), dtype=torch.float32,
+                                            pin_memory=True)
+            self.host_accum = torch.empty_like(self.host_weights, pin_memory=True)
+            self.cache_state = torch.empty(max(emb_cache_state_bytes(cache_rows), 256),
+                                           dtype=torch.uint8, device=dev)
         if storage is None:
-            self.weights = torch.empty((self.total_rows, self.D), dtype=torch.float32, device=dev)
+            nrows = cache_rows if self.tiered else self.total_rows
+            self.weights = torch.empty((nrows, self.D), dtype=torch.float32, device=dev)
             self.accum = torch.empty_like(self.weights)
             self.state = torch.zeros(emb_state_bytes(self.T), dtype=torch.uint8, device=dev)
             hb = emb_hash_bytes(self.T, self.hash_capacity) if hashed else 0
@@ -283,8 +333,17 @@ class EmbTables:
         d.init_std = init_std
         d.accum_init = accum_init
         d.init_storage = init
-        st, self.handle = emb_table_create(d, stream)
-        check(st, "emb_table_create")
+        if self.tiered:
+            tier = emb_tier_desc_t()
+            tier.host_weights = self.host_weights.data_ptr()
+            tier.host_accum = self.host_accum.data_ptr()
+            tier.cache_rows = int(cache_rows)
+            tier.cache_state = self.cache_state.data_ptr()
+            st, self.handle = emb_table_create_tiered(d, tier, stream)
+            check(st, "emb_table_create_tiered")
+        else:
+            st, self.handle = emb_table_create(d, stream)
+            check(st, "emb_table_create")
         self._ws = None
 
     def close(self):

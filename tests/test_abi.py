@@ -141,3 +141,55 @@ def test_status_strings():
     assert eb.emb_status_string(eb.EMB_ERR_TABLE_FULL) == "table full"
     assert eb.emb_status_string(eb.EMB_OK) == "ok"
     assert eb.emb_status_string(99) == "unknown status"
+
+
+def test_cache_state_bytes():
+    W = eb.EMB_CACHE_WAYS
+    for bad in (0, -W, W - 1, W + 1, 3 * W, 48 * W):
+        assert eb.emb_cache_state_bytes(bad) == 0, bad
+    small, big = eb.emb_cache_state_bytes(W), eb.emb_cache_state_bytes(1024 * W)
+    assert small > 0 and big > small and big % 256 == 0
+    # per slot at least the row it holds and the step it was last used at
+    assert big >= 1024 * W * 8
+
+
+def _tier(**kw):
+    t = eb.emb_tier_desc_t()
+    t.host_weights = kw.pop("host_weights", 0x50000000)
+    t.host_accum = kw.pop("host_accum", 0x60000000)
+    t.cache_rows = kw.pop("cache_rows", 4 * eb.EMB_CACHE_WAYS)
+    t.cache_state = kw.pop("cache_state", 0x70000000)
+    assert not kw
+    return t
+
+
+@pytest.mark.parametrize("dkw,tkw,code", [
+    (dict(), dict(), eb.EMB_ERR_INVALID_ARG),  # init_storage 0: stamps belong to one handle
+    (dict(init_storage=1, hashed=1, hash_capacity=1024, hash_slots=0x40000000), dict(),
+     eb.EMB_ERR_UNSUPPORTED),
+    (dict(init_storage=1), dict(cache_rows=0), eb.EMB_ERR_INVALID_ARG),
+    (dict(init_storage=1), dict(cache_rows=3 * eb.EMB_CACHE_WAYS), eb.EMB_ERR_INVALID_ARG),
+    (dict(init_storage=1), dict(cache_rows=32 * eb.EMB_CACHE_WAYS), eb.EMB_ERR_INVALID_ARG),
+    (dict(init_storage=1), dict(host_weights=None), eb.EMB_ERR_INVALID_ARG),
+    (dict(init_storage=1), dict(host_accum=0x60000008), eb.EMB_ERR_INVALID_ARG),
+    (dict(init_storage=1), dict(cache_state=0x70000010), eb.EMB_ERR_INVALID_ARG),
+    (dict(init_storage=1, dim=6), dict(), eb.EMB_ERR_INVALID_ARG),
+])
+def test_create_tiered_rejects(dkw, tkw, code):
+    # rows [100, 200]: 300 rows in all, so 32 sets of 16 do not fit
+    d, _keep = _desc(**dkw)
+    st, h = eb.emb_table_create_tiered(d, _tier(**tkw), 0)
+    assert st == code and h is None
+
+
+def test_cache_calls_on_a_dense_handle():
+    d, _keep = _desc(rows=[1000], dim=16)
+    st, h = eb.emb_table_create(d, 0)
+    assert st == eb.EMB_OK and h
+    try:
+        assert eb.emb_cache_flush(h, 0) == eb.EMB_ERR_UNSUPPORTED
+        assert eb.emb_cache_stats(h, 0)[0] == eb.EMB_ERR_UNSUPPORTED
+    finally:
+        eb.emb_table_destroy(h)
+    assert eb.emb_cache_flush(None, 0) == eb.EMB_ERR_INVALID_ARG
+    assert eb.emb_status_string(eb.EMB_ERR_CACHE_FULL) == "cache set full"
