@@ -234,7 +234,10 @@ emb_status_t emb_debug_sort_unique(emb_table_t h, const int64_t* offsets, const 
  *   EMB_PHASE_UNIQUE   run heads and the unique index of each reduction chunk;
  *   EMB_PHASE_REDUCE   the fused segmented-reduction + Adagrad kernel;
  *   EMB_PHASE_FIXUP    the kernel finishing rows that span reduction chunks;
- *   EMB_PHASE_HASH     all of emb_hash_find_or_insert.
+ *   EMB_PHASE_HASH     all of emb_hash_find_or_insert;
+ *   EMB_PHASE_CACHE    tiered tables: the kernel of emb_bag_prepare (or of
+ *                      the one-call backward) that writes evicted rows back
+ *                      to host memory and fetches the missing ones.
  * When `events` is not NULL, later calls on h record events[2p] (if not NULL)
  * just before phase p and events[2p+1] (if not NULL) just after it, with
  * hipEventRecord on the call's stream.  The array (2 * EMB_NUM_PHASES
@@ -248,7 +251,8 @@ typedef enum {
   EMB_PHASE_REDUCE = 4,
   EMB_PHASE_FIXUP = 5,
   EMB_PHASE_HASH = 6,
-  EMB_NUM_PHASES = 7
+  EMB_PHASE_CACHE = 7,
+  EMB_NUM_PHASES = 8
 } emb_phase_t;
 emb_status_t emb_set_phase_events(emb_table_t h, void* const* events);
 
@@ -307,9 +311,12 @@ emb_status_t emb_table_create_tiered(const emb_table_desc_t* desc, const emb_tie
  * them).  Afterwards the host arrays hold the table's current values. */
 emb_status_t emb_cache_flush(emb_table_t h, void* stream);
 
-/* HOST out: cumulative distinct rows looked up and misses over all prepares
- * of h (waits for the stream). */
-emb_status_t emb_cache_stats(emb_table_t h, void* stream, int64_t* lookups, int64_t* misses);
+/* HOST out: cumulative counts over all prepares of h (waits for the stream):
+ * distinct rows looked up, misses (rows fetched from host memory) and
+ * write-backs (evicted rows written to host memory; emb_cache_flush is not
+ * counted). */
+emb_status_t emb_cache_stats(emb_table_t h, void* stream, int64_t* lookups, int64_t* misses,
+                             int64_t* writebacks);
 
 #ifdef __cplusplus
 }

@@ -273,15 +273,17 @@ emb_status_t emb_cache_flush(emb_table_t t, void* stream) {
   return hip_status(launch_cache_flush(t->h, static_cast<hipStream_t>(stream)));
 }
 
-emb_status_t emb_cache_stats(emb_table_t t, void* stream, int64_t* lookups, int64_t* misses) {
-  if (!t || !lookups || !misses) return EMB_ERR_INVALID_ARG;
+emb_status_t emb_cache_stats(emb_table_t t, void* stream, int64_t* lookups, int64_t* misses,
+                             int64_t* writebacks) {
+  if (!t || !lookups || !misses || !writebacks) return EMB_ERR_INVALID_ARG;
   if (!t->h.tiered) return EMB_ERR_UNSUPPORTED;
-  uint64_t c[2] = {0, 0};
+  uint64_t c[3] = {0, 0, 0};
   hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
   if (e == hipSuccess) e = hipMemcpy(c, t->h.cache_state, sizeof(c), hipMemcpyDeviceToHost);
   if (e != hipSuccess) return EMB_ERR_HIP;
   *lookups = (int64_t)c[0];
   *misses = (int64_t)c[1];
+  *writebacks = (int64_t)c[2];
   return EMB_OK;
 }
 

@@ -33,6 +33,11 @@
 // summation order, do not depend on which slot holds a row.
 #include "embtab_internal.hpp"
 
+// Blocks of the row-move kernel per compute unit (see launch_move).
+#ifndef EMBTAB_MOVE_BLOCKS_PER_CU
+#define EMBTAB_MOVE_BLOCKS_PER_CU 1
+#endif
+
 namespace embtab {
 
 namespace {
@@ -148,16 +153,23 @@ __global__ __launch_bounds__(256) void k_cache_claim(
     if (atomicCAS(&stamp[base + best], bs, step) == bs) slot = base + (uint32_t)best;
   }
   const uint32_t u = miss_u[m];
+  uint32_t v = kNoRow;
   if (slot == kNoRow) {  // every slot of the set holds a row of this or the previous batch
     atomicOr(flags, EMB_FLAG_CACHE_FULL);
     slot_of_u[u] = kNoRow;
     mslot[m] = kNoRow;
-    return;
+  } else {
+    v = tag[slot];
+    victim[m] = v;
+    tag[slot] = row;
+    mslot[m] = slot;
+    slot_of_u[u] = slot;
   }
-  victim[m] = tag[slot];
-  tag[slot] = row;
-  mslot[m] = slot;
-  slot_of_u[u] = slot;
+  // count the write-backs: one device atomic per wave
+  const uint64_t wb = __ballot(v != kNoRow);
+  if (wb && (threadIdx.x & 63u) == (uint32_t)__ffsll((unsigned long long)wb) - 1u)
+    atomicAdd(reinterpret_cast<unsigned long long*>(&counters[2]),
+              (unsigned long long)__popcll(wb));
 }
 
 // One sub-group of SG lanes per miss, VEC float4 columns per lane.
@@ -181,12 +193,17 @@ __global__ __launch_bounds__(256) void k_cache_move(
       if (d4 >= D4) continue;
       f4* cw = reinterpret_cast<f4*>(W + (size_t)slot * D) + d4;
       f4* cg = reinterpret_cast<f4*>(G + (size_t)slot * D) + d4;
+      // all four loads first: the host reads (the long ones) are in flight
+      // together with the slot's old values
+      const f4 nw = reinterpret_cast<const f4*>(hostW + (size_t)row * D)[d4];
+      const f4 ng = reinterpret_cast<const f4*>(hostG + (size_t)row * D)[d4];
+      const f4 ow = *cw, og = *cg;
       if (v != kNoRow) {  // write the evicted row back
-        reinterpret_cast<f4*>(hostW + (size_t)v * D)[d4] = *cw;
-        reinterpret_cast<f4*>(hostG + (size_t)v * D)[d4] = *cg;
+        reinterpret_cast<f4*>(hostW + (size_t)v * D)[d4] = ow;
+        reinterpret_cast<f4*>(hostG + (size_t)v * D)[d4] = og;
       }
-      *cw = reinterpret_cast<const f4*>(hostW + (size_t)row * D)[d4];
-      *cg = reinterpret_cast<const f4*>(hostG + (size_t)row * D)[d4];
+      *cw = nw;
+      *cg = ng;
     }
   }
 }
@@ -247,15 +264,20 @@ __global__ __launch_bounds__(256) void k_cache_init(uint32_t* __restrict__ tag,
     tag[i] = kNoRow;
     stamp[i] = 0u;
   }
-  if (blockIdx.x == 0 && threadIdx.x < 2) counters[threadIdx.x] = 0ull;
+  if (blockIdx.x == 0 && threadIdx.x < 3) counters[threadIdx.x] = 0ull;
 }
 
 template <int SG, int VEC>
 hipError_t launch_move(const Handle& h, const uint32_t* mrow, const uint32_t* vict,
                        const uint32_t* mslot, const uint32_t* misc, uint32_t n, hipStream_t s) {
   constexpr int SGPB = 256 / SG;
+  // The host link, not the CUs, bounds this kernel: a block per CU keeps
+  // megabytes of reads in flight (far above the link's bandwidth-latency
+  // product) and leaves the CUs to the forward and backward of the batch
+  // before, which run beside it on another stream.
   int64_t grid = ((int64_t)n + SGPB - 1) / SGPB;
-  grid = grid < 1 ? 1 : (grid > 4096 ? 4096 : grid);
+  const int64_t cap = (int64_t)(h.cus > 0 ? h.cus : 256) * EMBTAB_MOVE_BLOCKS_PER_CU;
+  grid = grid < 1 ? 1 : (grid > cap ? cap : grid);
   hipLaunchKernelGGL((k_cache_move<SG, VEC>), dim3((unsigned)grid), dim3(256), 0, s, mrow, vict,
                      mslot, misc, h.W, h.G, h.hostW, h.hostG, h.D, n);
   return hipGetLastError();
@@ -296,6 +318,7 @@ hipError_t launch_cache_prepare(Handle& h, const Plan& p, const uint32_t* sorted
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int sg = subgroup_lanes(h.D), vec = vec_per_lane(h.D);
+  phase_mark(h, EMB_PHASE_CACHE, false, s);
   switch (sg) {
     case 1: e = launch_move<1, 1>(h, miss_row, vict, mslot, misc, n, s); break;
     case 2: e = launch_move<2, 1>(h, miss_row, vict, mslot, misc, n, s); break;
@@ -309,6 +332,7 @@ hipError_t launch_cache_prepare(Handle& h, const Plan& p, const uint32_t* sorted
           : vec == 3 ? launch_move<64, 3>(h, miss_row, vict, mslot, misc, n, s)
                      : launch_move<64, 4>(h, miss_row, vict, mslot, misc, n, s);
   }
+  phase_mark(h, EMB_PHASE_CACHE, true, s);
   if (e != hipSuccess) return e;
   if (p.chunk == 64)
     hipLaunchKernelGGL((k_cache_remap<64>), dim3(grid), dim3(256), 0, s, sorted_keys, perm, n,

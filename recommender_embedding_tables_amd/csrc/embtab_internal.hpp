@@ -82,7 +82,7 @@ struct Handle {
 // Cache state of a tiered table: counters, then per slot the row it holds
 // (kNoRow when empty) and the step it was last used at (0: never).
 struct CacheView {
-  uint64_t* counters;  // [0] distinct rows looked up, [1] misses
+  uint64_t* counters;  // [0] distinct rows looked up, [1] misses, [2] write-backs
   uint32_t* tag;
   uint32_t* stamp;
 };

@@ -49,8 +49,10 @@ EXPORTED = [
 ]
 
 EMB_PHASE_FORWARD, EMB_PHASE_KEYS, EMB_PHASE_SORT, EMB_PHASE_UNIQUE = 0, 1, 2, 3
-EMB_PHASE_REDUCE, EMB_PHASE_FIXUP, EMB_PHASE_HASH, EMB_NUM_PHASES = 4, 5, 6, 7
-PHASE_NAMES = ["forward", "keys", "sort", "unique", "reduce_adagrad", "fixup", "hash"]
+EMB_PHASE_REDUCE, EMB_PHASE_FIXUP, EMB_PHASE_HASH, EMB_PHASE_CACHE = 4, 5, 6, 7
+EMB_NUM_PHASES = 8
+PHASE_NAMES = ["forward", "keys", "sort", "unique", "reduce_adagrad", "fixup", "hash",
+               "cache_move"]
 
 
 class emb_table_desc_t(C.Structure):
@@ -121,7 +123,7 @@ def _load():
         "emb_table_create_tiered": (i32, [C.POINTER(emb_table_desc_t),
                                           C.POINTER(emb_tier_desc_t), P, C.POINTER(P)]),
         "emb_cache_flush": (i32, [P, P]),
-        "emb_cache_stats": (i32, [P, P, C.POINTER(i64), C.POINTER(i64)]),
+        "emb_cache_stats": (i32, [P, P, C.POINTER(i64), C.POINTER(i64), C.POINTER(i64)]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -199,10 +201,10 @@ def emb_cache_flush(handle, stream=None) -> int:
 
 
 def emb_cache_stats(handle, stream=None):
-    """Returns (status, lookups, misses)."""
-    a, b = C.c_int64(0), C.c_int64(0)
-    st = _lib.emb_cache_stats(handle, _stream(stream), C.byref(a), C.byref(b))
-    return st, int(a.value), int(b.value)
+    """Returns (status, lookups, misses, write-backs)."""
+    a, b, c = C.c_int64(0), C.c_int64(0), C.c_int64(0)
+    st = _lib.emb_cache_stats(handle, _stream(stream), C.byref(a), C.byref(b), C.byref(c))
+    return st, int(a.value), int(b.value), int(c.value)
 
 
 def emb_table_destroy(handle) -> int:

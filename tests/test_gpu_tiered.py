@@ -118,9 +118,12 @@ def test_tiered_matches_dense_oracle(case):
         # rows read at step k carry k steps of rounding: bound by the rows' size
         assert_within(out.cpu().numpy(), ref, S + 2 * step * w.lr, f"forward step {step}")
         o.backward_adagrad(offsets, ids, w.B, mean, grad, w.lr, w.eps)
-    st, looked, missed = eb.emb_cache_stats(tabs.handle)
+    st, looked, missed, wrote = eb.emb_cache_stats(tabs.handle)
     assert st == eb.EMB_OK and 0 < missed <= looked
     assert missed > distinct  # rows were evicted and fetched again
+    # a miss writes a row back unless it fills a slot for the first time, and
+    # at most min(slots, distinct rows) slots are ever filled
+    assert missed - min(nsets * eb.EMB_CACHE_WAYS, distinct) <= wrote < missed
     check_all_rows(tabs, o, int(np.sum(w.rows)), steps)
     assert eb.emb_status_sync(tabs.handle) == (eb.EMB_OK, 0)
     tabs.close()
@@ -146,8 +149,9 @@ def test_tiered_one_call_backward_and_refetch():
     assert eb.emb_bag_forward(tabs.handle, _t(offsets), _t(ids), w.B, ids.size, eb.EMB_POOL_SUM,
                               out) == eb.EMB_ERR_UNSUPPORTED
     check_all_rows(tabs, o, int(np.sum(w.rows)), steps)
-    st, looked, missed = eb.emb_cache_stats(tabs.handle)
+    st, looked, missed, wrote = eb.emb_cache_stats(tabs.handle)
     assert st == eb.EMB_OK and distinct < missed <= looked
+    assert missed - min(nsets * eb.EMB_CACHE_WAYS, distinct) <= wrote < missed
     assert eb.emb_status_sync(tabs.handle) == (eb.EMB_OK, 0)
     tabs.close()
 
@@ -199,8 +203,9 @@ def test_tiered_pipelined_two_workspaces():
         assert_within(outs[i].cpu().numpy(), ref, S + 2 * i * w.lr, f"forward {i}")
         o.backward_adagrad(offsets, ids, w.B, False, grads[i], w.lr, w.eps)
     check_all_rows(tabs, o, int(np.sum(w.rows)), steps)
-    st, looked, missed = eb.emb_cache_stats(tabs.handle)
+    st, looked, missed, wrote = eb.emb_cache_stats(tabs.handle)
     assert st == eb.EMB_OK and distinct < missed <= looked
+    assert missed - min(nsets * eb.EMB_CACHE_WAYS, distinct) <= wrote < missed
     assert eb.emb_status_sync(tabs.handle) == (eb.EMB_OK, 0)
     tabs.close()
 
