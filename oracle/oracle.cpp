@@ -24,6 +24,9 @@
 //  * Deduplicating repeated ids / one access per id per pass:  DeepRec page,
 //    section "model quality", EmbeddingVariable item 2; EcoRec page, section
 //    "research method" (merging redundant work on identical indices).
+//  * Adagrad with a per-period discount of the accumulator, all samples of
+//    one period discounted alike:  DeepRec page, section "model quality",
+//    item "Adagrad Decay Optimizer".
 //  * Dynamic insertion of unseen feature keys, no capacity planning:
 //    OneFlow OneEmbedding page, section "ease of use"; HugeCTR interview,
 //    section two (a hash table identifies every input feature before the
@@ -32,6 +35,12 @@
 // Readings where the pages are silent (each is listed in the design notes):
 //  * Adagrad is the textbook form (Duchi, Hazan and Singer, JMLR 2011):
 //    G <- G + g*g (per element), w <- w - lr * g / (sqrt(G) + eps).
+//  * Adagrad Decay (the page gives no formula): every accumulator is
+//    multiplied by rho at each period boundary.  Done lazily, a row last
+//    updated in period s and updated again in period p first takes
+//    G <- rho^(p - s) * G (no discount when p <= s), then the Adagrad step;
+//    its period becomes max(s, p).  Rows start with period 0.  rho = 1 is
+//    Adagrad.
 //  * Sum or mean pooling; mean divides by the bag length L (duplicates count,
 //    out-of-range ids count in L but contribute nothing); an empty bag is 0.
 //  * Bags are table-major (bag b = t*B + s); the output is [B, T, D].
@@ -118,6 +127,7 @@ struct Model {
   bool has_dense = false;
   std::vector<float> W0, G0;               // explicit initial table (small cases)
   std::map<int64_t, RowState> touched;     // rows written since creation
+  std::map<int64_t, uint32_t> period_of;   // Adagrad Decay: period of the last update (else 0)
   std::vector<std::map<uint64_t, int64_t>> keymap;
   std::vector<int64_t> n_live;
 
@@ -156,6 +166,55 @@ bool offsets_ok(const int64_t* offsets, int64_t bags, int64_t nnz) {
   for (int64_t b = 0; b < bags; ++b)
     if (offsets[b + 1] < offsets[b]) return false;
   return true;
+}
+
+// Summed gradient of every touched global row, in ascending occurrence
+// order (fp64): g_u = sum over occurrences of c_b * grad_out[s, t, :].
+int32_t row_gradients(Model* m, const int64_t* offsets, const int64_t* ids, int64_t B,
+                             int64_t nnz, int32_t pool_mean, const float* grad_out,
+                             std::map<int64_t, std::vector<double>>& gsum) {
+  const int64_t T = m->T, D = m->D, bags = T * B;
+  if (!offsets_ok(offsets, bags, nnz)) return 2;
+  int32_t flags = 0;
+  for (int64_t b = 0; b < bags; ++b) {
+    const int64_t t = b / B, s = b % B;
+    const int64_t L = offsets[b + 1] - offsets[b];
+    const double c = (pool_mean && L > 0) ? 1.0 / (double)L : 1.0;
+    const float* go = grad_out + (s * T + t) * D;
+    for (int64_t j = offsets[b]; j < offsets[b + 1]; ++j) {
+      const int64_t id = ids[j];
+      if (id < 0 || id >= m->rows[t]) { flags |= 1; continue; }
+      std::vector<double>& acc = gsum[m->row_off[t] + id];
+      if (acc.empty()) acc.assign(D, 0.0);
+      for (int64_t d = 0; d < D; ++d) acc[d] += c * (double)go[d];
+    }
+  }
+  return flags;
+}
+
+// One Adagrad step on every touched row; the accumulator is first multiplied
+// by `discount(row)` (1 for plain Adagrad).
+template <class Discount>
+void adagrad_rows(Model* m, const std::map<int64_t, std::vector<double>>& gsum, float lr,
+                         float eps, Discount discount) {
+  const int64_t D = m->D;
+  const double dlr = (double)lr, deps = (double)eps;
+  std::vector<float> w(D), g(D);
+  for (auto& kv : gsum) {
+    m->read(kv.first, w.data(), g.data());
+    const double f = discount(kv.first);
+    RowState next;
+    next.w.resize(D);
+    next.g.resize(D);
+    for (int64_t d = 0; d < D; ++d) {
+      const double gr = kv.second[d];
+      const double G1 = f * (double)g[d] + gr * gr;
+      const double w1 = (double)w[d] - dlr * gr / (std::sqrt(G1) + deps);
+      next.g[d] = (float)G1;
+      next.w[d] = (float)w1;
+    }
+    m->touched[kv.first] = std::move(next);
+  }
 }
 
 }  // namespace
@@ -288,40 +347,46 @@ int32_t orc_backward_adagrad(void* h, const int64_t* offsets, const int64_t* ids
                              int64_t nnz, int32_t pool_mean, const float* grad_out, float lr,
                              float eps) {
   Model* m = static_cast<Model*>(h);
-  const int64_t T = m->T, D = m->D, bags = T * B;
-  if (!offsets_ok(offsets, bags, nnz)) return 2;
-  int32_t flags = 0;
   std::map<int64_t, std::vector<double>> gsum;
-  for (int64_t b = 0; b < bags; ++b) {
-    const int64_t t = b / B, s = b % B;
-    const int64_t L = offsets[b + 1] - offsets[b];
-    const double c = (pool_mean && L > 0) ? 1.0 / (double)L : 1.0;
-    const float* go = grad_out + (s * T + t) * D;
-    for (int64_t j = offsets[b]; j < offsets[b + 1]; ++j) {
-      const int64_t id = ids[j];
-      if (id < 0 || id >= m->rows[t]) { flags |= 1; continue; }
-      std::vector<double>& acc = gsum[m->row_off[t] + id];
-      if (acc.empty()) acc.assign(D, 0.0);
-      for (int64_t d = 0; d < D; ++d) acc[d] += c * (double)go[d];
-    }
-  }
-  const double dlr = (double)lr, deps = (double)eps;
-  std::vector<float> w(D), g(D);
+  const int32_t flags = row_gradients(m, offsets, ids, B, nnz, pool_mean, grad_out, gsum);
+  if (flags & 2) return flags;
+  adagrad_rows(m, gsum, lr, eps, [](int64_t) { return 1.0; });
+  return flags;
+}
+
+// Adagrad Decay step in period `period` with discount rho per period.
+int32_t orc_backward_adagrad_decay(void* h, const int64_t* offsets, const int64_t* ids,
+                                   int64_t B, int64_t nnz, int32_t pool_mean,
+                                   const float* grad_out, float lr, float eps, float rho,
+                                   uint32_t period) {
+  Model* m = static_cast<Model*>(h);
+  if (!(rho > 0.0f && rho <= 1.0f)) return -1;
+  std::map<int64_t, std::vector<double>> gsum;
+  const int32_t flags = row_gradients(m, offsets, ids, B, nnz, pool_mean, grad_out, gsum);
+  if (flags & 2) return flags;
+  adagrad_rows(m, gsum, lr, eps, [&](int64_t row) {
+    auto it = m->period_of.find(row);
+    const uint32_t last = it == m->period_of.end() ? 0u : it->second;
+    const double elapsed = period > last ? (double)(period - last) : 0.0;
+    return std::pow((double)rho, elapsed);
+  });
   for (auto& kv : gsum) {
-    m->read(kv.first, w.data(), g.data());
-    RowState next;
-    next.w.resize(D);
-    next.g.resize(D);
-    for (int64_t d = 0; d < D; ++d) {
-      const double gr = kv.second[d];
-      const double G1 = (double)g[d] + gr * gr;
-      const double w1 = (double)w[d] - dlr * gr / (std::sqrt(G1) + deps);
-      next.g[d] = (float)G1;
-      next.w[d] = (float)w1;
-    }
-    m->touched[kv.first] = std::move(next);
+    uint32_t& last = m->period_of[kv.first];  // 0 when new
+    if (period > last) last = period;
   }
   return flags;
+}
+
+// Period of the last Adagrad Decay update of global rows grows[0..n) (0 if none).
+int32_t orc_read_periods(void* h, const int64_t* grows, int64_t n, uint32_t* out) {
+  Model* m = static_cast<Model*>(h);
+  const int64_t total = m->row_off[m->T];
+  for (int64_t i = 0; i < n; ++i) {
+    if (grows[i] < 0 || grows[i] >= total) return -1;
+    auto it = m->period_of.find(grows[i]);
+    out[i] = it == m->period_of.end() ? 0u : it->second;
+  }
+  return 0;
 }
 
 // Current values of global rows grows[0..n).

@@ -43,7 +43,10 @@ def _load():
         "orc_forward": (i32, [P, P, P, i64, i64, i32, P]),
         "orc_sort_unique": (i32, [P, P, P, i64, i64, P, P, P, P, P, P, P]),
         "orc_backward_adagrad": (i32, [P, P, P, i64, i64, i32, P, f32, f32]),
+        "orc_backward_adagrad_decay": (i32, [P, P, P, i64, i64, i32, P, f32, f32, f32,
+                                             C.c_uint32]),
         "orc_read_rows": (i32, [P, P, i64, P, P]),
+        "orc_read_periods": (i32, [P, P, i64, P]),
         "orc_touched_count": (i64, [P]),
         "orc_touched_rows": (i64, [P, P]),
         "orc_hash_find_or_insert": (i32, [P, P, P, i64, i64, P]),
@@ -149,6 +152,25 @@ class Oracle:
         assert grad_out.size == batch * self.T * self.D
         return int(_load().orc_backward_adagrad(self._h, _p(offsets), _p(ids), batch, ids.size,
                                                 int(bool(pool_mean)), _p(grad_out), lr, eps))
+
+    def backward_adagrad_decay(self, offsets, ids, batch, pool_mean, grad_out, lr, eps, rho,
+                               period):
+        """Adagrad Decay: accumulators discounted by rho per period (lazily, at a
+        row's next update), then the Adagrad step; the row's period becomes `period`."""
+        offsets = _arr(offsets, np.int64)
+        ids = _arr(ids, np.int64)
+        grad_out = _arr(grad_out, np.float32)
+        assert grad_out.size == batch * self.T * self.D
+        return int(_load().orc_backward_adagrad_decay(
+            self._h, _p(offsets), _p(ids), batch, ids.size, int(bool(pool_mean)), _p(grad_out),
+            lr, eps, rho, int(period)))
+
+    def read_periods(self, grows):
+        grows = _arr(grows, np.int64)
+        out = np.zeros(grows.size, np.uint32)
+        if _load().orc_read_periods(self._h, _p(grows), grows.size, _p(out)) != 0:
+            raise IndexError("oracle: row out of range")
+        return out
 
     def read_rows(self, grows):
         grows = _arr(grows, np.int64)

@@ -8,6 +8,9 @@ Pins used (none re-types the oracle's own loops):
   * library routines: torch.nn.functional.embedding_bag, torch.unique,
     numpy's stable argsort, torch.optim.Adagrad on a dense table, torch autograd;
   * invariants (counts sum to nnz, untouched rows bit-identical, |dw| < lr, ...);
+  * Adagrad Decay: rho = 1 against torch.optim.Adagrad, and the lazy per-row
+    periods against an eager model that discounts every accumulator at every
+    period boundary;
   * an independent Python dict model of first-occurrence key insertion.
 """
 import json
@@ -398,6 +401,88 @@ def test_two_steps_carry_state():
     np.testing.assert_allclose(G2[1], G0[1] + 2 * np.array([2, 4, 6]) ** 2, rtol=1e-6)
     np.testing.assert_allclose(G2[4], G0[4] + 2 * np.array([1, 0, 2]) ** 2, rtol=1e-6)
     assert W2[4, 1] == W0[4, 1]  # zero gradient leaves the weight alone
+
+
+# ---------------------------------------------------------- Adagrad Decay
+
+def test_worked_adagrad_decay():
+    # One row, rho = 1/2, accumulators chosen so every G' is a perfect square.
+    W0 = np.array([[1.0, 2.0]], np.float32)
+    o = orc.Oracle([1], 2, seed=0)
+    o.set_dense(W0, np.array([[48.0, 60.0]], np.float32))
+    off = np.array([0, 1], np.int64)
+    ids = np.array([0], np.int64)
+    step = lambda g, p: o.backward_adagrad_decay(off, ids, 1, False,
+                                                 np.array([[g]], np.float32), 0.5, 0.0, 0.5, p)
+    # period 2 (two boundaries since period 0): G' = 48/4 + 4 = 16, 60/4 + 1 = 16
+    assert step([2.0, 1.0], 2) == 0
+    W, G = o.read_rows([0])
+    np.testing.assert_array_equal(G, [[16, 16]])
+    np.testing.assert_array_equal(W, [[1 - 0.5 * 2 / 4, 2 - 0.5 * 1 / 4]])
+    # period 3: G' = 16/2 + 1 = 9, 16/2 + 8^2 = 72 -> use g = (1, 0): 9, 8
+    assert step([1.0, 0.0], 3) == 0
+    W, G = o.read_rows([0])
+    np.testing.assert_array_equal(G, [[9, 8]])
+    np.testing.assert_array_equal(W, np.array([[0.75 - 0.5 / 3, 1.875]], np.float32))
+    # a period before the row's own: no discount, its period stays 3
+    assert step([4.0, 1.0], 1) == 0
+    W, G = o.read_rows([0])
+    np.testing.assert_array_equal(G, [[25, 9]])
+    assert o.read_periods([0]).tolist() == [3]
+    np.testing.assert_allclose(W, [[0.75 - 0.5 / 3 - 0.5 * 4 / 5, 1.875 - 0.5 / 3]], rtol=3e-7)  # 3 fp32 roundings
+
+
+def test_adagrad_decay_rho_one_is_torch_adagrad():
+    T, D, B = 2, 4, 20
+    rows = np.array([9, 15])
+    lr, eps, accum = 0.05, 1e-8, 0.1
+    o = orc.Oracle(rows, D, seed=4, accum_init=accum)
+    n = int(rows.sum())
+    W0, _ = o.read_rows(np.arange(n))
+    p = torch.nn.Parameter(torch.from_numpy(W0.astype(np.float64)))
+    opt = torch.optim.Adagrad([p], lr=lr, eps=eps, initial_accumulator_value=accum)
+    for k, period in enumerate([0, 3, 3, 7]):
+        offsets, ids, grad = synth.random_small(20 + k, T, D, B, rows, max_len=4)
+        assert o.backward_adagrad_decay(offsets, ids, B, False, grad, lr, eps, 1.0, period) == 0
+        A = _dense_A(offsets, ids, T, B, rows, False)
+        p.grad = torch.from_numpy(A.T @ grad.transpose(1, 0, 2).reshape(T * B, D).astype(np.float64))
+        opt.step()
+    W1, G1 = o.read_rows(np.arange(n))
+    np.testing.assert_allclose(W1, p.detach().numpy().astype(np.float32), rtol=1e-6, atol=1e-8)
+    np.testing.assert_allclose(G1, opt.state[p]["sum"].numpy().astype(np.float32), rtol=1e-6)
+
+
+@pytest.mark.parametrize("pool_mean", [False, True])
+def test_adagrad_decay_equals_eager_per_period_discount(pool_mean):
+    # Eager model: at every period boundary every accumulator of the table is
+    # multiplied by rho, touched or not; then plain Adagrad on the dense
+    # gradient.  The oracle discounts lazily with per-row periods; after the
+    # last step, a row's effective accumulator is G * rho^(p_last - period_row).
+    T, D, B = 3, 5, 16
+    rows = np.array([7, 30, 12])
+    lr, eps, accum, rho = 0.02, 1e-8, 0.3, 0.8
+    o = orc.Oracle(rows, D, seed=6, accum_init=accum)
+    n = int(rows.sum())
+    W, _ = o.read_rows(np.arange(n))
+    W = W.astype(np.float64)
+    G = np.full((n, D), accum, np.float64)
+    G[:] = o.read_rows(np.arange(n))[1]
+    prev = 0
+    periods = [0, 1, 1, 2, 5, 5, 6]
+    for k, period in enumerate(periods):
+        offsets, ids, grad = synth.random_small(40 + k, T, D, B, rows, max_len=5)
+        assert o.backward_adagrad_decay(offsets, ids, B, pool_mean, grad, lr, eps, rho,
+                                        period) == 0
+        G *= rho ** (period - prev)
+        prev = period
+        A = _dense_A(offsets, ids, T, B, rows, pool_mean)
+        gW = A.T @ grad.transpose(1, 0, 2).reshape(T * B, D).astype(np.float64)
+        G += gW * gW
+        W -= lr * gW / (np.sqrt(G) + eps)
+    W1, G1 = o.read_rows(np.arange(n))
+    pr = o.read_periods(np.arange(n)).astype(np.float64)
+    np.testing.assert_allclose(W1, W.astype(np.float32), rtol=2e-6, atol=1e-8)
+    np.testing.assert_allclose(G1 * rho ** (periods[-1] - pr)[:, None], G, rtol=2e-6)
 
 
 # ------------------------------------------------------------------- hash
