@@ -199,6 +199,27 @@ emb_status_t emb_bag_backward_adagrad_prepared(emb_table_t h, int64_t batch, int
                                                float eps, void* ws, size_t ws_bytes,
                                                void* stream);
 
+/* emb_bag_backward_adagrad_prepared with the Adagrad Decay optimizer (DeepRec
+ * page, section "model quality", Adagrad Decay Optimizer: the accumulator is
+ * discounted per period, every sample of one period alike, so that long
+ * incremental training keeps learning).  The page gives no formula; this is
+ * the reading: at every period boundary every accumulator is multiplied by
+ * rho.  It is applied lazily, when a row is next updated:
+ *   s = row_periods[row];  if (period > s) G_row *= rho^(period - s)
+ *   then the Adagrad step of emb_bag_backward_adagrad;
+ *   row_periods[row] = max(s, period).
+ * row_periods: device uint32 [sum of rows], caller-owned, 4-byte aligned,
+ * all 0 at the start of training (rows start in period 0); only touched rows
+ * are read and written.  rho in (0, 1]; rho = 1 is plain Adagrad.  period:
+ * the caller's step / period length.  rho^k is computed as
+ * exp2f(k * log2(rho)) in fp32.  EMB_ERR_INVALID_ARG for a null or misaligned
+ * row_periods or rho outside (0, 1]; EMB_ERR_UNSUPPORTED on tiered tables. */
+emb_status_t emb_bag_backward_adagrad_decay_prepared(emb_table_t h, int64_t batch, int64_t nnz,
+                                                     emb_pool_t pool, const float* grad_out,
+                                                     float lr, float eps, float rho,
+                                                     uint32_t period, uint32_t* row_periods,
+                                                     void* ws, size_t ws_bytes, void* stream);
+
 /* Waits for `stream`, returns the highest-priority device error (TABLE_FULL,
  * CACHE_FULL, RESERVED_KEY, BAD_OFFSETS, OUT_OF_RANGE, in that order) or
  * EMB_OK, stores the raw EMB_FLAG_* bits in *flags_out (HOST, may be NULL)

@@ -415,10 +415,10 @@ emb_status_t emb_bag_forward_prepared(emb_table_t t, const int64_t* offsets, con
   return hip_status(e);
 }
 
-emb_status_t emb_bag_backward_adagrad_prepared(emb_table_t t, int64_t batch, int64_t nnz,
-                                               emb_pool_t pool, const float* grad_out, float lr,
-                                               float eps, void* ws, size_t ws_bytes,
-                                               void* stream) {
+static emb_status_t backward_prepared(emb_table_t t, int64_t batch, int64_t nnz,
+                                      emb_pool_t pool, const float* grad_out, float lr,
+                                      float eps, void* ws, size_t ws_bytes, void* stream,
+                                      const DecayArgs& dec) {
   if (!t || !grad_out) return EMB_ERR_INVALID_ARG;
   if (pool != EMB_POOL_SUM && pool != EMB_POOL_MEAN) return EMB_ERR_INVALID_ARG;
   if (!std::isfinite(lr) || !std::isfinite(eps) || eps < 0.0f) return EMB_ERR_INVALID_ARG;
@@ -433,7 +433,31 @@ emb_status_t emb_bag_backward_adagrad_prepared(emb_table_t t, int64_t batch, int
   char* w = static_cast<char*>(ws);
   sorted_arrays(t->h, p, w, &keys, &vals);
   return hip_status(launch_segment_adagrad(t->h, p, keys, vals, pool == EMB_POOL_MEAN, grad_out,
-                                           lr, eps, w, static_cast<hipStream_t>(stream)));
+                                           lr, eps, w, static_cast<hipStream_t>(stream), dec));
+}
+
+emb_status_t emb_bag_backward_adagrad_prepared(emb_table_t t, int64_t batch, int64_t nnz,
+                                               emb_pool_t pool, const float* grad_out, float lr,
+                                               float eps, void* ws, size_t ws_bytes,
+                                               void* stream) {
+  return backward_prepared(t, batch, nnz, pool, grad_out, lr, eps, ws, ws_bytes, stream,
+                           DecayArgs());
+}
+
+emb_status_t emb_bag_backward_adagrad_decay_prepared(emb_table_t t, int64_t batch, int64_t nnz,
+                                                     emb_pool_t pool, const float* grad_out,
+                                                     float lr, float eps, float rho,
+                                                     uint32_t period, uint32_t* row_periods,
+                                                     void* ws, size_t ws_bytes, void* stream) {
+  if (!t || !row_periods || (reinterpret_cast<uintptr_t>(row_periods) & 3u) != 0)
+    return EMB_ERR_INVALID_ARG;
+  if (!(rho > 0.0f && rho <= 1.0f)) return EMB_ERR_INVALID_ARG;
+  if (t->h.tiered) return EMB_ERR_UNSUPPORTED;  // the periods are indexed by table row
+  DecayArgs dec;
+  dec.stamps = row_periods;
+  dec.log2_rho = (float)std::log2((double)rho);
+  dec.period = period;
+  return backward_prepared(t, batch, nnz, pool, grad_out, lr, eps, ws, ws_bytes, stream, dec);
 }
 
 emb_status_t emb_debug_sort_unique(emb_table_t t, const int64_t* offsets, const int64_t* ids,

@@ -239,9 +239,18 @@ hipError_t launch_sort_unique(const Handle& h, const Plan& p, const int64_t* off
 // Segmented reduction + Adagrad over the sorted occurrences; on the way it
 // writes unique / seg_off / inverse.  With grad_out == nullptr it only writes
 // those and counts (W and G untouched).
+// Adagrad Decay (stamps != NULL): before its step a row's accumulator is
+// multiplied by 2^((period - stamp[row]) * log2_rho) when period > stamp[row],
+// and stamp[row] becomes max(stamp[row], period).
+struct DecayArgs {
+  uint32_t* stamps = nullptr;
+  float log2_rho = 0.0f;
+  uint32_t period = 0;
+};
 hipError_t launch_segment_adagrad(const Handle& h, const Plan& p, const uint32_t* keys,
                                   const uint32_t* perm, bool mean, const float* grad_out,
-                                  float lr, float eps, char* ws, hipStream_t s);
+                                  float lr, float eps, char* ws, hipStream_t s,
+                                  const DecayArgs& dec = DecayArgs());
 
 // Forward from a prepared workspace.  One-hot batches gather the rows in
 // sorted order; otherwise (a device flag of the prepare) the same launch runs

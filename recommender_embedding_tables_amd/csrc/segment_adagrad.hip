@@ -51,7 +51,14 @@ __device__ inline void adagrad_step(f4& w, f4& g2, const f4 g, float lr, float e
   }
 }
 
-template <int SG, int VEC, bool MEAN, int MPL, int UF, bool UPDATE>
+// Adagrad Decay: the accumulator's discount for a row last updated in period
+// `last` (DeepRec page, section "model quality", Adagrad Decay Optimizer:
+// one discount per period).  rho^(period - last) as 2^(elapsed * log2 rho).
+__device__ inline float decay_factor(uint32_t last, uint32_t period, float log2_rho) {
+  return period > last ? exp2f((float)(period - last) * log2_rho) : 1.0f;
+}
+
+template <int SG, int VEC, bool MEAN, int MPL, int UF, bool UPDATE, bool DECAY>
 __global__ __launch_bounds__(256) void k_seg_adagrad(
     const uint32_t* __restrict__ keys, const uint32_t* __restrict__ perm,
     const uint32_t* __restrict__ sgr, const float* __restrict__ sscale,
@@ -61,7 +68,8 @@ __global__ __launch_bounds__(256) void k_seg_adagrad(
     uint32_t* __restrict__ long_list, uint32_t* __restrict__ misc, uint32_t nbags,
     const uint32_t* __restrict__ chunk_base, const uint32_t* __restrict__ head_base,
     uint32_t* __restrict__ unique, uint32_t* __restrict__ seg_off,
-    uint32_t* __restrict__ inverse) {
+    uint32_t* __restrict__ inverse, uint32_t* __restrict__ stamps, float log2_rho,
+    uint32_t period) {
   constexpr int CH = SG * MPL;
   constexpr int SGPB = 256 / SG;
   const int lane = threadIdx.x % SG;
@@ -187,10 +195,17 @@ __global__ __launch_bounds__(256) void k_seg_adagrad(
         for (int v = 0; v < VEC; ++v) acc[v] += MEAN ? g[u][v] * cc[u] : g[u][v];
         if (endf[u]) {
           if (!startb[u]) {
+            float df = 1.0f;
+            if (DECAY) {
+              const uint32_t last = stamps[kk[u]];
+              df = decay_factor(last, period, log2_rho);
+              if (lane == 0 && period > last) stamps[kk[u]] = period;
+            }
 #pragma unroll
             for (int v = 0; v < VEC; ++v) {
               const int d4 = lane + v * SG;
               if (d4 < D4) {
+                if (DECAY) gv[u][v] *= df;
                 adagrad_step(wv[u][v], gv[u][v], acc[v], lr, eps);
                 *reinterpret_cast<f4*>(W + (size_t)kk[u] * D + 4 * d4) = wv[u][v];
                 *reinterpret_cast<f4*>(G + (size_t)kk[u] * D + 4 * d4) = gv[u][v];
@@ -236,12 +251,13 @@ __global__ __launch_bounds__(256) void k_seg_adagrad(
 // short spans first; the grid is sized to be resident at once, so the two
 // tiers run side by side.  The last block to finish clears the two span
 // counters, so every call starts from empty lists.
-template <int SG, int VEC, int NT>
+template <int SG, int VEC, int NT, bool DECAY>
 __global__ __launch_bounds__(NT) void k_fixup(
     const uint32_t* __restrict__ keys, uint32_t n, int32_t CH, float* __restrict__ W,
     float* __restrict__ G, int32_t D, float lr, float eps, const float* __restrict__ part_head,
     const float* __restrict__ part_tail, const uint32_t* __restrict__ span_list,
-    const uint32_t* __restrict__ long_list, uint32_t* __restrict__ misc) {
+    const uint32_t* __restrict__ long_list, uint32_t* __restrict__ misc,
+    uint32_t* __restrict__ stamps, float log2_rho, uint32_t period) {
   constexpr int SGPB = NT / SG;
   __shared__ f4 red[SGPB][SG * VEC];
   __shared__ uint32_t s_end;
@@ -306,6 +322,12 @@ __global__ __launch_bounds__(NT) void k_fixup(
     for (int v = 0; v < VEC; ++v) red[sgb][lane + v * SG] = acc[v];
     __syncthreads();
     if (sgb == 0 && c1 != 0xFFFFFFFFu) {
+      float df = 1.0f;
+      if (DECAY) {
+        const uint32_t last = stamps[row];
+        df = decay_factor(last, period, log2_rho);
+        if (lane == 0 && period > last) stamps[row] = period;
+      }
 #pragma unroll
       for (int v = 0; v < VEC; ++v) {
         const int d4 = lane + v * SG;
@@ -314,6 +336,7 @@ __global__ __launch_bounds__(NT) void k_fixup(
         for (int q = 0; q < SGPB; ++q) tot += red[q][lane + v * SG];
         f4 w = *reinterpret_cast<const f4*>(W + (size_t)row * D + 4 * d4);
         f4 g2 = *reinterpret_cast<const f4*>(G + (size_t)row * D + 4 * d4);
+        if (DECAY) g2 *= df;
         adagrad_step(w, g2, tot, lr, eps);
         *reinterpret_cast<f4*>(W + (size_t)row * D + 4 * d4) = w;
         *reinterpret_cast<f4*>(G + (size_t)row * D + 4 * d4) = g2;
@@ -336,12 +359,19 @@ __global__ __launch_bounds__(NT) void k_fixup(
     const uint64_t m = (__ballot(ends) >> lane_base) & (SG == 64 ? ~0ull : ((1ull << SG) - 1ull));
     if (m == 0) continue;  // cannot happen for a listed span
     const uint32_t c1 = c0 + 1 + (uint32_t)(__ffsll((unsigned long long)m) - 1);
+    float df = 1.0f;
+    if (DECAY) {
+      const uint32_t last = stamps[row];
+      df = decay_factor(last, period, log2_rho);
+      if (lane == 0 && period > last) stamps[row] = period;
+    }
 #pragma unroll
     for (int v = 0; v < VEC; ++v) {
       const int d4 = lane + v * SG;
       if (d4 >= D4) continue;
       f4 w = *reinterpret_cast<const f4*>(W + (size_t)row * D + 4 * d4);
       f4 g2 = *reinterpret_cast<const f4*>(G + (size_t)row * D + 4 * d4);
+      if (DECAY) g2 *= df;
       f4 tot = *reinterpret_cast<const f4*>(part_tail + (size_t)c0 * D + 4 * d4);
       uint32_t c = c0 + 1;
       for (; c + 3 <= c1; c += 4) {
@@ -374,9 +404,10 @@ __global__ __launch_bounds__(NT) void k_fixup(
   }
 }
 
-template <int SG, int VEC, bool MEAN>
+template <int SG, int VEC, bool MEAN, bool DECAY>
 hipError_t launch_t(const Handle& h, const Plan& p, const uint32_t* keys, const uint32_t* perm,
-                    const float* grad_out, float lr, float eps, char* ws, hipStream_t s) {
+                    const float* grad_out, float lr, float eps, char* ws, hipStream_t s,
+                    const DecayArgs& dec) {
   constexpr int MPL = chunk_rounds<SG>();
   constexpr int UF = VEC > 1 ? 2 : (SG < kSegUF ? SG : kSegUF);
   constexpr int SGPB = 256 / SG;
@@ -400,18 +431,18 @@ hipError_t launch_t(const Handle& h, const Plan& p, const uint32_t* keys, const 
   const uint32_t nbags = (uint32_t)(p.B * h.T);
   hipError_t e;
   if (!grad_out) {  // unique / seg_off / inverse only
-    hipLaunchKernelGGL((k_seg_adagrad<SG, VEC, false, MPL, UF, false>), dim3((unsigned)grid),
-                       dim3(256), 0, s, keys, perm, gr, scale, grad_out, h.W, h.G, n,
-                       (uint32_t)h.total_rows, h.D, lr, eps, ph, pt, spans, longs, misc, nbags,
-                       cbase, hbase, uniq, segs, inv);
+    hipLaunchKernelGGL((k_seg_adagrad<SG, VEC, false, MPL, UF, false, false>),
+                       dim3((unsigned)grid), dim3(256), 0, s, keys, perm, gr, scale, grad_out,
+                       h.W, h.G, n, (uint32_t)h.total_rows, h.D, lr, eps, ph, pt, spans, longs,
+                       misc, nbags, cbase, hbase, uniq, segs, inv, nullptr, 0.0f, 0u);
     e = hipGetLastError();
     return e == hipSuccess ? launch_unique_counts(p, ws, s) : e;
   }
   phase_mark(h, EMB_PHASE_REDUCE, false, s);
-  hipLaunchKernelGGL((k_seg_adagrad<SG, VEC, MEAN, MPL, UF, true>), dim3((unsigned)grid),
-                     dim3(256), 0, s, keys, perm, gr, scale, grad_out, h.W, h.G, n,
-                     (uint32_t)h.total_rows, h.D, lr, eps, ph, pt, spans, longs, misc, nbags,
-                     cbase, hbase, uniq, segs, inv);
+  hipLaunchKernelGGL((k_seg_adagrad<SG, VEC, MEAN, MPL, UF, true, DECAY>),
+                     dim3((unsigned)grid), dim3(256), 0, s, keys, perm, gr, scale, grad_out, h.W,
+                     h.G, n, (uint32_t)h.total_rows, h.D, lr, eps, ph, pt, spans, longs, misc,
+                     nbags, cbase, hbase, uniq, segs, inv, dec.stamps, dec.log2_rho, dec.period);
   phase_mark(h, EMB_PHASE_REDUCE, true, s);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -421,40 +452,49 @@ hipError_t launch_t(const Handle& h, const Plan& p, const uint32_t* keys, const 
   const int64_t resident = (int64_t)h.cus * (2048 / FNT);  // 32 waves per CU
   fgrid = fgrid < resident ? fgrid : resident;
   phase_mark(h, EMB_PHASE_FIXUP, false, s);
-  hipLaunchKernelGGL((k_fixup<SG, VEC, FNT>), dim3((unsigned)fgrid), dim3(FNT), 0, s, keys, n,
-                     SG * MPL, h.W, h.G, h.D, lr, eps, ph, pt, spans, longs, misc);
+  hipLaunchKernelGGL((k_fixup<SG, VEC, FNT, DECAY>), dim3((unsigned)fgrid), dim3(FNT), 0, s,
+                     keys, n, SG * MPL, h.W, h.G, h.D, lr, eps, ph, pt, spans, longs, misc,
+                     dec.stamps, dec.log2_rho, dec.period);
   phase_mark(h, EMB_PHASE_FIXUP, true, s);
   return hipGetLastError();
 }
 
-template <bool MEAN>
+template <bool MEAN, bool DECAY>
 hipError_t dispatch(const Handle& h, const Plan& p, const uint32_t* keys, const uint32_t* perm,
-                    const float* grad_out, float lr, float eps, char* ws, hipStream_t s) {
+                    const float* grad_out, float lr, float eps, char* ws, hipStream_t s,
+                    const DecayArgs& dec) {
   const int sg = subgroup_lanes(h.D), vec = vec_per_lane(h.D);
+#define EMBTAB_SEG_LAUNCH(SG_, VEC_) \
+  launch_t<SG_, VEC_, MEAN, DECAY>(h, p, keys, perm, grad_out, lr, eps, ws, s, dec)
   switch (sg) {
-    case 1: return launch_t<1, 1, MEAN>(h, p, keys, perm, grad_out, lr, eps, ws, s);
-    case 2: return launch_t<2, 1, MEAN>(h, p, keys, perm, grad_out, lr, eps, ws, s);
-    case 4: return launch_t<4, 1, MEAN>(h, p, keys, perm, grad_out, lr, eps, ws, s);
-    case 8: return launch_t<8, 1, MEAN>(h, p, keys, perm, grad_out, lr, eps, ws, s);
-    case 16: return launch_t<16, 1, MEAN>(h, p, keys, perm, grad_out, lr, eps, ws, s);
-    case 32: return launch_t<32, 1, MEAN>(h, p, keys, perm, grad_out, lr, eps, ws, s);
+    case 1: return EMBTAB_SEG_LAUNCH(1, 1);
+    case 2: return EMBTAB_SEG_LAUNCH(2, 1);
+    case 4: return EMBTAB_SEG_LAUNCH(4, 1);
+    case 8: return EMBTAB_SEG_LAUNCH(8, 1);
+    case 16: return EMBTAB_SEG_LAUNCH(16, 1);
+    case 32: return EMBTAB_SEG_LAUNCH(32, 1);
     default:
       switch (vec) {
-        case 1: return launch_t<64, 1, MEAN>(h, p, keys, perm, grad_out, lr, eps, ws, s);
-        case 2: return launch_t<64, 2, MEAN>(h, p, keys, perm, grad_out, lr, eps, ws, s);
-        case 3: return launch_t<64, 3, MEAN>(h, p, keys, perm, grad_out, lr, eps, ws, s);
-        default: return launch_t<64, 4, MEAN>(h, p, keys, perm, grad_out, lr, eps, ws, s);
+        case 1: return EMBTAB_SEG_LAUNCH(64, 1);
+        case 2: return EMBTAB_SEG_LAUNCH(64, 2);
+        case 3: return EMBTAB_SEG_LAUNCH(64, 3);
+        default: return EMBTAB_SEG_LAUNCH(64, 4);
       }
   }
+#undef EMBTAB_SEG_LAUNCH
 }
 
 }  // namespace
 
 hipError_t launch_segment_adagrad(const Handle& h, const Plan& p, const uint32_t* keys,
                                   const uint32_t* perm, bool mean, const float* grad_out,
-                                  float lr, float eps, char* ws, hipStream_t s) {
-  return mean ? dispatch<true>(h, p, keys, perm, grad_out, lr, eps, ws, s)
-              : dispatch<false>(h, p, keys, perm, grad_out, lr, eps, ws, s);
+                                  float lr, float eps, char* ws, hipStream_t s,
+                                  const DecayArgs& dec) {
+  if (dec.stamps && grad_out)
+    return mean ? dispatch<true, true>(h, p, keys, perm, grad_out, lr, eps, ws, s, dec)
+                : dispatch<false, true>(h, p, keys, perm, grad_out, lr, eps, ws, s, dec);
+  return mean ? dispatch<true, false>(h, p, keys, perm, grad_out, lr, eps, ws, s, dec)
+              : dispatch<false, false>(h, p, keys, perm, grad_out, lr, eps, ws, s, dec);
 }
 
 }  // namespace embtab

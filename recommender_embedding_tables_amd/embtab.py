@@ -46,6 +46,7 @@ EXPORTED = [
     "emb_debug_sort_unique", "emb_status_string", "emb_set_phase_events", "emb_bag_prepare",
     "emb_bag_backward_adagrad_prepared", "emb_bag_forward_prepared", "emb_cache_state_bytes",
     "emb_table_create_tiered", "emb_cache_flush", "emb_cache_stats",
+    "emb_bag_backward_adagrad_decay_prepared",
 ]
 
 EMB_PHASE_FORWARD, EMB_PHASE_KEYS, EMB_PHASE_SORT, EMB_PHASE_UNIQUE = 0, 1, 2, 3
@@ -119,6 +120,8 @@ def _load():
         "emb_bag_prepare": (i32, [P, P, P, i64, i64, i32, P, sz, P]),
         "emb_bag_forward_prepared": (i32, [P, P, P, i64, i64, i32, P, P, sz, P]),
         "emb_bag_backward_adagrad_prepared": (i32, [P, i64, i64, i32, P, f32, f32, P, sz, P]),
+        "emb_bag_backward_adagrad_decay_prepared": (i32, [P, i64, i64, i32, P, f32, f32, f32,
+                                                          C.c_uint32, P, P, sz, P]),
         "emb_cache_state_bytes": (sz, [i64]),
         "emb_table_create_tiered": (i32, [C.POINTER(emb_table_desc_t),
                                           C.POINTER(emb_tier_desc_t), P, C.POINTER(P)]),
@@ -245,6 +248,14 @@ def emb_bag_backward_adagrad_prepared(handle, batch, nnz, pool, grad_out, lr, ep
                                       stream=None) -> int:
     return _lib.emb_bag_backward_adagrad_prepared(handle, batch, nnz, pool, _ptr(grad_out), lr,
                                                   eps, _ptr(ws), ws_bytes, _stream(stream))
+
+
+def emb_bag_backward_adagrad_decay_prepared(handle, batch, nnz, pool, grad_out, lr, eps, rho,
+                                            period, row_periods, ws, ws_bytes,
+                                            stream=None) -> int:
+    return _lib.emb_bag_backward_adagrad_decay_prepared(
+        handle, batch, nnz, pool, _ptr(grad_out), lr, eps, rho, period, _ptr(row_periods),
+        _ptr(ws), ws_bytes, _stream(stream))
 
 
 def emb_status_sync(handle, stream=None):

@@ -193,3 +193,25 @@ def test_cache_calls_on_a_dense_handle():
         eb.emb_table_destroy(h)
     assert eb.emb_cache_flush(None, 0) == eb.EMB_ERR_INVALID_ARG
     assert eb.emb_status_string(eb.EMB_ERR_CACHE_FULL) == "cache set full"
+
+
+def test_decay_backward_host_checks():
+    d, _keep = _desc(rows=[1000, 24], dim=64)
+    st, h = eb.emb_table_create(d, 0)
+    assert st == eb.EMB_OK and h
+    try:
+        ws = eb.emb_workspace_bytes(h, 4096, 10000)
+        fake, per = 0x50000000, 0x60000000
+        call = lambda rho=0.9, periods=per, w=fake, wsb=ws, grad=fake: \
+            eb.emb_bag_backward_adagrad_decay_prepared(h, 4096, 10000, 0, grad, 0.01, 1e-8, rho,
+                                                       3, periods, w, wsb, 0)
+        for bad in (0.0, -0.5, 1.5, float("nan"), float("inf")):
+            assert call(rho=bad) == eb.EMB_ERR_INVALID_ARG, bad
+        assert call(periods=None) == eb.EMB_ERR_INVALID_ARG
+        assert call(periods=per + 2) == eb.EMB_ERR_INVALID_ARG  # 4-byte alignment
+        assert call(grad=None) == eb.EMB_ERR_INVALID_ARG
+        assert call(wsb=ws - 1) == eb.EMB_ERR_WORKSPACE
+        assert eb.emb_bag_backward_adagrad_decay_prepared(h, 0, 0, 0, fake, 0.01, 1e-8, 1.0, 0,
+                                                          per, fake, ws, 0) == eb.EMB_OK
+    finally:
+        eb.emb_table_destroy(h)
