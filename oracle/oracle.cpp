@@ -27,6 +27,9 @@
 //  * Adagrad with a per-period discount of the accumulator, all samples of
 //    one period discounted alike:  DeepRec page, section "model quality",
 //    item "Adagrad Decay Optimizer".
+//  * Feature admission (a key gets a row only once it is frequent enough):
+//    DeepRec page, section "model quality", EmbeddingVariable item 1
+//    (several admission methods; no formula is given).
 //  * Dynamic insertion of unseen feature keys, no capacity planning:
 //    OneFlow OneEmbedding page, section "ease of use"; HugeCTR interview,
 //    section two (a hash table identifies every input feature before the
@@ -54,8 +57,17 @@
 //    (Steele, Lea and Flood, OOPSLA 2014): uniform rows for dense tables and
 //    Box-Muller (1958) normal rows for inserted keys.
 //
+//  * Admission (the page names the feature only): a key without a row counts
+//    its occurrences over calls; in the call where its count reaches
+//    min_count it gets a row, in order of its first occurrence in that call
+//    (as a new key), and all its occurrences of that call see the row.  Until
+//    then its occurrences get id -2, "absent": the lookup gives 0 (counted in
+//    a mean bag's length) and the backward updates nothing, with no error
+//    bit.  A full call admits nothing (keys that would have been admitted get
+//    -1) but every count still advances.  min_count <= 1 is plain insertion.
+//
 // Return values of the orc_* calls that check data: a bit mask,
-//   1 = an id outside [0, rows of its table)       (occurrence contributes 0)
+//   1 = an id outside [0, rows of its table), other than -2 (contributes 0)
 //   2 = offsets not starting at 0, decreasing, or not ending at nnz
 //   4 = a key equal to the reserved all-ones value (id -1, nothing inserted)
 //   8 = table full (nothing inserted, new keys get id -1)
@@ -74,6 +86,7 @@ namespace {
 
 const uint64_t kReservedKey = ~0ull;
 const uint32_t kInvalidRow32 = 0xFFFFFFFFu;
+const int64_t kAbsentId = -2;  // a feature without a row (not admitted yet)
 
 // SplitMix64, one output step: the state advances by the golden-ratio
 // increment and the new state is passed through the variant-13 finalizer.
@@ -129,6 +142,7 @@ struct Model {
   std::map<int64_t, RowState> touched;     // rows written since creation
   std::map<int64_t, uint32_t> period_of;   // Adagrad Decay: period of the last update (else 0)
   std::vector<std::map<uint64_t, int64_t>> keymap;
+  std::vector<std::map<uint64_t, uint64_t>> seen;  // admission: occurrences of keys without a row
   std::vector<int64_t> n_live;
 
   int64_t table_of(int64_t grow) const {
@@ -183,7 +197,7 @@ int32_t row_gradients(Model* m, const int64_t* offsets, const int64_t* ids, int6
     const float* go = grad_out + (s * T + t) * D;
     for (int64_t j = offsets[b]; j < offsets[b + 1]; ++j) {
       const int64_t id = ids[j];
-      if (id < 0 || id >= m->rows[t]) { flags |= 1; continue; }
+      if (id < 0 || id >= m->rows[t]) { if (id != kAbsentId) flags |= 1; continue; }
       std::vector<double>& acc = gsum[m->row_off[t] + id];
       if (acc.empty()) acc.assign(D, 0.0);
       for (int64_t d = 0; d < D; ++d) acc[d] += c * (double)go[d];
@@ -248,6 +262,7 @@ void* orc_create(int64_t T, int64_t D, const int64_t* rows, int32_t hashed, uint
   m->stdv = stdv;
   m->accum0 = accum0;
   m->keymap.resize(T);
+  m->seen.resize(T);
   m->n_live.assign(T, 0);
   return m;
 }
@@ -280,7 +295,7 @@ int32_t orc_forward(void* h, const int64_t* offsets, const int64_t* ids, int64_t
     std::fill(acc.begin(), acc.end(), 0.0);
     for (int64_t j = offsets[b]; j < offsets[b + 1]; ++j) {
       const int64_t id = ids[j];
-      if (id < 0 || id >= m->rows[t]) { flags |= 1; continue; }
+      if (id < 0 || id >= m->rows[t]) { if (id != kAbsentId) flags |= 1; continue; }
       m->read(m->row_off[t] + id, w.data(), g.data());
       for (int64_t d = 0; d < D; ++d) acc[d] += (double)w[d];
     }
@@ -309,7 +324,7 @@ int32_t orc_sort_unique(void* h, const int64_t* offsets, const int64_t* ids, int
     for (int64_t j = offsets[b]; j < offsets[b + 1]; ++j) {
       const int64_t id = ids[j];
       uint32_t row = kInvalidRow32;
-      if (id < 0 || id >= m->rows[t]) flags |= 1;
+      if (id < 0 || id >= m->rows[t]) { if (id != kAbsentId) flags |= 1; }
       else row = (uint32_t)(m->row_off[t] + id);
       occ[j] = {row, (uint32_t)j};
     }
@@ -448,6 +463,57 @@ int32_t orc_hash_find_or_insert(void* h, const int64_t* offsets, const uint64_t*
     }
   }
   return flags;
+}
+
+// Find-or-insert with frequency admission (see the readings above).
+int32_t orc_hash_find_or_insert_admit(void* h, const int64_t* offsets, const uint64_t* keys,
+                                      int64_t B, int64_t nnz, int64_t* ids_out,
+                                      uint32_t min_count) {
+  Model* m = static_cast<Model*>(h);
+  const int64_t T = m->T, D = m->D, bags = T * B;
+  if (!m->hashed) return -1;
+  if (!offsets_ok(offsets, bags, nnz)) return 2;
+  int32_t flags = 0;
+  // Pass 1: counts of keys without a row advance; which of them reach min_count?
+  std::vector<std::set<uint64_t>> admitted(T);
+  bool full = false;
+  for (int64_t t = 0; t < T; ++t) {
+    for (int64_t j = offsets[t * B]; j < offsets[(t + 1) * B]; ++j) {
+      const uint64_t key = keys[j];
+      if (key == kReservedKey || m->keymap[t].count(key)) continue;
+      if (++m->seen[t][key] >= (uint64_t)(min_count > 0 ? min_count : 1)) admitted[t].insert(key);
+    }
+    if (m->n_live[t] + (int64_t)admitted[t].size() > m->rows[t]) full = true;
+  }
+  if (full) flags |= 8;
+  // Pass 2: ids; admitted keys get rows in order of first occurrence.
+  for (int64_t t = 0; t < T; ++t) {
+    for (int64_t j = offsets[t * B]; j < offsets[(t + 1) * B]; ++j) {
+      const uint64_t key = keys[j];
+      if (key == kReservedKey) { flags |= 4; ids_out[j] = -1; continue; }
+      auto it = m->keymap[t].find(key);
+      if (it != m->keymap[t].end()) { ids_out[j] = it->second; continue; }
+      if (!admitted[t].count(key)) { ids_out[j] = kAbsentId; continue; }
+      if (full) { ids_out[j] = -1; continue; }
+      const int64_t row = m->n_live[t]++;
+      m->keymap[t][key] = row;
+      m->seen[t].erase(key);
+      RowState rs;
+      rs.w.resize(D);
+      rs.g.assign(D, m->accum0);
+      for (int64_t d = 0; d < D; ++d) rs.w[d] = normal_value(m->seed, t, key, d, m->stdv);
+      m->touched[m->row_off[t] + row] = std::move(rs);
+      ids_out[j] = row;
+    }
+  }
+  return flags;
+}
+
+// Occurrences counted so far for a key of table t that has no row (0 if none).
+uint64_t orc_admission_count(void* h, int64_t t, uint64_t key) {
+  Model* m = static_cast<Model*>(h);
+  auto it = m->seen[t].find(key);
+  return it == m->seen[t].end() ? 0 : it->second;
 }
 
 int64_t orc_n_live(void* h, int64_t t) { return static_cast<Model*>(h)->n_live[t]; }

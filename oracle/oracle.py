@@ -50,6 +50,8 @@ def _load():
         "orc_touched_count": (i64, [P]),
         "orc_touched_rows": (i64, [P, P]),
         "orc_hash_find_or_insert": (i32, [P, P, P, i64, i64, P]),
+        "orc_hash_find_or_insert_admit": (i32, [P, P, P, i64, i64, P, C.c_uint32]),
+        "orc_admission_count": (u64, [P, i64, u64]),
         "orc_n_live": (i64, [P, i64]),
         "orc_hash_export": (i64, [P, i64, P, P, i64]),
     }
@@ -194,6 +196,19 @@ class Oracle:
         flags = _load().orc_hash_find_or_insert(self._h, _p(offsets), _p(keys), batch, keys.size,
                                                 _p(ids))
         return ids, int(flags)
+
+    def find_or_insert_admit(self, offsets, keys, batch, min_count):
+        """Find-or-insert where a key gets a row once its occurrences (over
+        calls) reach min_count; until then its ids are -2 (absent)."""
+        offsets = _arr(offsets, np.int64)
+        keys = _arr(keys, np.uint64)
+        ids = np.zeros(keys.size, np.int64)
+        flags = _load().orc_hash_find_or_insert_admit(self._h, _p(offsets), _p(keys), batch,
+                                                      keys.size, _p(ids), int(min_count))
+        return ids, int(flags)
+
+    def admission_count(self, t, key):
+        return int(_load().orc_admission_count(self._h, t, int(key)))
 
     def n_live(self, t):
         return int(_load().orc_n_live(self._h, t))

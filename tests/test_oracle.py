@@ -11,7 +11,8 @@ Pins used (none re-types the oracle's own loops):
   * Adagrad Decay: rho = 1 against torch.optim.Adagrad, and the lazy per-row
     periods against an eager model that discounts every accumulator at every
     period boundary;
-  * an independent Python dict model of first-occurrence key insertion.
+  * an independent Python dict model of first-occurrence key insertion, and a
+    counting model of frequency admission (min_count = 1 reduces to insertion).
 """
 import json
 import math
@@ -530,6 +531,120 @@ def test_hash_matches_dict_model_over_calls():
         assert dict(zip(keys.tolist(), rows.tolist())) == maps[t]
         assert sorted(rows.tolist()) == list(range(o.n_live(t)))  # bijection onto [0, n_live)
     assert any(f for _, f in ref) and not all(f for _, f in ref)
+
+
+# ------------------------------------------------------- feature admission
+
+def _admit_model(batches, T, B, cap, N):
+    """Per call and table: add the call's occurrence counts of keys without a
+    row, then admit (in order of first occurrence) those whose total reached N."""
+    from collections import Counter
+    maps = [dict() for _ in range(T)]
+    counts = [Counter() for _ in range(T)]
+    out = []
+    for off, keys in batches:
+        segs = [[int(k) for k in keys[off[t * B]:off[(t + 1) * B]]] for t in range(T)]
+        adm = []
+        for t in range(T):
+            counts[t].update(k for k in segs[t] if k != M64 and k not in maps[t])
+            order = list(dict.fromkeys(k for k in segs[t] if k != M64 and k not in maps[t]))
+            adm.append([k for k in order if counts[t][k] >= N])
+        full = any(len(maps[t]) + len(adm[t]) > cap for t in range(T))
+        ids = []
+        for t in range(T):
+            if not full:
+                for k in adm[t]:
+                    maps[t][k] = len(maps[t])
+                    del counts[t][k]
+            for k in segs[t]:
+                if k == M64:
+                    ids.append(-1)
+                elif k in maps[t]:
+                    ids.append(maps[t][k])
+                else:
+                    ids.append(-1 if k in adm[t] else -2)
+        out.append((np.array(ids, np.int64), full))
+    return out, maps, counts
+
+
+def test_worked_admission():
+    o = orc.Oracle([10], 4, hashed=True, seed=1)
+    A, Bk, Ck, Dk = 11, 22, 33, 44
+    one = lambda keys: o.find_or_insert_admit(np.array([0, len(keys)], np.int64),
+                                              np.array(keys, np.uint64), 1, 2)
+    # A occurs twice: admitted in this call, both occurrences see row 0
+    ids, fl = one([A, Bk, A, Ck])
+    assert fl == 0 and ids.tolist() == [0, -2, 0, -2]
+    # C and B reach 2 now: rows in order of first occurrence in this call
+    ids, fl = one([Ck, Bk, Dk, A])
+    assert fl == 0 and ids.tolist() == [1, 2, -2, 0]
+    assert o.admission_count(0, Dk) == 1 and o.admission_count(0, A) == 0
+    assert o.n_live(0) == 3
+
+
+def test_admission_min_count_one_is_plain_insertion():
+    T = 2
+    w = synth.workload(5, T=T, B=40, universe=300, hash_capacity=1024, max_load=0.5)
+    w.rows = np.full(T, 120, np.int64)
+    plain = orc.Oracle(w.rows, 4, hashed=True, seed=w.seed)
+    admit = orc.Oracle(w.rows, 4, hashed=True, seed=w.seed)
+    for bi in range(5):
+        off, ranks = synth.gen_batch(w, bi)
+        keys = synth.gen_keys(w, off, ranks)
+        assert plain.find_or_insert(off, keys, w.B)[0].tolist() == \
+            admit.find_or_insert_admit(off, keys, w.B, 1)[0].tolist()
+    for t in range(T):
+        assert [a.tolist() for a in plain.export(t)] == [a.tolist() for a in admit.export(t)]
+
+
+@pytest.mark.parametrize("N", [2, 3])
+def test_admission_matches_counting_model(N):
+    T, cap = 3, 90
+    w = synth.workload(5, T=T, B=60, universe=500, hash_capacity=1024, max_load=0.5)
+    w.rows = np.full(T, cap, np.int64)
+    o = orc.Oracle(w.rows, 4, hashed=True, seed=w.seed)
+    batches = []
+    for bi in range(8):
+        off, ranks = synth.gen_batch(w, bi)
+        keys = synth.gen_keys(w, off, ranks)
+        if bi == 2:
+            keys[5] = np.uint64(M64)  # a reserved key
+        batches.append((off, keys))
+    ref, maps, counts = _admit_model(batches, T, w.B, cap, N)
+    for (off, keys), (ids_ref, full) in zip(batches, ref):
+        ids, fl = o.find_or_insert_admit(off, keys, w.B, N)
+        assert ids.tolist() == ids_ref.tolist()
+        assert bool(fl & orc.ERR_TABLE_FULL) == full
+    for t in range(T):
+        keys, rows = o.export(t)
+        assert dict(zip(keys.tolist(), rows.tolist())) == maps[t]
+        for k, c in list(counts[t].items())[:50]:
+            assert o.admission_count(t, k) == c
+    fulls = [f for _, f in ref]
+    assert any(fulls) and not all(fulls)  # both regimes are exercised
+
+
+def test_absent_ids_contribute_nothing_without_error():
+    T, D, B = 2, 4, 30
+    rows = np.array([9, 14])
+    offsets, ids, grad = synth.random_small(7, T, D, B, rows, max_len=5)
+    ids = ids.copy()
+    ids[::3] = -2
+    o = orc.Oracle(rows, D, seed=2)
+    n = int(rows.sum())
+    W0, G0 = o.read_rows(np.arange(n))
+    for mean in (False, True):
+        out, fl = o.forward(offsets, ids, B, mean)
+        assert fl == 0
+        A = _dense_A(offsets, ids, T, B, rows, mean)  # -2 entries add nothing, count in L
+        np.testing.assert_allclose(out, _bags_to_out(A @ W0.astype(np.float64), T, B),
+                                   rtol=1e-6, atol=1e-7)
+    assert o.backward_adagrad(offsets, ids, B, False, grad, 0.1, 1e-8) == 0
+    A = _dense_A(offsets, ids, T, B, rows, False)
+    touched = np.abs(A).sum(axis=0) > 0
+    assert sorted(o.touched_rows().tolist()) == np.nonzero(touched)[0].tolist()
+    ids[0] = -3  # any other negative id is still an error
+    assert o.forward(offsets, ids, B, False)[1] == orc.ERR_OUT_OF_RANGE
 
 
 def test_hash_tables_are_independent_and_rows_initialised():
