@@ -34,8 +34,9 @@
  *    small) return at once and enqueue nothing.  Data errors found on the
  *    device set bits of a sticky error word in the state buffer, read and
  *    cleared by emb_status_sync:
- *      EMB_FLAG_OUT_OF_RANGE  an id outside [0, rows of its table): that
- *                             occurrence contributes 0 and updates nothing;
+ *      EMB_FLAG_OUT_OF_RANGE  an id outside [0, rows of its table) other
+ *                             than EMB_ID_ABSENT: that occurrence
+ *                             contributes 0 and updates nothing;
  *      EMB_FLAG_BAD_OFFSETS   offsets not starting at 0, decreasing, or not
  *                             ending at nnz: outputs of that call are
  *                             unspecified, but no memory outside the given
@@ -146,6 +147,35 @@ emb_status_t emb_hash_find_or_insert(emb_table_t h, const int64_t* offsets,
                                      const uint64_t* keys, int64_t batch, int64_t nnz,
                                      int64_t* ids_out, void* ws, size_t ws_bytes,
                                      void* stream);
+
+/* An id that marks an absent feature: the forward treats it as a zero row
+ * (counted in a mean bag's length), the backward updates nothing, and no
+ * error bit is set.  emb_hash_find_or_insert_admit returns it for keys that
+ * are not admitted yet. */
+#define EMB_ID_ABSENT (-2)
+
+/* emb_hash_find_or_insert with frequency admission (DeepRec page, section
+ * "model quality", EmbeddingVariable item 1: features are admitted before
+ * they get a row, so rare keys cost no row; the page gives no rule).  The
+ * reading: a key without a row counts its occurrences over calls in
+ * key_counts; in the call where its count reaches min_count it gets a row
+ * (in order of its first occurrence in that call, initialised as a new key)
+ * and every occurrence of it in that call gets the row.  Until then its
+ * occurrences get EMB_ID_ABSENT.  A counted key holds a hash slot.  A call
+ * that is full (rows or slots) admits nothing: keys that would have got a
+ * row get -1, EMB_FLAG_TABLE_FULL is set, and their counts stay, so a later
+ * call with room admits them at once; when slots run out, which keys got a
+ * slot (and a count) is unspecified.
+ *   key_counts: device uint32 [T * hash_capacity], caller-owned, 4-byte
+ *   aligned, zero before the first call and kept between calls.
+ *   min_count <= 1: same as emb_hash_find_or_insert (key_counts may be NULL).
+ * EMB_ERR_INVALID_ARG for a null or misaligned key_counts with
+ * min_count > 1; otherwise as emb_hash_find_or_insert. */
+emb_status_t emb_hash_find_or_insert_admit(emb_table_t h, const int64_t* offsets,
+                                           const uint64_t* keys, int64_t batch, int64_t nnz,
+                                           int64_t* ids_out, uint32_t min_count,
+                                           uint32_t* key_counts, void* ws, size_t ws_bytes,
+                                           void* stream);
 
 /* Pooled lookup ("Merlin Distributed Embeddings", introduction and
  * "Background"; HugeCTR interview, section three, technique (5)):

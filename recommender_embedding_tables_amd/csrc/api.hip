@@ -497,9 +497,9 @@ emb_status_t emb_debug_sort_unique(emb_table_t t, const int64_t* offsets, const 
   return hip_status(e);
 }
 
-emb_status_t emb_hash_find_or_insert(emb_table_t t, const int64_t* offsets, const uint64_t* keys,
-                                     int64_t batch, int64_t nnz, int64_t* ids_out, void* ws,
-                                     size_t ws_bytes, void* stream) {
+static emb_status_t find_or_insert(emb_table_t t, const int64_t* offsets, const uint64_t* keys,
+                                   int64_t batch, int64_t nnz, int64_t* ids_out, void* ws,
+                                   size_t ws_bytes, void* stream, const AdmitArgs& adm) {
   if (!t || (nnz > 0 && (!keys || !ids_out))) return EMB_ERR_INVALID_ARG;
   if (!t->h.hashed) return EMB_ERR_UNSUPPORTED;
   emb_status_t st = check_batch(t->h, offsets, batch, nnz);
@@ -511,7 +511,27 @@ emb_status_t emb_hash_find_or_insert(emb_table_t t, const int64_t* offsets, cons
   if (nnz == 0) return EMB_OK;
   return hip_status(launch_hash_find_or_insert(t->h, p, offsets, keys, ids_out,
                                                static_cast<char*>(ws),
-                                               static_cast<hipStream_t>(stream)));
+                                               static_cast<hipStream_t>(stream), adm));
+}
+
+emb_status_t emb_hash_find_or_insert(emb_table_t t, const int64_t* offsets, const uint64_t* keys,
+                                     int64_t batch, int64_t nnz, int64_t* ids_out, void* ws,
+                                     size_t ws_bytes, void* stream) {
+  return find_or_insert(t, offsets, keys, batch, nnz, ids_out, ws, ws_bytes, stream,
+                        AdmitArgs());
+}
+
+emb_status_t emb_hash_find_or_insert_admit(emb_table_t t, const int64_t* offsets,
+                                           const uint64_t* keys, int64_t batch, int64_t nnz,
+                                           int64_t* ids_out, uint32_t min_count,
+                                           uint32_t* key_counts, void* ws, size_t ws_bytes,
+                                           void* stream) {
+  if (min_count > 1 && (!key_counts || (reinterpret_cast<uintptr_t>(key_counts) & 3u) != 0))
+    return EMB_ERR_INVALID_ARG;
+  AdmitArgs adm;
+  adm.counts = key_counts;
+  adm.min_count = min_count;
+  return find_or_insert(t, offsets, keys, batch, nnz, ids_out, ws, ws_bytes, stream, adm);
 }
 
 emb_status_t emb_status_sync(emb_table_t t, void* stream, uint32_t* flags_out) {

@@ -17,6 +17,10 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 constexpr uint64_t kEmptyKey = 0xFFFFFFFFFFFFFFFFull;
 constexpr uint64_t kUnsetRow = 0xFFFFFFFFFFFFFFFFull;  // row word of an empty slot
 constexpr uint64_t kPendingBit = 1ull << 62;           // row word = kPendingBit | first j
+// row word of a key that is counted but not admitted yet (frequency admission);
+// above every kPendingBit | j, so the first-occurrence atomicMin still works
+constexpr uint64_t kCandRow = 0xFFFFFFFFFFFFFFFEull;
+constexpr int64_t kAbsentId = -2;  // id of a feature without a row: looks up 0, no error
 constexpr uint32_t kNoRow = 0xFFFFFFFFu;
 constexpr int kMaxTables = 1024;
 
@@ -279,9 +283,16 @@ hipError_t launch_cache_prepare(Handle& h, const Plan& p, const uint32_t* sorted
 hipError_t launch_cache_flush(const Handle& h, hipStream_t s);
 hipError_t launch_cache_init(const Handle& h, hipStream_t s);
 
+// Frequency admission (counts != NULL and min_count > 1): counts[t * cap + slot]
+// counts the occurrences of a key without a row; a key gets a row in the call
+// where its count reaches min_count, else its ids are kAbsentId.
+struct AdmitArgs {
+  uint32_t* counts = nullptr;
+  uint32_t min_count = 0;
+};
 hipError_t launch_hash_find_or_insert(const Handle& h, const Plan& p, const int64_t* offsets,
                                       const uint64_t* keys, int64_t* ids_out, char* ws,
-                                      hipStream_t s);
+                                      hipStream_t s, const AdmitArgs& adm = AdmitArgs());
 
 hipError_t launch_hash_export(const Handle& h, int t, uint64_t* key_of_row, hipStream_t s);
 

@@ -101,7 +101,7 @@ __device__ __forceinline__ uint32_t bag_tile(
         const int64_t id = idv[k];
         if (rowmap) r = rowmap[s_start[i]];  // resolved by the prepare (tiered tables)
         else if (id >= 0 && id < rows[tb[k]]) r = (uint32_t)row_off[tb[k]] + (uint32_t)id;
-        else bad |= EMB_FLAG_OUT_OF_RANGE;
+        else if (id != kAbsentId) bad |= EMB_FLAG_OUT_OF_RANGE;
       }
       s_row[i] = r;
     }
@@ -170,7 +170,7 @@ __device__ __forceinline__ uint32_t bag_tile(
             } else {
               const int64_t id = ids[st + kb + lane];
               if (id >= 0 && id < nr) r = roff + (uint32_t)id;
-              else bad |= EMB_FLAG_OUT_OF_RANGE;
+              else if (id != kAbsentId) bad |= EMB_FLAG_OUT_OF_RANGE;
             }
           }
           const uint32_t kend = (len - kb) < (uint32_t)SG ? (len - kb) : (uint32_t)SG;

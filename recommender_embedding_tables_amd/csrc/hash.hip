@@ -33,6 +33,15 @@
 //                  and (.., 2d+1); G = accum_init.
 // Row assignment follows first occurrence and is deterministic; which slot a
 // key lands in depends on CAS order and is not part of the contract.
+//
+// Frequency admission (DeepRec page, section "model quality", EmbeddingVariable
+// item 1: features are admitted before they get a row).  With a count array
+// and min_count > 1, a key's slot also counts its occurrences (one atomicAdd
+// per occurrence of a key without a row, in the probe); k_hash_first and
+// k_hash_assign treat a first occurrence as new only when its key's count has
+// reached min_count.  Other keys keep their slot with the row word kCandRow
+// and get id -2 (absent).  A full call admits nothing: its would-be keys keep
+// kCandRow (and their counts) instead of emptying their slots.
 #include "embtab_internal.hpp"
 
 namespace embtab {
@@ -94,7 +103,8 @@ struct Slot {
 __global__ __launch_bounds__(256) void k_hash_probe(
     const int64_t* __restrict__ tbw, const uint64_t* __restrict__ keys, int64_t B, int32_t T,
     int64_t nnz, Slot* __restrict__ slots, int64_t cap, int64_t* __restrict__ ids_out,
-    uint32_t* __restrict__ slot_of, uint32_t* __restrict__ flags, uint32_t* __restrict__ misc) {
+    uint32_t* __restrict__ slot_of, uint32_t* __restrict__ flags, uint32_t* __restrict__ misc,
+    uint32_t* __restrict__ counts) {
   extern __shared__ int64_t tb[];
   load_table_bounds(tb, tbw, T);
   const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -137,6 +147,7 @@ __global__ __launch_bounds__(256) void k_hash_probe(
       ids_out[j] = (int64_t)r;
       slot_of[j] = kNoSlot;
     } else {
+      if (counts) atomicAdd(&counts[(size_t)t * (size_t)cap + s], 1u);  // not admitted yet
       if (pend < r) atomicMin((unsigned long long*)&st[s].row, (unsigned long long)pend);
       slot_of[j] = (uint32_t)s;
     }
@@ -155,6 +166,13 @@ __device__ inline bool is_first(const Slot* slots, int64_t cap, const uint32_t* 
   return slots[(size_t)t * (size_t)cap + s].row == (kPendingBit | (uint64_t)j);
 }
 
+// A first occurrence whose key gets a row in this call: always without
+// admission, else once the key's count has reached min_count.
+__device__ inline bool admitted(const uint32_t* counts, uint32_t min_count, int64_t cap,
+                                const uint32_t* slot_of, int32_t t, int64_t j) {
+  return !counts || counts[(size_t)t * (size_t)cap + slot_of[j]] >= min_count;
+}
+
 // Per block: the number of first occurrences (bcnt) and, for every table
 // whose first occurrence position tb[t] falls in this block, the number of
 // first occurrences of the block before tb[t] (tpart[t]).  With the block
@@ -164,7 +182,9 @@ __global__ __launch_bounds__(256) void k_hash_first(const int64_t* __restrict__ 
                                                     const Slot* __restrict__ slots, int64_t cap,
                                                     const uint32_t* __restrict__ slot_of,
                                                     uint32_t* __restrict__ bcnt,
-                                                    uint32_t* __restrict__ tpart) {
+                                                    uint32_t* __restrict__ tpart,
+                                                    const uint32_t* __restrict__ counts,
+                                                    uint32_t min_count) {
   extern __shared__ int64_t tb[];
   __shared__ uint32_t lds4[4];
   load_table_bounds(tb, tbw, T);
@@ -173,7 +193,7 @@ __global__ __launch_bounds__(256) void k_hash_first(const int64_t* __restrict__ 
   int32_t t = 0;
   if (j < nnz) {
     t = table_of(tb, T, j);
-    f = is_first(slots, cap, slot_of, t, j);
+    f = is_first(slots, cap, slot_of, t, j) && admitted(counts, min_count, cap, slot_of, t, j);
   }
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const uint64_t m = __ballot(f);
@@ -286,17 +306,23 @@ __global__ __launch_bounds__(256) void k_hash_assign(
     const int64_t* __restrict__ tbw, int64_t B, int32_t T, int64_t nnz,
     Slot* __restrict__ slots, int64_t cap, const uint32_t* __restrict__ slot_of,
     const uint32_t* __restrict__ bbase, const int64_t* __restrict__ n_live,
-    const uint32_t* __restrict__ misc, uint32_t* __restrict__ newlist) {
+    const uint32_t* __restrict__ misc, uint32_t* __restrict__ newlist,
+    const uint32_t* __restrict__ counts, uint32_t min_count) {
   extern __shared__ int64_t tb[];
   __shared__ uint32_t lds4[4];
   load_table_bounds(tb, tbw, T);
   const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  bool f = false;
+  bool f = false, cand = false;
   int32_t t = 0;
   if (j < nnz) {
     t = table_of(tb, T, j);
     f = is_first(slots, cap, slot_of, t, j);
+    if (f && !admitted(counts, min_count, cap, slot_of, t, j)) {
+      f = false;  // counted, no row yet
+      cand = true;
+    }
   }
+  if (cand) slots[(size_t)t * (size_t)cap + slot_of[j]].row = kCandRow;
   // block-wide exclusive count of first occurrences before this thread
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const uint64_t m = __ballot(f);
@@ -309,8 +335,12 @@ __global__ __launch_bounds__(256) void k_hash_assign(
   const uint32_t full = misc[kMiscHashOverflow];
   Slot* sl = slots + (size_t)t * (size_t)cap + slot_of[j];
   if (full) {
-    sl->key = kEmptyKey;
-    sl->row = kUnsetRow;
+    if (counts) {  // nothing is admitted; the key stays counted
+      sl->row = kCandRow;
+    } else {       // the slot was empty before this call
+      sl->key = kEmptyKey;
+      sl->row = kUnsetRow;
+    }
     return;
   }
   const uint32_t rank = g - misc[kMiscHashNew + T + t];
@@ -327,6 +357,7 @@ __global__ __launch_bounds__(256) void k_hash_finish(
     int64_t nnz, const Slot* __restrict__ slots, int64_t cap, const uint32_t* __restrict__ slot_of,
     int64_t* __restrict__ ids_out, const uint32_t* __restrict__ newlist,
     const uint32_t* __restrict__ misc, int64_t* __restrict__ n_live,
+    const uint32_t* __restrict__ counts, uint32_t min_count,
     const int64_t* __restrict__ row_off, const int64_t* __restrict__ rows, float* __restrict__ W,
     float* __restrict__ G, int32_t D,
     uint64_t seed, float stdv, float g0, uint32_t nfin) {
@@ -341,12 +372,13 @@ __global__ __launch_bounds__(256) void k_hash_finish(
     if (j >= nnz) return;
     const uint32_t s = slot_of[j];
     if (s == kNoSlot) return;
-    if (full) {
-      ids_out[j] = -1;
+    const int32_t t = table_of(tb, T, j);
+    if (full) {  // keys that would have got a row: -1; keys still counted: absent
+      ids_out[j] = admitted(counts, min_count, cap, slot_of, t, j) ? -1 : kAbsentId;
       return;
     }
-    const int32_t t = table_of(tb, T, j);
-    ids_out[j] = (int64_t)slots[(size_t)t * (size_t)cap + s].row;
+    const uint64_t r = slots[(size_t)t * (size_t)cap + s].row;
+    ids_out[j] = r < kPendingBit ? (int64_t)r : kAbsentId;
     return;
   }
   if (full) return;
@@ -396,7 +428,8 @@ __global__ __launch_bounds__(256) void k_hash_export(const Slot* __restrict__ st
 
 hipError_t launch_hash_find_or_insert(const Handle& h, const Plan& p, const int64_t* offsets,
                                       const uint64_t* keys, int64_t* ids_out, char* ws,
-                                      hipStream_t s) {
+                                      hipStream_t s, const AdmitArgs& adm) {
+  uint32_t* counts = adm.min_count > 1 ? adm.counts : nullptr;
   const int64_t nnz = p.nnz;
   uint32_t* misc = reinterpret_cast<uint32_t*>(ws + p.misc);
   uint32_t* slot_of = reinterpret_cast<uint32_t*>(ws + p.h_slot);
@@ -411,20 +444,21 @@ hipError_t launch_hash_find_or_insert(const Handle& h, const Plan& p, const int6
   hipLaunchKernelGGL(k_hash_start, dim3(1), dim3(256), shm, s, offsets, p.B, h.T, nnz, tbw, misc,
                      kMiscHashNew + 2 * h.T);
   hipLaunchKernelGGL(k_hash_probe, dim3(grid), dim3(256), shm, s, tbw, keys, p.B, h.T, nnz,
-                     slots, h.capacity, ids_out, slot_of, h.sv.flags, misc);
+                     slots, h.capacity, ids_out, slot_of, h.sv.flags, misc, counts);
   uint32_t* tpart = misc + kMiscHashNew + 2 * h.T;
   hipLaunchKernelGGL(k_hash_first, dim3(grid), dim3(256), shm, s, tbw, p.B, h.T, nnz, slots,
-                     h.capacity, slot_of, bcnt, tpart);
+                     h.capacity, slot_of, bcnt, tpart, counts, adm.min_count);
   hipLaunchKernelGGL(k_hash_plan, dim3(1), dim3(1024), 0, s, bcnt, nb, tbw, h.T, nnz, tpart,
                      h.sv.n_live, h.sv.rows, misc, h.sv.flags);
   hipLaunchKernelGGL(k_hash_assign, dim3(grid), dim3(256), shm, s, tbw, p.B, h.T, nnz, slots,
-                     h.capacity, slot_of, bcnt, h.sv.n_live, misc, newlist);
+                     h.capacity, slot_of, bcnt, h.sv.n_live, misc, newlist, counts,
+                     adm.min_count);
   // new rows: at most one per occurrence; enough blocks for a cold start
   int64_t igrid = (nnz * (h.D / 4) + 255) / 256;
   igrid = igrid < 1 ? 1 : (igrid > 2048 ? 2048 : igrid);
   hipLaunchKernelGGL(k_hash_finish, dim3(grid + (unsigned)igrid), dim3(256), shm, s, tbw,
                      keys, p.B, h.T, nnz, slots, h.capacity, slot_of, ids_out, newlist, misc,
-                     h.sv.n_live, h.sv.row_off, h.sv.rows, h.W, h.G, h.D, h.seed, h.stdv,
+                     h.sv.n_live, counts, adm.min_count, h.sv.row_off, h.sv.rows, h.W, h.G, h.D, h.seed, h.stdv,
                      h.accum0, grid);
   phase_mark(h, EMB_PHASE_HASH, true, s);
   return hipGetLastError();

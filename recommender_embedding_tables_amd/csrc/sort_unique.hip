@@ -120,7 +120,7 @@ __global__ __launch_bounds__(256) void k_keys(const int64_t* __restrict__ offset
     const int64_t id = ids[j];
     uint32_t key = sentinel;
     if (id >= 0 && id < rows[t]) key = (uint32_t)row_off[t] + (uint32_t)id;
-    else bad |= EMB_FLAG_OUT_OF_RANGE;
+    else if (id != kAbsentId) bad |= EMB_FLAG_OUT_OF_RANGE;
     keys[j] = key;
     const uint32_t g = (uint32_t)(s * T + t);
     if (mean)  // grad row and scale side by side: one gather in the last pass

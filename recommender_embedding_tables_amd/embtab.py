@@ -33,6 +33,7 @@ EMB_FLAG_TABLE_FULL = 8
 EMB_FLAG_CACHE_FULL = 32
 
 EMB_CACHE_WAYS = 16
+EMB_ID_ABSENT = -2
 
 EMB_POOL_SUM = 0
 EMB_POOL_MEAN = 1
@@ -46,7 +47,7 @@ EXPORTED = [
     "emb_debug_sort_unique", "emb_status_string", "emb_set_phase_events", "emb_bag_prepare",
     "emb_bag_backward_adagrad_prepared", "emb_bag_forward_prepared", "emb_cache_state_bytes",
     "emb_table_create_tiered", "emb_cache_flush", "emb_cache_stats",
-    "emb_bag_backward_adagrad_decay_prepared",
+    "emb_bag_backward_adagrad_decay_prepared", "emb_hash_find_or_insert_admit",
 ]
 
 EMB_PHASE_FORWARD, EMB_PHASE_KEYS, EMB_PHASE_SORT, EMB_PHASE_UNIQUE = 0, 1, 2, 3
@@ -109,6 +110,7 @@ def _load():
         "emb_table_create": (i32, [C.POINTER(emb_table_desc_t), P, C.POINTER(P)]),
         "emb_table_destroy": (i32, [P]),
         "emb_hash_find_or_insert": (i32, [P, P, P, i64, i64, P, P, sz, P]),
+        "emb_hash_find_or_insert_admit": (i32, [P, P, P, i64, i64, P, C.c_uint32, P, P, sz, P]),
         "emb_bag_forward": (i32, [P, P, P, i64, i64, i32, P, P, sz, P]),
         "emb_bag_backward_adagrad": (i32, [P, P, P, i64, i64, i32, P, f32, f32, P, sz, P]),
         "emb_status_sync": (i32, [P, P, C.POINTER(u32)]),
@@ -218,6 +220,13 @@ def emb_hash_find_or_insert(handle, offsets, keys, batch, nnz, ids_out, ws, ws_b
                             stream=None) -> int:
     return _lib.emb_hash_find_or_insert(handle, _ptr(offsets), _ptr(keys), batch, nnz,
                                         _ptr(ids_out), _ptr(ws), ws_bytes, _stream(stream))
+
+
+def emb_hash_find_or_insert_admit(handle, offsets, keys, batch, nnz, ids_out, min_count,
+                                  key_counts, ws, ws_bytes, stream=None) -> int:
+    return _lib.emb_hash_find_or_insert_admit(handle, _ptr(offsets), _ptr(keys), batch, nnz,
+                                              _ptr(ids_out), min_count, _ptr(key_counts),
+                                              _ptr(ws), ws_bytes, _stream(stream))
 
 
 def emb_bag_forward(handle, offsets, ids, batch, nnz, pool, out, ws=None, ws_bytes=0,
