@@ -164,9 +164,12 @@ __global__ __launch_bounds__(256) void k_seg_adagrad(
       }
       if (!vld[0]) break;  // the rest of the chunk holds no valid keys
       f4 g[UF][VEC], wv[UF][VEC], gv[UF][VEC];
+      uint32_t last[UF];  // Adagrad Decay: period of the row finished at u
       if (UPDATE) {
 #pragma unroll
         for (int u = 0; u < UF; ++u) {
+          last[u] = 0u;
+          if (DECAY && endf[u] && !startb[u]) last[u] = stamps[kk[u]];
 #pragma unroll
           for (int v = 0; v < VEC; ++v) {
             const uint32_t d4 = (uint32_t)(lane + v * SG);
@@ -197,9 +200,8 @@ __global__ __launch_bounds__(256) void k_seg_adagrad(
           if (!startb[u]) {
             float df = 1.0f;
             if (DECAY) {
-              const uint32_t last = stamps[kk[u]];
-              df = decay_factor(last, period, log2_rho);
-              if (lane == 0 && period > last) stamps[kk[u]] = period;
+              df = decay_factor(last[u], period, log2_rho);
+              if (lane == 0 && period > last[u]) stamps[kk[u]] = period;
             }
 #pragma unroll
             for (int v = 0; v < VEC; ++v) {
