@@ -50,9 +50,14 @@
 //  * Duplicate ids in one batch: their gradients are summed and the row gets
 //    one Adagrad step.  Accumulation is in ascending occurrence order.
 //  * Sort is stable: equal rows keep ascending occurrence position.
-//  * A key not yet in table t's map gets row n_live[t] + (rank of its first
-//    occurrence among this call's new keys); the call is all-or-nothing when
-//    the new keys would exceed the table's row capacity.
+//  * A key not yet in table t's map gets, in order of its first occurrence
+//    among this call's new keys, the next free row (rows freed by eviction,
+//    oldest eviction first), else row n_live[t] (rows never used, ascending);
+//    the call is all-or-nothing when the new keys would exceed the rows left.
+//  * Eviction (DeepRec page, section "model quality", EmbeddingVariable item 1
+//    names eviction policies and gives none): keys whose row was last used
+//    before a given step leave the map and free their rows; the caller keeps
+//    the per-row last-use step.
 //  * Initial values come from a counter-based generator built on SplitMix64
 //    (Steele, Lea and Flood, OOPSLA 2014): uniform rows for dense tables and
 //    Box-Muller (1958) normal rows for inserted keys.
@@ -76,6 +81,8 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <algorithm>
+#include <deque>
 #include <map>
 #include <set>
 #include <vector>
@@ -143,7 +150,19 @@ struct Model {
   std::map<int64_t, uint32_t> period_of;   // Adagrad Decay: period of the last update (else 0)
   std::vector<std::map<uint64_t, int64_t>> keymap;
   std::vector<std::map<uint64_t, uint64_t>> seen;  // admission: occurrences of keys without a row
-  std::vector<int64_t> n_live;
+  std::vector<int64_t> n_live;                    // rows ever handed out (high-water mark)
+  std::vector<std::deque<int64_t>> free_rows;     // eviction: rows to hand out again, in order
+
+  // Rows a call may still hand out in table t, and the next one.
+  int64_t room(int64_t t) const { return (int64_t)free_rows[t].size() + rows[t] - n_live[t]; }
+  int64_t next_row(int64_t t) {
+    if (!free_rows[t].empty()) {
+      const int64_t r = free_rows[t].front();
+      free_rows[t].pop_front();
+      return r;
+    }
+    return n_live[t]++;
+  }
 
   int64_t table_of(int64_t grow) const {
     int64_t t = 0;
@@ -263,6 +282,7 @@ void* orc_create(int64_t T, int64_t D, const int64_t* rows, int32_t hashed, uint
   m->accum0 = accum0;
   m->keymap.resize(T);
   m->seen.resize(T);
+  m->free_rows.resize(T);
   m->n_live.assign(T, 0);
   return m;
 }
@@ -440,7 +460,7 @@ int32_t orc_hash_find_or_insert(void* h, const int64_t* offsets, const uint64_t*
       if (keys[j] == kReservedKey) continue;
       if (m->keymap[t].find(keys[j]) == m->keymap[t].end()) fresh.insert(keys[j]);
     }
-    if (m->n_live[t] + (int64_t)fresh.size() > m->rows[t]) full = true;
+    if ((int64_t)fresh.size() > m->room(t)) full = true;
   }
   if (full) flags |= 8;
   // Pass 2: look up, inserting in order of first occurrence unless full.
@@ -452,7 +472,7 @@ int32_t orc_hash_find_or_insert(void* h, const int64_t* offsets, const uint64_t*
       auto it = m->keymap[t].find(key);
       if (it != m->keymap[t].end()) { ids_out[j] = it->second; continue; }
       if (full) { ids_out[j] = -1; continue; }
-      const int64_t row = m->n_live[t]++;
+      const int64_t row = m->next_row(t);
       m->keymap[t][key] = row;
       RowState rs;
       rs.w.resize(D);
@@ -483,7 +503,7 @@ int32_t orc_hash_find_or_insert_admit(void* h, const int64_t* offsets, const uin
       if (key == kReservedKey || m->keymap[t].count(key)) continue;
       if (++m->seen[t][key] >= (uint64_t)(min_count > 0 ? min_count : 1)) admitted[t].insert(key);
     }
-    if (m->n_live[t] + (int64_t)admitted[t].size() > m->rows[t]) full = true;
+    if ((int64_t)admitted[t].size() > m->room(t)) full = true;
   }
   if (full) flags |= 8;
   // Pass 2: ids; admitted keys get rows in order of first occurrence.
@@ -495,7 +515,7 @@ int32_t orc_hash_find_or_insert_admit(void* h, const int64_t* offsets, const uin
       if (it != m->keymap[t].end()) { ids_out[j] = it->second; continue; }
       if (!admitted[t].count(key)) { ids_out[j] = kAbsentId; continue; }
       if (full) { ids_out[j] = -1; continue; }
-      const int64_t row = m->n_live[t]++;
+      const int64_t row = m->next_row(t);
       m->keymap[t][key] = row;
       m->seen[t].erase(key);
       RowState rs;
@@ -514,6 +534,36 @@ uint64_t orc_admission_count(void* h, int64_t t, uint64_t key) {
   Model* m = static_cast<Model*>(h);
   auto it = m->seen[t].find(key);
   return it == m->seen[t].end() ? 0 : it->second;
+}
+
+// Eviction: every key of every table whose row was last used before `before`
+// (last_used is indexed by global row) leaves the map; its row becomes free.
+// Each table's freed rows join the end of its free list in ascending order.
+// Counted keys without a row are forgotten.  Returns the number of evicted keys.
+int64_t orc_hash_evict(void* h, const uint32_t* last_used, uint32_t before) {
+  Model* m = static_cast<Model*>(h);
+  if (!m->hashed) return -1;
+  int64_t n = 0;
+  for (int64_t t = 0; t < m->T; ++t) {
+    std::vector<int64_t> freed;
+    for (auto it = m->keymap[t].begin(); it != m->keymap[t].end();) {
+      if (last_used[m->row_off[t] + it->second] < before) {
+        freed.push_back(it->second);
+        it = m->keymap[t].erase(it);
+      } else {
+        ++it;
+      }
+    }
+    std::sort(freed.begin(), freed.end());
+    for (int64_t r : freed) m->free_rows[t].push_back(r);
+    n += (int64_t)freed.size();
+    m->seen[t].clear();
+  }
+  return n;
+}
+
+int64_t orc_free_rows(void* h, int64_t t) {
+  return (int64_t) static_cast<Model*>(h)->free_rows[t].size();
 }
 
 int64_t orc_n_live(void* h, int64_t t) { return static_cast<Model*>(h)->n_live[t]; }

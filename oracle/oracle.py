@@ -53,6 +53,8 @@ def _load():
         "orc_hash_find_or_insert_admit": (i32, [P, P, P, i64, i64, P, C.c_uint32]),
         "orc_admission_count": (u64, [P, i64, u64]),
         "orc_n_live": (i64, [P, i64]),
+        "orc_hash_evict": (i64, [P, P, C.c_uint32]),
+        "orc_free_rows": (i64, [P, i64]),
         "orc_hash_export": (i64, [P, i64, P, P, i64]),
     }
     for name, (res, args) in sig.items():
@@ -206,6 +208,16 @@ class Oracle:
         flags = _load().orc_hash_find_or_insert_admit(self._h, _p(offsets), _p(keys), batch,
                                                       keys.size, _p(ids), int(min_count))
         return ids, int(flags)
+
+    def evict(self, last_used, before):
+        """Keys whose row (global index into last_used) was last used before
+        `before` leave the map; their rows are handed out again later."""
+        last_used = _arr(last_used, np.uint32)
+        assert last_used.size == int(self.row_off[-1])
+        return int(_load().orc_hash_evict(self._h, _p(last_used), int(before)))
+
+    def free_rows(self, t):
+        return int(_load().orc_free_rows(self._h, t))
 
     def admission_count(self, t, key):
         return int(_load().orc_admission_count(self._h, t, int(key)))

@@ -647,6 +647,106 @@ def test_absent_ids_contribute_nothing_without_error():
     assert o.forward(offsets, ids, B, False)[1] == orc.ERR_OUT_OF_RANGE
 
 
+# ---------------------------------------------------------------- eviction
+
+def test_worked_eviction_and_row_reuse():
+    o = orc.Oracle([4], 2, hashed=True, seed=1)
+    one = lambda keys: o.find_or_insert(np.array([0, len(keys)], np.int64),
+                                        np.array(keys, np.uint64), 1)
+    A, Bk, Ck, Dk, Ek, Fk = 10, 20, 30, 40, 50, 60
+    assert one([A, Bk, Ck, A])[0].tolist() == [0, 1, 2, 0]
+    # rows 1 and 2 were last used before step 4, row 0 after it
+    assert o.evict(np.array([5, 1, 3, 0], np.uint32), 4) == 2
+    assert o.free_rows(0) == 2 and o.n_live(0) == 3
+    # freed rows first (ascending), then the unused row 3
+    ids, fl = one([Dk, Ek, A, Fk])
+    assert fl == 0 and ids.tolist() == [1, 2, 0, 3]
+    assert o.free_rows(0) == 0 and o.n_live(0) == 4
+    keys, rows = o.export(0)
+    assert dict(zip(keys.tolist(), rows.tolist())) == {A: 0, Dk: 1, Ek: 2, Fk: 3}
+    # no room left: nothing is inserted
+    ids, fl = one([Bk])
+    assert fl == orc.ERR_TABLE_FULL and ids.tolist() == [-1]
+    # an evicted key that returns is a new key: a fresh row and fresh values
+    o.evict(np.array([9, 9, 9, 0], np.uint32), 5)  # evicts F (row 3)
+    W_before = o.read_rows([3])[0]
+    assert one([Bk])[0].tolist() == [3]
+    assert not np.array_equal(o.read_rows([3])[0], W_before)
+
+
+def _evict_model(calls, T, B, cap):
+    """Insertion with a free-row queue per table; calls are ("insert", off,
+    keys) or ("evict", last_used_per_table, before)."""
+    from collections import deque
+    maps = [dict() for _ in range(T)]
+    free = [deque() for _ in range(T)]
+    high = [0] * T
+    out = []
+    for c in calls:
+        if c[0] == "evict":
+            _, last, before = c
+            for t in range(T):
+                gone = sorted(r for k, r in maps[t].items() if last[t][r] < before)
+                maps[t] = {k: r for k, r in maps[t].items() if last[t][r] >= before}
+                free[t].extend(gone)
+            out.append(None)
+            continue
+        _, off, keys = c
+        segs = [[int(k) for k in keys[off[t * B]:off[(t + 1) * B]]] for t in range(T)]
+        new = [list(dict.fromkeys(k for k in segs[t] if k not in maps[t])) for t in range(T)]
+        full = any(len(new[t]) > len(free[t]) + cap - high[t] for t in range(T))
+        ids = []
+        for t in range(T):
+            if not full:
+                for k in new[t]:
+                    if free[t]:
+                        maps[t][k] = free[t].popleft()
+                    else:
+                        maps[t][k] = high[t]
+                        high[t] += 1
+            ids += [maps[t].get(k, -1) for k in segs[t]]
+        out.append((np.array(ids, np.int64), full))
+    return out, maps
+
+
+def test_eviction_matches_free_queue_model():
+    T, cap = 2, 120
+    w = synth.workload(5, T=T, B=50, universe=400, hash_capacity=1024, max_load=0.5)
+    w.rows = np.full(T, cap, np.int64)
+    o = orc.Oracle(w.rows, 4, hashed=True, seed=w.seed)
+    rng = np.random.default_rng(3)
+    calls = []
+    for bi in range(10):
+        off, ranks = synth.gen_batch(w, bi)
+        calls.append(("insert", off, synth.gen_keys(w, off, ranks)))
+        if bi % 3 == 2:
+            last = [rng.integers(0, 10, cap).astype(np.uint32) for _ in range(T)]
+            calls.append(("evict", last, 4))
+    ref, maps = _evict_model(calls, T, w.B, cap)
+    n_evicted = 0
+    for c, r in zip(calls, ref):
+        if c[0] == "evict":
+            n_evicted += o.evict(np.concatenate(c[1]), c[2])
+            continue
+        ids, fl = o.find_or_insert(c[1], c[2], w.B)
+        assert ids.tolist() == r[0].tolist()
+        assert bool(fl & orc.ERR_TABLE_FULL) == r[1]
+    for t in range(T):
+        keys, rows = o.export(t)
+        assert dict(zip(keys.tolist(), rows.tolist())) == maps[t]
+    assert n_evicted > 0 and any(r[1] for r in ref if r) and not all(r[1] for r in ref if r)
+
+
+def test_eviction_forgets_counted_keys():
+    o = orc.Oracle([8], 2, hashed=True, seed=1)
+    off = np.array([0, 2], np.int64)
+    o.find_or_insert_admit(off, np.array([7, 8], np.uint64), 1, 2)
+    assert o.admission_count(0, 7) == 1
+    o.evict(np.zeros(8, np.uint32), 0)  # evicts no row
+    assert o.admission_count(0, 7) == 0
+    assert o.find_or_insert_admit(off, np.array([7, 7], np.uint64), 1, 2)[0].tolist() == [0, 0]
+
+
 def test_hash_tables_are_independent_and_rows_initialised():
     o = orc.Oracle([10, 10], 3, hashed=True, seed=8, init_std=0.02, accum_init=0.1)
     off = np.array([0, 3, 5], np.int64)  # B = 1
