@@ -105,10 +105,12 @@ typedef struct {
   float accum_init;               /* initial Adagrad accumulator of every row */
   int32_t init_storage;           /* 1: initialise weights, accum, slots and state;
                                      0: attach to storage written by an earlier handle */
+  uint32_t* free_rows;            /* hashed only, may be NULL: device uint32 [sum rows], the
+                                     queue of rows freed by emb_hash_evict (needed for it) */
 } emb_table_desc_t;
 
 /* Bytes of the caller-owned state buffer for T tables (row offsets, row
- * capacities, live-row counters, error word). */
+ * capacities, live-row counters, free-row queue positions, error word). */
 size_t emb_state_bytes(int32_t num_tables);
 
 /* Bytes of the hash slot array: T * capacity slots of 16 bytes,
@@ -141,12 +143,38 @@ emb_status_t emb_table_destroy(emb_table_t h);
  * 2d) and (.., 2d+1), and its accumulator to accum_init.  All-or-nothing: if
  * the new keys of any table would exceed rows_per_table, nothing is inserted,
  * new keys get id -1 and EMB_FLAG_TABLE_FULL is set.  Reserved keys get -1.
+ * With eviction (emb_hash_evict) a new key takes a queued free row before
+ * row n_live[t], and the call is full when the new keys outnumber the queued
+ * rows plus the rows never used.
  * Row assignment is deterministic; slot positions are not (several layouts
  * are correct).  Needs a hashed handle. */
 emb_status_t emb_hash_find_or_insert(emb_table_t h, const int64_t* offsets,
                                      const uint64_t* keys, int64_t batch, int64_t nnz,
                                      int64_t* ids_out, void* ws, size_t ws_bytes,
                                      void* stream);
+
+/* Eviction of hashed keys (DeepRec page, section "model quality",
+ * EmbeddingVariable item 1: feature eviction policies; the page gives none).
+ * The reading: every key whose row was last used before `before` leaves its
+ * table and its row is freed.  Freed rows wait in a queue per table
+ * (desc->free_rows; rows freed by one call in ascending order) and are handed
+ * to new keys, oldest first, before rows never used; a reused row is
+ * initialised like any new key's.  The slot arrays are rebuilt from the
+ * remaining keys, and keys counted for admission but without a row are
+ * dropped (pass the admission key_counts to have them cleared; NULL if
+ * admission is not used).
+ *   row_last_used: device uint32 [sum rows], by global row, the caller's
+ *   record of each row's last use (for instance the row_periods written by
+ *   emb_bag_backward_adagrad_decay_prepared with period = step; with rho = 1
+ *   that is plain Adagrad).  Rows that hold no key are ignored.
+ *   ws: emb_hash_evict_workspace_bytes(h) bytes, 256-byte aligned (about
+ *   16 bytes per slot plus one per row).
+ * EMB_ERR_UNSUPPORTED on dense tables or without desc->free_rows. */
+size_t emb_hash_evict_workspace_bytes(emb_table_t h);
+emb_status_t emb_hash_evict(emb_table_t h, const uint32_t* row_last_used, uint32_t before,
+                            uint32_t* key_counts, void* ws, size_t ws_bytes, void* stream);
+/* HOST out [T]: rows waiting in each table's free-row queue (waits for the stream). */
+emb_status_t emb_hash_free_rows(emb_table_t h, void* stream, int64_t* queued_out);
 
 /* An id that marks an absent feature: the forward treats it as a zero row
  * (counted in a mean bag's length), the backward updates nothing, and no

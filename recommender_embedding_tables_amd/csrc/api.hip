@@ -160,7 +160,7 @@ static emb_status_t create_impl(const emb_table_desc_t* d, const emb_tier_desc_t
   }
   if (d->hashed) {
     if (emb_hash_bytes(d->num_tables, d->hash_capacity) == 0 || !d->hash_slots ||
-        !aligned16(d->hash_slots))
+        !aligned16(d->hash_slots) || (reinterpret_cast<uintptr_t>(d->free_rows) & 3u) != 0)
       return EMB_ERR_INVALID_ARG;
     if (!(d->max_load > 0.0f && d->max_load <= 0.9f)) return EMB_ERR_INVALID_ARG;
     for (int t = 0; t < d->num_tables; ++t)
@@ -202,6 +202,7 @@ static emb_status_t create_impl(const emb_table_desc_t* d, const emb_tier_desc_t
   h.hashed = d->hashed != 0;
   h.capacity = h.hashed ? d->hash_capacity : 0;
   h.slots = h.hashed ? d->hash_slots : nullptr;
+  h.free_rows = h.hashed ? d->free_rows : nullptr;
   h.seed = d->seed;
   h.lo = d->init_lo;
   h.hi = d->init_hi;
@@ -220,7 +221,7 @@ static emb_status_t create_impl(const emb_table_desc_t* d, const emb_tier_desc_t
   hipError_t e = hipSuccess;
   if (d->init_storage) {
     // state: flags 0, row offsets, capacities, live rows 0
-    std::vector<int64_t> host(3 * (size_t)h.T + 1, 0);
+    std::vector<int64_t> host(5 * (size_t)h.T + 1, 0);  // + free-row queues, empty
     for (int t = 0; t <= h.T; ++t) host[t] = h.row_off[t];
     for (int t = 0; t < h.T; ++t) host[h.T + 1 + t] = h.rows[t];
     e = hipMemsetAsync(h.sv.flags, 0, 256, s);
@@ -532,6 +533,36 @@ emb_status_t emb_hash_find_or_insert_admit(emb_table_t t, const int64_t* offsets
   adm.counts = key_counts;
   adm.min_count = min_count;
   return find_or_insert(t, offsets, keys, batch, nnz, ids_out, ws, ws_bytes, stream, adm);
+}
+
+size_t emb_hash_evict_workspace_bytes(emb_table_t t) {
+  if (!t || !t->h.hashed) return 0;
+  return hash_evict_workspace_bytes(t->h);
+}
+
+emb_status_t emb_hash_evict(emb_table_t t, const uint32_t* row_last_used, uint32_t before,
+                            uint32_t* key_counts, void* ws, size_t ws_bytes, void* stream) {
+  if (!t || !row_last_used || (reinterpret_cast<uintptr_t>(row_last_used) & 3u) != 0 ||
+      (reinterpret_cast<uintptr_t>(key_counts) & 3u) != 0)
+    return EMB_ERR_INVALID_ARG;
+  if (!t->h.hashed || !t->h.free_rows) return EMB_ERR_UNSUPPORTED;
+  if (!ws || ws_bytes < hash_evict_workspace_bytes(t->h) ||
+      (reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
+    return EMB_ERR_WORKSPACE;
+  return hip_status(launch_hash_evict(t->h, row_last_used, before, key_counts,
+                                      static_cast<char*>(ws), static_cast<hipStream_t>(stream)));
+}
+
+emb_status_t emb_hash_free_rows(emb_table_t t, void* stream, int64_t* queued_out) {
+  if (!t || !queued_out) return EMB_ERR_INVALID_ARG;
+  if (!t->h.hashed) return EMB_ERR_UNSUPPORTED;
+  std::vector<int64_t> q(2 * (size_t)t->h.T);
+  hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+  if (e == hipSuccess)  // q_head and q_tail are adjacent in the state
+    e = hipMemcpy(q.data(), t->h.sv.q_head, sizeof(int64_t) * q.size(), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return EMB_ERR_HIP;
+  for (int i = 0; i < t->h.T; ++i) queued_out[i] = q[t->h.T + i] - q[i];
+  return EMB_OK;
 }
 
 emb_status_t emb_status_sync(emb_table_t t, void* stream, uint32_t* flags_out) {

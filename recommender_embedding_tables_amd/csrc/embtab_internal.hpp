@@ -38,11 +38,16 @@ struct StateView {
   uint32_t* flags;
   int64_t* row_off;
   int64_t* rows;
-  int64_t* n_live;
+  int64_t* n_live;  // rows ever handed out (rows >= n_live were never used)
+  // Free-row queue of table t (hashed tables with eviction): entries
+  // q_head[t] .. q_tail[t] - 1, entry q stored at free_rows[row_off[t] + q % rows[t]]
+  // (a ring: at most rows[t] rows are free at once).
+  int64_t* q_head;
+  int64_t* q_tail;
 };
 
 inline size_t state_bytes(int T) {
-  size_t b = 256 + sizeof(int64_t) * (size_t)(3 * T + 1);
+  size_t b = 256 + sizeof(int64_t) * (size_t)(5 * T + 1);
   return (b + 255) & ~(size_t)255;
 }
 
@@ -53,6 +58,8 @@ inline StateView state_view(void* state, int T) {
   v.row_off = reinterpret_cast<int64_t*>(p + 256);
   v.rows = v.row_off + (T + 1);
   v.n_live = v.rows + T;
+  v.q_head = v.n_live + T;
+  v.q_tail = v.q_head + T;
   return v;
 }
 
@@ -65,6 +72,7 @@ struct Handle {
   float* G = nullptr;
   void* state = nullptr;
   StateView sv{};
+  uint32_t* free_rows = nullptr;  // hashed tables with eviction
   bool hashed = false;
   int64_t capacity = 0;
   void* slots = nullptr;
@@ -295,6 +303,9 @@ hipError_t launch_hash_find_or_insert(const Handle& h, const Plan& p, const int6
                                       hipStream_t s, const AdmitArgs& adm = AdmitArgs());
 
 hipError_t launch_hash_export(const Handle& h, int t, uint64_t* key_of_row, hipStream_t s);
+size_t hash_evict_workspace_bytes(const Handle& h);
+hipError_t launch_hash_evict(const Handle& h, const uint32_t* last_used, uint32_t before,
+                             uint32_t* key_counts, char* ws, hipStream_t s);
 
 hipError_t launch_debug_copy_sorted(const uint32_t* keys, uint32_t sentinel, uint32_t* out,
                                     int64_t n, hipStream_t s);

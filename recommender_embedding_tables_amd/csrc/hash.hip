@@ -217,6 +217,8 @@ __global__ __launch_bounds__(1024) void k_hash_plan(uint32_t* __restrict__ bcnt,
                                                     const uint32_t* __restrict__ tpart,
                                                     const int64_t* __restrict__ n_live,
                                                     const int64_t* __restrict__ rows,
+                                                    const int64_t* __restrict__ q_head,
+                                                    const int64_t* __restrict__ q_tail,
                                                     uint32_t* __restrict__ misc,
                                                     uint32_t* __restrict__ flags) {
   constexpr uint32_t PER = 16;
@@ -292,7 +294,8 @@ __global__ __launch_bounds__(1024) void k_hash_plan(uint32_t* __restrict__ bcnt,
     const uint32_t nw = b1 >= b0 ? b1 - b0 : 0u;
     misc[kMiscHashNew + t] = nw;
     misc[kMiscHashNew + T + t] = b0;
-    if (n_live[t] + (int64_t)nw > rows[t]) s_full = 1u;  // every writer stores 1
+    // rows left: queued free rows, then rows never used
+    if ((int64_t)nw > q_tail[t] - q_head[t] + rows[t] - n_live[t]) s_full = 1u;  // all store 1
   }
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -307,7 +310,10 @@ __global__ __launch_bounds__(256) void k_hash_assign(
     Slot* __restrict__ slots, int64_t cap, const uint32_t* __restrict__ slot_of,
     const uint32_t* __restrict__ bbase, const int64_t* __restrict__ n_live,
     const uint32_t* __restrict__ misc, uint32_t* __restrict__ newlist,
-    const uint32_t* __restrict__ counts, uint32_t min_count) {
+    const uint32_t* __restrict__ counts, uint32_t min_count,
+    const uint32_t* __restrict__ free_rows, const int64_t* __restrict__ row_off,
+    const int64_t* __restrict__ rows, const int64_t* __restrict__ q_head,
+    const int64_t* __restrict__ q_tail) {
   extern __shared__ int64_t tb[];
   __shared__ uint32_t lds4[4];
   load_table_bounds(tb, tbw, T);
@@ -344,7 +350,14 @@ __global__ __launch_bounds__(256) void k_hash_assign(
     return;
   }
   const uint32_t rank = g - misc[kMiscHashNew + T + t];
-  sl->row = (uint64_t)(n_live[t] + (int64_t)rank);
+  // queued free rows first (oldest first), then rows never used
+  const int64_t queued = q_tail[t] - q_head[t];
+  int64_t row;
+  if ((int64_t)rank < queued)
+    row = (int64_t)free_rows[row_off[t] + (q_head[t] + (int64_t)rank) % rows[t]];
+  else
+    row = n_live[t] + ((int64_t)rank - queued);
+  sl->row = (uint64_t)row;
   newlist[g] = (uint32_t)j;
 }
 
@@ -357,6 +370,7 @@ __global__ __launch_bounds__(256) void k_hash_finish(
     int64_t nnz, const Slot* __restrict__ slots, int64_t cap, const uint32_t* __restrict__ slot_of,
     int64_t* __restrict__ ids_out, const uint32_t* __restrict__ newlist,
     const uint32_t* __restrict__ misc, int64_t* __restrict__ n_live,
+    int64_t* __restrict__ q_head, const int64_t* __restrict__ q_tail,
     const uint32_t* __restrict__ counts, uint32_t min_count,
     const int64_t* __restrict__ row_off, const int64_t* __restrict__ rows, float* __restrict__ W,
     float* __restrict__ G, int32_t D,
@@ -366,8 +380,13 @@ __global__ __launch_bounds__(256) void k_hash_finish(
   const bool full = misc[kMiscHashOverflow] != 0u;
   if (blockIdx.x < nfin) {
     if (blockIdx.x == 0 && !full)
-      for (int t = threadIdx.x; t < T; t += blockDim.x)
-        n_live[t] += (int64_t)misc[kMiscHashNew + t];
+      for (int t = threadIdx.x; t < T; t += blockDim.x) {
+        const int64_t nw = (int64_t)misc[kMiscHashNew + t];
+        const int64_t queued = q_tail[t] - q_head[t];
+        const int64_t take = nw < queued ? nw : queued;
+        q_head[t] += take;
+        n_live[t] += nw - take;
+      }
     const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (j >= nnz) return;
     const uint32_t s = slot_of[j];
@@ -424,6 +443,191 @@ __global__ __launch_bounds__(256) void k_hash_export(const Slot* __restrict__ st
   }
 }
 
+
+// ------------------------------------------------------------------ eviction
+// emb_hash_evict (DeepRec page, section "model quality", EmbeddingVariable
+// item 1: eviction policies).  Keys whose row was last used before `before`
+// leave their table and their rows join the table's free-row queue, in
+// ascending order; the slot arrays are rebuilt from the other live keys, so
+// probe sequences stay short and counted keys without a row are dropped.
+//   k_evict_mark     per slot: flag the rows of evicted keys; copy the other
+//                    live keys to the table's survivor list
+//   k_evict_count    flagged rows per block of kEvictSpan rows
+//   k_evict_scan     one block: exclusive scan of the block counts
+//   k_evict_tables   per table: its first flagged row's global rank, and
+//                    how many of its rows are freed
+//   k_evict_scatter  a flagged row of table t with rank i (among t's flagged
+//                    rows) goes to queue entry q_tail[t] + i
+//   k_evict_finish   queue tails
+//   (slots filled empty)
+//   k_evict_reinsert survivors back into the empty slot arrays
+constexpr int64_t kEvictSpan = 4096;  // rows per counting block: 256 threads x 16
+
+__global__ __launch_bounds__(256) void k_evict_mark(const Slot* __restrict__ slots, int64_t cap,
+                                                    const int64_t* __restrict__ row_off,
+                                                    const uint32_t* __restrict__ last_used,
+                                                    uint32_t before, uint8_t* __restrict__ flag,
+                                                    Slot* __restrict__ surv,
+                                                    uint32_t* __restrict__ nsurv) {
+  const int32_t t = blockIdx.y;
+  const int64_t s = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  bool keep = false;
+  Slot sl{kEmptyKey, kUnsetRow};
+  if (s < cap) {
+    sl = slots[(size_t)t * (size_t)cap + s];
+    const int64_t nrows = row_off[t + 1] - row_off[t];
+    if (sl.key != kEmptyKey && sl.row < (uint64_t)nrows) {
+      const int64_t g = row_off[t] + (int64_t)sl.row;
+      if (last_used[g] < before) flag[g] = 1u;
+      else keep = true;
+    }
+  }
+  const uint64_t m = __ballot(keep);
+  if (m == 0) return;
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint32_t leader = (uint32_t)__ffsll((unsigned long long)m) - 1u;
+  uint32_t at = 0;
+  if (lane == leader) at = atomicAdd(&nsurv[t], (uint32_t)__popcll(m));
+  at = (uint32_t)__shfl((int)at, (int)leader, 64);
+  if (keep) surv[(size_t)t * (size_t)cap + at + lanes_below(m)] = sl;
+}
+
+// Flags of rows [16 i, 16 i + 16) of this block's span, as a count.
+__device__ inline uint32_t count16(const uint8_t* flag, int64_t lo, int64_t total) {
+  uint32_t c = 0;
+  if (lo + 16 <= total) {
+    const uint4 x = *reinterpret_cast<const uint4*>(flag + lo);
+    // each byte is 0 or 1
+    c = (uint32_t)__popc(x.x) + (uint32_t)__popc(x.y) + (uint32_t)__popc(x.z) +
+        (uint32_t)__popc(x.w);
+  } else {
+    for (int64_t r = lo; r < total; ++r) c += flag[r];
+  }
+  return c;
+}
+
+__global__ __launch_bounds__(256) void k_evict_count(const uint8_t* __restrict__ flag,
+                                                     int64_t total, uint32_t* __restrict__ bcnt) {
+  __shared__ uint32_t wsum[4];
+  const int64_t lo = (int64_t)blockIdx.x * kEvictSpan + 16 * (int64_t)threadIdx.x;
+  uint32_t c = count16(flag, lo, total);
+  for (int o = 32; o > 0; o >>= 1) c += (uint32_t)__shfl_down((int)c, o, 64);
+  if ((threadIdx.x & 63u) == 0) wsum[threadIdx.x >> 6] = c;
+  __syncthreads();
+  if (threadIdx.x == 0) bcnt[blockIdx.x] = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+}
+
+// One block of 1024 threads: bcnt[0 .. n) -> exclusive prefix sums, bcnt[n] = total.
+__global__ __launch_bounds__(1024) void k_evict_scan(uint32_t* __restrict__ bcnt, uint32_t n) {
+  __shared__ uint32_t wsum[16];
+  const uint32_t per = (n + 1023u) / 1024u;
+  const uint32_t lo = threadIdx.x * per;
+  const uint32_t hi = lo + per < n ? lo + per : n;
+  uint32_t sum = 0;
+  for (uint32_t i = lo; i < hi; ++i) sum += bcnt[i];
+  uint32_t x = sum;
+  const uint32_t lane = threadIdx.x & 63u, w = threadIdx.x >> 6;
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = (uint32_t)__shfl_up((int)x, o, 64);
+    if (lane >= (uint32_t)o) x += y;
+  }
+  if (lane == 63u) wsum[w] = x;
+  __syncthreads();
+  uint32_t before = 0, total = 0;
+  for (uint32_t i = 0; i < 16u; ++i) {
+    before += i < w ? wsum[i] : 0u;
+    total += wsum[i];
+  }
+  uint32_t run = before + x - sum;
+  for (uint32_t i = lo; i < hi; ++i) {
+    const uint32_t c = bcnt[i];
+    bcnt[i] = run;
+    run += c;
+  }
+  if (threadIdx.x == 0) bcnt[n] = total;
+}
+
+// Global rank (flags before it) of row r: block base plus the flags of its
+// block before r.
+__device__ inline uint32_t flag_rank(const uint8_t* flag, const uint32_t* bbase, int64_t r) {
+  const int64_t b = r / kEvictSpan;
+  uint32_t c = bbase[b];
+  for (int64_t q = b * kEvictSpan; q < r; ++q) c += flag[q];
+  return c;
+}
+
+__global__ __launch_bounds__(256) void k_evict_tables(const uint8_t* __restrict__ flag,
+                                                      const uint32_t* __restrict__ bbase,
+                                                      const int64_t* __restrict__ row_off,
+                                                      int32_t T, uint32_t* __restrict__ tbase,
+                                                      uint32_t* __restrict__ freed) {
+  for (int32_t t = blockIdx.x * 256 + threadIdx.x; t < T; t += gridDim.x * 256) {
+    const uint32_t p0 = flag_rank(flag, bbase, row_off[t]);
+    const uint32_t p1 = flag_rank(flag, bbase, row_off[t + 1]);
+    tbase[t] = p0;
+    freed[t] = p1 - p0;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_evict_scatter(
+    const uint8_t* __restrict__ flag, int64_t total, const uint32_t* __restrict__ bbase,
+    const int64_t* __restrict__ row_off, const int64_t* __restrict__ rows, int32_t T,
+    const uint32_t* __restrict__ tbase, const int64_t* __restrict__ q_tail,
+    uint32_t* __restrict__ free_rows) {
+  __shared__ uint32_t wsum[4];
+  const int64_t lo = (int64_t)blockIdx.x * kEvictSpan + 16 * (int64_t)threadIdx.x;
+  const uint32_t c = count16(flag, lo, total);
+  // exclusive count of the block's flags before this thread's 16 rows
+  uint32_t x = c;
+  const uint32_t lane = threadIdx.x & 63u, w = threadIdx.x >> 6;
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = (uint32_t)__shfl_up((int)x, o, 64);
+    if (lane >= (uint32_t)o) x += y;
+  }
+  if (lane == 63u) wsum[w] = x;
+  __syncthreads();
+  uint32_t rank = bbase[blockIdx.x] + x - c;
+  for (uint32_t i = 0; i < w; ++i) rank += wsum[i];
+  if (c == 0) return;
+  for (int64_t r = lo; r < lo + 16 && r < total; ++r) {
+    if (!flag[r]) continue;
+    int32_t a = 0, b = T;  // table of r: row_off[a] <= r < row_off[a + 1]
+    while (b - a > 1) {
+      const int32_t mid = (a + b) >> 1;
+      if (row_off[mid] <= r) a = mid;
+      else b = mid;
+    }
+    const int64_t q = q_tail[a] + (int64_t)(rank - tbase[a]);
+    free_rows[row_off[a] + q % rows[a]] = (uint32_t)(r - row_off[a]);
+    ++rank;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_evict_finish(const uint32_t* __restrict__ freed,
+                                                      int32_t T, int64_t* __restrict__ q_tail) {
+  for (int32_t t = threadIdx.x; t < T; t += 256) q_tail[t] += (int64_t)freed[t];
+}
+
+__global__ __launch_bounds__(256) void k_evict_reinsert(Slot* __restrict__ slots, int64_t cap,
+                                                        const Slot* __restrict__ surv,
+                                                        const uint32_t* __restrict__ nsurv) {
+  const int32_t t = blockIdx.y;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)nsurv[t]) return;
+  const Slot sl = surv[(size_t)t * (size_t)cap + i];
+  Slot* st = slots + (size_t)t * (size_t)cap;
+  const uint64_t mask = (uint64_t)cap - 1u;
+  uint64_t s = slot_mix(sl.key) & mask;
+  for (int64_t probe = 0; probe < cap; ++probe, s = (s + 1) & mask) {
+    const uint64_t old = atomicCAS((unsigned long long*)&st[s].key,
+                                   (unsigned long long)kEmptyKey, (unsigned long long)sl.key);
+    if (old == kEmptyKey) {
+      st[s].row = sl.row;
+      return;
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_hash_find_or_insert(const Handle& h, const Plan& p, const int64_t* offsets,
@@ -449,19 +653,91 @@ hipError_t launch_hash_find_or_insert(const Handle& h, const Plan& p, const int6
   hipLaunchKernelGGL(k_hash_first, dim3(grid), dim3(256), shm, s, tbw, p.B, h.T, nnz, slots,
                      h.capacity, slot_of, bcnt, tpart, counts, adm.min_count);
   hipLaunchKernelGGL(k_hash_plan, dim3(1), dim3(1024), 0, s, bcnt, nb, tbw, h.T, nnz, tpart,
-                     h.sv.n_live, h.sv.rows, misc, h.sv.flags);
+                     h.sv.n_live, h.sv.rows, h.sv.q_head, h.sv.q_tail, misc, h.sv.flags);
   hipLaunchKernelGGL(k_hash_assign, dim3(grid), dim3(256), shm, s, tbw, p.B, h.T, nnz, slots,
                      h.capacity, slot_of, bcnt, h.sv.n_live, misc, newlist, counts,
-                     adm.min_count);
+                     adm.min_count, h.free_rows, h.sv.row_off, h.sv.rows, h.sv.q_head,
+                     h.sv.q_tail);
   // new rows: at most one per occurrence; enough blocks for a cold start
   int64_t igrid = (nnz * (h.D / 4) + 255) / 256;
   igrid = igrid < 1 ? 1 : (igrid > 2048 ? 2048 : igrid);
   hipLaunchKernelGGL(k_hash_finish, dim3(grid + (unsigned)igrid), dim3(256), shm, s, tbw,
                      keys, p.B, h.T, nnz, slots, h.capacity, slot_of, ids_out, newlist, misc,
-                     h.sv.n_live, counts, adm.min_count, h.sv.row_off, h.sv.rows, h.W, h.G, h.D, h.seed, h.stdv,
+                     h.sv.n_live, h.sv.q_head, h.sv.q_tail, counts, adm.min_count,
+                     h.sv.row_off, h.sv.rows, h.W, h.G, h.D, h.seed, h.stdv,
                      h.accum0, grid);
   phase_mark(h, EMB_PHASE_HASH, true, s);
   return hipGetLastError();
+}
+
+// Workspace of emb_hash_evict: row flags, block counts, per-table ranks and
+// freed counts, survivor counts and survivor lists.
+struct EvictPlan {
+  size_t flag = 0, bcnt = 0, tbase = 0, freed = 0, nsurv = 0, surv = 0, total = 0;
+  int64_t nblocks = 0;
+};
+static EvictPlan evict_plan(const Handle& h) {
+  auto up = [](size_t b) { return (b + 255) & ~(size_t)255; };
+  EvictPlan p;
+  p.nblocks = (h.total_rows + kEvictSpan - 1) / kEvictSpan;
+  size_t o = 0;
+  p.flag = o;
+  o += up((size_t)p.nblocks * kEvictSpan);  // whole blocks: 16-byte reads stay inside
+  p.bcnt = o;
+  o += up(sizeof(uint32_t) * (size_t)(p.nblocks + 1));
+  p.tbase = o;
+  o += up(sizeof(uint32_t) * (size_t)h.T);
+  p.freed = o;
+  o += up(sizeof(uint32_t) * (size_t)h.T);
+  p.nsurv = o;
+  o += up(sizeof(uint32_t) * (size_t)h.T);
+  p.surv = o;
+  o += up(sizeof(Slot) * (size_t)h.T * (size_t)h.capacity);
+  p.total = o;
+  return p;
+}
+
+size_t hash_evict_workspace_bytes(const Handle& h) {
+  return h.hashed ? evict_plan(h).total : 0;
+}
+
+hipError_t launch_hash_evict(const Handle& h, const uint32_t* last_used, uint32_t before,
+                             uint32_t* key_counts, char* ws, hipStream_t s) {
+  const EvictPlan p = evict_plan(h);
+  uint8_t* flag = reinterpret_cast<uint8_t*>(ws + p.flag);
+  uint32_t* bcnt = reinterpret_cast<uint32_t*>(ws + p.bcnt);
+  uint32_t* tbase = reinterpret_cast<uint32_t*>(ws + p.tbase);
+  uint32_t* freed = reinterpret_cast<uint32_t*>(ws + p.freed);
+  uint32_t* nsurv = reinterpret_cast<uint32_t*>(ws + p.nsurv);
+  Slot* surv = reinterpret_cast<Slot*>(ws + p.surv);
+  Slot* slots = static_cast<Slot*>(h.slots);
+  hipError_t e = launch_fill_u64(reinterpret_cast<uint64_t*>(flag), 0ull,
+                                 (size_t)p.nblocks * kEvictSpan / 8, s);
+  if (e == hipSuccess) e = launch_zero_words(nsurv, h.T, s);
+  if (e != hipSuccess) return e;
+  const dim3 sgrid((unsigned)((h.capacity + 255) / 256), (unsigned)h.T);
+  hipLaunchKernelGGL(k_evict_mark, sgrid, dim3(256), 0, s, slots, h.capacity, h.sv.row_off,
+                     last_used, before, flag, surv, nsurv);
+  hipLaunchKernelGGL(k_evict_count, dim3((unsigned)p.nblocks), dim3(256), 0, s, flag,
+                     h.total_rows, bcnt);
+  hipLaunchKernelGGL(k_evict_scan, dim3(1), dim3(1024), 0, s, bcnt, (uint32_t)p.nblocks);
+  hipLaunchKernelGGL(k_evict_tables, dim3((unsigned)((h.T + 255) / 256)), dim3(256), 0, s, flag,
+                     bcnt, h.sv.row_off, h.T, tbase, freed);
+  hipLaunchKernelGGL(k_evict_scatter, dim3((unsigned)p.nblocks), dim3(256), 0, s, flag,
+                     h.total_rows, bcnt, h.sv.row_off, h.sv.rows, h.T, tbase, h.sv.q_tail,
+                     h.free_rows);
+  hipLaunchKernelGGL(k_evict_finish, dim3(1), dim3(256), 0, s, freed, h.T, h.sv.q_tail);
+  e = hipGetLastError();
+  if (e == hipSuccess)
+    e = launch_fill_u64(reinterpret_cast<uint64_t*>(slots), kEmptyKey,
+                        2 * (size_t)h.T * (size_t)h.capacity, s);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_evict_reinsert, sgrid, dim3(256), 0, s, slots, h.capacity, surv, nsurv);
+  e = hipGetLastError();
+  if (e == hipSuccess && key_counts)  // every counted key was dropped with its slot
+    e = launch_fill_u64(reinterpret_cast<uint64_t*>(key_counts), 0ull,
+                        (size_t)h.T * (size_t)h.capacity / 2, s);
+  return e;
 }
 
 hipError_t launch_hash_export(const Handle& h, int t, uint64_t* key_of_row, hipStream_t s) {

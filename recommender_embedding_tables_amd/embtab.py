@@ -48,6 +48,7 @@ EXPORTED = [
     "emb_bag_backward_adagrad_prepared", "emb_bag_forward_prepared", "emb_cache_state_bytes",
     "emb_table_create_tiered", "emb_cache_flush", "emb_cache_stats",
     "emb_bag_backward_adagrad_decay_prepared", "emb_hash_find_or_insert_admit",
+    "emb_hash_evict_workspace_bytes", "emb_hash_evict", "emb_hash_free_rows",
 ]
 
 EMB_PHASE_FORWARD, EMB_PHASE_KEYS, EMB_PHASE_SORT, EMB_PHASE_UNIQUE = 0, 1, 2, 3
@@ -75,6 +76,7 @@ class emb_table_desc_t(C.Structure):
         ("init_std", C.c_float),
         ("accum_init", C.c_float),
         ("init_storage", C.c_int32),
+        ("free_rows", C.c_void_p),
     ]
 
 
@@ -111,6 +113,9 @@ def _load():
         "emb_table_destroy": (i32, [P]),
         "emb_hash_find_or_insert": (i32, [P, P, P, i64, i64, P, P, sz, P]),
         "emb_hash_find_or_insert_admit": (i32, [P, P, P, i64, i64, P, C.c_uint32, P, P, sz, P]),
+        "emb_hash_evict_workspace_bytes": (sz, [P]),
+        "emb_hash_evict": (i32, [P, P, C.c_uint32, P, P, sz, P]),
+        "emb_hash_free_rows": (i32, [P, P, C.POINTER(i64)]),
         "emb_bag_forward": (i32, [P, P, P, i64, i64, i32, P, P, sz, P]),
         "emb_bag_backward_adagrad": (i32, [P, P, P, i64, i64, i32, P, f32, f32, P, sz, P]),
         "emb_status_sync": (i32, [P, P, C.POINTER(u32)]),
@@ -229,6 +234,22 @@ def emb_hash_find_or_insert_admit(handle, offsets, keys, batch, nnz, ids_out, mi
                                               _ptr(ws), ws_bytes, _stream(stream))
 
 
+def emb_hash_evict_workspace_bytes(handle) -> int:
+    return int(_lib.emb_hash_evict_workspace_bytes(handle))
+
+
+def emb_hash_evict(handle, row_last_used, before, key_counts, ws, ws_bytes, stream=None) -> int:
+    return _lib.emb_hash_evict(handle, _ptr(row_last_used), before, _ptr(key_counts), _ptr(ws),
+                               ws_bytes, _stream(stream))
+
+
+def emb_hash_free_rows(handle, num_tables, stream=None):
+    """Returns (status, [rows queued per table])."""
+    arr = (C.c_int64 * num_tables)()
+    st = _lib.emb_hash_free_rows(handle, _stream(stream), arr)
+    return st, list(arr)
+
+
 def emb_bag_forward(handle, offsets, ids, batch, nnz, pool, out, ws=None, ws_bytes=0,
                     stream=None) -> int:
     return _lib.emb_bag_forward(handle, _ptr(offsets), _ptr(ids), batch, nnz, pool, _ptr(out),
@@ -333,9 +354,13 @@ class EmbTables:
             self.state = torch.zeros(emb_state_bytes(self.T), dtype=torch.uint8, device=dev)
             hb = emb_hash_bytes(self.T, self.hash_capacity) if hashed else 0
             self.slots = torch.empty(max(hb, 16), dtype=torch.uint8, device=dev) if hashed else None
+            # free-row queue of emb_hash_evict: 4 bytes per row
+            self.free_rows = (torch.empty(self.total_rows, dtype=torch.int32, device=dev)
+                              if hashed else None)
             init = 1
         else:
-            self.weights, self.accum, self.state, self.slots = storage
+            self.weights, self.accum, self.state, self.slots = storage[:4]
+            self.free_rows = storage[4] if len(storage) > 4 else None
             init = 0
         self._rows_c = (C.c_int64 * self.T)(*self.rows)
         d = emb_table_desc_t()
@@ -349,6 +374,7 @@ class EmbTables:
         d.hash_capacity = self.hash_capacity
         d.max_load = max_load
         d.hash_slots = self.slots.data_ptr() if hashed else None
+        d.free_rows = self.free_rows.data_ptr() if self.free_rows is not None else None
         d.seed = seed
         d.init_lo = init_lo
         d.init_hi = init_hi

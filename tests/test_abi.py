@@ -215,3 +215,38 @@ def test_decay_backward_host_checks():
                                                           per, fake, ws, 0) == eb.EMB_OK
     finally:
         eb.emb_table_destroy(h)
+
+
+def test_evict_host_checks():
+    d, _keep = _desc(rows=[1000], dim=16)
+    st, h = eb.emb_table_create(d, 0)
+    assert st == eb.EMB_OK
+    try:  # a dense table has no keys to evict
+        assert eb.emb_hash_evict_workspace_bytes(h) == 0
+        assert eb.emb_hash_evict(h, 0x50000000, 3, None, 0x60000000, 1 << 30,
+                                 0) == eb.EMB_ERR_UNSUPPORTED
+    finally:
+        eb.emb_table_destroy(h)
+    for free_rows, expect in ((None, eb.EMB_ERR_UNSUPPORTED), (0x48000000, None)):
+        d, _keep = _desc(rows=[600, 100], dim=16, hashed=1, hash_capacity=1024,
+                         hash_slots=0x40000000, free_rows=free_rows)
+        st, h = eb.emb_table_create(d, 0)
+        assert st == eb.EMB_OK
+        try:
+            ws = eb.emb_hash_evict_workspace_bytes(h)
+            assert ws >= 2 * 1024 * 16 + 700 and ws % 256 == 0
+            call = lambda lu=0x50000000, kc=None, w=0x60000000, n=ws: eb.emb_hash_evict(
+                h, lu, 3, kc, w, n, 0)
+            if expect is not None:
+                assert call() == expect
+                continue
+            assert call(lu=None) == eb.EMB_ERR_INVALID_ARG
+            assert call(lu=0x50000002) == eb.EMB_ERR_INVALID_ARG
+            assert call(kc=0x58000001) == eb.EMB_ERR_INVALID_ARG
+            assert call(n=ws - 1) == eb.EMB_ERR_WORKSPACE
+            assert call(w=0x60000010) == eb.EMB_ERR_WORKSPACE
+        finally:
+            eb.emb_table_destroy(h)
+    d, _keep = _desc(rows=[600], dim=16, hashed=1, hash_capacity=1024, hash_slots=0x40000000,
+                     free_rows=0x48000002)  # misaligned queue
+    assert eb.emb_table_create(d, 0)[0] == eb.EMB_ERR_INVALID_ARG

@@ -1,0 +1,130 @@
+"""Eviction of hashed keys on the GPU against the oracle, through the C ABI:
+ids bit-exact across calls with evictions in between (freed rows handed out
+again, oldest first), the key<->row map, queue lengths, reused rows'
+initial values, admission counts dropped, and the whole lifecycle (admission,
+Adagrad Decay periods as the last-use record, eviction) over training steps."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as orc
+from recommender_embedding_tables_amd import synth
+from tests.helpers import abs_grad_sums, assert_within
+from tests.test_gpu_parity import _hash_call, _t, check_hash_state, make_pair, status
+from tests.test_gpu_admission import admit_call, counts_for
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+from recommender_embedding_tables_amd import embtab as eb  # noqa: E402
+
+DEV = torch.device("cuda")
+
+
+def evict(tabs, last_used, before, counts=None):
+    need = eb.emb_hash_evict_workspace_bytes(tabs.handle)
+    ws = torch.empty(need + 256, dtype=torch.uint8, device=DEV)
+    off = (-ws.data_ptr()) % 256
+    eb.check(eb.emb_hash_evict(tabs.handle, last_used, before, counts, ws[off:], need), "evict")
+    torch.cuda.synchronize()
+
+
+def global_rows(tabs, offsets, ids, B):
+    row_off = np.concatenate([[0], np.cumsum(tabs.rows)])
+    t = np.repeat(np.arange(tabs.T * B), np.diff(offsets)) // B
+    ok = ids >= 0
+    return (row_off[t] + ids)[ok]
+
+
+def test_eviction_matches_oracle_over_calls():
+    # tables small enough that rows run out without eviction
+    w = synth.workload(5, T=2, B=1200, universe=30_000, hash_capacity=1 << 14)
+    w.rows = np.array([5000, 7000], np.int64)
+    tabs, o = make_pair(w.rows, w.D, seed=31, hashed=True, cap=w.hash_capacity)
+    total = int(np.sum(w.rows))
+    last = np.zeros(total, np.uint32)
+    evicted = 0
+    for step in range(1, 10):
+        offsets, ranks = synth.gen_batch(w, step)
+        keys = synth.gen_keys(w, offsets, ranks)
+        ids = _hash_call(tabs, offsets, keys, w.B)
+        ref, fl = o.find_or_insert(offsets, keys, w.B)
+        np.testing.assert_array_equal(ids, ref)
+        last[global_rows(tabs, offsets, ids, w.B)] = step
+        if step % 2 == 0:  # keys not used in the last two calls leave
+            evict(tabs, _t(last), step - 1)
+            evicted += o.evict(last, step - 1)
+            st, queued = eb.emb_hash_free_rows(tabs.handle, tabs.T)
+            assert st == eb.EMB_OK and queued == [o.free_rows(t) for t in range(tabs.T)]
+            check_hash_state(tabs, o)
+        status(tabs)  # clears a full call's flag
+    assert evicted > 0
+    st, n_live = eb.emb_hash_n_live(tabs.handle, tabs.T)
+    assert n_live == [o.n_live(t) for t in range(tabs.T)]
+    check_hash_state(tabs, o)
+
+
+def test_eviction_drops_counted_keys_and_keeps_admitting():
+    w = synth.workload(5, T=2, B=1000, universe=20_000, hash_capacity=1 << 14)
+    w.rows = np.full(2, 6000, np.int64)
+    tabs, o = make_pair(w.rows, w.D, seed=32, hashed=True, cap=w.hash_capacity)
+    counts = counts_for(tabs)
+    total = int(np.sum(w.rows))
+    last = np.zeros(total, np.uint32)
+    for step in range(1, 7):
+        offsets, ranks = synth.gen_batch(w, step)
+        keys = synth.gen_keys(w, offsets, ranks)
+        ids = admit_call(tabs, counts, offsets, keys, w.B, 2)
+        np.testing.assert_array_equal(ids, o.find_or_insert_admit(offsets, keys, w.B, 2)[0])
+        last[global_rows(tabs, offsets, ids, w.B)] = step
+        if step == 3:
+            evict(tabs, _t(last), 2, counts)
+            o.evict(last, 2)
+            assert int(counts.abs().sum()) == 0
+    assert status(tabs) == (eb.EMB_OK, 0)
+    check_hash_state(tabs, o)
+
+
+def test_lifecycle_admission_decay_eviction():
+    # admission on insert, Adagrad Decay with rho = 1 (plain Adagrad) whose
+    # row periods are each row's last training step, eviction by those periods
+    w = synth.workload(5, T=2, B=1500, universe=25_000, hash_capacity=1 << 15)
+    w.rows = np.full(2, 9000, np.int64)
+    tabs, o = make_pair(w.rows, w.D, seed=33, hashed=True, cap=w.hash_capacity)
+    counts = counts_for(tabs)
+    total = int(np.sum(w.rows))
+    periods = torch.zeros(total, dtype=torch.int32, device=DEV)
+    carried = np.zeros((total, w.D))
+    for step in range(1, 9):
+        offsets, ranks = synth.gen_batch(w, step)
+        keys = synth.gen_keys(w, offsets, ranks)
+        ids = admit_call(tabs, counts, offsets, keys, w.B, 2)
+        np.testing.assert_array_equal(ids, o.find_or_insert_admit(offsets, keys, w.B, 2)[0])
+        grad = synth.gen_grad(w, step)
+        ws, need = tabs.workspace(w.B, ids.size)
+        eb.check(eb.emb_bag_prepare(tabs.handle, _t(offsets), _t(ids), w.B, ids.size,
+                                    eb.EMB_POOL_SUM, ws, need), "prepare")
+        eb.check(eb.emb_bag_backward_adagrad_decay_prepared(
+            tabs.handle, w.B, ids.size, eb.EMB_POOL_SUM, _t(grad), w.lr, w.eps, 1.0, step,
+            periods, ws, need), "backward")
+        o.backward_adagrad_decay(offsets, ids, w.B, False, grad, w.lr, w.eps, 1.0, step)
+        rows_u, sums = abs_grad_sums(offsets, ids, w.B, o.rows, grad, False, w.D)
+        carried[rows_u] += w.lr * sums / (np.sqrt(o.read_rows(rows_u)[1]) + w.eps)
+        if step % 3 == 0:
+            o_last = o.read_periods(np.arange(total))
+            torch.cuda.synchronize()
+            np.testing.assert_array_equal(periods.cpu().numpy().view(np.uint32), o_last)
+            evict(tabs, periods, step - 1, counts)
+            o.evict(o_last, step - 1)  # (a reused row keeps its old bound: looser, still valid)
+        assert status(tabs) == (eb.EMB_OK, 0)
+    st, n_live = eb.emb_hash_n_live(tabs.handle, tabs.T)
+    keys_live = []
+    for t in range(tabs.T):
+        k, r = o.export(t)
+        keys_live.append(r + int(np.sum(w.rows[:t])))
+    live = np.concatenate(keys_live)
+    Wr, Gr = o.read_rows(live)
+    assert_within(tabs.weights[_t(live)].cpu().numpy(), Wr, np.abs(Wr) + carried[live], "weights")
+    assert_within(tabs.accum[_t(live)].cpu().numpy(), Gr, np.abs(Gr) * 8, "accumulators")

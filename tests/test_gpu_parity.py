@@ -364,7 +364,7 @@ def check_hash_state(tabs, o, trained_lr=0.0):
         assert n_live[t] == o.n_live(t)
         kor = _export(tabs, t)[:n_live[t]]
         keys, rows = o.export(t)
-        ref = np.empty(n_live[t], np.uint64)
+        ref = np.full(n_live[t], np.uint64(eb.EMB_EMPTY_KEY))  # rows freed by eviction: no key
         ref[rows] = keys
         np.testing.assert_array_equal(kor, ref)  # key <-> row bijection, bit-exact
     # rows handed out so far: initial values and later updates match the oracle
