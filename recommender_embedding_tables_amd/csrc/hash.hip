@@ -450,46 +450,48 @@ __global__ __launch_bounds__(256) void k_hash_export(const Slot* __restrict__ st
 // leave their table and their rows join the table's free-row queue, in
 // ascending order; the slot arrays are rebuilt from the other live keys, so
 // probe sequences stay short and counted keys without a row are dropped.
-//   k_evict_mark     per slot: flag the rows of evicted keys; copy the other
-//                    live keys to the table's survivor list
+//   (slot arrays copied to the workspace, then filled empty)
+//   k_evict_rebuild  per slot of the copy: flag the row of an evicted key, or
+//                    insert the live key again (lock-free, as the probe does)
 //   k_evict_count    flagged rows per block of kEvictSpan rows
 //   k_evict_scan     one block: exclusive scan of the block counts
-//   k_evict_tables   per table: its first flagged row's global rank, and
-//                    how many of its rows are freed
+//   k_evict_tables   per table boundary: the flags before it (global rank)
 //   k_evict_scatter  a flagged row of table t with rank i (among t's flagged
 //                    rows) goes to queue entry q_tail[t] + i
 //   k_evict_finish   queue tails
-//   (slots filled empty)
-//   k_evict_reinsert survivors back into the empty slot arrays
 constexpr int64_t kEvictSpan = 4096;  // rows per counting block: 256 threads x 16
 
-__global__ __launch_bounds__(256) void k_evict_mark(const Slot* __restrict__ slots, int64_t cap,
-                                                    const int64_t* __restrict__ row_off,
-                                                    const uint32_t* __restrict__ last_used,
-                                                    uint32_t before, uint8_t* __restrict__ flag,
-                                                    Slot* __restrict__ surv,
-                                                    uint32_t* __restrict__ nsurv) {
+// Slot (t, s) of the copy of the slot arrays: a live key whose row was last
+// used before `before` flags its row; every other live key goes back into the
+// (emptied) slot array of its table.  Counted keys without a row are dropped.
+__global__ __launch_bounds__(256) void k_evict_rebuild(const Slot* __restrict__ old,
+                                                       Slot* __restrict__ slots, int64_t cap,
+                                                       const int64_t* __restrict__ row_off,
+                                                       const uint32_t* __restrict__ last_used,
+                                                       uint32_t before,
+                                                       uint8_t* __restrict__ flag) {
   const int32_t t = blockIdx.y;
-  const int64_t s = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  bool keep = false;
-  Slot sl{kEmptyKey, kUnsetRow};
-  if (s < cap) {
-    sl = slots[(size_t)t * (size_t)cap + s];
-    const int64_t nrows = row_off[t + 1] - row_off[t];
-    if (sl.key != kEmptyKey && sl.row < (uint64_t)nrows) {
-      const int64_t g = row_off[t] + (int64_t)sl.row;
-      if (last_used[g] < before) flag[g] = 1u;
-      else keep = true;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= cap) return;
+  const Slot sl = old[(size_t)t * (size_t)cap + i];
+  const int64_t nrows = row_off[t + 1] - row_off[t];
+  if (sl.key == kEmptyKey || sl.row >= (uint64_t)nrows) return;
+  const int64_t g = row_off[t] + (int64_t)sl.row;
+  if (last_used[g] < before) {
+    flag[g] = 1u;
+    return;
+  }
+  Slot* st = slots + (size_t)t * (size_t)cap;
+  const uint64_t mask = (uint64_t)cap - 1u;
+  uint64_t s = slot_mix(sl.key) & mask;
+  for (int64_t probe = 0; probe < cap; ++probe, s = (s + 1) & mask) {
+    const uint64_t prev = atomicCAS((unsigned long long*)&st[s].key,
+                                    (unsigned long long)kEmptyKey, (unsigned long long)sl.key);
+    if (prev == kEmptyKey) {
+      st[s].row = sl.row;
+      return;
     }
   }
-  const uint64_t m = __ballot(keep);
-  if (m == 0) return;
-  const uint32_t lane = threadIdx.x & 63u;
-  const uint32_t leader = (uint32_t)__ffsll((unsigned long long)m) - 1u;
-  uint32_t at = 0;
-  if (lane == leader) at = atomicAdd(&nsurv[t], (uint32_t)__popcll(m));
-  at = (uint32_t)__shfl((int)at, (int)leader, 64);
-  if (keep) surv[(size_t)t * (size_t)cap + at + lanes_below(m)] = sl;
 }
 
 // Flags of rows [16 i, 16 i + 16) of this block's span, as a count.
@@ -547,26 +549,26 @@ __global__ __launch_bounds__(1024) void k_evict_scan(uint32_t* __restrict__ bcnt
   if (threadIdx.x == 0) bcnt[n] = total;
 }
 
-// Global rank (flags before it) of row r: block base plus the flags of its
-// block before r.
-__device__ inline uint32_t flag_rank(const uint8_t* flag, const uint32_t* bbase, int64_t r) {
-  const int64_t b = r / kEvictSpan;
-  uint32_t c = bbase[b];
-  for (int64_t q = b * kEvictSpan; q < r; ++q) c += flag[q];
-  return c;
-}
-
+// Block t (0 <= t <= T): the global rank of row row_off[t], i.e. the flags
+// before it: its counting block's base plus the flags of that block before
+// it, counted by the whole block (16 rows per thread).
 __global__ __launch_bounds__(256) void k_evict_tables(const uint8_t* __restrict__ flag,
+                                                      int64_t total,
                                                       const uint32_t* __restrict__ bbase,
                                                       const int64_t* __restrict__ row_off,
-                                                      int32_t T, uint32_t* __restrict__ tbase,
-                                                      uint32_t* __restrict__ freed) {
-  for (int32_t t = blockIdx.x * 256 + threadIdx.x; t < T; t += gridDim.x * 256) {
-    const uint32_t p0 = flag_rank(flag, bbase, row_off[t]);
-    const uint32_t p1 = flag_rank(flag, bbase, row_off[t + 1]);
-    tbase[t] = p0;
-    freed[t] = p1 - p0;
-  }
+                                                      uint32_t* __restrict__ tbase) {
+  __shared__ uint32_t wsum[4];
+  const int64_t r = row_off[blockIdx.x];
+  const int64_t b = r / kEvictSpan;
+  const int64_t lo = b * kEvictSpan + 16 * (int64_t)threadIdx.x;
+  uint32_t c = 0;
+  if (lo + 16 <= r) c = count16(flag, lo, total);
+  else
+    for (int64_t q = lo; q < r; ++q) c += flag[q];
+  for (int o = 32; o > 0; o >>= 1) c += (uint32_t)__shfl_down((int)c, o, 64);
+  if ((threadIdx.x & 63u) == 0) wsum[threadIdx.x >> 6] = c;
+  __syncthreads();
+  if (threadIdx.x == 0) tbase[blockIdx.x] = bbase[b] + wsum[0] + wsum[1] + wsum[2] + wsum[3];
 }
 
 __global__ __launch_bounds__(256) void k_evict_scatter(
@@ -603,29 +605,9 @@ __global__ __launch_bounds__(256) void k_evict_scatter(
   }
 }
 
-__global__ __launch_bounds__(256) void k_evict_finish(const uint32_t* __restrict__ freed,
+__global__ __launch_bounds__(256) void k_evict_finish(const uint32_t* __restrict__ tbase,
                                                       int32_t T, int64_t* __restrict__ q_tail) {
-  for (int32_t t = threadIdx.x; t < T; t += 256) q_tail[t] += (int64_t)freed[t];
-}
-
-__global__ __launch_bounds__(256) void k_evict_reinsert(Slot* __restrict__ slots, int64_t cap,
-                                                        const Slot* __restrict__ surv,
-                                                        const uint32_t* __restrict__ nsurv) {
-  const int32_t t = blockIdx.y;
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= (int64_t)nsurv[t]) return;
-  const Slot sl = surv[(size_t)t * (size_t)cap + i];
-  Slot* st = slots + (size_t)t * (size_t)cap;
-  const uint64_t mask = (uint64_t)cap - 1u;
-  uint64_t s = slot_mix(sl.key) & mask;
-  for (int64_t probe = 0; probe < cap; ++probe, s = (s + 1) & mask) {
-    const uint64_t old = atomicCAS((unsigned long long*)&st[s].key,
-                                   (unsigned long long)kEmptyKey, (unsigned long long)sl.key);
-    if (old == kEmptyKey) {
-      st[s].row = sl.row;
-      return;
-    }
-  }
+  for (int32_t t = threadIdx.x; t < T; t += 256) q_tail[t] += (int64_t)(tbase[t + 1] - tbase[t]);
 }
 
 }  // namespace
@@ -670,10 +652,10 @@ hipError_t launch_hash_find_or_insert(const Handle& h, const Plan& p, const int6
   return hipGetLastError();
 }
 
-// Workspace of emb_hash_evict: row flags, block counts, per-table ranks and
-// freed counts, survivor counts and survivor lists.
+// Workspace of emb_hash_evict: row flags, block counts, per-table ranks, and
+// a copy of the slot arrays.
 struct EvictPlan {
-  size_t flag = 0, bcnt = 0, tbase = 0, freed = 0, nsurv = 0, surv = 0, total = 0;
+  size_t flag = 0, bcnt = 0, tbase = 0, copy = 0, total = 0;
   int64_t nblocks = 0;
 };
 static EvictPlan evict_plan(const Handle& h) {
@@ -686,12 +668,8 @@ static EvictPlan evict_plan(const Handle& h) {
   p.bcnt = o;
   o += up(sizeof(uint32_t) * (size_t)(p.nblocks + 1));
   p.tbase = o;
-  o += up(sizeof(uint32_t) * (size_t)h.T);
-  p.freed = o;
-  o += up(sizeof(uint32_t) * (size_t)h.T);
-  p.nsurv = o;
-  o += up(sizeof(uint32_t) * (size_t)h.T);
-  p.surv = o;
+  o += up(sizeof(uint32_t) * (size_t)(h.T + 1));
+  p.copy = o;
   o += up(sizeof(Slot) * (size_t)h.T * (size_t)h.capacity);
   p.total = o;
   return p;
@@ -707,36 +685,30 @@ hipError_t launch_hash_evict(const Handle& h, const uint32_t* last_used, uint32_
   uint8_t* flag = reinterpret_cast<uint8_t*>(ws + p.flag);
   uint32_t* bcnt = reinterpret_cast<uint32_t*>(ws + p.bcnt);
   uint32_t* tbase = reinterpret_cast<uint32_t*>(ws + p.tbase);
-  uint32_t* freed = reinterpret_cast<uint32_t*>(ws + p.freed);
-  uint32_t* nsurv = reinterpret_cast<uint32_t*>(ws + p.nsurv);
-  Slot* surv = reinterpret_cast<Slot*>(ws + p.surv);
+  Slot* copy = reinterpret_cast<Slot*>(ws + p.copy);
   Slot* slots = static_cast<Slot*>(h.slots);
+  const size_t nslots = (size_t)h.T * (size_t)h.capacity;
   hipError_t e = launch_fill_u64(reinterpret_cast<uint64_t*>(flag), 0ull,
                                  (size_t)p.nblocks * kEvictSpan / 8, s);
-  if (e == hipSuccess) e = launch_zero_words(nsurv, h.T, s);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(copy, slots, sizeof(Slot) * nslots, hipMemcpyDeviceToDevice, s);
+  if (e == hipSuccess) e = launch_fill_u64(reinterpret_cast<uint64_t*>(slots), kEmptyKey, 2 * nslots, s);
   if (e != hipSuccess) return e;
   const dim3 sgrid((unsigned)((h.capacity + 255) / 256), (unsigned)h.T);
-  hipLaunchKernelGGL(k_evict_mark, sgrid, dim3(256), 0, s, slots, h.capacity, h.sv.row_off,
-                     last_used, before, flag, surv, nsurv);
+  hipLaunchKernelGGL(k_evict_rebuild, sgrid, dim3(256), 0, s, copy, slots, h.capacity,
+                     h.sv.row_off, last_used, before, flag);
   hipLaunchKernelGGL(k_evict_count, dim3((unsigned)p.nblocks), dim3(256), 0, s, flag,
                      h.total_rows, bcnt);
   hipLaunchKernelGGL(k_evict_scan, dim3(1), dim3(1024), 0, s, bcnt, (uint32_t)p.nblocks);
-  hipLaunchKernelGGL(k_evict_tables, dim3((unsigned)((h.T + 255) / 256)), dim3(256), 0, s, flag,
-                     bcnt, h.sv.row_off, h.T, tbase, freed);
+  hipLaunchKernelGGL(k_evict_tables, dim3((unsigned)(h.T + 1)), dim3(256), 0, s, flag,
+                     h.total_rows, bcnt, h.sv.row_off, tbase);
   hipLaunchKernelGGL(k_evict_scatter, dim3((unsigned)p.nblocks), dim3(256), 0, s, flag,
                      h.total_rows, bcnt, h.sv.row_off, h.sv.rows, h.T, tbase, h.sv.q_tail,
                      h.free_rows);
-  hipLaunchKernelGGL(k_evict_finish, dim3(1), dim3(256), 0, s, freed, h.T, h.sv.q_tail);
-  e = hipGetLastError();
-  if (e == hipSuccess)
-    e = launch_fill_u64(reinterpret_cast<uint64_t*>(slots), kEmptyKey,
-                        2 * (size_t)h.T * (size_t)h.capacity, s);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_evict_reinsert, sgrid, dim3(256), 0, s, slots, h.capacity, surv, nsurv);
+  hipLaunchKernelGGL(k_evict_finish, dim3(1), dim3(256), 0, s, tbase, h.T, h.sv.q_tail);
   e = hipGetLastError();
   if (e == hipSuccess && key_counts)  // every counted key was dropped with its slot
-    e = launch_fill_u64(reinterpret_cast<uint64_t*>(key_counts), 0ull,
-                        (size_t)h.T * (size_t)h.capacity / 2, s);
+    e = launch_fill_u64(reinterpret_cast<uint64_t*>(key_counts), 0ull, nslots / 2, s);
   return e;
 }
 
