@@ -71,6 +71,11 @@
 //    bit.  A full call admits nothing (keys that would have been admitted get
 //    -1) but every count still advances.  min_count <= 1 is plain insertion.
 //
+// Adagrad Decay, admission and eviction are named by the DeepRec page but not
+// defined there: the oracle follows the readings above, which the tests pin
+// (worked cases, torch Adagrad at rho = 1, an eager discount model, counting
+// and free-queue models); against the pages themselves parity is unpinned.
+//
 // Return values of the orc_* calls that check data: a bit mask,
 //   1 = an id outside [0, rows of its table), other than -2 (contributes 0)
 //   2 = offsets not starting at 0, decreasing, or not ending at nnz
