@@ -27,6 +27,11 @@
 //  * Adagrad with a per-period discount of the accumulator, all samples of
 //    one period discounted alike:  DeepRec page, section "model quality",
 //    item "Adagrad Decay Optimizer".
+//  * The first consumer of the pooled embeddings fused with the lookup: the
+//    DLRM dot feature interaction (OneFlow OneEmbedding page, section
+//    "operator optimisation": a fused dot-interaction operator for DLRM;
+//    HugeCTR interview, section three, technique (5): pooling fused with the
+//    next layer to save memory traffic).
 //  * Feature admission (a key gets a row only once it is frequent enough):
 //    DeepRec page, section "model quality", EmbeddingVariable item 1
 //    (several admission methods; no formula is given).
@@ -70,6 +75,14 @@
 //    a mean bag's length) and the backward updates nothing, with no error
 //    bit.  A full call admits nothing (keys that would have been admitted get
 //    -1) but every count still advances.  min_count <= 1 is plain insertion.
+//
+//  * Dot interaction (the pages name the operator only; this is the DLRM
+//    model's definition, Naumov et al. 2019): per sample, z_0 = the dense
+//    feature vector [D], z_{t+1} = the pooled embedding of table t; the
+//    output is [z_0, z_i . z_j for i = 1..T, j = 0..i-1] (row-major order of
+//    the strict lower triangle), D + (T+1)T/2 values.  Its backward gives
+//    dz_i = sum_{j != i} g_ij z_j (g symmetric), the dense input's gradient
+//    (the copied z_0 slot plus dz_0) and the pooled embeddings' ([B, T, D]).
 //
 // Adagrad Decay, admission and eviction are named by the DeepRec page but not
 // defined there: the oracle follows the readings above, which the tests pin
@@ -425,6 +438,85 @@ int32_t orc_read_periods(void* h, const int64_t* grows, int64_t n, uint32_t* out
     if (grows[i] < 0 || grows[i] >= total) return -1;
     auto it = m->period_of.find(grows[i]);
     out[i] = it == m->period_of.end() ? 0u : it->second;
+  }
+  return 0;
+}
+
+// Pooled embedding of bag b = t*B + s in fp64 (sum or mean over its valid ids).
+static void pooled_fp64(Model* m, const int64_t* offsets, const int64_t* ids, int64_t B,
+                        int32_t pool_mean, int64_t t, int64_t s, double* z) {
+  const int64_t D = m->D, b = t * B + s;
+  std::vector<float> w(D), g(D);
+  for (int64_t d = 0; d < D; ++d) z[d] = 0.0;
+  const int64_t L = offsets[b + 1] - offsets[b];
+  for (int64_t j = offsets[b]; j < offsets[b + 1]; ++j) {
+    const int64_t id = ids[j];
+    if (id < 0 || id >= m->rows[t]) continue;
+    m->read(m->row_off[t] + id, w.data(), g.data());
+    for (int64_t d = 0; d < D; ++d) z[d] += (double)w[d];
+  }
+  if (pool_mean && L > 0)
+    for (int64_t d = 0; d < D; ++d) z[d] /= (double)L;
+}
+
+// The T + 1 vectors of sample s: z_0 = dense[s], z_{t+1} = pooled bag (t, s).
+static void interaction_vectors(Model* m, const int64_t* offsets, const int64_t* ids, int64_t B,
+                                int32_t pool_mean, const float* dense, int64_t s,
+                                std::vector<double>& Z) {
+  const int64_t T = m->T, D = m->D;
+  Z.assign((size_t)(T + 1) * D, 0.0);
+  for (int64_t d = 0; d < D; ++d) Z[d] = (double)dense[s * D + d];
+  for (int64_t t = 0; t < T; ++t) pooled_fp64(m, offsets, ids, B, pool_mean, t, s, &Z[(t + 1) * D]);
+}
+
+// out [B, D + (T+1)T/2]: z_0, then z_i . z_j for i = 1..T, j < i.
+int32_t orc_interact_forward(void* h, const int64_t* offsets, const int64_t* ids, int64_t B,
+                             int64_t nnz, int32_t pool_mean, const float* dense, float* out) {
+  Model* m = static_cast<Model*>(h);
+  const int64_t T = m->T, D = m->D, P = (T + 1) * T / 2;
+  if (!offsets_ok(offsets, T * B, nnz)) return 2;
+  std::vector<double> Z;
+  for (int64_t s = 0; s < B; ++s) {
+    interaction_vectors(m, offsets, ids, B, pool_mean, dense, s, Z);
+    float* o = out + s * (D + P);
+    for (int64_t d = 0; d < D; ++d) o[d] = (float)Z[d];
+    int64_t p = D;
+    for (int64_t i = 1; i <= T; ++i)
+      for (int64_t j = 0; j < i; ++j) {
+        double dot = 0.0;
+        for (int64_t d = 0; d < D; ++d) dot += Z[i * D + d] * Z[j * D + d];
+        o[p++] = (float)dot;
+      }
+  }
+  return 0;
+}
+
+// Backward of orc_interact_forward: grad_dense [B, D], grad_pooled [B, T, D].
+int32_t orc_interact_backward(void* h, const int64_t* offsets, const int64_t* ids, int64_t B,
+                              int64_t nnz, int32_t pool_mean, const float* dense,
+                              const float* grad_out, float* grad_dense, float* grad_pooled) {
+  Model* m = static_cast<Model*>(h);
+  const int64_t T = m->T, D = m->D, P = (T + 1) * T / 2;
+  if (!offsets_ok(offsets, T * B, nnz)) return 2;
+  std::vector<double> Z, G((size_t)(T + 1) * (T + 1)), dZ;
+  for (int64_t s = 0; s < B; ++s) {
+    interaction_vectors(m, offsets, ids, B, pool_mean, dense, s, Z);
+    const float* go = grad_out + s * (D + P);
+    std::fill(G.begin(), G.end(), 0.0);
+    int64_t p = D;
+    for (int64_t i = 1; i <= T; ++i)
+      for (int64_t j = 0; j < i; ++j, ++p) {
+        G[i * (T + 1) + j] = (double)go[p];
+        G[j * (T + 1) + i] = (double)go[p];
+      }
+    dZ.assign((size_t)(T + 1) * D, 0.0);
+    for (int64_t i = 0; i <= T; ++i)
+      for (int64_t j = 0; j <= T; ++j)
+        for (int64_t d = 0; d < D; ++d) dZ[i * D + d] += G[i * (T + 1) + j] * Z[j * D + d];
+    for (int64_t d = 0; d < D; ++d) grad_dense[s * D + d] = (float)((double)go[d] + dZ[d]);
+    for (int64_t t = 0; t < T; ++t)
+      for (int64_t d = 0; d < D; ++d)
+        grad_pooled[(s * T + t) * D + d] = (float)dZ[(t + 1) * D + d];
   }
   return 0;
 }

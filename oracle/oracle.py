@@ -46,6 +46,8 @@ def _load():
         "orc_backward_adagrad_decay": (i32, [P, P, P, i64, i64, i32, P, f32, f32, f32,
                                              C.c_uint32]),
         "orc_read_rows": (i32, [P, P, i64, P, P]),
+        "orc_interact_forward": (i32, [P, P, P, i64, i64, i32, P, P]),
+        "orc_interact_backward": (i32, [P, P, P, i64, i64, i32, P, P, P, P]),
         "orc_read_periods": (i32, [P, P, i64, P]),
         "orc_touched_count": (i64, [P]),
         "orc_touched_rows": (i64, [P, P]),
@@ -175,6 +177,27 @@ class Oracle:
         if _load().orc_read_periods(self._h, _p(grows), grows.size, _p(out)) != 0:
             raise IndexError("oracle: row out of range")
         return out
+
+    def interact_forward(self, offsets, ids, batch, pool_mean, dense):
+        """DLRM dot interaction over [dense, pooled embeddings]: [B, D + (T+1)T/2]."""
+        offsets, ids = _arr(offsets, np.int64), _arr(ids, np.int64)
+        dense = _arr(dense, np.float32)
+        P = (self.T + 1) * self.T // 2
+        out = np.zeros((batch, self.D + P), np.float32)
+        rc = _load().orc_interact_forward(self._h, _p(offsets), _p(ids), batch, ids.size,
+                                          int(bool(pool_mean)), _p(dense), _p(out))
+        return out, int(rc)
+
+    def interact_backward(self, offsets, ids, batch, pool_mean, dense, grad_out):
+        """Gradients of interact_forward: (grad_dense [B, D], grad_pooled [B, T, D])."""
+        offsets, ids = _arr(offsets, np.int64), _arr(ids, np.int64)
+        dense, grad_out = _arr(dense, np.float32), _arr(grad_out, np.float32)
+        gd = np.zeros((batch, self.D), np.float32)
+        gp = np.zeros((batch, self.T, self.D), np.float32)
+        rc = _load().orc_interact_backward(self._h, _p(offsets), _p(ids), batch, ids.size,
+                                           int(bool(pool_mean)), _p(dense), _p(grad_out),
+                                           _p(gd), _p(gp))
+        return gd, gp, int(rc)
 
     def read_rows(self, grows):
         grows = _arr(grows, np.int64)

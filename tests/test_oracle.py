@@ -8,6 +8,7 @@ Pins used (none re-types the oracle's own loops):
   * library routines: torch.nn.functional.embedding_bag, torch.unique,
     numpy's stable argsort, torch.optim.Adagrad on a dense table, torch autograd;
   * invariants (counts sum to nnz, untouched rows bit-identical, |dw| < lr, ...);
+  * dot interaction: torch (embedding_bag, bmm, tril_indices) and its autograd;
   * Adagrad Decay: rho = 1 against torch.optim.Adagrad, and the lazy per-row
     periods against an eager model that discounts every accumulator at every
     period boundary;
@@ -645,6 +646,60 @@ def test_absent_ids_contribute_nothing_without_error():
     assert sorted(o.touched_rows().tolist()) == np.nonzero(touched)[0].tolist()
     ids[0] = -3  # any other negative id is still an error
     assert o.forward(offsets, ids, B, False)[1] == orc.ERR_OUT_OF_RANGE
+
+
+# ------------------------------------------------------- dot interaction
+
+def test_worked_interaction():
+    o = orc.Oracle([2], 2, seed=0)
+    o.set_dense(np.array([[3, 4], [5, 6]], np.float32), np.ones((2, 2), np.float32))
+    off = np.array([0, 1], np.int64)
+    ids = np.array([0], np.int64)
+    dense = np.array([[1, 2]], np.float32)
+    out, rc = o.interact_forward(off, ids, 1, False, dense)
+    assert rc == 0 and out.tolist() == [[1, 2, 11]]  # z1 . z0 = 3 + 8
+    gd, gp, rc = o.interact_backward(off, ids, 1, False, dense, np.array([[0.5, -1, 2]], np.float32))
+    assert gd.tolist() == [[0.5 + 2 * 3, -1 + 2 * 4]] and gp.tolist() == [[[2 * 1, 2 * 2]]]
+
+
+def _torch_interaction(o, offsets, ids, B, rows, mean, dense):
+    """Pooled embeddings by torch's embedding_bag, then Z Z^T and its strict
+    lower triangle (fp64); returns (out, Z leaf tensors for autograd)."""
+    T, D = len(rows), o.D
+    row_off = np.concatenate([[0], np.cumsum(rows)])
+    W = torch.from_numpy(o.read_rows(np.arange(row_off[-1]))[0].astype(np.float64))
+    pooled = []
+    for t in range(T):
+        a, e = offsets[t * B], offsets[(t + 1) * B]
+        pooled.append(torch.nn.functional.embedding_bag(
+            torch.from_numpy(ids[a:e]), W[row_off[t]:row_off[t + 1]],
+            torch.from_numpy(offsets[t * B:(t + 1) * B] - a), mode="mean" if mean else "sum"))
+    pooled = torch.stack(pooled, dim=1).detach().requires_grad_(True)  # [B, T, D]
+    x = torch.from_numpy(dense.astype(np.float64)).requires_grad_(True)
+    Z = torch.cat([x[:, None, :], pooled], dim=1)                      # [B, T+1, D]
+    G = torch.bmm(Z, Z.transpose(1, 2).contiguous())
+    li, lj = torch.tril_indices(T + 1, T + 1, offset=-1)
+    return torch.cat([x, G[:, li, lj]], dim=1), x, pooled
+
+
+@pytest.mark.parametrize("mean", [False, True])
+def test_interaction_matches_torch_and_autograd(mean):
+    T, D, B = 4, 12, 25
+    rows = np.array([7, 30, 5, 16])
+    offsets, ids, _ = synth.random_small(11, T, D, B, rows, max_len=4, empty_frac=0.1)
+    o = orc.Oracle(rows, D, seed=4)
+    rng = np.random.default_rng(2)
+    dense = rng.standard_normal((B, D)).astype(np.float32)
+    out, rc = o.interact_forward(offsets, ids, B, mean, dense)
+    assert rc == 0 and out.shape == (B, D + (T + 1) * T // 2)
+    ref, x, pooled = _torch_interaction(o, offsets, ids, B, rows, mean, dense)
+    np.testing.assert_allclose(out, ref.detach().numpy().astype(np.float32), rtol=1e-6, atol=1e-7)
+    g = rng.standard_normal(out.shape).astype(np.float32)
+    ref.backward(torch.from_numpy(g.astype(np.float64)))
+    gd, gp, rc = o.interact_backward(offsets, ids, B, mean, dense, g)
+    assert rc == 0
+    np.testing.assert_allclose(gd, x.grad.numpy().astype(np.float32), rtol=1e-6, atol=1e-7)
+    np.testing.assert_allclose(gp, pooled.grad.numpy().astype(np.float32), rtol=1e-6, atol=1e-7)
 
 
 # ---------------------------------------------------------------- eviction
