@@ -153,6 +153,38 @@ emb_status_t emb_hash_find_or_insert(emb_table_t h, const int64_t* offsets,
                                      int64_t* ids_out, void* ws, size_t ws_bytes,
                                      void* stream);
 
+/* ------------------------------------------------------------------------
+ * The pooled embeddings' first consumer fused with the lookup: the DLRM dot
+ * feature interaction (OneFlow OneEmbedding page, section "operator
+ * optimisation": a fused dot-interaction operator for DLRM; HugeCTR
+ * interview, section three, technique (5): pooling fused with the next
+ * layer, so the pooled vectors do not go through device memory).  The pages
+ * name the operator only; this is the DLRM model's definition.  Per sample s,
+ * z_0 = dense[s, :] and z_{t+1} = the pooled bag (t, s) as emb_bag_forward
+ * computes it; the output row is
+ *   out[s] = [z_0 (D values), z_i . z_j for i = 1..T, j = 0..i-1]
+ * (the strict lower triangle of Z Z^T in row-major order), of length
+ * emb_interact_out_dim(h) = D + (T+1)T/2.  The [B, T, D] pooled tensor is not
+ * written.  Needs T + 1 <= 32, D % 16 == 0 and D <= 256 (EMB_ERR_UNSUPPORTED
+ * otherwise, and on tiered tables).  dense: [B, D] fp32, 16-byte aligned;
+ * out: [B, D + (T+1)T/2] fp32.  Ids as for emb_bag_forward (EMB_ID_ABSENT is
+ * a zero vector; out-of-range ids and bad offsets set the usual error bits).
+ * Dot products accumulate in fp32 on the matrix cores. */
+int64_t emb_interact_out_dim(emb_table_t h);
+emb_status_t emb_bag_forward_interact(emb_table_t h, const int64_t* offsets, const int64_t* ids,
+                                      int64_t batch, int64_t nnz, emb_pool_t pool,
+                                      const float* dense, float* out, void* stream);
+/* Backward of emb_bag_forward_interact for the same batch (the pooled vectors
+ * are gathered again): with g_ij = g_ji = grad_out[s, pair (i, j)] and
+ * g_ii = 0, dz_i = sum_j g_ij z_j;
+ *   grad_dense[s] = grad_out[s, 0:D] + dz_0          [B, D]
+ *   grad_pooled[s, t] = dz_{t+1}                      [B, T, D]
+ * grad_pooled is the grad_out of emb_bag_backward_adagrad(_prepared). */
+emb_status_t emb_interact_backward(emb_table_t h, const int64_t* offsets, const int64_t* ids,
+                                   int64_t batch, int64_t nnz, emb_pool_t pool,
+                                   const float* dense, const float* grad_out, float* grad_dense,
+                                   float* grad_pooled, void* stream);
+
 /* Eviction of hashed keys (DeepRec page, section "model quality",
  * EmbeddingVariable item 1: feature eviction policies; the page gives none).
  * The reading: every key whose row was last used before `before` leaves its

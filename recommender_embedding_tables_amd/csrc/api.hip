@@ -6,6 +6,7 @@
 #include <new>
 
 #include "embtab_internal.hpp"
+#include "interact.hpp"
 
 namespace embtab {
 
@@ -533,6 +534,48 @@ emb_status_t emb_hash_find_or_insert_admit(emb_table_t t, const int64_t* offsets
   adm.counts = key_counts;
   adm.min_count = min_count;
   return find_or_insert(t, offsets, keys, batch, nnz, ids_out, ws, ws_bytes, stream, adm);
+}
+
+int64_t emb_interact_out_dim(emb_table_t t) {
+  if (!t) return 0;
+  return (int64_t)t->h.D + (int64_t)(t->h.T + 1) * t->h.T / 2;
+}
+
+static emb_status_t interact_checks(emb_table_t t, const int64_t* offsets, const int64_t* ids,
+                                    int64_t batch, int64_t nnz, emb_pool_t pool,
+                                    const float* dense) {
+  if (!t || !dense || (nnz > 0 && !ids)) return EMB_ERR_INVALID_ARG;
+  if (pool != EMB_POOL_SUM && pool != EMB_POOL_MEAN) return EMB_ERR_INVALID_ARG;
+  if (!aligned16(dense)) return EMB_ERR_INVALID_ARG;
+  emb_status_t st = check_batch(t->h, offsets, batch, nnz);
+  if (st != EMB_OK) return st;
+  if (!interact_supported(t->h)) return EMB_ERR_UNSUPPORTED;
+  return EMB_OK;
+}
+
+emb_status_t emb_bag_forward_interact(emb_table_t t, const int64_t* offsets, const int64_t* ids,
+                                      int64_t batch, int64_t nnz, emb_pool_t pool,
+                                      const float* dense, float* out, void* stream) {
+  emb_status_t st = interact_checks(t, offsets, ids, batch, nnz, pool, dense);
+  if (st != EMB_OK) return st;
+  if (!out) return EMB_ERR_INVALID_ARG;
+  if (batch == 0) return EMB_OK;
+  return hip_status(launch_interact_forward(t->h, offsets, ids, batch, nnz,
+                                            pool == EMB_POOL_MEAN, dense, out,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+emb_status_t emb_interact_backward(emb_table_t t, const int64_t* offsets, const int64_t* ids,
+                                   int64_t batch, int64_t nnz, emb_pool_t pool,
+                                   const float* dense, const float* grad_out, float* grad_dense,
+                                   float* grad_pooled, void* stream) {
+  emb_status_t st = interact_checks(t, offsets, ids, batch, nnz, pool, dense);
+  if (st != EMB_OK) return st;
+  if (!grad_out || !grad_dense || !grad_pooled) return EMB_ERR_INVALID_ARG;
+  if (batch == 0) return EMB_OK;
+  return hip_status(launch_interact_backward(t->h, offsets, ids, batch, nnz,
+                                             pool == EMB_POOL_MEAN, dense, grad_out, grad_dense,
+                                             grad_pooled, static_cast<hipStream_t>(stream)));
 }
 
 size_t emb_hash_evict_workspace_bytes(emb_table_t t) {

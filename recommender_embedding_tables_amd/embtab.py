@@ -49,6 +49,7 @@ EXPORTED = [
     "emb_table_create_tiered", "emb_cache_flush", "emb_cache_stats",
     "emb_bag_backward_adagrad_decay_prepared", "emb_hash_find_or_insert_admit",
     "emb_hash_evict_workspace_bytes", "emb_hash_evict", "emb_hash_free_rows",
+    "emb_interact_out_dim", "emb_bag_forward_interact", "emb_interact_backward",
 ]
 
 EMB_PHASE_FORWARD, EMB_PHASE_KEYS, EMB_PHASE_SORT, EMB_PHASE_UNIQUE = 0, 1, 2, 3
@@ -114,6 +115,9 @@ def _load():
         "emb_hash_find_or_insert": (i32, [P, P, P, i64, i64, P, P, sz, P]),
         "emb_hash_find_or_insert_admit": (i32, [P, P, P, i64, i64, P, C.c_uint32, P, P, sz, P]),
         "emb_hash_evict_workspace_bytes": (sz, [P]),
+        "emb_interact_out_dim": (i64, [P]),
+        "emb_bag_forward_interact": (i32, [P, P, P, i64, i64, i32, P, P, P]),
+        "emb_interact_backward": (i32, [P, P, P, i64, i64, i32, P, P, P, P, P]),
         "emb_hash_evict": (i32, [P, P, C.c_uint32, P, P, sz, P]),
         "emb_hash_free_rows": (i32, [P, P, C.POINTER(i64)]),
         "emb_bag_forward": (i32, [P, P, P, i64, i64, i32, P, P, sz, P]),
@@ -232,6 +236,23 @@ def emb_hash_find_or_insert_admit(handle, offsets, keys, batch, nnz, ids_out, mi
     return _lib.emb_hash_find_or_insert_admit(handle, _ptr(offsets), _ptr(keys), batch, nnz,
                                               _ptr(ids_out), min_count, _ptr(key_counts),
                                               _ptr(ws), ws_bytes, _stream(stream))
+
+
+def emb_interact_out_dim(handle) -> int:
+    return int(_lib.emb_interact_out_dim(handle))
+
+
+def emb_bag_forward_interact(handle, offsets, ids, batch, nnz, pool, dense, out,
+                             stream=None) -> int:
+    return _lib.emb_bag_forward_interact(handle, _ptr(offsets), _ptr(ids), batch, nnz, pool,
+                                         _ptr(dense), _ptr(out), _stream(stream))
+
+
+def emb_interact_backward(handle, offsets, ids, batch, nnz, pool, dense, grad_out, grad_dense,
+                          grad_pooled, stream=None) -> int:
+    return _lib.emb_interact_backward(handle, _ptr(offsets), _ptr(ids), batch, nnz, pool,
+                                      _ptr(dense), _ptr(grad_out), _ptr(grad_dense),
+                                      _ptr(grad_pooled), _stream(stream))
 
 
 def emb_hash_evict_workspace_bytes(handle) -> int:

@@ -250,3 +250,34 @@ def test_evict_host_checks():
     d, _keep = _desc(rows=[600], dim=16, hashed=1, hash_capacity=1024, hash_slots=0x40000000,
                      free_rows=0x48000002)  # misaligned queue
     assert eb.emb_table_create(d, 0)[0] == eb.EMB_ERR_INVALID_ARG
+
+
+def test_interaction_host_checks():
+    d, _keep = _desc(rows=[100, 200, 50], dim=32)
+    st, h = eb.emb_table_create(d, 0)
+    assert st == eb.EMB_OK
+    try:
+        assert eb.emb_interact_out_dim(h) == 32 + 4 * 3 // 2
+        fake = 0x50000000
+        f = lambda dense=fake, pool=0, out=fake, batch=64: eb.emb_bag_forward_interact(
+            h, fake, fake, batch, 100, pool, dense, out, 0)
+        assert f(dense=None) == eb.EMB_ERR_INVALID_ARG
+        assert f(dense=fake + 4) == eb.EMB_ERR_INVALID_ARG  # 16-byte alignment
+        assert f(pool=5) == eb.EMB_ERR_INVALID_ARG
+        assert f(out=None) == eb.EMB_ERR_INVALID_ARG
+        assert f(batch=0) == eb.EMB_OK
+        assert eb.emb_interact_backward(h, fake, fake, 64, 100, 0, fake, None, fake, fake,
+                                        0) == eb.EMB_ERR_INVALID_ARG
+        assert eb.emb_interact_backward(h, fake, fake, 0, 0, 0, fake, fake, fake, fake,
+                                        0) == eb.EMB_OK
+    finally:
+        eb.emb_table_destroy(h)
+    for rows, dim in (([10] * 32, 16), ([10, 10], 20), ([10, 10], 272)):
+        d, _keep = _desc(rows=rows, dim=dim)
+        st, h = eb.emb_table_create(d, 0)
+        assert st == eb.EMB_OK
+        try:  # T + 1 > 32, D % 16 != 0, D > 256
+            assert eb.emb_bag_forward_interact(h, 0x50000000, 0x50000000, 4, 8, 0, 0x50000000,
+                                               0x50000000, 0) == eb.EMB_ERR_UNSUPPORTED
+        finally:
+            eb.emb_table_destroy(h)

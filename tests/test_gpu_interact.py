@@ -1,0 +1,156 @@
+"""The pooled lookup fused with the DLRM dot interaction, forward and
+backward, on the GPU against the oracle through the C ABI.  Cases cover one
+and two 16-row Gram blocks (T + 1 <= 16 and > 16), the largest shapes
+(T = 31, D = 256), mean pooling of multi-hot bags, empty bags, absent and
+out-of-range ids, and a training step whose embedding gradient comes from the
+interaction backward."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as orc
+from recommender_embedding_tables_amd import synth
+from tests.helpers import assert_within, forward_S
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+from recommender_embedding_tables_amd import embtab as eb  # noqa: E402
+
+DEV = torch.device("cuda")
+
+
+def _t(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def case(name):
+    if name == "one_hot_26":
+        return synth.workload(2, T=26, B=3000, D=128,
+                              rows=synth.log_uniform_rows(26, 2.0, 5.0, 3, 2)), False
+    if name == "multi_hot_mean_8":
+        w = synth.workload(3, T=8, B=2000, D=64)
+        w.rows = np.full(8, 30_000, np.int64)
+        return w, True
+    if name == "max_31x256":
+        return synth.workload(2, T=31, B=500, D=256, rows=np.full(31, 700)), False
+    w = synth.workload(3, T=5, B=700, D=16)  # ragged bags, some empty
+    w.rows = np.array([40, 900, 7, 300, 60], np.int64)
+    return w, False
+
+
+def batch_of(w, name):
+    if name == "small_ragged":  # bags of 0..6 ids, a fifth of them empty, some absent ids
+        offsets, ids, _ = synth.random_small(8, w.T, w.D, w.B, w.rows, max_len=6, empty_frac=0.2)
+        ids = ids.copy()
+        ids[::7] = eb.EMB_ID_ABSENT
+        return offsets, ids
+    return synth.gen_batch(w, 1)
+
+
+def z_abs(o, w, offsets, ids, dense, mean):
+    """|z| bound of every vector: |dense| and c_b * sum |W| ([B, T + 1, D])."""
+    pooled = forward_S(offsets, ids, w.B, o.rows, lambda g: o.read_rows(g)[0], mean, w.D)
+    return np.concatenate([np.abs(dense)[:, None, :], pooled], axis=1)
+
+
+@pytest.mark.parametrize("name", ["one_hot_26", "multi_hot_mean_8", "max_31x256",
+                                  "small_ragged"])
+def test_interaction_matches_oracle(name):
+    w, mean = case(name)
+    pool = eb.EMB_POOL_MEAN if mean else eb.EMB_POOL_SUM
+    tabs = eb.EmbTables(w.rows, w.D, seed=9)
+    o = orc.Oracle(w.rows, w.D, seed=9, init_lo=-0.05, init_hi=0.05, accum_init=0.1)
+    offsets, ids = batch_of(w, name)
+    rng = np.random.default_rng(4)
+    dense = rng.standard_normal((w.B, w.D)).astype(np.float32)
+    odim = eb.emb_interact_out_dim(tabs.handle)
+    P = (w.T + 1) * w.T // 2
+    assert odim == w.D + P
+    out = torch.empty((w.B, odim), dtype=torch.float32, device=DEV)
+    d_off, d_ids, d_dense = _t(offsets), _t(ids), _t(dense)
+    eb.check(eb.emb_bag_forward_interact(tabs.handle, d_off, d_ids, w.B, ids.size, pool, d_dense,
+                                         out), "forward_interact")
+    ref, rc = o.interact_forward(offsets, ids, w.B, mean, dense)
+    assert rc == 0
+    Z = z_abs(o, w, offsets, ids, dense, mean)
+    li, lj = np.tril_indices(w.T + 1, -1)
+    S = np.concatenate([np.abs(dense), np.einsum("bid,bjd->bij", Z, Z)[:, li, lj]], axis=1)
+    got = out.cpu().numpy()
+    np.testing.assert_array_equal(got[:, :w.D], dense)
+    assert_within(got, ref, S, "interaction")
+    # backward
+    g = rng.standard_normal((w.B, odim)).astype(np.float32)
+    gd = torch.empty((w.B, w.D), dtype=torch.float32, device=DEV)
+    gp = torch.empty((w.B, w.T, w.D), dtype=torch.float32, device=DEV)
+    eb.check(eb.emb_interact_backward(tabs.handle, d_off, d_ids, w.B, ids.size, pool, d_dense,
+                                      _t(g), gd, gp), "interact_backward")
+    rgd, rgp, rc = o.interact_backward(offsets, ids, w.B, mean, dense, g)
+    assert rc == 0
+    Gs = np.zeros((w.B, w.T + 1, w.T + 1))
+    Gs[:, li, lj] = np.abs(g[:, w.D:])
+    Gs[:, lj, li] = np.abs(g[:, w.D:])
+    SdZ = np.einsum("bij,bjd->bid", Gs, Z)
+    assert_within(gd.cpu().numpy(), rgd, np.abs(g[:, :w.D]) + SdZ[:, 0], "grad dense")
+    assert_within(gp.cpu().numpy(), rgp, SdZ[:, 1:], "grad pooled")
+    flags = eb.emb_status_sync(tabs.handle)
+    assert flags == (eb.EMB_OK, 0)
+    tabs.close()
+
+
+def test_out_of_range_ids_and_bad_offsets_are_flagged():
+    w, _ = case("small_ragged")
+    tabs = eb.EmbTables(w.rows, w.D, seed=9)
+    o = orc.Oracle(w.rows, w.D, seed=9, init_lo=-0.05, init_hi=0.05, accum_init=0.1)
+    offsets, ids = batch_of(w, "small_ragged")
+    ids = ids.copy()
+    ids[3] = 10 ** 6  # out of range: contributes 0 and flags
+    dense = np.ones((w.B, w.D), np.float32)
+    out = torch.empty((w.B, eb.emb_interact_out_dim(tabs.handle)), dtype=torch.float32,
+                      device=DEV)
+    eb.check(eb.emb_bag_forward_interact(tabs.handle, _t(offsets), _t(ids), w.B, ids.size,
+                                         eb.EMB_POOL_SUM, _t(dense), out), "forward_interact")
+    ref, _ = o.interact_forward(offsets, ids, w.B, False, dense)
+    np.testing.assert_allclose(out.cpu().numpy(), ref, rtol=1e-5, atol=1e-5)
+    assert eb.emb_status_sync(tabs.handle)[0] == eb.EMB_ERR_OUT_OF_RANGE
+    bad = offsets.copy()
+    bad[5] = bad[6] + 3  # decreasing: those bags count as empty, the call flags
+    eb.check(eb.emb_bag_forward_interact(tabs.handle, _t(bad), _t(ids), w.B, ids.size,
+                                         eb.EMB_POOL_SUM, _t(dense), out), "forward_interact")
+    assert eb.emb_status_sync(tabs.handle)[0] == eb.EMB_ERR_BAD_OFFSETS
+    tabs.close()
+
+
+def test_training_step_through_the_interaction():
+    # forward (fused), interaction backward, then the embedding backward with
+    # the pooled gradient: rows match the oracle's chain
+    w, _ = case("one_hot_26")
+    tabs = eb.EmbTables(w.rows, w.D, seed=10)
+    o = orc.Oracle(w.rows, w.D, seed=10, init_lo=-0.05, init_hi=0.05, accum_init=0.1)
+    offsets, ids = batch_of(w, "one_hot_26")
+    rng = np.random.default_rng(6)
+    dense = rng.standard_normal((w.B, w.D)).astype(np.float32)
+    g = (rng.standard_normal((w.B, eb.emb_interact_out_dim(tabs.handle))) * 0.1).astype(np.float32)
+    gd = torch.empty((w.B, w.D), dtype=torch.float32, device=DEV)
+    gp = torch.empty((w.B, w.T, w.D), dtype=torch.float32, device=DEV)
+    d_off, d_ids = _t(offsets), _t(ids)
+    eb.check(eb.emb_interact_backward(tabs.handle, d_off, d_ids, w.B, ids.size, eb.EMB_POOL_SUM,
+                                      _t(dense), _t(g), gd, gp), "interact_backward")
+    ws, need = tabs.workspace(w.B, ids.size)
+    eb.check(eb.emb_bag_backward_adagrad(tabs.handle, d_off, d_ids, w.B, ids.size,
+                                         eb.EMB_POOL_SUM, gp, w.lr, w.eps, ws, need), "backward")
+    # the oracle's chain, fed with the oracle's own pooled gradient
+    _, rgp, _ = o.interact_backward(offsets, ids, w.B, False, dense, g)
+    o.backward_adagrad(offsets, ids, w.B, False, rgp, w.lr, w.eps)
+    touched = o.touched_rows()
+    Wr, Gr = o.read_rows(touched)
+    Wg = tabs.weights[_t(touched)].cpu().numpy()
+    Gg = tabs.accum[_t(touched)].cpu().numpy()
+    # the pooled gradient's own error enters the step: a relative 1e-5 of it
+    # moves G by 2e-5 |G - G0| and w by about 1e-5 lr
+    assert_within(Gg, Gr, 3 * np.abs(Gr), "accumulator")
+    assert_within(Wg, Wr, np.abs(Wr) + 3 * w.lr, "weights")
+    assert eb.emb_status_sync(tabs.handle) == (eb.EMB_OK, 0)
+    tabs.close()
