@@ -68,88 +68,146 @@ __device__ inline void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Rows 0..T of Z for sample s: the dense input and the pooled bags.  Lane t
-// (t < T) owns bag (t, s); per position j of the bags, lane t resolves its
-// occurrence's row into LDS and every lane adds the rows of its NQ items
-// (table, float4 column).  All of a sample's row loads of one position are in
-// flight together.  Bags with offsets outside [0, nnz] or decreasing count as
-// empty and flag.
-template <bool MEAN, int NQ>
-__device__ void gather_z(const WaveLds& l, int64_t s, const float* __restrict__ dense,
-                         const int64_t* __restrict__ offsets, const int64_t* __restrict__ ids,
-                         const int64_t* __restrict__ row_off, const int64_t* __restrict__ rows,
-                         const float* __restrict__ W, int64_t B, int32_t T, int32_t D,
-                         int64_t nnz, uint32_t& bad) {
+// The samples of one wave, software-pipelined so that no global load latency
+// is exposed once per sample: while sample s's rows are in flight, the
+// previous sample's Z (still in LDS) is consumed (matrix-core products and
+// outputs), and the next sample's bag bounds and first ids are fetched.
+//   Lane t < T owns bag (t, s): its bounds, and the row of its occurrence at
+//   the current position, which it publishes in LDS; every lane then loads
+//   its NQ items (table, float4 column) of that row.  Position 0 of the next
+//   sample is resolved during this one; later positions of multi-hot bags are
+//   walked in place.  Bags whose offsets lie outside [0, nnz] or decrease
+//   count as empty and flag.  consume(sp) reads Z rows 0..T of sample sp;
+//   issue(s) may start the consumer's own loads for sample s (it is consumed
+//   one iteration later), and rotate() moves them to the consumer's side.
+template <bool MEAN, int NQ, class Issue, class Consume, class Rotate>
+__device__ void pipelined_samples(const WaveLds& l, int64_t first, int64_t stride,
+                                  const float* __restrict__ dense,
+                                  const int64_t* __restrict__ offsets,
+                                  const int64_t* __restrict__ ids,
+                                  const int64_t* __restrict__ row_off,
+                                  const int64_t* __restrict__ rows,
+                                  const float* __restrict__ W, int64_t B, int32_t T, int32_t D,
+                                  int64_t nnz, uint32_t& bad, Issue issue, Consume consume,
+                                  Rotate rotate) {
   const int lane = threadIdx.x & 63;
   const int D4 = D >> 2;
   const int zs = z_stride(D);
-  int64_t o0 = 0, o1 = 0;
-  if (lane < T) {
-    const int64_t b = (int64_t)lane * B + s;
-    o0 = offsets[b];
-    o1 = offsets[b + 1];
-    if (o0 < 0 || o1 < o0 || o1 > nnz) {
-      bad |= EMB_FLAG_BAD_OFFSETS;
-      o0 = o1 = 0;
-    }
-  }
-  const int64_t len = o1 - o0;
   const int64_t nrows = lane < T ? rows[lane] : 0, roff = lane < T ? row_off[lane] : 0;
-  int64_t maxlen = len;
-  for (int o = 32; o > 0; o >>= 1) {
-    const int64_t y = __shfl_xor(maxlen, o, 64);
-    maxlen = y > maxlen ? y : maxlen;
-  }
-  for (int c = lane; c < D4; c += 64)
-    *reinterpret_cast<f4v*>(l.z + 4 * c) =
-        *reinterpret_cast<const f4v*>(dense + (size_t)s * D + 4 * c);
-  int tt[NQ], cc[NQ];
+  // item q of this lane: table (tc >> 8) and float4 column (tc & 255); -1: none
+  int tc[NQ];
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
     const int it = q * 64 + lane;
-    tt[q] = it < T * D4 ? it / D4 : -1;
-    cc[q] = tt[q] >= 0 ? it - tt[q] * D4 : 0;
+    const int t = it / D4;
+    tc[q] = it < T * D4 ? (t << 8) | (it - t * D4) : -1;
   }
-  f4v acc[NQ];
-#pragma unroll
-  for (int q = 0; q < NQ; ++q) acc[q] = f4v{0.f, 0.f, 0.f, 0.f};
-  for (int64_t j = 0; j < maxlen; ++j) {
-    if (lane < T) {
-      uint32_t r = kNoRow;
-      if (j < len) {
-        const int64_t id = ids[o0 + j];
-        if (id >= 0 && id < nrows) r = (uint32_t)(roff + id);
-        else if (id != kAbsentId) bad |= EMB_FLAG_OUT_OF_RANGE;
+  auto bag_of = [&](int64_t s, int64_t& o0, int64_t& len) {
+    o0 = 0;
+    len = 0;
+    if (lane < T && s < B) {
+      const int64_t b = (int64_t)lane * B + s;
+      int64_t a = offsets[b], e = offsets[b + 1];
+      if (a < 0 || e < a || e > nnz) {
+        bad |= EMB_FLAG_BAD_OFFSETS;
+        a = e = 0;
       }
-      l.row[lane] = r;
+      o0 = a;
+      len = e - a;
     }
+  };
+  auto resolve = [&](int64_t o0, int64_t len, int64_t j) -> uint32_t {
+    uint32_t r = kNoRow;
+    if (lane < T && j < len) {
+      const int64_t id = ids[o0 + j];
+      if (id >= 0 && id < nrows) r = (uint32_t)(roff + id);
+      else if (id != kAbsentId) bad |= EMB_FLAG_OUT_OF_RANGE;
+    }
+    return r;
+  };
+  auto wave_max = [](int64_t v) {
+    for (int o = 32; o > 0; o >>= 1) {
+      const int64_t y = __shfl_xor(v, o, 64);
+      v = y > v ? y : v;
+    }
+    return v;
+  };
+  auto load_item = [&](int q) -> f4v {
+    const uint32_t r = tc[q] >= 0 ? l.row[tc[q] >> 8] : kNoRow;
+    const bool ok = r != kNoRow;
+    const f4v v =
+        *reinterpret_cast<const f4v*>(W + (ok ? (size_t)r * D + 4 * (tc[q] & 255) : 0));
+    return ok ? v : f4v{0.f, 0.f, 0.f, 0.f};
+  };
+
+  int64_t s = first;
+  int64_t o0, len;
+  bag_of(s, o0, len);
+  int64_t maxlen = wave_max(len);
+  if (lane < T) l.row[lane] = resolve(o0, len, 0);
+  wave_sync();
+  int64_t sp = -1;
+  while (s < B) {
+    const int64_t sn = s + stride;
+    int64_t o0n, lenn;
+    bag_of(sn, o0n, lenn);  // in flight during this sample
+    f4v dv[(256 / 4 + 63) / 64];
+#pragma unroll
+    for (int q = 0; q < (256 / 4 + 63) / 64; ++q) {
+      const int c = lane + 64 * q;
+      dv[q] = c < D4 ? *reinterpret_cast<const f4v*>(dense + (size_t)s * D + 4 * c)
+                     : f4v{0.f, 0.f, 0.f, 0.f};
+    }
+    f4v acc[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) acc[q] = load_item(q);  // position 0 of sample s
+    issue(s);
+    if (sp >= 0) consume(sp);  // the previous sample, from LDS
     wave_sync();
-    f4v x[NQ];
+    for (int64_t j = 1; j < maxlen; ++j) {  // later positions of multi-hot bags
+      if (lane < T) l.row[lane] = resolve(o0, len, j);
+      wave_sync();
+#pragma unroll
+      for (int q0 = 0; q0 < NQ; q0 += 4) {  // four loads in flight: few registers
+        f4v x[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) x[q] = load_item(q0 + q);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[q0 + q] += x[q];
+      }
+      wave_sync();
+    }
+    // Z of sample s: the dense row and the pooled bags
+#pragma unroll
+    for (int q = 0; q < (256 / 4 + 63) / 64; ++q) {
+      const int c = lane + 64 * q;
+      if (c < D4) *reinterpret_cast<f4v*>(l.z + 4 * c) = dv[q];
+    }
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
-      const uint32_t r = tt[q] >= 0 ? l.row[tt[q]] : kNoRow;
-      const bool ok = r != kNoRow;
-      const f4v v = *reinterpret_cast<const f4v*>(W + (ok ? (size_t)r * D + 4 * cc[q] : 0));
-      x[q] = ok ? v : f4v{0.f, 0.f, 0.f, 0.f};
+      const int t = tc[q] >= 0 ? tc[q] >> 8 : 0;
+      const int64_t lq = __shfl(len, t, 64);
+      if (tc[q] < 0) continue;
+      f4v v = acc[q];
+      if (MEAN && lq > 0) v *= 1.0f / (float)lq;
+      *reinterpret_cast<f4v*>(l.z + (size_t)(t + 1) * zs + 4 * (tc[q] & 255)) = v;
     }
-#pragma unroll
-    for (int q = 0; q < NQ; ++q) acc[q] += x[q];
-    wave_sync();  // l.row is rewritten by the next position
+    // position 0 of the next sample
+    if (lane < T) l.row[lane] = resolve(o0n, lenn, 0);
+    maxlen = wave_max(lenn);
+    o0 = o0n;
+    len = lenn;
+    wave_sync();
+    rotate();
+    sp = s;
+    s = sn;
   }
-  // every lane learns its items' bag lengths from the lanes that own them
-#pragma unroll
-  for (int q = 0; q < NQ; ++q) {
-    const int64_t lq = __shfl(len, tt[q] >= 0 ? tt[q] : 0, 64);
-    if (tt[q] < 0) continue;
-    f4v v = acc[q];
-    if (MEAN && lq > 0) v *= 1.0f / (float)lq;
-    *reinterpret_cast<f4v*>(l.z + (size_t)(tt[q] + 1) * zs + 4 * cc[q]) = v;
-  }
+  if (sp >= 0) consume(sp);
   wave_sync();
 }
 
 template <bool MEAN, int NQ>
-__global__ __launch_bounds__(256) void k_interact_fwd(
+__global__ __launch_bounds__(256, 2) void k_interact_fwd(
     const float* __restrict__ dense, const int64_t* __restrict__ offsets,
     const int64_t* __restrict__ ids, const int64_t* __restrict__ row_off,
     const int64_t* __restrict__ rows, const float* __restrict__ W, int64_t B, int32_t T,
@@ -163,8 +221,7 @@ __global__ __launch_bounds__(256) void k_interact_fwd(
   const int64_t ostride = (int64_t)D + P;
   uint32_t bad = 0;
   const int ri = lane & 15, kq = lane >> 4;
-  for (int64_t s = (int64_t)blockIdx.x * wpb + w; s < B; s += (int64_t)gridDim.x * wpb) {
-    gather_z<MEAN, NQ>(l, s, dense, offsets, ids, row_off, rows, W, B, T, D, nnz, bad);
+  auto consume = [&](int64_t s) {
     // the copied dense slot (rows of D + P floats: not 16-byte aligned)
     for (int d = lane; d < D; d += 64) out[s * ostride + d] = l.z[d];
     // Gram blocks (0,0), (1,0), (1,1) of Z Z^T; rows past T are zero
@@ -196,8 +253,10 @@ __global__ __launch_bounds__(256) void k_interact_fwd(
     }
     wave_sync();
     for (int p = lane; p < P; p += 64) out[s * ostride + D + p] = l.pairs[p];
-    wave_sync();
-  }
+  };
+  pipelined_samples<MEAN, NQ>(l, (int64_t)blockIdx.x * wpb + w, (int64_t)gridDim.x * wpb, dense,
+                              offsets, ids, row_off, rows, W, B, T, D, nnz, bad,
+                              [](int64_t) {}, consume, []() {});
   const uint32_t any = (uint32_t)(__ballot(bad != 0) != 0);
   if (any) {
     uint32_t all = bad;
@@ -207,7 +266,7 @@ __global__ __launch_bounds__(256) void k_interact_fwd(
 }
 
 template <bool MEAN, int NQ>
-__global__ __launch_bounds__(256) void k_interact_bwd(
+__global__ __launch_bounds__(256, 2) void k_interact_bwd(
     const float* __restrict__ dense, const int64_t* __restrict__ offsets,
     const int64_t* __restrict__ ids, const int64_t* __restrict__ row_off,
     const int64_t* __restrict__ rows, const float* __restrict__ W, int64_t B, int32_t T,
@@ -222,8 +281,7 @@ __global__ __launch_bounds__(256) void k_interact_bwd(
   const int64_t gstride = (int64_t)D + P;
   uint32_t bad = 0;
   const int ri = lane & 15, kq = lane >> 4;
-  for (int64_t s = (int64_t)blockIdx.x * wpb + w; s < B; s += (int64_t)gridDim.x * wpb) {
-    gather_z<MEAN, NQ>(l, s, dense, offsets, ids, row_off, rows, W, B, T, D, nnz, bad);
+  auto consume = [&](int64_t s) {
     // symmetric pair-gradient matrix, zero diagonal and padding
     const float* go = grad_out + s * gstride;
     for (int e = lane; e < 32 * 32; e += 64) {
@@ -236,31 +294,36 @@ __global__ __launch_bounds__(256) void k_interact_bwd(
       l.g[i * 33 + j] = v;
     }
     wave_sync();
-    const int mblocks = T + 1 > 16 ? 2 : 1;
+    const bool two = T + 1 > 16;
     for (int n0 = 0; n0 < D; n0 += 16) {
-      for (int mb = 0; mb < mblocks; ++mb) {
-        f4v acc = {0.f, 0.f, 0.f, 0.f};
-        // A[i][k] = G[16 mb + i][k], B[k][n] = Z[k][n0 + n] (zero past row T)
-        for (int k0 = 0; k0 < 32; k0 += 4) {
-          const int k = k0 + kq;
-          const float a = l.g[(16 * mb + ri) * 33 + k];
-          const float b = k <= T ? l.z[(size_t)k * zs + n0 + ri] : 0.0f;
-          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
-        }
-        // lane holds dZ[16 mb + 4 (l / 16) + r][n0 + l % 16]
-        const int col = n0 + (lane & 15);
+      // both 16-row blocks of dZ for these 16 columns, side by side:
+      // A[i][k] = G[16 mb + i][k], B[k][n] = Z[k][n0 + n] (zero past row T)
+      f4v acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = 16 * mb + 4 * (lane >> 4) + r;
-          if (row == 0)
-            grad_dense[s * D + col] = go[col] + acc[r];
-          else if (row <= T)
-            grad_pooled[((size_t)s * T + (row - 1)) * D + col] = acc[r];
-        }
+      for (int k0 = 0; k0 < 32; k0 += 4) {
+        const int k = k0 + kq;
+        const float b = k <= T ? l.z[(size_t)k * zs + n0 + ri] : 0.0f;
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(l.g[ri * 33 + k], b, acc0, 0, 0, 0);
+        if (two)
+          acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(l.g[(16 + ri) * 33 + k], b, acc1, 0, 0, 0);
+      }
+      // lane holds dZ[16 mb + 4 (l / 16) + r][n0 + l % 16]
+      const int col = n0 + (lane & 15);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 4 * (lane >> 4) + r;
+        if (row == 0)
+          grad_dense[s * D + col] = go[col] + acc0[r];
+        else if (row <= T)
+          grad_pooled[((size_t)s * T + (row - 1)) * D + col] = acc0[r];
+        if (two && 16 + row <= T)
+          grad_pooled[((size_t)s * T + (15 + row)) * D + col] = acc1[r];
       }
     }
-    wave_sync();
-  }
+  };
+  pipelined_samples<MEAN, NQ>(l, (int64_t)blockIdx.x * wpb + w, (int64_t)gridDim.x * wpb, dense,
+                              offsets, ids, row_off, rows, W, B, T, D, nnz, bad,
+                              [](int64_t) {}, consume, []() {});
   const uint32_t any = (uint32_t)(__ballot(bad != 0) != 0);
   if (any) {
     uint32_t all = bad;
