@@ -422,6 +422,22 @@ emb_status_t emb_table_create_tiered(const emb_table_desc_t* desc, const emb_tie
  * them).  Afterwards the host arrays hold the table's current values. */
 emb_status_t emb_cache_flush(emb_table_t h, void* stream);
 
+/* emb_bag_prepare in two parts, for tiered tables: emb_bag_prepare_ids runs
+ * the id-only stages (keys, sort, run heads; no cache access) and
+ * emb_cache_prepare the cache stages of the same workspace (lookup, claim,
+ * write-back and fetch, slot keys).  emb_bag_prepare_ids followed by
+ * emb_cache_prepare equals emb_bag_prepare.  Split, the id stages of batch
+ * i+2, the cache stage of batch i+1 and the forward and backward of batch i
+ * can run on three streams (three workspaces).  emb_cache_prepare calls come
+ * in batch order, and each waits for the backward of the batch two before
+ * it, as emb_bag_prepare does.  On a dense table emb_bag_prepare_ids is
+ * emb_bag_prepare and emb_cache_prepare returns EMB_ERR_UNSUPPORTED. */
+emb_status_t emb_bag_prepare_ids(emb_table_t h, const int64_t* offsets, const int64_t* ids,
+                                 int64_t batch, int64_t nnz, emb_pool_t pool, void* ws,
+                                 size_t ws_bytes, void* stream);
+emb_status_t emb_cache_prepare(emb_table_t h, int64_t batch, int64_t nnz, void* ws,
+                               size_t ws_bytes, void* stream);
+
 /* HOST out: cumulative counts over all prepares of h (waits for the stream):
  * distinct rows looked up, misses (rows fetched from host memory) and
  * write-backs (evicted rows written to host memory; emb_cache_flush is not

@@ -364,9 +364,9 @@ static void sorted_arrays(const Handle& h, const Plan& p, char* w, uint32_t** ke
   *vals = reinterpret_cast<uint32_t*>(w + (in_b ? p.valsB : p.valsA));
 }
 
-emb_status_t emb_bag_prepare(emb_table_t t, const int64_t* offsets, const int64_t* ids,
-                             int64_t batch, int64_t nnz, emb_pool_t pool, void* ws,
-                             size_t ws_bytes, void* stream) {
+static emb_status_t prepare_impl(emb_table_t t, const int64_t* offsets, const int64_t* ids,
+                                 int64_t batch, int64_t nnz, emb_pool_t pool, void* ws,
+                                 size_t ws_bytes, void* stream, bool with_cache) {
   if (!t || (nnz > 0 && !ids)) return EMB_ERR_INVALID_ARG;
   if (pool != EMB_POOL_SUM && pool != EMB_POOL_MEAN) return EMB_ERR_INVALID_ARG;
   emb_status_t st = check_batch(t->h, offsets, batch, nnz);
@@ -381,9 +381,40 @@ emb_status_t emb_bag_prepare(emb_table_t t, const int64_t* offsets, const int64_
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e =
       launch_sort_unique(t->h, p, offsets, ids, pool == EMB_POOL_MEAN, w, &keys, &vals, s);
-  if (e == hipSuccess && t->h.tiered)
+  if (e == hipSuccess && t->h.tiered && with_cache)
     e = launch_cache_prepare(t->h, p, keys, vals, spare_keys(p, w), w, s);
   return hip_status(e);
+}
+
+emb_status_t emb_bag_prepare(emb_table_t t, const int64_t* offsets, const int64_t* ids,
+                             int64_t batch, int64_t nnz, emb_pool_t pool, void* ws,
+                             size_t ws_bytes, void* stream) {
+  return prepare_impl(t, offsets, ids, batch, nnz, pool, ws, ws_bytes, stream, true);
+}
+
+emb_status_t emb_bag_prepare_ids(emb_table_t t, const int64_t* offsets, const int64_t* ids,
+                                 int64_t batch, int64_t nnz, emb_pool_t pool, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  return prepare_impl(t, offsets, ids, batch, nnz, pool, ws, ws_bytes, stream, false);
+}
+
+emb_status_t emb_cache_prepare(emb_table_t t, int64_t batch, int64_t nnz, void* ws,
+                               size_t ws_bytes, void* stream) {
+  if (!t || batch < 0 || nnz < 0) return EMB_ERR_INVALID_ARG;
+  if (!t->h.tiered) return EMB_ERR_UNSUPPORTED;
+  Plan p;
+  if (!make_plan(t->h, batch, nnz, &p)) return EMB_ERR_UNSUPPORTED;
+  if (!ws || ws_bytes < p.total || (reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
+    return EMB_ERR_WORKSPACE;
+  if (batch == 0) return EMB_OK;
+  char* w = static_cast<char*>(ws);
+  // the sorted row keys and positions the id stages left (the buffer the last
+  // radix pass wrote); the slot keys go to the other key buffer
+  const bool in_b = p.nnz > 0 && (p.passes % 2) == 1;
+  const uint32_t* keys = reinterpret_cast<const uint32_t*>(w + (in_b ? p.keysB : p.keysA));
+  const uint32_t* vals = reinterpret_cast<const uint32_t*>(w + (in_b ? p.valsB : p.valsA));
+  return hip_status(launch_cache_prepare(t->h, p, keys, vals, spare_keys(p, w), w,
+                                         static_cast<hipStream_t>(stream)));
 }
 
 emb_status_t emb_bag_forward_prepared(emb_table_t t, const int64_t* offsets, const int64_t* ids,

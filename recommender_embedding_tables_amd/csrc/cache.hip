@@ -33,9 +33,13 @@
 // summation order, do not depend on which slot holds a row.
 #include "embtab_internal.hpp"
 
-// Blocks of the row-move kernel per compute unit (see launch_move).
+// Blocks of the row-move kernel per compute unit (see launch_move), as a
+// fraction EMBTAB_MOVE_BLOCKS_PER_CU / EMBTAB_MOVE_CU_DIV.
 #ifndef EMBTAB_MOVE_BLOCKS_PER_CU
 #define EMBTAB_MOVE_BLOCKS_PER_CU 1
+#endif
+#ifndef EMBTAB_MOVE_CU_DIV
+#define EMBTAB_MOVE_CU_DIV 2
 #endif
 
 namespace embtab {
@@ -271,12 +275,13 @@ template <int SG, int VEC>
 hipError_t launch_move(const Handle& h, const uint32_t* mrow, const uint32_t* vict,
                        const uint32_t* mslot, const uint32_t* misc, uint32_t n, hipStream_t s) {
   constexpr int SGPB = 256 / SG;
-  // The host link, not the CUs, bounds this kernel: a block per CU keeps
-  // megabytes of reads in flight (far above the link's bandwidth-latency
-  // product) and leaves the CUs to the forward and backward of the batch
-  // before, which run beside it on another stream.
+  // The host link, not the CUs, bounds this kernel: a block per two CUs
+  // keeps megabytes of reads in flight (far above the link's bandwidth-latency
+  // product) and leaves the CUs to the id stages and the forward and
+  // backward of other batches, which run beside it on other streams.
   int64_t grid = ((int64_t)n + SGPB - 1) / SGPB;
-  const int64_t cap = (int64_t)(h.cus > 0 ? h.cus : 256) * EMBTAB_MOVE_BLOCKS_PER_CU;
+  const int64_t cap =
+      (int64_t)(h.cus > 0 ? h.cus : 256) * EMBTAB_MOVE_BLOCKS_PER_CU / EMBTAB_MOVE_CU_DIV;
   grid = grid < 1 ? 1 : (grid > cap ? cap : grid);
   hipLaunchKernelGGL((k_cache_move<SG, VEC>), dim3((unsigned)grid), dim3(256), 0, s, mrow, vict,
                      mslot, misc, h.W, h.G, h.hostW, h.hostG, h.D, n);

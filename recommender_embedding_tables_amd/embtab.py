@@ -50,6 +50,7 @@ EXPORTED = [
     "emb_bag_backward_adagrad_decay_prepared", "emb_hash_find_or_insert_admit",
     "emb_hash_evict_workspace_bytes", "emb_hash_evict", "emb_hash_free_rows",
     "emb_interact_out_dim", "emb_bag_forward_interact", "emb_interact_backward",
+    "emb_bag_prepare_ids", "emb_cache_prepare",
 ]
 
 EMB_PHASE_FORWARD, EMB_PHASE_KEYS, EMB_PHASE_SORT, EMB_PHASE_UNIQUE = 0, 1, 2, 3
@@ -137,6 +138,8 @@ def _load():
         "emb_table_create_tiered": (i32, [C.POINTER(emb_table_desc_t),
                                           C.POINTER(emb_tier_desc_t), P, C.POINTER(P)]),
         "emb_cache_flush": (i32, [P, P]),
+        "emb_bag_prepare_ids": (i32, [P, P, P, i64, i64, i32, P, sz, P]),
+        "emb_cache_prepare": (i32, [P, i64, i64, P, sz, P]),
         "emb_cache_stats": (i32, [P, P, C.POINTER(i64), C.POINTER(i64), C.POINTER(i64)]),
     }
     for name, (res, args) in sig.items():
@@ -208,6 +211,16 @@ def emb_table_create_tiered(desc: emb_table_desc_t, tier: emb_tier_desc_t, strea
     h = C.c_void_p()
     st = _lib.emb_table_create_tiered(C.byref(desc), C.byref(tier), _stream(stream), C.byref(h))
     return st, h.value
+
+
+def emb_bag_prepare_ids(handle, offsets, ids, batch, nnz, pool, ws, ws_bytes,
+                        stream=None) -> int:
+    return _lib.emb_bag_prepare_ids(handle, _ptr(offsets), _ptr(ids), batch, nnz, pool, _ptr(ws),
+                                    ws_bytes, _stream(stream))
+
+
+def emb_cache_prepare(handle, batch, nnz, ws, ws_bytes, stream=None) -> int:
+    return _lib.emb_cache_prepare(handle, batch, nnz, _ptr(ws), ws_bytes, _stream(stream))
 
 
 def emb_cache_flush(handle, stream=None) -> int:

@@ -188,6 +188,7 @@ def test_cache_calls_on_a_dense_handle():
     assert st == eb.EMB_OK and h
     try:
         assert eb.emb_cache_flush(h, 0) == eb.EMB_ERR_UNSUPPORTED
+        assert eb.emb_cache_prepare(h, 4, 4, 0x50000000, 1 << 20, 0) == eb.EMB_ERR_UNSUPPORTED
         assert eb.emb_cache_stats(h, 0)[0] == eb.EMB_ERR_UNSUPPORTED
     finally:
         eb.emb_table_destroy(h)

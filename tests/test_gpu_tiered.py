@@ -263,3 +263,71 @@ def test_tiered_bit_equal_to_dense_table(case):
     assert eb.emb_status_sync(tiered.handle) == (eb.EMB_OK, 0)
     tiered.close()
     dense.close()
+
+
+def test_tiered_three_streams_split_prepare():
+    # id stages of batch i+2, cache stage of batch i+1 and the forward and
+    # backward of batch i on three streams, three workspaces
+    w = synth.workload(2, T=3, B=300, D=32, rows=[2500, 12000, 400])
+    steps, nsets = 7, 128
+    batches = [synth.gen_batch(w, b) for b in range(steps)]
+    grads = [synth.gen_grad(w, b) for b in range(steps)]
+    worst, over, distinct = set_pressure(w, batches, nsets)
+    assert worst <= eb.EMB_CACHE_WAYS and over > 0
+    tabs, o = make_tiered(w.rows, w.D, nsets * eb.EMB_CACHE_WAYS)
+    nnz = batches[0][1].size
+    ws0, need = tabs.workspace(w.B, nnz)
+    wss = [ws0, torch.empty_like(ws0), torch.empty_like(ws0)]
+    main, s_ids, s_cache = torch.cuda.current_stream(), torch.cuda.Stream(), torch.cuda.Stream()
+    ids_done = [torch.cuda.Event() for _ in range(3)]
+    cache_done = [torch.cuda.Event() for _ in range(3)]
+    step_done = [torch.cuda.Event() for _ in range(3)]
+    started = set()
+    d_b = [(_t(off), _t(ids)) for off, ids in batches]
+    outs = []
+
+    def prep_ids(i):
+        if i >= steps:
+            return
+        if i >= 3:
+            s_ids.wait_event(step_done[i % 3])  # batch i - 3 used this workspace
+        eb.check(eb.emb_bag_prepare_ids(tabs.handle, d_b[i][0], d_b[i][1], w.B, nnz,
+                                        eb.EMB_POOL_SUM, wss[i % 3], need, s_ids), "prepare_ids")
+        ids_done[i % 3].record(s_ids)
+
+    def prep_cache(i):
+        if i >= steps:
+            return
+        s_cache.wait_event(ids_done[i % 3])
+        if i >= 2:
+            s_cache.wait_event(step_done[(i - 2) % 3])  # may evict rows of batch i - 2
+        eb.check(eb.emb_cache_prepare(tabs.handle, w.B, nnz, wss[i % 3], need, s_cache),
+                 "cache_prepare")
+        cache_done[i % 3].record(s_cache)
+
+    prep_ids(0)
+    prep_ids(1)
+    prep_cache(0)
+    for i in range(steps):
+        prep_ids(i + 2)
+        prep_cache(i + 1)
+        main.wait_event(cache_done[i % 3])
+        out = torch.empty((w.B, w.T, w.D), dtype=torch.float32, device=DEV)
+        eb.check(eb.emb_bag_forward_prepared(tabs.handle, d_b[i][0], d_b[i][1], w.B, nnz,
+                                             eb.EMB_POOL_SUM, out, wss[i % 3], need, main),
+                 "forward")
+        eb.check(eb.emb_bag_backward_adagrad_prepared(tabs.handle, w.B, nnz, eb.EMB_POOL_SUM,
+                                                      _t(grads[i]), w.lr, w.eps, wss[i % 3],
+                                                      need, main), "backward")
+        step_done[i % 3].record(main)
+        outs.append(out)
+    torch.cuda.synchronize()
+    for i in range(steps):
+        offsets, ids = batches[i]
+        ref, _ = o.forward(offsets, ids, w.B, False)
+        S = forward_S(offsets, ids, w.B, o.rows, lambda r: o.read_rows(r)[0], False, w.D)
+        assert_within(outs[i].cpu().numpy(), ref, S + 2 * i * w.lr, f"forward {i}")
+        o.backward_adagrad(offsets, ids, w.B, False, grads[i], w.lr, w.eps)
+    check_all_rows(tabs, o, int(np.sum(w.rows)), steps)
+    assert eb.emb_status_sync(tabs.handle) == (eb.EMB_OK, 0)
+    tabs.close()
