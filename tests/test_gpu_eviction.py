@@ -128,3 +128,27 @@ def test_lifecycle_admission_decay_eviction():
     Wr, Gr = o.read_rows(live)
     assert_within(tabs.weights[_t(live)].cpu().numpy(), Wr, np.abs(Wr) + carried[live], "weights")
     assert_within(tabs.accum[_t(live)].cpu().numpy(), Gr, np.abs(Gr) * 8, "accumulators")
+
+
+def test_evict_everything_then_reinsert():
+    w = synth.workload(5, T=2, B=800, universe=10_000, hash_capacity=1 << 13)
+    w.rows = np.full(2, 4000, np.int64)
+    tabs, o = make_pair(w.rows, w.D, seed=34, hashed=True, cap=w.hash_capacity)
+    total = int(np.sum(w.rows))
+    offsets, ranks = synth.gen_batch(w, 1)
+    keys = synth.gen_keys(w, offsets, ranks)
+    np.testing.assert_array_equal(_hash_call(tabs, offsets, keys, w.B),
+                                  o.find_or_insert(offsets, keys, w.B)[0])
+    last = np.zeros(total, np.uint32)
+    evict(tabs, _t(last), 0)  # nothing is older than 0: a no-op
+    assert o.evict(last, 0) == 0
+    check_hash_state(tabs, o)
+    evict(tabs, _t(last), 1)  # everything is
+    assert o.evict(last, 1) > 0
+    st, queued = eb.emb_hash_free_rows(tabs.handle, tabs.T)
+    assert queued == [o.free_rows(t) for t in range(tabs.T)] == [o.n_live(t) for t in range(2)]
+    # the same keys come back onto the freed rows, ascending, in first-occurrence order
+    np.testing.assert_array_equal(_hash_call(tabs, offsets, keys, w.B),
+                                  o.find_or_insert(offsets, keys, w.B)[0])
+    check_hash_state(tabs, o)
+    assert status(tabs) == (eb.EMB_OK, 0)

@@ -154,3 +154,36 @@ def test_training_step_through_the_interaction():
     assert_within(Wg, Wr, np.abs(Wr) + 3 * w.lr, "weights")
     assert eb.emb_status_sync(tabs.handle) == (eb.EMB_OK, 0)
     tabs.close()
+
+
+def test_interaction_all_bags_empty():
+    # nnz = 0: every pooled vector is zero, so the pairs are all zero and the
+    # dense slot is copied; the backward gives grad_dense = grad_out's slot
+    T, D, B = 5, 32, 300
+    rows = np.full(T, 50, np.int64)
+    tabs = eb.EmbTables(rows, D, seed=2)
+    offsets = np.zeros(T * B + 1, np.int64)
+    ids = np.zeros(1, np.int64)
+    dense = np.random.default_rng(1).standard_normal((B, D)).astype(np.float32)
+    odim = eb.emb_interact_out_dim(tabs.handle)
+    out = torch.full((B, odim), 7.0, dtype=torch.float32, device=DEV)
+    eb.check(eb.emb_bag_forward_interact(tabs.handle, _t(offsets), _t(ids), B, 0, eb.EMB_POOL_MEAN,
+                                         _t(dense), out), "forward_interact")
+    got = out.cpu().numpy()
+    np.testing.assert_array_equal(got[:, :D], dense)
+    np.testing.assert_array_equal(got[:, D:], 0.0)
+    g = np.random.default_rng(2).standard_normal((B, odim)).astype(np.float32)
+    gd = torch.empty((B, D), dtype=torch.float32, device=DEV)
+    gp = torch.empty((B, T, D), dtype=torch.float32, device=DEV)
+    eb.check(eb.emb_interact_backward(tabs.handle, _t(offsets), _t(ids), B, 0, eb.EMB_POOL_MEAN,
+                                      _t(dense), _t(g), gd, gp), "interact_backward")
+    np.testing.assert_array_equal(gd.cpu().numpy(), g[:, :D])  # dz_0 = sum_j g_0j z_j = 0
+    # dz_{t+1} = g_{t+1,0} z_0 (the only nonzero vector)
+    li, lj = np.tril_indices(T + 1, -1)
+    G = np.zeros((B, T + 1, T + 1), np.float64)
+    G[:, li, lj] = g[:, D:]
+    G[:, lj, li] = g[:, D:]
+    ref = G[:, 1:, 0:1] * dense[:, None, :].astype(np.float64)
+    np.testing.assert_allclose(gp.cpu().numpy(), ref, rtol=1e-6, atol=1e-7)
+    assert eb.emb_status_sync(tabs.handle) == (eb.EMB_OK, 0)
+    tabs.close()
