@@ -349,7 +349,7 @@ emb_status_t emb_bag_backward_adagrad(emb_table_t t, const int64_t* offsets, con
     keys = slot_keys;
   }
   if (e == hipSuccess)
-    e = launch_segment_adagrad(t->h, p, keys, perm, mean, grad_out, lr, eps, w, s);
+    e = launch_segment_adagrad(t->h, p, keys, mean, grad_out, lr, eps, w, s);
   return hip_status(e);
 }
 
@@ -465,8 +465,8 @@ static emb_status_t backward_prepared(emb_table_t t, int64_t batch, int64_t nnz,
   uint32_t *keys = nullptr, *vals = nullptr;
   char* w = static_cast<char*>(ws);
   sorted_arrays(t->h, p, w, &keys, &vals);
-  return hip_status(launch_segment_adagrad(t->h, p, keys, vals, pool == EMB_POOL_MEAN, grad_out,
-                                           lr, eps, w, static_cast<hipStream_t>(stream), dec));
+  return hip_status(launch_segment_adagrad(t->h, p, keys, pool == EMB_POOL_MEAN, grad_out, lr,
+                                           eps, w, static_cast<hipStream_t>(stream), dec));
 }
 
 emb_status_t emb_bag_backward_adagrad_prepared(emb_table_t t, int64_t batch, int64_t nnz,
@@ -509,8 +509,8 @@ emb_status_t emb_debug_sort_unique(emb_table_t t, const int64_t* offsets, const 
   char* w = static_cast<char*>(ws);
   uint32_t *keys = nullptr, *vals = nullptr;
   hipError_t e = launch_sort_unique(t->h, p, offsets, ids, false, w, &keys, &vals, s);
-  if (e == hipSuccess)  // unique / seg_off / inverse / counts; W and G untouched
-    e = launch_segment_adagrad(t->h, p, keys, vals, false, nullptr, 0.0f, 0.0f, w, s);
+  if (e == hipSuccess)  // counts from seg_off; W and G untouched
+    e = launch_unique_counts(p, w, s);
   const size_t nb = sizeof(uint32_t) * (size_t)nnz;
   if (e == hipSuccess && sorted_rows)
     e = launch_debug_copy_sorted(keys, (uint32_t)t->h.total_rows, sorted_rows, nnz, s);

@@ -242,15 +242,15 @@ hipError_t launch_zero_words(uint32_t* p, int n, hipStream_t s);
 hipError_t launch_forward(const Handle& h, const int64_t* offsets, const int64_t* ids,
                           int64_t B, int64_t nnz, bool mean, float* out, hipStream_t s);
 
-// Keys, radix sort and unique; results stay in the workspace.  *sorted_keys
-// and *sorted_vals receive the workspace addresses of the sorted arrays.
+// Keys, radix sort and unique (unique, seg_off, inverse, num_unique); results
+// stay in the workspace.  *sorted_keys and *sorted_vals receive the workspace
+// addresses of the sorted arrays.
 hipError_t launch_sort_unique(const Handle& h, const Plan& p, const int64_t* offsets,
                               const int64_t* ids, bool mean, char* ws, uint32_t** sorted_keys,
                               uint32_t** sorted_vals, hipStream_t s);
 
-// Segmented reduction + Adagrad over the sorted occurrences; on the way it
-// writes unique / seg_off / inverse.  With grad_out == nullptr it only writes
-// those and counts (W and G untouched).
+// Segmented reduction + Adagrad over the sorted occurrences (grad_out must not
+// be null).
 // Adagrad Decay (stamps != NULL): before its step a row's accumulator is
 // multiplied by 2^((period - stamp[row]) * log2_rho) when period > stamp[row],
 // and stamp[row] becomes max(stamp[row], period).
@@ -259,10 +259,9 @@ struct DecayArgs {
   float log2_rho = 0.0f;
   uint32_t period = 0;
 };
-hipError_t launch_segment_adagrad(const Handle& h, const Plan& p, const uint32_t* keys,
-                                  const uint32_t* perm, bool mean, const float* grad_out,
-                                  float lr, float eps, char* ws, hipStream_t s,
-                                  const DecayArgs& dec = DecayArgs());
+hipError_t launch_segment_adagrad(const Handle& h, const Plan& p, const uint32_t* keys, bool mean,
+                                  const float* grad_out, float lr, float eps, char* ws,
+                                  hipStream_t s, const DecayArgs& dec = DecayArgs());
 
 // Forward from a prepared workspace.  One-hot batches gather the rows in
 // sorted order; otherwise (a device flag of the prepare) the same launch runs

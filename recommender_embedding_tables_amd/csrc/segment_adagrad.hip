@@ -13,8 +13,8 @@
 // one chunk per sub-group of SG lanes (a row is D/4 float4 columns spread over
 // the lanes), so a Zipf-hot row with tens of thousands of occurrences is
 // spread over many sub-groups instead of serialising one.  A sub-group loads
-// the chunk's metadata once (sorted key, occurrence, grad row, mean scale: one
-// element per lane), then walks the positions UF at a time: it issues the UF
+// the chunk's metadata once (sorted key, grad row, mean scale: one element
+// per lane), then walks the positions UF at a time: it issues the UF
 // gradient-row loads and, for every segment that ends inside the group and
 // lies wholly in the chunk, the W and G rows, before accumulating in position
 // order; a finished segment is updated in registers and written back once.
@@ -58,17 +58,14 @@ __device__ inline float decay_factor(uint32_t last, uint32_t period, float log2_
   return period > last ? exp2f((float)(period - last) * log2_rho) : 1.0f;
 }
 
-template <int SG, int VEC, bool MEAN, int MPL, int UF, bool UPDATE, bool DECAY>
+template <int SG, int VEC, bool MEAN, int MPL, int UF, bool DECAY>
 __global__ __launch_bounds__(256) void k_seg_adagrad(
-    const uint32_t* __restrict__ keys, const uint32_t* __restrict__ perm,
-    const uint32_t* __restrict__ sgr, const float* __restrict__ sscale,
-    const float* __restrict__ grad, float* __restrict__ W, float* __restrict__ G, uint32_t n,
-    uint32_t sentinel, int32_t D, float lr, float eps, float* __restrict__ part_head,
-    float* __restrict__ part_tail, uint32_t* __restrict__ span_list,
-    uint32_t* __restrict__ long_list, uint32_t* __restrict__ misc, uint32_t nbags,
-    const uint32_t* __restrict__ chunk_base, const uint32_t* __restrict__ head_base,
-    uint32_t* __restrict__ unique, uint32_t* __restrict__ seg_off,
-    uint32_t* __restrict__ inverse, uint32_t* __restrict__ stamps, float log2_rho,
+    const uint32_t* __restrict__ keys, const uint32_t* __restrict__ sgr,
+    const float* __restrict__ sscale, const float* __restrict__ grad, float* __restrict__ W,
+    float* __restrict__ G, uint32_t n, uint32_t sentinel, int32_t D, float lr, float eps,
+    float* __restrict__ part_head, float* __restrict__ part_tail,
+    uint32_t* __restrict__ span_list, uint32_t* __restrict__ long_list,
+    uint32_t* __restrict__ misc, uint32_t nbags, uint32_t* __restrict__ stamps, float log2_rho,
     uint32_t period) {
   constexpr int CH = SG * MPL;
   constexpr int SGPB = 256 / SG;
@@ -86,16 +83,13 @@ __global__ __launch_bounds__(256) void k_seg_adagrad(
   const uint64_t kfar = (uint64_t)k1 + (uint64_t)SG * CH;
   const uint32_t key_far = kfar < n ? keys[kfar] : kNoRow;
   const uint32_t nchunks = (n + CH - 1) / CH;
-  // unique index of a run entering the chunk
-  uint32_t ucur = head_base[c / (256 / CH)] + chunk_base[c] - 1u;
 
-  uint32_t mkey[MPL], mj[MPL], mgr[MPL];
+  uint32_t mkey[MPL], mgr[MPL];
   float msc[MPL];
 #pragma unroll
   for (int i = 0; i < MPL; ++i) {
     const uint32_t k = k0 + i * SG + lane;
     mkey[i] = kNoRow;
-    mj[i] = 0u;
     mgr[i] = 0u;
     msc[i] = 1.0f;
     if (k < k1) mkey[i] = keys[k];
@@ -107,18 +101,14 @@ __global__ __launch_bounds__(256) void k_seg_adagrad(
       // grad row and scale were gathered into sorted order by the last sort
       // pass.  Positions not written by any bag (offsets that do not tile
       // [0, nnz)) may hold stale values: such an occurrence is dropped.
-      const uint32_t j = perm[k];
       const uint32_t g = sgr[k];
       if (mkey[i] < sentinel) {
-        if (j < n && g < nbags) {
-          mj[i] = j;
+        if (g < nbags) {
           mgr[i] = g;
-          if (MEAN && UPDATE) msc[i] = sscale[k];
+          if (MEAN) msc[i] = sscale[k];
         } else {
           mkey[i] = sentinel;
         }
-      } else if (j < n) {
-        inverse[j] = kNoRow;  // an out-of-range occurrence belongs to no unique row
       }
     }
   }
@@ -127,20 +117,18 @@ __global__ __launch_bounds__(256) void k_seg_adagrad(
 #pragma unroll
   for (int v = 0; v < VEC; ++v) acc[v] = f4{0.f, 0.f, 0.f, 0.f};
   bool first_seg = true;
-  uint32_t lastkey = key_prev;
   const uint32_t last = k1 - k0 - 1;  // last position of the chunk
 
 #pragma unroll
   for (int i = 0; i < MPL; ++i) {
     for (int l0 = 0; l0 < SG; l0 += UF) {
-      uint32_t kk[UF + 1], gg[UF], jj[UF];
+      uint32_t kk[UF + 1], gg[UF];
       float cc[UF];
 #pragma unroll
       for (int u = 0; u < UF; ++u) {
         kk[u] = (uint32_t)__shfl((int)mkey[i], l0 + u, SG);
-        jj[u] = (uint32_t)__shfl((int)mj[i], l0 + u, SG);
-        gg[u] = UPDATE ? (uint32_t)__shfl((int)mgr[i], l0 + u, SG) : 0u;
-        cc[u] = (MEAN && UPDATE) ? __shfl(msc[i], l0 + u, SG) : 1.0f;
+        gg[u] = (uint32_t)__shfl((int)mgr[i], l0 + u, SG);
+        cc[u] = MEAN ? __shfl(msc[i], l0 + u, SG) : 1.0f;
       }
       {
         // key of the position after the group
@@ -165,35 +153,22 @@ __global__ __launch_bounds__(256) void k_seg_adagrad(
       if (!vld[0]) break;  // the rest of the chunk holds no valid keys
       f4 g[UF][VEC], wv[UF][VEC], gv[UF][VEC];
       uint32_t last[UF];  // Adagrad Decay: period of the row finished at u
-      if (UPDATE) {
 #pragma unroll
-        for (int u = 0; u < UF; ++u) {
-          last[u] = 0u;
-          if (DECAY && endf[u] && !startb[u]) last[u] = stamps[kk[u]];
+      for (int u = 0; u < UF; ++u) {
+        last[u] = 0u;
+        if (DECAY && endf[u] && !startb[u]) last[u] = stamps[kk[u]];
 #pragma unroll
-          for (int v = 0; v < VEC; ++v) {
-            const uint32_t d4 = (uint32_t)(lane + v * SG);
-            const bool own = endf[u] && !startb[u] && d4 < (uint32_t)D4;
-            g[u][v] = load4_nt_or_zero(grad, gg[u], (uint32_t)D, d4, vld[u] && d4 < (uint32_t)D4);
-            wv[u][v] = load4_or_zero(W, kk[u], (uint32_t)D, d4, own);
-            gv[u][v] = load4_or_zero(G, kk[u], (uint32_t)D, d4, own);
-          }
+        for (int v = 0; v < VEC; ++v) {
+          const uint32_t d4 = (uint32_t)(lane + v * SG);
+          const bool own = endf[u] && !startb[u] && d4 < (uint32_t)D4;
+          g[u][v] = load4_nt_or_zero(grad, gg[u], (uint32_t)D, d4, vld[u] && d4 < (uint32_t)D4);
+          wv[u][v] = load4_or_zero(W, kk[u], (uint32_t)D, d4, own);
+          gv[u][v] = load4_or_zero(G, kk[u], (uint32_t)D, d4, own);
         }
       }
 #pragma unroll
       for (int u = 0; u < UF; ++u) {
         if (!vld[u]) continue;
-        const uint32_t p = (uint32_t)(i * SG + l0 + u);
-        const uint32_t prevk = u > 0 ? kk[u > 0 ? u - 1 : 0] : lastkey;
-        if (kk[u] != prevk) {
-          ++ucur;
-          if (lane == 0 && ucur < n) {  // always true for a prepared workspace
-            unique[ucur] = kk[u];
-            seg_off[ucur] = k0 + p;
-          }
-        }
-        if (lane == 0) inverse[jj[u]] = ucur;
-        if (!UPDATE) continue;
 #pragma unroll
         for (int v = 0; v < VEC; ++v) acc[v] += MEAN ? g[u][v] * cc[u] : g[u][v];
         if (endf[u]) {
@@ -236,7 +211,6 @@ __global__ __launch_bounds__(256) void k_seg_adagrad(
           }
         }
       }
-      lastkey = kk[UF - 1];
       first_seg = fs;
     }
   }
@@ -407,8 +381,7 @@ __global__ __launch_bounds__(NT) void k_fixup(
 }
 
 template <int SG, int VEC, bool MEAN, bool DECAY>
-hipError_t launch_t(const Handle& h, const Plan& p, const uint32_t* keys, const uint32_t* perm,
-                    const float* grad_out, float lr, float eps, char* ws, hipStream_t s,
+hipError_t launch_t(const Handle& h, const Plan& p, const uint32_t* keys, const float* grad_out, float lr, float eps, char* ws, hipStream_t s,
                     const DecayArgs& dec) {
   constexpr int MPL = chunk_rounds<SG>();
   constexpr int UF = VEC > 1 ? 2 : (SG < kSegUF ? SG : kSegUF);
@@ -425,26 +398,13 @@ hipError_t launch_t(const Handle& h, const Plan& p, const uint32_t* keys, const 
   uint32_t* spans = reinterpret_cast<uint32_t*>(ws + p.span_list);
   uint32_t* longs = reinterpret_cast<uint32_t*>(ws + p.long_list);
   uint32_t* misc = reinterpret_cast<uint32_t*>(ws + p.misc);
-  const uint32_t* cbase = reinterpret_cast<const uint32_t*>(ws + p.chunk_base);
-  const uint32_t* hbase = reinterpret_cast<const uint32_t*>(ws + p.head_base);
-  uint32_t* uniq = reinterpret_cast<uint32_t*>(ws + p.unique);
-  uint32_t* segs = reinterpret_cast<uint32_t*>(ws + p.seg_off);
-  uint32_t* inv = reinterpret_cast<uint32_t*>(ws + p.inverse);
   const uint32_t nbags = (uint32_t)(p.B * h.T);
   hipError_t e;
-  if (!grad_out) {  // unique / seg_off / inverse only
-    hipLaunchKernelGGL((k_seg_adagrad<SG, VEC, false, MPL, UF, false, false>),
-                       dim3((unsigned)grid), dim3(256), 0, s, keys, perm, gr, scale, grad_out,
-                       h.W, h.G, n, (uint32_t)h.total_rows, h.D, lr, eps, ph, pt, spans, longs,
-                       misc, nbags, cbase, hbase, uniq, segs, inv, nullptr, 0.0f, 0u);
-    e = hipGetLastError();
-    return e == hipSuccess ? launch_unique_counts(p, ws, s) : e;
-  }
   phase_mark(h, EMB_PHASE_REDUCE, false, s);
-  hipLaunchKernelGGL((k_seg_adagrad<SG, VEC, MEAN, MPL, UF, true, DECAY>),
-                     dim3((unsigned)grid), dim3(256), 0, s, keys, perm, gr, scale, grad_out, h.W,
-                     h.G, n, (uint32_t)h.total_rows, h.D, lr, eps, ph, pt, spans, longs, misc,
-                     nbags, cbase, hbase, uniq, segs, inv, dec.stamps, dec.log2_rho, dec.period);
+  hipLaunchKernelGGL((k_seg_adagrad<SG, VEC, MEAN, MPL, UF, DECAY>), dim3((unsigned)grid),
+                     dim3(256), 0, s, keys, gr, scale, grad_out, h.W, h.G, n,
+                     (uint32_t)h.total_rows, h.D, lr, eps, ph, pt, spans, longs, misc, nbags,
+                     dec.stamps, dec.log2_rho, dec.period);
   phase_mark(h, EMB_PHASE_REDUCE, true, s);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -462,12 +422,11 @@ hipError_t launch_t(const Handle& h, const Plan& p, const uint32_t* keys, const 
 }
 
 template <bool MEAN, bool DECAY>
-hipError_t dispatch(const Handle& h, const Plan& p, const uint32_t* keys, const uint32_t* perm,
-                    const float* grad_out, float lr, float eps, char* ws, hipStream_t s,
+hipError_t dispatch(const Handle& h, const Plan& p, const uint32_t* keys, const float* grad_out, float lr, float eps, char* ws, hipStream_t s,
                     const DecayArgs& dec) {
   const int sg = subgroup_lanes(h.D), vec = vec_per_lane(h.D);
 #define EMBTAB_SEG_LAUNCH(SG_, VEC_) \
-  launch_t<SG_, VEC_, MEAN, DECAY>(h, p, keys, perm, grad_out, lr, eps, ws, s, dec)
+  launch_t<SG_, VEC_, MEAN, DECAY>(h, p, keys, grad_out, lr, eps, ws, s, dec)
   switch (sg) {
     case 1: return EMBTAB_SEG_LAUNCH(1, 1);
     case 2: return EMBTAB_SEG_LAUNCH(2, 1);
@@ -488,15 +447,15 @@ hipError_t dispatch(const Handle& h, const Plan& p, const uint32_t* keys, const 
 
 }  // namespace
 
-hipError_t launch_segment_adagrad(const Handle& h, const Plan& p, const uint32_t* keys,
-                                  const uint32_t* perm, bool mean, const float* grad_out,
-                                  float lr, float eps, char* ws, hipStream_t s,
-                                  const DecayArgs& dec) {
-  if (dec.stamps && grad_out)
-    return mean ? dispatch<true, true>(h, p, keys, perm, grad_out, lr, eps, ws, s, dec)
-                : dispatch<false, true>(h, p, keys, perm, grad_out, lr, eps, ws, s, dec);
-  return mean ? dispatch<true, false>(h, p, keys, perm, grad_out, lr, eps, ws, s, dec)
-              : dispatch<false, false>(h, p, keys, perm, grad_out, lr, eps, ws, s, dec);
+hipError_t launch_segment_adagrad(const Handle& h, const Plan& p, const uint32_t* keys, bool mean,
+                                  const float* grad_out, float lr, float eps, char* ws,
+                                  hipStream_t s, const DecayArgs& dec) {
+  if (!grad_out) return hipErrorInvalidValue;
+  if (dec.stamps)
+    return mean ? dispatch<true, true>(h, p, keys, grad_out, lr, eps, ws, s, dec)
+                : dispatch<false, true>(h, p, keys, grad_out, lr, eps, ws, s, dec);
+  return mean ? dispatch<true, false>(h, p, keys, grad_out, lr, eps, ws, s, dec)
+              : dispatch<false, false>(h, p, keys, grad_out, lr, eps, ws, s, dec);
 }
 
 }  // namespace embtab

@@ -26,10 +26,13 @@
 //   k_chunk_scan    one block: exclusive scan of the chunk head counts, giving
 //                   the unique index of each chunk's first run; num_unique and
 //                   seg_off[num_unique].
-// The reduction kernel that follows walks the sorted occurrences anyway and
-// writes unique[u], seg_off[u] and inverse[perm[k]] on the way; counts[u] =
-// seg_off[u+1] - seg_off[u] (k_unique_counts) is formed only for the sort /
-// unique export, since no training step reads it.
+//   k_materialize   unique[u], seg_off[u] and inverse[perm[k]] for every sorted
+//                   position k (u = run heads at or before k, minus one).
+// These kernels need only the ids, so a caller can run them for the next batch
+// beside this batch's forward and backward; the scattered inverse stores then
+// stay off the training kernels' stream.  counts[u] = seg_off[u+1] - seg_off[u]
+// (k_unique_counts) is formed only for the sort / unique export, since no
+// training step reads it.
 #include "embtab_internal.hpp"
 
 namespace embtab {
@@ -449,9 +452,46 @@ __global__ __launch_bounds__(256) void k_copy_sorted(const uint32_t* __restrict_
   }
 }
 
+// unique / seg_off / inverse from the sorted keys: position k's unique index
+// is the number of run heads at or before k, minus one (block bases from the
+// scanned head totals).
+__global__ __launch_bounds__(256) void k_materialize(const uint32_t* __restrict__ keys,
+                                                     const uint32_t* __restrict__ perm, uint32_t n,
+                                                     uint32_t sentinel,
+                                                     const uint32_t* __restrict__ hbase,
+                                                     uint32_t* __restrict__ unique,
+                                                     uint32_t* __restrict__ seg_off,
+                                                     uint32_t* __restrict__ inverse) {
+  __shared__ uint32_t wcnt[4];
+  const uint32_t k = blockIdx.x * 256u + threadIdx.x;
+  const uint32_t lane = threadIdx.x & 63u, wv = threadIdx.x >> 6;
+  uint32_t key = sentinel;
+  bool head = false;
+  if (k < n) {
+    key = keys[k];
+    head = key < sentinel && (k == 0 || keys[k - 1] != key);
+  }
+  const uint64_t m = __ballot(head);
+  if (lane == 0) wcnt[wv] = (uint32_t)__popcll(m);
+  __syncthreads();
+  uint32_t before = hbase[blockIdx.x];
+  for (uint32_t i = 0; i < wv; ++i) before += wcnt[i];
+  const uint32_t incl = before + lanes_below(m) + (head ? 1u : 0u);
+  if (k < n) {
+    const uint32_t j = perm[k];
+    const uint32_t u = incl - 1u;
+    if (j < n) inverse[j] = key < sentinel ? u : kNoRow;
+    if (head) {
+      unique[u] = key;
+      seg_off[u] = k;
+    }
+  }
+}
+
 }  // namespace
 
-hipError_t launch_sort_unique(const Handle& h, const Plan& p, const int64_t* offsets,
+hipError_t launch_sort_unique(
+const Handle& h, const Plan& p, const int64_t* offsets,
                               const int64_t* ids, bool mean, char* ws, uint32_t** sorted_keys,
                               uint32_t** sorted_vals, hipStream_t s) {
   const uint32_t n = (uint32_t)p.nnz;
@@ -527,6 +567,10 @@ hipError_t launch_sort_unique(const Handle& h, const Plan& p, const int64_t* off
                          cbase, btot, misc);
   }
   hipLaunchKernelGGL(k_chunk_scan, dim3(1), dim3(1024), 0, s, btot, hgrid, misc, seg_off);
+  if (n > 0)
+    hipLaunchKernelGGL(k_materialize, dim3(hgrid), dim3(256), 0, s, kin, vin, n, sentinel, btot,
+                       reinterpret_cast<uint32_t*>(ws + p.unique), seg_off,
+                       reinterpret_cast<uint32_t*>(ws + p.inverse));
   phase_mark(h, EMB_PHASE_UNIQUE, true, s);
   *sorted_keys = kin;
   *sorted_vals = vin;
