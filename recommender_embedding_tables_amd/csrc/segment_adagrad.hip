@@ -58,20 +58,34 @@ __device__ inline float decay_factor(uint32_t last, uint32_t period, float log2_
   return period > last ? exp2f((float)(period - last) * log2_rho) : 1.0f;
 }
 
+// A run that crosses chunk boundaries but neither enters the block from the
+// previous one nor leaves it into the next is finished inside the block: the
+// chunk where it ends keeps its own part sum and the row's W and G in
+// registers, the earlier chunks leave their parts in LDS, and after the block
+// barrier it adds them in chunk order (the order of k_fixup) and applies the
+// step.  Only runs that cross a block boundary go to the span lists.
+template <int VEC>
+struct BlockRun {
+  uint32_t row = kNoRow;  // kNoRow: this chunk finishes no run of the block
+  uint32_t last = 0u;     // Adagrad Decay: the row's period before this call
+  f4 acc[VEC], w[VEC], g2[VEC];
+};
+
+// Walks chunk c (one sub-group).  key_bb / key_ba: the keys just before and
+// just after the block.  A run continuing past the chunk and lying wholly in
+// the block leaves its part in part_lds and its row in *slot_key.
 template <int SG, int VEC, bool MEAN, int MPL, int UF, bool DECAY>
-__global__ __launch_bounds__(256) void k_seg_adagrad(
+__device__ __forceinline__ void seg_chunk(
     const uint32_t* __restrict__ keys, const uint32_t* __restrict__ sgr,
     const float* __restrict__ sscale, const float* __restrict__ grad, float* __restrict__ W,
     float* __restrict__ G, uint32_t n, uint32_t sentinel, int32_t D, float lr, float eps,
     float* __restrict__ part_head, float* __restrict__ part_tail,
     uint32_t* __restrict__ span_list, uint32_t* __restrict__ long_list,
     uint32_t* __restrict__ misc, uint32_t nbags, uint32_t* __restrict__ stamps, float log2_rho,
-    uint32_t period) {
+    uint32_t period, uint32_t c, uint32_t key_bb, uint32_t key_ba, f4* part_lds,
+    uint32_t* slot_key, BlockRun<VEC>& fin) {
   constexpr int CH = SG * MPL;
-  constexpr int SGPB = 256 / SG;
   const int lane = threadIdx.x % SG;
-  const int sgb = threadIdx.x / SG;
-  const uint32_t c = blockIdx.x * SGPB + sgb;
   const uint32_t k0 = c * CH;
   if (k0 >= n) return;
   const uint32_t k1 = (k0 + CH < n) ? k0 + CH : n;
@@ -156,11 +170,14 @@ __global__ __launch_bounds__(256) void k_seg_adagrad(
 #pragma unroll
       for (int u = 0; u < UF; ++u) {
         last[u] = 0u;
-        if (DECAY && endf[u] && !startb[u]) last[u] = stamps[kk[u]];
+        // the row is updated by this sub-group: its run starts here, or it
+        // started in an earlier chunk of this block
+        const bool mine = endf[u] && (!startb[u] || kk[u] != key_bb);
+        if (DECAY && mine) last[u] = stamps[kk[u]];
 #pragma unroll
         for (int v = 0; v < VEC; ++v) {
           const uint32_t d4 = (uint32_t)(lane + v * SG);
-          const bool own = endf[u] && !startb[u] && d4 < (uint32_t)D4;
+          const bool own = mine && d4 < (uint32_t)D4;
           g[u][v] = load4_nt_or_zero(grad, gg[u], (uint32_t)D, d4, vld[u] && d4 < (uint32_t)D4);
           wv[u][v] = load4_or_zero(W, kk[u], (uint32_t)D, d4, own);
           gv[u][v] = load4_or_zero(G, kk[u], (uint32_t)D, d4, own);
@@ -188,6 +205,15 @@ __global__ __launch_bounds__(256) void k_seg_adagrad(
                 *reinterpret_cast<f4*>(G + (size_t)kk[u] * D + 4 * d4) = gv[u][v];
               }
             }
+          } else if (kk[u] != key_bb) {  // finished after the block barrier
+            fin.row = kk[u];
+            fin.last = last[u];
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) {
+              fin.acc[v] = acc[v];
+              fin.w[v] = wv[u][v];
+              fin.g2[v] = gv[u][v];
+            }
           } else {
 #pragma unroll
             for (int v = 0; v < VEC; ++v) {
@@ -197,6 +223,10 @@ __global__ __launch_bounds__(256) void k_seg_adagrad(
           }
 #pragma unroll
           for (int v = 0; v < VEC; ++v) acc[v] = f4{0.f, 0.f, 0.f, 0.f};
+        } else if (cont[u] && kk[u] != key_bb && kk[u] != key_ba) {
+#pragma unroll
+          for (int v = 0; v < VEC; ++v) part_lds[lane + v * SG] = acc[v];
+          *slot_key = kk[u];
         } else if (cont[u]) {
           float* dst = startb[u] ? part_head : part_tail;
 #pragma unroll
@@ -213,6 +243,56 @@ __global__ __launch_bounds__(256) void k_seg_adagrad(
       }
       first_seg = fs;
     }
+  }
+}
+
+
+template <int SG, int VEC, bool MEAN, int MPL, int UF, bool DECAY>
+__global__ __launch_bounds__(256) void k_seg_adagrad(
+    const uint32_t* __restrict__ keys, const uint32_t* __restrict__ sgr,
+    const float* __restrict__ sscale, const float* __restrict__ grad, float* __restrict__ W,
+    float* __restrict__ G, uint32_t n, uint32_t sentinel, int32_t D, float lr, float eps,
+    float* __restrict__ part_head, float* __restrict__ part_tail,
+    uint32_t* __restrict__ span_list, uint32_t* __restrict__ long_list,
+    uint32_t* __restrict__ misc, uint32_t nbags, uint32_t* __restrict__ stamps, float log2_rho,
+    uint32_t period) {
+  constexpr int CH = SG * MPL;
+  constexpr int SGPB = 256 / SG;
+  __shared__ f4 s_part[SGPB][SG * VEC];
+  __shared__ uint32_t s_key[SGPB];
+  const int lane = threadIdx.x % SG;
+  const int sgb = threadIdx.x / SG;
+  const uint32_t c = blockIdx.x * SGPB + sgb;
+  const uint64_t b0 = (uint64_t)blockIdx.x * SGPB * CH, b1 = b0 + (uint64_t)SGPB * CH;
+  const uint32_t key_bb = b0 > 0 ? keys[b0 - 1] : kNoRow;
+  const uint32_t key_ba = b1 < n ? keys[b1] : kNoRow;
+  BlockRun<VEC> fin;
+  uint32_t slot_key = kNoRow;
+  seg_chunk<SG, VEC, MEAN, MPL, UF, DECAY>(keys, sgr, sscale, grad, W, G, n, sentinel, D, lr, eps,
+                                           part_head, part_tail, span_list, long_list, misc,
+                                           nbags, stamps, log2_rho, period, c, key_bb, key_ba,
+                                           s_part[sgb], &slot_key, fin);
+  if (lane == 0) s_key[sgb] = slot_key;
+  __syncthreads();
+  if (fin.row == kNoRow) return;
+  // chunks c0 .. c-1 of this block hold the run's earlier parts
+  int i0 = sgb;
+  while (i0 > 0 && s_key[i0 - 1] == fin.row) --i0;
+  const int D4 = D >> 2;
+  const float df = DECAY ? decay_factor(fin.last, period, log2_rho) : 1.0f;
+  if (DECAY && lane == 0 && period > fin.last) stamps[fin.row] = period;
+#pragma unroll
+  for (int v = 0; v < VEC; ++v) {
+    const int d4 = lane + v * SG;
+    if (d4 >= D4) continue;
+    f4 tot = s_part[i0][lane + v * SG];
+    for (int i = i0 + 1; i < sgb; ++i) tot += s_part[i][lane + v * SG];
+    tot += fin.acc[v];
+    f4 g2 = fin.g2[v];
+    if (DECAY) g2 *= df;
+    adagrad_step(fin.w[v], g2, tot, lr, eps);
+    *reinterpret_cast<f4*>(W + (size_t)fin.row * D + 4 * d4) = fin.w[v];
+    *reinterpret_cast<f4*>(G + (size_t)fin.row * D + 4 * d4) = g2;
   }
 }
 
