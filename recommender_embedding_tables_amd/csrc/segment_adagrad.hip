@@ -42,6 +42,16 @@ namespace {
 // Sorted positions walked per group by one sub-group (rows in flight).
 constexpr int kSegUF = EMBTAB_SEG_UF;
 
+// The accumulator G is read and written once per touched row per step and
+// read by nothing else, so its rows use non-temporal loads and stores: they
+// would only evict the W rows and gradient metadata the step reuses from L2
+// and MALL.  (Measured on 26 tables: 0.623 -> 0.600 ms per step; the same for
+// W loads or stores, or for the forward's row loads, did not pay.)
+__device__ inline void store4_nt(float* __restrict__ base, size_t row, uint32_t D, uint32_t d4,
+                                 const f4 x) {
+  __builtin_nontemporal_store(x, reinterpret_cast<f4*>(base + row * D + 4u * d4));
+}
+
 __device__ inline void adagrad_step(f4& w, f4& g2, const f4 g, float lr, float eps) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -180,7 +190,7 @@ __device__ __forceinline__ void seg_chunk(
           const bool own = mine && d4 < (uint32_t)D4;
           g[u][v] = load4_nt_or_zero(grad, gg[u], (uint32_t)D, d4, vld[u] && d4 < (uint32_t)D4);
           wv[u][v] = load4_or_zero(W, kk[u], (uint32_t)D, d4, own);
-          gv[u][v] = load4_or_zero(G, kk[u], (uint32_t)D, d4, own);
+          gv[u][v] = load4_nt_or_zero(G, kk[u], (uint32_t)D, d4, own);
         }
       }
 #pragma unroll
@@ -202,7 +212,7 @@ __device__ __forceinline__ void seg_chunk(
                 if (DECAY) gv[u][v] *= df;
                 adagrad_step(wv[u][v], gv[u][v], acc[v], lr, eps);
                 *reinterpret_cast<f4*>(W + (size_t)kk[u] * D + 4 * d4) = wv[u][v];
-                *reinterpret_cast<f4*>(G + (size_t)kk[u] * D + 4 * d4) = gv[u][v];
+                store4_nt(G, kk[u], (uint32_t)D, (uint32_t)d4, gv[u][v]);
               }
             }
           } else if (kk[u] != key_bb) {  // finished after the block barrier
@@ -292,7 +302,7 @@ __global__ __launch_bounds__(256) void k_seg_adagrad(
     if (DECAY) g2 *= df;
     adagrad_step(fin.w[v], g2, tot, lr, eps);
     *reinterpret_cast<f4*>(W + (size_t)fin.row * D + 4 * d4) = fin.w[v];
-    *reinterpret_cast<f4*>(G + (size_t)fin.row * D + 4 * d4) = g2;
+    store4_nt(G, fin.row, (uint32_t)D, (uint32_t)d4, g2);
   }
 }
 
@@ -391,11 +401,12 @@ __global__ __launch_bounds__(NT) void k_fixup(
         f4 tot = *reinterpret_cast<const f4*>(part_tail + (size_t)c0 * D + 4 * d4);
         for (int q = 0; q < SGPB; ++q) tot += red[q][lane + v * SG];
         f4 w = *reinterpret_cast<const f4*>(W + (size_t)row * D + 4 * d4);
-        f4 g2 = *reinterpret_cast<const f4*>(G + (size_t)row * D + 4 * d4);
+        f4 g2 = __builtin_nontemporal_load(
+            reinterpret_cast<const f4*>(G + (size_t)row * D + 4 * d4));
         if (DECAY) g2 *= df;
         adagrad_step(w, g2, tot, lr, eps);
         *reinterpret_cast<f4*>(W + (size_t)row * D + 4 * d4) = w;
-        *reinterpret_cast<f4*>(G + (size_t)row * D + 4 * d4) = g2;
+        store4_nt(G, row, (uint32_t)D, (uint32_t)d4, g2);
       }
     }
     __syncthreads();
@@ -426,7 +437,8 @@ __global__ __launch_bounds__(NT) void k_fixup(
       const int d4 = lane + v * SG;
       if (d4 >= D4) continue;
       f4 w = *reinterpret_cast<const f4*>(W + (size_t)row * D + 4 * d4);
-      f4 g2 = *reinterpret_cast<const f4*>(G + (size_t)row * D + 4 * d4);
+      f4 g2 = __builtin_nontemporal_load(
+          reinterpret_cast<const f4*>(G + (size_t)row * D + 4 * d4));
       if (DECAY) g2 *= df;
       f4 tot = *reinterpret_cast<const f4*>(part_tail + (size_t)c0 * D + 4 * d4);
       uint32_t c = c0 + 1;
@@ -443,7 +455,7 @@ __global__ __launch_bounds__(NT) void k_fixup(
       for (; c <= c1; ++c) tot += *reinterpret_cast<const f4*>(part_head + (size_t)c * D + 4 * d4);
       adagrad_step(w, g2, tot, lr, eps);
       *reinterpret_cast<f4*>(W + (size_t)row * D + 4 * d4) = w;
-      *reinterpret_cast<f4*>(G + (size_t)row * D + 4 * d4) = g2;
+      store4_nt(G, row, (uint32_t)D, (uint32_t)d4, g2);
     }
   }
 
