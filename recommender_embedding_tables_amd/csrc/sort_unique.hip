@@ -63,12 +63,16 @@ __device__ inline uint32_t block_excl_scan(uint32_t v, uint32_t* total, uint32_t
 }
 
 // One block per `bpb` consecutive bags in CSR order (bpb <= 256, chosen so
-// a block covers about 256 occurrences).  Thread i < bpb checks bag b0 + i;
-// the bag offsets go to LDS, and the block then walks the occurrences
+// a block covers about 256 occurrences).  Thread i < bpb checks bag b0 + i.
+// When every bag of the block holds exactly the occurrence with its own index
+// (one-hot features), thread i writes occurrence b0 + i directly from loads it
+// issued beside the offsets (the id at its own index, its table's bounds).
+// Otherwise the bag offsets go to LDS, and the block walks the occurrences
 // [offsets[b0], offsets[b0 + bpb]) with consecutive threads on consecutive
 // occurrences (coalesced id loads and key stores, whatever the bag lengths),
 // finding each occurrence's bag by binary search in LDS.  The value of
-// occurrence j is j itself, so it is not stored.
+// occurrence j is j itself, so it is not stored.  T * B < 2^32 (grad rows are
+// 32-bit).
 __global__ __launch_bounds__(256) void k_keys(const int64_t* __restrict__ offsets,
                                               const int64_t* __restrict__ ids,
                                               const int64_t* __restrict__ row_off,
@@ -88,10 +92,15 @@ __global__ __launch_bounds__(256) void k_keys(const int64_t* __restrict__ offset
   if (nb <= 0) return;  // empty batch (the grid has one block)
   if (threadIdx.x == 0) s_bad = 0u;
   const bool mine = threadIdx.x < nb;
-  int64_t o0 = 0, o1 = 1;
+  int64_t o0 = 0, o1 = 1, own_id = 0, own_rows = 0, own_off = 0;
+  uint32_t own_t = 0;
   if (mine) {
     o0 = offsets[b];
     o1 = offsets[b + 1];
+    own_t = (uint32_t)b / (uint32_t)B;
+    own_rows = rows[own_t];
+    own_off = row_off[own_t];
+    if (b < nnz) own_id = ids[b];  // the id of bag b if the bag is one-hot in place
   }
   {
     const uint64_t mm = __ballot(o1 - o0 != 1);
@@ -108,29 +117,43 @@ __global__ __launch_bounds__(256) void k_keys(const int64_t* __restrict__ offset
     s_off[threadIdx.x] = o0 < 0 ? 0 : (o0 > nnz ? nnz : o0);
     if (threadIdx.x == nb - 1) s_off[nb] = o1 < 0 ? 0 : (o1 > nnz ? nnz : o1);
   }
-  __syncthreads();
-  const int64_t j0 = s_off[0], j1 = s_off[nb];
-  for (int64_t j = j0 + threadIdx.x; j < j1; j += 256) {
-    // last bag i of the block with s_off[i] <= j (bags of length 0 are skipped)
-    int lo = 0, hi = (int)nb - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (s_off[mid] <= j) lo = mid;
-      else hi = mid - 1;
+  const bool in_place = !mine || (o0 == b && o1 == b + 1 && o1 <= nnz);
+  if (__syncthreads_and(in_place)) {
+    if (mine) {
+      uint32_t key = sentinel;
+      if (own_id >= 0 && own_id < own_rows) key = (uint32_t)own_off + (uint32_t)own_id;
+      else if (own_id != kAbsentId) bad |= EMB_FLAG_OUT_OF_RANGE;
+      keys[b] = key;
+      const uint32_t g = ((uint32_t)b - own_t * (uint32_t)B) * (uint32_t)T + own_t;
+      if (mean)
+        reinterpret_cast<uint2*>(gr)[b] = make_uint2(g, __float_as_uint(1.0f));
+      else
+        gr[b] = g;
     }
-    const int64_t bag = b0 + lo;
-    const int64_t t = bag / B, s = bag - t * B;
-    const int64_t id = ids[j];
-    uint32_t key = sentinel;
-    if (id >= 0 && id < rows[t]) key = (uint32_t)row_off[t] + (uint32_t)id;
-    else if (id != kAbsentId) bad |= EMB_FLAG_OUT_OF_RANGE;
-    keys[j] = key;
-    const uint32_t g = (uint32_t)(s * T + t);
-    if (mean)  // grad row and scale side by side: one gather in the last pass
-      reinterpret_cast<uint2*>(gr)[j] =
-          make_uint2(g, __float_as_uint(1.0f / (float)(s_off[lo + 1] - s_off[lo])));
-    else
-      gr[j] = g;
+  } else {
+    const int64_t j0 = s_off[0], j1 = s_off[nb];
+    for (int64_t j = j0 + threadIdx.x; j < j1; j += 256) {
+      // last bag i of the block with s_off[i] <= j (bags of length 0 are skipped)
+      int lo = 0, hi = (int)nb - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_off[mid] <= j) lo = mid;
+        else hi = mid - 1;
+      }
+      const int64_t bag = b0 + lo;
+      const int64_t t = bag / B, s = bag - t * B;
+      const int64_t id = ids[j];
+      uint32_t key = sentinel;
+      if (id >= 0 && id < rows[t]) key = (uint32_t)row_off[t] + (uint32_t)id;
+      else if (id != kAbsentId) bad |= EMB_FLAG_OUT_OF_RANGE;
+      keys[j] = key;
+      const uint32_t g = (uint32_t)(s * T + t);
+      if (mean)  // grad row and scale side by side: one gather in the last pass
+        reinterpret_cast<uint2*>(gr)[j] =
+            make_uint2(g, __float_as_uint(1.0f / (float)(s_off[lo + 1] - s_off[lo])));
+      else
+        gr[j] = g;
+    }
   }
   if (bad) atomicOr(&s_bad, bad);
   __syncthreads();
