@@ -18,11 +18,14 @@
 // gradient-row loads and, for every segment that ends inside the group and
 // lies wholly in the chunk, the W and G rows, before accumulating in position
 // order; a finished segment is updated in registers and written back once.
-// A segment that crosses a chunk boundary leaves fp32 partial sums (the
-// chunk's "tail" part where it starts, "head" parts in the chunks it covers);
-// its start chunk is appended to one of two span lists, by whether the
-// segment ends within SG chunks of its start, and k_fixup adds the parts in
-// chunk order and applies the step.  Every sum has a fixed order, so the
+// A segment that crosses a chunk boundary leaves fp32 part sums in LDS.  If
+// it lies wholly in the block, the chunk where it ends adds them and applies
+// the step after the block barrier.  If it crosses a block edge, the block
+// adds its chunks' parts and leaves one part per block in memory (the "tail"
+// part where it starts, a "head" part in each later block it covers); its
+// start block is appended to one of two span lists, by whether the segment
+// ends within kShortSpan blocks of its start, and k_fixup adds the parts in
+// block order and applies the step.  Every sum has a fixed order, so the
 // result is deterministic and no float atomics are used.
 //
 // Finishing such a segment inside this kernel, by the sub-group of the chunk
@@ -41,6 +44,10 @@ namespace {
 
 // Sorted positions walked per group by one sub-group (rows in flight).
 constexpr int kSegUF = EMBTAB_SEG_UF;
+// A run crossing reduction blocks is a short span for k_fixup (one sub-group)
+// when it ends within kShortSpan blocks after the one where it starts (at
+// most SG), else a long span (a whole fixup block).
+constexpr uint32_t kShortSpan = 8;
 
 // The accumulator G is read and written once per touched row per step and
 // read by nothing else, so its rows use non-temporal loads and stores: they
@@ -89,11 +96,10 @@ __device__ __forceinline__ void seg_chunk(
     const uint32_t* __restrict__ keys, const uint32_t* __restrict__ sgr,
     const float* __restrict__ sscale, const float* __restrict__ grad, float* __restrict__ W,
     float* __restrict__ G, uint32_t n, uint32_t sentinel, int32_t D, float lr, float eps,
-    float* __restrict__ part_head, float* __restrict__ part_tail,
-    uint32_t* __restrict__ span_list, uint32_t* __restrict__ long_list,
-    uint32_t* __restrict__ misc, uint32_t nbags, uint32_t* __restrict__ stamps, float log2_rho,
-    uint32_t period, uint32_t c, uint32_t key_bb, uint32_t key_ba, f4* part_lds,
-    uint32_t* slot_key, BlockRun<VEC>& fin) {
+    uint32_t nbags, uint32_t* __restrict__ stamps, float log2_rho, uint32_t period, uint32_t c,
+    uint32_t key_bb, uint32_t key_ba, f4* part_lds,
+    uint32_t* slot_key, f4* in_lds, uint32_t* in_key, f4* out_lds, uint32_t* out_key,
+    BlockRun<VEC>& fin) {
   constexpr int CH = SG * MPL;
   const int lane = threadIdx.x % SG;
   const uint32_t k0 = c * CH;
@@ -102,11 +108,6 @@ __device__ __forceinline__ void seg_chunk(
   const int D4 = D >> 2;
   const uint32_t key_prev = k0 > 0 ? keys[k0 - 1] : kNoRow;
   const uint32_t key_next = k1 < n ? keys[k1] : kNoRow;
-  // First position of chunk c + 1 + SG: a segment that starts here and still
-  // holds it spans more than SG chunks and goes to the long-span list.
-  const uint64_t kfar = (uint64_t)k1 + (uint64_t)SG * CH;
-  const uint32_t key_far = kfar < n ? keys[kfar] : kNoRow;
-  const uint32_t nchunks = (n + CH - 1) / CH;
 
   uint32_t mkey[MPL], mgr[MPL];
   float msc[MPL];
@@ -224,12 +225,10 @@ __device__ __forceinline__ void seg_chunk(
               fin.w[v] = wv[u][v];
               fin.g2[v] = gv[u][v];
             }
-          } else {
+          } else {  // the run entered the block from the previous one
 #pragma unroll
-            for (int v = 0; v < VEC; ++v) {
-              const int d4 = lane + v * SG;
-              if (d4 < D4) *reinterpret_cast<f4*>(part_head + (size_t)c * D + 4 * d4) = acc[v];
-            }
+            for (int v = 0; v < VEC; ++v) in_lds[lane + v * SG] = acc[v];
+            *in_key = kk[u];
           }
 #pragma unroll
           for (int v = 0; v < VEC; ++v) acc[v] = f4{0.f, 0.f, 0.f, 0.f};
@@ -237,18 +236,11 @@ __device__ __forceinline__ void seg_chunk(
 #pragma unroll
           for (int v = 0; v < VEC; ++v) part_lds[lane + v * SG] = acc[v];
           *slot_key = kk[u];
-        } else if (cont[u]) {
-          float* dst = startb[u] ? part_head : part_tail;
+        } else if (cont[u]) {  // the run crosses an edge of the block
+          f4* dst = kk[u] == key_bb ? in_lds : out_lds;
 #pragma unroll
-          for (int v = 0; v < VEC; ++v) {
-            const int d4 = lane + v * SG;
-            if (d4 < D4) *reinterpret_cast<f4*>(dst + (size_t)c * D + 4 * d4) = acc[v];
-          }
-          if (!startb[u] && lane == 0) {
-            const bool lng = key_far == kk[u];
-            const uint32_t slot = atomicAdd(&misc[lng ? kMiscLongCount : kMiscSpanCount], 1u);
-            if (slot < nchunks) (lng ? long_list : span_list)[slot] = c;
-          }
+          for (int v = 0; v < VEC; ++v) dst[lane + v * SG] = acc[v];
+          *(kk[u] == key_bb ? in_key : out_key) = kk[u];
         }
       }
       first_seg = fs;
@@ -268,27 +260,71 @@ __global__ __launch_bounds__(256) void k_seg_adagrad(
     uint32_t period) {
   constexpr int CH = SG * MPL;
   constexpr int SGPB = 256 / SG;
+  constexpr int BP = SGPB * CH;  // sorted positions per block
   __shared__ f4 s_part[SGPB][SG * VEC];
-  __shared__ uint32_t s_key[SGPB];
+  __shared__ f4 s_in[SGPB][SG * VEC];
+  __shared__ f4 s_out[SGPB][SG * VEC];
+  __shared__ uint32_t s_key[SGPB], s_in_key[SGPB], s_out_key[SGPB];
   const int lane = threadIdx.x % SG;
   const int sgb = threadIdx.x / SG;
-  const uint32_t c = blockIdx.x * SGPB + sgb;
-  const uint64_t b0 = (uint64_t)blockIdx.x * SGPB * CH, b1 = b0 + (uint64_t)SGPB * CH;
+  const uint32_t blk = blockIdx.x;
+  const uint32_t c = blk * SGPB + sgb;
+  const uint64_t b0 = (uint64_t)blk * BP, b1 = b0 + (uint64_t)BP;
   const uint32_t key_bb = b0 > 0 ? keys[b0 - 1] : kNoRow;
   const uint32_t key_ba = b1 < n ? keys[b1] : kNoRow;
   BlockRun<VEC> fin;
-  uint32_t slot_key = kNoRow;
+  uint32_t slot_key = kNoRow, in_key = kNoRow, out_key = kNoRow;
   seg_chunk<SG, VEC, MEAN, MPL, UF, DECAY>(keys, sgr, sscale, grad, W, G, n, sentinel, D, lr, eps,
-                                           part_head, part_tail, span_list, long_list, misc,
                                            nbags, stamps, log2_rho, period, c, key_bb, key_ba,
-                                           s_part[sgb], &slot_key, fin);
-  if (lane == 0) s_key[sgb] = slot_key;
+                                           s_part[sgb], &slot_key, s_in[sgb], &in_key,
+                                           s_out[sgb], &out_key, fin);
+  if (lane == 0) {
+    s_key[sgb] = slot_key;
+    s_in_key[sgb] = in_key;
+    s_out_key[sgb] = out_key;
+  }
   __syncthreads();
+  const int D4 = D >> 2;
+  // Runs crossing the block's edges: the block adds its chunks' parts in chunk
+  // order and leaves one part per run, indexed by block: part_head[blk] for
+  // the run that entered from the previous block (the whole block's sum when
+  // the run covers the block), part_tail[blk] for a run that starts here and
+  // continues into the next block, which is listed for k_fixup.
+  if (sgb == 0 && key_bb < sentinel && s_in_key[0] == key_bb) {
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) {
+      const int d4 = lane + v * SG;
+      if (d4 >= D4) continue;
+      f4 tot = s_in[0][lane + v * SG];
+      for (int i = 1; i < SGPB && s_in_key[i] == key_bb; ++i) tot += s_in[i][lane + v * SG];
+      *reinterpret_cast<f4*>(part_head + (size_t)blk * D + 4 * d4) = tot;
+    }
+  }
+  if (sgb == SGPB - 1 && key_ba < sentinel && key_ba != key_bb &&
+      s_out_key[SGPB - 1] == key_ba) {
+    int j = SGPB - 1;
+    while (j > 0 && s_out_key[j - 1] == key_ba) --j;
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) {
+      const int d4 = lane + v * SG;
+      if (d4 >= D4) continue;
+      f4 tot = s_out[j][lane + v * SG];
+      for (int i = j + 1; i < SGPB; ++i) tot += s_out[i][lane + v * SG];
+      *reinterpret_cast<f4*>(part_tail + (size_t)blk * D + 4 * d4) = tot;
+    }
+    if (lane == 0) {
+      // long: the run still covers the last position of block blk + kShortSpan
+      constexpr uint32_t LB = SG < kShortSpan ? SG : kShortSpan;
+      const uint64_t far = ((uint64_t)blk + LB + 1) * BP - 1;
+      const bool lng = far < n && keys[far] == key_ba;
+      const uint32_t slot = atomicAdd(&misc[lng ? kMiscLongCount : kMiscSpanCount], 1u);
+      if (slot < gridDim.x) (lng ? long_list : span_list)[slot] = blk;
+    }
+  }
   if (fin.row == kNoRow) return;
   // chunks c0 .. c-1 of this block hold the run's earlier parts
   int i0 = sgb;
   while (i0 > 0 && s_key[i0 - 1] == fin.row) --i0;
-  const int D4 = D >> 2;
   const float df = DECAY ? decay_factor(fin.last, period, log2_rho) : 1.0f;
   if (DECAY && lane == 0 && period > fin.last) stamps[fin.row] = period;
 #pragma unroll
@@ -306,20 +342,23 @@ __global__ __launch_bounds__(256) void k_seg_adagrad(
   }
 }
 
-// Rows whose occurrences cross chunk boundaries ("spans") are finished by one
-// kernel in two tiers.  A long span (more than SG chunks; Zipf-hot rows) gets
-// a whole block: NT/SG sub-groups each add every (NT/SG)-th head part in chunk
+// Rows whose occurrences cross reduction blocks ("spans") are finished by one
+// kernel in two tiers.  The reduction leaves one part per block: part_tail[b0]
+// in the block where the run starts, part_head[b] in every later block it
+// covers.  A long span (more than kShortSpan blocks; Zipf-hot rows) gets a
+// whole block: NT/SG sub-groups each add every (NT/SG)-th head part in block
 // order, then sub-group 0 adds tail + their sums in sub-group order.  A short
-// span gets one sub-group: lane i tests whether the run ends in chunk
-// c0+1+i, so the end is found with one load per lane, then the tail of c0 and
-// the heads of c0+1 .. c1 are added in chunk order.  Blocks take long spans
-// from the front of the grid and sub-groups of the other blocks take the
-// short spans first; the grid is sized to be resident at once, so the two
-// tiers run side by side.  The last block to finish clears the two span
-// counters, so every call starts from empty lists.
+// span gets one sub-group: lane i tests whether the run ends in block b0+1+i,
+// so the end is found with one load per lane, then the tail of b0 and the
+// heads of b0+1 .. b1 are added in block order.  Blocks take long spans from
+// the front of the grid and sub-groups of the other blocks take the short
+// spans first; the grid is sized to be resident at once, so the two tiers run
+// side by side.  The last block to finish clears the two span counters, so
+// every call starts from empty lists.  BP: sorted positions per reduction
+// block.
 template <int SG, int VEC, int NT, bool DECAY>
 __global__ __launch_bounds__(NT) void k_fixup(
-    const uint32_t* __restrict__ keys, uint32_t n, int32_t CH, float* __restrict__ W,
+    const uint32_t* __restrict__ keys, uint32_t n, int32_t BP, float* __restrict__ W,
     float* __restrict__ G, int32_t D, float lr, float eps, const float* __restrict__ part_head,
     const float* __restrict__ part_tail, const uint32_t* __restrict__ span_list,
     const uint32_t* __restrict__ long_list, uint32_t* __restrict__ misc,
@@ -330,30 +369,30 @@ __global__ __launch_bounds__(NT) void k_fixup(
   const int lane = threadIdx.x % SG;
   const int sgb = threadIdx.x / SG;
   const int D4 = D >> 2;
-  const uint32_t nchunks = (n + (uint32_t)CH - 1) / (uint32_t)CH;
+  const uint32_t nblk = (n + (uint32_t)BP - 1) / (uint32_t)BP;
   uint32_t nlong = misc[kMiscLongCount];
   uint32_t nshort = misc[kMiscSpanCount];
-  nlong = nlong < nchunks ? nlong : nchunks;
-  nshort = nshort < nchunks ? nshort : nchunks;
+  nlong = nlong < nblk ? nlong : nblk;
+  nshort = nshort < nblk ? nshort : nblk;
 
   for (uint32_t sp = blockIdx.x; sp < nlong; sp += gridDim.x) {
     const uint32_t c0 = long_list[sp];
-    const uint32_t row = keys[(c0 + 1) * (uint32_t)CH - 1u];
-    // The chunk where the run ends: the first chunk c > c0 whose successor
-    // position no longer holds `row`.  NT chunks are tested per round.
+    const uint32_t row = keys[(c0 + 1) * (uint32_t)BP - 1u];
+    // The block where the run ends: the first block b > b0 whose successor
+    // position no longer holds `row`.  NT blocks are tested per round.
     if (threadIdx.x == 0) s_end = 0xFFFFFFFFu;
     __syncthreads();
     for (uint32_t cb = c0 + 1;; cb += NT) {
       const uint32_t cc = cb + threadIdx.x;
-      const uint64_t nxt = (uint64_t)(cc + 1) * (uint32_t)CH;
+      const uint64_t nxt = (uint64_t)(cc + 1) * (uint32_t)BP;
       bool ends = false;
-      if ((uint64_t)cc * (uint32_t)CH < n) ends = (nxt >= n) || keys[nxt] != row;
+      if ((uint64_t)cc * (uint32_t)BP < n) ends = (nxt >= n) || keys[nxt] != row;
       if (ends) atomicMin(&s_end, cc);
       __syncthreads();
       const uint32_t e = s_end;
       __syncthreads();
       if (e != 0xFFFFFFFFu) break;
-      if ((uint64_t)(cb + NT) * (uint32_t)CH >= n) break;  // cannot happen for a listed span
+      if ((uint64_t)(cb + NT) * (uint32_t)BP >= n) break;  // cannot happen for a listed span
     }
     const uint32_t c1 = s_end;
     f4 acc[VEC];
@@ -418,11 +457,11 @@ __global__ __launch_bounds__(NT) void k_fixup(
   const uint32_t rb = (blockIdx.x + gridDim.x - nlong % gridDim.x) % gridDim.x;
   for (uint32_t sp = rb * SGPB + sgb; sp < nshort; sp += nsg) {
     const uint32_t c0 = span_list[sp];
-    const uint32_t row = keys[(c0 + 1) * (uint32_t)CH - 1u];  // chunk c0 is full
+    const uint32_t row = keys[(c0 + 1) * (uint32_t)BP - 1u];  // block c0 is full
     const uint32_t cc = c0 + 1 + lane;
-    const uint64_t nxt = (uint64_t)(cc + 1) * (uint32_t)CH;
+    const uint64_t nxt = (uint64_t)(cc + 1) * (uint32_t)BP;
     bool ends = false;
-    if ((uint64_t)cc * (uint32_t)CH < n) ends = (nxt >= n) || keys[nxt] != row;
+    if ((uint64_t)cc * (uint32_t)BP < n) ends = (nxt >= n) || keys[nxt] != row;
     const uint64_t m = (__ballot(ends) >> lane_base) & (SG == 64 ? ~0ull : ((1ull << SG) - 1ull));
     if (m == 0) continue;  // cannot happen for a listed span
     const uint32_t c1 = c0 + 1 + (uint32_t)(__ffsll((unsigned long long)m) - 1);
@@ -473,8 +512,8 @@ __global__ __launch_bounds__(NT) void k_fixup(
 }
 
 template <int SG, int VEC, bool MEAN, bool DECAY>
-hipError_t launch_t(const Handle& h, const Plan& p, const uint32_t* keys, const float* grad_out, float lr, float eps, char* ws, hipStream_t s,
-                    const DecayArgs& dec) {
+hipError_t launch_t(const Handle& h, const Plan& p, const uint32_t* keys, const float* grad_out,
+                    float lr, float eps, char* ws, hipStream_t s, const DecayArgs& dec) {
   constexpr int MPL = chunk_rounds<SG>();
   constexpr int UF = VEC > 1 ? 2 : (SG < kSegUF ? SG : kSegUF);
   constexpr int SGPB = 256 / SG;
@@ -502,12 +541,12 @@ hipError_t launch_t(const Handle& h, const Plan& p, const uint32_t* keys, const 
   if (e != hipSuccess) return e;
   constexpr int FNT = VEC == 1 ? 1024 : (VEC == 2 ? 512 : 256);
   constexpr int FSG = FNT / SG;
-  int64_t fgrid = (chunks + FSG - 1) / FSG;
+  int64_t fgrid = (grid + FSG - 1) / FSG;  // at most one span per reduction block
   const int64_t resident = (int64_t)h.cus * (2048 / FNT);  // 32 waves per CU
   fgrid = fgrid < resident ? fgrid : resident;
   phase_mark(h, EMB_PHASE_FIXUP, false, s);
   hipLaunchKernelGGL((k_fixup<SG, VEC, FNT, DECAY>), dim3((unsigned)fgrid), dim3(FNT), 0, s,
-                     keys, n, SG * MPL, h.W, h.G, h.D, lr, eps, ph, pt, spans, longs, misc,
+                     keys, n, SGPB * SG * MPL, h.W, h.G, h.D, lr, eps, ph, pt, spans, longs, misc,
                      dec.stamps, dec.log2_rho, dec.period);
   phase_mark(h, EMB_PHASE_FIXUP, true, s);
   return hipGetLastError();

@@ -1,7 +1,8 @@
 """Adagrad Decay (per-period accumulator discount) on the GPU against the
 oracle, through the C ABI: rows within the multi-step fp32 bound, each row's
 period bit-exact, untouched rows bit-identical.  Cases cover rows finished
-inside a reduction chunk and rows spanning chunks (the fixup kernel's short
+inside a reduction chunk, rows spanning chunks of one reduction block
+(finished in the block) and rows spanning blocks (the fixup kernel's short
 and long spans), sum and mean pooling, and rows wider than 64 lanes."""
 import numpy as np
 import pytest

@@ -262,8 +262,9 @@ def test_backward_hot_rows_span_many_chunks():
 def test_backward_run_lengths_cross_chunk_boundaries(D, mean):
     # Row r occurs 1 + (r % 97) times, so the runs of the sorted occurrences
     # start and end at every offset of the 32- and 64-position reduction
-    # chunks: runs inside one chunk, across one boundary (finished by the chunk
-    # where they start) and across several (partial sums + fixup).
+    # chunks: runs inside one chunk, across chunk boundaries inside one
+    # reduction block (parts added in LDS by the block) and across block
+    # boundaries (partial sums + fixup).
     nrows = 600
     lens = 1 + np.arange(nrows) % 97
     ids = np.repeat(np.arange(nrows, dtype=np.int64), lens)
