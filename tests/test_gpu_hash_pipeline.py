@@ -1,0 +1,109 @@
+"""The three-stream schedule bench.py runs for hashed tables, against the
+oracle through the C ABI: find-or-insert of batch i+2 on one stream, the
+prepare of batch i+1 on a second, forward and backward of batch i on the
+third, with three workspaces.  New rows handed out by the later hash calls
+are never rows of the batch being trained, so every result equals the
+sequential one: ids bit for bit, pooled outputs and rows within the fp32
+bound."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as orc
+from recommender_embedding_tables_amd import synth
+from tests.helpers import assert_within, forward_S
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+from recommender_embedding_tables_amd import embtab as eb  # noqa: E402
+
+DEV = torch.device("cuda")
+
+
+def _t(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def test_hashed_three_stream_schedule():
+    w = synth.workload(5, T=2, B=3000, universe=60_000, hash_capacity=1 << 17)
+    w.rows = np.full(w.T, int(0.625 * w.hash_capacity), np.int64)
+    steps = 5
+    pool = eb.EMB_POOL_SUM
+    tabs = eb.EmbTables(w.rows, w.D, hashed=True, hash_capacity=w.hash_capacity, seed=9,
+                        init_std=w.init_std, accum_init=w.accum_init)
+    o = orc.Oracle(w.rows, w.D, hashed=True, seed=9, init_std=w.init_std,
+                   accum_init=w.accum_init)
+    host, dev = [], []
+    for b in range(steps):
+        offsets, ranks = synth.gen_batch(w, b)
+        keys = synth.gen_keys(w, offsets, ranks)
+        host.append((offsets, keys))
+        dev.append((_t(offsets), _t(keys.view(np.int64)),
+                    torch.empty(keys.size, dtype=torch.int64, device=DEV)))
+    grads = [synth.gen_grad(w, b) for b in range(steps)]
+    nnz = max(k.size for _, k in host)
+    ws0, need = tabs.workspace(w.B, nnz)
+    wss = [ws0, torch.empty_like(ws0), torch.empty_like(ws0)]
+    outs = [torch.empty((w.B, w.T, w.D), dtype=torch.float32, device=DEV) for _ in range(steps)]
+    main, s_hash, s_prep = torch.cuda.current_stream(), torch.cuda.Stream(), torch.cuda.Stream()
+    hashed = [torch.cuda.Event() for _ in range(steps)]
+    prepared = [torch.cuda.Event() for _ in range(steps)]
+    trained = [torch.cuda.Event() for _ in range(steps)]
+
+    def hash_stage(i):
+        if i >= steps:
+            return
+        if i >= 3:
+            s_hash.wait_event(trained[i - 3])  # batch i - 3 used this workspace
+        d_off, d_keys, d_ids = dev[i]
+        eb.check(eb.emb_hash_find_or_insert(tabs.handle, d_off, d_keys, w.B, d_ids.numel(),
+                                            d_ids, wss[i % 3], need, s_hash), "find_or_insert")
+        hashed[i].record(s_hash)
+
+    def prepare_stage(i):
+        if i >= steps:
+            return
+        s_prep.wait_event(hashed[i])
+        d_off, _, d_ids = dev[i]
+        eb.check(eb.emb_bag_prepare(tabs.handle, d_off, d_ids, w.B, d_ids.numel(), pool,
+                                    wss[i % 3], need, s_prep), "prepare")
+        prepared[i].record(s_prep)
+
+    hash_stage(0)
+    hash_stage(1)
+    prepare_stage(0)
+    for i in range(steps):
+        hash_stage(i + 2)
+        prepare_stage(i + 1)
+        main.wait_event(prepared[i])
+        d_off, _, d_ids = dev[i]
+        eb.check(eb.emb_bag_forward_prepared(tabs.handle, d_off, d_ids, w.B, d_ids.numel(), pool,
+                                             outs[i], wss[i % 3], need, main), "forward")
+        eb.check(eb.emb_bag_backward_adagrad_prepared(tabs.handle, w.B, d_ids.numel(), pool,
+                                                      _t(grads[i]), w.lr, w.eps, wss[i % 3],
+                                                      need, main), "backward")
+        trained[i].record(main)
+    torch.cuda.synchronize()
+
+    for i in range(steps):
+        offsets, keys = host[i]
+        ref_ids, fl = o.find_or_insert(offsets, keys, w.B)
+        assert fl == 0
+        np.testing.assert_array_equal(dev[i][2].cpu().numpy(), ref_ids)
+        ref_out, _ = o.forward(offsets, ref_ids, w.B, False)
+        S = forward_S(offsets, ref_ids, w.B, o.rows, lambda r: o.read_rows(r)[0], False, w.D)
+        assert_within(outs[i].cpu().numpy(), ref_out, S, f"pooled output of step {i}")
+        o.backward_adagrad(offsets, ref_ids, w.B, False, grads[i], w.lr, w.eps)
+    rows = o.touched_rows()
+    Wg = tabs.weights[_t(rows)].cpu().numpy()
+    Gg = tabs.accum[_t(rows)].cpu().numpy()
+    Wr, Gr = o.read_rows(rows)
+    assert_within(Gg, Gr, np.abs(Gr).astype(np.float64) * steps, "accumulator")
+    assert_within(Wg, Wr, np.abs(Wr) + steps * w.lr, "weights")
+    st, n_live = eb.emb_hash_n_live(tabs.handle, w.T)
+    assert st == eb.EMB_OK and list(n_live) == [o.n_live(t) for t in range(w.T)]
+    assert eb.emb_status_sync(tabs.handle) == (eb.EMB_OK, 0)
+    tabs.close()
