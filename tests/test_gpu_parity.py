@@ -286,6 +286,39 @@ def test_backward_run_lengths_cross_chunk_boundaries(D, mean):
     assert status(tabs) == (eb.EMB_OK, 0)
 
 
+@pytest.mark.parametrize("D,mean", [(128, False), (64, True), (256, False), (4, True)])
+def test_backward_runs_aligned_to_reduction_blocks(D, mean):
+    # A reduction block covers BP = 256 * (32 / SG rounded up to 1) sorted
+    # positions (SG = D/4 rounded up to a power of two, at most 64).  Run
+    # lengths of BP, 2 BP, 3 BP and BP +- 1 start and end exactly at block
+    # edges, cover whole blocks (the block's part is the whole sum), or cross
+    # an edge by one position; the short runs between them shift the phase.
+    sg = 1
+    while sg < D // 4 and sg < 64:
+        sg *= 2
+    BP = 256 * max(1, 32 // sg)
+    lens = [BP, 2 * BP, BP - 1, BP + 1, 1, 3 * BP, BP // 2, BP // 2, BP - 1, 2, BP + 1, 7,
+            9 * BP + 3, 1, 1, BP]
+    nrows = len(lens)
+    ids = np.repeat(np.arange(nrows, dtype=np.int64), lens)
+    rng = np.random.default_rng(D + 1)
+    ids = ids[rng.permutation(ids.size)]
+    bag_lens = rng.integers(1, 4, ids.size)
+    ends = np.cumsum(bag_lens)
+    B = int(np.searchsorted(ends, ids.size))
+    offsets = np.concatenate([[0], ends[:B]]).astype(np.int64)
+    offsets[-1] = ids.size
+    grad = rng.standard_normal((B, 1, D)).astype(np.float32)
+    tabs, o = make_pair(np.array([nrows + 3]), D, seed=13)
+    r = check_sort_unique(tabs, o, offsets, ids, B)
+    assert r["num_unique"] == nrows
+    gpu_backward(tabs, offsets, ids, B, mean, grad, 0.01, 1e-8)
+    o.backward_adagrad(offsets, ids, B, mean, grad, 0.01, 1e-8)
+    check_rows(tabs, o, offsets, ids, B, mean, grad, 0.01, 1e-8,
+               extra_rows=np.arange(nrows, nrows + 3))
+    assert status(tabs) == (eb.EMB_OK, 0)
+
+
 def test_backward_one_hot_zipf_two_steps():
     w = synth.workload(2, T=4, B=20000, rows=[100, 3000, 1_000_000, 20])
     tabs, o = make_pair(w.rows, w.D, seed=4)
