@@ -263,8 +263,10 @@ emb_status_t emb_bag_backward_adagrad(emb_table_t h, const int64_t* offsets,
 
 /* The same backward split in two, so that the id-only stages can overlap the
  * forward gather (they need offsets and ids but not grad_out):
- *   emb_bag_prepare                    occurrence keys, stable sort and run
- *                                      heads (unique indexing), left in `ws`;
+ *   emb_bag_prepare                    occurrence keys, stable sort, run
+ *                                      heads and the unique rows, their
+ *                                      segment offsets and the inverse map,
+ *                                      left in `ws`;
  *   emb_bag_backward_adagrad_prepared  segmented reduction + Adagrad from a
  *                                      workspace prepared for the same batch,
  *                                      nnz and pool (same semantics as
@@ -342,9 +344,10 @@ emb_status_t emb_debug_sort_unique(emb_table_t h, const int64_t* offsets, const 
  *   EMB_PHASE_FORWARD  the pooled-gather kernel of emb_bag_forward;
  *   EMB_PHASE_KEYS     occurrence keys of emb_bag_backward_adagrad;
  *   EMB_PHASE_SORT     all radix passes;
- *   EMB_PHASE_UNIQUE   run heads and the unique index of each reduction chunk;
+ *   EMB_PHASE_UNIQUE   run heads, the unique index of each reduction chunk,
+ *                      and unique / seg_off / inverse;
  *   EMB_PHASE_REDUCE   the fused segmented-reduction + Adagrad kernel;
- *   EMB_PHASE_FIXUP    the kernel finishing rows that span reduction chunks;
+ *   EMB_PHASE_FIXUP    the kernel finishing rows that span reduction blocks;
  *   EMB_PHASE_HASH     all of emb_hash_find_or_insert;
  *   EMB_PHASE_CACHE    tiered tables: the kernel of emb_bag_prepare (or of
  *                      the one-call backward) that writes evicted rows back
