@@ -486,7 +486,10 @@ __global__ __launch_bounds__(256) void k_materialize(const uint32_t* __restrict_
                                                      uint32_t* __restrict__ seg_off,
                                                      uint32_t* __restrict__ inverse) {
   __shared__ uint32_t wcnt[4];
-  const uint32_t k = blockIdx.x * 256u + threadIdx.x;
+  // XCD-contiguous blocks: the inverse stores of neighbouring sorted positions
+  // (one table's occurrences, a narrow range of inverse) meet in one L2
+  const uint32_t blk = xcd_block();
+  const uint32_t k = blk * 256u + threadIdx.x;
   const uint32_t lane = threadIdx.x & 63u, wv = threadIdx.x >> 6;
   uint32_t key = sentinel;
   bool head = false;
@@ -497,7 +500,7 @@ __global__ __launch_bounds__(256) void k_materialize(const uint32_t* __restrict_
   const uint64_t m = __ballot(head);
   if (lane == 0) wcnt[wv] = (uint32_t)__popcll(m);
   __syncthreads();
-  uint32_t before = hbase[blockIdx.x];
+  uint32_t before = hbase[blk];
   for (uint32_t i = 0; i < wv; ++i) before += wcnt[i];
   const uint32_t incl = before + lanes_below(m) + (head ? 1u : 0u);
   if (k < n) {
