@@ -253,7 +253,9 @@ __global__ __launch_bounds__(256) void k_sort_scatter(
   const int radix = 1 << nbits;
   const uint32_t mask = (uint32_t)radix - 1u;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const uint32_t tile = blockIdx.x;
+  // XCD-contiguous tiles: a digit's runs from neighbouring tiles share cache
+  // lines of the output, so their partial-line stores meet in one L2
+  const uint32_t tile = xcd_block();
   for (int i = threadIdx.x; i < 4 * kMaxRadix; i += 256) (&whist[0][0])[i] = 0u;
   const uint32_t base = tile * (uint32_t)kSortTile + (uint32_t)w * (kSortItems * 64);
   uint32_t kv[kSortItems], vv[kSortItems], lr[kSortItems];
