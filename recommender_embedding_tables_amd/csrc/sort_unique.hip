@@ -181,7 +181,9 @@ __global__ __launch_bounds__(256) void k_sort_hist(const uint32_t* __restrict__ 
   const uint32_t mask = (uint32_t)radix - 1u;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   for (int i = threadIdx.x; i < 4 * kMaxRadix; i += 256) (&whist[0][0])[i] = 0u;
-  const uint32_t tile = blockIdx.x;
+  // XCD-contiguous tiles: the per-digit counts of neighbouring tiles share
+  // cache lines of tile_hist
+  const uint32_t tile = xcd_block();
   const uint32_t base = tile * (uint32_t)kSortTile + (uint32_t)w * (kSortItems * 64);
   uint32_t kv[kSortItems];
 #pragma unroll
@@ -360,7 +362,8 @@ __global__ __launch_bounds__(256) void k_chunk_heads(const uint32_t* __restrict_
                                                      uint32_t* __restrict__ misc) {
   constexpr int CPB = 256 / CH;
   __shared__ uint32_t s_cnt[CPB];
-  const uint32_t k = blockIdx.x * 256u + threadIdx.x;
+  const uint32_t blk = xcd_block();  // neighbouring blocks' counts share cache lines
+  const uint32_t k = blk * 256u + threadIdx.x;
   bool head = false;
   if (k < n) {
     const uint32_t key = keys[k];
@@ -381,11 +384,11 @@ __global__ __launch_bounds__(256) void k_chunk_heads(const uint32_t* __restrict_
     uint32_t run = 0;
 #pragma unroll
     for (int i = 0; i < CPB; ++i) {
-      const uint32_t c = blockIdx.x * CPB + i;
+      const uint32_t c = blk * CPB + i;
       if (c < nch) cloc[c] = run;
       run += s_cnt[i];
     }
-    btot[blockIdx.x] = run;
+    btot[blk] = run;
   }
 }
 
