@@ -319,6 +319,32 @@ def test_backward_runs_aligned_to_reduction_blocks(D, mean):
     assert status(tabs) == (eb.EMB_OK, 0)
 
 
+@pytest.mark.parametrize("seed", range(10))
+def test_backward_random_sweep(seed):
+    # Random table counts, widths (every sub-group size, and two float4 per
+    # lane), bag lengths with empty bags, and Zipf-skewed ids over small tables,
+    # so that hot runs cross chunks, reduction blocks and many blocks.
+    rng = np.random.default_rng(1000 + seed)
+    T = int(rng.integers(1, 5))
+    D = int(rng.choice([4, 8, 12, 16, 32, 60, 64, 128, 132, 256, 512]))
+    B = int(rng.integers(200, 4000))
+    mean = bool(rng.integers(0, 2))
+    rows = rng.integers(5, 3000, size=T).astype(np.int64)
+    lens = rng.integers(0, 9, size=T * B)
+    offsets = synth.offsets_from_lengths(lens.astype(np.int64))
+    ids = np.empty(int(offsets[-1]), np.int64)
+    for t in range(T):
+        a, b = int(offsets[t * B]), int(offsets[(t + 1) * B])
+        ids[a:b] = synth.zipf_ranks(rng, int(rows[t]), 1.2, b - a)  # rows 0 .. N-1
+    grad = rng.standard_normal((B, T, D)).astype(np.float32)
+    tabs, o = make_pair(rows, D, seed=seed)
+    gpu_backward(tabs, offsets, ids, B, mean, grad, 0.01, 1e-8)
+    assert o.backward_adagrad(offsets, ids, B, mean, grad, 0.01, 1e-8) == 0
+    check_rows(tabs, o, offsets, ids, B, mean, grad, 0.01, 1e-8,
+               extra_rows=np.arange(0, int(rows.sum()), 5))
+    assert status(tabs) == (eb.EMB_OK, 0)
+
+
 def test_backward_one_hot_zipf_two_steps():
     w = synth.workload(2, T=4, B=20000, rows=[100, 3000, 1_000_000, 20])
     tabs, o = make_pair(w.rows, w.D, seed=4)
