@@ -1,10 +1,11 @@
-"""The three-stream schedule bench.py runs for hashed tables, against the
-oracle through the C ABI: find-or-insert of batch i+2 on one stream, the
-prepare of batch i+1 on a second, forward and backward of batch i on the
-third, with three workspaces.  New rows handed out by the later hash calls
-are never rows of the batch being trained, so every result equals the
-sequential one: ids bit for bit, pooled outputs and rows within the fp32
-bound."""
+"""The schedules bench.py runs for hashed tables, against the oracle through
+the C ABI.  Depth 2: find-or-insert of batch i+2 on one stream, the prepare
+of batch i+1 on a second, forward and backward of batch i on the third (three
+workspaces).  Depth 3: find-or-insert of batch i+3, the prepare of batch i+2
+on one of two streams (alternating), forward and backward of batch i (four
+workspaces).  New rows handed out by the later hash calls are never rows of
+the batch being trained, so every result equals the sequential one: ids bit
+for bit, pooled outputs and rows within the fp32 bound."""
 import numpy as np
 import pytest
 import torch
@@ -27,10 +28,12 @@ def _t(a):
     return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
 
 
-def test_hashed_three_stream_schedule():
+@pytest.mark.parametrize("depth", [2, 3])
+def test_hashed_pipelined_schedule(depth):
     w = synth.workload(5, T=2, B=3000, universe=60_000, hash_capacity=1 << 17)
     w.rows = np.full(w.T, int(0.625 * w.hash_capacity), np.int64)
-    steps = 5
+    steps = 6
+    nws = depth + 1
     pool = eb.EMB_POOL_SUM
     tabs = eb.EmbTables(w.rows, w.D, hashed=True, hash_capacity=w.hash_capacity, seed=9,
                         init_std=w.init_std, accum_init=w.accum_init)
@@ -46,9 +49,10 @@ def test_hashed_three_stream_schedule():
     grads = [synth.gen_grad(w, b) for b in range(steps)]
     nnz = max(k.size for _, k in host)
     ws0, need = tabs.workspace(w.B, nnz)
-    wss = [ws0, torch.empty_like(ws0), torch.empty_like(ws0)]
+    wss = [ws0] + [torch.empty_like(ws0) for _ in range(nws - 1)]
     outs = [torch.empty((w.B, w.T, w.D), dtype=torch.float32, device=DEV) for _ in range(steps)]
-    main, s_hash, s_prep = torch.cuda.current_stream(), torch.cuda.Stream(), torch.cuda.Stream()
+    main, s_hash = torch.cuda.current_stream(), torch.cuda.Stream()
+    s_preps = [torch.cuda.Stream(), torch.cuda.Stream()]
     hashed = [torch.cuda.Event() for _ in range(steps)]
     prepared = [torch.cuda.Event() for _ in range(steps)]
     trained = [torch.cuda.Event() for _ in range(steps)]
@@ -56,34 +60,36 @@ def test_hashed_three_stream_schedule():
     def hash_stage(i):
         if i >= steps:
             return
-        if i >= 3:
-            s_hash.wait_event(trained[i - 3])  # batch i - 3 used this workspace
+        if i >= nws:
+            s_hash.wait_event(trained[i - nws])  # batch i - nws used this workspace
         d_off, d_keys, d_ids = dev[i]
         eb.check(eb.emb_hash_find_or_insert(tabs.handle, d_off, d_keys, w.B, d_ids.numel(),
-                                            d_ids, wss[i % 3], need, s_hash), "find_or_insert")
+                                            d_ids, wss[i % nws], need, s_hash), "find_or_insert")
         hashed[i].record(s_hash)
 
     def prepare_stage(i):
         if i >= steps:
             return
+        s_prep = s_preps[i % 2] if depth == 3 else s_preps[0]
         s_prep.wait_event(hashed[i])
         d_off, _, d_ids = dev[i]
         eb.check(eb.emb_bag_prepare(tabs.handle, d_off, d_ids, w.B, d_ids.numel(), pool,
-                                    wss[i % 3], need, s_prep), "prepare")
+                                    wss[i % nws], need, s_prep), "prepare")
         prepared[i].record(s_prep)
 
-    hash_stage(0)
-    hash_stage(1)
-    prepare_stage(0)
+    for j in range(depth):
+        hash_stage(j)
+    for j in range(depth - 1):
+        prepare_stage(j)
     for i in range(steps):
-        hash_stage(i + 2)
-        prepare_stage(i + 1)
+        hash_stage(i + depth)
+        prepare_stage(i + depth - 1)
         main.wait_event(prepared[i])
         d_off, _, d_ids = dev[i]
         eb.check(eb.emb_bag_forward_prepared(tabs.handle, d_off, d_ids, w.B, d_ids.numel(), pool,
-                                             outs[i], wss[i % 3], need, main), "forward")
+                                             outs[i], wss[i % nws], need, main), "forward")
         eb.check(eb.emb_bag_backward_adagrad_prepared(tabs.handle, w.B, d_ids.numel(), pool,
-                                                      _t(grads[i]), w.lr, w.eps, wss[i % 3],
+                                                      _t(grads[i]), w.lr, w.eps, wss[i % nws],
                                                       need, main), "backward")
         trained[i].record(main)
     torch.cuda.synchronize()
