@@ -555,10 +555,14 @@ def test_prepared_backward_on_side_stream_matches_oracle():
     assert status(tabs) == (eb.EMB_OK, 0)
 
 
-@pytest.mark.parametrize("case", ["one_hot", "one_hot_oor", "multi_hot", "with_empty",
-                                  "nnz_equals_bags"])
+@pytest.mark.parametrize("case", ["one_hot", "one_hot_oor", "one_hot_distinct", "multi_hot",
+                                  "with_empty", "nnz_equals_bags"])
 def test_forward_prepared_matches_oracle(case):
-    if case.startswith("one_hot") or case == "nnz_equals_bags":
+    if case == "one_hot_distinct":
+        # uniform ids over large tables: nearly every sorted run is one id
+        w = synth.workload(4, T=2, B=6000, rows=[3_000_000, 3_000_000])
+        mean = False
+    elif case.startswith("one_hot") or case == "nnz_equals_bags":
         w = synth.workload(2, T=4, B=7000, rows=[50, 9000, 1_000_000, 3])
         mean = False
     else:
