@@ -1,0 +1,83 @@
+"""Host-side rules of bench.py, on the CPU: the options it refuses before any
+GPU work, and the algorithmic byte counts its roofline divides by, checked
+against the sizes the workloads fix (output [B, T, D] fp32 written once,
+distinct rows read once, 16 bytes of W and G read and written per element of
+each touched row)."""
+import importlib.util
+import os
+import subprocess
+import sys
+
+import numpy as np
+
+from recommender_embedding_tables_amd import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _bench_module():
+    spec = importlib.util.spec_from_file_location("bench_host", os.path.join(ROOT, "bench.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def _run(*args):
+    return subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *args], cwd=ROOT,
+                          capture_output=True, text=True, timeout=300)
+
+
+def test_more_than_one_gpu_is_refused():
+    r = _run("--gpus", "2")
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""  # no JSON line
+
+
+def test_schedules_that_do_not_fit_the_workload_are_refused():
+    r = _run("--workload", "1", "--schedule", "pipelined4")
+    assert r.returncode == 2 and "hashed tables" in r.stderr
+    r = _run("--workload", "1", "--graph")  # default schedule is pipelined
+    assert r.returncode == 2 and "--graph" in r.stderr
+    r = _run("--workload", "1", "--evict-every", "4", "--schedule", "prepared")
+    assert r.returncode == 2 and "hashed workload" in r.stderr
+
+
+def test_algorithmic_bytes_of_the_26_table_step():
+    bench = _bench_module()
+    w = synth.workload(2)
+    offsets, ids = synth.gen_batch(w, 0)
+    nnz, bags = ids.size, w.T * w.B
+    assert nnz == bags == 1_703_936  # one-hot
+    U = 300_000
+    b = bench.algorithmic_bytes(w, offsets, ids, U)
+    out_bytes = 65536 * 26 * 128 * 4
+    assert out_bytes == 872_415_232
+    csr = (bags + 1) * 8 + nnz * 8
+    # forward: CSR in, each distinct row read once, the output written once
+    assert b["forward"] == csr + U * 128 * 4 + out_bytes
+    # reduction + Adagrad: a sorted key and grad-row index per occurrence, the
+    # upstream gradient read once, W and G read and written for U rows
+    assert b["reduce_adagrad"] == nnz * 8 + out_bytes + U * 128 * 16
+    assert b["step"] == sum(v for k, v in b.items() if k != "step")
+    assert "hash" not in b
+
+
+def test_mean_pooling_adds_the_scale_per_occurrence():
+    bench = _bench_module()
+    w = synth.workload(3, T=2, B=1000)
+    offsets, ids = synth.gen_batch(w, 0)
+    b = bench.algorithmic_bytes(w, offsets, ids, 500)
+    dense = w.B * w.T * w.D * 4
+    assert b["reduce_adagrad"] == ids.size * 12 + dense + 500 * w.D * 16
+
+
+def test_hashed_step_counts_the_key_and_slot_traffic():
+    bench = _bench_module()
+    w = synth.workload(5, T=2, B=1000)
+    offsets, ids = synth.gen_batch(w, 0)
+    U = 4000
+    b = bench.algorithmic_bytes(w, offsets, ids, U)
+    # offsets in, u64 keys in, one 16-byte slot per distinct key, int64 ids out
+    assert b["hash"] == (w.T * w.B + 1) * 8 + ids.size * 8 + U * 16 + ids.size * 8
+    assert np.isclose(b["step"], sum(v for k, v in b.items() if k != "step"))
