@@ -120,7 +120,13 @@ size_t emb_state_bytes(int32_t num_tables);
 size_t emb_hash_bytes(int32_t num_tables, int64_t capacity);
 
 /* Workspace bytes that any call on handle h with `batch` samples and `nnz`
- * occurrences needs (the maximum over all calls).  0 on invalid arguments. */
+ * occurrences needs (the maximum over all calls).  0 on invalid arguments.
+ *
+ * Size limits shared by every call that takes a batch: nnz < 2^32 - 16 and
+ * batch * T < 2^32 - 16, because sorted positions and bag indices are 32-bit on
+ * the device with the top values kept as sentinels.  Outside them a call
+ * returns EMB_ERR_UNSUPPORTED before it enqueues anything, and this function
+ * returns 0. */
 size_t emb_workspace_bytes(emb_table_t h, int64_t batch, int64_t nnz);
 
 /* Create a handle over caller-owned storage.  With init_storage = 1 it enqueues

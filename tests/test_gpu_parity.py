@@ -178,6 +178,41 @@ def test_forward_empty_bags_and_empty_batch():
     assert status(tabs) == (eb.EMB_OK, 0)
 
 
+def test_size_limits_rejected_before_any_launch():
+    # nnz and batch * T must stay below 2^32 - 16; beyond that every call
+    # returns EMB_ERR_UNSUPPORTED from host code, so the small buffers passed
+    # here are never read
+    rows = np.array([50, 60])
+    B = 64
+    tabs, o = make_pair(rows, 8)
+    limit = 0xFFFFFFF0
+    assert eb.emb_workspace_bytes(tabs.handle, B, limit) == 0
+    assert eb.emb_workspace_bytes(tabs.handle, limit // 2, 10) == 0  # batch * T == limit
+    assert eb.emb_workspace_bytes(tabs.handle, B, limit - 1) > 0  # sized, not allocated
+    offsets, ids, _ = synth.random_small(3, 2, 8, B, rows, max_len=3)
+    d_off, d_ids = _t(offsets), _t(ids)
+    out = torch.zeros((B, 2, 8), dtype=torch.float32, device=DEV)
+    grad = torch.zeros_like(out)
+    ws, need = tabs.workspace(B, ids.size)
+    P = eb.EMB_POOL_SUM
+    for batch, nnz in ((B, limit), (limit // 2, ids.size)):
+        assert eb.emb_bag_forward(tabs.handle, d_off, d_ids, batch, nnz, P, out) == \
+            eb.EMB_ERR_UNSUPPORTED
+        assert eb.emb_bag_prepare(tabs.handle, d_off, d_ids, batch, nnz, P, ws, need) == \
+            eb.EMB_ERR_UNSUPPORTED
+        assert eb.emb_bag_forward_prepared(tabs.handle, d_off, d_ids, batch, nnz, P, out, ws,
+                                           need) == eb.EMB_ERR_UNSUPPORTED
+        assert eb.emb_bag_backward_adagrad(tabs.handle, d_off, d_ids, batch, nnz, P, grad, 0.01,
+                                           1e-8, ws, need) == eb.EMB_ERR_UNSUPPORTED
+        assert eb.emb_bag_backward_adagrad_prepared(tabs.handle, batch, nnz, P, grad, 0.01, 1e-8,
+                                                    ws, need) == eb.EMB_ERR_UNSUPPORTED
+    assert status(tabs) == (eb.EMB_OK, 0)
+    # nothing was enqueued: the zeroed output is untouched, and the handle works
+    assert int(torch.count_nonzero(out)) == 0
+    check_forward(tabs, o, offsets, ids, B, False)
+    assert status(tabs) == (eb.EMB_OK, 0)
+
+
 def test_forward_out_of_range_flagged():
     rows = np.array([10, 10])
     offsets = np.array([0, 2, 3, 5, 6], np.int64)  # B = 2
