@@ -20,7 +20,8 @@
 //                   staging of the tile in LDS in digit order, then writes in
 //                   which consecutive lanes store consecutive addresses.
 //   (hist / scan / scatter once per digit; digits of at most 9 bits cover
-//    ceil(log2(total_rows + 1)) key bits, so three passes sort 2^27 rows.)
+//    ceil(log2(total_rows + 1)) key bits, so three passes sort 2^27 rows.
+//    A batch of at most one tile takes the scatter alone per digit.)
 //   k_chunk_heads   run heads per reduction chunk (ballot), and the number of
 //                   valid (in-range) occurrences.
 //   k_chunk_scan    one block: exclusive scan of the chunk head counts, giving
@@ -298,18 +299,22 @@ __global__ __launch_bounds__(256) void k_sort_scatter(
   __syncthreads();
   {
     // Tile-local digit starts and global digit bases (radix <= 512: two per thread).
+    // A single tile's own counts are the digit totals and its offsets are 0,
+    // so the histogram and scan launches are skipped and nothing is read.
+    const bool solo = ntiles == 1u;
     const int d0 = 2 * threadIdx.x, d1 = d0 + 1;
     const uint32_t a0 = d0 < radix ? dstart[d0] : 0u, a1 = d1 < radix ? dstart[d1] : 0u;
-    const uint32_t t0 = d0 < radix ? digit_tot[d0] : 0u, t1 = d1 < radix ? digit_tot[d1] : 0u;
+    const uint32_t t0 = solo ? a0 : (d0 < radix ? digit_tot[d0] : 0u);
+    const uint32_t t1 = solo ? a1 : (d1 < radix ? digit_tot[d1] : 0u);
     const uint32_t ea = block_excl_scan(a0 + a1, nullptr, lds4);
     const uint32_t et = block_excl_scan(t0 + t1, nullptr, lds4);
     if (d0 < radix) {
       dstart[d0] = ea;
-      gbase[d0] = et + tile_off[(size_t)d0 * ntiles + tile];
+      gbase[d0] = et + (solo ? 0u : tile_off[(size_t)d0 * ntiles + tile]);
     }
     if (d1 < radix) {
       dstart[d1] = ea + a0;
-      gbase[d1] = et + t0 + tile_off[(size_t)d1 * ntiles + tile];
+      gbase[d1] = et + t0 + (solo ? 0u : tile_off[(size_t)d1 * ntiles + tile]);
     }
   }
   __syncthreads();
@@ -561,9 +566,12 @@ const Handle& h, const Plan& p, const int64_t* offsets,
   if (n > 0) {
     for (int pass = 0; pass < p.passes; ++pass) {
       const int radix = 1 << p.dbits[pass];
-      hipLaunchKernelGGL(k_sort_hist, dim3(ntiles), dim3(256), 0, s, kin, n, p.shift[pass],
-                         p.dbits[pass], tile_hist, ntiles);
-      hipLaunchKernelGGL(k_sort_scan, dim3(radix), dim3(256), 0, s, tile_hist, ntiles, digit_tot);
+      if (ntiles > 1) {  // a single tile ranks itself inside the scatter
+        hipLaunchKernelGGL(k_sort_hist, dim3(ntiles), dim3(256), 0, s, kin, n, p.shift[pass],
+                           p.dbits[pass], tile_hist, ntiles);
+        hipLaunchKernelGGL(k_sort_scan, dim3(radix), dim3(256), 0, s, tile_hist, ntiles,
+                           digit_tot);
+      }
       const bool last = pass + 1 == p.passes;
       uint32_t* gro = last ? reinterpret_cast<uint32_t*>(ws + p.sgr) : nullptr;
       float* sco = (last && mean) ? reinterpret_cast<float*>(ws + p.sscale) : nullptr;

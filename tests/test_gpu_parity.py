@@ -238,9 +238,26 @@ def test_bad_offsets_flagged_without_fault():
 
 # ----------------------------------------------------------------- sort / unique
 
-@pytest.mark.parametrize("case", ["one_hot_zipf", "multi_hot", "tiny", "single_row", "oor"])
+@pytest.mark.parametrize("case", ["one_hot_zipf", "multi_hot", "tiny", "single_row", "oor",
+                                  "one_tile_full", "one_tile_ragged", "two_tiles"])
 def test_sort_unique_bit_exact(case):
-    if case == "one_hot_zipf":
+    # a batch of at most 4096 ids is one sort tile, ranked by the scatter alone
+    if case == "one_tile_full":  # 4096 one-hot ids, 23-bit keys: three passes
+        w = synth.workload(2, T=2, B=2048, rows=[5_000_000, 40_000])
+        offsets, ids = synth.gen_batch(w)
+        rows, B = w.rows, w.B
+        assert ids.size == 4096
+    elif case == "one_tile_ragged":
+        rows, B = np.array([3_000_000, 9]), 900
+        offsets, ids, _ = synth.random_small(8, 2, 4, B, rows, max_len=3)
+        ids[::13] = 3_000_000  # out of range in either table
+        assert 0 < ids.size < 4096
+    elif case == "two_tiles":
+        w = synth.workload(2, T=1, B=4097, rows=[6_000_000])
+        offsets, ids = synth.gen_batch(w)
+        rows, B = w.rows, w.B
+        assert ids.size == 4097
+    elif case == "one_hot_zipf":
         w = synth.workload(2, T=7, B=9000, rows=[100, 20_000, 3, 7_000_000, 450, 60_000, 1])
         offsets, ids = synth.gen_batch(w)
         rows, B = w.rows, w.B
