@@ -9,6 +9,7 @@ import subprocess
 import sys
 
 import numpy as np
+import pytest
 
 from recommender_embedding_tables_amd import synth
 
@@ -34,6 +35,9 @@ def test_more_than_one_gpu_is_refused():
     assert r.stdout == ""  # no JSON line
 
 
+@pytest.mark.skipif(not os.path.exists(os.path.join(ROOT, "recommender_embedding_tables_amd",
+                                                    "libembtab.so")),
+                    reason="the HIP library is not built")
 def test_schedules_that_do_not_fit_the_workload_are_refused():
     r = _run("--workload", "1", "--schedule", "pipelined4")
     assert r.returncode == 2 and "hashed tables" in r.stderr
