@@ -352,8 +352,11 @@ emb_status_t emb_debug_sort_unique(emb_table_t h, const int64_t* offsets, const 
  *   EMB_PHASE_SORT     all radix passes;
  *   EMB_PHASE_UNIQUE   run heads, the unique index of each reduction chunk,
  *                      and unique / seg_off / inverse;
- *   EMB_PHASE_REDUCE   the fused segmented-reduction + Adagrad kernel;
- *   EMB_PHASE_FIXUP    the kernel finishing rows that span reduction blocks;
+ *   EMB_PHASE_REDUCE   the fused segmented-reduction + Adagrad kernel (which
+ *                      also finishes the rows whose occurrences span its
+ *                      blocks);
+ *   EMB_PHASE_FIXUP    reserved: no events are recorded for it (rows spanning
+ *                      reduction blocks are finished inside the reduction);
  *   EMB_PHASE_HASH     all of emb_hash_find_or_insert;
  *   EMB_PHASE_CACHE    tiered tables: the kernel of emb_bag_prepare (or of
  *                      the one-call backward) that writes evicted rows back

@@ -73,8 +73,9 @@ bool make_plan(const Handle& h, int64_t B, int64_t nnz, Plan* p) {
   const size_t nc = (size_t)(p->nchunks > 0 ? p->nchunks : 1);
   p->part_head = take(sizeof(float) * nc * (size_t)h.D);
   p->part_tail = take(sizeof(float) * nc * (size_t)h.D);
-  p->span_list = take(sizeof(uint32_t) * nc);
-  p->long_list = take(sizeof(uint32_t) * nc);
+  p->span_u = take(sizeof(uint32_t) * (nc + 2));
+  p->span_cnt = take(sizeof(uint32_t) * (nc + 2));
+  p->bp = reduce_block_positions(h.D);
   p->chunk_base = take(sizeof(uint32_t) * (nc + 1));
   p->head_base = take(sizeof(uint32_t) * ((size_t)(nnz + 255) / 256 + 1));
   if (h.hashed) {

@@ -145,6 +145,10 @@ inline int chunk_len(int D) {
   int sg = subgroup_lanes(D);
   return sg >= kChunkMin ? sg : kChunkMin;
 }
+// Sorted positions per reduction block (256 threads: 256 / SG chunks).
+inline uint32_t reduce_block_positions(int D) {
+  return (uint32_t)(chunk_len(D) * (256 / subgroup_lanes(D)));
+}
 
 // ---------------------------------------------------------------- workspace plan
 struct Plan {
@@ -161,7 +165,13 @@ struct Plan {
   size_t tile_hist, digit_tot;
   size_t unique, seg_off, counts, inverse;
   size_t misc;  // uint32[64 + 3T]
-  size_t part_head, part_tail, span_list, long_list;
+  size_t part_head, part_tail;
+  // Runs crossing reduction blocks: span_u[b] = unique index of the run that
+  // crosses the edge before block b (kNoRow: none), from the prepare;
+  // span_cnt[b] = blocks arrived at the span that starts in block b (zeroed
+  // by the prepare, left at zero by the block that finishes the span).
+  size_t span_u, span_cnt;
+  uint32_t bp = 0;  // sorted positions per reduction block
   size_t chunk_base;  // heads in the earlier chunks of the chunk's 256-position block
   size_t head_base;   // heads before each 256-position block (nnz / 256 + 1)
   size_t h_slot, h_first, h_tcnt, h_tb;  // hash find-or-insert
@@ -173,11 +183,8 @@ struct Plan {
 enum : int {
   kMiscNumUnique = 0,
   kMiscNumValid = 1,
-  kMiscSpanCount = 2,
   kMiscHashOverflow = 3,
-  kMiscLongCount = 4,
   kMiscNotOneHot = 5,  // some bag of the prepared batch does not hold exactly one id
-  kMiscFixDone = 6,    // blocks of the span fixup that have finished
   kMiscCacheMiss = 7,  // tiered: misses of this prepare
   kMiscHashNew = 8,  // per table: new keys [T], their base rank [T], block part [T]
 };

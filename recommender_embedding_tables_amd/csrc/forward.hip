@@ -264,7 +264,9 @@ __global__ __launch_bounds__(256) void k_fwd_sorted(
   constexpr int SGPB = 256 / SG;
   constexpr int UF = VEC > 1 ? 2 : (SG < 4 ? SG : 4);
   const uint32_t lane = threadIdx.x % SG;
-  const uint32_t c = xcd_block() * SGPB + threadIdx.x / SG;
+  // Chunks in launch order (no XCD remap): measured faster here, since the
+  // row loads walk W in ascending order across the whole chip at once.
+  const uint32_t c = blockIdx.x * SGPB + threadIdx.x / SG;
   const uint32_t k0 = c * CH;
   if (k0 >= n) return;
   const uint32_t D4 = D >> 2;

@@ -20,13 +20,22 @@
 // order; a finished segment is updated in registers and written back once.
 // A segment that crosses a chunk boundary leaves fp32 part sums in LDS.  If
 // it lies wholly in the block, the chunk where it ends adds them and applies
-// the step after the block barrier.  If it crosses a block edge, the block
-// adds its chunks' parts and leaves one part per block in memory (the "tail"
-// part where it starts, a "head" part in each later block it covers); its
-// start block is appended to one of two span lists, by whether the segment
-// ends within kShortSpan blocks of its start, and k_fixup adds the parts in
-// block order and applies the step.  Every sum has a fixed order, so the
-// result is deterministic and no float atomics are used.
+// the step after the block barrier.  If it crosses a block edge ("span"), the
+// block adds its chunks' parts and leaves one part per block in memory (the
+// "tail" part in the block where it starts, a "head" part in each later
+// block it covers), then counts itself on the span's counter; the last of the
+// span's blocks to arrive adds the parts in block order and applies the step.
+// The prepare has recorded, for every block edge that a run crosses, which
+// run it is, so each block knows how many blocks share its spans.  Every sum
+// has a fixed order, so the result is deterministic and no float atomics are
+// used.
+//
+// The parts are the only data blocks exchange.  They are written through to
+// memory and read past the L2 (agent-scope atomic stores and loads: each XCD
+// has its own L2), and the writer waits for its stores to complete before it
+// counts itself, so the block that finishes a span sees every part without a
+// write-back of whole caches.  (A release/acquire fence per part, which
+// writes back the XCD's L2, was measured to double the kernel's time.)
 //
 // Finishing such a segment inside this kernel, by the sub-group of the chunk
 // where it starts reading on into the next one, was measured slower: the two
@@ -44,10 +53,6 @@ namespace {
 
 // Sorted positions walked per group by one sub-group (rows in flight).
 constexpr int kSegUF = EMBTAB_SEG_UF;
-// A run crossing reduction blocks is a short span for k_fixup (one sub-group)
-// when it ends within kShortSpan blocks after the one where it starts (at
-// most SG), else a long span (a whole fixup block).
-constexpr uint32_t kShortSpan = 8;
 
 // The accumulator G is read and written once per touched row per step and
 // read by nothing else, so its rows use non-temporal loads and stores: they
@@ -57,6 +62,21 @@ constexpr uint32_t kShortSpan = 8;
 __device__ inline void store4_nt(float* __restrict__ base, size_t row, uint32_t D, uint32_t d4,
                                  const f4 x) {
   __builtin_nontemporal_store(x, reinterpret_cast<f4*>(base + row * D + 4u * d4));
+}
+
+// A part of a span, stored and loaded coherently across XCDs (see above).
+__device__ inline void store4_coherent(float* p, const f4 x) {
+  __hip_atomic_store(p + 0, x[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(p + 1, x[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(p + 2, x[2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(p + 3, x[3], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline f4 load4_coherent(const float* p) {
+  float* q = const_cast<float*>(p);
+  return f4{__hip_atomic_load(q + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+            __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+            __hip_atomic_load(q + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+            __hip_atomic_load(q + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)};
 }
 
 __device__ inline void adagrad_step(f4& w, f4& g2, const f4 g, float lr, float eps) {
@@ -79,8 +99,8 @@ __device__ inline float decay_factor(uint32_t last, uint32_t period, float log2_
 // previous one nor leaves it into the next is finished inside the block: the
 // chunk where it ends keeps its own part sum and the row's W and G in
 // registers, the earlier chunks leave their parts in LDS, and after the block
-// barrier it adds them in chunk order (the order of k_fixup) and applies the
-// step.  Only runs that cross a block boundary go to the span lists.
+// barrier it adds them in chunk order and applies the step.  Only runs that
+// cross a block boundary leave parts in memory.
 template <int VEC>
 struct BlockRun {
   uint32_t row = kNoRow;  // kNoRow: this chunk finishes no run of the block
@@ -249,18 +269,84 @@ __device__ __forceinline__ void seg_chunk(
 }
 
 
+// One block's arrival at span [bs, be] of `row` (called by the sub-group
+// that wrote the block's part, after its stores).  The counter of the span's
+// first block counts arrivals; the last of the be - bs + 1 blocks resets it
+// and finishes the row: tail part of bs, then the head parts of bs+1 .. be,
+// added in block order, then the Adagrad step.
+template <int SG, int VEC, bool DECAY>
+__device__ __forceinline__ void span_arrive(
+    uint32_t row, uint32_t bs, uint32_t be, const float* __restrict__ part_head,
+    const float* __restrict__ part_tail, uint32_t* __restrict__ span_cnt, float* __restrict__ W,
+    float* __restrict__ G, int32_t D, float lr, float eps, uint32_t* __restrict__ stamps,
+    float log2_rho, uint32_t period) {
+  const int lane = threadIdx.x % SG;
+  const int D4 = D >> 2;
+  // this wave's part stores have completed (they were written through)
+  __builtin_amdgcn_s_waitcnt(0);
+  uint32_t seen = 0u;
+  if (lane == 0)
+    seen = __hip_atomic_fetch_add(&span_cnt[bs], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  seen = (uint32_t)__shfl((int)seen, 0, SG);
+  if (seen != be - bs) return;  // another block of the span arrives later
+  if (lane == 0) __hip_atomic_store(&span_cnt[bs], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  uint32_t last = 0u;
+  if (DECAY) last = stamps[row];
+  f4 w[VEC], g2[VEC], tot[VEC];
+#pragma unroll
+  for (int v = 0; v < VEC; ++v) {
+    const uint32_t d4 = (uint32_t)(lane + v * SG);
+    const bool ok = d4 < (uint32_t)D4;
+    w[v] = load4_or_zero(W, row, (uint32_t)D, d4, ok);
+    g2[v] = load4_nt_or_zero(G, row, (uint32_t)D, d4, ok);
+    tot[v] = ok ? load4_coherent(part_tail + (size_t)bs * D + 4 * d4) : f4{0.f, 0.f, 0.f, 0.f};
+  }
+  // head parts four blocks at a time, added in block order
+  for (uint32_t c = bs + 1; c <= be; c += 4) {
+    f4 x[4][VEC];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) {
+        const uint32_t d4 = (uint32_t)(lane + v * SG);
+        x[q][v] = (c + q <= be && d4 < (uint32_t)D4)
+                      ? load4_coherent(part_head + (size_t)(c + q) * D + 4 * d4)
+                      : f4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int v = 0; v < VEC; ++v)
+        if (c + q <= be) tot[v] += x[q][v];
+  }
+  float df = 1.0f;
+  if (DECAY) {
+    df = decay_factor(last, period, log2_rho);
+    if (lane == 0 && period > last) stamps[row] = period;
+  }
+#pragma unroll
+  for (int v = 0; v < VEC; ++v) {
+    const int d4 = lane + v * SG;
+    if (d4 >= D4) continue;
+    if (DECAY) g2[v] *= df;
+    adagrad_step(w[v], g2[v], tot[v], lr, eps);
+    *reinterpret_cast<f4*>(W + (size_t)row * D + 4 * d4) = w[v];
+    store4_nt(G, row, (uint32_t)D, (uint32_t)d4, g2[v]);
+  }
+}
+
 template <int SG, int VEC, bool MEAN, int MPL, int UF, bool DECAY>
 __global__ __launch_bounds__(256) void k_seg_adagrad(
     const uint32_t* __restrict__ keys, const uint32_t* __restrict__ sgr,
     const float* __restrict__ sscale, const float* __restrict__ grad, float* __restrict__ W,
     float* __restrict__ G, uint32_t n, uint32_t sentinel, int32_t D, float lr, float eps,
     float* __restrict__ part_head, float* __restrict__ part_tail,
-    uint32_t* __restrict__ span_list, uint32_t* __restrict__ long_list,
-    uint32_t* __restrict__ misc, uint32_t nbags, uint32_t* __restrict__ stamps, float log2_rho,
-    uint32_t period) {
+    const uint32_t* __restrict__ span_u, const uint32_t* __restrict__ seg_off,
+    uint32_t* __restrict__ span_cnt, uint32_t nbags, uint32_t* __restrict__ stamps,
+    float log2_rho, uint32_t period) {
   constexpr int CH = SG * MPL;
   constexpr int SGPB = 256 / SG;
-  constexpr int BP = SGPB * CH;  // sorted positions per block
+  constexpr uint32_t BP = SGPB * CH;  // sorted positions per block
   __shared__ f4 s_part[SGPB][SG * VEC];
   __shared__ f4 s_in[SGPB][SG * VEC];
   __shared__ f4 s_out[SGPB][SG * VEC];
@@ -272,6 +358,10 @@ __global__ __launch_bounds__(256) void k_seg_adagrad(
   const uint64_t b0 = (uint64_t)blk * BP, b1 = b0 + (uint64_t)BP;
   const uint32_t key_bb = b0 > 0 ? keys[b0 - 1] : kNoRow;
   const uint32_t key_ba = b1 < n ? keys[b1] : kNoRow;
+  // The runs crossing this block's edges (unique indices, kNoRow for none),
+  // recorded by the prepare; loaded now, used after the block's walk.
+  const uint32_t sp_in = b0 > 0 ? span_u[blk] : kNoRow;
+  const uint32_t sp_out = b1 < n ? span_u[blk + 1] : kNoRow;
   BlockRun<VEC> fin;
   uint32_t slot_key = kNoRow, in_key = kNoRow, out_key = kNoRow;
   seg_chunk<SG, VEC, MEAN, MPL, UF, DECAY>(keys, sgr, sscale, grad, W, G, n, sentinel, D, lr, eps,
@@ -289,19 +379,23 @@ __global__ __launch_bounds__(256) void k_seg_adagrad(
   // order and leaves one part per run, indexed by block: part_head[blk] for
   // the run that entered from the previous block (the whole block's sum when
   // the run covers the block), part_tail[blk] for a run that starts here and
-  // continues into the next block, which is listed for k_fixup.
-  if (sgb == 0 && key_bb < sentinel && s_in_key[0] == key_bb) {
+  // continues into the next block.  Then it counts itself on the counter of
+  // the span's first block; the last of the span's blocks finishes the row.
+  if (sgb == 0 && key_bb < sentinel && s_in_key[0] == key_bb && sp_in != kNoRow) {
 #pragma unroll
     for (int v = 0; v < VEC; ++v) {
       const int d4 = lane + v * SG;
       if (d4 >= D4) continue;
       f4 tot = s_in[0][lane + v * SG];
       for (int i = 1; i < SGPB && s_in_key[i] == key_bb; ++i) tot += s_in[i][lane + v * SG];
-      *reinterpret_cast<f4*>(part_head + (size_t)blk * D + 4 * d4) = tot;
+      store4_coherent(part_head + (size_t)blk * D + 4 * d4, tot);
     }
+    const uint32_t st = seg_off[sp_in], en = seg_off[sp_in + 1];
+    span_arrive<SG, VEC, DECAY>(key_bb, st / BP, (en - 1) / BP, part_head, part_tail, span_cnt, W,
+                                G, D, lr, eps, stamps, log2_rho, period);
   }
   if (sgb == SGPB - 1 && key_ba < sentinel && key_ba != key_bb &&
-      s_out_key[SGPB - 1] == key_ba) {
+      s_out_key[SGPB - 1] == key_ba && sp_out != kNoRow) {
     int j = SGPB - 1;
     while (j > 0 && s_out_key[j - 1] == key_ba) --j;
 #pragma unroll
@@ -310,16 +404,11 @@ __global__ __launch_bounds__(256) void k_seg_adagrad(
       if (d4 >= D4) continue;
       f4 tot = s_out[j][lane + v * SG];
       for (int i = j + 1; i < SGPB; ++i) tot += s_out[i][lane + v * SG];
-      *reinterpret_cast<f4*>(part_tail + (size_t)blk * D + 4 * d4) = tot;
+      store4_coherent(part_tail + (size_t)blk * D + 4 * d4, tot);
     }
-    if (lane == 0) {
-      // long: the run still covers the last position of block blk + kShortSpan
-      constexpr uint32_t LB = SG < kShortSpan ? SG : kShortSpan;
-      const uint64_t far = ((uint64_t)blk + LB + 1) * BP - 1;
-      const bool lng = far < n && keys[far] == key_ba;
-      const uint32_t slot = atomicAdd(&misc[lng ? kMiscLongCount : kMiscSpanCount], 1u);
-      if (slot < gridDim.x) (lng ? long_list : span_list)[slot] = blk;
-    }
+    const uint32_t en = seg_off[sp_out + 1];
+    span_arrive<SG, VEC, DECAY>(key_ba, blk, (en - 1) / BP, part_head, part_tail, span_cnt, W, G,
+                                D, lr, eps, stamps, log2_rho, period);
   }
   if (fin.row == kNoRow) return;
   // chunks c0 .. c-1 of this block hold the run's earlier parts
@@ -342,175 +431,6 @@ __global__ __launch_bounds__(256) void k_seg_adagrad(
   }
 }
 
-// Rows whose occurrences cross reduction blocks ("spans") are finished by one
-// kernel in two tiers.  The reduction leaves one part per block: part_tail[b0]
-// in the block where the run starts, part_head[b] in every later block it
-// covers.  A long span (more than kShortSpan blocks; Zipf-hot rows) gets a
-// whole block: NT/SG sub-groups each add every (NT/SG)-th head part in block
-// order, then sub-group 0 adds tail + their sums in sub-group order.  A short
-// span gets one sub-group: lane i tests whether the run ends in block b0+1+i,
-// so the end is found with one load per lane, then the tail of b0 and the
-// heads of b0+1 .. b1 are added in block order.  Blocks take long spans from
-// the front of the grid and sub-groups of the other blocks take the short
-// spans first; the grid is sized to be resident at once, so the two tiers run
-// side by side.  The last block to finish clears the two span counters, so
-// every call starts from empty lists.  BP: sorted positions per reduction
-// block.
-template <int SG, int VEC, int NT, bool DECAY>
-__global__ __launch_bounds__(NT) void k_fixup(
-    const uint32_t* __restrict__ keys, uint32_t n, int32_t BP, float* __restrict__ W,
-    float* __restrict__ G, int32_t D, float lr, float eps, const float* __restrict__ part_head,
-    const float* __restrict__ part_tail, const uint32_t* __restrict__ span_list,
-    const uint32_t* __restrict__ long_list, uint32_t* __restrict__ misc,
-    uint32_t* __restrict__ stamps, float log2_rho, uint32_t period) {
-  constexpr int SGPB = NT / SG;
-  __shared__ f4 red[SGPB][SG * VEC];
-  __shared__ uint32_t s_end;
-  const int lane = threadIdx.x % SG;
-  const int sgb = threadIdx.x / SG;
-  const int D4 = D >> 2;
-  const uint32_t nblk = (n + (uint32_t)BP - 1) / (uint32_t)BP;
-  uint32_t nlong = misc[kMiscLongCount];
-  uint32_t nshort = misc[kMiscSpanCount];
-  nlong = nlong < nblk ? nlong : nblk;
-  nshort = nshort < nblk ? nshort : nblk;
-
-  for (uint32_t sp = blockIdx.x; sp < nlong; sp += gridDim.x) {
-    const uint32_t c0 = long_list[sp];
-    const uint32_t row = keys[(c0 + 1) * (uint32_t)BP - 1u];
-    // The block where the run ends: the first block b > b0 whose successor
-    // position no longer holds `row`.  NT blocks are tested per round.
-    if (threadIdx.x == 0) s_end = 0xFFFFFFFFu;
-    __syncthreads();
-    for (uint32_t cb = c0 + 1;; cb += NT) {
-      const uint32_t cc = cb + threadIdx.x;
-      const uint64_t nxt = (uint64_t)(cc + 1) * (uint32_t)BP;
-      bool ends = false;
-      if ((uint64_t)cc * (uint32_t)BP < n) ends = (nxt >= n) || keys[nxt] != row;
-      if (ends) atomicMin(&s_end, cc);
-      __syncthreads();
-      const uint32_t e = s_end;
-      __syncthreads();
-      if (e != 0xFFFFFFFFu) break;
-      if ((uint64_t)(cb + NT) * (uint32_t)BP >= n) break;  // cannot happen for a listed span
-    }
-    const uint32_t c1 = s_end;
-    f4 acc[VEC];
-#pragma unroll
-    for (int v = 0; v < VEC; ++v) acc[v] = f4{0.f, 0.f, 0.f, 0.f};
-    if (c1 != 0xFFFFFFFFu) {
-      uint32_t cc = c0 + 1 + sgb;
-      for (; cc + 3 * SGPB <= c1; cc += 4 * SGPB) {
-        f4 x[4][VEC];
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-          for (int v = 0; v < VEC; ++v) {
-            const int d4 = lane + v * SG;
-            x[q][v] = d4 < D4 ? *reinterpret_cast<const f4*>(part_head + (size_t)(cc + q * SGPB) * D + 4 * d4)
-                              : f4{0.f, 0.f, 0.f, 0.f};
-          }
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-          for (int v = 0; v < VEC; ++v) acc[v] += x[q][v];
-      }
-      for (; cc <= c1; cc += SGPB) {
-#pragma unroll
-        for (int v = 0; v < VEC; ++v) {
-          const int d4 = lane + v * SG;
-          if (d4 < D4) acc[v] += *reinterpret_cast<const f4*>(part_head + (size_t)cc * D + 4 * d4);
-        }
-      }
-    }
-#pragma unroll
-    for (int v = 0; v < VEC; ++v) red[sgb][lane + v * SG] = acc[v];
-    __syncthreads();
-    if (sgb == 0 && c1 != 0xFFFFFFFFu) {
-      float df = 1.0f;
-      if (DECAY) {
-        const uint32_t last = stamps[row];
-        df = decay_factor(last, period, log2_rho);
-        if (lane == 0 && period > last) stamps[row] = period;
-      }
-#pragma unroll
-      for (int v = 0; v < VEC; ++v) {
-        const int d4 = lane + v * SG;
-        if (d4 >= D4) continue;
-        f4 tot = *reinterpret_cast<const f4*>(part_tail + (size_t)c0 * D + 4 * d4);
-        for (int q = 0; q < SGPB; ++q) tot += red[q][lane + v * SG];
-        f4 w = *reinterpret_cast<const f4*>(W + (size_t)row * D + 4 * d4);
-        f4 g2 = __builtin_nontemporal_load(
-            reinterpret_cast<const f4*>(G + (size_t)row * D + 4 * d4));
-        if (DECAY) g2 *= df;
-        adagrad_step(w, g2, tot, lr, eps);
-        *reinterpret_cast<f4*>(W + (size_t)row * D + 4 * d4) = w;
-        store4_nt(G, row, (uint32_t)D, (uint32_t)d4, g2);
-      }
-    }
-    __syncthreads();
-  }
-
-  const int lane_base = (int)(threadIdx.x & 63u) - lane;  // first lane of this sub-group in the wave
-  const uint32_t nsg = gridDim.x * SGPB;
-  // Short spans go first to the blocks without a long span.
-  const uint32_t rb = (blockIdx.x + gridDim.x - nlong % gridDim.x) % gridDim.x;
-  for (uint32_t sp = rb * SGPB + sgb; sp < nshort; sp += nsg) {
-    const uint32_t c0 = span_list[sp];
-    const uint32_t row = keys[(c0 + 1) * (uint32_t)BP - 1u];  // block c0 is full
-    const uint32_t cc = c0 + 1 + lane;
-    const uint64_t nxt = (uint64_t)(cc + 1) * (uint32_t)BP;
-    bool ends = false;
-    if ((uint64_t)cc * (uint32_t)BP < n) ends = (nxt >= n) || keys[nxt] != row;
-    const uint64_t m = (__ballot(ends) >> lane_base) & (SG == 64 ? ~0ull : ((1ull << SG) - 1ull));
-    if (m == 0) continue;  // cannot happen for a listed span
-    const uint32_t c1 = c0 + 1 + (uint32_t)(__ffsll((unsigned long long)m) - 1);
-    float df = 1.0f;
-    if (DECAY) {
-      const uint32_t last = stamps[row];
-      df = decay_factor(last, period, log2_rho);
-      if (lane == 0 && period > last) stamps[row] = period;
-    }
-#pragma unroll
-    for (int v = 0; v < VEC; ++v) {
-      const int d4 = lane + v * SG;
-      if (d4 >= D4) continue;
-      f4 w = *reinterpret_cast<const f4*>(W + (size_t)row * D + 4 * d4);
-      f4 g2 = __builtin_nontemporal_load(
-          reinterpret_cast<const f4*>(G + (size_t)row * D + 4 * d4));
-      if (DECAY) g2 *= df;
-      f4 tot = *reinterpret_cast<const f4*>(part_tail + (size_t)c0 * D + 4 * d4);
-      uint32_t c = c0 + 1;
-      for (; c + 3 <= c1; c += 4) {
-        const f4 x0 = *reinterpret_cast<const f4*>(part_head + (size_t)c * D + 4 * d4);
-        const f4 x1 = *reinterpret_cast<const f4*>(part_head + (size_t)(c + 1) * D + 4 * d4);
-        const f4 x2 = *reinterpret_cast<const f4*>(part_head + (size_t)(c + 2) * D + 4 * d4);
-        const f4 x3 = *reinterpret_cast<const f4*>(part_head + (size_t)(c + 3) * D + 4 * d4);
-        tot += x0;
-        tot += x1;
-        tot += x2;
-        tot += x3;
-      }
-      for (; c <= c1; ++c) tot += *reinterpret_cast<const f4*>(part_head + (size_t)c * D + 4 * d4);
-      adagrad_step(w, g2, tot, lr, eps);
-      *reinterpret_cast<f4*>(W + (size_t)row * D + 4 * d4) = w;
-      store4_nt(G, row, (uint32_t)D, (uint32_t)d4, g2);
-    }
-  }
-
-  // Every block has read the counters (they bound its loops); the last block
-  // to get here clears them for the next call on this workspace.
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t done = atomicAdd(&misc[kMiscFixDone], 1u);
-    if (done == gridDim.x - 1u) {
-      atomicExch(&misc[kMiscSpanCount], 0u);
-      atomicExch(&misc[kMiscLongCount], 0u);
-      atomicExch(&misc[kMiscFixDone], 0u);
-    }
-  }
-}
-
 template <int SG, int VEC, bool MEAN, bool DECAY>
 hipError_t launch_t(const Handle& h, const Plan& p, const uint32_t* keys, const float* grad_out,
                     float lr, float eps, char* ws, hipStream_t s, const DecayArgs& dec) {
@@ -526,29 +446,16 @@ hipError_t launch_t(const Handle& h, const Plan& p, const uint32_t* keys, const 
   float* scale = reinterpret_cast<float*>(ws + p.sscale);
   float* ph = reinterpret_cast<float*>(ws + p.part_head);
   float* pt = reinterpret_cast<float*>(ws + p.part_tail);
-  uint32_t* spans = reinterpret_cast<uint32_t*>(ws + p.span_list);
-  uint32_t* longs = reinterpret_cast<uint32_t*>(ws + p.long_list);
-  uint32_t* misc = reinterpret_cast<uint32_t*>(ws + p.misc);
+  const uint32_t* span_u = reinterpret_cast<const uint32_t*>(ws + p.span_u);
+  const uint32_t* seg_off = reinterpret_cast<const uint32_t*>(ws + p.seg_off);
+  uint32_t* span_cnt = reinterpret_cast<uint32_t*>(ws + p.span_cnt);
   const uint32_t nbags = (uint32_t)(p.B * h.T);
-  hipError_t e;
   phase_mark(h, EMB_PHASE_REDUCE, false, s);
   hipLaunchKernelGGL((k_seg_adagrad<SG, VEC, MEAN, MPL, UF, DECAY>), dim3((unsigned)grid),
                      dim3(256), 0, s, keys, gr, scale, grad_out, h.W, h.G, n,
-                     (uint32_t)h.total_rows, h.D, lr, eps, ph, pt, spans, longs, misc, nbags,
-                     dec.stamps, dec.log2_rho, dec.period);
+                     (uint32_t)h.total_rows, h.D, lr, eps, ph, pt, span_u, seg_off, span_cnt,
+                     nbags, dec.stamps, dec.log2_rho, dec.period);
   phase_mark(h, EMB_PHASE_REDUCE, true, s);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  constexpr int FNT = VEC == 1 ? 1024 : (VEC == 2 ? 512 : 256);
-  constexpr int FSG = FNT / SG;
-  int64_t fgrid = (grid + FSG - 1) / FSG;  // at most one span per reduction block
-  const int64_t resident = (int64_t)h.cus * (2048 / FNT);  // 32 waves per CU
-  fgrid = fgrid < resident ? fgrid : resident;
-  phase_mark(h, EMB_PHASE_FIXUP, false, s);
-  hipLaunchKernelGGL((k_fixup<SG, VEC, FNT, DECAY>), dim3((unsigned)fgrid), dim3(FNT), 0, s,
-                     keys, n, SGPB * SG * MPL, h.W, h.G, h.D, lr, eps, ph, pt, spans, longs, misc,
-                     dec.stamps, dec.log2_rho, dec.period);
-  phase_mark(h, EMB_PHASE_FIXUP, true, s);
   return hipGetLastError();
 }
 

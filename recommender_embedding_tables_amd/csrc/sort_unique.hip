@@ -487,14 +487,18 @@ __global__ __launch_bounds__(256) void k_copy_sorted(const uint32_t* __restrict_
 
 // unique / seg_off / inverse from the sorted keys: position k's unique index
 // is the number of run heads at or before k, minus one (block bases from the
-// scanned head totals).
+// scanned head totals).  At the first position of every reduction block (bp
+// positions each) it also records the run that crosses the block's leading
+// edge (its unique index, or kNoRow) and zeroes the block's span counter.
 __global__ __launch_bounds__(256) void k_materialize(const uint32_t* __restrict__ keys,
                                                      const uint32_t* __restrict__ perm, uint32_t n,
                                                      uint32_t sentinel,
                                                      const uint32_t* __restrict__ hbase,
                                                      uint32_t* __restrict__ unique,
                                                      uint32_t* __restrict__ seg_off,
-                                                     uint32_t* __restrict__ inverse) {
+                                                     uint32_t* __restrict__ inverse, uint32_t bp,
+                                                     uint32_t* __restrict__ span_u,
+                                                     uint32_t* __restrict__ span_cnt) {
   __shared__ uint32_t wcnt[4];
   // XCD-contiguous blocks: the inverse stores of neighbouring sorted positions
   // (one table's occurrences, a narrow range of inverse) meet in one L2
@@ -520,6 +524,10 @@ __global__ __launch_bounds__(256) void k_materialize(const uint32_t* __restrict_
     if (head) {
       unique[u] = key;
       seg_off[u] = k;
+    }
+    if (k % bp == 0u) {
+      span_u[k / bp] = (key < sentinel && !head) ? u : kNoRow;
+      span_cnt[k / bp] = 0u;
     }
   }
 }
@@ -609,7 +617,9 @@ const Handle& h, const Plan& p, const int64_t* offsets,
   if (n > 0)
     hipLaunchKernelGGL(k_materialize, dim3(hgrid), dim3(256), 0, s, kin, vin, n, sentinel, btot,
                        reinterpret_cast<uint32_t*>(ws + p.unique), seg_off,
-                       reinterpret_cast<uint32_t*>(ws + p.inverse));
+                       reinterpret_cast<uint32_t*>(ws + p.inverse), p.bp,
+                       reinterpret_cast<uint32_t*>(ws + p.span_u),
+                       reinterpret_cast<uint32_t*>(ws + p.span_cnt));
   phase_mark(h, EMB_PHASE_UNIQUE, true, s);
   *sorted_keys = kin;
   *sorted_vals = vin;
