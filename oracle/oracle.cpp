@@ -75,6 +75,13 @@
 //    a mean bag's length) and the backward updates nothing, with no error
 //    bit.  A full call admits nothing (keys that would have been admitted get
 //    -1) but every count still advances.  min_count <= 1 is plain insertion.
+//  * A table holds at most slot_limit keys, live or counted (the GPU table
+//    keeps at most 0.9 of its slots in use, so that its probes stay short).
+//    A call whose keys that are neither live nor counted would push a table
+//    past it keeps none of them: it admits nothing, counts no new key, the
+//    counts of already counted keys still advance, and every occurrence of a
+//    key without a row gets -1 (full).  With plain insertion the bound is
+//    never the binding one (rows <= slot_limit).
 //
 //  * Dot interaction (the pages name the operator only; this is the DLRM
 //    model's definition, Naumov et al. 2019): per sample, z_0 = the dense
@@ -169,6 +176,7 @@ struct Model {
   std::vector<std::map<uint64_t, int64_t>> keymap;
   std::vector<std::map<uint64_t, uint64_t>> seen;  // admission: occurrences of keys without a row
   std::vector<int64_t> n_live;                    // rows ever handed out (high-water mark)
+  int64_t slot_limit = INT64_MAX;                 // keys (live or counted) a table may hold
   std::vector<std::deque<int64_t>> free_rows;     // eviction: rows to hand out again, in order
 
   // Rows a call may still hand out in table t, and the next one.
@@ -281,6 +289,14 @@ float orc_init_uniform(uint64_t seed, int64_t t, int64_t row, int64_t d, float l
 }
 float orc_init_normal(uint64_t seed, int64_t t, uint64_t key, int64_t d, float stdv) {
   return normal_value(seed, t, key, d, stdv);
+}
+
+// Keys (live or counted for admission) each hashed table may hold.
+int32_t orc_set_slot_limit(void* h, int64_t limit) {
+  Model* m = static_cast<Model*>(h);
+  if (!m || limit < 1) return -1;
+  m->slot_limit = limit;
+  return 0;
 }
 
 void* orc_create(int64_t T, int64_t D, const int64_t* rows, int32_t hashed, uint64_t seed,
@@ -591,6 +607,31 @@ int32_t orc_hash_find_or_insert_admit(void* h, const int64_t* offsets, const uin
   if (!m->hashed) return -1;
   if (!offsets_ok(offsets, bags, nnz)) return 2;
   int32_t flags = 0;
+  // Pass 0: keys that are neither live nor counted; would they overfill a table?
+  bool over = false;
+  for (int64_t t = 0; t < T; ++t) {
+    std::set<uint64_t> unknown;
+    for (int64_t j = offsets[t * B]; j < offsets[(t + 1) * B]; ++j) {
+      const uint64_t key = keys[j];
+      if (key == kReservedKey || m->keymap[t].count(key) || m->seen[t].count(key)) continue;
+      unknown.insert(key);
+    }
+    const int64_t held = (int64_t)(m->keymap[t].size() + m->seen[t].size());
+    if (held + (int64_t)unknown.size() > m->slot_limit) over = true;
+  }
+  if (over) {
+    for (int64_t t = 0; t < T; ++t)
+      for (int64_t j = offsets[t * B]; j < offsets[(t + 1) * B]; ++j) {
+        const uint64_t key = keys[j];
+        if (key == kReservedKey) { flags |= 4; ids_out[j] = -1; continue; }
+        auto it = m->keymap[t].find(key);
+        if (it != m->keymap[t].end()) { ids_out[j] = it->second; continue; }
+        auto c = m->seen[t].find(key);
+        if (c != m->seen[t].end()) ++c->second;
+        ids_out[j] = -1;
+      }
+    return flags | 8;
+  }
   // Pass 1: counts of keys without a row advance; which of them reach min_count?
   std::vector<std::set<uint64_t>> admitted(T);
   bool full = false;

@@ -39,6 +39,7 @@ def _load():
         "orc_init_normal": (f32, [u64, i64, u64, i64, f32]),
         "orc_create": (P, [i64, i64, P, i32, u64, f32, f32, f32, f32]),
         "orc_destroy": (None, [P]),
+        "orc_set_slot_limit": (i32, [P, i64]),
         "orc_set_dense": (i32, [P, P, P]),
         "orc_forward": (i32, [P, P, P, i64, i64, i32, P]),
         "orc_sort_unique": (i32, [P, P, P, i64, i64, P, P, P, P, P, P, P]),
@@ -95,7 +96,7 @@ class Oracle:
     """Sequential model of a set of T tables of dim D (dense or hashed)."""
 
     def __init__(self, rows_per_table, dim, hashed=False, seed=0, init_lo=-0.05,
-                 init_hi=0.05, init_std=0.01, accum_init=0.1):
+                 init_hi=0.05, init_std=0.01, accum_init=0.1, slot_limit=None):
         lib = _load()
         self.rows = _arr(rows_per_table, np.int64)
         self.T = int(self.rows.size)
@@ -106,6 +107,8 @@ class Oracle:
                                  init_lo, init_hi, init_std, accum_init)
         if not self._h:
             raise ValueError("oracle: bad table description")
+        if slot_limit is not None and lib.orc_set_slot_limit(self._h, int(slot_limit)) != 0:
+            raise ValueError("oracle: bad slot limit")
 
     def close(self):
         if self._h:

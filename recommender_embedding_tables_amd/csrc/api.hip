@@ -56,7 +56,7 @@ bool make_plan(const Handle& h, int64_t B, int64_t nnz, Plan* p) {
     o += align_up(bytes);
     return at;
   };
-  p->misc = take(sizeof(uint32_t) * (64 + 3 * (size_t)h.T));
+  p->misc = take(sizeof(uint32_t) * misc_words(h.T));
   p->keysA = take(n4);
   p->valsA = take(n4);
   p->keysB = take(n4);
@@ -83,8 +83,9 @@ bool make_plan(const Handle& h, int64_t B, int64_t nnz, Plan* p) {
     p->h_first = take(n4);
     p->h_tcnt = take(sizeof(uint32_t) * (size_t)((nnz + 255) / 256 + 1));
     p->h_tb = take(sizeof(int64_t) * (size_t)(h.T + 1));
+    p->h_fresh = take((size_t)(nnz > 0 ? nnz : 1));
   } else {
-    p->h_slot = p->h_first = p->h_tcnt = p->h_tb = 0;
+    p->h_slot = p->h_first = p->h_tcnt = p->h_tb = p->h_fresh = 0;
   }
   if (h.tiered) {
     p->c_slot = take(n4);       // cache slot of each distinct row
@@ -223,7 +224,7 @@ static emb_status_t create_impl(const emb_table_desc_t* d, const emb_tier_desc_t
   hipError_t e = hipSuccess;
   if (d->init_storage) {
     // state: flags 0, row offsets, capacities, live rows 0
-    std::vector<int64_t> host(5 * (size_t)h.T + 1, 0);  // + free-row queues, empty
+    std::vector<int64_t> host(6 * (size_t)h.T + 1, 0);  // + free-row queues, slots: empty
     for (int t = 0; t <= h.T; ++t) host[t] = h.row_off[t];
     for (int t = 0; t < h.T; ++t) host[h.T + 1 + t] = h.rows[t];
     e = hipMemsetAsync(h.sv.flags, 0, 256, s);

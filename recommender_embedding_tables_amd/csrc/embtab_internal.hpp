@@ -33,7 +33,7 @@ constexpr int kMaxRadix = 1 << kMaxDigitBits;
 
 // ---------------------------------------------------------------- state buffer
 // [0, 256): uint32 error word (+ padding); then int64 row_off[T+1], rows[T],
-// n_live[T].
+// n_live[T], q_head[T], q_tail[T], slots_used[T].
 struct StateView {
   uint32_t* flags;
   int64_t* row_off;
@@ -44,10 +44,13 @@ struct StateView {
   // (a ring: at most rows[t] rows are free at once).
   int64_t* q_head;
   int64_t* q_tail;
+  // Hashed tables: slots holding a key (live keys and keys counted for
+  // admission), bounded by kMaxSlotLoad of the capacity.
+  int64_t* slots_used;
 };
 
 inline size_t state_bytes(int T) {
-  size_t b = 256 + sizeof(int64_t) * (size_t)(5 * T + 1);
+  size_t b = 256 + sizeof(int64_t) * (size_t)(6 * T + 1);
   return (b + 255) & ~(size_t)255;
 }
 
@@ -60,6 +63,7 @@ inline StateView state_view(void* state, int T) {
   v.n_live = v.rows + T;
   v.q_head = v.n_live + T;
   v.q_tail = v.q_head + T;
+  v.slots_used = v.q_tail + T;
   return v;
 }
 
@@ -174,7 +178,7 @@ struct Plan {
   uint32_t bp = 0;  // sorted positions per reduction block
   size_t chunk_base;  // heads in the earlier chunks of the chunk's 256-position block
   size_t head_base;   // heads before each 256-position block (nnz / 256 + 1)
-  size_t h_slot, h_first, h_tcnt, h_tb;  // hash find-or-insert
+  size_t h_slot, h_first, h_tcnt, h_tb, h_fresh;  // hash find-or-insert
   size_t c_slot, c_miss, c_vict, c_mslot, c_rowmap;  // tiered: cache lookup
   size_t total = 0;
 };
@@ -183,11 +187,23 @@ struct Plan {
 enum : int {
   kMiscNumUnique = 0,
   kMiscNumValid = 1,
+  kMiscHashAbort = 2,  // the hash call's offsets are invalid: it inserts nothing
   kMiscHashOverflow = 3,
   kMiscNotOneHot = 5,  // some bag of the prepared batch does not hold exactly one id
   kMiscCacheMiss = 7,  // tiered: misses of this prepare
-  kMiscHashNew = 8,  // per table: new keys [T], their base rank [T], block part [T]
+  kMiscHashSlotFull = 4,  // the call's new keys would exceed a table's slot bound
+  // per table: new keys [T], their base rank [T], block part [T + 1], then
+  // the slots this call claimed [T] (at kMiscHashNew + 3T + 1)
+  kMiscHashNew = 8,
 };
+inline size_t misc_words(int T) { return 64 + 4 * (size_t)T + 8; }
+
+// A hashed table keeps at most this share of its slots holding keys (live or
+// counted for admission); linear probes then stay short.
+constexpr double kMaxSlotLoad = 0.9;
+// Probes per occurrence before a call is declared full (reached only if the
+// slot bound above failed to hold).
+constexpr int64_t kMaxProbe = 8192;
 
 bool make_plan(const Handle& h, int64_t B, int64_t nnz, Plan* p);
 

@@ -34,6 +34,16 @@
 // Row assignment follows first occurrence and is deterministic; which slot a
 // key lands in depends on CAS order and is not part of the contract.
 //
+// Calls that cannot be kept are undone whole (all-or-nothing):
+//   * rows: a table's new keys exceed its free rows (full);
+//   * slots: the keys holding a table's slots (live keys and keys counted for
+//     admission) would exceed kMaxSlotLoad of its capacity (full);
+//   * offsets: the CSR offsets do not start at 0, end at nnz and rise (bad
+//     offsets); such a call leaves even the admission counts as they were.
+// Slots claimed by the call are emptied again, so probe sequences stay short:
+// a probe walks at most kMaxProbe slots, and reaching that bound also makes
+// the call full.
+//
 // Frequency admission (DeepRec page, section "model quality", EmbeddingVariable
 // item 1: features are admitted before they get a row).  With a count array
 // and min_count > 1, a key's slot also counts its occurrences (one atomicAdd
@@ -71,15 +81,32 @@ __device__ inline void load_table_bounds(int64_t* tb, const int64_t* __restrict_
   __syncthreads();
 }
 
+// Tables are the occurrence ranges [tb[t], tb[t+1]) with tb[0] = 0 and
+// tb[T] = nnz, so every occurrence belongs to exactly one table whatever the
+// offsets hold; offsets that do not start at 0, end at nnz and rise at the
+// table starts mark the call aborted (k_hash_probe checks the other bags).
 __global__ __launch_bounds__(256) void k_hash_start(const int64_t* __restrict__ offsets, int64_t B,
                                                     int32_t T, int64_t nnz,
                                                     int64_t* __restrict__ tbw,
-                                                    uint32_t* __restrict__ misc, int32_t nzero) {
+                                                    uint32_t* __restrict__ misc, int32_t nzero,
+                                                    uint32_t* __restrict__ flags) {
   extern __shared__ int64_t tb[];
+  __shared__ uint32_t s_bad;
+  if (threadIdx.x == 0) s_bad = 0u;
   for (int i = threadIdx.x; i < nzero; i += blockDim.x) misc[i] = 0u;
+  __syncthreads();
   for (int t = threadIdx.x; t <= T; t += blockDim.x) {
     const int64_t v = offsets[(int64_t)t * B];
+    if ((t == 0 && v != 0) || (t == T && v != nnz)) s_bad = 1u;
     tb[t] = v < 0 ? 0 : (v > nnz ? nnz : v);
+  }
+  __syncthreads();
+  for (int t = threadIdx.x + 1; t <= T; t += blockDim.x)
+    if (tb[t] < tb[t - 1]) s_bad = 1u;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    tb[0] = 0;
+    tb[T] = nnz;
   }
   __syncthreads();
   for (int o = 1; o <= T; o <<= 1) {  // running maximum, log-step (T + 1 <= 1025)
@@ -93,6 +120,15 @@ __global__ __launch_bounds__(256) void k_hash_start(const int64_t* __restrict__ 
     __syncthreads();
   }
   for (int t = threadIdx.x; t <= T; t += blockDim.x) tbw[t] = tb[t];
+  if (threadIdx.x == 0 && s_bad) {
+    misc[kMiscHashAbort] = 1u;
+    atomicOr(flags, EMB_FLAG_BAD_OFFSETS);
+  }
+}
+
+// misc word of the number of slots table t's keys claimed in this call.
+__device__ inline uint32_t misc_fresh(int32_t T, int32_t t) {
+  return (uint32_t)(kMiscHashNew + 3 * T + 1 + t);
 }
 
 struct Slot {
@@ -104,11 +140,23 @@ __global__ __launch_bounds__(256) void k_hash_probe(
     const int64_t* __restrict__ tbw, const uint64_t* __restrict__ keys, int64_t B, int32_t T,
     int64_t nnz, Slot* __restrict__ slots, int64_t cap, int64_t* __restrict__ ids_out,
     uint32_t* __restrict__ slot_of, uint32_t* __restrict__ flags, uint32_t* __restrict__ misc,
-    uint32_t* __restrict__ counts) {
+    uint32_t* __restrict__ counts, const int64_t* __restrict__ offsets,
+    uint8_t* __restrict__ fresh_of) {
   extern __shared__ int64_t tb[];
   load_table_bounds(tb, tbw, T);
   const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  {
+    // the bags' offsets rise (the ends and table starts are k_hash_start's)
+    bool bad = false;
+    const int64_t nbags = (int64_t)T * B, stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t b = j; b < nbags; b += stride) bad = bad || offsets[b + 1] < offsets[b];
+    if (__ballot(bad) != 0ull && (threadIdx.x & 63u) == 0u) {
+      misc[kMiscHashAbort] = 1u;
+      atomicOr(flags, EMB_FLAG_BAD_OFFSETS);
+    }
+  }
   if (j >= nnz) return;
+  fresh_of[j] = 0;
   const uint64_t key = keys[j];
   if (key == kEmptyKey) {
     ids_out[j] = -1;
@@ -134,12 +182,16 @@ __global__ __launch_bounds__(256) void k_hash_probe(
     }
     if (sl.key == kEmptyKey || sl.key == key) break;
   }
-  for (; probe < cap; ++probe, s = (s + 1) & mask) {
+  for (; probe < cap && probe < kMaxProbe; ++probe, s = (s + 1) & mask) {
     uint64_t k = __hip_atomic_load(&st[s].key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (k == kEmptyKey) {
       const uint64_t old = atomicCAS((unsigned long long*)&st[s].key, (unsigned long long)kEmptyKey,
                                      (unsigned long long)key);
       k = (old == kEmptyKey) ? key : old;
+      if (old == kEmptyKey) {  // this occurrence claimed the slot: one per new key
+        fresh_of[j] = 1;
+        atomicAdd(&misc[misc_fresh(T, t)], 1u);
+      }
     }
     if (k != key) continue;
     const uint64_t r = __hip_atomic_load(&st[s].row, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -153,7 +205,7 @@ __global__ __launch_bounds__(256) void k_hash_probe(
     }
     return;
   }
-  // every slot of the table is taken: the call cannot insert
+  // no free slot within kMaxProbe (or none at all): the call cannot insert
   slot_of[j] = kNoSlot;
   ids_out[j] = -1;
   misc[kMiscHashOverflow] = 1u;
@@ -220,10 +272,12 @@ __global__ __launch_bounds__(1024) void k_hash_plan(uint32_t* __restrict__ bcnt,
                                                     const int64_t* __restrict__ q_head,
                                                     const int64_t* __restrict__ q_tail,
                                                     uint32_t* __restrict__ misc,
-                                                    uint32_t* __restrict__ flags) {
+                                                    uint32_t* __restrict__ flags,
+                                                    const int64_t* __restrict__ slots_used,
+                                                    int64_t slot_limit) {
   constexpr uint32_t PER = 16;
   __shared__ uint32_t wsum[16];
-  __shared__ uint32_t s_full;
+  __shared__ uint32_t s_full, s_slot;
   uint32_t carry = 0;
   const uint32_t lane = threadIdx.x & 63u, w = threadIdx.x >> 6;
   for (uint32_t base = 0; base < nblocks; base += 1024u * PER) {
@@ -280,7 +334,10 @@ __global__ __launch_bounds__(1024) void k_hash_plan(uint32_t* __restrict__ bcnt,
     carry += total;
   }
   __syncthreads();  // the bases written above are read back below
-  if (threadIdx.x == 0) s_full = misc[kMiscHashOverflow];
+  if (threadIdx.x == 0) {
+    s_full = misc[kMiscHashOverflow];
+    s_slot = 0u;
+  }
   __syncthreads();
   // table t's first occurrences have ranks [base_t, base_{t+1}) among this
   // call's first occurrences, in occurrence (and so table) order
@@ -296,12 +353,17 @@ __global__ __launch_bounds__(1024) void k_hash_plan(uint32_t* __restrict__ bcnt,
     misc[kMiscHashNew + T + t] = b0;
     // rows left: queued free rows, then rows never used
     if ((int64_t)nw > q_tail[t] - q_head[t] + rows[t] - n_live[t]) s_full = 1u;  // all store 1
+    // slots: the keys already holding one, and the slots this call claimed
+    if (slots_used[t] + (int64_t)misc[misc_fresh(T, t)] > slot_limit) s_slot = 1u;
   }
   __syncthreads();
   if (threadIdx.x == 0) {
-    misc[kMiscHashOverflow] = s_full;
+    const uint32_t abort_call = misc[kMiscHashAbort];
+    const uint32_t drop = s_slot | abort_call;  // keep none of the claimed slots
+    misc[kMiscHashOverflow] = s_full | drop;
+    misc[kMiscHashSlotFull] = drop;
     misc[kMiscNumUnique] = carry;  // new keys of this call (all tables)
-    if (s_full) atomicOr(flags, EMB_FLAG_TABLE_FULL);
+    if ((s_full | s_slot) && !abort_call) atomicOr(flags, EMB_FLAG_TABLE_FULL);
   }
 }
 
@@ -374,24 +436,49 @@ __global__ __launch_bounds__(256) void k_hash_finish(
     const uint32_t* __restrict__ counts, uint32_t min_count,
     const int64_t* __restrict__ row_off, const int64_t* __restrict__ rows, float* __restrict__ W,
     float* __restrict__ G, int32_t D,
-    uint64_t seed, float stdv, float g0, uint32_t nfin) {
+    uint64_t seed, float stdv, float g0, uint32_t nfin, Slot* __restrict__ wslots,
+    const uint8_t* __restrict__ fresh_of, int64_t* __restrict__ slots_used,
+    uint32_t* __restrict__ wcounts) {
   extern __shared__ int64_t tb[];
   load_table_bounds(tb, tbw, T);
   const bool full = misc[kMiscHashOverflow] != 0u;
+  // slot bound exceeded or bad offsets: none of the claimed slots is kept
+  const bool drop = misc[kMiscHashSlotFull] != 0u;
   if (blockIdx.x < nfin) {
-    if (blockIdx.x == 0 && !full)
+    if (blockIdx.x == 0) {
       for (int t = threadIdx.x; t < T; t += blockDim.x) {
-        const int64_t nw = (int64_t)misc[kMiscHashNew + t];
-        const int64_t queued = q_tail[t] - q_head[t];
-        const int64_t take = nw < queued ? nw : queued;
-        q_head[t] += take;
-        n_live[t] += nw - take;
+        if (!full) {
+          const int64_t nw = (int64_t)misc[kMiscHashNew + t];
+          const int64_t queued = q_tail[t] - q_head[t];
+          const int64_t take = nw < queued ? nw : queued;
+          q_head[t] += take;
+          n_live[t] += nw - take;
+        }
+        // the claimed slots stay: as rows, or as counted keys (a full call
+        // with admission keeps its would-be keys counted)
+        if (!drop && (!full || counts)) slots_used[t] += (int64_t)misc[misc_fresh(T, t)];
       }
+    }
     const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (j >= nnz) return;
     const uint32_t s = slot_of[j];
     if (s == kNoSlot) return;
     const int32_t t = table_of(tb, T, j);
+    if (drop) {
+      ids_out[j] = -1;
+      const bool aborted = misc[kMiscHashAbort] != 0u;
+      uint32_t* cnt = counts ? wcounts + (size_t)t * (size_t)cap + s : nullptr;
+      // bad offsets: every occurrence takes back its count (a claimed slot's
+      // count returns to 0); slot bound: only the claimed slots' counts go
+      if (cnt && aborted) atomicSub(cnt, 1u);
+      if (fresh_of[j]) {  // this occurrence claimed the slot: empty it again
+        Slot* sl = wslots + (size_t)t * (size_t)cap + s;
+        sl->key = kEmptyKey;
+        sl->row = kUnsetRow;
+        if (cnt && !aborted) *cnt = 0u;
+      }
+      return;
+    }
     if (full) {  // keys that would have got a row: -1; keys still counted: absent
       ids_out[j] = admitted(counts, min_count, cap, slot_of, t, j) ? -1 : kAbsentId;
       return;
@@ -606,8 +693,15 @@ __global__ __launch_bounds__(256) void k_evict_scatter(
 }
 
 __global__ __launch_bounds__(256) void k_evict_finish(const uint32_t* __restrict__ tbase,
-                                                      int32_t T, int64_t* __restrict__ q_tail) {
-  for (int32_t t = threadIdx.x; t < T; t += 256) q_tail[t] += (int64_t)(tbase[t + 1] - tbase[t]);
+                                                      int32_t T, int64_t* __restrict__ q_tail,
+                                                      const int64_t* __restrict__ q_head,
+                                                      const int64_t* __restrict__ n_live,
+                                                      int64_t* __restrict__ slots_used) {
+  for (int32_t t = threadIdx.x; t < T; t += 256) {
+    q_tail[t] += (int64_t)(tbase[t + 1] - tbase[t]);
+    // the slot arrays now hold the live keys only (counted keys were dropped)
+    slots_used[t] = n_live[t] - (q_tail[t] - q_head[t]);
+  }
 }
 
 }  // namespace
@@ -627,15 +721,19 @@ hipError_t launch_hash_find_or_insert(const Handle& h, const Plan& p, const int6
   const unsigned grid = nb > 0 ? nb : 1;
   phase_mark(h, EMB_PHASE_HASH, false, s);
   int64_t* tbw = reinterpret_cast<int64_t*>(ws + p.h_tb);
+  uint8_t* fresh_of = reinterpret_cast<uint8_t*>(ws + p.h_fresh);
   hipLaunchKernelGGL(k_hash_start, dim3(1), dim3(256), shm, s, offsets, p.B, h.T, nnz, tbw, misc,
-                     kMiscHashNew + 2 * h.T);
+                     kMiscHashNew + 4 * h.T + 1, h.sv.flags);
   hipLaunchKernelGGL(k_hash_probe, dim3(grid), dim3(256), shm, s, tbw, keys, p.B, h.T, nnz,
-                     slots, h.capacity, ids_out, slot_of, h.sv.flags, misc, counts);
+                     slots, h.capacity, ids_out, slot_of, h.sv.flags, misc, counts, offsets,
+                     fresh_of);
   uint32_t* tpart = misc + kMiscHashNew + 2 * h.T;
   hipLaunchKernelGGL(k_hash_first, dim3(grid), dim3(256), shm, s, tbw, p.B, h.T, nnz, slots,
                      h.capacity, slot_of, bcnt, tpart, counts, adm.min_count);
+  const int64_t slot_limit = (int64_t)(kMaxSlotLoad * (double)h.capacity);
   hipLaunchKernelGGL(k_hash_plan, dim3(1), dim3(1024), 0, s, bcnt, nb, tbw, h.T, nnz, tpart,
-                     h.sv.n_live, h.sv.rows, h.sv.q_head, h.sv.q_tail, misc, h.sv.flags);
+                     h.sv.n_live, h.sv.rows, h.sv.q_head, h.sv.q_tail, misc, h.sv.flags,
+                     h.sv.slots_used, slot_limit);
   hipLaunchKernelGGL(k_hash_assign, dim3(grid), dim3(256), shm, s, tbw, p.B, h.T, nnz, slots,
                      h.capacity, slot_of, bcnt, h.sv.n_live, misc, newlist, counts,
                      adm.min_count, h.free_rows, h.sv.row_off, h.sv.rows, h.sv.q_head,
@@ -647,7 +745,7 @@ hipError_t launch_hash_find_or_insert(const Handle& h, const Plan& p, const int6
                      keys, p.B, h.T, nnz, slots, h.capacity, slot_of, ids_out, newlist, misc,
                      h.sv.n_live, h.sv.q_head, h.sv.q_tail, counts, adm.min_count,
                      h.sv.row_off, h.sv.rows, h.W, h.G, h.D, h.seed, h.stdv,
-                     h.accum0, grid);
+                     h.accum0, grid, slots, fresh_of, h.sv.slots_used, counts);
   phase_mark(h, EMB_PHASE_HASH, true, s);
   return hipGetLastError();
 }
@@ -705,7 +803,8 @@ hipError_t launch_hash_evict(const Handle& h, const uint32_t* last_used, uint32_
   hipLaunchKernelGGL(k_evict_scatter, dim3((unsigned)p.nblocks), dim3(256), 0, s, flag,
                      h.total_rows, bcnt, h.sv.row_off, h.sv.rows, h.T, tbase, h.sv.q_tail,
                      h.free_rows);
-  hipLaunchKernelGGL(k_evict_finish, dim3(1), dim3(256), 0, s, tbase, h.T, h.sv.q_tail);
+  hipLaunchKernelGGL(k_evict_finish, dim3(1), dim3(256), 0, s, tbase, h.T, h.sv.q_tail,
+                     h.sv.q_head, h.sv.n_live, h.sv.slots_used);
   e = hipGetLastError();
   if (e == hipSuccess && key_counts)  // every counted key was dropped with its slot
     e = launch_fill_u64(reinterpret_cast<uint64_t*>(key_counts), 0ull, nslots / 2, s);
