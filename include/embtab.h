@@ -422,11 +422,14 @@ size_t emb_cache_state_bytes(int64_t cache_rows);
 
 /* Like emb_table_create, with desc->weights / desc->accum the HBM cache
  * ([C, D] each) and the table itself in tier->host_weights / host_accum.
- * init_storage must be 1: it initialises the host rows exactly as a dense
- * table's (same counter-based values) and empties the cache.  desc->hashed
- * must be 0 (else EMB_ERR_UNSUPPORTED).  EMB_ERR_INVALID_ARG for a null tier,
- * null or misaligned pointers, init_storage 0, cache_rows that
- * emb_cache_state_bytes rejects or above the table's total rows. */
+ * init_storage = 1 initialises the host rows exactly as a dense table's (same
+ * counter-based values) and empties the cache.  init_storage = 0 attaches to
+ * host rows and a state written by an earlier handle, which must have called
+ * emb_cache_flush after its last backward (the cache is not carried over: it
+ * starts empty).  desc->hashed must be 0 (else EMB_ERR_UNSUPPORTED).
+ * EMB_ERR_INVALID_ARG for a null tier, null or misaligned pointers,
+ * cache_rows that emb_cache_state_bytes rejects or above the table's total
+ * rows. */
 emb_status_t emb_table_create_tiered(const emb_table_desc_t* desc, const emb_tier_desc_t* tier,
                                      void* stream, emb_table_t* out);
 

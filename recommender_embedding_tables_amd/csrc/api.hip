@@ -172,8 +172,6 @@ static emb_status_t create_impl(const emb_table_desc_t* d, const emb_tier_desc_t
   }
   if (tier) {
     if (d->hashed) return EMB_ERR_UNSUPPORTED;
-    // the step stamps of a cache state belong to the handle that filled it
-    if (!d->init_storage) return EMB_ERR_INVALID_ARG;
     if (!tier->host_weights || !tier->host_accum || !tier->cache_state ||
         !aligned16(tier->host_weights) || !aligned16(tier->host_accum) ||
         (reinterpret_cast<uintptr_t>(tier->cache_state) & 255u) != 0)
@@ -222,6 +220,11 @@ static emb_status_t create_impl(const emb_table_desc_t* d, const emb_tier_desc_t
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
+  if (!d->init_storage && h.tiered) {
+    // attach: the host arrays hold every row (the earlier handle flushed its
+    // cache); the cache starts empty, its recency stamps with this handle
+    e = launch_cache_init(h, s);
+  }
   if (d->init_storage) {
     // state: flags 0, row offsets, capacities, live rows 0
     std::vector<int64_t> host(6 * (size_t)h.T + 1, 0);  // + free-row queues, slots: empty

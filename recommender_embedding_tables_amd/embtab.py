@@ -364,7 +364,8 @@ class EmbTables:
 
     def __init__(self, rows_per_table, dim, *, hashed=False, hash_capacity=0, max_load=0.625,
                  seed=0, init_lo=-0.05, init_hi=0.05, init_std=0.01, accum_init=0.1,
-                 device="cuda", stream=None, storage=None, cache_rows=0):
+                 device="cuda", stream=None, storage=None, cache_rows=0,
+                 host_storage=None):
         import torch
         self.rows = [int(r) for r in rows_per_table]
         self.T = len(self.rows)
@@ -375,10 +376,13 @@ class EmbTables:
         dev = torch.device(device)
         self.tiered = cache_rows > 0
         if self.tiered:
-            # the table in pinned host memory; weights / accum below are the HBM cache
-            self.host_weights = torch.empty((self.total_rows, self.D), dtype=torch.float32,
-                                            pin_memory=True)
-            self.host_accum = torch.empty_like(self.host_weights, pin_memory=True)
+            if host_storage is not None:  # attach: the host rows of an earlier (flushed) handle
+                self.host_weights, self.host_accum = host_storage
+            else:
+                # the table in pinned host memory; weights / accum below are the HBM cache
+                self.host_weights = torch.empty((self.total_rows, self.D), dtype=torch.float32,
+                                                pin_memory=True)
+                self.host_accum = torch.empty_like(self.host_weights, pin_memory=True)
             self.cache_state = torch.empty(max(emb_cache_state_bytes(cache_rows), 256),
                                            dtype=torch.uint8, device=dev)
         if storage is None:

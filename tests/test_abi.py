@@ -164,7 +164,7 @@ def _tier(**kw):
 
 
 @pytest.mark.parametrize("dkw,tkw,code", [
-    (dict(), dict(), eb.EMB_ERR_INVALID_ARG),  # init_storage 0: stamps belong to one handle
+    (dict(init_storage=1), dict(host_weights=0x50000008), eb.EMB_ERR_INVALID_ARG),
     (dict(init_storage=1, hashed=1, hash_capacity=1024, hash_slots=0x40000000), dict(),
      eb.EMB_ERR_UNSUPPORTED),
     (dict(init_storage=1), dict(cache_rows=0), eb.EMB_ERR_INVALID_ARG),
