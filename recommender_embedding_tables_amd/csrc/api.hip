@@ -686,3 +686,36 @@ emb_status_t emb_hash_export(emb_table_t t, int32_t table, uint64_t* key_of_row,
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------- stream ceilings
+
+static bool aligned16p(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+emb_status_t emb_stream_copy(void* dst, const void* src, size_t bytes, void* stream) {
+  if (!dst || !src || bytes % 16 != 0 || !aligned16p(dst) || !aligned16p(src))
+    return EMB_ERR_INVALID_ARG;
+  return launch_stream(0, dst, src, bytes, 0.0f, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? EMB_OK
+             : EMB_ERR_HIP;
+}
+
+emb_status_t emb_stream_fill(void* dst, float value, size_t bytes, void* stream) {
+  if (!dst || bytes % 16 != 0 || !aligned16p(dst)) return EMB_ERR_INVALID_ARG;
+  return launch_stream(1, dst, nullptr, bytes, value, static_cast<hipStream_t>(stream)) ==
+                 hipSuccess
+             ? EMB_OK
+             : EMB_ERR_HIP;
+}
+
+size_t emb_stream_read_sink_floats(size_t bytes) { return stream_blocks(bytes); }
+
+emb_status_t emb_stream_read(const void* src, size_t bytes, float* sink, size_t sink_floats,
+                             void* stream) {
+  if (!src || !sink || bytes % 16 != 0 || !aligned16p(src) ||
+      sink_floats < emb_stream_read_sink_floats(bytes))
+    return EMB_ERR_INVALID_ARG;
+  return launch_stream(2, sink, src, bytes, 0.0f, static_cast<hipStream_t>(stream)) ==
+                 hipSuccess
+             ? EMB_OK
+             : EMB_ERR_HIP;
+}

@@ -329,6 +329,11 @@ size_t hash_evict_workspace_bytes(const Handle& h);
 hipError_t launch_hash_evict(const Handle& h, const uint32_t* last_used, uint32_t before,
                              uint32_t* key_counts, char* ws, hipStream_t s);
 
+// Stream kernels (kind 0 copy, 1 fill, 2 read into one float per block).
+unsigned stream_blocks(size_t bytes);
+hipError_t launch_stream(int kind, void* dst, const void* src, size_t bytes, float value,
+                         hipStream_t s);
+
 hipError_t launch_debug_copy_sorted(const uint32_t* keys, uint32_t sentinel, uint32_t* out,
                                     int64_t n, hipStream_t s);
 

@@ -50,7 +50,8 @@ EXPORTED = [
     "emb_bag_backward_adagrad_decay_prepared", "emb_hash_find_or_insert_admit",
     "emb_hash_evict_workspace_bytes", "emb_hash_evict", "emb_hash_free_rows",
     "emb_interact_out_dim", "emb_bag_forward_interact", "emb_interact_backward",
-    "emb_bag_prepare_ids", "emb_cache_prepare",
+    "emb_bag_prepare_ids", "emb_cache_prepare", "emb_stream_copy", "emb_stream_fill",
+    "emb_stream_read_sink_floats", "emb_stream_read",
 ]
 
 EMB_PHASE_FORWARD, EMB_PHASE_KEYS, EMB_PHASE_SORT, EMB_PHASE_UNIQUE = 0, 1, 2, 3
@@ -141,6 +142,10 @@ def _load():
         "emb_bag_prepare_ids": (i32, [P, P, P, i64, i64, i32, P, sz, P]),
         "emb_cache_prepare": (i32, [P, i64, i64, P, sz, P]),
         "emb_cache_stats": (i32, [P, P, C.POINTER(i64), C.POINTER(i64), C.POINTER(i64)]),
+        "emb_stream_copy": (i32, [P, P, sz, P]),
+        "emb_stream_fill": (i32, [P, f32, sz, P]),
+        "emb_stream_read_sink_floats": (sz, [sz]),
+        "emb_stream_read": (i32, [P, sz, P, sz, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -452,3 +457,19 @@ class EmbTables:
         if self._ws is None or self._ws.numel() < need:
             self._ws = torch.empty(need + 256, dtype=torch.uint8, device=self.weights.device)
         return self._ws, need
+
+
+def emb_stream_copy(dst, src, nbytes, stream=None) -> int:
+    return _lib.emb_stream_copy(_ptr(dst), _ptr(src), nbytes, _stream(stream))
+
+
+def emb_stream_fill(dst, value, nbytes, stream=None) -> int:
+    return _lib.emb_stream_fill(_ptr(dst), value, nbytes, _stream(stream))
+
+
+def emb_stream_read_sink_floats(nbytes) -> int:
+    return int(_lib.emb_stream_read_sink_floats(nbytes))
+
+
+def emb_stream_read(src, nbytes, sink, sink_floats, stream=None) -> int:
+    return _lib.emb_stream_read(_ptr(src), nbytes, _ptr(sink), sink_floats, _stream(stream))
