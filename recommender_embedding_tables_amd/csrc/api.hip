@@ -354,7 +354,7 @@ emb_status_t emb_bag_backward_adagrad(emb_table_t t, const int64_t* offsets, con
     keys = slot_keys;
   }
   if (e == hipSuccess)
-    e = launch_segment_adagrad(t->h, p, keys, mean, grad_out, lr, eps, w, s);
+    e = launch_segment_adagrad(t->h, p, keys, perm, mean, grad_out, lr, eps, w, s);
   return hip_status(e);
 }
 
@@ -470,8 +470,8 @@ static emb_status_t backward_prepared(emb_table_t t, int64_t batch, int64_t nnz,
   uint32_t *keys = nullptr, *vals = nullptr;
   char* w = static_cast<char*>(ws);
   sorted_arrays(t->h, p, w, &keys, &vals);
-  return hip_status(launch_segment_adagrad(t->h, p, keys, pool == EMB_POOL_MEAN, grad_out, lr,
-                                           eps, w, static_cast<hipStream_t>(stream), dec));
+  return hip_status(launch_segment_adagrad(t->h, p, keys, vals, pool == EMB_POOL_MEAN, grad_out,
+                                           lr, eps, w, static_cast<hipStream_t>(stream), dec));
 }
 
 emb_status_t emb_bag_backward_adagrad_prepared(emb_table_t t, int64_t batch, int64_t nnz,

@@ -241,6 +241,14 @@ __device__ inline f4 load4_nt_or_zero(const float* __restrict__ base, size_t row
   return ok ? x : f4{0.f, 0.f, 0.f, 0.f};
 }
 
+// Grad row (= output row s*T + t) of occurrence j of a batch whose every bag
+// holds just the occurrence with its own index (one-hot): its bag is j, the
+// table j / B and the sample j % B.
+__device__ inline uint32_t one_hot_grad_row(uint32_t j, uint32_t B, uint32_t T) {
+  const uint32_t t = j / B;
+  return (j - t * B) * T + t;
+}
+
 // One SplitMix64 step from `state` (Steele, Lea and Flood 2014).
 __device__ inline uint64_t sm64(uint64_t state) {
   uint64_t z = state + 0x9E3779B97F4A7C15ull;
@@ -282,9 +290,12 @@ struct DecayArgs {
   float log2_rho = 0.0f;
   uint32_t period = 0;
 };
-hipError_t launch_segment_adagrad(const Handle& h, const Plan& p, const uint32_t* keys, bool mean,
-                                  const float* grad_out, float lr, float eps, char* ws,
-                                  hipStream_t s, const DecayArgs& dec = DecayArgs());
+// perm: the sorted occurrence indices (one-hot batches derive the grad row
+// from them).
+hipError_t launch_segment_adagrad(const Handle& h, const Plan& p, const uint32_t* keys,
+                                  const uint32_t* perm, bool mean, const float* grad_out,
+                                  float lr, float eps, char* ws, hipStream_t s,
+                                  const DecayArgs& dec = DecayArgs());
 
 // Forward from a prepared workspace.  One-hot batches gather the rows in
 // sorted order; otherwise (a device flag of the prepare) the same launch runs

@@ -278,8 +278,8 @@ __global__ __launch_bounds__(256) void k_fwd_sorted(
     mgr[i] = nbags;
     if (k < n) {
       mkey[i] = keys[k];
-      const uint32_t g = gr[k];  // grad row (= output row) of sorted position k
-      mgr[i] = g < nbags ? g : nbags;
+      const uint32_t v = perm[k];  // occurrence v is bag v: its output row
+      mgr[i] = v < n ? one_hot_grad_row(v, B, T) : nbags;
     }
   }
   uint32_t prevkey = kNoRow;

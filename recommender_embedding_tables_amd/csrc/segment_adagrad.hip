@@ -119,7 +119,8 @@ __device__ __forceinline__ void seg_chunk(
     uint32_t nbags, uint32_t* __restrict__ stamps, float log2_rho, uint32_t period, uint32_t c,
     uint32_t key_bb, uint32_t key_ba, f4* part_lds,
     uint32_t* slot_key, f4* in_lds, uint32_t* in_key, f4* out_lds, uint32_t* out_key,
-    BlockRun<VEC>& fin) {
+    BlockRun<VEC>& fin, const uint32_t* __restrict__ perm, bool one_hot, uint32_t B,
+    uint32_t T) {
   constexpr int CH = SG * MPL;
   const int lane = threadIdx.x % SG;
   const uint32_t k0 = c * CH;
@@ -144,13 +145,20 @@ __device__ __forceinline__ void seg_chunk(
     const uint32_t k = k0 + i * SG + lane;
     if (k < k1) {
       // grad row and scale were gathered into sorted order by the last sort
-      // pass.  Positions not written by any bag (offsets that do not tile
-      // [0, nnz)) may hold stale values: such an occurrence is dropped.
-      const uint32_t g = sgr[k];
+      // pass (one-hot batches: computed from the occurrence index).  Positions
+      // not written by any bag (offsets that do not tile [0, nnz)) may hold
+      // stale values: such an occurrence is dropped.
+      uint32_t g;
+      if (one_hot) {
+        const uint32_t v = perm[k];
+        g = v < n ? one_hot_grad_row(v, B, T) : nbags;
+      } else {
+        g = sgr[k];
+      }
       if (mkey[i] < sentinel) {
         if (g < nbags) {
           mgr[i] = g;
-          if (MEAN) msc[i] = sscale[k];
+          if (MEAN && !one_hot) msc[i] = sscale[k];
         } else {
           mkey[i] = sentinel;
         }
@@ -343,7 +351,8 @@ __global__ __launch_bounds__(256) void k_seg_adagrad(
     float* __restrict__ part_head, float* __restrict__ part_tail,
     const uint32_t* __restrict__ span_u, const uint32_t* __restrict__ seg_off,
     uint32_t* __restrict__ span_cnt, uint32_t nbags, uint32_t* __restrict__ stamps,
-    float log2_rho, uint32_t period) {
+    float log2_rho, uint32_t period, const uint32_t* __restrict__ perm,
+    const uint32_t* __restrict__ misc, uint32_t B, uint32_t T) {
   constexpr int CH = SG * MPL;
   constexpr int SGPB = 256 / SG;
   constexpr uint32_t BP = SGPB * CH;  // sorted positions per block
@@ -367,7 +376,8 @@ __global__ __launch_bounds__(256) void k_seg_adagrad(
   seg_chunk<SG, VEC, MEAN, MPL, UF, DECAY>(keys, sgr, sscale, grad, W, G, n, sentinel, D, lr, eps,
                                            nbags, stamps, log2_rho, period, c, key_bb, key_ba,
                                            s_part[sgb], &slot_key, s_in[sgb], &in_key,
-                                           s_out[sgb], &out_key, fin);
+                                           s_out[sgb], &out_key, fin, perm,
+                                           misc[kMiscNotOneHot] == 0u, B, T);
   if (lane == 0) {
     s_key[sgb] = slot_key;
     s_in_key[sgb] = in_key;
@@ -432,8 +442,9 @@ __global__ __launch_bounds__(256) void k_seg_adagrad(
 }
 
 template <int SG, int VEC, bool MEAN, bool DECAY>
-hipError_t launch_t(const Handle& h, const Plan& p, const uint32_t* keys, const float* grad_out,
-                    float lr, float eps, char* ws, hipStream_t s, const DecayArgs& dec) {
+hipError_t launch_t(const Handle& h, const Plan& p, const uint32_t* keys, const uint32_t* perm,
+                    const float* grad_out, float lr, float eps, char* ws, hipStream_t s,
+                    const DecayArgs& dec) {
   constexpr int MPL = chunk_rounds<SG>();
   constexpr int UF = VEC > 1 ? 2 : (SG < kSegUF ? SG : kSegUF);
   constexpr int SGPB = 256 / SG;
@@ -454,17 +465,20 @@ hipError_t launch_t(const Handle& h, const Plan& p, const uint32_t* keys, const 
   hipLaunchKernelGGL((k_seg_adagrad<SG, VEC, MEAN, MPL, UF, DECAY>), dim3((unsigned)grid),
                      dim3(256), 0, s, keys, gr, scale, grad_out, h.W, h.G, n,
                      (uint32_t)h.total_rows, h.D, lr, eps, ph, pt, span_u, seg_off, span_cnt,
-                     nbags, dec.stamps, dec.log2_rho, dec.period);
+                     nbags, dec.stamps, dec.log2_rho, dec.period, perm,
+                     reinterpret_cast<const uint32_t*>(ws + p.misc), (uint32_t)p.B,
+                     (uint32_t)h.T);
   phase_mark(h, EMB_PHASE_REDUCE, true, s);
   return hipGetLastError();
 }
 
 template <bool MEAN, bool DECAY>
-hipError_t dispatch(const Handle& h, const Plan& p, const uint32_t* keys, const float* grad_out, float lr, float eps, char* ws, hipStream_t s,
+hipError_t dispatch(const Handle& h, const Plan& p, const uint32_t* keys, const uint32_t* perm,
+                    const float* grad_out, float lr, float eps, char* ws, hipStream_t s,
                     const DecayArgs& dec) {
   const int sg = subgroup_lanes(h.D), vec = vec_per_lane(h.D);
 #define EMBTAB_SEG_LAUNCH(SG_, VEC_) \
-  launch_t<SG_, VEC_, MEAN, DECAY>(h, p, keys, grad_out, lr, eps, ws, s, dec)
+  launch_t<SG_, VEC_, MEAN, DECAY>(h, p, keys, perm, grad_out, lr, eps, ws, s, dec)
   switch (sg) {
     case 1: return EMBTAB_SEG_LAUNCH(1, 1);
     case 2: return EMBTAB_SEG_LAUNCH(2, 1);
@@ -485,15 +499,16 @@ hipError_t dispatch(const Handle& h, const Plan& p, const uint32_t* keys, const 
 
 }  // namespace
 
-hipError_t launch_segment_adagrad(const Handle& h, const Plan& p, const uint32_t* keys, bool mean,
-                                  const float* grad_out, float lr, float eps, char* ws,
-                                  hipStream_t s, const DecayArgs& dec) {
+hipError_t launch_segment_adagrad(const Handle& h, const Plan& p, const uint32_t* keys,
+                                  const uint32_t* perm, bool mean, const float* grad_out,
+                                  float lr, float eps, char* ws, hipStream_t s,
+                                  const DecayArgs& dec) {
   if (!grad_out) return hipErrorInvalidValue;
   if (dec.stamps)
-    return mean ? dispatch<true, true>(h, p, keys, grad_out, lr, eps, ws, s, dec)
-                : dispatch<false, true>(h, p, keys, grad_out, lr, eps, ws, s, dec);
-  return mean ? dispatch<true, false>(h, p, keys, grad_out, lr, eps, ws, s, dec)
-              : dispatch<false, false>(h, p, keys, grad_out, lr, eps, ws, s, dec);
+    return mean ? dispatch<true, true>(h, p, keys, perm, grad_out, lr, eps, ws, s, dec)
+                : dispatch<false, true>(h, p, keys, perm, grad_out, lr, eps, ws, s, dec);
+  return mean ? dispatch<true, false>(h, p, keys, perm, grad_out, lr, eps, ws, s, dec)
+              : dispatch<false, false>(h, p, keys, perm, grad_out, lr, eps, ws, s, dec);
 }
 
 }  // namespace embtab

@@ -235,11 +235,11 @@ __global__ __launch_bounds__(256) void k_sort_scan(uint32_t* __restrict__ tile_h
 }
 
 // FIRST: the values are the positions themselves (not read).  The last pass
-// (gr_out != nullptr) also writes each sorted occurrence's grad row (and mean
-// scale), so the consumers of the sort read them with coalesced loads: computed
-// from the occurrence index when every bag holds one id (a flag of k_keys),
-// else gathered; a stale occurrence index gets the invalid grad row
-// 0xFFFFFFFF.
+// (gr_out != nullptr) also gathers each sorted occurrence's grad row (and
+// mean scale) into sorted order, so the consumers of the sort read them with
+// coalesced loads; a stale occurrence index gets the invalid grad row
+// 0xFFFFFFFF.  When every bag holds one id (a flag of k_keys) the grad row
+// follows from the occurrence index and the consumers compute it from perm.
 template <bool FIRST>
 __global__ __launch_bounds__(256) void k_sort_scatter(
     const uint32_t* __restrict__ keys_in, const uint32_t* __restrict__ vals_in,
@@ -339,11 +339,10 @@ __global__ __launch_bounds__(256) void k_sort_scatter(
     const uint32_t v = svals[i];
     keys_out[g] = k;
     vals_out[g] = v;
-    if (gr_out) {
-      if (one_hot) {  // occurrence v is bag v: table v / B, sample v % B
-        gr_out[g] = v < n ? (v % B) * T + v / B : 0xFFFFFFFFu;
-        if (sc_out) sc_out[g] = 1.0f;
-      } else if (sc_out) {  // (grad row, scale) pairs
+    // one-hot batches: the consumers take the grad row from the occurrence
+    // index (perm) itself, so nothing more is written
+    if (gr_out && !one_hot) {
+      if (sc_out) {  // (grad row, scale) pairs
         const uint2 x = v < n ? reinterpret_cast<const uint2*>(gr_in)[v]
                               : make_uint2(0xFFFFFFFFu, 0u);
         gr_out[g] = x.x;
