@@ -62,6 +62,7 @@ bool make_plan(const Handle& h, int64_t B, int64_t nnz, Plan* p) {
   p->keysB = take(n4);
   p->valsB = take(n4);
   p->gr = take(2 * n4);  // grad row, or (grad row, mean scale) pairs
+  p->kblk = take((size_t)(B * (int64_t)h.T) + 1);  // at most one key block per bag
   p->sgr = take(n4);
   p->sscale = take(n4);
   p->tile_hist = take(sizeof(uint32_t) * kMaxRadix * nt);

@@ -165,6 +165,7 @@ struct Plan {
   int64_t nchunks = 0;  // reduction chunks
   int chunk = 0;
   size_t keysA, valsA, keysB, valsB, gr;
+  size_t kblk;  // per key block: 1 when every bag of the block holds its own occurrence
   size_t sgr, sscale;  // grad row and mean scale of each sorted occurrence
   size_t tile_hist, digit_tot;
   size_t unique, seg_off, counts, inverse;

@@ -67,7 +67,9 @@ __device__ inline uint32_t block_excl_scan(uint32_t v, uint32_t* total, uint32_t
 // a block covers about 256 occurrences).  Thread i < bpb checks bag b0 + i.
 // When every bag of the block holds exactly the occurrence with its own index
 // (one-hot features), thread i writes occurrence b0 + i directly from loads it
-// issued beside the offsets (the id at its own index, its table's bounds).
+// issued beside the offsets (the id at its own index, its table's bounds),
+// and the block is marked in place (its grad rows are not stored: occurrence
+// j's is s*T + t of bag j).
 // Otherwise the bag offsets go to LDS, and the block walks the occurrences
 // [offsets[b0], offsets[b0 + bpb]) with consecutive threads on consecutive
 // occurrences (coalesced id loads and key stores, whatever the bag lengths),
@@ -83,7 +85,7 @@ __global__ __launch_bounds__(256) void k_keys(const int64_t* __restrict__ offset
                                               uint32_t* __restrict__ flags,
                                               uint32_t* __restrict__ misc, int64_t B, int32_t T,
                                               int64_t nnz, uint32_t sentinel, int32_t mean,
-                                              int32_t bpb) {
+                                              int32_t bpb, uint8_t* __restrict__ in_place_blk) {
   __shared__ int64_t s_off[257];
   __shared__ uint32_t s_bad;
   const int64_t nbags = B * (int64_t)T;
@@ -120,18 +122,17 @@ __global__ __launch_bounds__(256) void k_keys(const int64_t* __restrict__ offset
   }
   const bool in_place = !mine || (o0 == b && o1 == b + 1 && o1 <= nnz);
   if (__syncthreads_and(in_place)) {
+    // the grad row of these occurrences follows from their index: the block
+    // is recorded as in place and writes none
+    if (threadIdx.x == 0) in_place_blk[blockIdx.x] = 1;
     if (mine) {
       uint32_t key = sentinel;
       if (own_id >= 0 && own_id < own_rows) key = (uint32_t)own_off + (uint32_t)own_id;
       else if (own_id != kAbsentId) bad |= EMB_FLAG_OUT_OF_RANGE;
       keys[b] = key;
-      const uint32_t g = ((uint32_t)b - own_t * (uint32_t)B) * (uint32_t)T + own_t;
-      if (mean)
-        reinterpret_cast<uint2*>(gr)[b] = make_uint2(g, __float_as_uint(1.0f));
-      else
-        gr[b] = g;
     }
   } else {
+    if (threadIdx.x == 0) in_place_blk[blockIdx.x] = 0;
     const int64_t j0 = s_off[0], j1 = s_off[nb];
     for (int64_t j = j0 + threadIdx.x; j < j1; j += 256) {
       // last bag i of the block with s_off[i] <= j (bags of length 0 are skipped)
@@ -246,7 +247,8 @@ __global__ __launch_bounds__(256) void k_sort_scatter(
     uint32_t* __restrict__ keys_out, uint32_t* __restrict__ vals_out, uint32_t n, int shift,
     int nbits, const uint32_t* __restrict__ tile_off, const uint32_t* __restrict__ digit_tot,
     uint32_t ntiles, const uint32_t* __restrict__ gr_in, uint32_t* __restrict__ gr_out,
-    float* __restrict__ sc_out, const uint32_t* __restrict__ misc, uint32_t B, uint32_t T) {
+    float* __restrict__ sc_out, const uint32_t* __restrict__ misc, uint32_t B, uint32_t T,
+    const uint8_t* __restrict__ in_place_blk, uint32_t bpb, uint32_t nkblk) {
   __shared__ uint32_t whist[4][kMaxRadix];
   __shared__ uint32_t dstart[kMaxRadix];
   __shared__ uint32_t gbase[kMaxRadix];
@@ -342,13 +344,17 @@ __global__ __launch_bounds__(256) void k_sort_scatter(
     // one-hot batches: the consumers take the grad row from the occurrence
     // index (perm) itself, so nothing more is written
     if (gr_out && !one_hot) {
+      // occurrences of in-place key blocks: bag v, length 1 (key block v / bpb
+      // holds exactly occurrences v of its own bags when it is in place)
+      const bool ip = v < n && v / bpb < nkblk && in_place_blk[v / bpb] != 0;
       if (sc_out) {  // (grad row, scale) pairs
-        const uint2 x = v < n ? reinterpret_cast<const uint2*>(gr_in)[v]
-                              : make_uint2(0xFFFFFFFFu, 0u);
+        const uint2 x = ip ? make_uint2(one_hot_grad_row(v, B, T), __float_as_uint(1.0f))
+                           : (v < n ? reinterpret_cast<const uint2*>(gr_in)[v]
+                                    : make_uint2(0xFFFFFFFFu, 0u));
         gr_out[g] = x.x;
         sc_out[g] = __uint_as_float(x.y);
       } else {
-        gr_out[g] = v < n ? gr_in[v] : 0xFFFFFFFFu;
+        gr_out[g] = ip ? one_hot_grad_row(v, B, T) : (v < n ? gr_in[v] : 0xFFFFFFFFu);
       }
     }
   }
@@ -558,9 +564,10 @@ const Handle& h, const Plan& p, const int64_t* offsets,
   phase_mark(h, EMB_PHASE_KEYS, false, s);
   hipError_t e = launch_zero_words(misc, 64 + 2 * h.T, s);
   if (e != hipSuccess) return e;
+  uint8_t* in_place_blk = reinterpret_cast<uint8_t*>(ws + p.kblk);
   hipLaunchKernelGGL(k_keys, dim3(kgrid > 0 ? kgrid : 1), dim3(256), 0, s, offsets, ids,
                      h.sv.row_off, h.sv.rows, kA, gr, h.sv.flags, misc, p.B, h.T,
-                     p.nnz, sentinel, mean ? 1 : 0, bpb);
+                     p.nnz, sentinel, mean ? 1 : 0, bpb, in_place_blk);
   phase_mark(h, EMB_PHASE_KEYS, true, s);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -585,11 +592,13 @@ const Handle& h, const Plan& p, const int64_t* offsets,
       if (pass == 0)
         hipLaunchKernelGGL(k_sort_scatter<true>, dim3(ntiles), dim3(256), 0, s, kin, vin, kout,
                            vout, n, p.shift[pass], p.dbits[pass], tile_hist, digit_tot, ntiles, gr,
-                           gro, sco, misc, (uint32_t)p.B, (uint32_t)h.T);
+                           gro, sco, misc, (uint32_t)p.B, (uint32_t)h.T, in_place_blk,
+                           (uint32_t)bpb, kgrid);
       else
         hipLaunchKernelGGL(k_sort_scatter<false>, dim3(ntiles), dim3(256), 0, s, kin, vin, kout,
                            vout, n, p.shift[pass], p.dbits[pass], tile_hist, digit_tot, ntiles, gr,
-                           gro, sco, misc, (uint32_t)p.B, (uint32_t)h.T);
+                           gro, sco, misc, (uint32_t)p.B, (uint32_t)h.T, in_place_blk,
+                           (uint32_t)bpb, kgrid);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
       uint32_t* tk = kin;

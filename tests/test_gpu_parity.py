@@ -298,6 +298,29 @@ def test_backward_small_ragged(D, mean):
     assert status(tabs) == (eb.EMB_OK, 0)
 
 
+@pytest.mark.parametrize("mean", [False, True])
+def test_backward_mixed_one_hot_and_multi_hot_bags(mean):
+    """Tables 0 and 1 one-hot, table 2 multi-hot: the key blocks over tables 0
+    and 1 hold every bag's own occurrence and store no grad rows, the others
+    do, and the last radix pass takes each occurrence's grad row from the
+    right one (sort/unique bit-exact, rows against the oracle)."""
+    rows = np.array([3000, 700, 1500])
+    B, D = 700, 32
+    rng = np.random.default_rng(77)
+    lens = np.concatenate([np.ones(2 * B, np.int64), rng.integers(0, 5, B)])
+    offsets = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    t = np.repeat(np.arange(3 * B), lens) // B
+    ids = (rng.zipf(1.3, offsets[-1]) - 1) % rows[t]
+    grad = rng.standard_normal((B, 3, D)).astype(np.float32)
+    tabs, o = make_pair(rows, D, seed=15)
+    check_sort_unique(tabs, o, offsets, ids, B)
+    gpu_backward(tabs, offsets, ids, B, mean, grad, 0.01, 1e-8)
+    assert o.backward_adagrad(offsets, ids, B, mean, grad, 0.01, 1e-8) == 0
+    check_rows(tabs, o, offsets, ids, B, mean, grad, 0.01, 1e-8,
+               extra_rows=np.arange(0, rows.sum(), 5))
+    assert status(tabs) == (eb.EMB_OK, 0)
+
+
 def test_backward_hot_rows_span_many_chunks():
     # Zipf(1.2) over a small table: the hottest rows cover hundreds of chunks.
     w = synth.workload(3, T=2, B=8000)
