@@ -235,7 +235,7 @@ __global__ __launch_bounds__(256) void k_cache_remap(
     if (slot != kNoRow) out = slot;
   }
   slot_keys[k] = out;
-  if (misc[kMiscNotOneHot] != 0u) {
+  if (batch_not_one_hot(misc)) {
     const uint32_t j = perm[k];
     if (j < n) rowmap[j] = out < sentinel ? out : kNoRow;
   }

@@ -93,6 +93,7 @@ struct Handle {
   uint32_t cache_sets = 0;  // a power of two
   char* cache_state = nullptr;
   uint32_t step = 0;  // prepares so far (cache recency stamps)
+  mutable uint32_t prepare_gen = 0;  // key builds so far (tags the one-hot flag)
 };
 
 // Cache state of a tiered table: counters, then per slot the row it holds
@@ -190,7 +191,10 @@ enum : int {
   kMiscNumValid = 1,
   kMiscHashAbort = 2,  // the hash call's offsets are invalid: it inserts nothing
   kMiscHashOverflow = 3,
-  kMiscNotOneHot = 5,  // some bag of the prepared batch does not hold exactly one id
+  // some bag of the prepared batch does not hold exactly one id: this word
+  // equals kMiscPrepareGen (the prepare's number, stored by its key build)
+  kMiscNotOneHot = 5,
+  kMiscPrepareGen = 6,
   kMiscCacheMiss = 7,  // tiered: misses of this prepare
   kMiscHashSlotFull = 4,  // the call's new keys would exceed a table's slot bound
   // per table: new keys [T], their base rank [T], block part [T + 1], then
@@ -240,6 +244,13 @@ __device__ inline f4 load4_nt_or_zero(const float* __restrict__ base, size_t row
   const size_t off = ok ? row * D + 4u * d4 : 0u;
   const f4 x = __builtin_nontemporal_load(reinterpret_cast<const f4*>(base + off));
   return ok ? x : f4{0.f, 0.f, 0.f, 0.f};
+}
+
+// Whether some bag of the prepared batch holds other than one id (the key
+// build tags the flag word with its own number, so no clearing launch is
+// needed; a stale tag can only select the general path, which is exact too).
+__device__ inline bool batch_not_one_hot(const uint32_t* misc) {
+  return misc[kMiscNotOneHot] == misc[kMiscPrepareGen];
 }
 
 // Grad row (= output row s*T + t) of occurrence j of a batch whose every bag

@@ -253,7 +253,7 @@ __global__ __launch_bounds__(256) void k_fwd_sorted(
     const int64_t* __restrict__ ids, const int64_t* __restrict__ row_off,
     const int64_t* __restrict__ rows, uint32_t* __restrict__ flags, uint32_t B, uint32_t T,
     uint32_t S, const uint32_t* __restrict__ rowmap) {
-  if (misc[kMiscNotOneHot] != 0u) {
+  if (batch_not_one_hot(misc)) {
     __shared__ BagTileLds lds;
     const uint32_t bad = bag_tile<SG, VEC, MEAN, UNR>(xcd_block(), offsets, ids, W, row_off,
                                                       rows, out, B, T, D, n, S, lds, rowmap);

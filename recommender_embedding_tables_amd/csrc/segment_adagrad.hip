@@ -377,7 +377,7 @@ __global__ __launch_bounds__(256) void k_seg_adagrad(
                                            nbags, stamps, log2_rho, period, c, key_bb, key_ba,
                                            s_part[sgb], &slot_key, s_in[sgb], &in_key,
                                            s_out[sgb], &out_key, fin, perm,
-                                           misc[kMiscNotOneHot] == 0u, B, T);
+                                           !batch_not_one_hot(misc), B, T);
   if (lane == 0) {
     s_key[sgb] = slot_key;
     s_in_key[sgb] = in_key;

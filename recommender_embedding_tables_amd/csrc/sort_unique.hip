@@ -85,9 +85,15 @@ __global__ __launch_bounds__(256) void k_keys(const int64_t* __restrict__ offset
                                               uint32_t* __restrict__ flags,
                                               uint32_t* __restrict__ misc, int64_t B, int32_t T,
                                               int64_t nnz, uint32_t sentinel, int32_t mean,
-                                              int32_t bpb, uint8_t* __restrict__ in_place_blk) {
+                                              int32_t bpb, uint8_t* __restrict__ in_place_blk,
+                                              uint32_t gen, int32_t nmisc) {
   __shared__ int64_t s_off[257];
   __shared__ uint32_t s_bad;
+  if (blockIdx.x == 0) {
+    // the prepare's counters start at zero; the one-hot flag is tagged instead
+    for (int i = threadIdx.x; i < nmisc; i += 256)
+      if (i != kMiscNotOneHot) misc[i] = i == kMiscPrepareGen ? gen : 0u;
+  }
   const int64_t nbags = B * (int64_t)T;
   const int64_t b0 = (int64_t)blockIdx.x * bpb;
   const int64_t b = b0 + threadIdx.x;
@@ -107,9 +113,9 @@ __global__ __launch_bounds__(256) void k_keys(const int64_t* __restrict__ offset
   }
   {
     const uint64_t mm = __ballot(o1 - o0 != 1);
-    // a plain store of a constant: device atomics on one word from every
-    // block would serialise
-    if ((threadIdx.x & 63u) == 0u && mm != 0ull) misc[kMiscNotOneHot] = 1u;
+    // a plain store of the prepare's tag: device atomics on one word from
+    // every block would serialise
+    if ((threadIdx.x & 63u) == 0u && mm != 0ull) misc[kMiscNotOneHot] = gen;
   }
   uint32_t bad = 0;
   if (mine) {
@@ -333,7 +339,7 @@ __global__ __launch_bounds__(256) void k_sort_scatter(
   __syncthreads();
   const uint32_t tbase = tile * (uint32_t)kSortTile;
   const uint32_t tn = (n - tbase) < (uint32_t)kSortTile ? (n - tbase) : (uint32_t)kSortTile;
-  const bool one_hot = gr_out && misc[kMiscNotOneHot] == 0u;
+  const bool one_hot = gr_out && !batch_not_one_hot(misc);
   for (uint32_t i = threadIdx.x; i < tn; i += 256) {
     const uint32_t k = skeys[i];
     const uint32_t d = (k >> shift) & mask;
@@ -562,12 +568,13 @@ const Handle& h, const Plan& p, const int64_t* offsets,
   while (bpb > 1 && (int64_t)bpb * p.nnz > 256 * nbags * 2) bpb >>= 1;
   const unsigned kgrid = (unsigned)((nbags + bpb - 1) / bpb);
   phase_mark(h, EMB_PHASE_KEYS, false, s);
-  hipError_t e = launch_zero_words(misc, 64 + 2 * h.T, s);
-  if (e != hipSuccess) return e;
   uint8_t* in_place_blk = reinterpret_cast<uint8_t*>(ws + p.kblk);
+  uint32_t gen = ++h.prepare_gen;
+  if (gen == 0u) gen = ++h.prepare_gen;
   hipLaunchKernelGGL(k_keys, dim3(kgrid > 0 ? kgrid : 1), dim3(256), 0, s, offsets, ids,
                      h.sv.row_off, h.sv.rows, kA, gr, h.sv.flags, misc, p.B, h.T,
-                     p.nnz, sentinel, mean ? 1 : 0, bpb, in_place_blk);
+                     p.nnz, sentinel, mean ? 1 : 0, bpb, in_place_blk, gen, 64 + 2 * h.T);
+  hipError_t e;
   phase_mark(h, EMB_PHASE_KEYS, true, s);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
