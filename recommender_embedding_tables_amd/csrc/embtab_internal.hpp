@@ -93,7 +93,6 @@ struct Handle {
   uint32_t cache_sets = 0;  // a power of two
   char* cache_state = nullptr;
   uint32_t step = 0;  // prepares so far (cache recency stamps)
-  mutable uint32_t prepare_gen = 0;  // key builds so far (tags the one-hot flag)
 };
 
 // Cache state of a tiered table: counters, then per slot the row it holds

@@ -34,11 +34,24 @@
 // stay off the training kernels' stream.  counts[u] = seg_off[u+1] - seg_off[u]
 // (k_unique_counts) is formed only for the sort / unique export, since no
 // training step reads it.
+#include <atomic>
+
 #include "embtab_internal.hpp"
 
 namespace embtab {
 
 namespace {
+
+// Number of this key build among all key builds of the process (never 0).
+// It tags the one-hot flag word of the workspace; being unique per process
+// rather than per handle, a workspace that several handles share cannot hold
+// a stale tag equal to the current one.
+uint32_t next_prepare_gen() {
+  static std::atomic<uint32_t> n{0};
+  uint32_t g = n.fetch_add(1u, std::memory_order_relaxed) + 1u;
+  if (g == 0u) g = n.fetch_add(1u, std::memory_order_relaxed) + 1u;
+  return g;
+}
 
 // Exclusive scan of one value per thread over a 256-thread block.
 __device__ inline uint32_t block_excl_scan(uint32_t v, uint32_t* total, uint32_t* lds4) {
@@ -569,8 +582,7 @@ const Handle& h, const Plan& p, const int64_t* offsets,
   const unsigned kgrid = (unsigned)((nbags + bpb - 1) / bpb);
   phase_mark(h, EMB_PHASE_KEYS, false, s);
   uint8_t* in_place_blk = reinterpret_cast<uint8_t*>(ws + p.kblk);
-  uint32_t gen = ++h.prepare_gen;
-  if (gen == 0u) gen = ++h.prepare_gen;
+  uint32_t gen = next_prepare_gen();
   hipLaunchKernelGGL(k_keys, dim3(kgrid > 0 ? kgrid : 1), dim3(256), 0, s, offsets, ids,
                      h.sv.row_off, h.sv.rows, kA, gr, h.sv.flags, misc, p.B, h.T,
                      p.nnz, sentinel, mean ? 1 : 0, bpb, in_place_blk, gen, 64 + 2 * h.T);
