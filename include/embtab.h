@@ -267,6 +267,25 @@ emb_status_t emb_bag_backward_adagrad(emb_table_t h, const int64_t* offsets,
                                       emb_pool_t pool, const float* grad_out, float lr,
                                       float eps, void* ws, size_t ws_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * emb_bag_backward_adagrad with its workspace taken from a buffer of
+ * EMB_NOALLOC_SCRATCH_BYTES bytes that the library holds on each device, from
+ * its load onto that device until the process ends.  Same arguments, result
+ * and errors as emb_bag_backward_adagrad, without ws and ws_bytes; it
+ * allocates and frees nothing.  EMB_ERR_WORKSPACE (nothing enqueued) when
+ * emb_workspace_bytes(h, batch, nnz) > EMB_NOALLOC_SCRATCH_BYTES; EMB_ERR_HIP
+ * when the buffer's device address could not be resolved at handle creation.
+ * Every call on one device shares that device's buffer, which keeps the last
+ * call's contents (each call writes what it reads): calls ordered on one
+ * stream are safe, calls that overlap in time on one device (other streams,
+ * other threads, other handles) race and give undefined results. */
+#define EMB_NOALLOC_SCRATCH_BYTES (64u << 20)
+emb_status_t emb_bag_backward_adagrad_noalloc(emb_table_t h, const int64_t* offsets,
+                                              const int64_t* ids, int64_t batch, int64_t nnz,
+                                              emb_pool_t pool, const float* grad_out, float lr,
+                                              float eps, void* stream);
+
 /* The same backward split in two, so that the id-only stages can overlap the
  * forward gather (they need offsets and ids but not grad_out):
  *   emb_bag_prepare                    occurrence keys, stable sort, run

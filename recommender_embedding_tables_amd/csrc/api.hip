@@ -3,14 +3,40 @@
 // call on the caller's stream.  No device memory is allocated here.
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <new>
 
 #include "embtab_internal.hpp"
 #include "interact.hpp"
 
+// The workspace of emb_bag_backward_adagrad_noalloc: one copy per device,
+// held from the library's load onto that device until the process ends.
+// Host code never uses this name as an address (on the host it is only a
+// stand-in); it uses the device address resolved for each device below.
+static __device__ __align__(256) unsigned char scratch[EMB_NOALLOC_SCRATCH_BYTES];
+
 namespace embtab {
 
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};  // address of `scratch` on each device
+
+// Address of `dev`'s copy of `scratch`, resolved once per device; `dev` must
+// be the current device.  Null when the runtime cannot give it.
+void* device_scratch(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) == hipSuccess && p != nullptr)
+      g_scratch[dev] = p;
+    else
+      (void)hipGetLastError();
+  }
+  return g_scratch[dev];
+}
 
 size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -214,10 +240,13 @@ static emb_status_t create_impl(const emb_table_desc_t* d, const emb_tier_desc_t
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) == hipSuccess &&
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-        cus > 0)
+        cus > 0) {
       h.cus = cus;
-    else
+      h.device = dev;
+      h.scratch = device_scratch(dev);
+    } else {
       (void)hipGetLastError();  // no device visible: keep the default
+    }
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
@@ -357,6 +386,26 @@ emb_status_t emb_bag_backward_adagrad(emb_table_t t, const int64_t* offsets, con
   if (e == hipSuccess)
     e = launch_segment_adagrad(t->h, p, keys, perm, mean, grad_out, lr, eps, w, s);
   return hip_status(e);
+}
+
+emb_status_t emb_bag_backward_adagrad_noalloc(emb_table_t t, const int64_t* offsets,
+                                              const int64_t* ids, int64_t batch, int64_t nnz,
+                                              emb_pool_t pool, const float* grad_out, float lr,
+                                              float eps, void* stream) {
+  if (!t) return EMB_ERR_INVALID_ARG;
+  // sizes that make no plan (need 0) and every other argument are judged by
+  // emb_bag_backward_adagrad itself, before it enqueues anything
+  const size_t need = emb_workspace_bytes(t, batch, nnz);
+  if (need > (size_t)EMB_NOALLOC_SCRATCH_BYTES) return EMB_ERR_WORKSPACE;
+  if (!t->h.scratch) {
+    // without a workspace the call returns an argument error or, for
+    // valid arguments, EMB_ERR_WORKSPACE: here that is the unresolved buffer
+    const emb_status_t st = emb_bag_backward_adagrad(t, offsets, ids, batch, nnz, pool,
+                                                     grad_out, lr, eps, nullptr, 0, stream);
+    return st == EMB_ERR_WORKSPACE ? EMB_ERR_HIP : st;
+  }
+  return emb_bag_backward_adagrad(t, offsets, ids, batch, nnz, pool, grad_out, lr, eps,
+                                  t->h.scratch, (size_t)EMB_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 // launch_sort_unique ping-pongs A -> B -> A ... once per radix pass.  For a

@@ -85,6 +85,10 @@ struct Handle {
   bool timing = false;
   hipEvent_t events[2 * EMB_NUM_PHASES] = {};
   int cus = 256;  // compute units of the device current at creation
+  int device = -1;  // the device current at creation (-1: none visible)
+  // this device's copy of the library's own workspace, for callers that
+  // cannot allocate one (null if its address could not be resolved)
+  void* scratch = nullptr;
   // tiered tables: W / G above are the HBM cache, the table is in host memory
   bool tiered = false;
   float* hostW = nullptr;

@@ -33,6 +33,7 @@ EMB_FLAG_TABLE_FULL = 8
 EMB_FLAG_CACHE_FULL = 32
 
 EMB_CACHE_WAYS = 16
+EMB_NOALLOC_SCRATCH_BYTES = 64 << 20
 EMB_ID_ABSENT = -2
 
 EMB_POOL_SUM = 0
@@ -43,7 +44,8 @@ EMB_EMPTY_KEY = 0xFFFFFFFFFFFFFFFF
 EXPORTED = [
     "emb_state_bytes", "emb_hash_bytes", "emb_workspace_bytes", "emb_table_create",
     "emb_table_destroy", "emb_hash_find_or_insert", "emb_bag_forward",
-    "emb_bag_backward_adagrad", "emb_status_sync", "emb_hash_n_live", "emb_hash_export",
+    "emb_bag_backward_adagrad", "emb_bag_backward_adagrad_noalloc", "emb_status_sync",
+    "emb_hash_n_live", "emb_hash_export",
     "emb_debug_sort_unique", "emb_status_string", "emb_set_phase_events", "emb_bag_prepare",
     "emb_bag_backward_adagrad_prepared", "emb_bag_forward_prepared", "emb_cache_state_bytes",
     "emb_table_create_tiered", "emb_cache_flush", "emb_cache_stats",
@@ -124,6 +126,7 @@ def _load():
         "emb_hash_free_rows": (i32, [P, P, C.POINTER(i64)]),
         "emb_bag_forward": (i32, [P, P, P, i64, i64, i32, P, P, sz, P]),
         "emb_bag_backward_adagrad": (i32, [P, P, P, i64, i64, i32, P, f32, f32, P, sz, P]),
+        "emb_bag_backward_adagrad_noalloc": (i32, [P, P, P, i64, i64, i32, P, f32, f32, P]),
         "emb_status_sync": (i32, [P, P, C.POINTER(u32)]),
         "emb_hash_n_live": (i32, [P, P, P]),
         "emb_hash_export": (i32, [P, i32, P, P]),
@@ -300,6 +303,12 @@ def emb_bag_backward_adagrad(handle, offsets, ids, batch, nnz, pool, grad_out, l
     return _lib.emb_bag_backward_adagrad(handle, _ptr(offsets), _ptr(ids), batch, nnz, pool,
                                          _ptr(grad_out), lr, eps, _ptr(ws), ws_bytes,
                                          _stream(stream))
+
+
+def emb_bag_backward_adagrad_noalloc(handle, offsets, ids, batch, nnz, pool, grad_out, lr, eps,
+                                     stream=None) -> int:
+    return _lib.emb_bag_backward_adagrad_noalloc(handle, _ptr(offsets), _ptr(ids), batch, nnz,
+                                                 pool, _ptr(grad_out), lr, eps, _stream(stream))
 
 
 def emb_bag_prepare(handle, offsets, ids, batch, nnz, pool, ws, ws_bytes, stream=None) -> int:

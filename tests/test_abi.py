@@ -124,6 +124,23 @@ def test_host_checks_on_attached_handle():
                                            0) == eb.EMB_ERR_WORKSPACE
         assert eb.emb_bag_forward_prepared(h, fake, fake, 4096, 10000, 0, None, fake, ws,
                                            0) == eb.EMB_ERR_INVALID_ARG
+        # the backward on the library's own buffer: a batch over the buffer, sizes
+        # beyond the 32-bit indices and bad arguments fail before any launch
+        lim = eb.EMB_NOALLOC_SCRATCH_BYTES
+        assert eb.emb_workspace_bytes(h, 4096, 4_000_000) > lim
+        assert eb.emb_bag_backward_adagrad_noalloc(None, fake, fake, 4096, 10000, 0, fake, 0.01,
+                                                   1e-8, 0) == eb.EMB_ERR_INVALID_ARG
+        assert eb.emb_bag_backward_adagrad_noalloc(h, fake, fake, 4096, 4_000_000, 0, fake, 0.01,
+                                                   1e-8, 0) == eb.EMB_ERR_WORKSPACE
+        assert eb.emb_bag_backward_adagrad_noalloc(h, fake, fake, 4096, 2**33, 0, fake, 0.01,
+                                                   1e-8, 0) == eb.EMB_ERR_UNSUPPORTED
+        assert eb.emb_bag_backward_adagrad_noalloc(h, fake, fake, 4096, 10000, 0, fake,
+                                                   float("nan"), 1e-8,
+                                                   0) == eb.EMB_ERR_INVALID_ARG
+        assert eb.emb_bag_backward_adagrad_noalloc(h, fake, fake, 4096, 10000, 5, fake, 0.01,
+                                                   1e-8, 0) == eb.EMB_ERR_INVALID_ARG
+        assert eb.emb_bag_backward_adagrad_noalloc(h, None, fake, 4096, 10000, 0, fake, 0.01,
+                                                   1e-8, 0) == eb.EMB_ERR_INVALID_ARG
         # hash calls on a dense handle
         assert eb.emb_hash_find_or_insert(h, fake, fake, 4096, 10000, fake, fake, ws,
                                           0) == eb.EMB_ERR_UNSUPPORTED
