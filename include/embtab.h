@@ -483,14 +483,16 @@ emb_status_t emb_cache_stats(emb_table_t h, void* stream, int64_t* lookups, int6
  * What HBM sustains on this device for plain streams, the yardstick the
  * benchmark reports beside the published peak (every kernel of the path is
  * bound by HBM bandwidth: "NVIDIA Merlin Distributed Embeddings" page,
- * section "Background").  Hand-written dwordx4 kernels with non-temporal
- * loads and stores, eight 256-thread blocks per compute unit, asynchronous
- * on `stream` (a hipStream_t; NULL is the null stream).
+ * section "Background").  Hand-written dwordx4 kernels, one 16-byte item per
+ * thread and one 256-thread block per 4 KiB (the fastest form measured on
+ * MI355X); copy loads and stores are non-temporal, fill stores plain, read
+ * loads non-temporal.  Asynchronous on `stream` (a hipStream_t; NULL is the
+ * null stream).
  *   emb_stream_copy  dst[0, bytes) = src[0, bytes)   (bytes read + bytes written)
  *   emb_stream_fill  dst[0, bytes) = value, as fp32 words
- *   emb_stream_read  reads src[0, bytes); writes one float per block (a sum
- *                    of the block's words) to sink, which must hold
- *                    emb_stream_read_sink_floats(bytes) floats
+ *   emb_stream_read  reads src[0, bytes), four items per thread; writes one
+ *                    float per wave (a sum of its words) to sink, which must
+ *                    hold emb_stream_read_sink_floats(bytes) floats
  * All pointers are device pointers, 16-byte aligned; bytes a multiple of 16
  * (0 launches nothing).  EMB_ERR_INVALID_ARG for null or misaligned pointers,
  * a bad size or a short sink; EMB_ERR_HIP if the launch fails.  The buffers

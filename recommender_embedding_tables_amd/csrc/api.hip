@@ -757,7 +757,7 @@ emb_status_t emb_stream_fill(void* dst, float value, size_t bytes, void* stream)
              : EMB_ERR_HIP;
 }
 
-size_t emb_stream_read_sink_floats(size_t bytes) { return stream_blocks(bytes); }
+size_t emb_stream_read_sink_floats(size_t bytes) { return stream_read_sink_floats(bytes); }
 
 emb_status_t emb_stream_read(const void* src, size_t bytes, float* sink, size_t sink_floats,
                              void* stream) {

@@ -356,7 +356,7 @@ hipError_t launch_hash_evict(const Handle& h, const uint32_t* last_used, uint32_
                              uint32_t* key_counts, char* ws, hipStream_t s);
 
 // Stream kernels (kind 0 copy, 1 fill, 2 read into one float per block).
-unsigned stream_blocks(size_t bytes);
+size_t stream_read_sink_floats(size_t bytes);
 hipError_t launch_stream(int kind, void* dst, const void* src, size_t bytes, float value,
                          hipStream_t s);
 

@@ -235,11 +235,21 @@ __global__ __launch_bounds__(256) void k_bag_forward(
   if (bad) atomicOr(flags, bad);
 }
 
+// Sorted positions per sub-group of the one-hot forward: kFwdChunk when the
+// sub-group has that many lanes (one position in each of its first lanes),
+// else the reduction's chunk.  Chunks of 8 measured faster than 32 (4 or 16
+// slower than 8): more blocks keep more output rows in flight.
+constexpr int kFwdChunk = 8;
+template <int SG, int MPL>
+constexpr int fwd_chunk() {
+  return SG >= kFwdChunk ? kFwdChunk : SG * MPL;
+}
+
 // One-hot batches after the sort: every bag holds one id, so the output row of
 // occurrence j is W[row_j] stored at out[grad_row(j)].  Walking the sorted
 // occurrences, a Zipf-hot row is read once per chunk and then stored to each
-// of its bags, and W is visited in ascending address order.  Chunks and
-// sub-groups are those of the reduction kernel; MPL metadata entries per lane.
+// of its bags, and W is visited in ascending address order.  Sub-groups are
+// those of the reduction kernel, chunks are fwd_chunk() positions.
 //
 // Whether the batch is one-hot is known only on the device (a flag set while
 // the keys were built), so the same launch also holds the general pooled
@@ -260,9 +270,12 @@ __global__ __launch_bounds__(256) void k_fwd_sorted(
     if (bad) atomicOr(flags, bad);
     return;
   }
-  constexpr int CH = SG * MPL;
+  constexpr int CH = fwd_chunk<SG, MPL>();
+  constexpr int ML = CH < SG * MPL ? 1 : MPL;  // metadata entries per lane
+  constexpr int LPR = CH < SG ? CH : SG;       // positions per metadata round
   constexpr int SGPB = 256 / SG;
   constexpr int UF = VEC > 1 ? 2 : (SG < 4 ? SG : 4);
+  static_assert(LPR % UF == 0, "rows in flight must divide a round");
   const uint32_t lane = threadIdx.x % SG;
   // Chunks in launch order (no XCD remap): measured faster here, since the
   // row loads walk W in ascending order across the whole chip at once.
@@ -270,13 +283,13 @@ __global__ __launch_bounds__(256) void k_fwd_sorted(
   const uint32_t k0 = c * CH;
   if (k0 >= n) return;
   const uint32_t D4 = D >> 2;
-  uint32_t mkey[MPL], mgr[MPL];
+  uint32_t mkey[ML], mgr[ML];
 #pragma unroll
-  for (int i = 0; i < MPL; ++i) {
+  for (int i = 0; i < ML; ++i) {
     const uint32_t k = k0 + i * SG + lane;
     mkey[i] = kNoRow;
     mgr[i] = nbags;
-    if (k < n) {
+    if (k < n && lane < (uint32_t)LPR) {
       mkey[i] = keys[k];
       const uint32_t v = perm[k];  // occurrence v is bag v: its output row
       mgr[i] = v < n ? one_hot_grad_row(v, B, T) : nbags;
@@ -287,9 +300,9 @@ __global__ __launch_bounds__(256) void k_fwd_sorted(
 #pragma unroll
   for (int v = 0; v < VEC; ++v) prevrow[v] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int i = 0; i < MPL; ++i) {
+  for (int i = 0; i < ML; ++i) {
 #pragma unroll 1
-    for (int l0 = 0; l0 < SG; l0 += UF) {
+    for (int l0 = 0; l0 < LPR; l0 += UF) {
       uint32_t kk[UF], gg[UF];
 #pragma unroll
       for (int u = 0; u < UF; ++u) {
@@ -403,7 +416,8 @@ hipError_t launch_sorted_t(const Handle& h, const Plan& p, const int64_t* offset
                            float* out, char* ws, const uint32_t* rowmap, hipStream_t s) {
   constexpr int MPL = chunk_rounds<SG>();
   constexpr int SGPB = 256 / SG;
-  const int64_t chunks = (p.nnz + SG * MPL - 1) / (SG * MPL);
+  constexpr int CH = fwd_chunk<SG, MPL>();
+  const int64_t chunks = (p.nnz + CH - 1) / CH;
   const int64_t S = tile_samples(h.T, p.B, p.nnz);
   const int64_t tiles = (p.B + S - 1) / S;
   int64_t grid = (chunks + SGPB - 1) / SGPB;
