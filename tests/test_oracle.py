@@ -2,7 +2,8 @@
 
 Pins used (none re-types the oracle's own loops):
   * the published SplitMix64 test vector and the finalizer's invertibility;
-  * distribution tests of the uniform and Box-Muller draws;
+  * distribution tests of the uniform and Box-Muller draws, and Box-Muller's
+    special angles (0, 1/4, 1/2, 3/4 turn), radius offset and sign pattern;
   * hand-worked cases whose results are exact small numbers (closed forms);
   * brute force: a dense bag-by-row matrix A with out = A.W and grad_W = A^T.grad;
   * library routines: torch.nn.functional.embedding_bag, torch.unique,
@@ -105,6 +106,64 @@ def test_normal_init_distribution():
     assert abs(vals.mean()) < 3 * 0.01 / math.sqrt(vals.size) * 2
     assert abs(vals.std() / 0.01 - 1.0) < 0.02
     assert stats.kstest(vals / 0.01, "norm").pvalue > 1e-4
+
+
+# Keys whose angle draw (top 24 bits of draw_bits(17, 2, key, 1), the draw of
+# element d = 0 that sets the angle) is exactly 0, 1/4, 1/2 or 3/4 of a turn;
+# found by a search over keys 0 .. 2^27 with the SplitMix64 generator above.
+BM_SPECIAL = {0: 8887970, 1 << 22: 2850444, 1 << 23: 2767190, 3 << 22: 7346599}
+# a key whose radius draw (element 0) has top bits below 8 and whose angle is
+# within 1/128 turn of 0: the +1/2 offset of the radius uniform shows there
+BM_SMALL_RADIUS = 106498525
+
+
+def _radius(h1):
+    return math.sqrt(-2.0 * math.log(((h1 >> 40) + 0.5) / 16777216.0))
+
+
+def test_normal_init_box_muller_special_angles():
+    # Box-Muller's cosine branch: z = R cos(theta); at theta = 0 the deviate is
+    # the radius, at a half turn minus the radius, at a quarter turn 0.  A sine
+    # branch, a pi instead of 2 pi, or the two draws exchanged fails here.
+    for top, key in BM_SPECIAL.items():
+        h1, h2 = orc.draw_bits(17, 2, key, 0), orc.draw_bits(17, 2, key, 1)
+        assert h2 >> 40 == top
+        z = orc.init_normal(17, 2, key, 0, 1.0)
+        r = _radius(h1)
+        if top == 0:
+            assert z == np.float32(r)
+        elif top == 1 << 23:
+            assert z == np.float32(-r)
+        else:
+            assert abs(z) < 1e-6 * r
+
+
+def test_normal_init_box_muller_radius_offset():
+    h1, h2 = orc.draw_bits(17, 2, BM_SMALL_RADIUS, 0), orc.draw_bits(17, 2, BM_SMALL_RADIUS, 1)
+    top1, top2 = h1 >> 40, h2 >> 40
+    assert top1 < 8 and (top2 < (1 << 17) or top2 > (1 << 24) - (1 << 17))
+    cos_min = math.cos(2 * math.pi / 128)
+    r_half = _radius(h1)
+    r_plain = math.sqrt(-2.0 * math.log(top1 / 16777216.0)) if top1 else math.inf
+    assert r_plain * cos_min > r_half * (1 + 1e-6)  # the two readings are told apart
+    z = orc.init_normal(17, 2, BM_SMALL_RADIUS, 0, 1.0)
+    assert r_half * cos_min <= z <= r_half * (1 + 1e-6)
+
+
+def test_normal_init_sign_and_radius_bound():
+    # sign(z) = sign(cos(2 pi u2)) with u2 from the odd draw 2d + 1, and
+    # |z| <= R from the even draw 2d, for every element d
+    rng = np.random.default_rng(11)
+    keys = rng.integers(0, 2**63, 400, dtype=np.int64)
+    for k in keys:
+        for d in range(8):
+            h1 = orc.draw_bits(5, 1, int(k), 2 * d)
+            u2 = (orc.draw_bits(5, 1, int(k), 2 * d + 1) >> 40) / 16777216.0
+            z = orc.init_normal(5, 1, int(k), d, 1.0)
+            assert abs(z) <= _radius(h1) * (1 + 1e-6)
+            turn = u2 % 0.5
+            if 0.002 < abs(turn - 0.25):  # away from the zeros of the cosine
+                assert (z > 0) == (u2 < 0.25 or u2 > 0.75)
 
 
 # --------------------------------------------------------- hand-worked cases
