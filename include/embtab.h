@@ -204,12 +204,15 @@ emb_status_t emb_interact_backward(emb_table_t h, const int64_t* offsets, const 
  *   row_last_used: device uint32 [sum rows], by global row, the caller's
  *   record of each row's last use (for instance the row_periods written by
  *   emb_bag_backward_adagrad_decay_prepared with period = step; with rho = 1
- *   that is plain Adagrad).  Rows that hold no key are ignored.
+ *   that is plain Adagrad).  Rows that hold no key are ignored.  Every row
+ *   the call frees gets EMB_PERIOD_FRESH there, so that when it is the
+ *   row_periods array the key that next receives the row starts from an
+ *   undiscounted accumulator.
  *   ws: emb_hash_evict_workspace_bytes(h) bytes, 256-byte aligned (about
  *   16 bytes per slot plus one per row).
  * EMB_ERR_UNSUPPORTED on dense tables or without desc->free_rows. */
 size_t emb_hash_evict_workspace_bytes(emb_table_t h);
-emb_status_t emb_hash_evict(emb_table_t h, const uint32_t* row_last_used, uint32_t before,
+emb_status_t emb_hash_evict(emb_table_t h, uint32_t* row_last_used, uint32_t before,
                             uint32_t* key_counts, void* ws, size_t ws_bytes, void* stream);
 /* HOST out [T]: rows waiting in each table's free-row queue (waits for the stream). */
 emb_status_t emb_hash_free_rows(emb_table_t h, void* stream, int64_t* queued_out);
@@ -326,11 +329,16 @@ emb_status_t emb_bag_backward_adagrad_prepared(emb_table_t h, int64_t batch, int
  *   then the Adagrad step of emb_bag_backward_adagrad;
  *   row_periods[row] = max(s, period).
  * row_periods: device uint32 [sum of rows], caller-owned, 4-byte aligned,
- * all 0 at the start of training (rows start in period 0); only touched rows
- * are read and written.  rho in (0, 1]; rho = 1 is plain Adagrad.  period:
+ * all 0 at the start of training for dense tables (rows start in period 0),
+ * all EMB_PERIOD_FRESH for hashed tables; only touched rows are read and
+ * written.  EMB_PERIOD_FRESH marks a row whose key is new (never updated, or
+ * freed by emb_hash_evict and handed to another key): its accumulator is the
+ * initial one, which the row's next update does not discount; that update
+ * sets the row's period to `period`.  rho in (0, 1]; rho = 1 is plain Adagrad.  period:
  * the caller's step / period length.  rho^k is computed as
  * exp2f(k * log2(rho)) in fp32.  EMB_ERR_INVALID_ARG for a null or misaligned
  * row_periods or rho outside (0, 1]; EMB_ERR_UNSUPPORTED on tiered tables. */
+#define EMB_PERIOD_FRESH 0xFFFFFFFFu
 emb_status_t emb_bag_backward_adagrad_decay_prepared(emb_table_t h, int64_t batch, int64_t nnz,
                                                      emb_pool_t pool, const float* grad_out,
                                                      float lr, float eps, float rho,

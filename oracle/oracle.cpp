@@ -47,8 +47,11 @@
 //    multiplied by rho at each period boundary.  Done lazily, a row last
 //    updated in period s and updated again in period p first takes
 //    G <- rho^(p - s) * G (no discount when p <= s), then the Adagrad step;
-//    its period becomes max(s, p).  Rows start with period 0.  rho = 1 is
-//    Adagrad.
+//    its period becomes max(s, p).  Rows of dense tables start with period 0.
+//    A row of a hashed table that has no key yet, or was freed by eviction,
+//    is fresh (period all-ones): the key it next receives starts from the
+//    initial accumulator, which the following update does not discount; that
+//    update sets the row's period to p.  rho = 1 is Adagrad.
 //  * Sum or mean pooling; mean divides by the bag length L (duplicates count,
 //    out-of-range ids count in L but contribute nothing); an empty bag is 0.
 //  * Bags are table-major (bag b = t*B + s); the output is [B, T, D].
@@ -119,6 +122,7 @@ namespace {
 const uint64_t kReservedKey = ~0ull;
 const uint32_t kInvalidRow32 = 0xFFFFFFFFu;
 const int64_t kAbsentId = -2;  // a feature without a row (not admitted yet)
+const uint32_t kFreshPeriod = 0xFFFFFFFFu;  // Adagrad Decay: a row whose key is new
 
 // SplitMix64, one output step: the state advances by the golden-ratio
 // increment and the new state is passed through the variant-13 finalizer.
@@ -172,7 +176,13 @@ struct Model {
   bool has_dense = false;
   std::vector<float> W0, G0;               // explicit initial table (small cases)
   std::map<int64_t, RowState> touched;     // rows written since creation
-  std::map<int64_t, uint32_t> period_of;   // Adagrad Decay: period of the last update (else 0)
+  // Adagrad Decay: period of each row's last update; rows not listed are in
+  // period 0 (dense tables) or fresh (hashed tables)
+  std::map<int64_t, uint32_t> period_of;
+  uint32_t period_of_row(int64_t row) const {
+    auto it = period_of.find(row);
+    return it != period_of.end() ? it->second : (hashed ? kFreshPeriod : 0u);
+  }
   std::vector<std::map<uint64_t, int64_t>> keymap;
   std::vector<std::map<uint64_t, uint64_t>> seen;  // admission: occurrences of keys without a row
   std::vector<int64_t> n_live;                    // rows ever handed out (high-water mark)
@@ -434,14 +444,13 @@ int32_t orc_backward_adagrad_decay(void* h, const int64_t* offsets, const int64_
   const int32_t flags = row_gradients(m, offsets, ids, B, nnz, pool_mean, grad_out, gsum);
   if (flags & 2) return flags;
   adagrad_rows(m, gsum, lr, eps, [&](int64_t row) {
-    auto it = m->period_of.find(row);
-    const uint32_t last = it == m->period_of.end() ? 0u : it->second;
-    const double elapsed = period > last ? (double)(period - last) : 0.0;
+    const uint32_t last = m->period_of_row(row);
+    const double elapsed = (last != kFreshPeriod && period > last) ? (double)(period - last) : 0.0;
     return std::pow((double)rho, elapsed);
   });
   for (auto& kv : gsum) {
-    uint32_t& last = m->period_of[kv.first];  // 0 when new
-    if (period > last) last = period;
+    const uint32_t last = m->period_of_row(kv.first);
+    m->period_of[kv.first] = (last == kFreshPeriod || period > last) ? period : last;
   }
   return flags;
 }
@@ -452,8 +461,7 @@ int32_t orc_read_periods(void* h, const int64_t* grows, int64_t n, uint32_t* out
   const int64_t total = m->row_off[m->T];
   for (int64_t i = 0; i < n; ++i) {
     if (grows[i] < 0 || grows[i] >= total) return -1;
-    auto it = m->period_of.find(grows[i]);
-    out[i] = it == m->period_of.end() ? 0u : it->second;
+    out[i] = m->period_of_row(grows[i]);
   }
   return 0;
 }
@@ -693,7 +701,10 @@ int64_t orc_hash_evict(void* h, const uint32_t* last_used, uint32_t before) {
       }
     }
     std::sort(freed.begin(), freed.end());
-    for (int64_t r : freed) m->free_rows[t].push_back(r);
+    for (int64_t r : freed) {
+      m->free_rows[t].push_back(r);
+      m->period_of.erase(m->row_off[t] + r);  // fresh for the key it receives next
+    }
     n += (int64_t)freed.size();
     m->seen[t].clear();
   }

@@ -669,7 +669,7 @@ size_t emb_hash_evict_workspace_bytes(emb_table_t t) {
   return hash_evict_workspace_bytes(t->h);
 }
 
-emb_status_t emb_hash_evict(emb_table_t t, const uint32_t* row_last_used, uint32_t before,
+emb_status_t emb_hash_evict(emb_table_t t, uint32_t* row_last_used, uint32_t before,
                             uint32_t* key_counts, void* ws, size_t ws_bytes, void* stream) {
   if (!t || !row_last_used || (reinterpret_cast<uintptr_t>(row_last_used) & 3u) != 0 ||
       (reinterpret_cast<uintptr_t>(key_counts) & 3u) != 0)

@@ -21,6 +21,7 @@ constexpr uint64_t kPendingBit = 1ull << 62;           // row word = kPendingBit
 // above every kPendingBit | j, so the first-occurrence atomicMin still works
 constexpr uint64_t kCandRow = 0xFFFFFFFFFFFFFFFEull;
 constexpr int64_t kAbsentId = -2;  // id of a feature without a row: looks up 0, no error
+constexpr uint32_t kFreshPeriod = EMB_PERIOD_FRESH;  // Adagrad Decay: a row whose key is new
 constexpr uint32_t kNoRow = 0xFFFFFFFFu;
 constexpr int kMaxTables = 1024;
 
@@ -352,7 +353,7 @@ hipError_t launch_hash_find_or_insert(const Handle& h, const Plan& p, const int6
 
 hipError_t launch_hash_export(const Handle& h, int t, uint64_t* key_of_row, hipStream_t s);
 size_t hash_evict_workspace_bytes(const Handle& h);
-hipError_t launch_hash_evict(const Handle& h, const uint32_t* last_used, uint32_t before,
+hipError_t launch_hash_evict(const Handle& h, uint32_t* last_used, uint32_t before,
                              uint32_t* key_counts, char* ws, hipStream_t s);
 
 // Stream kernels (kind 0 copy, 1 fill, 2 read into one float per block).

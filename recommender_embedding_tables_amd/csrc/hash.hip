@@ -554,7 +554,7 @@ constexpr int64_t kEvictSpan = 4096;  // rows per counting block: 256 threads x 
 __global__ __launch_bounds__(256) void k_evict_rebuild(const Slot* __restrict__ old,
                                                        Slot* __restrict__ slots, int64_t cap,
                                                        const int64_t* __restrict__ row_off,
-                                                       const uint32_t* __restrict__ last_used,
+                                                       uint32_t* __restrict__ last_used,
                                                        uint32_t before,
                                                        uint8_t* __restrict__ flag) {
   const int32_t t = blockIdx.y;
@@ -566,6 +566,7 @@ __global__ __launch_bounds__(256) void k_evict_rebuild(const Slot* __restrict__ 
   const int64_t g = row_off[t] + (int64_t)sl.row;
   if (last_used[g] < before) {
     flag[g] = 1u;
+    last_used[g] = kFreshPeriod;  // the next key on this row starts undiscounted
     return;
   }
   Slot* st = slots + (size_t)t * (size_t)cap;
@@ -777,7 +778,7 @@ size_t hash_evict_workspace_bytes(const Handle& h) {
   return h.hashed ? evict_plan(h).total : 0;
 }
 
-hipError_t launch_hash_evict(const Handle& h, const uint32_t* last_used, uint32_t before,
+hipError_t launch_hash_evict(const Handle& h, uint32_t* last_used, uint32_t before,
                              uint32_t* key_counts, char* ws, hipStream_t s) {
   const EvictPlan p = evict_plan(h);
   uint8_t* flag = reinterpret_cast<uint8_t*>(ws + p.flag);

@@ -90,9 +90,15 @@ __device__ inline void adagrad_step(f4& w, f4& g2, const f4 g, float lr, float e
 
 // Adagrad Decay: the accumulator's discount for a row last updated in period
 // `last` (DeepRec page, section "model quality", Adagrad Decay Optimizer:
-// one discount per period).  rho^(period - last) as 2^(elapsed * log2 rho).
+// one discount per period).  rho^(period - last) as 2^(elapsed * log2 rho);
+// none for a fresh row (a new key's initial accumulator).
 __device__ inline float decay_factor(uint32_t last, uint32_t period, float log2_rho) {
-  return period > last ? exp2f((float)(period - last) * log2_rho) : 1.0f;
+  return (last != kFreshPeriod && period > last) ? exp2f((float)(period - last) * log2_rho)
+                                                 : 1.0f;
+}
+// Whether an update in `period` moves the row's period stamp (to `period`).
+__device__ inline bool period_advances(uint32_t last, uint32_t period) {
+  return last == kFreshPeriod || period > last;
 }
 
 // A run that crosses chunk boundaries but neither enters the block from the
@@ -232,7 +238,7 @@ __device__ __forceinline__ void seg_chunk(
             float df = 1.0f;
             if (DECAY) {
               df = decay_factor(last[u], period, log2_rho);
-              if (lane == 0 && period > last[u]) stamps[kk[u]] = period;
+              if (lane == 0 && period_advances(last[u], period)) stamps[kk[u]] = period;
             }
 #pragma unroll
             for (int v = 0; v < VEC; ++v) {
@@ -330,7 +336,7 @@ __device__ __forceinline__ void span_arrive(
   float df = 1.0f;
   if (DECAY) {
     df = decay_factor(last, period, log2_rho);
-    if (lane == 0 && period > last) stamps[row] = period;
+    if (lane == 0 && period_advances(last, period)) stamps[row] = period;
   }
 #pragma unroll
   for (int v = 0; v < VEC; ++v) {
@@ -425,7 +431,7 @@ __global__ __launch_bounds__(256) void k_seg_adagrad(
   int i0 = sgb;
   while (i0 > 0 && s_key[i0 - 1] == fin.row) --i0;
   const float df = DECAY ? decay_factor(fin.last, period, log2_rho) : 1.0f;
-  if (DECAY && lane == 0 && period > fin.last) stamps[fin.row] = period;
+  if (DECAY && lane == 0 && period_advances(fin.last, period)) stamps[fin.row] = period;
 #pragma unroll
   for (int v = 0; v < VEC; ++v) {
     const int d4 = lane + v * SG;

@@ -34,6 +34,7 @@ EMB_FLAG_CACHE_FULL = 32
 
 EMB_CACHE_WAYS = 16
 EMB_NOALLOC_SCRATCH_BYTES = 64 << 20
+EMB_PERIOD_FRESH = 0xFFFFFFFF
 EMB_ID_ABSENT = -2
 
 EMB_POOL_SUM = 0

@@ -15,6 +15,79 @@ import numpy as np
 REL, ABS = 1e-5, 1e-6
 
 
+class StepBounds:
+    """The per-step rule carried over several Adagrad steps (first-order error
+    propagation), per element of every row:
+
+      before the first step   e_W = e_G = 0 (the initial tables are bit-exact);
+                              a hashed row given a key: e_W = REL*|w0| + ABS, e_G = 0
+      step i on a row         a = sum_k c_k |grad_k| of the row in this step
+        e_G <- e_G + REL*(|G_before| + a^2) + ABS
+        e_W <- e_W + REL*(|w_before| + lr*a/(sqrt(G_after)+eps)) + ABS
+                   + lr*a/(2*G_after^1.5) * e_G          (the step's sensitivity to G)
+      rows a step does not touch keep their bounds.
+
+    An input error passes into the next step with factor 1 (w' = w - ..., G' =
+    G*df + g^2 with df <= 1), so the bounds add up along the oracle's own
+    trajectory, read before and after each oracle step."""
+
+    def __init__(self, total_rows, D):
+        self.eW = np.zeros((int(total_rows), int(D)))
+        self.eG = np.zeros((int(total_rows), int(D)))
+
+    def assigned(self, o, rows):
+        """Rows that just got a key: fresh initial values (within the rule)."""
+        rows = np.asarray(rows, np.int64)
+        if rows.size:
+            W, _ = o.read_rows(rows)
+            self.eW[rows] = REL * np.abs(W.astype(np.float64)) + ABS
+            self.eG[rows] = 0.0
+
+    def step(self, o, rows_u, sums, lr, eps, oracle_step):
+        """Runs oracle_step() (the oracle's update of rows_u) and carries the bounds."""
+        rows_u = np.asarray(rows_u, np.int64)
+        W0, G0 = o.read_rows(rows_u) if rows_u.size else (None, None)
+        rc = oracle_step()
+        if rows_u.size:
+            W1, G1 = o.read_rows(rows_u)
+            a = np.asarray(sums, np.float64)
+            G1 = G1.astype(np.float64)
+            eG = self.eG[rows_u] + REL * (np.abs(G0.astype(np.float64)) + a * a) + ABS
+            eW = (self.eW[rows_u] + ABS +
+                  REL * (np.abs(W0.astype(np.float64)) + lr * a / (np.sqrt(G1) + eps)) +
+                  lr * a / (2.0 * G1 ** 1.5) * eG)
+            self.eG[rows_u] = eG
+            self.eW[rows_u] = eW
+        return rc
+
+    def check(self, W_gpu, G_gpu, W_ref, G_ref, rows, what):
+        rows = np.asarray(rows, np.int64)
+        for name, g, r, e in (("weights", W_gpu, W_ref, self.eW[rows]),
+                              ("accumulators", G_gpu, G_ref, self.eG[rows])):
+            err = np.abs(np.asarray(g, np.float64) - np.asarray(r, np.float64))
+            bad = err > e
+            if bad.any():
+                idx = np.argwhere(bad)[:5]
+                raise AssertionError(
+                    f"{what} {name}: {int(bad.sum())} of {bad.size} outside the carried bound; "
+                    f"first {idx.tolist()}: err {err[bad][:5]} bound {e[bad][:5]}")
+
+
+def key_rows(o):
+    """{global row: key} of every live key of a hashed oracle."""
+    m = {}
+    for t in range(o.T):
+        k, r = o.export(t)
+        base = int(o.row_off[t])
+        m.update({base + int(rr): int(kk) for kk, rr in zip(k, r)})
+    return m
+
+
+def rows_given_keys(before, after):
+    """Global rows whose key in `after` is new (inserted, or reused after eviction)."""
+    return np.array(sorted(r for r, k in after.items() if before.get(r) != k), np.int64)
+
+
 def assert_within(gpu, ref, S, what):
     gpu = np.asarray(gpu, np.float64)
     ref = np.asarray(ref, np.float64)
@@ -79,3 +152,29 @@ def forward_S(offsets, ids, B, rows, W_rows_of, pool_mean, D):
         S_bag[nonempty] /= lens[nonempty, None]
     # table-major bags -> [B, T, D]
     return S_bag.reshape(T, B, D).transpose(1, 0, 2)
+
+
+# ------------------------------------------------------------ guard bands
+GUARD_BYTES = 4096  # a multiple of 256: the guarded region keeps its alignment
+CANARY = 0xA5
+
+
+class Guarded:
+    """A device buffer of `nbytes` (viewed as `shape` of `dtype`) with GUARD_BYTES
+    canary bytes before and after it; check() asserts that no call wrote there."""
+
+    def __init__(self, shape, dtype, device, nbytes=None):
+        import torch
+        if nbytes is None:
+            nbytes = int(np.prod(shape)) * torch.empty((), dtype=dtype).element_size()
+        self.nbytes = int(nbytes)
+        self.buf = torch.full((2 * GUARD_BYTES + self.nbytes,), CANARY, dtype=torch.uint8,
+                              device=device)
+        inner = self.buf[GUARD_BYTES:GUARD_BYTES + self.nbytes]
+        self.t = inner.view(dtype).view(shape) if shape is not None else inner
+
+    def check(self, what):
+        head = self.buf[:GUARD_BYTES]
+        tail = self.buf[GUARD_BYTES + self.nbytes:]
+        ok = bool((head == CANARY).all()) and bool((tail == CANARY).all())
+        assert ok, f"{what}: a call wrote outside its buffer (guard band changed)"

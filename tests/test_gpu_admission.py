@@ -8,7 +8,8 @@ import torch
 
 from oracle import oracle as orc
 from recommender_embedding_tables_amd import synth
-from tests.helpers import abs_grad_sums, assert_within, forward_S
+from tests.helpers import (REL, StepBounds, abs_grad_sums, assert_within, forward_S, key_rows,
+                           rows_given_keys)
 from tests.test_gpu_parity import _hash_call, _t, check_hash_state, make_pair, status
 
 pytestmark = pytest.mark.gpu
@@ -103,14 +104,16 @@ def test_training_on_absent_ids():
     w.rows = np.full(2, int(0.625 * (1 << 15)), np.int64)
     tabs, o = make_pair(w.rows, w.D, seed=8, hashed=True, cap=w.hash_capacity)
     counts = counts_for(tabs)
-    # a row's weight carries the bound of every step that updated it:
-    # lr * sum_k c_k |g_k| / (sqrt(G') + eps) per step (tests/helpers.py)
-    carried = np.zeros((int(np.sum(w.rows)), w.D))
+    # the per-step rule carried over the steps (tests/helpers.py StepBounds);
+    # a lookup of a row adds that row's carried weight bound to its term
+    bounds = StepBounds(int(np.sum(w.rows)), w.D)
     for step in range(3):
         offsets, ranks = synth.gen_batch(w, step)
         keys = synth.gen_keys(w, offsets, ranks)
         ids = admit_call(tabs, counts, offsets, keys, w.B, 3)
+        before = key_rows(o)
         ref, _ = o.find_or_insert_admit(offsets, keys, w.B, 3)
+        bounds.assigned(o, rows_given_keys(before, key_rows(o)))
         np.testing.assert_array_equal(ids, ref)
         assert (ids == eb.EMB_ID_ABSENT).any()
         for mean in (False, True):
@@ -121,20 +124,21 @@ def test_training_on_absent_ids():
             torch.cuda.synchronize()
             r, fl = o.forward(offsets, ids, w.B, mean)
             assert fl == 0
-            S = forward_S(offsets, ids, w.B, o.rows,
-                          lambda g: np.abs(o.read_rows(g)[0]) + carried[g], mean, w.D)
+            S = (forward_S(offsets, ids, w.B, o.rows, lambda g: np.abs(o.read_rows(g)[0]), mean,
+                           w.D) +
+                 forward_S(offsets, ids, w.B, o.rows, lambda g: bounds.eW[g], mean, w.D) / REL)
             assert_within(out.cpu().numpy(), r, S, f"forward step {step}")
         grad = synth.gen_grad(w, step)
         ws, need = tabs.workspace(w.B, ids.size)
         eb.check(eb.emb_bag_backward_adagrad(tabs.handle, _t(offsets), _t(ids), w.B, ids.size,
                                              eb.EMB_POOL_SUM, _t(grad), w.lr, w.eps, ws, need),
                  "backward")
-        assert o.backward_adagrad(offsets, ids, w.B, False, grad, w.lr, w.eps) == 0
         rows_u, sums = abs_grad_sums(offsets, ids, w.B, o.rows, grad, False, w.D)
-        carried[rows_u] += w.lr * sums / (np.sqrt(o.read_rows(rows_u)[1]) + w.eps)
+        assert bounds.step(o, rows_u, sums, w.lr, w.eps, lambda: o.backward_adagrad(
+            offsets, ids, w.B, False, grad, w.lr, w.eps)) == 0
         assert status(tabs) == (eb.EMB_OK, 0)
     st, n_live = eb.emb_hash_n_live(tabs.handle, tabs.T)
     live = np.concatenate([np.arange(n) + int(np.sum(w.rows[:t])) for t, n in enumerate(n_live)])
     Wr, Gr = o.read_rows(live)
-    assert_within(tabs.weights[_t(live)].cpu().numpy(), Wr, np.abs(Wr) + carried[live], "weights")
-    assert_within(tabs.accum[_t(live)].cpu().numpy(), Gr, np.abs(Gr) * 3, "accumulators")
+    bounds.check(tabs.weights[_t(live)].cpu().numpy(), tabs.accum[_t(live)].cpu().numpy(), Wr, Gr,
+                 live, "admission, 3 steps")

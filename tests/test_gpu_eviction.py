@@ -9,7 +9,7 @@ import torch
 
 from oracle import oracle as orc
 from recommender_embedding_tables_amd import synth
-from tests.helpers import abs_grad_sums, assert_within
+from tests.helpers import StepBounds, abs_grad_sums, key_rows, rows_given_keys
 from tests.test_gpu_parity import _hash_call, _t, check_hash_state, make_pair, status
 from tests.test_gpu_admission import admit_call, counts_for
 
@@ -87,47 +87,59 @@ def test_eviction_drops_counted_keys_and_keeps_admitting():
     check_hash_state(tabs, o)
 
 
-def test_lifecycle_admission_decay_eviction():
-    # admission on insert, Adagrad Decay with rho = 1 (plain Adagrad) whose
-    # row periods are each row's last training step, eviction by those periods
+@pytest.mark.parametrize("rho", [1.0, 0.8])
+def test_lifecycle_admission_decay_eviction(rho):
+    # admission on insert, Adagrad Decay whose row periods are each row's last
+    # training step, eviction by those periods, freed rows handed to new keys.
+    # The periods start fresh (hashed tables); eviction marks the rows it frees
+    # fresh again, so a reused row's new key starts undiscounted (rho < 1).
     w = synth.workload(5, T=2, B=1500, universe=25_000, hash_capacity=1 << 15)
     w.rows = np.full(2, 9000, np.int64)
     tabs, o = make_pair(w.rows, w.D, seed=33, hashed=True, cap=w.hash_capacity)
     counts = counts_for(tabs)
     total = int(np.sum(w.rows))
-    periods = torch.zeros(total, dtype=torch.int32, device=DEV)
-    carried = np.zeros((total, w.D))
+    periods = torch.full((total,), -1, dtype=torch.int32, device=DEV)  # EMB_PERIOD_FRESH
+    bounds = StepBounds(total, w.D)
+    reused, ever_live = 0, set()
     for step in range(1, 9):
         offsets, ranks = synth.gen_batch(w, step)
         keys = synth.gen_keys(w, offsets, ranks)
         ids = admit_call(tabs, counts, offsets, keys, w.B, 2)
+        before = key_rows(o)
         np.testing.assert_array_equal(ids, o.find_or_insert_admit(offsets, keys, w.B, 2)[0])
+        after = key_rows(o)
+        new_rows = rows_given_keys(before, after)
+        reused += sum(1 for r in new_rows if int(r) in ever_live)  # rows freed by an eviction
+        ever_live.update(after)
+        bounds.assigned(o, new_rows)
         grad = synth.gen_grad(w, step)
         ws, need = tabs.workspace(w.B, ids.size)
         eb.check(eb.emb_bag_prepare(tabs.handle, _t(offsets), _t(ids), w.B, ids.size,
                                     eb.EMB_POOL_SUM, ws, need), "prepare")
         eb.check(eb.emb_bag_backward_adagrad_decay_prepared(
-            tabs.handle, w.B, ids.size, eb.EMB_POOL_SUM, _t(grad), w.lr, w.eps, 1.0, step,
+            tabs.handle, w.B, ids.size, eb.EMB_POOL_SUM, _t(grad), w.lr, w.eps, rho, step,
             periods, ws, need), "backward")
-        o.backward_adagrad_decay(offsets, ids, w.B, False, grad, w.lr, w.eps, 1.0, step)
         rows_u, sums = abs_grad_sums(offsets, ids, w.B, o.rows, grad, False, w.D)
-        carried[rows_u] += w.lr * sums / (np.sqrt(o.read_rows(rows_u)[1]) + w.eps)
+        bounds.step(o, rows_u, sums, w.lr, w.eps,
+                    lambda: o.backward_adagrad_decay(offsets, ids, w.B, False, grad, w.lr, w.eps,
+                                                     rho, step))
         if step % 3 == 0:
             o_last = o.read_periods(np.arange(total))
             torch.cuda.synchronize()
             np.testing.assert_array_equal(periods.cpu().numpy().view(np.uint32), o_last)
             evict(tabs, periods, step - 1, counts)
-            o.evict(o_last, step - 1)  # (a reused row keeps its old bound: looser, still valid)
+            o.evict(o_last, step - 1)
+            torch.cuda.synchronize()
+            # the freed rows are fresh on both sides
+            np.testing.assert_array_equal(periods.cpu().numpy().view(np.uint32),
+                                          o.read_periods(np.arange(total)))
         assert status(tabs) == (eb.EMB_OK, 0)
+    assert reused > 0  # freed rows were handed to new keys
     st, n_live = eb.emb_hash_n_live(tabs.handle, tabs.T)
-    keys_live = []
-    for t in range(tabs.T):
-        k, r = o.export(t)
-        keys_live.append(r + int(np.sum(w.rows[:t])))
-    live = np.concatenate(keys_live)
+    live = np.array(sorted(key_rows(o)), np.int64)
     Wr, Gr = o.read_rows(live)
-    assert_within(tabs.weights[_t(live)].cpu().numpy(), Wr, np.abs(Wr) + carried[live], "weights")
-    assert_within(tabs.accum[_t(live)].cpu().numpy(), Gr, np.abs(Gr) * 8, "accumulators")
+    bounds.check(tabs.weights[_t(live)].cpu().numpy(), tabs.accum[_t(live)].cpu().numpy(), Wr, Gr,
+                 live, "lifecycle")
 
 
 def test_evict_everything_then_reinsert():

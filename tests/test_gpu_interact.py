@@ -10,7 +10,7 @@ import torch
 
 from oracle import oracle as orc
 from recommender_embedding_tables_amd import synth
-from tests.helpers import assert_within, forward_S
+from tests.helpers import Guarded, assert_within, forward_S
 
 pytestmark = pytest.mark.gpu
 
@@ -69,10 +69,13 @@ def test_interaction_matches_oracle(name):
     odim = eb.emb_interact_out_dim(tabs.handle)
     P = (w.T + 1) * w.T // 2
     assert odim == w.D + P
-    out = torch.empty((w.B, odim), dtype=torch.float32, device=DEV)
+    out_g = Guarded((w.B, odim), torch.float32, DEV)
+    out = out_g.t
     d_off, d_ids, d_dense = _t(offsets), _t(ids), _t(dense)
     eb.check(eb.emb_bag_forward_interact(tabs.handle, d_off, d_ids, w.B, ids.size, pool, d_dense,
                                          out), "forward_interact")
+    torch.cuda.synchronize()
+    out_g.check("interaction output")
     ref, rc = o.interact_forward(offsets, ids, w.B, mean, dense)
     assert rc == 0
     Z = z_abs(o, w, offsets, ids, dense, mean)
@@ -83,10 +86,14 @@ def test_interaction_matches_oracle(name):
     assert_within(got, ref, S, "interaction")
     # backward
     g = rng.standard_normal((w.B, odim)).astype(np.float32)
-    gd = torch.empty((w.B, w.D), dtype=torch.float32, device=DEV)
-    gp = torch.empty((w.B, w.T, w.D), dtype=torch.float32, device=DEV)
+    gd_g = Guarded((w.B, w.D), torch.float32, DEV)
+    gp_g = Guarded((w.B, w.T, w.D), torch.float32, DEV)
+    gd, gp = gd_g.t, gp_g.t
     eb.check(eb.emb_interact_backward(tabs.handle, d_off, d_ids, w.B, ids.size, pool, d_dense,
                                       _t(g), gd, gp), "interact_backward")
+    torch.cuda.synchronize()
+    gd_g.check("grad dense")
+    gp_g.check("grad pooled")
     rgd, rgp, rc = o.interact_backward(offsets, ids, w.B, mean, dense, g)
     assert rc == 0
     Gs = np.zeros((w.B, w.T + 1, w.T + 1))

@@ -10,7 +10,8 @@ import torch
 
 from oracle import oracle as orc
 from recommender_embedding_tables_amd import synth
-from tests.helpers import abs_grad_sums, assert_within, forward_S, occurrence_rows
+from tests.helpers import (Guarded, StepBounds, abs_grad_sums, assert_within, forward_S,
+                           occurrence_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -40,32 +41,47 @@ def status(tabs):
     return eb.emb_status_sync(tabs.handle)
 
 
+def guarded_workspace(tabs, B, nnz):
+    need = eb.emb_workspace_bytes(tabs.handle, B, nnz)
+    assert need > 0
+    return Guarded(None, torch.uint8, DEV, nbytes=need), need
+
+
 def gpu_forward(tabs, offsets, ids, B, mean):
-    out = torch.empty((B, tabs.T, tabs.D), dtype=torch.float32, device=DEV)
+    out = Guarded((B, tabs.T, tabs.D), torch.float32, DEV)
     eb.check(eb.emb_bag_forward(tabs.handle, _t(offsets), _t(ids), B, ids.size,
-                                eb.EMB_POOL_MEAN if mean else eb.EMB_POOL_SUM, out), "forward")
-    return out
+                                eb.EMB_POOL_MEAN if mean else eb.EMB_POOL_SUM, out.t), "forward")
+    torch.cuda.synchronize()
+    out.check("forward output")
+    return out.t
 
 
 def gpu_backward(tabs, offsets, ids, B, mean, grad, lr, eps):
-    ws, need = tabs.workspace(B, ids.size)
+    ws, need = guarded_workspace(tabs, B, ids.size)
     g = _t(grad)
     eb.check(eb.emb_bag_backward_adagrad(tabs.handle, _t(offsets), _t(ids), B, ids.size,
                                          eb.EMB_POOL_MEAN if mean else eb.EMB_POOL_SUM, g, lr, eps,
-                                         ws, need), "backward")
+                                         ws.t, need), "backward")
+    torch.cuda.synchronize()
+    ws.check("backward workspace")
 
 
 def gpu_sort_unique(tabs, offsets, ids, B):
     n = ids.size
     u32 = dict(dtype=torch.int32, device=DEV)
-    out = {k: torch.empty(n, **u32) for k in ("sorted_rows", "perm", "unique", "counts", "inverse")}
-    out["seg_off"] = torch.empty(n + 1, **u32)
+    gd = {k: Guarded((n,), torch.int32, DEV)
+          for k in ("sorted_rows", "perm", "unique", "counts", "inverse")}
+    gd["seg_off"] = Guarded((n + 1,), torch.int32, DEV)
+    out = {k: v.t for k, v in gd.items()}
     nu = torch.zeros(1, **u32)
-    ws, need = tabs.workspace(B, n)
+    ws, need = guarded_workspace(tabs, B, n)
     eb.check(eb.emb_debug_sort_unique(tabs.handle, _t(offsets), _t(ids), B, n, out["sorted_rows"],
                                       out["perm"], out["unique"], out["counts"], out["seg_off"],
-                                      out["inverse"], nu, ws, need), "sort_unique")
+                                      out["inverse"], nu, ws.t, need), "sort_unique")
     torch.cuda.synchronize()
+    ws.check("sort/unique workspace")
+    for k, v in gd.items():
+        v.check(k)
     U = int(nu.item())
     res = {k: v.cpu().numpy().view(np.uint32) for k, v in out.items()}
     res["unique"] = res["unique"][:U]
@@ -339,7 +355,7 @@ def test_backward_run_lengths_cross_chunk_boundaries(D, mean):
     # start and end at every offset of the 32- and 64-position reduction
     # chunks: runs inside one chunk, across chunk boundaries inside one
     # reduction block (parts added in LDS by the block) and across block
-    # boundaries (partial sums + fixup).
+    # boundaries (one part per block, added by the span's last block to arrive).
     nrows = 600
     lens = 1 + np.arange(nrows) % 97
     ids = np.repeat(np.arange(nrows, dtype=np.int64), lens)
@@ -423,19 +439,19 @@ def test_backward_random_sweep(seed):
 def test_backward_one_hot_zipf_two_steps():
     w = synth.workload(2, T=4, B=20000, rows=[100, 3000, 1_000_000, 20])
     tabs, o = make_pair(w.rows, w.D, seed=4)
+    bounds = StepBounds(int(np.sum(w.rows)), w.D)
     for step in range(2):
         offsets, ids = synth.gen_batch(w, step)
         grad = synth.gen_grad(w, step)
         gpu_backward(tabs, offsets, ids, w.B, False, grad, w.lr, w.eps)
-        o.backward_adagrad(offsets, ids, w.B, False, grad, w.lr, w.eps)
-    # compare the union of touched rows after both steps
+        rows_u, sums = abs_grad_sums(offsets, ids, w.B, o.rows, grad, False, w.D)
+        bounds.step(o, rows_u, sums, w.lr, w.eps,
+                    lambda: o.backward_adagrad(offsets, ids, w.B, False, grad, w.lr, w.eps))
+    # the union of touched rows after both steps, within the carried bound
     rows = o.touched_rows()
-    Wg = tabs.weights[_t(rows)].cpu().numpy()
-    Gg = tabs.accum[_t(rows)].cpu().numpy()
     Wr, Gr = o.read_rows(rows)
-    # two steps: bound by the per-step bound applied twice (|w| + 2*lr, |G| stays the scale)
-    assert_within(Gg, Gr, np.abs(Gr) * 2, "accumulator (2 steps)")
-    assert_within(Wg, Wr, np.abs(Wr) + 2 * w.lr, "weights (2 steps)")
+    bounds.check(tabs.weights[_t(rows)].cpu().numpy(), tabs.accum[_t(rows)].cpu().numpy(), Wr, Gr,
+                 rows, "two steps")
 
 
 def test_backward_is_deterministic():
@@ -477,12 +493,14 @@ def test_backward_empty_batch_is_noop():
 # ----------------------------------------------------------------- hash
 
 def _hash_call(tabs, offsets, keys, B):
-    ids = torch.empty(keys.size, dtype=torch.int64, device=DEV)
-    ws, need = tabs.workspace(B, keys.size)
+    ids = Guarded((keys.size,), torch.int64, DEV)
+    ws, need = guarded_workspace(tabs, B, keys.size)
     eb.check(eb.emb_hash_find_or_insert(tabs.handle, _t(offsets), _t(keys.view(np.int64)), B,
-                                        keys.size, ids, ws, need), "find_or_insert")
+                                        keys.size, ids.t, ws.t, need), "find_or_insert")
     torch.cuda.synchronize()
-    return ids.cpu().numpy()
+    ids.check("find_or_insert ids")
+    ws.check("find_or_insert workspace")
+    return ids.t.cpu().numpy()
 
 
 def _export(tabs, t):
@@ -663,14 +681,19 @@ def test_forward_prepared_matches_oracle(case):
         assert offsets[-1] == ids.size == w.B * w.T
     tabs, o = make_pair(w.rows, w.D, seed=31)
     d_off, d_ids = _t(offsets), _t(ids)
-    ws, need = tabs.workspace(w.B, ids.size)
+    wsg, need = guarded_workspace(tabs, w.B, ids.size)
+    ws = wsg.t
     pool = eb.EMB_POOL_MEAN if mean else eb.EMB_POOL_SUM
     eb.check(eb.emb_bag_prepare(tabs.handle, d_off, d_ids, w.B, ids.size, pool, ws, need),
              "prepare")
-    out = torch.full((w.B, w.T, w.D), float("nan"), dtype=torch.float32, device=DEV)
+    outg = Guarded((w.B, w.T, w.D), torch.float32, DEV)
+    out = outg.t
+    out.fill_(float("nan"))
     eb.check(eb.emb_bag_forward_prepared(tabs.handle, d_off, d_ids, w.B, ids.size, pool, out, ws,
                                          need), "forward_prepared")
     torch.cuda.synchronize()
+    outg.check("forward_prepared output")
+    wsg.check("prepared workspace")
     ref, fl = o.forward(offsets, ids, w.B, mean)
     if case.startswith("one_hot"):
         np.testing.assert_array_equal(out.cpu().numpy(), ref)  # a copy of one row, or 0
@@ -686,6 +709,7 @@ def test_forward_prepared_matches_oracle(case):
                                                   w.eps, ws, need), "backward_prepared")
     o.backward_adagrad(offsets, ids, w.B, mean, grad, w.lr, w.eps)
     torch.cuda.synchronize()
+    wsg.check("prepared workspace after the backward")
     check_rows(tabs, o, offsets, ids, w.B, mean, grad, w.lr, w.eps)
 
 

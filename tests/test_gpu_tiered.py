@@ -8,7 +8,7 @@ import torch
 
 from oracle import oracle as orc
 from recommender_embedding_tables_amd import synth
-from tests.helpers import abs_grad_sums, assert_within, forward_S
+from tests.helpers import REL, StepBounds, abs_grad_sums, assert_within, forward_S
 
 pytestmark = pytest.mark.gpu
 
@@ -65,19 +65,30 @@ def host_rows(tabs, rows):
     return tabs.host_weights[r].numpy(), tabs.host_accum[r].numpy()
 
 
-def check_all_rows(tabs, o, total, bound_steps):
-    """Touched rows within the bound of `bound_steps` steps, the rest exact."""
+def check_all_rows(tabs, o, total, bounds):
+    """Touched rows within the per-step rule carried over the steps, the rest exact."""
     touched = o.touched_rows()
     Wg, Gg = host_rows(tabs, touched)
     Wr, Gr = o.read_rows(touched)
-    lr = 0.01
-    assert_within(Gg, Gr, np.abs(Gr).astype(np.float64) * bound_steps, "accumulator")
-    assert_within(Wg, Wr, np.abs(Wr) + bound_steps * lr, "weights")
+    bounds.check(Wg, Gg, Wr, Gr, touched, "tiered rows")
     rest = np.setdiff1d(np.arange(total), touched)
     Wg, Gg = host_rows(tabs, rest)
     Wr, Gr = o.read_rows(rest)
     np.testing.assert_array_equal(Wg, Wr)
     np.testing.assert_array_equal(Gg, Gr)
+
+
+def oracle_step(bounds, o, offsets, ids, B, mean, grad, w):
+    """The oracle's backward + Adagrad, with the bounds carried over it."""
+    rows_u, sums = abs_grad_sums(offsets, ids, B, o.rows, grad, mean, w.D)
+    bounds.step(o, rows_u, sums, w.lr, w.eps,
+                lambda: o.backward_adagrad(offsets, ids, B, mean, grad, w.lr, w.eps))
+
+
+def forward_bound(bounds, o, offsets, ids, B, mean, D):
+    """S of the pooled outputs, plus the carried weight bounds of the rows they read."""
+    return (forward_S(offsets, ids, B, o.rows, lambda r: np.abs(o.read_rows(r)[0]), mean, D) +
+            forward_S(offsets, ids, B, o.rows, lambda r: bounds.eW[r], mean, D) / REL)
 
 
 def prepared_step(tabs, w, offsets, ids, grad, pool, ws, need, stream=None):
@@ -106,6 +117,7 @@ def test_tiered_matches_dense_oracle(case):
     worst, over, distinct = set_pressure(w, batches, nsets)
     assert worst <= eb.EMB_CACHE_WAYS and over > 0
     tabs, o = make_tiered(w.rows, w.D, nsets * eb.EMB_CACHE_WAYS)
+    bounds = StepBounds(int(np.sum(w.rows)), w.D)
     pool = eb.EMB_POOL_MEAN if mean else eb.EMB_POOL_SUM
     for step in range(steps):
         offsets, ids = batches[step]
@@ -114,17 +126,16 @@ def test_tiered_matches_dense_oracle(case):
         out = prepared_step(tabs, w, offsets, ids, grad, pool, ws, need)
         torch.cuda.synchronize()
         ref, _ = o.forward(offsets, ids, w.B, mean)
-        S = forward_S(offsets, ids, w.B, o.rows, lambda r: o.read_rows(r)[0], mean, w.D)
-        # rows read at step k carry k steps of rounding: bound by the rows' size
-        assert_within(out.cpu().numpy(), ref, S + 2 * step * w.lr, f"forward step {step}")
-        o.backward_adagrad(offsets, ids, w.B, mean, grad, w.lr, w.eps)
+        S = forward_bound(bounds, o, offsets, ids, w.B, mean, w.D)
+        assert_within(out.cpu().numpy(), ref, S, f"forward step {step}")
+        oracle_step(bounds, o, offsets, ids, w.B, mean, grad, w)
     st, looked, missed, wrote = eb.emb_cache_stats(tabs.handle)
     assert st == eb.EMB_OK and 0 < missed <= looked
     assert missed > distinct  # rows were evicted and fetched again
     # a miss writes a row back unless it fills a slot for the first time, and
     # at most min(slots, distinct rows) slots are ever filled
     assert missed - min(nsets * eb.EMB_CACHE_WAYS, distinct) <= wrote < missed
-    check_all_rows(tabs, o, int(np.sum(w.rows)), steps)
+    check_all_rows(tabs, o, int(np.sum(w.rows)), bounds)
     assert eb.emb_status_sync(tabs.handle) == (eb.EMB_OK, 0)
     tabs.close()
 
@@ -136,6 +147,7 @@ def test_tiered_one_call_backward_and_refetch():
     worst, over, distinct = set_pressure(w, batches, nsets)
     assert worst <= eb.EMB_CACHE_WAYS and over > 0
     tabs, o = make_tiered(w.rows, w.D, nsets * eb.EMB_CACHE_WAYS)
+    bounds = StepBounds(int(np.sum(w.rows)), w.D)
     for step in range(steps):
         offsets, ids = batches[step]
         grad = synth.gen_grad(w, step)
@@ -143,12 +155,12 @@ def test_tiered_one_call_backward_and_refetch():
         eb.check(eb.emb_bag_backward_adagrad(tabs.handle, _t(offsets), _t(ids), w.B, ids.size,
                                              eb.EMB_POOL_SUM, _t(grad), w.lr, w.eps, ws, need),
                  "backward")
-        o.backward_adagrad(offsets, ids, w.B, False, grad, w.lr, w.eps)
+        oracle_step(bounds, o, offsets, ids, w.B, False, grad, w)
     # the non-prepared forward needs the prepare's row resolution
     out = torch.empty((w.B, w.T, w.D), dtype=torch.float32, device=DEV)
     assert eb.emb_bag_forward(tabs.handle, _t(offsets), _t(ids), w.B, ids.size, eb.EMB_POOL_SUM,
                               out) == eb.EMB_ERR_UNSUPPORTED
-    check_all_rows(tabs, o, int(np.sum(w.rows)), steps)
+    check_all_rows(tabs, o, int(np.sum(w.rows)), bounds)
     st, looked, missed, wrote = eb.emb_cache_stats(tabs.handle)
     assert st == eb.EMB_OK and distinct < missed <= looked
     assert missed - min(nsets * eb.EMB_CACHE_WAYS, distinct) <= wrote < missed
@@ -165,6 +177,7 @@ def test_tiered_pipelined_two_workspaces():
     worst, over, distinct = set_pressure(w, batches, nsets)
     assert worst <= eb.EMB_CACHE_WAYS and over > 0
     tabs, o = make_tiered(w.rows, w.D, nsets * eb.EMB_CACHE_WAYS)
+    bounds = StepBounds(int(np.sum(w.rows)), w.D)
     grads = [synth.gen_grad(w, b) for b in range(steps)]
     nnz = batches[0][1].size
     ws0, need = tabs.workspace(w.B, nnz)
@@ -199,10 +212,10 @@ def test_tiered_pipelined_two_workspaces():
     for i in range(steps):
         offsets, ids = batches[i]
         ref, _ = o.forward(offsets, ids, w.B, False)
-        S = forward_S(offsets, ids, w.B, o.rows, lambda r: o.read_rows(r)[0], False, w.D)
-        assert_within(outs[i].cpu().numpy(), ref, S + 2 * i * w.lr, f"forward {i}")
-        o.backward_adagrad(offsets, ids, w.B, False, grads[i], w.lr, w.eps)
-    check_all_rows(tabs, o, int(np.sum(w.rows)), steps)
+        S = forward_bound(bounds, o, offsets, ids, w.B, False, w.D)
+        assert_within(outs[i].cpu().numpy(), ref, S, f"forward {i}")
+        oracle_step(bounds, o, offsets, ids, w.B, False, grads[i], w)
+    check_all_rows(tabs, o, int(np.sum(w.rows)), bounds)
     st, looked, missed, wrote = eb.emb_cache_stats(tabs.handle)
     assert st == eb.EMB_OK and distinct < missed <= looked
     assert missed - min(nsets * eb.EMB_CACHE_WAYS, distinct) <= wrote < missed
@@ -275,6 +288,7 @@ def test_tiered_three_streams_split_prepare():
     worst, over, distinct = set_pressure(w, batches, nsets)
     assert worst <= eb.EMB_CACHE_WAYS and over > 0
     tabs, o = make_tiered(w.rows, w.D, nsets * eb.EMB_CACHE_WAYS)
+    bounds = StepBounds(int(np.sum(w.rows)), w.D)
     nnz = batches[0][1].size
     ws0, need = tabs.workspace(w.B, nnz)
     wss = [ws0, torch.empty_like(ws0), torch.empty_like(ws0)]
@@ -325,9 +339,9 @@ def test_tiered_three_streams_split_prepare():
     for i in range(steps):
         offsets, ids = batches[i]
         ref, _ = o.forward(offsets, ids, w.B, False)
-        S = forward_S(offsets, ids, w.B, o.rows, lambda r: o.read_rows(r)[0], False, w.D)
-        assert_within(outs[i].cpu().numpy(), ref, S + 2 * i * w.lr, f"forward {i}")
-        o.backward_adagrad(offsets, ids, w.B, False, grads[i], w.lr, w.eps)
-    check_all_rows(tabs, o, int(np.sum(w.rows)), steps)
+        S = forward_bound(bounds, o, offsets, ids, w.B, False, w.D)
+        assert_within(outs[i].cpu().numpy(), ref, S, f"forward {i}")
+        oracle_step(bounds, o, offsets, ids, w.B, False, grads[i], w)
+    check_all_rows(tabs, o, int(np.sum(w.rows)), bounds)
     assert eb.emb_status_sync(tabs.handle) == (eb.EMB_OK, 0)
     tabs.close()

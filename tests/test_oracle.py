@@ -493,6 +493,37 @@ def test_worked_adagrad_decay():
     np.testing.assert_allclose(W, [[0.75 - 0.5 / 3 - 0.5 * 4 / 5, 1.875 - 0.5 / 3]], rtol=3e-7)  # 3 fp32 roundings
 
 
+def test_worked_adagrad_decay_fresh_rows_of_hashed_tables():
+    # A key's row starts from the initial accumulator, which its first update
+    # does not discount, whatever the period; a dense table's rows are in
+    # period 0 from the start.  rho = 1/2, accum_init = 12: G' = 12 + g^2.
+    o = orc.Oracle([2], 1, hashed=True, seed=3, accum_init=12.0)
+    one = lambda keys: o.find_or_insert(np.array([0, len(keys)], np.int64),
+                                        np.array(keys, np.uint64), 1)[0]
+    step = lambda ids, g, p: o.backward_adagrad_decay(np.array([0, 1], np.int64), ids, 1, False,
+                                                      np.array([[[g]]], np.float32), 0.5, 0.0,
+                                                      0.5, p)
+    assert o.read_periods([0, 1]).tolist() == [0xFFFFFFFF] * 2  # no key yet: fresh
+    assert one([77]).tolist() == [0]
+    assert step(np.array([0]), 2.0, 5) == 0  # inserted and first updated in period 5
+    assert o.read_rows([0])[1].tolist() == [[16.0]]  # 12 + 4, no rho^5
+    assert o.read_periods([0]).tolist() == [5]
+    assert step(np.array([0]), 2.0, 7) == 0  # two periods later: 16/4 + 4
+    assert o.read_rows([0])[1].tolist() == [[8.0]]
+    # evicted at period 9: the row is fresh again; a new key receives it
+    assert o.evict(np.array([7, 0], np.uint32), 9) == 1
+    assert o.read_periods([0]).tolist() == [0xFFFFFFFF]
+    assert one([88]).tolist() == [0]
+    assert step(np.array([0]), 2.0, 12) == 0
+    assert o.read_rows([0])[1].tolist() == [[16.0]]  # not 12 * 2^-12 + 4
+    assert o.read_periods([0]).tolist() == [12]
+    # dense tables: rows start in period 0, so a first update in period 2 discounts
+    d = orc.Oracle([1], 1, seed=0, accum_init=12.0)
+    d.backward_adagrad_decay(np.array([0, 1], np.int64), np.array([0]), 1, False,
+                             np.array([[[2.0]]], np.float32), 0.5, 0.0, 0.5, 2)
+    assert d.read_rows([0])[1].tolist() == [[7.0]]  # 12/4 + 4
+
+
 def test_adagrad_decay_rho_one_is_torch_adagrad():
     T, D, B = 2, 4, 20
     rows = np.array([9, 15])
