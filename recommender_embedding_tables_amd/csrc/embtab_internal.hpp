@@ -222,6 +222,36 @@ __device__ inline uint32_t lanes_below(uint64_t m) {
                                    __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave (every lane active).
+// Within each row of 16 lanes a Hillis-Steele scan on DPP row shifts by 1, 2,
+// 4 and 8 (a lane whose source lies before its row adds nothing); then rows 1
+// and 3 add the last lane of rows 0 and 2, and the upper half adds lane 31,
+// both through readlane.  No LDS and no ds_bpermute.
+template <int CTRL>
+__device__ inline uint32_t dpp_shifted(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+__device__ inline uint32_t wave_incl_scan(uint32_t x) {
+  const uint32_t lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  const uint32_t r = lane & 15u;
+  uint32_t t;
+  t = dpp_shifted<0x111>(x);  // row_shr:1
+  if (r >= 1u) x += t;
+  t = dpp_shifted<0x112>(x);  // row_shr:2
+  if (r >= 2u) x += t;
+  t = dpp_shifted<0x114>(x);  // row_shr:4
+  if (r >= 4u) x += t;
+  t = dpp_shifted<0x118>(x);  // row_shr:8
+  if (r >= 8u) x += t;
+  const uint32_t row0 = (uint32_t)__builtin_amdgcn_readlane((int)x, 15);
+  const uint32_t row2 = (uint32_t)__builtin_amdgcn_readlane((int)x, 47);
+  if ((lane & 48u) == 16u) x += row0;
+  if ((lane & 48u) == 48u) x += row2;
+  const uint32_t half = (uint32_t)__builtin_amdgcn_readlane((int)x, 31);
+  if (lane >= 32u) x += half;
+  return x;
+}
+
 // Block index remapped so that each of the 8 XCDs (which take hardware blocks
 // round-robin) works on one contiguous range of logical blocks, keeping the
 // cache lines a range shares inside one XCD's L2.

@@ -300,11 +300,7 @@ __global__ __launch_bounds__(1024) void k_hash_plan(uint32_t* __restrict__ bcnt,
 #pragma unroll
     for (int q = 0; q < (int)PER; ++q) sum += v[q];
     uint32_t x = sum;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const uint32_t y = (uint32_t)__shfl_up((int)x, o, 64);
-      if (lane >= (uint32_t)o) x += y;
-    }
+    x = wave_incl_scan(x);
     if (lane == 63u) wsum[w] = x;
     __syncthreads();
     uint32_t before = 0, total = 0;
@@ -617,10 +613,7 @@ __global__ __launch_bounds__(1024) void k_evict_scan(uint32_t* __restrict__ bcnt
   for (uint32_t i = lo; i < hi; ++i) sum += bcnt[i];
   uint32_t x = sum;
   const uint32_t lane = threadIdx.x & 63u, w = threadIdx.x >> 6;
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = (uint32_t)__shfl_up((int)x, o, 64);
-    if (lane >= (uint32_t)o) x += y;
-  }
+  x = wave_incl_scan(x);
   if (lane == 63u) wsum[w] = x;
   __syncthreads();
   uint32_t before = 0, total = 0;
@@ -670,10 +663,7 @@ __global__ __launch_bounds__(256) void k_evict_scatter(
   // exclusive count of the block's flags before this thread's 16 rows
   uint32_t x = c;
   const uint32_t lane = threadIdx.x & 63u, w = threadIdx.x >> 6;
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = (uint32_t)__shfl_up((int)x, o, 64);
-    if (lane >= (uint32_t)o) x += y;
-  }
+  x = wave_incl_scan(x);
   if (lane == 63u) wsum[w] = x;
   __syncthreads();
   uint32_t rank = bbase[blockIdx.x] + x - c;

@@ -57,11 +57,7 @@ uint32_t next_prepare_gen() {
 __device__ inline uint32_t block_excl_scan(uint32_t v, uint32_t* total, uint32_t* lds4) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   uint32_t x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    uint32_t y = (uint32_t)__shfl_up((int)x, o, 64);
-    if (lane >= o) x += y;
-  }
+  x = wave_incl_scan(x);
   if (lane == 63) lds4[w] = x;
   __syncthreads();
   uint32_t before = 0, all = 0;
@@ -452,11 +448,7 @@ __global__ __launch_bounds__(1024) void k_chunk_scan(uint32_t* __restrict__ hc, 
 #pragma unroll
     for (int q = 0; q < (int)PER; ++q) sum += v[q];
     uint32_t x = sum;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const uint32_t y = (uint32_t)__shfl_up((int)x, o, 64);
-      if (lane >= (uint32_t)o) x += y;
-    }
+    x = wave_incl_scan(x);
     if (lane == 63u) wsum[w] = x;
     __syncthreads();
     uint32_t before = 0, total = 0;
