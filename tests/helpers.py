@@ -29,19 +29,51 @@ class StepBounds:
 
     An input error passes into the next step with factor 1 (w' = w - ..., G' =
     G*df + g^2 with df <= 1), so the bounds add up along the oracle's own
-    trajectory, read before and after each oracle step."""
+    trajectory, read before and after each oracle step.  Only rows that carry
+    a bound are stored (sorted global rows and their [n, D] bounds)."""
 
     def __init__(self, total_rows, D):
-        self.eW = np.zeros((int(total_rows), int(D)))
-        self.eG = np.zeros((int(total_rows), int(D)))
+        self.D = int(D)
+        self.rows = np.zeros(0, np.int64)
+        self._eW = np.zeros((0, self.D))
+        self._eG = np.zeros((0, self.D))
+
+    def _positions(self, rows):
+        """Positions of `rows` in the store, adding the missing ones (bound 0)."""
+        rows = np.asarray(rows, np.int64)
+        new = np.setdiff1d(rows, self.rows)
+        if new.size:
+            allr = np.concatenate([self.rows, new])
+            order = np.argsort(allr, kind="stable")
+            self.rows = allr[order]
+            z = np.zeros((new.size, self.D))
+            self._eW = np.concatenate([self._eW, z])[order]
+            self._eG = np.concatenate([self._eG, z])[order]
+        return np.searchsorted(self.rows, rows)
+
+    def bounds_of(self, rows):
+        """(e_W, e_G) of `rows` ([n, D] each); 0 for rows that carry none."""
+        rows = np.asarray(rows, np.int64)
+        eW = np.zeros((rows.size, self.D))
+        eG = np.zeros((rows.size, self.D))
+        if self.rows.size and rows.size:
+            pos = np.minimum(np.searchsorted(self.rows, rows), self.rows.size - 1)
+            hit = self.rows[pos] == rows
+            eW[hit] = self._eW[pos[hit]]
+            eG[hit] = self._eG[pos[hit]]
+        return eW, eG
+
+    def weight_bound(self, rows):
+        return self.bounds_of(rows)[0]
 
     def assigned(self, o, rows):
         """Rows that just got a key: fresh initial values (within the rule)."""
         rows = np.asarray(rows, np.int64)
         if rows.size:
             W, _ = o.read_rows(rows)
-            self.eW[rows] = REL * np.abs(W.astype(np.float64)) + ABS
-            self.eG[rows] = 0.0
+            pos = self._positions(rows)
+            self._eW[pos] = REL * np.abs(W.astype(np.float64)) + ABS
+            self._eG[pos] = 0.0
 
     def step(self, o, rows_u, sums, lr, eps, oracle_step):
         """Runs oracle_step() (the oracle's update of rows_u) and carries the bounds."""
@@ -52,18 +84,18 @@ class StepBounds:
             W1, G1 = o.read_rows(rows_u)
             a = np.asarray(sums, np.float64)
             G1 = G1.astype(np.float64)
-            eG = self.eG[rows_u] + REL * (np.abs(G0.astype(np.float64)) + a * a) + ABS
-            eW = (self.eW[rows_u] + ABS +
+            pos = self._positions(rows_u)
+            eG = self._eG[pos] + REL * (np.abs(G0.astype(np.float64)) + a * a) + ABS
+            eW = (self._eW[pos] + ABS +
                   REL * (np.abs(W0.astype(np.float64)) + lr * a / (np.sqrt(G1) + eps)) +
                   lr * a / (2.0 * G1 ** 1.5) * eG)
-            self.eG[rows_u] = eG
-            self.eW[rows_u] = eW
+            self._eG[pos] = eG
+            self._eW[pos] = eW
         return rc
 
     def check(self, W_gpu, G_gpu, W_ref, G_ref, rows, what):
-        rows = np.asarray(rows, np.int64)
-        for name, g, r, e in (("weights", W_gpu, W_ref, self.eW[rows]),
-                              ("accumulators", G_gpu, G_ref, self.eG[rows])):
+        eW, eG = self.bounds_of(rows)
+        for name, g, r, e in (("weights", W_gpu, W_ref, eW), ("accumulators", G_gpu, G_ref, eG)):
             err = np.abs(np.asarray(g, np.float64) - np.asarray(r, np.float64))
             bad = err > e
             if bad.any():

@@ -126,7 +126,7 @@ def test_training_on_absent_ids():
             assert fl == 0
             S = (forward_S(offsets, ids, w.B, o.rows, lambda g: np.abs(o.read_rows(g)[0]), mean,
                            w.D) +
-                 forward_S(offsets, ids, w.B, o.rows, lambda g: bounds.eW[g], mean, w.D) / REL)
+                 forward_S(offsets, ids, w.B, o.rows, bounds.weight_bound, mean, w.D) / REL)
             assert_within(out.cpu().numpy(), r, S, f"forward step {step}")
         grad = synth.gen_grad(w, step)
         ws, need = tabs.workspace(w.B, ids.size)

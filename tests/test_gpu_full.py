@@ -1,11 +1,13 @@
-"""Parity at the full workload sizes, in the launch sequence bench.py times
+"""Parity at the full workload sizes, in the launch sequences bench.py times
 (emb_bag_prepare -> emb_bag_forward_prepared -> emb_bag_backward_adagrad_prepared,
-plus emb_hash_find_or_insert for the hashed workload).
+plus emb_hash_find_or_insert for the hashed workload; the default 26-table
+step also in its grouped and pipelined stream patterns).
 
 Integer outputs are compared bit for bit (sorted rows, permutation, unique,
-counts, inverse, the key -> row map); fp32 outputs within 1e-5 * S + 1e-6.
-Row checks cover every touched row and a seeded sample of untouched rows plus
-the neighbours of touched rows, which must keep their initial values exactly.
+counts, inverse, the key -> row map); fp32 outputs within 1e-5 * S + 1e-6,
+carried over the steps (tests/helpers.py StepBounds).  Row checks cover every
+touched row and a seeded sample of untouched rows plus the neighbours of
+touched rows, which must keep their initial values exactly.
 """
 import gc
 
@@ -15,7 +17,8 @@ import torch
 
 from oracle import oracle as orc
 from recommender_embedding_tables_amd import synth
-from tests.helpers import abs_grad_sums, assert_within, forward_S
+from recommender_embedding_tables_amd.hipevents import HipEvents
+from tests.helpers import REL, StepBounds, abs_grad_sums, assert_within, forward_S
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -66,26 +69,35 @@ def prepared_step(tabs, w, d_off, d_ids, nnz, grad):
     return out
 
 
-def check_forward(out, o, w, offsets, ids, exact):
+def check_forward(out, o, w, offsets, ids, exact, bounds=None):
+    """exact: one-hot sums of rows no step has updated yet (copies of one row)."""
     ref, _ = o.forward(offsets, ids, w.B, w.pool_mean)
     got = out.cpu().numpy()
     if exact:
         np.testing.assert_array_equal(got, ref)
     else:
-        S = forward_S(offsets, ids, w.B, o.rows, lambda r: o.read_rows(r)[0], w.pool_mean, w.D)
+        S = forward_S(offsets, ids, w.B, o.rows, lambda r: np.abs(o.read_rows(r)[0]),
+                      w.pool_mean, w.D)
+        if bounds is not None:  # rows updated by earlier steps carry their bounds
+            S = S + forward_S(offsets, ids, w.B, o.rows, bounds.weight_bound, w.pool_mean,
+                              w.D) / REL
         assert_within(got, ref, S, "forward")
 
 
-def check_rows_after(tabs, o, w, offsets, ids, grad, W_before_rows, seed=0):
-    """Touched rows within the bound; a sample of untouched rows bit-identical."""
+def oracle_step(o, w, offsets, ids, grad, bounds):
+    """The oracle's backward + Adagrad, with the per-step bounds carried over it."""
     uniq, gsum = abs_grad_sums(offsets, ids, w.B, o.rows, grad, w.pool_mean, w.D)
+    assert bounds.step(o, uniq, gsum, w.lr, w.eps, lambda: o.backward_adagrad(
+        offsets, ids, w.B, w.pool_mean, grad, w.lr, w.eps)) == 0
+    return uniq
+
+
+def check_rows_after(tabs, o, w, uniq, bounds, seed=0):
+    """Rows `uniq` within the carried bound; a sample of untouched rows bit-identical."""
     Wg = tabs.weights[_t(uniq)].cpu().numpy()
     Gg = tabs.accum[_t(uniq)].cpu().numpy()
     Wr, Gr = o.read_rows(uniq)
-    SG = np.abs(Gr).astype(np.float64) + gsum ** 2
-    SW = np.abs(Wr) + w.lr + w.lr * gsum / (np.sqrt(Gr.astype(np.float64)) + w.eps)
-    assert_within(Gg, Gr, SG, "accumulator")
-    assert_within(Wg, Wr, SW, "weights")
+    bounds.check(Wg, Gg, Wr, Gr, uniq, "rows")
     # untouched: neighbours of touched rows and a seeded random sample
     rng = np.random.default_rng(seed)
     cand = np.concatenate([uniq - 1, uniq + 1, rng.integers(0, w.total_rows, 200_000)])
@@ -126,16 +138,16 @@ def check_sort_unique(tabs, o, w, offsets, ids):
 def run_dense_workload(cfg, steps=1, exact_forward=False, **over):
     w = synth.workload(cfg, **over)
     tabs, o = tables_for(w)
+    bounds = StepBounds(w.total_rows, w.D)
     for step in range(steps):
         offsets, ids = synth.gen_batch(w, step)
         grad = synth.gen_grad(w, step)
         if step == 0:
             check_sort_unique(tabs, o, w, offsets, ids)
         out = prepared_step(tabs, w, _t(offsets), _t(ids), ids.size, grad)
-        if step == 0:  # later steps read rows that already carry one step's rounding
-            check_forward(out, o, w, offsets, ids, exact_forward)
-        o.backward_adagrad(offsets, ids, w.B, w.pool_mean, grad, w.lr, w.eps)
-        check_rows_after(tabs, o, w, offsets, ids, grad, None, seed=step)
+        check_forward(out, o, w, offsets, ids, exact_forward and step == 0, bounds)
+        uniq = oracle_step(o, w, offsets, ids, grad, bounds)
+        check_rows_after(tabs, o, w, uniq, bounds, seed=step)
     assert eb.emb_status_sync(tabs.handle) == (eb.EMB_OK, 0)
     tabs.close()
 
@@ -158,6 +170,7 @@ def test_full_cfg2_pipelined_schedule():
     need_bytes(44 << 30)
     w = synth.workload(2)
     tabs, o = tables_for(w)
+    bounds = StepBounds(w.total_rows, w.D)
     steps = 3
     batches = [synth.gen_batch(w, b) for b in range(steps)]
     d_batches = [(_t(off), _t(ids)) for off, ids in batches]
@@ -193,10 +206,78 @@ def test_full_cfg2_pipelined_schedule():
         done[i % 2].record(main)
         torch.cuda.synchronize()
         offsets, ids = batches[i]
-        check_forward(out, o, w, offsets, ids, exact=(i == 0))
-        o.backward_adagrad(offsets, ids, w.B, False, grads[i], w.lr, w.eps)
-        check_rows_after(tabs, o, w, offsets, ids, grads[i], None, seed=i)
+        check_forward(out, o, w, offsets, ids, i == 0, bounds)
+        uniq = oracle_step(o, w, offsets, ids, grads[i], bounds)
+        check_rows_after(tabs, o, w, uniq, bounds, seed=i)
     assert eb.emb_status_sync(tabs.handle) == (eb.EMB_OK, 0)
+    tabs.close()
+
+
+def test_full_cfg2_grouped_schedule():
+    # The launch pattern bench.py times by default (grouped; here groups of two
+    # batches): the prepares of the next group's batches go to a second stream,
+    # into the other half of 2 * KG workspaces, right after the first training
+    # step of the current group; fence-less device-scope events order the two
+    # streams once per group.  Every step's output is kept and checked against
+    # the oracle afterwards, then every row any step touched.
+    need_bytes(52 << 30)
+    w = synth.workload(2)
+    tabs, o = tables_for(w)
+    bounds = StepBounds(w.total_rows, w.D)
+    KG, groups = 2, 2
+    steps = KG * groups
+    batches = [synth.gen_batch(w, b) for b in range(steps)]
+    d_batches = [(_t(off), _t(ids)) for off, ids in batches]
+    grads = [synth.gen_grad(w, b) for b in range(steps)]
+    d_grads = [_t(g) for g in grads]
+    pool = eb.EMB_POOL_SUM
+    nnz = batches[0][1].size
+    ws0, need = tabs.workspace(w.B, nnz)
+    wsg = [ws0] + [torch.empty_like(ws0) for _ in range(2 * KG - 1)]
+    outs = [torch.empty((w.B, w.T, w.D), dtype=torch.float32, device=DEV) for _ in range(steps)]
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()  # default priority
+    hev = HipEvents()
+    prep_ev = [hev.create(timing=False) for _ in range(2)]
+    step_ev = [hev.create(timing=False) for _ in range(2)]
+
+    def prep(j, slot):
+        d_off, d_ids = d_batches[j]
+        eb.check(eb.emb_bag_prepare(tabs.handle, d_off, d_ids, w.B, nnz, pool, wsg[slot], need,
+                                    side), "prepare")
+
+    for i in range(steps):
+        g, r = divmod(i, KG)
+        if i == 0:
+            for q in range(KG):
+                prep(q, q)
+            hev.record(prep_ev[0], side)
+        if r == 0:
+            hev.wait(main, prep_ev[g % 2])
+        cur = wsg[(g % 2) * KG + r]
+        d_off, d_ids = d_batches[i]
+        eb.check(eb.emb_bag_forward_prepared(tabs.handle, d_off, d_ids, w.B, nnz, pool, outs[i],
+                                             cur, need, main), "forward")
+        eb.check(eb.emb_bag_backward_adagrad_prepared(tabs.handle, w.B, nnz, pool, d_grads[i],
+                                                      w.lr, w.eps, cur, need, main), "backward")
+        if r == KG - 1:
+            hev.record(step_ev[g % 2], main)
+        if r == 0 and g + 1 < groups:
+            if g > 0:
+                hev.wait(side, step_ev[(g + 1) % 2])  # group g - 1 left these workspaces
+            for q in range(KG):
+                prep(KG * (g + 1) + q, ((g + 1) % 2) * KG + q)
+            hev.record(prep_ev[(g + 1) % 2], side)
+    torch.cuda.synchronize()
+    hev.close()
+    assert eb.emb_status_sync(tabs.handle) == (eb.EMB_OK, 0)
+    touched = []
+    for i in range(steps):
+        offsets, ids = batches[i]
+        check_forward(outs[i], o, w, offsets, ids, i == 0, bounds)
+        outs[i] = None
+        touched.append(oracle_step(o, w, offsets, ids, grads[i], bounds))
+    check_rows_after(tabs, o, w, np.unique(np.concatenate(touched)), bounds, seed=7)
     tabs.close()
 
 
@@ -223,6 +304,7 @@ def test_full_cfg5_hashed_dynamic_keys():
     need_bytes(60 << 30)
     w = synth.workload(5)
     tabs, o = tables_for(w)
+    bounds = StepBounds(w.total_rows, w.D)
     # warm part of each table with a seeded prefill of 2M distinct keys per table
     rng = np.random.default_rng(77)
     pre_off = np.arange(0, w.T * 500_000 + 1, dtype=np.int64) * 4  # B = 500000 bags of 4 keys
@@ -233,6 +315,11 @@ def test_full_cfg5_hashed_dynamic_keys():
     ref, fl = o.find_or_insert(pre_off, pre_keys, pw.B)
     assert fl == 0
     np.testing.assert_array_equal(ids.cpu().numpy(), ref)
+    row_off = np.concatenate([[0], np.cumsum(w.rows)])
+    assigned = lambda: np.concatenate([np.arange(o.n_live(t)) + row_off[t]  # noqa: E731
+                                       for t in range(w.T)])
+    live_before = assigned()
+    bounds.assigned(o, live_before)
     for step in range(2):
         offsets, ranks = synth.gen_batch(w, step)
         keys = synth.gen_keys(w, offsets, ranks)
@@ -240,18 +327,16 @@ def test_full_cfg5_hashed_dynamic_keys():
         ref_ids, fl = o.find_or_insert(offsets, keys, w.B)
         assert fl == 0
         np.testing.assert_array_equal(d_ids.cpu().numpy(), ref_ids)
+        live_now = assigned()  # new keys got fresh rows (no eviction here)
+        bounds.assigned(o, np.setdiff1d(live_now, live_before))
+        live_before = live_now
         grad = synth.gen_grad(w, step)
         out = prepared_step(tabs, w, _t(offsets), d_ids, keys.size, grad)
-        if step == 0:
-            check_forward(out, o, w, offsets, ref_ids, exact=False)
-        o.backward_adagrad(offsets, ref_ids, w.B, False, grad, w.lr, w.eps)
-        uniq, gsum = abs_grad_sums(offsets, ref_ids, w.B, o.rows, grad, False, w.D)
-        Wg = tabs.weights[_t(uniq)].cpu().numpy()
-        Gg = tabs.accum[_t(uniq)].cpu().numpy()
+        check_forward(out, o, w, offsets, ref_ids, False, bounds)
+        uniq = oracle_step(o, w, offsets, ref_ids, grad, bounds)
         Wr, Gr = o.read_rows(uniq)
-        assert_within(Gg, Gr, np.abs(Gr).astype(np.float64) + gsum ** 2, "accumulator")
-        assert_within(Wg, Wr, np.abs(Wr) + w.lr + w.lr * gsum / np.sqrt(Gr.astype(np.float64)),
-                      "weights")
+        bounds.check(tabs.weights[_t(uniq)].cpu().numpy(), tabs.accum[_t(uniq)].cpu().numpy(),
+                     Wr, Gr, uniq, f"hashed step {step}")
     # the key -> row map is the oracle's, bit for bit
     st, n_live = eb.emb_hash_n_live(tabs.handle, w.T)
     assert st == eb.EMB_OK

@@ -88,7 +88,7 @@ def oracle_step(bounds, o, offsets, ids, B, mean, grad, w):
 def forward_bound(bounds, o, offsets, ids, B, mean, D):
     """S of the pooled outputs, plus the carried weight bounds of the rows they read."""
     return (forward_S(offsets, ids, B, o.rows, lambda r: np.abs(o.read_rows(r)[0]), mean, D) +
-            forward_S(offsets, ids, B, o.rows, lambda r: bounds.eW[r], mean, D) / REL)
+            forward_S(offsets, ids, B, o.rows, bounds.weight_bound, mean, D) / REL)
 
 
 def prepared_step(tabs, w, offsets, ids, grad, pool, ws, need, stream=None):
