@@ -85,3 +85,30 @@ def test_hashed_step_counts_the_key_and_slot_traffic():
     # offsets in, u64 keys in, one 16-byte slot per distinct key, int64 ids out
     assert b["hash"] == (w.T * w.B + 1) * 8 + ids.size * 8 + U * 16 + ids.size * 8
     assert np.isclose(b["step"], sum(v for k, v in b.items() if k != "step"))
+
+
+def test_table_wise_shards_cover_every_table_once_and_balance_lookups():
+    bench = _bench_module()
+    w = synth.workload(2)
+    for P in (2, 4, 8, 26):
+        sh = bench.shard_tables(w.rows, P)
+        assert len(sh) == P
+        assert sorted(np.concatenate(sh).tolist()) == list(range(w.T))
+        sizes = [len(s) for s in sh]
+        assert max(sizes) - min(sizes) <= 1  # one-hot lookups per GPU differ by one table
+        assert all(np.all(np.diff(s) > 0) for s in sh)
+    # the snake order gives the largest table's owner none of the next P - 1 largest
+    sh = bench.shard_tables(w.rows, 8)
+    order = np.argsort(-w.rows, kind="stable")
+    owner = {int(t): r for r, s in enumerate(sh) for t in s}
+    assert len({owner[int(t)] for t in order[:8]}) == 8
+
+
+@pytest.mark.skipif(not os.path.exists(os.path.join(ROOT, "recommender_embedding_tables_amd",
+                                                    "libembtab.so")),
+                    reason="the HIP library is not built")
+def test_shard_option_is_refused_where_it_does_not_apply():
+    r = _run("--workload", "5", "--shard", "0/4")
+    assert r.returncode == 2 and "--shard" in r.stderr
+    r = _run("--shard", "8/8")
+    assert r.returncode == 2 and "--shard" in r.stderr
