@@ -16,9 +16,10 @@
 // v_mfma_f32_16x16x4_f32, lane l supplying A[l % 16][l / 16] and
 // B[l / 16][l % 16] and holding D[4 (l / 16) + r][l % 16] in register r.
 // Only the lower 16 x 16 blocks (0,0), (1,0), (1,1) are formed; both
-// operands of a block are rows of Z, so each K-step loads two values per
-// lane for three products.  Pairs are staged in LDS and written as one
-// contiguous row per sample.
+// operands of a block are rows of Z, so the K-steps may take the columns in
+// any order common to A and B: each 16-column step reads one float4 of each
+// row block per lane and feeds four K-steps (twelve products).  Pairs are
+// staged in LDS and written as one contiguous row per sample.
 //
 // The backward gathers Z again and forms dZ = G Z with G the symmetric
 // matrix of the pair gradients (zero diagonal): M-blocks of 16 rows, N-blocks
@@ -38,16 +39,17 @@ constexpr int kZRows = 32;  // T + 1 <= 32
 
 // LDS of one wave: Z [T + 1][D + 4] (the row stride D + 4 spreads the 16 rows
 // of a K-step over the banks; rows T+1..31 are zeros supplied in registers),
-// the symmetric pair matrix [32][33] (backward), pair staging (forward) and
-// the row of every table's current occurrence.
+// the symmetric pair matrix [32][kGStride] (backward; 16-byte rows),
+// pair staging (forward) and the row of every table's current occurrence.
+constexpr int kGStride = 36;
 __host__ __device__ inline int z_stride(int D) { return D + 4; }
 __host__ __device__ inline size_t wave_lds_floats(int T, int D, bool bwd) {
-  return (size_t)(T + 1) * z_stride(D) + (bwd ? 32 * 33 : 512) + 32;
+  return (size_t)(T + 1) * z_stride(D) + (bwd ? 32 * kGStride : 512) + 32;
 }
 
 struct WaveLds {
   float* z;       // [T + 1][D + 4]
-  float* g;       // [32][33]  (backward)
+  float* g;       // [32][kGStride]  (backward)
   float* pairs;   // [<= 496]  (forward)
   uint32_t* row;  // [32]
 };
@@ -58,7 +60,7 @@ __device__ inline WaveLds wave_lds(float* base, int T, int D, bool bwd, int w) {
   l.z = p;
   l.g = p + (size_t)(T + 1) * z_stride(D);
   l.pairs = l.g;
-  l.row = reinterpret_cast<uint32_t*>(l.g + (bwd ? 32 * 33 : 512));
+  l.row = reinterpret_cast<uint32_t*>(l.g + (bwd ? 32 * kGStride : 512));
   return l;
 }
 
@@ -71,7 +73,9 @@ __device__ inline void wave_sync() {
 // The samples of one wave, software-pipelined so that no global load latency
 // is exposed once per sample: while sample s's rows are in flight, the
 // previous sample's Z (still in LDS) is consumed (matrix-core products and
-// outputs), and the next sample's bag bounds and first ids are fetched.
+// outputs), the first id of each bag of the next sample is fetched (its bag
+// bounds were fetched one sample earlier) and so are the bag bounds of the
+// sample after it.
 //   Lane t < T owns bag (t, s): its bounds, and the row of its occurrence at
 //   the current position, which it publishes in LDS; every lane then loads
 //   its NQ items (table, float4 column) of that row.  Position 0 of the next
@@ -80,7 +84,7 @@ __device__ inline void wave_sync() {
 //   count as empty and flag.  consume(sp) reads Z rows 0..T of sample sp;
 //   issue(s) may start the consumer's own loads for sample s (it is consumed
 //   one iteration later), and rotate() moves them to the consumer's side.
-template <bool MEAN, int NQ, class Issue, class Consume, class Rotate>
+template <bool MEAN, int NQ, bool HOLD_ITEMS, class Issue, class Consume, class Rotate>
 __device__ void pipelined_samples(const WaveLds& l, int64_t first, int64_t stride,
                                   const float* __restrict__ dense,
                                   const int64_t* __restrict__ offsets,
@@ -93,18 +97,48 @@ __device__ void pipelined_samples(const WaveLds& l, int64_t first, int64_t strid
   const int lane = threadIdx.x & 63;
   const int D4 = D >> 2;
   const int zs = z_stride(D);
-  const int64_t nrows = lane < T ? rows[lane] : 0, roff = lane < T ? row_off[lane] : 0;
-  // item q of this lane: table (tc >> 8) and float4 column (tc & 255); -1: none
-  int tc[NQ];
+  // rows, global row offsets and valid offsets all fit 32 bits (the calls
+  // reject nnz >= 2^32 - 16; global rows are 32-bit)
+  const uint32_t nrows = lane < T ? (uint32_t)rows[lane] : 0u;
+  const uint32_t roff = lane < T ? (uint32_t)row_off[lane] : 0u;
+  // Item q of this lane is the flat (table, float4 column) index 64 q + lane:
+  // table = index / D4, column = the rest.  HOLD_ITEMS keeps them packed in
+  // NQ registers (table << 8 | column, -1 past the last item); otherwise they
+  // are recomputed at each use from an opaque copy of the lane id (so that
+  // the compiler does not hold them across the sample loop either), with the
+  // quotient in fp32: for index < 2048 and D4 <= 64, (index + 1/2) / D4 lies
+  // at least 1/128 from an integer, far beyond the rounding error.
+  const int nitems = T * D4;
+  const float rd4 = 1.0f / (float)D4;
+  int tc[HOLD_ITEMS ? NQ : 1];
+  if constexpr (HOLD_ITEMS) {
 #pragma unroll
-  for (int q = 0; q < NQ; ++q) {
-    const int it = q * 64 + lane;
-    const int t = it / D4;
-    tc[q] = it < T * D4 ? (t << 8) | (it - t * D4) : -1;
+    for (int q = 0; q < NQ; ++q) {
+      const int it = q * 64 + lane;
+      const int t = it / D4;
+      tc[q] = it < nitems ? (t << 8) | (it - t * D4) : -1;
+    }
   }
-  auto bag_of = [&](int64_t s, int64_t& o0, int64_t& len) {
-    o0 = 0;
-    len = 0;
+  auto opaque_lane = [&]() {
+    int v = lane;
+    if constexpr (!HOLD_ITEMS) asm volatile("" : "+v"(v));
+    return v;
+  };
+  auto item_of = [&](int ln, int q, int& t, int& c) -> bool {
+    if constexpr (HOLD_ITEMS) {
+      t = tc[q] >> 8;
+      c = tc[q] & 255;
+      return tc[q] >= 0;
+    } else {
+      const int it = q * 64 + ln;
+      t = (int)(((float)it + 0.5f) * rd4);
+      c = it - t * D4;
+      return it < nitems;
+    }
+  };
+  auto bag_of = [&](int64_t s, uint32_t& o0, uint32_t& len) {
+    o0 = 0u;
+    len = 0u;
     if (lane < T && s < B) {
       const int64_t b = (int64_t)lane * B + s;
       int64_t a = offsets[b], e = offsets[b + 1];
@@ -112,45 +146,56 @@ __device__ void pipelined_samples(const WaveLds& l, int64_t first, int64_t strid
         bad |= EMB_FLAG_BAD_OFFSETS;
         a = e = 0;
       }
-      o0 = a;
-      len = e - a;
+      o0 = (uint32_t)a;
+      len = (uint32_t)(e - a);
     }
   };
-  auto resolve = [&](int64_t o0, int64_t len, int64_t j) -> uint32_t {
+  // the row of id `id` at position j of a bag of `len` ids (lanes < T)
+  auto row_of = [&](int64_t id, uint32_t len, uint32_t j) -> uint32_t {
     uint32_t r = kNoRow;
     if (lane < T && j < len) {
-      const int64_t id = ids[o0 + j];
-      if (id >= 0 && id < nrows) r = (uint32_t)(roff + id);
+      if (id >= 0 && id < (int64_t)nrows) r = roff + (uint32_t)id;
       else if (id != kAbsentId) bad |= EMB_FLAG_OUT_OF_RANGE;
     }
     return r;
   };
-  auto wave_max = [](int64_t v) {
+  auto id_at = [&](uint32_t o0, uint32_t len, uint32_t j) -> int64_t {
+    return (lane < T && j < len) ? ids[(size_t)o0 + j] : kAbsentId;
+  };
+  auto resolve = [&](uint32_t o0, uint32_t len, uint32_t j) -> uint32_t {
+    return row_of(id_at(o0, len, j), len, j);
+  };
+  auto wave_max = [](uint32_t v) {
     for (int o = 32; o > 0; o >>= 1) {
-      const int64_t y = __shfl_xor(v, o, 64);
+      const uint32_t y = (uint32_t)__shfl_xor((int)v, o, 64);
       v = y > v ? y : v;
     }
-    return v;
+    return (uint32_t)__builtin_amdgcn_readfirstlane(v);
   };
-  auto load_item = [&](int q) -> f4v {
-    const uint32_t r = tc[q] >= 0 ? l.row[tc[q] >> 8] : kNoRow;
+  auto load_item = [&](int ln, int q) -> f4v {
+    int t, c;
+    const bool in = item_of(ln, q, t, c);
+    const uint32_t r = in ? l.row[t] : kNoRow;
     const bool ok = r != kNoRow;
-    const f4v v =
-        *reinterpret_cast<const f4v*>(W + (ok ? (size_t)r * D + 4 * (tc[q] & 255) : 0));
+    const f4v v = *reinterpret_cast<const f4v*>(W + (ok ? (size_t)r * D + 4 * c : 0));
     return ok ? v : f4v{0.f, 0.f, 0.f, 0.f};
   };
 
   int64_t s = first;
-  int64_t o0, len;
+  uint32_t o0, len, o0n, lenn;
   bag_of(s, o0, len);
-  int64_t maxlen = wave_max(len);
+  bag_of(s + stride, o0n, lenn);
+  uint32_t maxlen = wave_max(len);
   if (lane < T) l.row[lane] = resolve(o0, len, 0);
   wave_sync();
   int64_t sp = -1;
   while (s < B) {
     const int64_t sn = s + stride;
-    int64_t o0n, lenn;
-    bag_of(sn, o0n, lenn);  // in flight during this sample
+    // in flight during this sample: the bag bounds of the sample after the
+    // next one, and the first id of every bag of the next one
+    uint32_t o0nn, lennn;
+    bag_of(sn + stride, o0nn, lennn);
+    const int64_t idn = id_at(o0n, lenn, 0);
     f4v dv[(256 / 4 + 63) / 64];
 #pragma unroll
     for (int q = 0; q < (256 / 4 + 63) / 64; ++q) {
@@ -159,19 +204,23 @@ __device__ void pipelined_samples(const WaveLds& l, int64_t first, int64_t strid
                      : f4v{0.f, 0.f, 0.f, 0.f};
     }
     f4v acc[NQ];
+    {
+      const int ln = opaque_lane();
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) acc[q] = load_item(q);  // position 0 of sample s
+      for (int q = 0; q < NQ; ++q) acc[q] = load_item(ln, q);  // position 0 of sample s
+    }
     issue(s);
     if (sp >= 0) consume(sp);  // the previous sample, from LDS
     wave_sync();
-    for (int64_t j = 1; j < maxlen; ++j) {  // later positions of multi-hot bags
+    for (uint32_t j = 1; j < maxlen; ++j) {  // later positions of multi-hot bags
       if (lane < T) l.row[lane] = resolve(o0, len, j);
       wave_sync();
+      const int ln = opaque_lane();
 #pragma unroll
       for (int q0 = 0; q0 < NQ; q0 += 4) {  // four loads in flight: few registers
         f4v x[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) x[q] = load_item(q0 + q);
+        for (int q = 0; q < 4; ++q) x[q] = load_item(ln, q0 + q);
 #pragma unroll
         for (int q = 0; q < 4; ++q) acc[q0 + q] += x[q];
       }
@@ -183,20 +232,26 @@ __device__ void pipelined_samples(const WaveLds& l, int64_t first, int64_t strid
       const int c = lane + 64 * q;
       if (c < D4) *reinterpret_cast<f4v*>(l.z + 4 * c) = dv[q];
     }
+    {
+      const int ln = opaque_lane();
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-      const int t = tc[q] >= 0 ? tc[q] >> 8 : 0;
-      const int64_t lq = __shfl(len, t, 64);
-      if (tc[q] < 0) continue;
-      f4v v = acc[q];
-      if (MEAN && lq > 0) v *= 1.0f / (float)lq;
-      *reinterpret_cast<f4v*>(l.z + (size_t)(t + 1) * zs + 4 * (tc[q] & 255)) = v;
+      for (int q = 0; q < NQ; ++q) {
+        int t, c;
+        const bool in = item_of(ln, q, t, c);
+        const uint32_t lq = (uint32_t)__shfl((int)len, in ? t : 0, 64);
+        if (!in) continue;
+        f4v v = acc[q];
+        if (MEAN && lq > 0) v *= 1.0f / (float)lq;
+        *reinterpret_cast<f4v*>(l.z + (size_t)(t + 1) * zs + 4 * c) = v;
+      }
     }
     // position 0 of the next sample
-    if (lane < T) l.row[lane] = resolve(o0n, lenn, 0);
+    if (lane < T) l.row[lane] = row_of(idn, lenn, 0);
     maxlen = wave_max(lenn);
     o0 = o0n;
     len = lenn;
+    o0n = o0nn;
+    lenn = lennn;
     wave_sync();
     rotate();
     sp = s;
@@ -224,17 +279,38 @@ __global__ __launch_bounds__(256, 2) void k_interact_fwd(
   auto consume = [&](int64_t s) {
     // the copied dense slot (rows of D + P floats: not 16-byte aligned)
     for (int d = lane; d < D; d += 64) out[s * ostride + d] = l.z[d];
-    // Gram blocks (0,0), (1,0), (1,1) of Z Z^T; rows past T are zero
+    // Gram blocks (0,0), (1,0), (1,1) of Z Z^T; rows past T are zero.  Both
+    // operands are rows of Z, so the sum over k may visit the columns in any
+    // order shared by A and B: in each 16-column step lane (ri, kq) supplies
+    // the four adjacent columns 4 kq .. 4 kq + 3 (one 16-byte LDS read per
+    // row) to four consecutive K-steps.  Rows past T read row T (in bounds)
+    // and are replaced by zeros.
     f4v a00 = {0.f, 0.f, 0.f, 0.f}, a10 = a00, a11 = a00;
     const bool two = T + 1 > 16;
     const bool has0 = ri <= T, has1 = 16 + ri <= T;
-    for (int k0 = 0; k0 < D; k0 += 4) {
-      const float z0 = has0 ? l.z[(size_t)ri * zs + k0 + kq] : 0.0f;
-      a00 = __builtin_amdgcn_mfma_f32_16x16x4f32(z0, z0, a00, 0, 0, 0);
-      if (two) {
-        const float z1 = has1 ? l.z[(size_t)(16 + ri) * zs + k0 + kq] : 0.0f;
-        a10 = __builtin_amdgcn_mfma_f32_16x16x4f32(z1, z0, a10, 0, 0, 0);
-        a11 = __builtin_amdgcn_mfma_f32_16x16x4f32(z1, z1, a11, 0, 0, 0);
+    const f4v zero = {0.f, 0.f, 0.f, 0.f};
+    const float* z0p = l.z + (size_t)(has0 ? ri : T) * zs + 4 * kq;
+    const float* z1p = l.z + (size_t)(has1 ? 16 + ri : T) * zs + 4 * kq;
+    if (two) {
+      for (int k0 = 0; k0 < D; k0 += 16) {
+        f4v x0 = *reinterpret_cast<const f4v*>(z0p + k0);
+        f4v x1 = *reinterpret_cast<const f4v*>(z1p + k0);
+        x0 = has0 ? x0 : zero;
+        x1 = has1 ? x1 : zero;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          a00 = __builtin_amdgcn_mfma_f32_16x16x4f32(x0[m], x0[m], a00, 0, 0, 0);
+          a10 = __builtin_amdgcn_mfma_f32_16x16x4f32(x1[m], x0[m], a10, 0, 0, 0);
+          a11 = __builtin_amdgcn_mfma_f32_16x16x4f32(x1[m], x1[m], a11, 0, 0, 0);
+        }
+      }
+    } else {
+      for (int k0 = 0; k0 < D; k0 += 16) {
+        f4v x0 = *reinterpret_cast<const f4v*>(z0p + k0);
+        x0 = has0 ? x0 : zero;
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+          a00 = __builtin_amdgcn_mfma_f32_16x16x4f32(x0[m], x0[m], a00, 0, 0, 0);
       }
     }
     // lane holds block[4 (l / 16) + r][l % 16]; pairs i > j go to staging
@@ -254,9 +330,10 @@ __global__ __launch_bounds__(256, 2) void k_interact_fwd(
     wave_sync();
     for (int p = lane; p < P; p += 64) out[s * ostride + D + p] = l.pairs[p];
   };
-  pipelined_samples<MEAN, NQ>(l, (int64_t)blockIdx.x * wpb + w, (int64_t)gridDim.x * wpb, dense,
-                              offsets, ids, row_off, rows, W, B, T, D, nnz, bad,
-                              [](int64_t) {}, consume, []() {});
+  // up to 16 items per lane stay in registers; more would spill
+  pipelined_samples<MEAN, NQ, (NQ <= 16)>(l, (int64_t)blockIdx.x * wpb + w,
+                                    (int64_t)gridDim.x * wpb, dense, offsets, ids, row_off, rows,
+                                    W, B, T, D, nnz, bad, [](int64_t) {}, consume, []() {});
   const uint32_t any = (uint32_t)(__ballot(bad != 0) != 0);
   if (any) {
     uint32_t all = bad;
@@ -281,49 +358,109 @@ __global__ __launch_bounds__(256, 2) void k_interact_bwd(
   const int64_t gstride = (int64_t)D + P;
   uint32_t bad = 0;
   const int ri = lane & 15, kq = lane >> 4;
-  auto consume = [&](int64_t s) {
-    // symmetric pair-gradient matrix, zero diagonal and padding
-    const float* go = grad_out + s * gstride;
-    for (int e = lane; e < 32 * 32; e += 64) {
-      const int i = e >> 5, j = e & 31;
-      float v = 0.0f;
-      if (i != j && i <= T && j <= T) {
-        const int hi = i > j ? i : j, lo = i > j ? j : i;
-        v = go[D + hi * (hi - 1) / 2 + lo];
+  // The symmetric pair-gradient matrix G: its diagonal and the entries past
+  // row or column T stay zero for every sample; each sample rewrites the
+  // pair entries only.
+  for (int e = lane; e < 32 * kGStride; e += 64) l.g[e] = 0.0f;
+  // The pair gradients of the sample being gathered are loaded with its rows
+  // (issue) and written to G after the previous sample has been consumed
+  // (rotate): pair p = (i, j), i > j, at p = i (i - 1) / 2 + j of the pair
+  // row, goes to G[i][j] and G[j][i].
+  constexpr int kPairIt = (kZRows * (kZRows - 1) / 2 + 63) / 64;
+  float pr[kPairIt];
+  auto issue = [&](int64_t s) {
+    const float* gp = grad_out + s * gstride + D;
+#pragma unroll
+    for (int it = 0; it < kPairIt; ++it) {
+      const int p = lane + 64 * it;
+      pr[it] = p < P ? gp[p] : 0.0f;
+    }
+  };
+  auto rotate = [&]() {
+#pragma unroll
+    for (int it = 0; it < kPairIt; ++it) {
+      const int p = lane + 64 * it;
+      if (p < P) {
+        int i = (int)((1.0f + __builtin_sqrtf((float)(8 * p + 1))) * 0.5f);
+        if (i * (i - 1) / 2 > p) --i;
+        else if ((i + 1) * i / 2 <= p) ++i;
+        const int j = p - i * (i - 1) / 2;
+        l.g[i * kGStride + j] = pr[it];
+        l.g[j * kGStride + i] = pr[it];
       }
-      l.g[i * 33 + j] = v;
     }
     wave_sync();
+  };
+  auto consume = [&](int64_t s) {
+    // the dense slot's upstream gradient, added to dz_0 once the products are
+    // done (loaded now, used last)
+    const float* go = grad_out + s * gstride;
+    float gdn[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int d = lane + 64 * q;
+      gdn[q] = d < D ? go[d] : 0.0f;
+    }
     const bool two = T + 1 > 16;
+    // K runs over the rows of Z in the order k = 8 kq + m (m = 0..7) for both
+    // operands: lane (ri, kq) takes G[ri][8 kq .. 8 kq + 7] as two float4 and
+    // Z[8 kq + m][n0 + ri] (zero past row T; rows past T read row T).
+    const float* ga = l.g + ri * kGStride + 8 * kq;
+    const float* gb = l.g + (16 + ri) * kGStride + 8 * kq;
     for (int n0 = 0; n0 < D; n0 += 16) {
       // both 16-row blocks of dZ for these 16 columns, side by side:
-      // A[i][k] = G[16 mb + i][k], B[k][n] = Z[k][n0 + n] (zero past row T)
+      // A[i][k] = G[16 mb + i][k], B[k][n] = Z[k][n0 + n].  G is read again
+      // for every column block rather than held in registers.
       f4v acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
 #pragma unroll
-      for (int k0 = 0; k0 < 32; k0 += 4) {
-        const int k = k0 + kq;
-        const float b = k <= T ? l.z[(size_t)k * zs + n0 + ri] : 0.0f;
-        acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(l.g[ri * 33 + k], b, acc0, 0, 0, 0);
-        if (two)
-          acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(l.g[(16 + ri) * 33 + k], b, acc1, 0, 0, 0);
+      for (int h = 0; h < 2; ++h) {  // K-steps 4 h .. 4 h + 3: fewer registers live
+        asm volatile("" ::: "memory");
+        float bz[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const int k = 8 * kq + 4 * h + m;
+          const float v = l.z[(size_t)(k <= T ? k : T) * zs + n0 + ri];
+          bz[m] = k <= T ? v : 0.0f;
+        }
+        const f4v g0 = *reinterpret_cast<const f4v*>(ga + 4 * h);
+        if (two) {
+          const f4v g1 = *reinterpret_cast<const f4v*>(gb + 4 * h);
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(g0[m], bz[m], acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(g1[m], bz[m], acc1, 0, 0, 0);
+          }
+        } else {
+#pragma unroll
+          for (int m = 0; m < 4; ++m)
+            acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(g0[m], bz[m], acc0, 0, 0, 0);
+        }
       }
-      // lane holds dZ[16 mb + 4 (l / 16) + r][n0 + l % 16]
+      // lane holds dZ[16 mb + 4 (l / 16) + r][n0 + l % 16].  dz_0 goes to
+      // Z's row 0, whose columns n0 .. n0 + 15 no later block reads.
       const int col = n0 + (lane & 15);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = 4 * (lane >> 4) + r;
         if (row == 0)
-          grad_dense[s * D + col] = go[col] + acc0[r];
+          l.z[col] = acc0[r];
         else if (row <= T)
           grad_pooled[((size_t)s * T + (row - 1)) * D + col] = acc0[r];
         if (two && 16 + row <= T)
           grad_pooled[((size_t)s * T + (15 + row)) * D + col] = acc1[r];
       }
     }
+    wave_sync();
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int d = lane + 64 * q;
+      if (d < D) grad_dense[s * D + d] = gdn[q] + l.z[d];
+    }
   };
-  pipelined_samples<MEAN, NQ>(l, (int64_t)blockIdx.x * wpb + w, (int64_t)gridDim.x * wpb, dense,
-                              offsets, ids, row_off, rows, W, B, T, D, nnz, bad,
-                              [](int64_t) {}, consume, []() {});
+  // the backward's products need the registers: its items are recomputed
+  pipelined_samples<MEAN, NQ, false>(l, (int64_t)blockIdx.x * wpb + w,
+                                     (int64_t)gridDim.x * wpb, dense, offsets, ids, row_off,
+                                     rows, W, B, T, D, nnz, bad, issue, consume, rotate);
   const uint32_t any = (uint32_t)(__ballot(bad != 0) != 0);
   if (any) {
     uint32_t all = bad;
