@@ -123,7 +123,7 @@ struct BlockRun {
 // Walks chunk c (one sub-group).  key_bb / key_ba: the keys just before and
 // just after the block.  A run continuing past the chunk and lying wholly in
 // the block leaves its part in part_lds and its row in *slot_key.
-template <int SG, int VEC, bool MEAN, int MPL, int UF, bool DECAY>
+template <int SG, int VEC, bool MEAN, int MPL, int UF, bool DECAY, bool REUSE>
 __device__ __forceinline__ void seg_chunk(
     const uint32_t* __restrict__ keys, const uint32_t* __restrict__ sgr,
     const float* __restrict__ sscale, const float* __restrict__ grad, float* __restrict__ W,
@@ -229,7 +229,11 @@ __device__ __forceinline__ void seg_chunk(
         for (int v = 0; v < VEC; ++v) {
           const uint32_t d4 = (uint32_t)(lane + v * SG);
           const bool own = mine && d4 < (uint32_t)D4;
-          g[u][v] = load4_nt_or_zero(grad, gg[u], (uint32_t)D, d4, vld[u] && d4 < (uint32_t)D4);
+          // a gradient row read by one occurrence only is not kept in the
+          // caches; rows read once per occurrence of their bag (REUSE) are
+          g[u][v] = REUSE ? load4_or_zero(grad, gg[u], (uint32_t)D, d4, vld[u] && d4 < (uint32_t)D4)
+                          : load4_nt_or_zero(grad, gg[u], (uint32_t)D, d4,
+                                             vld[u] && d4 < (uint32_t)D4);
           wv[u][v] = load4_or_zero(W, kk[u], (uint32_t)D, d4, own);
           gv[u][v] = load4_nt_or_zero(G, kk[u], (uint32_t)D, d4, own);
         }
@@ -355,7 +359,7 @@ __device__ __forceinline__ void span_arrive(
   }
 }
 
-template <int SG, int VEC, bool MEAN, int MPL, int UF, bool DECAY>
+template <int SG, int VEC, bool MEAN, int MPL, int UF, bool DECAY, bool REUSE>
 __global__ __launch_bounds__(256) void k_seg_adagrad(
     const uint32_t* __restrict__ keys, const uint32_t* __restrict__ sgr,
     const float* __restrict__ sscale, const float* __restrict__ grad, float* __restrict__ W,
@@ -385,7 +389,7 @@ __global__ __launch_bounds__(256) void k_seg_adagrad(
   const uint32_t sp_out = b1 < n ? span_u[blk + 1] : kNoRow;
   BlockRun<VEC> fin;
   uint32_t slot_key = kNoRow, in_key = kNoRow, out_key = kNoRow;
-  seg_chunk<SG, VEC, MEAN, MPL, UF, DECAY>(keys, sgr, sscale, grad, W, G, n, sentinel, D, lr, eps,
+  seg_chunk<SG, VEC, MEAN, MPL, UF, DECAY, REUSE>(keys, sgr, sscale, grad, W, G, n, sentinel, D, lr, eps,
                                            nbags, stamps, log2_rho, period, c, key_bb, key_ba,
                                            s_part[sgb], &slot_key, s_in[sgb], &in_key,
                                            s_out[sgb], &out_key, fin, perm,
@@ -453,7 +457,7 @@ __global__ __launch_bounds__(256) void k_seg_adagrad(
   }
 }
 
-template <int SG, int VEC, bool MEAN, bool DECAY>
+template <int SG, int VEC, bool MEAN, bool DECAY, bool REUSE>
 hipError_t launch_t(const Handle& h, const Plan& p, const uint32_t* keys, const uint32_t* perm,
                     const float* grad_out, float lr, float eps, char* ws, hipStream_t s,
                     const DecayArgs& dec) {
@@ -474,7 +478,7 @@ hipError_t launch_t(const Handle& h, const Plan& p, const uint32_t* keys, const 
   uint32_t* span_cnt = reinterpret_cast<uint32_t*>(ws + p.span_cnt);
   const uint32_t nbags = (uint32_t)(p.B * h.T);
   phase_mark(h, EMB_PHASE_REDUCE, false, s);
-  hipLaunchKernelGGL((k_seg_adagrad<SG, VEC, MEAN, MPL, UF, DECAY>), dim3((unsigned)grid),
+  hipLaunchKernelGGL((k_seg_adagrad<SG, VEC, MEAN, MPL, UF, DECAY, REUSE>), dim3((unsigned)grid),
                      dim3(256), 0, s, keys, gr, scale, grad_out, h.W, h.G, n,
                      (uint32_t)h.total_rows, h.D, lr, eps, ph, pt, span_u, seg_off, span_cnt,
                      nbags, dec.stamps, dec.log2_rho, dec.period, perm,
@@ -484,13 +488,13 @@ hipError_t launch_t(const Handle& h, const Plan& p, const uint32_t* keys, const 
   return hipGetLastError();
 }
 
-template <bool MEAN, bool DECAY>
+template <bool MEAN, bool DECAY, bool REUSE>
 hipError_t dispatch(const Handle& h, const Plan& p, const uint32_t* keys, const uint32_t* perm,
                     const float* grad_out, float lr, float eps, char* ws, hipStream_t s,
                     const DecayArgs& dec) {
   const int sg = subgroup_lanes(h.D), vec = vec_per_lane(h.D);
 #define EMBTAB_SEG_LAUNCH(SG_, VEC_) \
-  launch_t<SG_, VEC_, MEAN, DECAY>(h, p, keys, perm, grad_out, lr, eps, ws, s, dec)
+  launch_t<SG_, VEC_, MEAN, DECAY, REUSE>(h, p, keys, perm, grad_out, lr, eps, ws, s, dec)
   switch (sg) {
     case 1: return EMBTAB_SEG_LAUNCH(1, 1);
     case 2: return EMBTAB_SEG_LAUNCH(2, 1);
@@ -516,11 +520,19 @@ hipError_t launch_segment_adagrad(const Handle& h, const Plan& p, const uint32_t
                                   float lr, float eps, char* ws, hipStream_t s,
                                   const DecayArgs& dec) {
   if (!grad_out) return hipErrorInvalidValue;
-  if (dec.stamps)
-    return mean ? dispatch<true, true>(h, p, keys, perm, grad_out, lr, eps, ws, s, dec)
-                : dispatch<false, true>(h, p, keys, perm, grad_out, lr, eps, ws, s, dec);
-  return mean ? dispatch<true, false>(h, p, keys, perm, grad_out, lr, eps, ws, s, dec)
-              : dispatch<false, false>(h, p, keys, perm, grad_out, lr, eps, ws, s, dec);
+  // Whether a bag's gradient row is read by more than one occurrence: a cache
+  // policy only (both forms give the same result).  nnz == B * T means one id
+  // per bag as a rule (the kernel checks one-hot batches exactly where it
+  // matters); mean pooling is taken as multi-hot.
+  const bool reuse = mean || p.nnz != p.B * (int64_t)h.T;
+  if (dec.stamps) {
+    if (mean) return dispatch<true, true, true>(h, p, keys, perm, grad_out, lr, eps, ws, s, dec);
+    return reuse ? dispatch<false, true, true>(h, p, keys, perm, grad_out, lr, eps, ws, s, dec)
+                 : dispatch<false, true, false>(h, p, keys, perm, grad_out, lr, eps, ws, s, dec);
+  }
+  if (mean) return dispatch<true, false, true>(h, p, keys, perm, grad_out, lr, eps, ws, s, dec);
+  return reuse ? dispatch<false, false, true>(h, p, keys, perm, grad_out, lr, eps, ws, s, dec)
+               : dispatch<false, false, false>(h, p, keys, perm, grad_out, lr, eps, ws, s, dec);
 }
 
 }  // namespace embtab
