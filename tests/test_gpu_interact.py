@@ -1,7 +1,8 @@
 """The pooled lookup fused with the DLRM dot interaction, forward and
 backward, on the GPU against the oracle through the C ABI.  Cases cover one
 and two 16-row Gram blocks (T + 1 <= 16 and > 16), the largest shapes
-(T = 31, D = 256), mean pooling of multi-hot bags, empty bags, absent and
+(T = 31, D = 256), widths whose float4 count is not a power of two (D = 48,
+112), mean pooling of multi-hot bags, empty bags, absent and
 out-of-range ids, and a training step whose embedding gradient comes from the
 interaction backward."""
 import numpy as np
@@ -36,6 +37,13 @@ def case(name):
         return w, True
     if name == "max_31x256":
         return synth.workload(2, T=31, B=500, D=256, rows=np.full(31, 700)), False
+    if name == "multi_hot_d48":  # D / 4 = 12: item tables from a quotient by 12
+        w = synth.workload(3, T=13, B=600, D=48)
+        w.rows = np.full(13, 5_000, np.int64)
+        return w, False
+    if name == "one_hot_26_d112":  # D / 4 = 28, 12 items per lane, two row blocks
+        return synth.workload(2, T=26, B=700, D=112,
+                              rows=synth.log_uniform_rows(26, 2.0, 4.0, 3, 2)), False
     w = synth.workload(3, T=5, B=700, D=16)  # ragged bags, some empty
     w.rows = np.array([40, 900, 7, 300, 60], np.int64)
     return w, False
@@ -57,7 +65,7 @@ def z_abs(o, w, offsets, ids, dense, mean):
 
 
 @pytest.mark.parametrize("name", ["one_hot_26", "multi_hot_mean_8", "max_31x256",
-                                  "small_ragged"])
+                                  "small_ragged", "multi_hot_d48", "one_hot_26_d112"])
 def test_interaction_matches_oracle(name):
     w, mean = case(name)
     pool = eb.EMB_POOL_MEAN if mean else eb.EMB_POOL_SUM
