@@ -35,6 +35,9 @@
 //  * Feature admission (a key gets a row only once it is frequent enough):
 //    DeepRec page, section "model quality", EmbeddingVariable item 1
 //    (several admission methods; no formula is given).
+//  * Quantized exchange of embeddings between ranks: floats are quantized to
+//    int8 before the exchange and dequantized after (OneFlow OneEmbedding
+//    page, section "quantized compression").
 //  * Dynamic insertion of unseen feature keys, no capacity planning:
 //    OneFlow OneEmbedding page, section "ease of use"; HugeCTR interview,
 //    section two (a hash table identifies every input feature before the
@@ -58,6 +61,12 @@
 //  * Duplicate ids in one batch: their gradients are summed and the row gets
 //    one Adagrad step.  Accumulation is in ascending occurrence order.
 //  * Sort is stable: equal rows keep ascending occurrence position.
+//  * int8 exchange payload (the page gives no scheme): one symmetric scale per
+//    row of D values, codes in [-127, 127].  amax = max |x|; a zero row has
+//    scale 0 and codes 0; otherwise inv = 127 / amax, code = x * inv rounded
+//    to nearest (ties to even), scale = amax / 127, each step in fp32 (a code
+//    is an integer decided by floating point, so the oracle decides it in the
+//    same precision as the kernel).  Dequantized value: code * scale in fp32.
 //  * A key not yet in table t's map gets, in order of its first occurrence
 //    among this call's new keys, the next free row (rows freed by eviction,
 //    oldest eviction first), else row n_live[t] (rows never used, ascending);
@@ -726,6 +735,39 @@ int64_t orc_hash_export(void* h, int64_t t, uint64_t* keys, int64_t* rows, int64
     ++i;
   }
   return i;
+}
+
+// int8 exchange payload, row by row (the scheme is in the header notes).
+int32_t orc_quantize_rows_int8(const float* x, int64_t rows, int64_t D, int8_t* codes,
+                               float* scales) {
+  if (rows < 0 || D < 1 || (rows > 0 && (!x || !codes || !scales))) return -1;
+  for (int64_t r = 0; r < rows; ++r) {
+    const float* xr = x + r * D;
+    int8_t* cr = codes + r * D;
+    float amax = 0.0f;
+    for (int64_t d = 0; d < D; ++d) amax = std::max(amax, std::fabs(xr[d]));
+    if (amax == 0.0f) {
+      scales[r] = 0.0f;
+      for (int64_t d = 0; d < D; ++d) cr[d] = 0;
+      continue;
+    }
+    const float inv = 127.0f / amax;
+    for (int64_t d = 0; d < D; ++d) {
+      float v = std::nearbyint(xr[d] * inv);  // default rounding: to nearest, ties to even
+      v = std::min(127.0f, std::max(-127.0f, v));
+      cr[d] = (int8_t)v;
+    }
+    scales[r] = amax / 127.0f;
+  }
+  return 0;
+}
+
+int32_t orc_dequantize_rows_int8(const int8_t* codes, const float* scales, int64_t rows,
+                                 int64_t D, float* y) {
+  if (rows < 0 || D < 1 || (rows > 0 && (!codes || !scales || !y))) return -1;
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t d = 0; d < D; ++d) y[r * D + d] = (float)codes[r * D + d] * scales[r];
+  return 0;
 }
 
 }  // extern "C"

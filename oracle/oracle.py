@@ -59,6 +59,8 @@ def _load():
         "orc_hash_evict": (i64, [P, P, C.c_uint32]),
         "orc_free_rows": (i64, [P, i64]),
         "orc_hash_export": (i64, [P, i64, P, P, i64]),
+        "orc_quantize_rows_int8": (i32, [P, i64, i64, P, P]),
+        "orc_dequantize_rows_int8": (i32, [P, P, i64, i64, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -82,6 +84,26 @@ def splitmix64(x):
 
 def draw_bits(seed, t, r, i):
     return int(_load().orc_draw_bits(seed, t, r, i))
+
+
+def quantize_rows_int8(x):
+    """x: [rows, D] fp32 -> (codes int8 [rows, D], scales fp32 [rows])."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    rows, D = x.shape
+    codes = np.empty((rows, D), np.int8)
+    scales = np.empty(rows, np.float32)
+    assert _load().orc_quantize_rows_int8(_p(x), rows, D, _p(codes), _p(scales)) == 0
+    return codes, scales
+
+
+def dequantize_rows_int8(codes, scales):
+    """codes int8 [rows, D], scales fp32 [rows] -> fp32 [rows, D]."""
+    codes = np.ascontiguousarray(codes, dtype=np.int8)
+    scales = np.ascontiguousarray(scales, dtype=np.float32)
+    rows, D = codes.shape
+    y = np.empty((rows, D), np.float32)
+    assert _load().orc_dequantize_rows_int8(_p(codes), _p(scales), rows, D, _p(y)) == 0
+    return y
 
 
 def init_uniform(seed, t, row, d, lo, hi):

@@ -53,6 +53,10 @@ int64_t orc_hash_evict(void* h, const uint32_t* last_used, uint32_t before);
 int64_t orc_free_rows(void* h, int64_t t);
 int64_t orc_n_live(void* h, int64_t t);
 int64_t orc_hash_export(void* h, int64_t t, uint64_t* keys, int64_t* rows, int64_t cap);
+int32_t orc_quantize_rows_int8(const float* x, int64_t rows, int64_t D, int8_t* codes,
+                               float* scales);
+int32_t orc_dequantize_rows_int8(const int8_t* codes, const float* scales, int64_t rows,
+                                 int64_t D, float* y);
 }
 
 namespace {
@@ -166,6 +170,16 @@ void dense_round(int iter) {
   const int64_t nt = orc_touched_rows(h, touched.data());
   std::vector<float> w(D * (nt + 1)), g(D * (nt + 1));
   check(orc_read_rows(h, touched.data(), nt, w.data(), g.data()) == 0, "read rows", iter);
+  // int8 exchange payload of the pooled output, and back
+  {
+    const int64_t nr = (int64_t)B * T;
+    std::vector<int8_t> codes(nr * D + 1);
+    std::vector<float> scales(nr + 1), back(nr * D + 1);
+    check(orc_quantize_rows_int8(out.data(), nr, D, codes.data(), scales.data()) == 0,
+          "quantize", iter);
+    check(orc_dequantize_rows_int8(codes.data(), scales.data(), nr, D, back.data()) == 0,
+          "dequantize", iter);
+  }
   // invalid offsets: flagged, nothing written
   if (b.nnz > 0 && T * B > 1) {
     std::vector<int64_t> bad = b.offsets;
