@@ -511,6 +511,29 @@ size_t emb_stream_read_sink_floats(size_t bytes);
 emb_status_t emb_stream_read(const void* src, size_t bytes, float* sink, size_t sink_floats,
                              void* stream);
 
+/* ---------------------------------------------------------------- int8 exchange payload
+ * A table-wise split over ranks exchanges the pooled embeddings [B, T, D]
+ * (forward) and their gradients (backward); the OneFlow OneEmbedding page
+ * (section "quantized compression") quantizes that payload from float to
+ * int8 before the exchange and dequantizes it after.  The page gives no
+ * scheme; this is the reading, per row of `dim` values (rows = B * T for a
+ * pooled tensor), each step in fp32:
+ *   amax = max_d |x_d|;  amax == 0: scale 0 and codes 0;
+ *   otherwise code_d = round-to-nearest-even(x_d * (127 / amax)), clamped to
+ *   [-127, 127], and scale = amax / 127;
+ *   dequantized y_d = code_d * scale.
+ * x: [rows, dim] fp32, 16-byte aligned; codes: [rows, dim] int8, 4-byte
+ * aligned; scales: [rows] fp32, 4-byte aligned; y: [rows, dim] fp32, 16-byte
+ * aligned.  dim a multiple of 4 in [4, 1024].  x must be finite.  Device
+ * pointers, asynchronous on `stream`; rows = 0 launches nothing.
+ * EMB_ERR_INVALID_ARG for bad sizes, null or misaligned pointers; EMB_ERR_HIP
+ * if the launch fails.  The payload is 1/4 of the fp32 bytes plus 4 bytes
+ * per row. */
+emb_status_t emb_quantize_rows_int8(const float* x, int64_t rows, int32_t dim, int8_t* codes,
+                                    float* scales, void* stream);
+emb_status_t emb_dequantize_rows_int8(const int8_t* codes, const float* scales, int64_t rows,
+                                      int32_t dim, float* y, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

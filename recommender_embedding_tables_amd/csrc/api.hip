@@ -759,6 +759,38 @@ emb_status_t emb_stream_fill(void* dst, float value, size_t bytes, void* stream)
 
 size_t emb_stream_read_sink_floats(size_t bytes) { return stream_read_sink_floats(bytes); }
 
+// ---------------------------------------------------------------- int8 exchange payload
+
+static bool aligned4p(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+static bool quant_dims_ok(int64_t rows, int32_t dim) {
+  return rows >= 0 && dim >= 4 && dim % 4 == 0 && dim <= 1024;
+}
+
+emb_status_t emb_quantize_rows_int8(const float* x, int64_t rows, int32_t dim, int8_t* codes,
+                                    float* scales, void* stream) {
+  if (!quant_dims_ok(rows, dim)) return EMB_ERR_INVALID_ARG;
+  if (rows == 0) return EMB_OK;
+  if (!x || !codes || !scales || !aligned16p(x) || !aligned4p(codes) || !aligned4p(scales))
+    return EMB_ERR_INVALID_ARG;
+  return launch_quantize_rows(x, rows, dim, codes, scales, static_cast<hipStream_t>(stream)) ==
+                 hipSuccess
+             ? EMB_OK
+             : EMB_ERR_HIP;
+}
+
+emb_status_t emb_dequantize_rows_int8(const int8_t* codes, const float* scales, int64_t rows,
+                                      int32_t dim, float* y, void* stream) {
+  if (!quant_dims_ok(rows, dim)) return EMB_ERR_INVALID_ARG;
+  if (rows == 0) return EMB_OK;
+  if (!codes || !scales || !y || !aligned4p(codes) || !aligned4p(scales) || !aligned16p(y))
+    return EMB_ERR_INVALID_ARG;
+  return launch_dequantize_rows(codes, scales, rows, dim, y,
+                                static_cast<hipStream_t>(stream)) == hipSuccess
+             ? EMB_OK
+             : EMB_ERR_HIP;
+}
+
 emb_status_t emb_stream_read(const void* src, size_t bytes, float* sink, size_t sink_floats,
                              void* stream) {
   if (!src || !sink || bytes % 16 != 0 || !aligned16p(src) ||

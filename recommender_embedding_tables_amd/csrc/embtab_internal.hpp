@@ -391,6 +391,13 @@ size_t stream_read_sink_floats(size_t bytes);
 hipError_t launch_stream(int kind, void* dst, const void* src, size_t bytes, float value,
                          hipStream_t s);
 
+// int8 exchange payload: one symmetric scale per row of D values (D % 4 == 0,
+// D <= 1024); codes 4-byte aligned, x and y 16-byte aligned.
+hipError_t launch_quantize_rows(const float* x, int64_t rows, int32_t D, int8_t* codes,
+                                float* scales, hipStream_t s);
+hipError_t launch_dequantize_rows(const int8_t* codes, const float* scales, int64_t rows,
+                                  int32_t D, float* y, hipStream_t s);
+
 hipError_t launch_debug_copy_sorted(const uint32_t* keys, uint32_t sentinel, uint32_t* out,
                                     int64_t n, hipStream_t s);
 

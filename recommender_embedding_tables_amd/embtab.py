@@ -54,7 +54,8 @@ EXPORTED = [
     "emb_hash_evict_workspace_bytes", "emb_hash_evict", "emb_hash_free_rows",
     "emb_interact_out_dim", "emb_bag_forward_interact", "emb_interact_backward",
     "emb_bag_prepare_ids", "emb_cache_prepare", "emb_stream_copy", "emb_stream_fill",
-    "emb_stream_read_sink_floats", "emb_stream_read",
+    "emb_stream_read_sink_floats", "emb_stream_read", "emb_quantize_rows_int8",
+    "emb_dequantize_rows_int8",
 ]
 
 EMB_PHASE_FORWARD, EMB_PHASE_KEYS, EMB_PHASE_SORT, EMB_PHASE_UNIQUE = 0, 1, 2, 3
@@ -150,6 +151,8 @@ def _load():
         "emb_stream_fill": (i32, [P, f32, sz, P]),
         "emb_stream_read_sink_floats": (sz, [sz]),
         "emb_stream_read": (i32, [P, sz, P, sz, P]),
+        "emb_quantize_rows_int8": (i32, [P, i64, i32, P, P, P]),
+        "emb_dequantize_rows_int8": (i32, [P, P, i64, i32, P, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -483,3 +486,13 @@ def emb_stream_read_sink_floats(nbytes) -> int:
 
 def emb_stream_read(src, nbytes, sink, sink_floats, stream=None) -> int:
     return _lib.emb_stream_read(_ptr(src), nbytes, _ptr(sink), sink_floats, _stream(stream))
+
+
+def emb_quantize_rows_int8(x, rows, dim, codes, scales, stream=None) -> int:
+    return _lib.emb_quantize_rows_int8(_ptr(x), rows, dim, _ptr(codes), _ptr(scales),
+                                       _stream(stream))
+
+
+def emb_dequantize_rows_int8(codes, scales, rows, dim, y, stream=None) -> int:
+    return _lib.emb_dequantize_rows_int8(_ptr(codes), _ptr(scales), rows, dim, _ptr(y),
+                                         _stream(stream))

@@ -16,7 +16,7 @@ eb = pytest.importorskip("recommender_embedding_tables_amd.embtab",
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(emb_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(emb_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_exports_every_declared_symbol():
@@ -299,3 +299,25 @@ def test_interaction_host_checks():
                                                0x50000000, 0) == eb.EMB_ERR_UNSUPPORTED
         finally:
             eb.emb_table_destroy(h)
+
+
+def test_int8_payload_host_checks():
+    # argument checks only: nothing is launched
+    x, c, s, y = 0x50000000, 0x50000000, 0x50000000, 0x50000000
+    def q(*a):
+        return eb.emb_quantize_rows_int8(*a, 0)
+
+    def dq(*a):
+        return eb.emb_dequantize_rows_int8(*a, 0)
+
+    assert q(x, 0, 128, c, s) == eb.EMB_OK and dq(c, s, 0, 128, y) == eb.EMB_OK
+    for dim in (0, 2, 6, 1028):  # a multiple of 4 in [4, 1024]
+        assert q(x, 4, dim, c, s) == eb.EMB_ERR_INVALID_ARG
+        assert dq(c, s, 4, dim, y) == eb.EMB_ERR_INVALID_ARG
+    assert q(x, -1, 8, c, s) == eb.EMB_ERR_INVALID_ARG
+    assert q(None, 4, 8, c, s) == eb.EMB_ERR_INVALID_ARG
+    assert q(x + 4, 4, 8, c, s) == eb.EMB_ERR_INVALID_ARG  # x 16-byte aligned
+    assert q(x, 4, 8, c + 2, s) == eb.EMB_ERR_INVALID_ARG  # codes 4-byte aligned
+    assert q(x, 4, 8, c, s + 1) == eb.EMB_ERR_INVALID_ARG
+    assert dq(c, s, 4, 8, y + 8) == eb.EMB_ERR_INVALID_ARG  # y 16-byte aligned
+    assert dq(c, None, 4, 8, y) == eb.EMB_ERR_INVALID_ARG
