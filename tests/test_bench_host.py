@@ -112,3 +112,11 @@ def test_shard_option_is_refused_where_it_does_not_apply():
     assert r.returncode == 2 and "--shard" in r.stderr
     r = _run("--shard", "8/8")
     assert r.returncode == 2 and "--shard" in r.stderr
+
+
+@pytest.mark.skipif(not os.path.exists(os.path.join(ROOT, "recommender_embedding_tables_amd",
+                                                    "libembtab.so")),
+                    reason="the HIP library is not built")
+def test_int8_exchange_needs_the_pooled_output():
+    r = _run("--interact", "--schedule", "prepared", "--int8-exchange")
+    assert r.returncode == 2 and "--int8-exchange" in r.stderr
