@@ -314,6 +314,19 @@ emb_status_t emb_bag_prepare(emb_table_t h, const int64_t* offsets, const int64_
 emb_status_t emb_bag_forward_prepared(emb_table_t h, const int64_t* offsets, const int64_t* ids,
                                       int64_t batch, int64_t nnz, emb_pool_t pool, float* out,
                                       void* ws, size_t ws_bytes, void* stream);
+/* emb_bag_forward_prepared writing the int8 exchange payload of a table-wise
+ * split instead of fp32 rows: for every bag b' = s*T + t (the rows of `out`),
+ * codes[b', :] and scales[b'] are what emb_quantize_rows_int8 gives for the
+ * pooled row; the fp32 rows are never written (a quarter of the output bytes
+ * plus 4 bytes per bag).  codes [B*T, D] int8 and scales [B*T] fp32, both
+ * 4-byte aligned.  On one-hot batches the pooled row is the table row itself,
+ * so the payload is exactly the quantized row; on multi-hot batches it is
+ * quantized from the fp32 sum, whose rounding may move a code by one against
+ * the quantized exact sum.  Errors as emb_bag_forward_prepared. */
+emb_status_t emb_bag_forward_prepared_int8(emb_table_t h, const int64_t* offsets,
+                                           const int64_t* ids, int64_t batch, int64_t nnz,
+                                           emb_pool_t pool, int8_t* codes, float* scales,
+                                           void* ws, size_t ws_bytes, void* stream);
 emb_status_t emb_bag_backward_adagrad_prepared(emb_table_t h, int64_t batch, int64_t nnz,
                                                emb_pool_t pool, const float* grad_out, float lr,
                                                float eps, void* ws, size_t ws_bytes,

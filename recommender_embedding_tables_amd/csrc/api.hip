@@ -524,6 +524,36 @@ static emb_status_t backward_prepared(emb_table_t t, int64_t batch, int64_t nnz,
                                            lr, eps, w, static_cast<hipStream_t>(stream), dec));
 }
 
+emb_status_t emb_bag_forward_prepared_int8(emb_table_t t, const int64_t* offsets,
+                                           const int64_t* ids, int64_t batch, int64_t nnz,
+                                           emb_pool_t pool, int8_t* codes, float* scales,
+                                           void* ws, size_t ws_bytes, void* stream) {
+  if (!t || !codes || !scales || (nnz > 0 && !ids)) return EMB_ERR_INVALID_ARG;
+  if (pool != EMB_POOL_SUM && pool != EMB_POOL_MEAN) return EMB_ERR_INVALID_ARG;
+  emb_status_t st = check_batch(t->h, offsets, batch, nnz);
+  if (st != EMB_OK) return st;
+  if ((reinterpret_cast<uintptr_t>(codes) & 3u) != 0 ||
+      (reinterpret_cast<uintptr_t>(scales) & 3u) != 0)
+    return EMB_ERR_INVALID_ARG;
+  Plan p;
+  if (!make_plan(t->h, batch, nnz, &p)) return EMB_ERR_UNSUPPORTED;
+  if (!ws || ws_bytes < p.total || (reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
+    return EMB_ERR_WORKSPACE;
+  if (batch == 0) return EMB_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+  uint32_t *keys = nullptr, *vals = nullptr;
+  sorted_arrays(t->h, p, w, &keys, &vals);
+  phase_mark(t->h, EMB_PHASE_FORWARD, false, s);
+  const uint32_t* rowmap =
+      t->h.tiered ? reinterpret_cast<const uint32_t*>(w + p.c_rowmap) : nullptr;
+  hipError_t e = launch_forward_prepared_int8(t->h, p, offsets, ids, pool == EMB_POOL_MEAN,
+                                              nnz == batch * (int64_t)t->h.T, keys, vals, codes,
+                                              scales, w, rowmap, s);
+  phase_mark(t->h, EMB_PHASE_FORWARD, true, s);
+  return hip_status(e);
+}
+
 emb_status_t emb_bag_backward_adagrad_prepared(emb_table_t t, int64_t batch, int64_t nnz,
                                                emb_pool_t pool, const float* grad_out, float lr,
                                                float eps, void* ws, size_t ws_bytes,

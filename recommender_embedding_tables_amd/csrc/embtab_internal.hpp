@@ -353,6 +353,14 @@ hipError_t launch_forward_sorted(const Handle& h, const Plan& p, const int64_t* 
                                  const uint32_t* perm, float* out, char* ws,
                                  const uint32_t* rowmap, hipStream_t s);
 // The pooled kernel alone (the ids and offsets are read directly).
+// The prepared forward writing the int8 exchange payload (codes [B*T, D],
+// one scale per row) instead of fp32 rows: the sorted one-hot kernel when
+// maybe_one_hot (nnz == B * T), else the pooled one.
+hipError_t launch_forward_prepared_int8(const Handle& h, const Plan& p, const int64_t* offsets,
+                                        const int64_t* ids, bool mean, bool maybe_one_hot,
+                                        const uint32_t* keys, const uint32_t* perm,
+                                        int8_t* codes, float* scales, char* ws,
+                                        const uint32_t* rowmap, hipStream_t s);
 hipError_t launch_forward_bags(const Handle& h, const int64_t* offsets, const int64_t* ids,
                                int64_t B, int64_t nnz, bool mean, float* out,
                                const uint32_t* rowmap, hipStream_t s);
@@ -391,8 +399,27 @@ size_t stream_read_sink_floats(size_t bytes);
 hipError_t launch_stream(int kind, void* dst, const void* src, size_t bytes, float value,
                          hipStream_t s);
 
-// int8 exchange payload: one symmetric scale per row of D values (D % 4 == 0,
-// D <= 1024); codes 4-byte aligned, x and y 16-byte aligned.
+// int8 exchange payload, per row of D values: amax = max |x|, inv = 127 / amax
+// (0 for a zero row), code = x * inv rounded to nearest with ties to even and
+// clamped to +-127, scale = amax / 127; every step in fp32.  The quantize
+// kernel and the fused forward share these two helpers.
+__device__ inline float abs_max4(f4 v) {
+  return __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(v[0]), __builtin_fabsf(v[1])),
+                         __builtin_fmaxf(__builtin_fabsf(v[2]), __builtin_fabsf(v[3])));
+}
+// The four codes of one float4, packed little-endian in a word.
+__device__ inline uint32_t int8_code_word(f4 v, float inv) {
+  uint32_t w = 0u;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float q =
+        __builtin_fminf(127.0f, __builtin_fmaxf(-127.0f, __builtin_rintf(v[e] * inv)));
+    w |= (uint32_t)(uint8_t)(int8_t)(int)q << (8 * e);
+  }
+  return w;
+}
+
+// D % 4 == 0, D <= 1024; codes 4-byte aligned, x and y 16-byte aligned.
 hipError_t launch_quantize_rows(const float* x, int64_t rows, int32_t D, int8_t* codes,
                                 float* scales, hipStream_t s);
 hipError_t launch_dequantize_rows(const int8_t* codes, const float* scales, int64_t rows,

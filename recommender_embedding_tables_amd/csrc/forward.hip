@@ -36,13 +36,53 @@ struct BagTileLds {
   uint32_t start[kFwdTileBags], len[kFwdTileBags], row[kFwdTileBags];
 };
 
+// Where a pooled row goes, written by all SG lanes of its sub-group at once:
+// fp32 rows of `out` [bags, D], or the int8 exchange payload of a table-wise
+// split (codes [bags, D] and one scale per row, quantized as
+// emb_quantize_rows_int8 does it, so the fp32 rows are never written).
+struct F32Rows {
+  float* out;
+  template <int SG, int VEC>
+  __device__ __forceinline__ void put(size_t row, uint32_t D, uint32_t lane,
+                                      const f4 (&v)[VEC]) const {
+    const uint32_t D4 = D >> 2;
+#pragma unroll
+    for (int k = 0; k < VEC; ++k) {
+      const uint32_t d4 = lane + k * SG;
+      if (d4 < D4)
+        __builtin_nontemporal_store(v[k], reinterpret_cast<f4*>(out + row * D + 4 * d4));
+    }
+  }
+};
+struct I8Rows {
+  uint32_t* codes;  // four codes per word
+  float* scales;
+  template <int SG, int VEC>
+  __device__ __forceinline__ void put(size_t row, uint32_t D, uint32_t lane,
+                                      const f4 (&v)[VEC]) const {
+    const uint32_t D4 = D >> 2;
+    float amax = 0.0f;
+#pragma unroll
+    for (int k = 0; k < VEC; ++k)
+      if (lane + k * SG < D4) amax = __builtin_fmaxf(amax, abs_max4(v[k]));
+    for (int o = SG / 2; o > 0; o >>= 1) amax = __builtin_fmaxf(amax, __shfl_xor(amax, o, SG));
+    const float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
+#pragma unroll
+    for (int k = 0; k < VEC; ++k) {
+      const uint32_t d4 = lane + k * SG;
+      if (d4 < D4) __builtin_nontemporal_store(int8_code_word(v[k], inv), codes + row * D4 + d4);
+    }
+    if (lane == 0) scales[row] = amax / 127.0f;
+  }
+};
+
 // Pools sample tile `tile` (samples tile*S .. tile*S + S - 1 of every table);
 // returns the EMB_FLAG_* bits it found.  Called by all 256 threads of a block.
-template <int SG, int VEC, bool MEAN, int UNR>
+template <int SG, int VEC, bool MEAN, int UNR, class OUT>
 __device__ __forceinline__ uint32_t bag_tile(
     uint32_t tile, const int64_t* __restrict__ offsets, const int64_t* __restrict__ ids,
     const float* __restrict__ W, const int64_t* __restrict__ row_off,
-    const int64_t* __restrict__ rows, float* __restrict__ out, uint32_t B, uint32_t T,
+    const int64_t* __restrict__ rows, OUT out, uint32_t B, uint32_t T,
     uint32_t D, uint32_t nnz, uint32_t S, BagTileLds& lds, const uint32_t* __restrict__ rowmap) {
   constexpr int SGPB = 256 / SG;
   uint32_t* s_start = lds.start;
@@ -195,43 +235,32 @@ __device__ __forceinline__ uint32_t bag_tile(
           }
         }
         const float c = (MEAN && len > 0u) ? 1.0f / (float)len : 1.0f;
-        const size_t o = (qbase + q0 + u) * D;
+        f4 rr[VEC];
 #pragma unroll
-        for (int v = 0; v < VEC; ++v) {
-          const uint32_t d4 = lane + v * SG;
-          if (d4 < D4) {
-            const f4 rr = MEAN ? a[v] * c : a[v];
-            __builtin_nontemporal_store(rr, reinterpret_cast<f4*>(out + o + 4 * d4));
-          }
-        }
+        for (int v = 0; v < VEC; ++v) rr[v] = MEAN ? a[v] * c : a[v];
+        out.template put<SG, VEC>(qbase + q0 + u, D, lane, rr);
       }
       continue;
     }
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
       if (q0 + u >= ntile) continue;
-      const size_t o = (qbase + q0 + u) * D;
-#pragma unroll
-      for (int v = 0; v < VEC; ++v) {
-        const uint32_t d4 = lane + v * SG;
-        if (d4 < D4)
-          __builtin_nontemporal_store(acc[u][v], reinterpret_cast<f4*>(out + o + 4 * d4));
-      }
+      out.template put<SG, VEC>(qbase + q0 + u, D, lane, acc[u]);
     }
   }
   return bad;
 }
 
-template <int SG, int VEC, bool MEAN, int UNR>
+template <int SG, int VEC, bool MEAN, int UNR, class OUT>
 __global__ __launch_bounds__(256) void k_bag_forward(
     const int64_t* __restrict__ offsets, const int64_t* __restrict__ ids,
     const float* __restrict__ W, const int64_t* __restrict__ row_off,
-    const int64_t* __restrict__ rows, float* __restrict__ out, uint32_t* __restrict__ flags,
+    const int64_t* __restrict__ rows, OUT out, uint32_t* __restrict__ flags,
     uint32_t B, uint32_t T, uint32_t D, uint32_t nnz, uint32_t S,
     const uint32_t* __restrict__ rowmap) {
   __shared__ BagTileLds lds;
-  const uint32_t bad = bag_tile<SG, VEC, MEAN, UNR>(xcd_block(), offsets, ids, W, row_off, rows,
-                                                    out, B, T, D, nnz, S, lds, rowmap);
+  const uint32_t bad = bag_tile<SG, VEC, MEAN, UNR, OUT>(xcd_block(), offsets, ids, W, row_off,
+                                                         rows, out, B, T, D, nnz, S, lds, rowmap);
   if (bad) atomicOr(flags, bad);
 }
 
@@ -254,10 +283,10 @@ constexpr int fwd_chunk() {
 // Whether the batch is one-hot is known only on the device (a flag set while
 // the keys were built), so the same launch also holds the general pooled
 // kernel: when the flag is set, block i pools sample tile i instead.
-template <int SG, int VEC, int MPL, bool MEAN, int UNR>
+template <int SG, int VEC, int MPL, bool MEAN, int UNR, class OUT>
 __global__ __launch_bounds__(256) void k_fwd_sorted(
     const uint32_t* __restrict__ keys, const uint32_t* __restrict__ perm,
-    const uint32_t* __restrict__ gr, const float* __restrict__ W, float* __restrict__ out,
+    const uint32_t* __restrict__ gr, const float* __restrict__ W, OUT out,
     uint32_t n, uint32_t sentinel, uint32_t D, uint32_t nbags,
     const uint32_t* __restrict__ misc, const int64_t* __restrict__ offsets,
     const int64_t* __restrict__ ids, const int64_t* __restrict__ row_off,
@@ -265,8 +294,8 @@ __global__ __launch_bounds__(256) void k_fwd_sorted(
     uint32_t S, const uint32_t* __restrict__ rowmap) {
   if (batch_not_one_hot(misc)) {
     __shared__ BagTileLds lds;
-    const uint32_t bad = bag_tile<SG, VEC, MEAN, UNR>(xcd_block(), offsets, ids, W, row_off,
-                                                      rows, out, B, T, D, n, S, lds, rowmap);
+    const uint32_t bad = bag_tile<SG, VEC, MEAN, UNR, OUT>(xcd_block(), offsets, ids, W, row_off,
+                                                           rows, out, B, T, D, n, S, lds, rowmap);
     if (bad) atomicOr(flags, bad);
     return;
   }
@@ -326,15 +355,7 @@ __global__ __launch_bounds__(256) void k_fwd_sorted(
 #pragma unroll
           for (int v = 0; v < VEC; ++v) x[u][v] = u == 0 ? prevrow[v] : x[u > 0 ? u - 1 : 0][v];
         }
-        if (gg[u] < nbags) {
-#pragma unroll
-          for (int v = 0; v < VEC; ++v) {
-            const uint32_t d4 = lane + v * SG;
-            if (d4 < D4)
-              __builtin_nontemporal_store(x[u][v],
-                                          reinterpret_cast<f4*>(out + (size_t)gg[u] * D + 4 * d4));
-          }
-        }
+        if (gg[u] < nbags) out.template put<SG, VEC>(gg[u], D, lane, x[u]);
       }
       prevkey = kk[UF - 1];
 #pragma unroll
@@ -357,36 +378,36 @@ constexpr int fwd_unroll() {
   return VEC == 1 ? 8 : (VEC == 2 ? 4 : 2);  // one-hot rows in flight per lane
 }
 
-template <int SG, int VEC, bool MEAN>
+template <int SG, int VEC, bool MEAN, class OUT>
 hipError_t launch_t(const Handle& h, const int64_t* offsets, const int64_t* ids, int64_t B,
-                    int64_t nnz, float* out, const uint32_t* rowmap, hipStream_t s) {
+                    int64_t nnz, OUT out, const uint32_t* rowmap, hipStream_t s) {
   const int64_t S = tile_samples(h.T, B, nnz);
   const int64_t grid = (B + S - 1) / S;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((k_bag_forward<SG, VEC, MEAN, fwd_unroll<VEC>()>), dim3((unsigned)grid),
+  hipLaunchKernelGGL((k_bag_forward<SG, VEC, MEAN, fwd_unroll<VEC>(), OUT>), dim3((unsigned)grid),
                      dim3(256), 0, s, offsets, ids, h.W, h.sv.row_off, h.sv.rows, out,
                      h.sv.flags, (uint32_t)B, (uint32_t)h.T, (uint32_t)h.D, (uint32_t)nnz,
                      (uint32_t)S, rowmap);
   return hipGetLastError();
 }
 
-template <bool MEAN>
+template <bool MEAN, class OUT>
 hipError_t dispatch(const Handle& h, const int64_t* offsets, const int64_t* ids, int64_t B,
-                    int64_t nnz, float* out, const uint32_t* rowmap, hipStream_t s) {
+                    int64_t nnz, OUT out, const uint32_t* rowmap, hipStream_t s) {
   const int sg = subgroup_lanes(h.D), vec = vec_per_lane(h.D);
   switch (sg) {
-    case 1: return launch_t<1, 1, MEAN>(h, offsets, ids, B, nnz, out, rowmap, s);
-    case 2: return launch_t<2, 1, MEAN>(h, offsets, ids, B, nnz, out, rowmap, s);
-    case 4: return launch_t<4, 1, MEAN>(h, offsets, ids, B, nnz, out, rowmap, s);
-    case 8: return launch_t<8, 1, MEAN>(h, offsets, ids, B, nnz, out, rowmap, s);
-    case 16: return launch_t<16, 1, MEAN>(h, offsets, ids, B, nnz, out, rowmap, s);
-    case 32: return launch_t<32, 1, MEAN>(h, offsets, ids, B, nnz, out, rowmap, s);
+    case 1: return launch_t<1, 1, MEAN, OUT>(h, offsets, ids, B, nnz, out, rowmap, s);
+    case 2: return launch_t<2, 1, MEAN, OUT>(h, offsets, ids, B, nnz, out, rowmap, s);
+    case 4: return launch_t<4, 1, MEAN, OUT>(h, offsets, ids, B, nnz, out, rowmap, s);
+    case 8: return launch_t<8, 1, MEAN, OUT>(h, offsets, ids, B, nnz, out, rowmap, s);
+    case 16: return launch_t<16, 1, MEAN, OUT>(h, offsets, ids, B, nnz, out, rowmap, s);
+    case 32: return launch_t<32, 1, MEAN, OUT>(h, offsets, ids, B, nnz, out, rowmap, s);
     default:
       switch (vec) {
-        case 1: return launch_t<64, 1, MEAN>(h, offsets, ids, B, nnz, out, rowmap, s);
-        case 2: return launch_t<64, 2, MEAN>(h, offsets, ids, B, nnz, out, rowmap, s);
-        case 3: return launch_t<64, 3, MEAN>(h, offsets, ids, B, nnz, out, rowmap, s);
-        default: return launch_t<64, 4, MEAN>(h, offsets, ids, B, nnz, out, rowmap, s);
+        case 1: return launch_t<64, 1, MEAN, OUT>(h, offsets, ids, B, nnz, out, rowmap, s);
+        case 2: return launch_t<64, 2, MEAN, OUT>(h, offsets, ids, B, nnz, out, rowmap, s);
+        case 3: return launch_t<64, 3, MEAN, OUT>(h, offsets, ids, B, nnz, out, rowmap, s);
+        default: return launch_t<64, 4, MEAN, OUT>(h, offsets, ids, B, nnz, out, rowmap, s);
       }
   }
 }
@@ -396,8 +417,9 @@ hipError_t dispatch(const Handle& h, const int64_t* offsets, const int64_t* ids,
 hipError_t launch_forward(const Handle& h, const int64_t* offsets, const int64_t* ids,
                           int64_t B, int64_t nnz, bool mean, float* out, hipStream_t s) {
   phase_mark(h, EMB_PHASE_FORWARD, false, s);
-  hipError_t e = mean ? dispatch<true>(h, offsets, ids, B, nnz, out, nullptr, s)
-                      : dispatch<false>(h, offsets, ids, B, nnz, out, nullptr, s);
+  const F32Rows o{out};
+  hipError_t e = mean ? dispatch<true>(h, offsets, ids, B, nnz, o, nullptr, s)
+                      : dispatch<false>(h, offsets, ids, B, nnz, o, nullptr, s);
   phase_mark(h, EMB_PHASE_FORWARD, true, s);
   return e;
 }
@@ -405,15 +427,16 @@ hipError_t launch_forward(const Handle& h, const int64_t* offsets, const int64_t
 hipError_t launch_forward_bags(const Handle& h, const int64_t* offsets, const int64_t* ids,
                                int64_t B, int64_t nnz, bool mean, float* out,
                                const uint32_t* rowmap, hipStream_t s) {
-  return mean ? dispatch<true>(h, offsets, ids, B, nnz, out, rowmap, s)
-              : dispatch<false>(h, offsets, ids, B, nnz, out, rowmap, s);
+  const F32Rows o{out};
+  return mean ? dispatch<true>(h, offsets, ids, B, nnz, o, rowmap, s)
+              : dispatch<false>(h, offsets, ids, B, nnz, o, rowmap, s);
 }
 
 namespace {
-template <int SG, int VEC, bool MEAN>
+template <int SG, int VEC, bool MEAN, class OUT>
 hipError_t launch_sorted_t(const Handle& h, const Plan& p, const int64_t* offsets,
                            const int64_t* ids, const uint32_t* keys, const uint32_t* perm,
-                           float* out, char* ws, const uint32_t* rowmap, hipStream_t s) {
+                           OUT out, char* ws, const uint32_t* rowmap, hipStream_t s) {
   constexpr int MPL = chunk_rounds<SG>();
   constexpr int SGPB = 256 / SG;
   constexpr int CH = fwd_chunk<SG, MPL>();
@@ -423,7 +446,8 @@ hipError_t launch_sorted_t(const Handle& h, const Plan& p, const int64_t* offset
   int64_t grid = (chunks + SGPB - 1) / SGPB;
   grid = grid > tiles ? grid : tiles;  // enough blocks for either path
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((k_fwd_sorted<SG, VEC, MPL, MEAN, fwd_unroll<VEC>()>), dim3((unsigned)grid),
+  hipLaunchKernelGGL((k_fwd_sorted<SG, VEC, MPL, MEAN, fwd_unroll<VEC>(), OUT>),
+                     dim3((unsigned)grid),
                      dim3(256), 0, s, keys, perm,
                      reinterpret_cast<const uint32_t*>(ws + p.sgr), h.W, out, (uint32_t)p.nnz,
                      (uint32_t)h.total_rows, (uint32_t)h.D, (uint32_t)(p.B * h.T),
@@ -432,13 +456,13 @@ hipError_t launch_sorted_t(const Handle& h, const Plan& p, const int64_t* offset
   return hipGetLastError();
 }
 
-template <bool MEAN>
+template <bool MEAN, class OUT>
 hipError_t dispatch_sorted(const Handle& h, const Plan& p, const int64_t* offsets,
                            const int64_t* ids, const uint32_t* keys, const uint32_t* perm,
-                           float* out, char* ws, const uint32_t* rowmap, hipStream_t s) {
+                           OUT out, char* ws, const uint32_t* rowmap, hipStream_t s) {
   const int sg = subgroup_lanes(h.D), vec = vec_per_lane(h.D);
 #define EMB_SORTED(SG_, VEC_) \
-  launch_sorted_t<SG_, VEC_, MEAN>(h, p, offsets, ids, keys, perm, out, ws, rowmap, s)
+  launch_sorted_t<SG_, VEC_, MEAN, OUT>(h, p, offsets, ids, keys, perm, out, ws, rowmap, s)
   switch (sg) {
     case 1: return EMB_SORTED(1, 1);
     case 2: return EMB_SORTED(2, 1);
@@ -462,8 +486,22 @@ hipError_t launch_forward_sorted(const Handle& h, const Plan& p, const int64_t* 
                                  const int64_t* ids, bool mean, const uint32_t* keys,
                                  const uint32_t* perm, float* out, char* ws,
                                  const uint32_t* rowmap, hipStream_t s) {
-  return mean ? dispatch_sorted<true>(h, p, offsets, ids, keys, perm, out, ws, rowmap, s)
-              : dispatch_sorted<false>(h, p, offsets, ids, keys, perm, out, ws, rowmap, s);
+  const F32Rows o{out};
+  return mean ? dispatch_sorted<true>(h, p, offsets, ids, keys, perm, o, ws, rowmap, s)
+              : dispatch_sorted<false>(h, p, offsets, ids, keys, perm, o, ws, rowmap, s);
+}
+
+hipError_t launch_forward_prepared_int8(const Handle& h, const Plan& p, const int64_t* offsets,
+                                        const int64_t* ids, bool mean, bool maybe_one_hot,
+                                        const uint32_t* keys, const uint32_t* perm,
+                                        int8_t* codes, float* scales, char* ws,
+                                        const uint32_t* rowmap, hipStream_t s) {
+  const I8Rows o{reinterpret_cast<uint32_t*>(codes), scales};
+  if (maybe_one_hot)
+    return mean ? dispatch_sorted<true>(h, p, offsets, ids, keys, perm, o, ws, rowmap, s)
+                : dispatch_sorted<false>(h, p, offsets, ids, keys, perm, o, ws, rowmap, s);
+  return mean ? dispatch<true>(h, offsets, ids, p.B, p.nnz, o, rowmap, s)
+              : dispatch<false>(h, offsets, ids, p.B, p.nnz, o, rowmap, s);
 }
 
 }  // namespace embtab

@@ -24,11 +24,6 @@ namespace embtab {
 
 namespace {
 
-__device__ inline uint32_t code_byte(float x, float inv) {
-  const float q = __builtin_fminf(127.0f, __builtin_fmaxf(-127.0f, __builtin_rintf(x * inv)));
-  return (uint32_t)(uint8_t)(int8_t)(int)q;
-}
-
 template <int SG, int VEC>
 __global__ __launch_bounds__(256) void k_quantize_rows(const float* __restrict__ x, int64_t rows,
                                                        int32_t D, uint32_t* __restrict__ codes,
@@ -45,10 +40,7 @@ __global__ __launch_bounds__(256) void k_quantize_rows(const float* __restrict__
   for (int k = 0; k < VEC; ++k) {
     const int c = lane + k * SG;
     v[k] = c < D4 ? __builtin_nontemporal_load(xr + c) : f4{0.f, 0.f, 0.f, 0.f};
-    amax = __builtin_fmaxf(amax, __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(v[k][0]),
-                                                                 __builtin_fabsf(v[k][1])),
-                                                 __builtin_fmaxf(__builtin_fabsf(v[k][2]),
-                                                                 __builtin_fabsf(v[k][3]))));
+    amax = __builtin_fmaxf(amax, abs_max4(v[k]));
   }
   for (int o = SG / 2; o > 0; o >>= 1) amax = __builtin_fmaxf(amax, __shfl_xor(amax, o, SG));
   const float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
@@ -57,9 +49,7 @@ __global__ __launch_bounds__(256) void k_quantize_rows(const float* __restrict__
   for (int k = 0; k < VEC; ++k) {
     const int c = lane + k * SG;
     if (c < D4) {
-      const uint32_t w = code_byte(v[k][0], inv) | (code_byte(v[k][1], inv) << 8) |
-                         (code_byte(v[k][2], inv) << 16) | (code_byte(v[k][3], inv) << 24);
-      __builtin_nontemporal_store(w, cr + c);
+      __builtin_nontemporal_store(int8_code_word(v[k], inv), cr + c);
     }
   }
   if (lane == 0) scales[r] = amax / 127.0f;

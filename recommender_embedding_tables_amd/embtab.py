@@ -55,7 +55,7 @@ EXPORTED = [
     "emb_interact_out_dim", "emb_bag_forward_interact", "emb_interact_backward",
     "emb_bag_prepare_ids", "emb_cache_prepare", "emb_stream_copy", "emb_stream_fill",
     "emb_stream_read_sink_floats", "emb_stream_read", "emb_quantize_rows_int8",
-    "emb_dequantize_rows_int8",
+    "emb_dequantize_rows_int8", "emb_bag_forward_prepared_int8",
 ]
 
 EMB_PHASE_FORWARD, EMB_PHASE_KEYS, EMB_PHASE_SORT, EMB_PHASE_UNIQUE = 0, 1, 2, 3
@@ -152,6 +152,7 @@ def _load():
         "emb_stream_read_sink_floats": (sz, [sz]),
         "emb_stream_read": (i32, [P, sz, P, sz, P]),
         "emb_quantize_rows_int8": (i32, [P, i64, i32, P, P, P]),
+        "emb_bag_forward_prepared_int8": (i32, [P, P, P, i64, i64, i32, P, P, P, sz, P]),
         "emb_dequantize_rows_int8": (i32, [P, P, i64, i32, P, P]),
     }
     for name, (res, args) in sig.items():
@@ -491,6 +492,13 @@ def emb_stream_read(src, nbytes, sink, sink_floats, stream=None) -> int:
 def emb_quantize_rows_int8(x, rows, dim, codes, scales, stream=None) -> int:
     return _lib.emb_quantize_rows_int8(_ptr(x), rows, dim, _ptr(codes), _ptr(scales),
                                        _stream(stream))
+
+
+def emb_bag_forward_prepared_int8(handle, offsets, ids, batch, nnz, pool, codes, scales, ws,
+                                  ws_bytes, stream=None) -> int:
+    return _lib.emb_bag_forward_prepared_int8(handle, _ptr(offsets), _ptr(ids), batch, nnz,
+                                              pool, _ptr(codes), _ptr(scales), _ptr(ws),
+                                              ws_bytes, _stream(stream))
 
 
 def emb_dequantize_rows_int8(codes, scales, rows, dim, y, stream=None) -> int:

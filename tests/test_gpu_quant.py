@@ -68,3 +68,69 @@ def test_int8_payload_full_pooled_shape():
     np.testing.assert_array_equal(codes, rc)
     np.testing.assert_array_equal(scales, rs)
     np.testing.assert_array_equal(y, orc.dequantize_rows_int8(rc, rs))
+
+
+# ------------------------------------------------ forward writing the payload
+
+from recommender_embedding_tables_amd import synth  # noqa: E402
+from tests.helpers import forward_S  # noqa: E402
+
+
+def _workload(name):
+    if name == "one_hot":
+        return synth.workload(2, T=26, B=2000, D=128,
+                              rows=synth.log_uniform_rows(26, 2.0, 5.0, 3, 2))
+    w = synth.workload(3, T=6, B=500, D=64)
+    w.rows = np.full(6, 20_000, np.int64)
+    w.pool_mean = name == "multi_hot_mean"
+    return w
+
+
+@pytest.mark.parametrize("name", ["one_hot", "multi_hot_sum", "multi_hot_mean"])
+def test_forward_prepared_int8(name):
+    w = _workload(name)
+    tabs = eb.EmbTables(w.rows, w.D, seed=5)
+    o = orc.Oracle(w.rows, w.D, seed=5, init_lo=-0.05, init_hi=0.05, accum_init=0.1)
+    offsets, ids = synth.gen_batch(w, 0)
+    d_off, d_ids = torch.from_numpy(offsets).to(DEV), torch.from_numpy(ids).to(DEV)
+    pool = eb.EMB_POOL_MEAN if w.pool_mean else eb.EMB_POOL_SUM
+    nb = w.B * w.T
+    ws, need = tabs.workspace(w.B, ids.size)
+    eb.check(eb.emb_bag_prepare(tabs.handle, d_off, d_ids, w.B, ids.size, pool, ws, need),
+             "prepare")
+    cg = Guarded((nb, w.D), torch.int8, DEV)
+    sg = Guarded((nb,), torch.float32, DEV)
+    eb.check(eb.emb_bag_forward_prepared_int8(tabs.handle, d_off, d_ids, w.B, ids.size, pool,
+                                              cg.t, sg.t, ws, need), "forward_prepared_int8")
+    # the same launch writing fp32 rows, quantized by the stand-alone kernel:
+    # the fused payload equals it bit for bit
+    out = torch.empty((w.B, w.T, w.D), dtype=torch.float32, device=DEV)
+    eb.check(eb.emb_bag_forward_prepared(tabs.handle, d_off, d_ids, w.B, ids.size, pool, out,
+                                         ws, need), "forward_prepared")
+    c2 = torch.empty((nb, w.D), dtype=torch.int8, device=DEV)
+    s2 = torch.empty(nb, dtype=torch.float32, device=DEV)
+    eb.check(eb.emb_quantize_rows_int8(out, nb, w.D, c2, s2), "quantize")
+    torch.cuda.synchronize()
+    cg.check("codes")
+    sg.check("scales")
+    codes, scales = cg.t.cpu().numpy(), sg.t.cpu().numpy()
+    np.testing.assert_array_equal(codes, c2.cpu().numpy())
+    np.testing.assert_array_equal(scales, s2.cpu().numpy())
+    assert eb.emb_status_sync(tabs.handle) == (eb.EMB_OK, 0)
+    # against the oracle: its pooled rows quantized by its own payload function
+    ref, _ = o.forward(offsets, ids, w.B, w.pool_mean)
+    rc, rs = orc.quantize_rows_int8(ref.reshape(nb, w.D))
+    if name == "one_hot":  # a one-hot row is a copy: exact
+        np.testing.assert_array_equal(codes, rc)
+        np.testing.assert_array_equal(scales, rs)
+        return
+    # multi-hot: the fp32 sum may differ from the rounded exact sum within the
+    # pooled tolerance, which can move a code by one and the scale slightly
+    S = forward_S(offsets, ids, w.B, o.rows, lambda g: o.read_rows(g)[0], w.pool_mean,
+                  w.D).reshape(nb, w.D)
+    tol = 1e-5 * S + 1e-6
+    assert np.all(np.abs(codes.astype(np.int32) - rc.astype(np.int32)) <= 1)
+    assert np.all(np.abs(scales - rs) <= tol.max(axis=1) / 127 + 2 ** -22 * rs)
+    deq = codes.astype(np.float64) * scales[:, None]
+    assert np.all(np.abs(deq - ref.reshape(nb, w.D)) <=
+                  0.5 * scales[:, None] * (1 + 1e-5) + tol + 2 ** -22 * np.abs(deq))
