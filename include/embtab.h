@@ -327,6 +327,18 @@ emb_status_t emb_bag_forward_prepared_int8(emb_table_t h, const int64_t* offsets
                                            const int64_t* ids, int64_t batch, int64_t nnz,
                                            emb_pool_t pool, int8_t* codes, float* scales,
                                            void* ws, size_t ws_bytes, void* stream);
+/* emb_bag_backward_adagrad_prepared with the upstream gradient given as the
+ * int8 exchange payload (what the table owner of a table-wise split receives):
+ * grad_codes [B*T, D] int8 and grad_scales [B*T] fp32, both 4-byte aligned;
+ * the gradient of bag b' is grad_codes[b', :] * grad_scales[b'] in fp32, so
+ * the result equals emb_bag_backward_adagrad_prepared on the output of
+ * emb_dequantize_rows_int8 bit for bit, reading a quarter of the bytes.
+ * Errors as emb_bag_backward_adagrad_prepared. */
+emb_status_t emb_bag_backward_adagrad_prepared_int8(emb_table_t h, int64_t batch, int64_t nnz,
+                                                    emb_pool_t pool, const int8_t* grad_codes,
+                                                    const float* grad_scales, float lr,
+                                                    float eps, void* ws, size_t ws_bytes,
+                                                    void* stream);
 emb_status_t emb_bag_backward_adagrad_prepared(emb_table_t h, int64_t batch, int64_t nnz,
                                                emb_pool_t pool, const float* grad_out, float lr,
                                                float eps, void* ws, size_t ws_bytes,

@@ -524,6 +524,31 @@ static emb_status_t backward_prepared(emb_table_t t, int64_t batch, int64_t nnz,
                                            lr, eps, w, static_cast<hipStream_t>(stream), dec));
 }
 
+emb_status_t emb_bag_backward_adagrad_prepared_int8(emb_table_t t, int64_t batch, int64_t nnz,
+                                                    emb_pool_t pool, const int8_t* grad_codes,
+                                                    const float* grad_scales, float lr,
+                                                    float eps, void* ws, size_t ws_bytes,
+                                                    void* stream) {
+  if (!t || !grad_codes || !grad_scales) return EMB_ERR_INVALID_ARG;
+  if (pool != EMB_POOL_SUM && pool != EMB_POOL_MEAN) return EMB_ERR_INVALID_ARG;
+  if (!std::isfinite(lr) || !std::isfinite(eps) || eps < 0.0f) return EMB_ERR_INVALID_ARG;
+  if (batch < 0 || nnz < 0) return EMB_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(grad_codes) & 3u) != 0 ||
+      (reinterpret_cast<uintptr_t>(grad_scales) & 3u) != 0)
+    return EMB_ERR_INVALID_ARG;
+  Plan p;
+  if (!make_plan(t->h, batch, nnz, &p)) return EMB_ERR_UNSUPPORTED;
+  if (!ws || ws_bytes < p.total || (reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
+    return EMB_ERR_WORKSPACE;
+  if (batch == 0) return EMB_OK;
+  uint32_t *keys = nullptr, *vals = nullptr;
+  char* w = static_cast<char*>(ws);
+  sorted_arrays(t->h, p, w, &keys, &vals);
+  return hip_status(launch_segment_adagrad_int8(t->h, p, keys, vals, pool == EMB_POOL_MEAN,
+                                                grad_codes, grad_scales, lr, eps, w,
+                                                static_cast<hipStream_t>(stream)));
+}
+
 emb_status_t emb_bag_forward_prepared_int8(emb_table_t t, const int64_t* offsets,
                                            const int64_t* ids, int64_t batch, int64_t nnz,
                                            emb_pool_t pool, int8_t* codes, float* scales,

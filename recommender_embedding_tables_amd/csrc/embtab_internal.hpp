@@ -342,6 +342,12 @@ hipError_t launch_segment_adagrad(const Handle& h, const Plan& p, const uint32_t
                                   const uint32_t* perm, bool mean, const float* grad_out,
                                   float lr, float eps, char* ws, hipStream_t s,
                                   const DecayArgs& dec = DecayArgs());
+// The same reduction with the gradient rows given as the int8 exchange payload
+// (codes [bags, D], one scale per row; plain Adagrad).
+hipError_t launch_segment_adagrad_int8(const Handle& h, const Plan& p, const uint32_t* keys,
+                                       const uint32_t* perm, bool mean, const int8_t* codes,
+                                       const float* scales, float lr, float eps, char* ws,
+                                       hipStream_t s);
 
 // Forward from a prepared workspace.  One-hot batches gather the rows in
 // sorted order; otherwise (a device flag of the prepare) the same launch runs

@@ -107,6 +107,32 @@ __device__ inline bool period_advances(uint32_t last, uint32_t period) {
   return last == kFreshPeriod || period > last;
 }
 
+// Where the gradient rows come from: fp32 rows of grad_out [bags, D], or the
+// int8 exchange payload as a table-wise split receives it (codes [bags, D]
+// and one scale per row; a value is code * scale in fp32, the dequantized
+// payload exactly).  Non-temporal loads for rows read once, cached loads for
+// rows read once per occurrence of their bag (REUSE).
+struct F32Grad {
+  const float* g;
+  template <bool REUSE>
+  __device__ __forceinline__ f4 load(uint32_t row, uint32_t D, uint32_t d4, bool ok) const {
+    return REUSE ? load4_or_zero(g, row, D, d4, ok) : load4_nt_or_zero(g, row, D, d4, ok);
+  }
+};
+struct I8Grad {
+  const uint32_t* codes;  // four codes per word
+  const float* scales;
+  template <bool REUSE>
+  __device__ __forceinline__ f4 load(uint32_t row, uint32_t D, uint32_t d4, bool ok) const {
+    const size_t off = ok ? (size_t)row * (D >> 2) + d4 : 0u;
+    const uint32_t w = REUSE ? codes[off] : __builtin_nontemporal_load(codes + off);
+    const float sc = scales[ok ? row : 0u];
+    const f4 x = {(float)(int8_t)(w & 0xFFu) * sc, (float)(int8_t)((w >> 8) & 0xFFu) * sc,
+                  (float)(int8_t)((w >> 16) & 0xFFu) * sc, (float)(int8_t)(w >> 24) * sc};
+    return ok ? x : f4{0.f, 0.f, 0.f, 0.f};
+  }
+};
+
 // A run that crosses chunk boundaries but neither enters the block from the
 // previous one nor leaves it into the next is finished inside the block: the
 // chunk where it ends keeps its own part sum and the row's W and G in
@@ -123,10 +149,10 @@ struct BlockRun {
 // Walks chunk c (one sub-group).  key_bb / key_ba: the keys just before and
 // just after the block.  A run continuing past the chunk and lying wholly in
 // the block leaves its part in part_lds and its row in *slot_key.
-template <int SG, int VEC, bool MEAN, int MPL, int UF, bool DECAY, bool REUSE>
+template <int SG, int VEC, bool MEAN, int MPL, int UF, bool DECAY, bool REUSE, class GRAD>
 __device__ __forceinline__ void seg_chunk(
     const uint32_t* __restrict__ keys, const uint32_t* __restrict__ sgr,
-    const float* __restrict__ sscale, const float* __restrict__ grad, float* __restrict__ W,
+    const float* __restrict__ sscale, GRAD grad, float* __restrict__ W,
     float* __restrict__ G, uint32_t n, uint32_t sentinel, int32_t D, float lr, float eps,
     uint32_t nbags, uint32_t* __restrict__ stamps, float log2_rho, uint32_t period, uint32_t c,
     uint32_t key_bb, uint32_t key_ba, f4* part_lds,
@@ -229,11 +255,8 @@ __device__ __forceinline__ void seg_chunk(
         for (int v = 0; v < VEC; ++v) {
           const uint32_t d4 = (uint32_t)(lane + v * SG);
           const bool own = mine && d4 < (uint32_t)D4;
-          // a gradient row read by one occurrence only is not kept in the
-          // caches; rows read once per occurrence of their bag (REUSE) are
-          g[u][v] = REUSE ? load4_or_zero(grad, gg[u], (uint32_t)D, d4, vld[u] && d4 < (uint32_t)D4)
-                          : load4_nt_or_zero(grad, gg[u], (uint32_t)D, d4,
-                                             vld[u] && d4 < (uint32_t)D4);
+          g[u][v] = grad.template load<REUSE>(gg[u], (uint32_t)D, d4,
+                                              vld[u] && d4 < (uint32_t)D4);
           wv[u][v] = load4_or_zero(W, kk[u], (uint32_t)D, d4, own);
           gv[u][v] = load4_nt_or_zero(G, kk[u], (uint32_t)D, d4, own);
         }
@@ -359,10 +382,10 @@ __device__ __forceinline__ void span_arrive(
   }
 }
 
-template <int SG, int VEC, bool MEAN, int MPL, int UF, bool DECAY, bool REUSE>
+template <int SG, int VEC, bool MEAN, int MPL, int UF, bool DECAY, bool REUSE, class GRAD>
 __global__ __launch_bounds__(256) void k_seg_adagrad(
     const uint32_t* __restrict__ keys, const uint32_t* __restrict__ sgr,
-    const float* __restrict__ sscale, const float* __restrict__ grad, float* __restrict__ W,
+    const float* __restrict__ sscale, GRAD grad, float* __restrict__ W,
     float* __restrict__ G, uint32_t n, uint32_t sentinel, int32_t D, float lr, float eps,
     float* __restrict__ part_head, float* __restrict__ part_tail,
     const uint32_t* __restrict__ span_u, const uint32_t* __restrict__ seg_off,
@@ -389,11 +412,10 @@ __global__ __launch_bounds__(256) void k_seg_adagrad(
   const uint32_t sp_out = b1 < n ? span_u[blk + 1] : kNoRow;
   BlockRun<VEC> fin;
   uint32_t slot_key = kNoRow, in_key = kNoRow, out_key = kNoRow;
-  seg_chunk<SG, VEC, MEAN, MPL, UF, DECAY, REUSE>(keys, sgr, sscale, grad, W, G, n, sentinel, D, lr, eps,
-                                           nbags, stamps, log2_rho, period, c, key_bb, key_ba,
-                                           s_part[sgb], &slot_key, s_in[sgb], &in_key,
-                                           s_out[sgb], &out_key, fin, perm,
-                                           !batch_not_one_hot(misc), B, T);
+  seg_chunk<SG, VEC, MEAN, MPL, UF, DECAY, REUSE, GRAD>(
+      keys, sgr, sscale, grad, W, G, n, sentinel, D, lr, eps, nbags, stamps, log2_rho, period, c,
+      key_bb, key_ba, s_part[sgb], &slot_key, s_in[sgb], &in_key, s_out[sgb], &out_key, fin, perm,
+      !batch_not_one_hot(misc), B, T);
   if (lane == 0) {
     s_key[sgb] = slot_key;
     s_in_key[sgb] = in_key;
@@ -457,9 +479,9 @@ __global__ __launch_bounds__(256) void k_seg_adagrad(
   }
 }
 
-template <int SG, int VEC, bool MEAN, bool DECAY, bool REUSE>
+template <int SG, int VEC, bool MEAN, bool DECAY, bool REUSE, class GRAD>
 hipError_t launch_t(const Handle& h, const Plan& p, const uint32_t* keys, const uint32_t* perm,
-                    const float* grad_out, float lr, float eps, char* ws, hipStream_t s,
+                    GRAD grad_out, float lr, float eps, char* ws, hipStream_t s,
                     const DecayArgs& dec) {
   constexpr int MPL = chunk_rounds<SG>();
   constexpr int UF = VEC > 1 ? 2 : (SG < kSegUF ? SG : kSegUF);
@@ -478,7 +500,8 @@ hipError_t launch_t(const Handle& h, const Plan& p, const uint32_t* keys, const 
   uint32_t* span_cnt = reinterpret_cast<uint32_t*>(ws + p.span_cnt);
   const uint32_t nbags = (uint32_t)(p.B * h.T);
   phase_mark(h, EMB_PHASE_REDUCE, false, s);
-  hipLaunchKernelGGL((k_seg_adagrad<SG, VEC, MEAN, MPL, UF, DECAY, REUSE>), dim3((unsigned)grid),
+  hipLaunchKernelGGL((k_seg_adagrad<SG, VEC, MEAN, MPL, UF, DECAY, REUSE, GRAD>),
+                     dim3((unsigned)grid),
                      dim3(256), 0, s, keys, gr, scale, grad_out, h.W, h.G, n,
                      (uint32_t)h.total_rows, h.D, lr, eps, ph, pt, span_u, seg_off, span_cnt,
                      nbags, dec.stamps, dec.log2_rho, dec.period, perm,
@@ -488,13 +511,13 @@ hipError_t launch_t(const Handle& h, const Plan& p, const uint32_t* keys, const 
   return hipGetLastError();
 }
 
-template <bool MEAN, bool DECAY, bool REUSE>
+template <bool MEAN, bool DECAY, bool REUSE, class GRAD>
 hipError_t dispatch(const Handle& h, const Plan& p, const uint32_t* keys, const uint32_t* perm,
-                    const float* grad_out, float lr, float eps, char* ws, hipStream_t s,
+                    GRAD grad_out, float lr, float eps, char* ws, hipStream_t s,
                     const DecayArgs& dec) {
   const int sg = subgroup_lanes(h.D), vec = vec_per_lane(h.D);
 #define EMBTAB_SEG_LAUNCH(SG_, VEC_) \
-  launch_t<SG_, VEC_, MEAN, DECAY, REUSE>(h, p, keys, perm, grad_out, lr, eps, ws, s, dec)
+  launch_t<SG_, VEC_, MEAN, DECAY, REUSE, GRAD>(h, p, keys, perm, grad_out, lr, eps, ws, s, dec)
   switch (sg) {
     case 1: return EMBTAB_SEG_LAUNCH(1, 1);
     case 2: return EMBTAB_SEG_LAUNCH(2, 1);
@@ -520,19 +543,33 @@ hipError_t launch_segment_adagrad(const Handle& h, const Plan& p, const uint32_t
                                   float lr, float eps, char* ws, hipStream_t s,
                                   const DecayArgs& dec) {
   if (!grad_out) return hipErrorInvalidValue;
+  const F32Grad g{grad_out};
   // Whether a bag's gradient row is read by more than one occurrence: a cache
   // policy only (both forms give the same result).  nnz == B * T means one id
   // per bag as a rule (the kernel checks one-hot batches exactly where it
   // matters); mean pooling is taken as multi-hot.
   const bool reuse = mean || p.nnz != p.B * (int64_t)h.T;
   if (dec.stamps) {
-    if (mean) return dispatch<true, true, true>(h, p, keys, perm, grad_out, lr, eps, ws, s, dec);
-    return reuse ? dispatch<false, true, true>(h, p, keys, perm, grad_out, lr, eps, ws, s, dec)
-                 : dispatch<false, true, false>(h, p, keys, perm, grad_out, lr, eps, ws, s, dec);
+    if (mean) return dispatch<true, true, true>(h, p, keys, perm, g, lr, eps, ws, s, dec);
+    return reuse ? dispatch<false, true, true>(h, p, keys, perm, g, lr, eps, ws, s, dec)
+                 : dispatch<false, true, false>(h, p, keys, perm, g, lr, eps, ws, s, dec);
   }
-  if (mean) return dispatch<true, false, true>(h, p, keys, perm, grad_out, lr, eps, ws, s, dec);
-  return reuse ? dispatch<false, false, true>(h, p, keys, perm, grad_out, lr, eps, ws, s, dec)
-               : dispatch<false, false, false>(h, p, keys, perm, grad_out, lr, eps, ws, s, dec);
+  if (mean) return dispatch<true, false, true>(h, p, keys, perm, g, lr, eps, ws, s, dec);
+  return reuse ? dispatch<false, false, true>(h, p, keys, perm, g, lr, eps, ws, s, dec)
+               : dispatch<false, false, false>(h, p, keys, perm, g, lr, eps, ws, s, dec);
+}
+
+hipError_t launch_segment_adagrad_int8(const Handle& h, const Plan& p, const uint32_t* keys,
+                                       const uint32_t* perm, bool mean, const int8_t* codes,
+                                       const float* scales, float lr, float eps, char* ws,
+                                       hipStream_t s) {
+  if (!codes || !scales) return hipErrorInvalidValue;
+  const I8Grad g{reinterpret_cast<const uint32_t*>(codes), scales};
+  const DecayArgs dec;
+  const bool reuse = mean || p.nnz != p.B * (int64_t)h.T;
+  if (mean) return dispatch<true, false, true>(h, p, keys, perm, g, lr, eps, ws, s, dec);
+  return reuse ? dispatch<false, false, true>(h, p, keys, perm, g, lr, eps, ws, s, dec)
+               : dispatch<false, false, false>(h, p, keys, perm, g, lr, eps, ws, s, dec);
 }
 
 }  // namespace embtab

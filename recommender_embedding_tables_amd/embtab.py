@@ -56,6 +56,7 @@ EXPORTED = [
     "emb_bag_prepare_ids", "emb_cache_prepare", "emb_stream_copy", "emb_stream_fill",
     "emb_stream_read_sink_floats", "emb_stream_read", "emb_quantize_rows_int8",
     "emb_dequantize_rows_int8", "emb_bag_forward_prepared_int8",
+    "emb_bag_backward_adagrad_prepared_int8",
 ]
 
 EMB_PHASE_FORWARD, EMB_PHASE_KEYS, EMB_PHASE_SORT, EMB_PHASE_UNIQUE = 0, 1, 2, 3
@@ -153,6 +154,8 @@ def _load():
         "emb_stream_read": (i32, [P, sz, P, sz, P]),
         "emb_quantize_rows_int8": (i32, [P, i64, i32, P, P, P]),
         "emb_bag_forward_prepared_int8": (i32, [P, P, P, i64, i64, i32, P, P, P, sz, P]),
+        "emb_bag_backward_adagrad_prepared_int8": (i32, [P, i64, i64, i32, P, P, f32, f32, P, sz,
+                                                         P]),
         "emb_dequantize_rows_int8": (i32, [P, P, i64, i32, P, P]),
     }
     for name, (res, args) in sig.items():
@@ -499,6 +502,13 @@ def emb_bag_forward_prepared_int8(handle, offsets, ids, batch, nnz, pool, codes,
     return _lib.emb_bag_forward_prepared_int8(handle, _ptr(offsets), _ptr(ids), batch, nnz,
                                               pool, _ptr(codes), _ptr(scales), _ptr(ws),
                                               ws_bytes, _stream(stream))
+
+
+def emb_bag_backward_adagrad_prepared_int8(handle, batch, nnz, pool, grad_codes, grad_scales, lr,
+                                           eps, ws, ws_bytes, stream=None) -> int:
+    return _lib.emb_bag_backward_adagrad_prepared_int8(handle, batch, nnz, pool,
+                                                       _ptr(grad_codes), _ptr(grad_scales), lr,
+                                                       eps, _ptr(ws), ws_bytes, _stream(stream))
 
 
 def emb_dequantize_rows_int8(codes, scales, rows, dim, y, stream=None) -> int:

@@ -134,3 +134,53 @@ def test_forward_prepared_int8(name):
     deq = codes.astype(np.float64) * scales[:, None]
     assert np.all(np.abs(deq - ref.reshape(nb, w.D)) <=
                   0.5 * scales[:, None] * (1 + 1e-5) + tol + 2 ** -22 * np.abs(deq))
+
+
+# ------------------------------------ backward reading the received payload
+
+from tests.helpers import StepBounds, abs_grad_sums  # noqa: E402
+
+
+@pytest.mark.parametrize("name", ["one_hot", "multi_hot_sum", "multi_hot_mean"])
+def test_backward_prepared_int8(name):
+    w = _workload(name)
+    a = eb.EmbTables(w.rows, w.D, seed=6)
+    b = eb.EmbTables(w.rows, w.D, seed=6)
+    o = orc.Oracle(w.rows, w.D, seed=6, init_lo=-0.05, init_hi=0.05, accum_init=0.1)
+    offsets, ids = synth.gen_batch(w, 1)
+    d_off, d_ids = torch.from_numpy(offsets).to(DEV), torch.from_numpy(ids).to(DEV)
+    pool = eb.EMB_POOL_MEAN if w.pool_mean else eb.EMB_POOL_SUM
+    nb = w.B * w.T
+    grad = np.random.default_rng(3).standard_normal((nb, w.D)).astype(np.float32)
+    codes, scales = orc.quantize_rows_int8(grad)
+    gdq = orc.dequantize_rows_int8(codes, scales).reshape(w.B, w.T, w.D)
+    lr, eps = 0.01, 1e-8
+    for tabs in (a, b):
+        ws, need = tabs.workspace(w.B, ids.size)
+        eb.check(eb.emb_bag_prepare(tabs.handle, d_off, d_ids, w.B, ids.size, pool, ws, need),
+                 "prepare")
+        if tabs is a:
+            cg = Guarded((nb, w.D), torch.int8, DEV)
+            sg = Guarded((nb,), torch.float32, DEV)
+            cg.t.copy_(torch.from_numpy(codes))
+            sg.t.copy_(torch.from_numpy(scales))
+            eb.check(eb.emb_bag_backward_adagrad_prepared_int8(
+                a.handle, w.B, ids.size, pool, cg.t, sg.t, lr, eps, ws, need), "backward_int8")
+        else:
+            eb.check(eb.emb_bag_backward_adagrad_prepared(
+                b.handle, w.B, ids.size, pool, torch.from_numpy(gdq).to(DEV), lr, eps, ws, need),
+                "backward")
+        torch.cuda.synchronize()
+    cg.check("grad codes")
+    sg.check("grad scales")
+    # the payload read in place of its dequantized rows: the same tables bit for bit
+    assert torch.equal(a.weights, b.weights) and torch.equal(a.accum, b.accum)
+    assert eb.emb_status_sync(a.handle) == (eb.EMB_OK, 0)
+    # and the oracle's step on the dequantized gradient, within the per-step rule
+    bounds = StepBounds(sum(w.rows), w.D)
+    uniq, gsum = abs_grad_sums(offsets, ids, w.B, o.rows, gdq, w.pool_mean, w.D)
+    assert bounds.step(o, uniq, gsum, lr, eps, lambda: o.backward_adagrad(
+        offsets, ids, w.B, w.pool_mean, gdq, lr, eps)) == 0
+    Wr, Gr = o.read_rows(uniq)
+    bounds.check(a.weights[torch.from_numpy(uniq).to(DEV)].cpu().numpy(),
+                 a.accum[torch.from_numpy(uniq).to(DEV)].cpu().numpy(), Wr, Gr, uniq, "rows")
