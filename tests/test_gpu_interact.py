@@ -3,8 +3,9 @@ backward, on the GPU against the oracle through the C ABI.  Cases cover one
 and two 16-row Gram blocks (T + 1 <= 16 and > 16), the largest shapes
 (T = 31, D = 256), widths whose float4 count is not a power of two (D = 48,
 112), mean pooling of multi-hot bags, empty bags, absent and
-out-of-range ids, and a training step whose embedding gradient comes from the
-interaction backward."""
+out-of-range ids, ten seeded random shapes (T from 1 to 31, D a multiple of
+16 up to 256, batches from 1 sample), and a training step whose embedding
+gradient comes from the interaction backward."""
 import numpy as np
 import pytest
 import torch
@@ -44,6 +45,14 @@ def case(name):
     if name == "one_hot_26_d112":  # D / 4 = 28, 12 items per lane, two row blocks
         return synth.workload(2, T=26, B=700, D=112,
                               rows=synth.log_uniform_rows(26, 2.0, 4.0, 3, 2)), False
+    if name.startswith("rand"):  # seeded random shape within the supported range
+        rng = np.random.default_rng(700 + int(name[4:]))
+        T = int(rng.integers(1, 32))
+        D = 16 * int(rng.integers(1, 17))
+        B = int(rng.choice([1, 2, 63, 65, int(rng.integers(100, 1500))]))
+        w = synth.workload(3, T=T, B=B, D=D)
+        w.rows = rng.integers(1, 5_000, size=T).astype(np.int64)
+        return w, bool(rng.integers(0, 2))
     w = synth.workload(3, T=5, B=700, D=16)  # ragged bags, some empty
     w.rows = np.array([40, 900, 7, 300, 60], np.int64)
     return w, False
@@ -55,6 +64,16 @@ def batch_of(w, name):
         ids = ids.copy()
         ids[::7] = eb.EMB_ID_ABSENT
         return offsets, ids
+    if name.startswith("rand"):  # even: one id per bag; odd: ragged bags, some empty
+        k = int(name[4:])
+        if k % 2 == 0:
+            rng = np.random.default_rng(800 + k)
+            offsets = np.arange(w.T * w.B + 1, dtype=np.int64)
+            ids = np.concatenate([rng.integers(0, r, size=w.B) for r in w.rows]).astype(np.int64)
+            return offsets, ids
+        offsets, ids, _ = synth.random_small(900 + k, w.T, w.D, w.B, w.rows, max_len=5,
+                                             empty_frac=0.15)
+        return offsets, ids
     return synth.gen_batch(w, 1)
 
 
@@ -65,7 +84,8 @@ def z_abs(o, w, offsets, ids, dense, mean):
 
 
 @pytest.mark.parametrize("name", ["one_hot_26", "multi_hot_mean_8", "max_31x256",
-                                  "small_ragged", "multi_hot_d48", "one_hot_26_d112"])
+                                  "small_ragged", "multi_hot_d48", "one_hot_26_d112"]
+                         + [f"rand{k}" for k in range(10)])
 def test_interaction_matches_oracle(name):
     w, mean = case(name)
     pool = eb.EMB_POOL_MEAN if mean else eb.EMB_POOL_SUM
