@@ -4,6 +4,10 @@ prepare, the prepared forward (its one-hot and pooled branches), the forward
 that writes the int8 payload, the prepared backward with Adagrad, the one
 that reads the int8 gradient payload, and the forward without a workspace.
 
+The hashed sweep runs three calls per configuration: find-or-insert (ids
+and the key-to-row map bit for bit), then the prepared step on the ids, with
+the per-step rule carried over the steps.
+
 Each configuration draws the table count, the row width (one lane per row up
 to several float4 per lane, widths whose float4 count is not a power of two),
 the batch size, the bag shape (one id per bag; as many ids as bags without
@@ -17,7 +21,7 @@ import torch
 
 from oracle import oracle as orc
 from recommender_embedding_tables_amd import synth
-from tests.helpers import Guarded, abs_grad_sums, assert_within, forward_S
+from tests.helpers import REL, Guarded, StepBounds, abs_grad_sums, assert_within, forward_S
 
 pytestmark = pytest.mark.gpu
 
@@ -161,3 +165,97 @@ def test_prepared_path_random_config(seed):
     for tabs in (a, b):
         assert eb.emb_status_sync(tabs.handle) == want
         assert eb.emb_status_sync(tabs.handle) == (eb.EMB_OK, 0)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_hashed_prepared_path_random_config(seed):
+    rng = np.random.default_rng(6000 + seed)
+    T = int(rng.integers(1, 5))
+    D = [4, 12, 36, 64, 100, 128, 260, 516][seed]
+    cap = 1 << int(rng.integers(10, 15))
+    rows = np.full(T, int(0.625 * cap), np.int64)
+    B = int(rng.choice([1, 5, 200, int(rng.integers(500, 3000))]))
+    mean = bool(rng.integers(0, 2))
+    kind = ["one_hot", "poisson", "as_many_as_bags"][seed % 3]
+    # each table's keys come from a universe no larger than its rows: no call is full
+    univ = [rng.integers(1, 2 ** 63, size=int(rng.integers(1, rows[0] + 1)), dtype=np.uint64)
+            for _ in range(T)]
+    print(f"seed {seed}: T={T} D={D} cap={cap} B={B} {kind} mean={mean} "
+          f"universe={[u.size for u in univ]}", flush=True)
+    pool = eb.EMB_POOL_MEAN if mean else eb.EMB_POOL_SUM
+    kw = dict(seed=seed, init_lo=-0.05, init_hi=0.05, init_std=0.01, accum_init=0.1)
+    tabs = eb.EmbTables(rows, D, hashed=True, hash_capacity=cap, max_load=0.625, **kw)
+    o = orc.Oracle(rows, D, hashed=True, **kw)
+    bounds = StepBounds(int(rows.sum()), D)
+    row_off = np.concatenate([[0], np.cumsum(rows)])
+    live = lambda: np.concatenate([np.arange(o.n_live(t)) + row_off[t]  # noqa: E731
+                                   for t in range(T)])
+    live_before = live()
+    for call in range(3):
+        if kind == "one_hot":
+            lens = np.ones(T * B, np.int64)
+        elif kind == "as_many_as_bags":
+            lens = np.ones(T * B, np.int64)
+            k = np.arange(call % 2, T * B - 1, 4)
+            lens[k], lens[k + 1] = 2, 0
+        else:
+            lens = rng.poisson(3.0, size=T * B).astype(np.int64)
+        offsets = synth.offsets_from_lengths(lens)
+        nnz = int(offsets[-1])
+        keys = np.empty(nnz, np.uint64)
+        for t in range(T):
+            a, b = int(offsets[t * B]), int(offsets[(t + 1) * B])
+            keys[a:b] = univ[t][synth.zipf_ranks(rng, univ[t].size, 1.1, b - a)]
+        d_off = _t(offsets)
+        need = eb.emb_workspace_bytes(tabs.handle, B, nnz)
+        ws = Guarded(None, torch.uint8, DEV, nbytes=need)
+        idg = Guarded((nnz,), torch.int64, DEV)
+        eb.check(eb.emb_hash_find_or_insert(tabs.handle, d_off, _t(keys.view(np.int64)), B, nnz,
+                                            idg.t, ws.t, need), "find_or_insert")
+        torch.cuda.synchronize()
+        ref_ids, fl = o.find_or_insert(offsets, keys, B)
+        assert fl == 0
+        np.testing.assert_array_equal(idg.t.cpu().numpy(), ref_ids)
+        live_now = live()
+        bounds.assigned(o, np.setdiff1d(live_now, live_before))
+        live_before = live_now
+
+        grad = rng.standard_normal((B, T, D)).astype(np.float32)
+        out = Guarded((B, T, D), torch.float32, DEV)
+        eb.check(eb.emb_bag_prepare(tabs.handle, d_off, idg.t, B, nnz, pool, ws.t, need),
+                 "prepare")
+        eb.check(eb.emb_bag_forward_prepared(tabs.handle, d_off, idg.t, B, nnz, pool, out.t,
+                                             ws.t, need), "forward_prepared")
+        torch.cuda.synchronize()
+        got = out.t.cpu().numpy()
+        eb.check(eb.emb_bag_backward_adagrad_prepared(tabs.handle, B, nnz, pool, _t(grad), LR,
+                                                      EPS, ws.t, need), "backward_prepared")
+        torch.cuda.synchronize()
+        for g, what in ((ws, "workspace"), (idg, "ids"), (out, "forward output")):
+            g.check(f"{what}, call {call}")
+
+        ref, _ = o.forward(offsets, ref_ids, B, mean)
+        S = forward_S(offsets, ref_ids, B, o.rows, lambda r: np.abs(o.read_rows(r)[0]), mean, D)
+        S = S + forward_S(offsets, ref_ids, B, o.rows, bounds.weight_bound, mean, D) / REL
+        assert_within(got, ref, S, f"forward, call {call}")
+        uniq, gsum = abs_grad_sums(offsets, ref_ids, B, o.rows, grad, mean, D)
+        assert bounds.step(o, uniq, gsum, LR, EPS, lambda: o.backward_adagrad(
+            offsets, ref_ids, B, mean, grad, LR, EPS)) == 0
+        if uniq.size:
+            Wr, Gr = o.read_rows(uniq)
+            bounds.check(tabs.weights[_t(uniq)].cpu().numpy(), tabs.accum[_t(uniq)].cpu().numpy(),
+                         Wr, Gr, uniq, f"rows, call {call}")
+    # the key -> row map, bit for bit
+    st, n_live = eb.emb_hash_n_live(tabs.handle, T)
+    assert st == eb.EMB_OK
+    for t in range(T):
+        assert n_live[t] == o.n_live(t)
+        kor = torch.empty(int(rows[t]), dtype=torch.int64, device=DEV)
+        eb.check(eb.emb_hash_export(tabs.handle, t, kor), "export")
+        k_t, r_t = o.export(t)
+        want = np.empty(n_live[t], np.uint64)
+        want[r_t] = k_t
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(kor[:n_live[t]].cpu().numpy().view(np.uint64), want)
+    assert eb.emb_status_sync(tabs.handle) == (eb.EMB_OK, 0)
+    tabs.close()
