@@ -5,14 +5,15 @@ workspaces).  Depth 3: find-or-insert of batch i+3, the prepare of batch i+2
 on one of two streams (alternating), forward and backward of batch i (four
 workspaces).  New rows handed out by the later hash calls are never rows of
 the batch being trained, so every result equals the sequential one: ids bit
-for bit, pooled outputs and rows within the fp32 bound."""
+for bit, pooled outputs and rows within the per-step rule carried over the
+steps."""
 import numpy as np
 import pytest
 import torch
 
 from oracle import oracle as orc
 from recommender_embedding_tables_amd import synth
-from tests.helpers import assert_within, forward_S
+from tests.helpers import REL, StepBounds, abs_grad_sums, assert_within, forward_S
 
 pytestmark = pytest.mark.gpu
 
@@ -94,21 +95,32 @@ def test_hashed_pipelined_schedule(depth):
         trained[i].record(main)
     torch.cuda.synchronize()
 
+    # the oracle replays the calls in order, carrying the per-step rule
+    bounds = StepBounds(int(np.sum(w.rows)), w.D)
+    row_off = np.concatenate([[0], np.cumsum(w.rows)])
+    live = lambda: np.concatenate([np.arange(o.n_live(t)) + row_off[t]  # noqa: E731
+                                   for t in range(w.T)])
+    live_before = live()
     for i in range(steps):
         offsets, keys = host[i]
         ref_ids, fl = o.find_or_insert(offsets, keys, w.B)
         assert fl == 0
         np.testing.assert_array_equal(dev[i][2].cpu().numpy(), ref_ids)
+        live_now = live()
+        bounds.assigned(o, np.setdiff1d(live_now, live_before))  # fresh rows of new keys
+        live_before = live_now
         ref_out, _ = o.forward(offsets, ref_ids, w.B, False)
-        S = forward_S(offsets, ref_ids, w.B, o.rows, lambda r: o.read_rows(r)[0], False, w.D)
+        S = forward_S(offsets, ref_ids, w.B, o.rows, lambda r: np.abs(o.read_rows(r)[0]), False,
+                      w.D)
+        S = S + forward_S(offsets, ref_ids, w.B, o.rows, bounds.weight_bound, False, w.D) / REL
         assert_within(outs[i].cpu().numpy(), ref_out, S, f"pooled output of step {i}")
-        o.backward_adagrad(offsets, ref_ids, w.B, False, grads[i], w.lr, w.eps)
+        uniq, gsum = abs_grad_sums(offsets, ref_ids, w.B, o.rows, grads[i], False, w.D)
+        assert bounds.step(o, uniq, gsum, w.lr, w.eps, lambda: o.backward_adagrad(
+            offsets, ref_ids, w.B, False, grads[i], w.lr, w.eps)) == 0
     rows = o.touched_rows()
-    Wg = tabs.weights[_t(rows)].cpu().numpy()
-    Gg = tabs.accum[_t(rows)].cpu().numpy()
     Wr, Gr = o.read_rows(rows)
-    assert_within(Gg, Gr, np.abs(Gr).astype(np.float64) * steps, "accumulator")
-    assert_within(Wg, Wr, np.abs(Wr) + steps * w.lr, "weights")
+    bounds.check(tabs.weights[_t(rows)].cpu().numpy(), tabs.accum[_t(rows)].cpu().numpy(),
+                 Wr, Gr, rows, "rows after the steps")
     st, n_live = eb.emb_hash_n_live(tabs.handle, w.T)
     assert st == eb.EMB_OK and list(n_live) == [o.n_live(t) for t in range(w.T)]
     assert eb.emb_status_sync(tabs.handle) == (eb.EMB_OK, 0)

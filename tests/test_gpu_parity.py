@@ -10,7 +10,7 @@ import torch
 
 from oracle import oracle as orc
 from recommender_embedding_tables_amd import synth
-from tests.helpers import (Guarded, StepBounds, abs_grad_sums, assert_within, forward_S,
+from tests.helpers import (REL, Guarded, StepBounds, abs_grad_sums, assert_within, forward_S,
                            occurrence_rows)
 
 pytestmark = pytest.mark.gpu
@@ -510,7 +510,7 @@ def _export(tabs, t):
     return k.cpu().numpy().view(np.uint64)
 
 
-def check_hash_state(tabs, o, trained_lr=0.0):
+def check_hash_state(tabs, o, bounds=None):
     st, n_live = eb.emb_hash_n_live(tabs.handle, tabs.T)
     assert st == eb.EMB_OK
     for t in range(tabs.T):
@@ -520,15 +520,19 @@ def check_hash_state(tabs, o, trained_lr=0.0):
         ref = np.full(n_live[t], np.uint64(eb.EMB_EMPTY_KEY))  # rows freed by eviction: no key
         ref[rows] = keys
         np.testing.assert_array_equal(kor, ref)  # key <-> row bijection, bit-exact
-    # rows handed out so far: initial values and later updates match the oracle
+    # rows handed out so far: initial values (within the rule for a fresh row)
+    # or, given the bounds carried over training steps, within those
     live = np.concatenate([np.arange(n) + int(np.sum(tabs.rows[:t]))
                            for t, n in enumerate(n_live)]) if sum(n_live) else np.zeros(0, int)
     if live.size:
         Wg = tabs.weights[_t(live)].cpu().numpy()
+        Gg = tabs.accum[_t(live)].cpu().numpy()
         Wr, Gr = o.read_rows(live)
-        assert_within(Wg, Wr, np.abs(Wr) + trained_lr, "hashed rows")
-        if trained_lr == 0.0:
-            np.testing.assert_array_equal(tabs.accum[_t(live)].cpu().numpy(), Gr)
+        if bounds is None:
+            assert_within(Wg, Wr, np.abs(Wr), "hashed rows")
+            np.testing.assert_array_equal(Gg, Gr)
+        else:
+            bounds.check(Wg, Gg, Wr, Gr, live, "hashed rows")
 
 
 def test_hash_matches_oracle_over_calls():
@@ -600,18 +604,34 @@ def test_hash_then_train_step():
     w = synth.workload(5, T=2, B=2000, universe=20_000, hash_capacity=1 << 15)
     w.rows = np.full(2, int(0.625 * (1 << 15)), np.int64)
     tabs, o = make_pair(w.rows, w.D, seed=8, hashed=True, cap=w.hash_capacity)
+    bounds = StepBounds(int(np.sum(w.rows)), w.D)
+    row_off = np.concatenate([[0], np.cumsum(w.rows)])
+    live = lambda: np.concatenate([np.arange(o.n_live(t)) + row_off[t]  # noqa: E731
+                                   for t in range(w.T)])
+    live_before = live()
     for step in range(2):
         offsets, ranks = synth.gen_batch(w, step)
         keys = synth.gen_keys(w, offsets, ranks)
         ids = _hash_call(tabs, offsets, keys, w.B)
         ref, _ = o.find_or_insert(offsets, keys, w.B)
         np.testing.assert_array_equal(ids, ref)
-        out, _ = check_forward(tabs, o, offsets, ids, w.B, False)
+        live_now = live()
+        bounds.assigned(o, np.setdiff1d(live_now, live_before))  # fresh rows of new keys
+        live_before = live_now
+        out = gpu_forward(tabs, offsets, ids, w.B, False).cpu().numpy()
+        ref_out, _ = o.forward(offsets, ids, w.B, False)
+        S = forward_S(offsets, ids, w.B, o.rows, lambda r: np.abs(o.read_rows(r)[0]), False, w.D)
+        S = S + forward_S(offsets, ids, w.B, o.rows, bounds.weight_bound, False, w.D) / REL
+        assert_within(out, ref_out, S, f"forward, step {step}")
         grad = synth.gen_grad(w, step)
         gpu_backward(tabs, offsets, ids, w.B, False, grad, w.lr, w.eps)
-        o.backward_adagrad(offsets, ids, w.B, False, grad, w.lr, w.eps)
-        check_rows(tabs, o, offsets, ids, w.B, False, grad, w.lr, w.eps)
-    check_hash_state(tabs, o, trained_lr=2 * w.lr)
+        uniq, gsum = abs_grad_sums(offsets, ids, w.B, o.rows, grad, False, w.D)
+        assert bounds.step(o, uniq, gsum, w.lr, w.eps, lambda: o.backward_adagrad(
+            offsets, ids, w.B, False, grad, w.lr, w.eps)) == 0
+        Wr, Gr = o.read_rows(uniq)
+        bounds.check(tabs.weights[_t(uniq)].cpu().numpy(), tabs.accum[_t(uniq)].cpu().numpy(),
+                     Wr, Gr, uniq, f"rows, step {step}")
+    check_hash_state(tabs, o, bounds)
 
 
 def test_prepared_backward_on_side_stream_matches_oracle():
@@ -622,6 +642,7 @@ def test_prepared_backward_on_side_stream_matches_oracle():
     main = torch.cuda.current_stream()
     side = torch.cuda.Stream()
     ev_a, ev_b = torch.cuda.Event(), torch.cuda.Event()
+    bounds = StepBounds(int(np.sum(w.rows)), w.D)
     for step in range(2):
         offsets, ids = synth.gen_batch(w, step)
         grad = synth.gen_grad(w, step)
@@ -641,10 +662,15 @@ def test_prepared_backward_on_side_stream_matches_oracle():
                  "prepared backward")
         torch.cuda.synchronize()
         ref, _ = o.forward(offsets, ids, w.B, True)
-        S = forward_S(offsets, ids, w.B, o.rows, lambda r: o.read_rows(r)[0], True, w.D)
+        S = forward_S(offsets, ids, w.B, o.rows, lambda r: np.abs(o.read_rows(r)[0]), True, w.D)
+        S = S + forward_S(offsets, ids, w.B, o.rows, bounds.weight_bound, True, w.D) / REL
         assert_within(out.cpu().numpy(), ref, S, "forward (side-stream step)")
-        o.backward_adagrad(offsets, ids, w.B, True, grad, w.lr, w.eps)
-        check_rows(tabs, o, offsets, ids, w.B, True, grad, w.lr, w.eps)
+        uniq, gsum = abs_grad_sums(offsets, ids, w.B, o.rows, grad, True, w.D)
+        assert bounds.step(o, uniq, gsum, w.lr, w.eps, lambda: o.backward_adagrad(
+            offsets, ids, w.B, True, grad, w.lr, w.eps)) == 0
+        Wr, Gr = o.read_rows(uniq)
+        bounds.check(tabs.weights[_t(uniq)].cpu().numpy(), tabs.accum[_t(uniq)].cpu().numpy(),
+                     Wr, Gr, uniq, f"rows, step {step}")
     assert status(tabs) == (eb.EMB_OK, 0)
 
 
@@ -725,19 +751,18 @@ def test_prepared_backward_twice_on_one_prepare():
     eb.check(eb.emb_bag_prepare(tabs.handle, _t(offsets), _t(ids), w.B, ids.size, pool, ws, need),
              "prepare")
     grads = [synth.gen_grad(w, step) for step in range(2)]
+    bounds = StepBounds(int(np.sum(w.rows)), w.D)
     for grad in grads:
         eb.check(eb.emb_bag_backward_adagrad_prepared(tabs.handle, w.B, ids.size, pool, _t(grad),
                                                       w.lr, w.eps, ws, need), "backward_prepared")
-        o.backward_adagrad(offsets, ids, w.B, True, grad, w.lr, w.eps)
+        uniq, gsum = abs_grad_sums(offsets, ids, w.B, o.rows, grad, True, w.D)
+        assert bounds.step(o, uniq, gsum, w.lr, w.eps, lambda: o.backward_adagrad(
+            offsets, ids, w.B, True, grad, w.lr, w.eps)) == 0
     torch.cuda.synchronize()
-    # bound of two steps: the per-step terms of both steps added
-    uniq, g0 = abs_grad_sums(offsets, ids, w.B, o.rows, grads[0], True, w.D)
-    _, g1 = abs_grad_sums(offsets, ids, w.B, o.rows, grads[1], True, w.D)
+    # the two steps within the per-step rule carried over them
     Wr, Gr = o.read_rows(uniq)
-    Gr64 = Gr.astype(np.float64)
-    assert_within(tabs.accum[_t(uniq)].cpu().numpy(), Gr, Gr64 + g0 ** 2 + g1 ** 2, "accumulator")
-    assert_within(tabs.weights[_t(uniq)].cpu().numpy(), Wr,
-                  np.abs(Wr) + 2 * w.lr + w.lr * (g0 + g1) / np.sqrt(Gr64), "weights")
+    bounds.check(tabs.weights[_t(uniq)].cpu().numpy(), tabs.accum[_t(uniq)].cpu().numpy(),
+                 Wr, Gr, uniq, "two steps")
     untouched = np.setdiff1d(np.arange(int(w.rows.sum())), uniq)
     Wu, Gu = o.read_rows(untouched)
     np.testing.assert_array_equal(tabs.weights[_t(untouched)].cpu().numpy(), Wu)
