@@ -120,3 +120,28 @@ def test_shard_option_is_refused_where_it_does_not_apply():
 def test_int8_exchange_needs_the_pooled_output():
     r = _run("--interact", "--schedule", "prepared", "--int8-exchange")
     assert r.returncode == 2 and "--int8-exchange" in r.stderr
+
+
+def test_stored_traffic_is_dropped_once_the_kernel_sources_change(tmp_path, monkeypatch):
+    # The committed counter summaries count only for the kernel sources they
+    # were taken from: a copy of the reduction's summary with another source
+    # hash gives no traffic, and then no step ratio for the gate either.
+    bench = _bench_module()
+    assert bench.stored_traffic("reduce_adagrad", 3) is None  # the 26-table workload only
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    src = open(os.path.join(ROOT, "profiles", "reduce_adagrad_26tables_traffic.txt")).read()
+    lines = [("source_sha256: " + "0" * 64) if ln.startswith("source_sha256:") else ln
+             for ln in src.splitlines()]
+    (prof / "reduce_adagrad_26tables_traffic.txt").write_text("\n".join(lines) + "\n")
+    (prof / "step_26tables_traffic.txt").write_text("measured_over_algorithmic: 1.0\n")
+    for f in [ln.split(":", 1)[1].split() for ln in lines if ln.startswith("source_files:")][0]:
+        (tmp_path / f).parent.mkdir(parents=True, exist_ok=True)
+        (tmp_path / f).write_bytes(open(os.path.join(ROOT, f), "rb").read())
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.stored_traffic("reduce_adagrad", 2) is None
+    assert bench.stored_step_traffic_ratio() is None
+    # with the matching hash the same copy gives the stored figures
+    (prof / "reduce_adagrad_26tables_traffic.txt").write_text(src)
+    assert bench.stored_traffic("reduce_adagrad", 2) > 0
+    assert bench.stored_step_traffic_ratio() == 1.0
