@@ -330,8 +330,9 @@ __global__ __launch_bounds__(256, 2) void k_interact_fwd(
     wave_sync();
     for (int p = lane; p < P; p += 64) out[s * ostride + D + p] = l.pairs[p];
   };
-  // up to 16 items per lane stay in registers; more would spill
-  pipelined_samples<MEAN, NQ, (NQ <= 16)>(l, (int64_t)blockIdx.x * wpb + w,
+  // up to 16 items per lane stay in registers (sum pooling; with mean pooling
+  // the bag-length scale leaves too few registers, and 16 held items spill)
+  pipelined_samples<MEAN, NQ, (NQ <= 16 && !MEAN)>(l, (int64_t)blockIdx.x * wpb + w,
                                     (int64_t)gridDim.x * wpb, dense, offsets, ids, row_off, rows,
                                     W, B, T, D, nnz, bad, [](int64_t) {}, consume, []() {});
   const uint32_t any = (uint32_t)(__ballot(bad != 0) != 0);
