@@ -43,6 +43,11 @@ constexpr int kZRows = 32;  // T + 1 <= 32
 // pair staging (forward) and the row of every table's current occurrence.
 constexpr int kGStride = 36;
 __host__ __device__ inline int z_stride(int D) { return D + 4; }
+// Rows wider than 128 floats (a multiple of 32) go through the pipeline in two
+// column halves: both kernels are separable over columns (the Gram matrix is a
+// sum over them, dZ = G Z column by column), and a half keeps the registers
+// and LDS of a 128-float row.  Z then holds one half.
+__host__ __device__ inline int col_blocks(int D) { return D > 128 && D % 32 == 0 ? 2 : 1; }
 __host__ __device__ inline size_t wave_lds_floats(int T, int D, bool bwd) {
   return (size_t)(T + 1) * z_stride(D) + (bwd ? 32 * kGStride : 512) + 32;
 }
@@ -81,10 +86,13 @@ __device__ inline void wave_sync() {
 //   its NQ items (table, float4 column) of that row.  Position 0 of the next
 //   sample is resolved during this one; later positions of multi-hot bags are
 //   walked in place.  Bags whose offsets lie outside [0, nnz] or decrease
-//   count as empty and flag.  consume(sp) reads Z rows 0..T of sample sp;
+//   count as empty and flag.  Rows of more than 128 floats go round in two
+//   column halves (the bag bounds, ids and rows resolved once per sample);
+//   consume(sp, hp) reads Z rows 0..T of half hp of sample sp;
 //   issue(s) may start the consumer's own loads for sample s (it is consumed
-//   one iteration later), and rotate() moves them to the consumer's side.
-template <bool MEAN, int NQ, bool HOLD_ITEMS, class Issue, class Consume, class Rotate>
+//   in the next one or two iterations), and rotate() moves them to the
+//   consumer's side after the sample's first half.
+template <bool MEAN, int NQ, int NH, bool HOLD_ITEMS, class Issue, class Consume, class Rotate>
 __device__ void pipelined_samples(const WaveLds& l, int64_t first, int64_t stride,
                                   const float* __restrict__ dense,
                                   const int64_t* __restrict__ offsets,
@@ -95,8 +103,9 @@ __device__ void pipelined_samples(const WaveLds& l, int64_t first, int64_t strid
                                   int64_t nnz, uint32_t& bad, Issue issue, Consume consume,
                                   Rotate rotate) {
   const int lane = threadIdx.x & 63;
-  const int D4 = D >> 2;
-  const int zs = z_stride(D);
+  const int Dh = D / NH;  // the columns of one half (NH = col_blocks(D))
+  const int D4 = Dh >> 2;
+  const int zs = z_stride(Dh);
   // rows, global row offsets and valid offsets all fit 32 bits (the calls
   // reject nnz >= 2^32 - 16; global rows are 32-bit)
   const uint32_t nrows = lane < T ? (uint32_t)rows[lane] : 0u;
@@ -172,12 +181,12 @@ __device__ void pipelined_samples(const WaveLds& l, int64_t first, int64_t strid
     }
     return (uint32_t)__builtin_amdgcn_readfirstlane(v);
   };
-  auto load_item = [&](int ln, int q) -> f4v {
+  auto load_item = [&](int ln, int q, int hcol) -> f4v {
     int t, c;
     const bool in = item_of(ln, q, t, c);
     const uint32_t r = in ? l.row[t] : kNoRow;
     const bool ok = r != kNoRow;
-    const f4v v = *reinterpret_cast<const f4v*>(W + (ok ? (size_t)r * D + 4 * c : 0));
+    const f4v v = *reinterpret_cast<const f4v*>(W + (ok ? (size_t)r * D + hcol + 4 * c : 0));
     return ok ? v : f4v{0.f, 0.f, 0.f, 0.f};
   };
 
@@ -189,79 +198,90 @@ __device__ void pipelined_samples(const WaveLds& l, int64_t first, int64_t strid
   if (lane < T) l.row[lane] = resolve(o0, len, 0);
   wave_sync();
   int64_t sp = -1;
+  int hp = 0;
   while (s < B) {
     const int64_t sn = s + stride;
-    // in flight during this sample: the bag bounds of the sample after the
-    // next one, and the first id of every bag of the next one
-    uint32_t o0nn, lennn;
-    bag_of(sn + stride, o0nn, lennn);
-    const int64_t idn = id_at(o0n, lenn, 0);
-    f4v dv[(256 / 4 + 63) / 64];
-#pragma unroll
-    for (int q = 0; q < (256 / 4 + 63) / 64; ++q) {
-      const int c = lane + 64 * q;
-      dv[q] = c < D4 ? *reinterpret_cast<const f4v*>(dense + (size_t)s * D + 4 * c)
-                     : f4v{0.f, 0.f, 0.f, 0.f};
-    }
-    f4v acc[NQ];
-    {
-      const int ln = opaque_lane();
-#pragma unroll
-      for (int q = 0; q < NQ; ++q) acc[q] = load_item(ln, q);  // position 0 of sample s
-    }
-    issue(s);
-    if (sp >= 0) consume(sp);  // the previous sample, from LDS
-    wave_sync();
-    for (uint32_t j = 1; j < maxlen; ++j) {  // later positions of multi-hot bags
-      if (lane < T) l.row[lane] = resolve(o0, len, j);
+    // in flight during this sample's first half: the bag bounds of the sample
+    // after the next one, and the first id of every bag of the next one
+    uint32_t o0nn = 0u, lennn = 0u;
+    int64_t idn = kAbsentId;
+    for (int h = 0; h < NH; ++h) {
+      const int hcol = h * Dh;
+      if (h == 0) {
+        bag_of(sn + stride, o0nn, lennn);
+        idn = id_at(o0n, lenn, 0);
+      }
+      f4v dv[(256 / 4 + 63) / 64];
+  #pragma unroll
+      for (int q = 0; q < (256 / 4 + 63) / 64; ++q) {
+        const int c = lane + 64 * q;
+        dv[q] = c < D4 ? *reinterpret_cast<const f4v*>(dense + (size_t)s * D + hcol + 4 * c)
+                       : f4v{0.f, 0.f, 0.f, 0.f};
+      }
+      f4v acc[NQ];
+      {
+        const int ln = opaque_lane();
+  #pragma unroll
+        for (int q = 0; q < NQ; ++q) acc[q] = load_item(ln, q, hcol);  // position 0 of sample s
+      }
+      if (h == 0) issue(s);
+      if (sp >= 0) consume(sp, hp);  // the previous half or sample, from LDS
       wave_sync();
-      const int ln = opaque_lane();
-#pragma unroll
-      for (int q0 = 0; q0 < NQ; q0 += 4) {  // four loads in flight: few registers
-        f4v x[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) x[q] = load_item(ln, q0 + q);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) acc[q0 + q] += x[q];
+      for (uint32_t j = 1; j < maxlen; ++j) {  // later positions of multi-hot bags
+        if (lane < T) l.row[lane] = resolve(o0, len, j);
+        wave_sync();
+        const int ln = opaque_lane();
+  #pragma unroll
+        for (int q0 = 0; q0 < NQ; q0 += 4) {  // four loads in flight: few registers
+          f4v x[4];
+  #pragma unroll
+          for (int q = 0; q < 4; ++q) x[q] = load_item(ln, q0 + q, hcol);
+  #pragma unroll
+          for (int q = 0; q < 4; ++q) acc[q0 + q] += x[q];
+        }
+        wave_sync();
+      }
+      // Z of sample s (this half): the dense row and the pooled bags
+  #pragma unroll
+      for (int q = 0; q < (256 / 4 + 63) / 64; ++q) {
+        const int c = lane + 64 * q;
+        if (c < D4) *reinterpret_cast<f4v*>(l.z + 4 * c) = dv[q];
+      }
+      {
+        const int ln = opaque_lane();
+  #pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+          int t, c;
+          const bool in = item_of(ln, q, t, c);
+          const uint32_t lq = (uint32_t)__shfl((int)len, in ? t : 0, 64);
+          if (!in) continue;
+          f4v v = acc[q];
+          if (MEAN && lq > 0) v *= 1.0f / (float)lq;
+          *reinterpret_cast<f4v*>(l.z + (size_t)(t + 1) * zs + 4 * c) = v;
+        }
+      }
+      if (h == NH - 1) {  // position 0 of the next sample
+        if (lane < T) l.row[lane] = row_of(idn, lenn, 0);
+        maxlen = wave_max(lenn);
+        o0 = o0n;
+        len = lenn;
+        o0n = o0nn;
+        lenn = lennn;
+      } else if (maxlen > 1) {  // the walk moved on: position 0 again for the next half
+        if (lane < T) l.row[lane] = resolve(o0, len, 0);
       }
       wave_sync();
+      if (h == 0) rotate();
+      sp = s;
+      hp = h;
     }
-    // Z of sample s: the dense row and the pooled bags
-#pragma unroll
-    for (int q = 0; q < (256 / 4 + 63) / 64; ++q) {
-      const int c = lane + 64 * q;
-      if (c < D4) *reinterpret_cast<f4v*>(l.z + 4 * c) = dv[q];
-    }
-    {
-      const int ln = opaque_lane();
-#pragma unroll
-      for (int q = 0; q < NQ; ++q) {
-        int t, c;
-        const bool in = item_of(ln, q, t, c);
-        const uint32_t lq = (uint32_t)__shfl((int)len, in ? t : 0, 64);
-        if (!in) continue;
-        f4v v = acc[q];
-        if (MEAN && lq > 0) v *= 1.0f / (float)lq;
-        *reinterpret_cast<f4v*>(l.z + (size_t)(t + 1) * zs + 4 * c) = v;
-      }
-    }
-    // position 0 of the next sample
-    if (lane < T) l.row[lane] = row_of(idn, lenn, 0);
-    maxlen = wave_max(lenn);
-    o0 = o0n;
-    len = lenn;
-    o0n = o0nn;
-    lenn = lennn;
-    wave_sync();
-    rotate();
-    sp = s;
     s = sn;
   }
-  if (sp >= 0) consume(sp);
+  if (sp >= 0) consume(sp, hp);
   wave_sync();
 }
 
-template <bool MEAN, int NQ>
+template <bool MEAN, int NQ, int NH>
 __global__ __launch_bounds__(256, 2) void k_interact_fwd(
     const float* __restrict__ dense, const int64_t* __restrict__ offsets,
     const int64_t* __restrict__ ids, const int64_t* __restrict__ row_off,
@@ -270,29 +290,33 @@ __global__ __launch_bounds__(256, 2) void k_interact_fwd(
   extern __shared__ float lds[];
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int wpb = blockDim.x >> 6;
-  const WaveLds l = wave_lds(lds, T, D, false, w);
-  const int zs = z_stride(D);
+  const int Dh = D / NH;
+  const WaveLds l = wave_lds(lds, T, Dh, false, w);
+  const int zs = z_stride(Dh);
   const int P = (T + 1) * T / 2;
   const int64_t ostride = (int64_t)D + P;
   uint32_t bad = 0;
   const int ri = lane & 15, kq = lane >> 4;
-  auto consume = [&](int64_t s) {
+  // the Gram blocks, summed over the column halves of a sample
+  f4v a00 = {0.f, 0.f, 0.f, 0.f}, a10 = a00, a11 = a00;
+  auto consume = [&](int64_t s, int h) {
+    const int hcol = h * Dh;
     // the copied dense slot (rows of D + P floats: not 16-byte aligned)
-    for (int d = lane; d < D; d += 64) out[s * ostride + d] = l.z[d];
+    for (int d = lane; d < Dh; d += 64) out[s * ostride + hcol + d] = l.z[d];
     // Gram blocks (0,0), (1,0), (1,1) of Z Z^T; rows past T are zero.  Both
     // operands are rows of Z, so the sum over k may visit the columns in any
     // order shared by A and B: in each 16-column step lane (ri, kq) supplies
     // the four adjacent columns 4 kq .. 4 kq + 3 (one 16-byte LDS read per
     // row) to four consecutive K-steps.  Rows past T read row T (in bounds)
     // and are replaced by zeros.
-    f4v a00 = {0.f, 0.f, 0.f, 0.f}, a10 = a00, a11 = a00;
     const bool two = T + 1 > 16;
     const bool has0 = ri <= T, has1 = 16 + ri <= T;
     const f4v zero = {0.f, 0.f, 0.f, 0.f};
+    if (h == 0) a00 = a10 = a11 = zero;
     const float* z0p = l.z + (size_t)(has0 ? ri : T) * zs + 4 * kq;
     const float* z1p = l.z + (size_t)(has1 ? 16 + ri : T) * zs + 4 * kq;
     if (two) {
-      for (int k0 = 0; k0 < D; k0 += 16) {
+      for (int k0 = 0; k0 < Dh; k0 += 16) {
         f4v x0 = *reinterpret_cast<const f4v*>(z0p + k0);
         f4v x1 = *reinterpret_cast<const f4v*>(z1p + k0);
         x0 = has0 ? x0 : zero;
@@ -305,7 +329,7 @@ __global__ __launch_bounds__(256, 2) void k_interact_fwd(
         }
       }
     } else {
-      for (int k0 = 0; k0 < D; k0 += 16) {
+      for (int k0 = 0; k0 < Dh; k0 += 16) {
         f4v x0 = *reinterpret_cast<const f4v*>(z0p + k0);
         x0 = has0 ? x0 : zero;
 #pragma unroll
@@ -313,6 +337,7 @@ __global__ __launch_bounds__(256, 2) void k_interact_fwd(
           a00 = __builtin_amdgcn_mfma_f32_16x16x4f32(x0[m], x0[m], a00, 0, 0, 0);
       }
     }
+    if (h != NH - 1) return;
     // lane holds block[4 (l / 16) + r][l % 16]; pairs i > j go to staging
     const int j0 = lane & 15;
 #pragma unroll
@@ -330,9 +355,10 @@ __global__ __launch_bounds__(256, 2) void k_interact_fwd(
     wave_sync();
     for (int p = lane; p < P; p += 64) out[s * ostride + D + p] = l.pairs[p];
   };
-  // up to 16 items per lane stay in registers (sum pooling; with mean pooling
-  // the bag-length scale leaves too few registers, and 16 held items spill)
-  pipelined_samples<MEAN, NQ, (NQ <= 16 && !MEAN)>(l, (int64_t)blockIdx.x * wpb + w,
+  // up to 16 items per lane stay in registers (sum pooling over whole rows;
+  // with mean pooling, or with the Gram sums carried across column halves,
+  // 16 held items spill)
+  pipelined_samples<MEAN, NQ, NH, (NQ <= 16 && !MEAN && NH == 1)>(l, (int64_t)blockIdx.x * wpb + w,
                                     (int64_t)gridDim.x * wpb, dense, offsets, ids, row_off, rows,
                                     W, B, T, D, nnz, bad, [](int64_t) {}, consume, []() {});
   const uint32_t any = (uint32_t)(__ballot(bad != 0) != 0);
@@ -343,7 +369,7 @@ __global__ __launch_bounds__(256, 2) void k_interact_fwd(
   }
 }
 
-template <bool MEAN, int NQ>
+template <bool MEAN, int NQ, int NH>
 __global__ __launch_bounds__(256, 2) void k_interact_bwd(
     const float* __restrict__ dense, const int64_t* __restrict__ offsets,
     const int64_t* __restrict__ ids, const int64_t* __restrict__ row_off,
@@ -353,8 +379,9 @@ __global__ __launch_bounds__(256, 2) void k_interact_bwd(
   extern __shared__ float lds[];
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int wpb = blockDim.x >> 6;
-  const WaveLds l = wave_lds(lds, T, D, true, w);
-  const int zs = z_stride(D);
+  const int Dh = D / NH;
+  const WaveLds l = wave_lds(lds, T, Dh, true, w);
+  const int zs = z_stride(Dh);
   const int P = (T + 1) * T / 2;
   const int64_t gstride = (int64_t)D + P;
   uint32_t bad = 0;
@@ -392,15 +419,16 @@ __global__ __launch_bounds__(256, 2) void k_interact_bwd(
     }
     wave_sync();
   };
-  auto consume = [&](int64_t s) {
+  auto consume = [&](int64_t s, int h) {
+    const int hcol = h * Dh;
     // the dense slot's upstream gradient, added to dz_0 once the products are
     // done (loaded now, used last)
-    const float* go = grad_out + s * gstride;
+    const float* go = grad_out + s * gstride + hcol;
     float gdn[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int d = lane + 64 * q;
-      gdn[q] = d < D ? go[d] : 0.0f;
+      gdn[q] = d < Dh ? go[d] : 0.0f;
     }
     const bool two = T + 1 > 16;
     // K runs over the rows of Z in the order k = 8 kq + m (m = 0..7) for both
@@ -408,7 +436,7 @@ __global__ __launch_bounds__(256, 2) void k_interact_bwd(
     // Z[8 kq + m][n0 + ri] (zero past row T; rows past T read row T).
     const float* ga = l.g + ri * kGStride + 8 * kq;
     const float* gb = l.g + (16 + ri) * kGStride + 8 * kq;
-    for (int n0 = 0; n0 < D; n0 += 16) {
+    for (int n0 = 0; n0 < Dh; n0 += 16) {
       // both 16-row blocks of dZ for these 16 columns, side by side:
       // A[i][k] = G[16 mb + i][k], B[k][n] = Z[k][n0 + n].  G is read again
       // for every column block rather than held in registers.
@@ -446,20 +474,20 @@ __global__ __launch_bounds__(256, 2) void k_interact_bwd(
         if (row == 0)
           l.z[col] = acc0[r];
         else if (row <= T)
-          grad_pooled[((size_t)s * T + (row - 1)) * D + col] = acc0[r];
+          grad_pooled[((size_t)s * T + (row - 1)) * D + hcol + col] = acc0[r];
         if (two && 16 + row <= T)
-          grad_pooled[((size_t)s * T + (15 + row)) * D + col] = acc1[r];
+          grad_pooled[((size_t)s * T + (15 + row)) * D + hcol + col] = acc1[r];
       }
     }
     wave_sync();
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int d = lane + 64 * q;
-      if (d < D) grad_dense[s * D + d] = gdn[q] + l.z[d];
+      if (d < Dh) grad_dense[s * D + hcol + d] = gdn[q] + l.z[d];
     }
   };
   // the backward's products need the registers: its items are recomputed
-  pipelined_samples<MEAN, NQ, false>(l, (int64_t)blockIdx.x * wpb + w,
+  pipelined_samples<MEAN, NQ, NH, false>(l, (int64_t)blockIdx.x * wpb + w,
                                      (int64_t)gridDim.x * wpb, dense, offsets, ids, row_off,
                                      rows, W, B, T, D, nnz, bad, issue, consume, rotate);
   const uint32_t any = (uint32_t)(__ballot(bad != 0) != 0);
@@ -488,28 +516,29 @@ unsigned interact_grid(const Handle& h, const void* fn, int64_t B, int wpb, size
 
 // Items (table, float4 column) per lane, rounded up to 4, 8, 16 or 32.
 int items_per_lane(const Handle& h) {
-  const int n = (h.T * (h.D / 4) + 63) / 64;
+  const int n = (h.T * (h.D / col_blocks(h.D) / 4) + 63) / 64;
   return n <= 4 ? 4 : n <= 8 ? 8 : n <= 16 ? 16 : 32;
 }
 
-template <bool BWD, bool MEAN, int NQ>
+template <bool BWD, bool MEAN, int NQ, int NH>
 hipError_t launch_nq(const Handle& h, const int64_t* offsets, const int64_t* ids, int64_t B,
                      int64_t nnz, const float* dense, float* out, const float* grad_out,
                      float* grad_dense, float* grad_pooled, hipStream_t s) {
-  const int wpb = waves_per_block(h.D);
-  const size_t shm = sizeof(float) * wave_lds_floats(h.T, h.D, BWD) * (size_t)wpb;
+  const int Dh = h.D / col_blocks(h.D);
+  const int wpb = waves_per_block(Dh);
+  const size_t shm = sizeof(float) * wave_lds_floats(h.T, Dh, BWD) * (size_t)wpb;
   // more than 64 KiB of dynamic LDS has to be allowed per kernel
-  const void* fn = BWD ? reinterpret_cast<const void*>(&k_interact_bwd<MEAN, NQ>)
-                       : reinterpret_cast<const void*>(&k_interact_fwd<MEAN, NQ>);
+  const void* fn = BWD ? reinterpret_cast<const void*>(&k_interact_bwd<MEAN, NQ, NH>)
+                       : reinterpret_cast<const void*>(&k_interact_fwd<MEAN, NQ, NH>);
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
   if (e != hipSuccess) return e;
   const unsigned grid = interact_grid(h, fn, B, wpb, shm);
   if (BWD)
-    hipLaunchKernelGGL((k_interact_bwd<MEAN, NQ>), dim3(grid), dim3(64 * wpb), shm, s, dense,
+    hipLaunchKernelGGL((k_interact_bwd<MEAN, NQ, NH>), dim3(grid), dim3(64 * wpb), shm, s, dense,
                        offsets, ids, h.sv.row_off, h.sv.rows, h.W, B, h.T, h.D, nnz, grad_out,
                        grad_dense, grad_pooled, h.sv.flags);
   else
-    hipLaunchKernelGGL((k_interact_fwd<MEAN, NQ>), dim3(grid), dim3(64 * wpb), shm, s, dense,
+    hipLaunchKernelGGL((k_interact_fwd<MEAN, NQ, NH>), dim3(grid), dim3(64 * wpb), shm, s, dense,
                        offsets, ids, h.sv.row_off, h.sv.rows, h.W, B, h.T, h.D, nnz, out,
                        h.sv.flags);
   return hipGetLastError();
@@ -519,20 +548,23 @@ template <bool BWD, bool MEAN>
 hipError_t launch_mean(const Handle& h, const int64_t* offsets, const int64_t* ids, int64_t B,
                        int64_t nnz, const float* dense, float* out, const float* grad_out,
                        float* grad_dense, float* grad_pooled, hipStream_t s) {
-  switch (items_per_lane(h)) {
-    case 4:
-      return launch_nq<BWD, MEAN, 4>(h, offsets, ids, B, nnz, dense, out, grad_out, grad_dense,
-                                     grad_pooled, s);
-    case 8:
-      return launch_nq<BWD, MEAN, 8>(h, offsets, ids, B, nnz, dense, out, grad_out, grad_dense,
-                                     grad_pooled, s);
-    case 16:
-      return launch_nq<BWD, MEAN, 16>(h, offsets, ids, B, nnz, dense, out, grad_out, grad_dense,
-                                      grad_pooled, s);
-    default:
-      return launch_nq<BWD, MEAN, 32>(h, offsets, ids, B, nnz, dense, out, grad_out, grad_dense,
-                                      grad_pooled, s);
+#define EMB_IA(NQ, NH)                                                                     \
+  return launch_nq<BWD, MEAN, NQ, NH>(h, offsets, ids, B, nnz, dense, out, grad_out, grad_dense, \
+                                      grad_pooled, s)
+  if (col_blocks(h.D) == 2) {  // a half has at most 31 x 32 items: 16 per lane
+    switch (items_per_lane(h)) {
+      case 4: EMB_IA(4, 2);
+      case 8: EMB_IA(8, 2);
+      default: EMB_IA(16, 2);
+    }
   }
+  switch (items_per_lane(h)) {
+    case 4: EMB_IA(4, 1);
+    case 8: EMB_IA(8, 1);
+    case 16: EMB_IA(16, 1);
+    default: EMB_IA(32, 1);
+  }
+#undef EMB_IA
 }
 
 }  // namespace

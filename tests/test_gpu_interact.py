@@ -3,7 +3,8 @@ backward, on the GPU against the oracle through the C ABI.  Cases cover one
 and two 16-row Gram blocks (T + 1 <= 16 and > 16), the largest shapes
 (T = 31, D = 256), widths whose float4 count is not a power of two (D = 48,
 112), mean pooling of multi-hot bags, empty bags, absent and
-out-of-range ids, ten seeded random shapes (T from 1 to 31, D a multiple of
+out-of-range ids, rows of more than 128 floats taken in two column halves
+(one-hot, multi-hot mean, ragged with empty bags), ten seeded random shapes (T from 1 to 31, D a multiple of
 16 up to 256, batches from 1 sample), and a training step whose embedding
 gradient comes from the interaction backward."""
 import numpy as np
@@ -45,6 +46,14 @@ def case(name):
     if name == "one_hot_26_d112":  # D / 4 = 28, 12 items per lane, two row blocks
         return synth.workload(2, T=26, B=700, D=112,
                               rows=synth.log_uniform_rows(26, 2.0, 4.0, 3, 2)), False
+    if name == "multi_hot_mean_d256":  # two column halves, bags walked once per half
+        w = synth.workload(3, T=5, B=400, D=256)
+        w.rows = np.array([3000, 50, 7000, 900, 20], np.int64)
+        return w, True
+    if name == "ragged_d192":  # two halves of 96 columns, empty bags, absent ids
+        w = synth.workload(3, T=7, B=300, D=192)
+        w.rows = np.array([40, 900, 7, 300, 60, 5000, 2], np.int64)
+        return w, False
     if name.startswith("rand"):  # seeded random shape within the supported range
         rng = np.random.default_rng(700 + int(name[4:]))
         T = int(rng.integers(1, 32))
@@ -59,7 +68,7 @@ def case(name):
 
 
 def batch_of(w, name):
-    if name == "small_ragged":  # bags of 0..6 ids, a fifth of them empty, some absent ids
+    if name in ("small_ragged", "ragged_d192"):  # bags of 0..6 ids, a fifth empty, some absent
         offsets, ids, _ = synth.random_small(8, w.T, w.D, w.B, w.rows, max_len=6, empty_frac=0.2)
         ids = ids.copy()
         ids[::7] = eb.EMB_ID_ABSENT
@@ -84,7 +93,8 @@ def z_abs(o, w, offsets, ids, dense, mean):
 
 
 @pytest.mark.parametrize("name", ["one_hot_26", "multi_hot_mean_8", "max_31x256",
-                                  "small_ragged", "multi_hot_d48", "one_hot_26_d112"]
+                                  "small_ragged", "multi_hot_d48", "one_hot_26_d112",
+                                  "multi_hot_mean_d256", "ragged_d192"]
                          + [f"rand{k}" for k in range(10)])
 def test_interaction_matches_oracle(name):
     w, mean = case(name)
