@@ -43,11 +43,16 @@ constexpr int kZRows = 32;  // T + 1 <= 32
 // pair staging (forward) and the row of every table's current occurrence.
 constexpr int kGStride = 36;
 __host__ __device__ inline int z_stride(int D) { return D + 4; }
-// Rows wider than 128 floats (a multiple of 32) go through the pipeline in two
-// column halves: both kernels are separable over columns (the Gram matrix is a
-// sum over them, dZ = G Z column by column), and a half keeps the registers
-// and LDS of a 128-float row.  Z then holds one half.
-__host__ __device__ inline int col_blocks(int D) { return D > 128 && D % 32 == 0 ? 2 : 1; }
+// Rows wider than 128 floats go through the pipeline in two column halves
+// (widths multiples of 16, the first the wider): both kernels are separable
+// over columns (the Gram matrix is a sum over them, dZ = G Z column by
+// column), and a half keeps the registers and LDS of a 128-float row.  Z then
+// holds one half.
+__host__ __device__ inline int col_blocks(int D) { return D > 128 ? 2 : 1; }
+__host__ __device__ inline int half_width(int D, int h) {  // columns of half h
+  const int w0 = col_blocks(D) == 1 ? D : 16 * ((D / 16 + 1) / 2);
+  return h == 0 ? w0 : D - w0;
+}
 __host__ __device__ inline size_t wave_lds_floats(int T, int D, bool bwd) {
   return (size_t)(T + 1) * z_stride(D) + (bwd ? 32 * kGStride : 512) + 32;
 }
@@ -103,9 +108,9 @@ __device__ void pipelined_samples(const WaveLds& l, int64_t first, int64_t strid
                                   int64_t nnz, uint32_t& bad, Issue issue, Consume consume,
                                   Rotate rotate) {
   const int lane = threadIdx.x & 63;
-  const int Dh = D / NH;  // the columns of one half (NH = col_blocks(D))
-  const int D4 = Dh >> 2;
-  const int zs = z_stride(Dh);
+  static_assert(NH == 1 || !HOLD_ITEMS, "held items assume one column block");
+  const int zs = z_stride(half_width(D, 0));  // NH = col_blocks(D)
+  int D4 = half_width(D, 0) >> 2;  // float4 columns of the current half
   // rows, global row offsets and valid offsets all fit 32 bits (the calls
   // reject nnz >= 2^32 - 16; global rows are 32-bit)
   const uint32_t nrows = lane < T ? (uint32_t)rows[lane] : 0u;
@@ -117,8 +122,8 @@ __device__ void pipelined_samples(const WaveLds& l, int64_t first, int64_t strid
   // the compiler does not hold them across the sample loop either), with the
   // quotient in fp32: for index < 2048 and D4 <= 64, (index + 1/2) / D4 lies
   // at least 1/128 from an integer, far beyond the rounding error.
-  const int nitems = T * D4;
-  const float rd4 = 1.0f / (float)D4;
+  int nitems = T * D4;
+  float rd4 = 1.0f / (float)D4;
   int tc[HOLD_ITEMS ? NQ : 1];
   if constexpr (HOLD_ITEMS) {
 #pragma unroll
@@ -206,7 +211,12 @@ __device__ void pipelined_samples(const WaveLds& l, int64_t first, int64_t strid
     uint32_t o0nn = 0u, lennn = 0u;
     int64_t idn = kAbsentId;
     for (int h = 0; h < NH; ++h) {
-      const int hcol = h * Dh;
+      const int hcol = h == 0 ? 0 : half_width(D, 0);
+      if (NH > 1) {
+        D4 = half_width(D, h) >> 2;
+        nitems = T * D4;
+        rd4 = 1.0f / (float)D4;
+      }
       if (h == 0) {
         bag_of(sn + stride, o0nn, lennn);
         idn = id_at(o0n, lenn, 0);
@@ -290,9 +300,8 @@ __global__ __launch_bounds__(256, 2) void k_interact_fwd(
   extern __shared__ float lds[];
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int wpb = blockDim.x >> 6;
-  const int Dh = D / NH;
-  const WaveLds l = wave_lds(lds, T, Dh, false, w);
-  const int zs = z_stride(Dh);
+  const WaveLds l = wave_lds(lds, T, half_width(D, 0), false, w);
+  const int zs = z_stride(half_width(D, 0));
   const int P = (T + 1) * T / 2;
   const int64_t ostride = (int64_t)D + P;
   uint32_t bad = 0;
@@ -300,7 +309,8 @@ __global__ __launch_bounds__(256, 2) void k_interact_fwd(
   // the Gram blocks, summed over the column halves of a sample
   f4v a00 = {0.f, 0.f, 0.f, 0.f}, a10 = a00, a11 = a00;
   auto consume = [&](int64_t s, int h) {
-    const int hcol = h * Dh;
+    const int hcol = h == 0 ? 0 : half_width(D, 0);
+    const int Dh = half_width(D, h);
     // the copied dense slot (rows of D + P floats: not 16-byte aligned)
     for (int d = lane; d < Dh; d += 64) out[s * ostride + hcol + d] = l.z[d];
     // Gram blocks (0,0), (1,0), (1,1) of Z Z^T; rows past T are zero.  Both
@@ -358,9 +368,11 @@ __global__ __launch_bounds__(256, 2) void k_interact_fwd(
   // up to 16 items per lane stay in registers (sum pooling over whole rows;
   // with mean pooling, or with the Gram sums carried across column halves,
   // 16 held items spill)
-  pipelined_samples<MEAN, NQ, NH, (NQ <= 16 && !MEAN && NH == 1)>(l, (int64_t)blockIdx.x * wpb + w,
-                                    (int64_t)gridDim.x * wpb, dense, offsets, ids, row_off, rows,
-                                    W, B, T, D, nnz, bad, [](int64_t) {}, consume, []() {});
+  constexpr bool kHold = NQ <= 16 && !MEAN && NH == 1;
+  pipelined_samples<MEAN, NQ, NH, kHold>(l, (int64_t)blockIdx.x * wpb + w,
+                                         (int64_t)gridDim.x * wpb, dense, offsets, ids, row_off,
+                                         rows, W, B, T, D, nnz, bad, [](int64_t) {}, consume,
+                                         []() {});
   const uint32_t any = (uint32_t)(__ballot(bad != 0) != 0);
   if (any) {
     uint32_t all = bad;
@@ -379,9 +391,8 @@ __global__ __launch_bounds__(256, 2) void k_interact_bwd(
   extern __shared__ float lds[];
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int wpb = blockDim.x >> 6;
-  const int Dh = D / NH;
-  const WaveLds l = wave_lds(lds, T, Dh, true, w);
-  const int zs = z_stride(Dh);
+  const WaveLds l = wave_lds(lds, T, half_width(D, 0), true, w);
+  const int zs = z_stride(half_width(D, 0));
   const int P = (T + 1) * T / 2;
   const int64_t gstride = (int64_t)D + P;
   uint32_t bad = 0;
@@ -420,7 +431,8 @@ __global__ __launch_bounds__(256, 2) void k_interact_bwd(
     wave_sync();
   };
   auto consume = [&](int64_t s, int h) {
-    const int hcol = h * Dh;
+    const int hcol = h == 0 ? 0 : half_width(D, 0);
+    const int Dh = half_width(D, h);
     // the dense slot's upstream gradient, added to dz_0 once the products are
     // done (loaded now, used last)
     const float* go = grad_out + s * gstride + hcol;
@@ -514,17 +526,17 @@ unsigned interact_grid(const Handle& h, const void* fn, int64_t B, int wpb, size
   return (unsigned)(want < cap ? (want > 0 ? want : 1) : cap);
 }
 
-// Items (table, float4 column) per lane, rounded up to 4, 8, 16 or 32.
+// Items (table, float4 column) per lane, rounded up to 4, 8 or 16.
 int items_per_lane(const Handle& h) {
-  const int n = (h.T * (h.D / col_blocks(h.D) / 4) + 63) / 64;
-  return n <= 4 ? 4 : n <= 8 ? 8 : n <= 16 ? 16 : 32;
+  const int n = (h.T * (half_width(h.D, 0) / 4) + 63) / 64;
+  return n <= 4 ? 4 : n <= 8 ? 8 : 16;
 }
 
 template <bool BWD, bool MEAN, int NQ, int NH>
 hipError_t launch_nq(const Handle& h, const int64_t* offsets, const int64_t* ids, int64_t B,
                      int64_t nnz, const float* dense, float* out, const float* grad_out,
                      float* grad_dense, float* grad_pooled, hipStream_t s) {
-  const int Dh = h.D / col_blocks(h.D);
+  const int Dh = half_width(h.D, 0);
   const int wpb = waves_per_block(Dh);
   const size_t shm = sizeof(float) * wave_lds_floats(h.T, Dh, BWD) * (size_t)wpb;
   // more than 64 KiB of dynamic LDS has to be allowed per kernel
@@ -551,7 +563,8 @@ hipError_t launch_mean(const Handle& h, const int64_t* offsets, const int64_t* i
 #define EMB_IA(NQ, NH)                                                                     \
   return launch_nq<BWD, MEAN, NQ, NH>(h, offsets, ids, B, nnz, dense, out, grad_out, grad_dense, \
                                       grad_pooled, s)
-  if (col_blocks(h.D) == 2) {  // a half has at most 31 x 32 items: 16 per lane
+  // a row or half of at most 128 floats has at most 31 x 32 items: 16 per lane
+  if (col_blocks(h.D) == 2) {
     switch (items_per_lane(h)) {
       case 4: EMB_IA(4, 2);
       case 8: EMB_IA(8, 2);
@@ -561,8 +574,7 @@ hipError_t launch_mean(const Handle& h, const int64_t* offsets, const int64_t* i
   switch (items_per_lane(h)) {
     case 4: EMB_IA(4, 1);
     case 8: EMB_IA(8, 1);
-    case 16: EMB_IA(16, 1);
-    default: EMB_IA(32, 1);
+    default: EMB_IA(16, 1);
   }
 #undef EMB_IA
 }
